@@ -1,0 +1,248 @@
+#!/usr/bin/env python3
+"""Benchmark of the spectral transform KV-cache codec on one MI355X.
+
+Workload (one "step" = one pass of the whole hot path over one batch):
+  Llama-3.1-8B-shaped layer: 8 KV heads x {K, V} = 16 streams of 32768 bf16
+  tokens (head dim 128), spiked-Gaussian synthetic data (lambda_i = i^-1.2,
+  2 outlier channels at 20x), calibrated on the first 2048 tokens.
+  For each average budget 4.0 / 2.0 / 1.33 bits: batched encode of the 16
+  streams, batched decode, and one decode-step attention (32 query heads,
+  GQA 4) over the packed cache. Plus the Walsh-Hadamard comparison path
+  (3-bit Lloyd-Max codebook) encode + decode on 16 Student-t(3) streams of
+  the same shape. Calibration runs once, before timing.
+
+Prints ONE JSON line. `value` is the algorithmic bytes of all steps divided
+by their wall time on the GPU stream (GB/s); per-op figures are in
+`breakdown`; `roofline` is for the op with the largest time share;
+`cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+WORKLOAD = 2
+RHT_WORKLOAD = 3
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--tokens", type=int, default=None, help="override tokens per stream (testing only)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    return ap.parse_args()
+
+
+def algorithmic_bytes(total_bits, n, streams, elem=2):
+    """Encode or decode: read/write the tokens plus the packed records."""
+    return streams * n * (128 * elem + total_bits / 8.0)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: this build runs on one GPU only (no collectives or sharding); "
+              "run it with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    import spectral_transform_codec_amd as stc
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    w = synth.WORKLOADS[WORKLOAD]
+    w3 = synth.WORKLOADS[RHT_WORKLOAD]
+    n = args.tokens or w.n_tokens
+    heads = w.kv_heads
+    S = 2 * heads                       # K and V of every KV head
+    g = w.group
+
+    # ------------------------------------------------------------ inputs
+    t_setup = time.time()
+    x2 = torch.empty((S, n, 128), dtype=torch.bfloat16, device=dev)
+    x3 = torch.empty((S, n, 128), dtype=torch.bfloat16, device=dev)
+    for h in range(heads):
+        for kind in (0, 1):
+            x2[2 * h + kind] = torch.from_numpy(synth.stream(w, 0, 0, h, kind, n=n)).to(dev, torch.bfloat16)
+            x3[2 * h + kind] = torch.from_numpy(synth.stream(w3, 0, 0, h, kind, n=n)).to(dev, torch.bfloat16)
+    q = torch.from_numpy(np.stack([synth.queries(w, 0, 0, h) for h in range(heads)])).to(dev)
+
+    # ------------------------------------------------ calibration (untimed)
+    t_cal = time.time()
+    budgets = list(w.budgets)
+    arrays = {}
+    for b in budgets:
+        arrays[b] = stc.StateArray([stc.calibrate_head(x2[s], w.n_calib, b) for s in range(S)])
+    torch.cuda.synchronize()
+    cal_s = time.time() - t_cal
+    cb, _ = stc.lloyd_max(synth.sphere_coordinate_samples())
+    cb32 = cb.astype(np.float32)
+    rht_arr = stc.StateArray([stc.rht_state_init(synth.random_signs(3, 0, 0, s // 2, s % 2), cb32)
+                              for s in range(S)])
+    kmap = torch.arange(0, S, 2, dtype=torch.int32, device=dev)
+    vmap = torch.arange(1, S, 2, dtype=torch.int32, device=dev)
+
+    # ---------------------------------------------------- buffers (untimed)
+    packed = {b: torch.empty((S, stc.packed_bytes(arrays[b].max_bits, n)), dtype=torch.uint8, device=dev)
+              for b in budgets}
+    xhat = torch.empty((S, n, 128), dtype=torch.bfloat16, device=dev)
+    attn_out = {b: torch.empty((heads, g, 128), dtype=torch.float32, device=dev) for b in budgets}
+    ws = torch.empty(stc.attend_workspace_bytes(heads, g, n), dtype=torch.uint8, device=dev)
+    rpacked = torch.empty((S, stc.packed_bytes(384, n)), dtype=torch.uint8, device=dev)
+    rnorms = torch.empty((S, n), dtype=torch.float32, device=dev)
+    setup_s = time.time() - t_setup
+
+    ops = []  # (name, fn, algorithmic bytes)
+    for b in budgets:
+        B = arrays[b].max_bits
+        ops.append((f"encode@{b}", (lambda b=b: stc.encode_kv_batched(arrays[b], x2, packed=packed[b])),
+                    algorithmic_bytes(B, n, S)))
+        ops.append((f"decode@{b}", (lambda b=b: stc.decode_kv_batched(arrays[b], packed[b], n, out=xhat)),
+                    algorithmic_bytes(B, n, S)))
+        kp, vp = packed[b][0::2], packed[b][1::2]
+        ops.append((f"attend@{b}",
+                    (lambda b=b, kp=kp, vp=vp: stc.attend_compressed_batched(arrays[b], kmap, vmap, kp, vp, n, q,
+                                                                            ws=ws, out=attn_out[b])),
+                    heads * n * 2 * B / 8.0 + 2 * q.numel() * 4))
+    ops.append(("rht_encode", lambda: stc.encode_kv_batched(rht_arr, x3, packed=rpacked, norms=rnorms),
+                S * n * (256 + 48 + 4)))
+    ops.append(("rht_decode", lambda: stc.decode_kv_batched(rht_arr, rpacked, n, norms=rnorms, out=xhat),
+                S * n * (256 + 48 + 4)))
+
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        for _, fn, _ in ops:
+            fn()
+    torch.cuda.synchronize()
+
+    # ------------------------------------------------------- timed region
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in ops]
+          for _ in range(args.steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for k in range(args.steps):
+        for i, (_, fn, _) in enumerate(ops):
+            ev[k][i][0].record(stream)
+            fn()
+            ev[k][i][1].record(stream)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    ms_per_step = total_ms / args.steps
+
+    per_op = {}
+    for i, (name, _, nbytes) in enumerate(ops):
+        ms = [ev[k][i][0].elapsed_time(ev[k][i][1]) for k in range(args.steps)]
+        avg = sum(ms) / len(ms)
+        per_op[name] = {"ms": round(avg, 5), "GBps": round(nbytes / (avg * 1e-3) / 1e9, 1),
+                        "pct_hbm_peak": round(100.0 * nbytes / (avg * 1e-3) / 1e9 / HBM_PEAK_GBPS, 1),
+                        "bytes": int(nbytes)}
+    step_bytes = sum(o[2] for o in ops)
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    dominant = max(ops, key=lambda o: per_op[o[0]]["ms"])
+    dname = dominant[0]
+    d_ms = per_op[dname]["ms"]
+    achieved = dominant[2] / (d_ms * 1e-3) / 1e9
+    codec_names = [o[0] for o in ops if o[0].startswith(("encode", "decode"))]
+    codec_bytes = sum(o[2] for o in ops if o[0] in codec_names)
+    codec_ms = sum(per_op[nm]["ms"] for nm in codec_names)
+    attn_names = [o[0] for o in ops if o[0].startswith("attend")]
+
+    # --------------------------------------------- CPU oracle baseline
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(args.cpu_seconds)
+
+    line = {
+        "metric": "KV codec encode/decode GB/s (% of HBM peak); compressed decode-attn tokens/s",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "Llama-3.1-8B-shaped layer: 8 KV heads x K/V = 16 streams x "
+                               f"{n} bf16 tokens, head_dim 128, budgets {budgets} bits, "
+                               "GQA-4 decode attention; plus 16 Student-t(3) streams through the "
+                               "Walsh-Hadamard 3-bit path",
+                   "streams": S, "tokens": n, "budgets": budgets, "group": g},
+        "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 1),
+        "codec_GBps": round(codec_bytes / (codec_ms * 1e-3) / 1e9, 1),
+        "attn_tokens_per_s": {nm: round(1e3 / per_op[nm]["ms"], 1) for nm in attn_names},
+        "breakdown": per_op,
+        "roofline": {"bound": "hbm", "kernel": dname, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None},
+        "cpu_baseline": cpu,
+        "setup_s": round(setup_s, 2),
+        "calibrate_s": round(cal_s, 2),
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(seconds):
+    """The CPU oracle, as it stands, on a bounded sample of the workload: one
+    K/V head pair of 4096 tokens at 2.0 bits (calibrate, encode, decode both
+    streams, one attention step) plus one Walsh-Hadamard stream of 4096
+    tokens (encode + decode), repeated for about `seconds`. BLAS limited to
+    one thread."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import synth
+    from oracle import codec, rht
+
+    w, w3 = synth.WORKLOADS[WORKLOAD], synth.WORKLOADS[RHT_WORKLOAD]
+    n = 4096
+    k = synth.stream(w, 0, 0, 0, 0, n=n)
+    v = synth.stream(w, 0, 0, 0, 1, n=n)
+    x3 = synth.stream(w3, 0, 0, 0, 0, n=n)
+    q = synth.queries(w, 0, 0, 0).astype(np.float64)
+    cb = rht.codebook_fp32(rht.lloyd_max(synth.sphere_coordinate_samples(200000))[0])
+    rst = rht.make_state(synth.random_signs(3, 0, 0, 0, 0), cb)
+    nbytes_rep = 2 * 2 * algorithmic_bytes(256, n, 1) + n * 2 * 256 / 8.0 + 2 * n * (256 + 48 + 4)
+    reps, total_bytes = 0, 0.0
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        while True:
+            ks, vs = codec.calibrate_head(k, 2048, 2.0), codec.calibrate_head(v, 2048, 2.0)
+            kp, vp = codec.encode_kv(ks, k), codec.encode_kv(vs, v)
+            codec.decode_kv(ks, kp, n, "bf16")
+            codec.decode_kv(vs, vp, n, "bf16")
+            codec.attend_compressed(ks, vs, kp, vp, n, q)
+            p3, n3 = rht.encode_kv(rst, x3)
+            rht.decode_kv(rst, p3, n3, n, "bf16")
+            reps += 1
+            total_bytes += nbytes_rep
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                break
+    return {"value": round(total_bytes / el / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{reps} x (1 KV head pair x {n} tokens at 2.0 bits: calibrate+encode+decode+attention; "
+                      f"1 Student-t stream x {n} tokens: RHT encode+decode), BLAS 1 thread, {el:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

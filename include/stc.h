@@ -1,0 +1,242 @@
+/*
+ * stc.h -- C ABI of the spectral transform KV-cache codec for MI355X (gfx950).
+ *
+ * What the codec computes (sources are cited by page title and section):
+ *
+ *  - Calibration. Per stream (one layer / batch / KV head / K-or-V), the
+ *    uncentred second moment of representative tokens is diagonalised; the
+ *    tokens are coded in its energy-ordered orthonormal eigenbasis.
+ *    ("Sintesi Tecnica: SPECTRA", gist.science, "Metodologia" observations 1
+ *    and 3, "La Pipeline di SPECTRA" step 1; Dutch ablation summary
+ *    "Technisch Overzicht: Ablatie ...", "Experimentele Opstelling",
+ *    SpectralQuant: a per-head eigenbasis calibrated on representative tokens.)
+ *  - Allocation. Integer bits per latent channel by reverse water-filling on
+ *    the eigenvalues; 0-bit channels are dropped. (SPECTRA summary,
+ *    "Metodologia" observation 2, "La Pipeline" step 2.)
+ *  - Encode. Each token is projected onto the basis, each kept channel is
+ *    scalar-quantized independently and the codes are appended to the stream.
+ *    (SPECTRA summary, "La Pipeline" step 3.)
+ *  - Decode / attention. Codes are unpacked, dequantized and rotated back; a
+ *    decode-step attention reads the packed K/V directly. (SPECTRA summary,
+ *    "La Pipeline" step 3 and "Significato e Rivendicazioni"; SPECTRA abstract,
+ *    arxivdaily.com: the cache is re-read in full at every generated token.)
+ *  - Comparison path. A randomized Walsh-Hadamard rotation with a fixed
+ *    Lloyd-Max codebook on every channel (Dutch ablation summary,
+ *    "Experimentele Opstelling", TurboQuant).
+ *
+ * Readings of the pages fixed by this library (the pages leave them open):
+ *  - second moment over the first n_calib tokens, no mean removed;
+ *  - eigenvalues descending; each eigenvector's largest-magnitude entry made
+ *    positive (lowest row index on a tie);
+ *  - water-filling is the greedy integer allocation under the model
+ *    D_j(b) = lambda_j 4^-b with widths 0..8, ties to the lowest channel,
+ *    total bits per token B = floor(avg_bits * d + 0.5);
+ *  - a kept channel j with L = 2^b_j levels uses the midrise uniform quantizer
+ *    with step delta_j = sqrt(lambda_j) * delta*(b_j), delta*(b) being the
+ *    MSE-optimal step for a unit Gaussian; the code is the number of
+ *    thresholds t_k = fl32((k - L/2) delta_j), k = 1..L-1, with t_k <= fl32(c)
+ *    (NaN -> 0); the level of code q is (q - (L-1)/2) delta_j;
+ *  - packed format F1: token t occupies stream bits [t*B, (t+1)*B); kept
+ *    channels in ascending index take bits [o_j, o_j + b_j), least
+ *    significant bit first; stream bit i is bit (i & 7) of byte (i >> 3); a
+ *    stream of n tokens is ceil(n*B/8) bytes, zero-padded to a multiple of 16;
+ *  - decode output is rounded to the stream dtype (bf16: round to nearest even);
+ *  - the Walsh-Hadamard path stores each token's L2 norm as fp32 next to the
+ *    codes, rotates y = H D (x / |x|) / sqrt(d) (H Sylvester order, D = +-1)
+ *    and codes every channel with 3 bits against the fp32 midpoints of an
+ *    8-entry fp32 codebook.
+ *
+ * Conventions for every call:
+ *  - d must be 128 on the GPU path (STC_EUNSUPPORTED otherwise).
+ *  - All buffers are owned by the caller. Pointers named *_dev are device
+ *    memory (HBM) of the current HIP device; all other pointers are host
+ *    memory. The library allocates no device memory.
+ *  - Arguments are validated before any device work; on an error nothing is
+ *    written and the status says why (see stc_last_error for a message).
+ *  - Device work is enqueued on the given stream and is asynchronous unless a
+ *    call says it synchronizes. Asynchronous faults surface at the caller's
+ *    next synchronization.
+ *  - A state is a device blob of stc_state_bytes() bytes (256-byte aligned)
+ *    plus a host stc_head_info written by the same call. Batched calls take
+ *    an array of states laid out back to back (stride stc_state_bytes()).
+ */
+#ifndef STC_H
+#define STC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* stc_stream_t; /* a hipStream_t; NULL = default stream */
+
+typedef int32_t stc_status;
+enum {
+  STC_OK = 0,
+  STC_EINVAL = -1,       /* null pointer, bad size, stride or alignment */
+  STC_EUNSUPPORTED = -2, /* d != 128, unknown dtype or transform */
+  STC_EBUDGET = -3,      /* bit vector does not sum to the budget, a width > 8,
+                            or budget > 8 d */
+  STC_EWORKSPACE = -4,   /* workspace too small */
+  STC_EDEVICE = -5       /* a HIP call failed */
+};
+
+enum { STC_F32 = 0, STC_BF16 = 1 };                                   /* K/V dtype */
+enum { STC_XFORM_EIGEN = 0, STC_XFORM_IDENTITY = 1, STC_XFORM_RHT = 2 }; /* transform */
+
+#define STC_D 128
+#define STC_MAX_BITS 8
+#define STC_RHT_BITS 3
+
+/* Host-side summary of a state, written by the calls that build one. */
+typedef struct {
+  int32_t d;            /* head dimension (128) */
+  int32_t xform;        /* STC_XFORM_* */
+  int32_t total_bits;   /* B, bits per token record */
+  int32_t n_kept;       /* channels with a non-zero width */
+  uint8_t bits[STC_D];  /* width of each latent channel (0..8) */
+  double lambda[STC_D]; /* second-moment eigenvalues (EIGEN), diagonal (IDENTITY) */
+  double steps[STC_D];  /* quantizer step of each kept channel (0 if dropped) */
+} stc_head_info;
+
+/* ------------------------------------------------------------ sizes */
+size_t stc_state_bytes(void);
+/* ceil(n_tokens * total_bits / 8) rounded up to a multiple of 16 (format F1). */
+size_t stc_packed_bytes(int32_t total_bits, int64_t n_tokens);
+/* Workspace of stc_attend_compressed_batched. */
+size_t stc_attend_workspace_bytes(int64_t n_pairs, int32_t group, int64_t n_tokens);
+
+/* ------------------------------------------------------- host math
+ * These run on the host only and need no GPU.                        */
+
+/* floor(avg_bits * d + 0.5). */
+int32_t stc_total_bits(float avg_bits, int32_t d);
+
+/* MSE-optimal step of the 2^bits-level midrise uniform quantizer for N(0,1),
+ * bits in 1..8 (returns NaN otherwise). */
+double stc_delta_star(int32_t bits);
+
+/* Greedy reverse water-filling: total_bits bits over d channels, one at a time
+ * to argmax lambda_j 2^(-2 b_j) among b_j < 8 (lambda <= 0 counts as 0; ties
+ * to the lowest j). bits_out[d]. STC_EBUDGET if total_bits > 8 d or < 0. */
+stc_status stc_water_fill(int32_t d, const double* lambda, int32_t total_bits, uint8_t* bits_out);
+
+/* Symmetric eigendecomposition A = U diag(lambda) U^T (cyclic Jacobi, fp64),
+ * lambda descending, columns sign-fixed as above. A, U row-major d*d. */
+stc_status stc_eigh(int32_t d, const double* a, double* u_out, double* lambda_out);
+
+/* Lloyd's algorithm on training samples for a `levels`-entry scalar codebook:
+ * start at the sample quantiles (k+1/2)/levels (linear interpolation between
+ * order statistics), thresholds = midpoints, centroids = cell means (a sample
+ * equal to a threshold joins the upper cell); stop once no centroid moves by
+ * tol or more, or after max_iter rounds. centroids_out[levels], ascending. */
+stc_status stc_lloyd_max(const double* samples, int64_t n, int32_t levels, double tol,
+                         int32_t max_iter, double* centroids_out, int32_t* iters_out);
+
+/* ------------------------------------------------------- states */
+
+/* Build a state from a given basis (EIGEN: u row-major d*d, column j = latent
+ * channel j; IDENTITY: u must be NULL), its variances and a bit vector.
+ * steps NULL: steps_j = sqrt(max(lambda_j,0)) * delta*(b_j); otherwise the
+ * given steps are used (e.g. to reproduce another implementation's state).
+ * Fills *info and state_dev; synchronizes `stream`. */
+stc_status stc_state_init(int32_t d, int32_t xform, const double* u, const double* lambda,
+                          const uint8_t* bits, const double* steps, stc_head_info* info,
+                          void* state_dev, stc_stream_t stream);
+
+/* Build a Walsh-Hadamard state: signs[d] in {-1,+1}, codebook[8] fp32
+ * ascending. Fills *info and state_dev; synchronizes `stream`. */
+stc_status stc_rht_state_init(int32_t d, const int8_t* signs, const float* codebook,
+                              stc_head_info* info, void* state_dev, stc_stream_t stream);
+
+/* Calibrate one stream: second moment of the first n_calib tokens of x_dev
+ * ([n][ld] of dtype, row t at x_dev + t*ld elements) computed on the GPU in
+ * fp64, eigendecomposition on the host (EIGEN) or its diagonal (IDENTITY),
+ * water-filling of floor(avg_bits*d+0.5) bits unless `bits` (host, d widths)
+ * is given, then as stc_state_init. Synchronizes `stream`. */
+stc_status stc_calibrate_head(int32_t d, int64_t n_calib, const void* x_dev, int32_t dtype,
+                              int64_t ld, float avg_bits, const uint8_t* bits, int32_t xform,
+                              stc_head_info* info, void* state_dev, stc_stream_t stream);
+
+/* Read back a state's basis as fp32, row-major d*d (u[i*d+j] = U_ij).
+ * Synchronizes `stream`. */
+stc_status stc_state_basis(const void* state_dev, float* u_out, stc_stream_t stream);
+
+/* ---------------------------------------------------------- codec
+ * Batched layout: stream s uses state (state_of_stream_dev ? map[s] : s) of
+ * the states array; its tokens are x_dev + s*x_stream_stride (elements), row t
+ * at + t*ld; its packed bytes are packed_dev + s*packed_stream_stride; its
+ * norms (Walsh-Hadamard states only) norms_dev + s*n_tokens. All streams of a
+ * call have n_tokens tokens and use states of one family (all EIGEN/IDENTITY,
+ * or all RHT). infos[n_states] are the host summaries of the states, used for
+ * validation (packed_stream_stride must hold the largest stream).
+ * x rows must be 16-byte aligned (ld*elem and x_stream_stride*elem multiples
+ * of 16); packed_stream_stride a multiple of 16.                         */
+
+stc_status stc_encode_kv_batched(const void* states_dev, int64_t n_states,
+                                 const int32_t* state_of_stream_dev, const stc_head_info* infos,
+                                 int64_t n_streams, int64_t n_tokens, const void* x_dev,
+                                 int32_t dtype, int64_t ld, int64_t x_stream_stride,
+                                 void* packed_dev, int64_t packed_stream_stride,
+                                 float* norms_dev, stc_stream_t stream);
+
+stc_status stc_decode_kv_batched(const void* states_dev, int64_t n_states,
+                                 const int32_t* state_of_stream_dev, const stc_head_info* infos,
+                                 int64_t n_streams, int64_t n_tokens, const void* packed_dev,
+                                 int64_t packed_stream_stride, const float* norms_dev,
+                                 void* x_out_dev, int32_t dtype, int64_t ld,
+                                 int64_t x_stream_stride, stc_stream_t stream);
+
+/* One stream. */
+stc_status stc_encode_kv(const stc_head_info* info, const void* state_dev, int64_t n_tokens,
+                         const void* x_dev, int32_t dtype, int64_t ld, void* packed_dev,
+                         float* norms_dev, stc_stream_t stream);
+stc_status stc_decode_kv(const stc_head_info* info, const void* state_dev, int64_t n_tokens,
+                         const void* packed_dev, const float* norms_dev, void* x_out_dev,
+                         int32_t dtype, int64_t ld, stc_stream_t stream);
+
+/* Quantize and pack given latent coefficients (fp32 [n][128], row stride
+ * 128) with an EIGEN/IDENTITY state: the encode path without the
+ * projection. For bit-exact checks of the quantizer and the format. */
+stc_status stc_quantize_pack_f32(const stc_head_info* info, const void* state_dev, int64_t n_tokens,
+                                 const float* coeffs_dev, void* packed_dev, stc_stream_t stream);
+
+/* ------------------------------------------------------ attention
+ * One decode step for n_pairs KV heads (pair p: K stream with state
+ * k_state_of_pair[p] and bytes k_packed_dev + p*packed_pair_stride, V stream
+ * likewise), each shared by `group` query heads (1..16):
+ *   out[p][h][:] = sum_t softmax_t(scale * q[p][h] . K_hat_t) V_hat_t
+ * over all n_tokens cached tokens, with K_hat/V_hat the exact reconstructions
+ * of the packed codes (never materialised: scores are taken in the latent
+ * basis and the weighted code average is rotated back once). q_dev, out_dev:
+ * fp32 [n_pairs][group][128]. EIGEN/IDENTITY states only. ws_dev: at least
+ * stc_attend_workspace_bytes(n_pairs, group, n_tokens) bytes, 256-aligned. */
+stc_status stc_attend_compressed_batched(const void* states_dev, int64_t n_states,
+                                         const int32_t* k_state_of_pair_dev,
+                                         const int32_t* v_state_of_pair_dev,
+                                         const stc_head_info* infos, int64_t n_pairs,
+                                         int64_t n_tokens, const void* k_packed_dev,
+                                         const void* v_packed_dev, int64_t packed_pair_stride,
+                                         int32_t group, const float* q_dev, float* out_dev,
+                                         float scale, void* ws_dev, size_t ws_bytes,
+                                         stc_stream_t stream);
+
+/* One KV head. */
+stc_status stc_attend_compressed(const stc_head_info* k_info, const void* k_state_dev,
+                                 const stc_head_info* v_info, const void* v_state_dev,
+                                 int64_t n_tokens, const void* k_packed_dev,
+                                 const void* v_packed_dev, int32_t group, const float* q_dev,
+                                 float* out_dev, float scale, void* ws_dev, size_t ws_bytes,
+                                 stc_stream_t stream);
+
+/* ------------------------------------------------------ diagnostics */
+const char* stc_status_str(stc_status s);
+/* Message of the last error on the calling thread ("" if none). */
+const char* stc_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* STC_H */

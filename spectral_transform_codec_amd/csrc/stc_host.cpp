@@ -1,0 +1,685 @@
+// Host side of libstc: argument validation, the calibration math that runs on
+// the CPU (eigendecomposition, water-filling, quantizer steps, Lloyd-Max), the
+// construction of device state blobs, and the C ABI entry points.
+//
+// Sources, by page title and section (the pages are web summaries):
+//  - "Sintesi Tecnica: SPECTRA" (gist.science), "Metodologia: SPECTRA"
+//    observations 1-3 and "La Pipeline di SPECTRA" steps 1-3.
+//  - "Technisch Overzicht: Ablatie, Statistische Inferentie en Validatie voor
+//    KV-Cache Compressie" (gist.science), "Experimentele Opstelling".
+// The readings taken where the pages are silent are listed in include/stc.h.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <limits>
+#include <numeric>
+#include <string>
+#include <vector>
+
+#include "stc_internal.h"
+
+using namespace stc;
+
+namespace {
+
+thread_local std::string g_err;
+
+stc_status fail(stc_status code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+stc_status ok() {
+  g_err.clear();
+  return STC_OK;
+}
+
+stc_status hip_check(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(STC_EDEVICE, "%s: %s", what, hipGetErrorString(e));
+  return STC_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// ------------------------------------------------------------ bf16 helpers
+uint16_t bf16_bits_rne(float f) {
+  uint32_t u;
+  std::memcpy(&u, &f, 4);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);  // NaN stays NaN
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+double bf16_value(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  std::memcpy(&f, &u, 4);
+  return (double)f;
+}
+// hi + lo split of a double into two bf16 values (hi = RNE(v), lo = RNE(v - hi)).
+void split_bf16(double v, uint16_t* hi, uint16_t* lo) {
+  *hi = bf16_bits_rne((float)v);
+  *lo = bf16_bits_rne((float)(v - bf16_value(*hi)));
+}
+
+// ------------------------------------------------ MSE-optimal uniform step
+// Slope of the MSE of the 2^b-level midrise uniform quantizer with step
+// delta on N(0,1). By symmetry only the cells of the non-negative half are
+// summed: cell i = [i delta, (i+1) delta) (the last one open) with level
+// (i + 1/2) delta. The moving cell edges contribute nothing because each edge
+// is the midpoint of its two levels, so the slope is
+//   -4 sum_i m_i ( int_cell x phi(x) dx - m_i delta P(cell) ),  m_i = i + 1/2.
+double mse_slope(double delta, int levels) {
+  const double inv_sqrt2pi = 0.39894228040143267794;
+  const int half = levels / 2;
+  double acc = 0.0;
+  for (int i = 0; i < half; ++i) {
+    const double a = i * delta;
+    const bool last = (i == half - 1);
+    const double b = last ? 0.0 : (i + 1) * delta;
+    const double phia = inv_sqrt2pi * std::exp(-0.5 * a * a);
+    const double phib = last ? 0.0 : inv_sqrt2pi * std::exp(-0.5 * b * b);
+    const double qa = 0.5 * std::erfc(a / std::sqrt(2.0));
+    const double qb = last ? 0.0 : 0.5 * std::erfc(b / std::sqrt(2.0));
+    const double m = i + 0.5;
+    acc += m * ((phia - phib) - m * delta * (qa - qb));
+  }
+  return -4.0 * acc;
+}
+
+double delta_star_impl(int bits) {
+  const int levels = 1 << bits;
+  double lo = 1e-6, hi = 4.0;  // slope < 0 at lo, > 0 at hi for every b in 1..8
+  for (int it = 0; it < 400; ++it) {
+    const double mid = 0.5 * (lo + hi);
+    if (mid <= lo || mid >= hi) break;
+    if (mse_slope(mid, levels) < 0.0) lo = mid; else hi = mid;
+  }
+  return 0.5 * (lo + hi);
+}
+
+// --------------------------------------------------------- cyclic Jacobi
+// Golub & Van Loan, cyclic Jacobi: sweep over all (p, q), p < q, annihilating
+// a_pq with the rotation from the symmetric 2x2 Schur decomposition, until a
+// sweep finds every off-diagonal entry negligible next to its diagonal pair.
+void jacobi_eigh(int n, std::vector<double>& a, std::vector<double>& v) {
+  v.assign((size_t)n * n, 0.0);
+  for (int i = 0; i < n; ++i) v[(size_t)i * n + i] = 1.0;
+  for (int sweep = 0; sweep < 60; ++sweep) {
+    bool rotated = false;
+    for (int p = 0; p < n - 1; ++p) {
+      for (int q = p + 1; q < n; ++q) {
+        const double apq = a[(size_t)p * n + q];
+        const double app = a[(size_t)p * n + p];
+        const double aqq = a[(size_t)q * n + q];
+        if (apq == 0.0) continue;
+        const double g = 100.0 * std::fabs(apq);
+        if (sweep > 3 && std::fabs(app) + g == std::fabs(app) && std::fabs(aqq) + g == std::fabs(aqq)) {
+          a[(size_t)p * n + q] = a[(size_t)q * n + p] = 0.0;
+          continue;
+        }
+        rotated = true;
+        const double theta = (aqq - app) / (2.0 * apq);
+        double t;
+        if (std::fabs(theta) > 1e150) {
+          t = 0.5 / theta;
+        } else {
+          t = (theta >= 0.0 ? 1.0 : -1.0) / (std::fabs(theta) + std::sqrt(theta * theta + 1.0));
+        }
+        const double c = 1.0 / std::sqrt(t * t + 1.0);
+        const double s = t * c;
+        for (int k = 0; k < n; ++k) {  // columns p, q
+          const double akp = a[(size_t)k * n + p], akq = a[(size_t)k * n + q];
+          a[(size_t)k * n + p] = c * akp - s * akq;
+          a[(size_t)k * n + q] = s * akp + c * akq;
+        }
+        for (int k = 0; k < n; ++k) {  // rows p, q
+          const double apk = a[(size_t)p * n + k], aqk = a[(size_t)q * n + k];
+          a[(size_t)p * n + k] = c * apk - s * aqk;
+          a[(size_t)q * n + k] = s * apk + c * aqk;
+        }
+        a[(size_t)p * n + q] = a[(size_t)q * n + p] = 0.0;
+        for (int k = 0; k < n; ++k) {
+          const double vkp = v[(size_t)k * n + p], vkq = v[(size_t)k * n + q];
+          v[(size_t)k * n + p] = c * vkp - s * vkq;
+          v[(size_t)k * n + q] = s * vkp + c * vkq;
+        }
+      }
+    }
+    if (!rotated) break;
+  }
+}
+
+// Sort eigenpairs by descending eigenvalue (stable), then make the
+// largest-magnitude entry of every column positive (lowest row on a tie).
+void sort_and_fix_signs(int n, const std::vector<double>& diag, const std::vector<double>& v,
+                        double* u_out, double* lam_out) {
+  std::vector<int> order(n);
+  std::iota(order.begin(), order.end(), 0);
+  std::stable_sort(order.begin(), order.end(), [&](int x, int y) { return diag[x] > diag[y]; });
+  for (int j = 0; j < n; ++j) {
+    const int src = order[j];
+    lam_out[j] = diag[src];
+    int kmax = 0;
+    double vmax = -1.0;
+    for (int i = 0; i < n; ++i) {
+      const double m = std::fabs(v[(size_t)i * n + src]);
+      if (m > vmax) { vmax = m; kmax = i; }
+    }
+    const double sgn = v[(size_t)kmax * n + src] < 0.0 ? -1.0 : 1.0;
+    for (int i = 0; i < n; ++i) u_out[(size_t)i * n + j] = sgn * v[(size_t)i * n + src];
+  }
+}
+
+// ------------------------------------------------------ state construction
+stc_status build_eigen_blob(int d, int xform, const double* u, const double* lambda,
+                            const uint8_t* bits, const double* steps_in, stc_head_info* info,
+                            std::vector<unsigned char>& blob) {
+  blob.assign(STATE_BYTES, 0);
+  DevHdr* h = reinterpret_cast<DevHdr*>(blob.data() + OFF_HDR);
+  float* u32 = reinterpret_cast<float*>(blob.data() + OFF_U32);
+  uint16_t* ut_hi = reinterpret_cast<uint16_t*>(blob.data() + OFF_UT_HI);
+  uint16_t* ut_lo = reinterpret_cast<uint16_t*>(blob.data() + OFF_UT_LO);
+  uint16_t* w_hi = reinterpret_cast<uint16_t*>(blob.data() + OFF_W_HI);
+  uint16_t* w_lo = reinterpret_cast<uint16_t*>(blob.data() + OFF_W_LO);
+  float* thr = reinterpret_cast<float*>(blob.data() + OFF_THR);
+
+  std::vector<double> ud((size_t)d * d, 0.0);
+  if (xform == STC_XFORM_IDENTITY) {
+    for (int i = 0; i < d; ++i) ud[(size_t)i * d + i] = 1.0;
+  } else {
+    for (size_t k = 0; k < (size_t)d * d; ++k) ud[k] = u[k];
+  }
+  double steps[D];
+  int total = 0, n_kept = 0, last = -1, nthr = 0;
+  for (int j = 0; j < d; ++j) {
+    const int b = bits[j];
+    total += b;
+    if (b > 0) { ++n_kept; last = j; }
+    if (b == 0) steps[j] = 0.0;
+    else if (steps_in) steps[j] = steps_in[j];
+    else steps[j] = std::sqrt(std::max(lambda[j], 0.0)) * delta_star_impl(b);
+  }
+  h->xform = xform;
+  h->total_bits = total;
+  h->n_kept = n_kept;
+  h->nmax16 = last < 0 ? 0 : 16 * ((last + 16) / 16);
+  h->kmax32 = last < 0 ? 0 : 32 * ((last + 32) / 32);
+  int off = 0;
+  for (int j = 0; j < d; ++j) {
+    const int b = bits[j];
+    h->bits[j] = (uint8_t)b;
+    h->off[j] = (uint16_t)off;
+    off += b;
+    if (b > 0) {
+      const int L = 1 << b;
+      h->inv_step[j] = steps[j] > 0.0 ? (float)(1.0 / steps[j]) : 0.0f;
+      h->ybias[j] = (float)(L / 2) + QEPS;
+      h->lm1[j] = L - 1;
+      h->thr_base[j] = nthr;
+      for (int k = 1; k < L; ++k) thr[nthr++] = (float)(((double)k - (double)(L / 2)) * steps[j]);
+      h->step32[j] = (float)steps[j];
+      h->halfspan[j] = 0.5f * (float)(L - 1);
+    } else {
+      h->inv_step[j] = 0.0f;
+      h->ybias[j] = 0.5f;
+      h->lm1[j] = 0;
+      h->thr_base[j] = 0;
+      h->step32[j] = 0.0f;
+      h->halfspan[j] = 0.0f;
+    }
+  }
+  for (int i = 0; i < d; ++i) {
+    double bias = 0.0;
+    for (int j = 0; j < d; ++j) {
+      const double uij = ud[(size_t)i * d + j];
+      u32[i * D + j] = (float)uij;
+      split_bf16(uij, &ut_hi[j * D + i], &ut_lo[j * D + i]);
+      if (bits[j] > 0) bias += uij * steps[j] * 0.5 * (double)((1 << bits[j]) - 1);
+    }
+    h->bias[i] = (float)bias;
+  }
+  for (int R = 0; R < D; ++R) {
+    const int i = w_row_dim(R);
+    for (int j = 0; j < d; ++j) split_bf16(ud[(size_t)i * d + j] * steps[j], &w_hi[R * D + j], &w_lo[R * D + j]);
+  }
+  if (info) {
+    info->d = d;
+    info->xform = xform;
+    info->total_bits = total;
+    info->n_kept = n_kept;
+    for (int j = 0; j < d; ++j) {
+      info->bits[j] = bits[j];
+      info->lambda[j] = lambda ? lambda[j] : 0.0;
+      info->steps[j] = steps[j];
+    }
+  }
+  return STC_OK;
+}
+
+stc_status upload(const std::vector<unsigned char>& blob, void* state_dev, stc_stream_t stream) {
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  stc_status st = hip_check(hipMemcpyAsync(state_dev, blob.data(), blob.size(), hipMemcpyHostToDevice, s),
+                            "state upload");
+  if (st) return st;
+  return hip_check(hipStreamSynchronize(s), "state upload sync");
+}
+
+stc_status check_state_ptr(const void* p, const char* name) {
+  if (!p) return fail(STC_EINVAL, "%s is NULL", name);
+  if (!aligned(p, 256)) return fail(STC_EINVAL, "%s must be 256-byte aligned", name);
+  return STC_OK;
+}
+
+int elem_size(int32_t dtype) { return dtype == STC_F32 ? 4 : 2; }
+
+}  // namespace
+
+extern "C" {
+
+const char* stc_status_str(stc_status s) {
+  switch (s) {
+    case STC_OK: return "ok";
+    case STC_EINVAL: return "invalid argument";
+    case STC_EUNSUPPORTED: return "unsupported";
+    case STC_EBUDGET: return "bit budget";
+    case STC_EWORKSPACE: return "workspace too small";
+    case STC_EDEVICE: return "device error";
+    default: return "unknown status";
+  }
+}
+
+const char* stc_last_error(void) { return g_err.c_str(); }
+
+size_t stc_state_bytes(void) { return STATE_BYTES; }
+
+size_t stc_packed_bytes(int32_t total_bits, int64_t n_tokens) {
+  if (total_bits < 0 || n_tokens < 0) return 0;
+  return packed_bytes(total_bits, n_tokens);
+}
+
+size_t stc_attend_workspace_bytes(int64_t n_pairs, int32_t group, int64_t n_tokens) {
+  if (n_pairs <= 0 || n_tokens <= 0 || group <= 0) return 256;
+  const int64_t splits = att_n_splits(n_pairs, n_tokens);
+  size_t q = (size_t)n_pairs * ATT_QTAB_BYTES;
+  size_t parts = (size_t)n_pairs * splits * group * ATT_PART_FLOATS * sizeof(float);
+  return (q + parts + 255) / 256 * 256;
+}
+
+int32_t stc_total_bits(float avg_bits, int32_t d) {
+  return (int32_t)std::floor((double)avg_bits * d + 0.5);
+}
+
+double stc_delta_star(int32_t bits) {
+  if (bits < 1 || bits > STC_MAX_BITS) return std::numeric_limits<double>::quiet_NaN();
+  static double cache[STC_MAX_BITS + 1] = {0};
+  if (cache[bits] == 0.0) cache[bits] = delta_star_impl(bits);
+  return cache[bits];
+}
+
+stc_status stc_water_fill(int32_t d, const double* lambda, int32_t total_bits, uint8_t* bits_out) {
+  if (d <= 0 || !lambda || !bits_out) return fail(STC_EINVAL, "water_fill: bad arguments");
+  if (total_bits < 0 || total_bits > STC_MAX_BITS * d)
+    return fail(STC_EBUDGET, "water_fill: budget %d outside [0, %d]", total_bits, STC_MAX_BITS * d);
+  std::vector<int> b(d, 0);
+  for (int it = 0; it < total_bits; ++it) {
+    int best = -1;
+    double bestv = -1.0;
+    for (int j = 0; j < d; ++j) {
+      if (b[j] >= STC_MAX_BITS) continue;
+      const double lam = lambda[j] > 0.0 ? lambda[j] : 0.0;
+      const double g = std::ldexp(lam, -2 * b[j]);
+      if (g > bestv) { bestv = g; best = j; }
+    }
+    b[best] += 1;
+  }
+  for (int j = 0; j < d; ++j) bits_out[j] = (uint8_t)b[j];
+  return ok();
+}
+
+stc_status stc_eigh(int32_t d, const double* a, double* u_out, double* lambda_out) {
+  if (d <= 0 || !a || !u_out || !lambda_out) return fail(STC_EINVAL, "eigh: bad arguments");
+  std::vector<double> m(a, a + (size_t)d * d), v;
+  // symmetrize exactly (the input is symmetric up to rounding at most)
+  for (int i = 0; i < d; ++i)
+    for (int j = i + 1; j < d; ++j) m[(size_t)j * d + i] = m[(size_t)i * d + j];
+  jacobi_eigh(d, m, v);
+  std::vector<double> diag(d);
+  for (int i = 0; i < d; ++i) diag[i] = m[(size_t)i * d + i];
+  sort_and_fix_signs(d, diag, v, u_out, lambda_out);
+  return ok();
+}
+
+stc_status stc_lloyd_max(const double* samples, int64_t n, int32_t levels, double tol, int32_t max_iter,
+                         double* centroids_out, int32_t* iters_out) {
+  if (!samples || n < 2 || levels < 2 || !centroids_out) return fail(STC_EINVAL, "lloyd_max: bad arguments");
+  std::vector<double> y(samples, samples + n);
+  std::sort(y.begin(), y.end());
+  std::vector<long double> pre((size_t)n + 1, 0.0L);
+  for (int64_t i = 0; i < n; ++i) pre[i + 1] = pre[i] + (long double)y[i];
+  std::vector<double> c(levels), nc(levels), t(levels - 1);
+  for (int k = 0; k < levels; ++k) {  // sample quantile (k + 1/2)/levels, linear interpolation
+    const double p = (k + 0.5) / levels;
+    const double hpos = (double)(n - 1) * p;
+    const int64_t lo = (int64_t)std::floor(hpos);
+    const double frac = hpos - (double)lo;
+    const double a = y[lo], b = y[std::min<int64_t>(lo + 1, n - 1)];
+    c[k] = frac >= 0.5 ? b - (b - a) * (1.0 - frac) : a + (b - a) * frac;
+  }
+  int it = 0;
+  for (it = 1; it <= max_iter; ++it) {
+    for (int k = 0; k < levels - 1; ++k) t[k] = 0.5 * (c[k] + c[k + 1]);
+    int64_t start = 0;
+    double moved = 0.0;
+    for (int k = 0; k < levels; ++k) {
+      const int64_t end = (k == levels - 1) ? n : (int64_t)(std::lower_bound(y.begin(), y.end(), t[k]) - y.begin());
+      const int64_t cnt = end - start;
+      nc[k] = cnt > 0 ? (double)((pre[end] - pre[start]) / (long double)cnt) : c[k];
+      moved = std::max(moved, std::fabs(nc[k] - c[k]));
+      start = end;
+    }
+    c = nc;
+    if (moved < tol) break;
+  }
+  for (int k = 0; k < levels; ++k) centroids_out[k] = c[k];
+  if (iters_out) *iters_out = std::min(it, max_iter);
+  return ok();
+}
+
+stc_status stc_state_init(int32_t d, int32_t xform, const double* u, const double* lambda,
+                          const uint8_t* bits, const double* steps, stc_head_info* info,
+                          void* state_dev, stc_stream_t stream) {
+  if (d != D) return fail(STC_EUNSUPPORTED, "state_init: d=%d (only %d is supported)", d, D);
+  if (xform != STC_XFORM_EIGEN && xform != STC_XFORM_IDENTITY)
+    return fail(STC_EUNSUPPORTED, "state_init: xform %d", xform);
+  if (xform == STC_XFORM_EIGEN && !u) return fail(STC_EINVAL, "state_init: EIGEN needs a basis");
+  if (xform == STC_XFORM_IDENTITY && u) return fail(STC_EINVAL, "state_init: IDENTITY takes no basis");
+  if (!lambda || !bits || !info) return fail(STC_EINVAL, "state_init: NULL lambda/bits/info");
+  if (stc_status s = check_state_ptr(state_dev, "state_dev")) return s;
+  for (int j = 0; j < d; ++j)
+    if (bits[j] > STC_MAX_BITS) return fail(STC_EBUDGET, "state_init: width %d > 8 at channel %d", bits[j], j);
+  if (steps)
+    for (int j = 0; j < d; ++j)
+      if (bits[j] && !(steps[j] >= 0.0 && std::isfinite(steps[j])))
+        return fail(STC_EINVAL, "state_init: bad step at channel %d", j);
+  std::vector<unsigned char> blob;
+  build_eigen_blob(d, xform, u, lambda, bits, steps, info, blob);
+  if (stc_status s = upload(blob, state_dev, stream)) return s;
+  return ok();
+}
+
+stc_status stc_rht_state_init(int32_t d, const int8_t* signs, const float* codebook, stc_head_info* info,
+                              void* state_dev, stc_stream_t stream) {
+  if (d != D) return fail(STC_EUNSUPPORTED, "rht_state_init: d=%d (only %d is supported)", d, D);
+  if (!signs || !codebook || !info) return fail(STC_EINVAL, "rht_state_init: NULL argument");
+  if (stc_status s = check_state_ptr(state_dev, "state_dev")) return s;
+  for (int i = 0; i < d; ++i)
+    if (signs[i] != 1 && signs[i] != -1) return fail(STC_EINVAL, "rht_state_init: sign %d is not +-1", i);
+  for (int k = 0; k < 8; ++k)
+    if (!std::isfinite(codebook[k]) || (k && !(codebook[k] > codebook[k - 1])))
+      return fail(STC_EINVAL, "rht_state_init: codebook must be finite and increasing");
+  std::vector<unsigned char> blob(STATE_BYTES, 0);
+  DevHdr* h = reinterpret_cast<DevHdr*>(blob.data());
+  h->xform = STC_XFORM_RHT;
+  h->total_bits = STC_RHT_BITS * d;
+  h->n_kept = d;
+  h->nmax16 = d;
+  h->kmax32 = d;
+  for (int j = 0; j < d; ++j) {
+    h->bits[j] = STC_RHT_BITS;
+    h->off[j] = (uint16_t)(STC_RHT_BITS * j);
+    h->sign[j] = (float)signs[j];
+  }
+  for (int k = 0; k < 8; ++k) h->cb[k] = codebook[k];
+  for (int k = 0; k < 7; ++k) h->cb_thr[k] = (float)(0.5 * ((double)codebook[k] + (double)codebook[k + 1]));
+  info->d = d;
+  info->xform = STC_XFORM_RHT;
+  info->total_bits = h->total_bits;
+  info->n_kept = d;
+  for (int j = 0; j < d; ++j) {
+    info->bits[j] = STC_RHT_BITS;
+    info->lambda[j] = 0.0;
+    info->steps[j] = 0.0;
+  }
+  if (stc_status s = upload(blob, state_dev, stream)) return s;
+  return ok();
+}
+
+stc_status stc_calibrate_head(int32_t d, int64_t n_calib, const void* x_dev, int32_t dtype, int64_t ld,
+                              float avg_bits, const uint8_t* bits, int32_t xform, stc_head_info* info,
+                              void* state_dev, stc_stream_t stream) {
+  if (d != D) return fail(STC_EUNSUPPORTED, "calibrate_head: d=%d (only %d is supported)", d, D);
+  if (xform != STC_XFORM_EIGEN && xform != STC_XFORM_IDENTITY)
+    return fail(STC_EUNSUPPORTED, "calibrate_head: xform %d (use stc_rht_state_init for RHT)", xform);
+  if (dtype != STC_F32 && dtype != STC_BF16) return fail(STC_EUNSUPPORTED, "calibrate_head: dtype %d", dtype);
+  if (!x_dev || !info) return fail(STC_EINVAL, "calibrate_head: NULL argument");
+  if (n_calib <= 0) return fail(STC_EINVAL, "calibrate_head: n_calib must be positive");
+  if (ld < d) return fail(STC_EINVAL, "calibrate_head: ld < d");
+  if (!aligned(x_dev, 16) || (ld * elem_size(dtype)) % 16) return fail(STC_EINVAL, "calibrate_head: x rows must be 16-byte aligned");
+  if (stc_status s = check_state_ptr(state_dev, "state_dev")) return s;
+  if (!(avg_bits >= 0.0f) || !std::isfinite(avg_bits)) return fail(STC_EBUDGET, "calibrate_head: bad budget");
+  const int32_t budget = stc_total_bits(avg_bits, d);
+  if (budget > STC_MAX_BITS * d) return fail(STC_EBUDGET, "calibrate_head: budget %d > %d", budget, STC_MAX_BITS * d);
+  if (bits) {
+    int sum = 0;
+    for (int j = 0; j < d; ++j) {
+      if (bits[j] > STC_MAX_BITS) return fail(STC_EBUDGET, "calibrate_head: width > 8 at channel %d", j);
+      sum += bits[j];
+    }
+    if (sum != budget) return fail(STC_EBUDGET, "calibrate_head: widths sum to %d, budget is %d", sum, budget);
+  }
+  // second moment on the GPU (fp64), into the state's scratch region
+  double* gram_dev = reinterpret_cast<double*>(static_cast<unsigned char*>(state_dev) + OFF_GRAM);
+  if (launch_gram(x_dev, dtype, ld, n_calib, gram_dev, stream)) return fail(STC_EDEVICE, "gram launch: %s", hipGetErrorString(hipGetLastError()));
+  std::vector<double> g((size_t)d * d);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (stc_status st = hip_check(hipMemcpyAsync(g.data(), gram_dev, g.size() * sizeof(double), hipMemcpyDeviceToHost, s), "gram download")) return st;
+  if (stc_status st = hip_check(hipStreamSynchronize(s), "gram sync")) return st;
+  std::vector<double> u((size_t)d * d), lam(d);
+  if (xform == STC_XFORM_EIGEN) {
+    stc_eigh(d, g.data(), u.data(), lam.data());
+  } else {
+    for (int j = 0; j < d; ++j) lam[j] = g[(size_t)j * d + j];
+  }
+  std::vector<uint8_t> b(d);
+  if (bits) std::copy(bits, bits + d, b.begin());
+  else if (stc_status st = stc_water_fill(d, lam.data(), budget, b.data())) return st;
+  std::vector<unsigned char> blob;
+  build_eigen_blob(d, xform, xform == STC_XFORM_EIGEN ? u.data() : nullptr, lam.data(), b.data(), nullptr, info, blob);
+  // keep the second moment in the blob's scratch region
+  std::memcpy(blob.data() + OFF_GRAM, g.data(), g.size() * sizeof(double));
+  if (stc_status st = upload(blob, state_dev, stream)) return st;
+  return ok();
+}
+
+stc_status stc_state_basis(const void* state_dev, float* u_out, stc_stream_t stream) {
+  if (stc_status s = check_state_ptr(state_dev, "state_dev")) return s;
+  if (!u_out) return fail(STC_EINVAL, "state_basis: NULL output");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (stc_status st = hip_check(hipMemcpyAsync(u_out, static_cast<const unsigned char*>(state_dev) + OFF_U32,
+                                               (size_t)D * D * sizeof(float), hipMemcpyDeviceToHost, s), "basis download")) return st;
+  if (stc_status st = hip_check(hipStreamSynchronize(s), "basis sync")) return st;
+  return ok();
+}
+
+// ------------------------------------------------------------- codec calls
+static stc_status check_batch(const char* who, const void* states_dev, int64_t n_states,
+                              const stc_head_info* infos, int64_t n_streams, int64_t n_tokens,
+                              int64_t packed_stride, bool* is_rht, int* max_bits) {
+  if (stc_status s = check_state_ptr(states_dev, "states_dev")) return s;
+  if (!infos) return fail(STC_EINVAL, "%s: NULL infos", who);
+  if (n_states <= 0 || n_streams <= 0) return fail(STC_EINVAL, "%s: need at least one state and stream", who);
+  if (n_tokens < 0) return fail(STC_EINVAL, "%s: negative token count", who);
+  if (n_tokens > (int64_t)1 << 31) return fail(STC_EINVAL, "%s: more than 2^31 tokens per stream", who);
+  int mb = 0;
+  bool rht = infos[0].xform == STC_XFORM_RHT;
+  for (int64_t i = 0; i < n_states; ++i) {
+    const stc_head_info& f = infos[i];
+    if (f.d != D) return fail(STC_EUNSUPPORTED, "%s: state %lld has d=%d", who, (long long)i, f.d);
+    if ((f.xform == STC_XFORM_RHT) != rht) return fail(STC_EINVAL, "%s: states mix RHT and eigen families", who);
+    if (f.xform < 0 || f.xform > 2) return fail(STC_EUNSUPPORTED, "%s: xform %d", who, f.xform);
+    if (f.total_bits < 0 || f.total_bits > STC_MAX_BITS * D) return fail(STC_EBUDGET, "%s: total_bits %d", who, f.total_bits);
+    mb = std::max(mb, f.total_bits);
+  }
+  if (packed_stride % 16) return fail(STC_EINVAL, "%s: packed stride must be a multiple of 16", who);
+  if (n_streams > 1 && (size_t)packed_stride < packed_bytes(mb, n_tokens))
+    return fail(STC_EINVAL, "%s: packed stride %lld < %zu bytes", who, (long long)packed_stride, packed_bytes(mb, n_tokens));
+  *is_rht = rht;
+  *max_bits = mb;
+  return STC_OK;
+}
+
+stc_status stc_encode_kv_batched(const void* states_dev, int64_t n_states, const int32_t* map,
+                                 const stc_head_info* infos, int64_t n_streams, int64_t n_tokens,
+                                 const void* x_dev, int32_t dtype, int64_t ld, int64_t x_stream_stride,
+                                 void* packed_dev, int64_t packed_stream_stride, float* norms_dev,
+                                 stc_stream_t stream) {
+  bool rht = false;
+  int mb = 0;
+  if (stc_status s = check_batch("encode_kv", states_dev, n_states, infos, n_streams, n_tokens,
+                                 packed_stream_stride, &rht, &mb)) return s;
+  if (dtype != STC_F32 && dtype != STC_BF16) return fail(STC_EUNSUPPORTED, "encode_kv: dtype %d", dtype);
+  if (rht && dtype != STC_BF16) return fail(STC_EUNSUPPORTED, "encode_kv: the RHT path takes bf16 tokens");
+  if (n_tokens == 0) return ok();
+  if (!x_dev || !packed_dev) return fail(STC_EINVAL, "encode_kv: NULL buffer");
+  if (rht && !norms_dev) return fail(STC_EINVAL, "encode_kv: RHT states need a norms buffer");
+  const int es = elem_size(dtype);
+  if (ld < D || !aligned(x_dev, 16) || (ld * es) % 16 || (x_stream_stride * es) % 16)
+    return fail(STC_EINVAL, "encode_kv: x rows must be >= 128 elements and 16-byte aligned");
+  if (n_streams > 1 && x_stream_stride < (n_tokens - 1) * ld + D)
+    return fail(STC_EINVAL, "encode_kv: x stream stride too small");
+  if (!aligned(packed_dev, 16)) return fail(STC_EINVAL, "encode_kv: packed buffer must be 16-byte aligned");
+  if (rht && !aligned(norms_dev, 4)) return fail(STC_EINVAL, "encode_kv: norms misaligned");
+  EncodeLaunch a{static_cast<const unsigned char*>(states_dev), map, n_states, n_streams, n_tokens, ld,
+                 x_stream_stride, packed_stream_stride, x_dev, static_cast<unsigned char*>(packed_dev), norms_dev,
+                 dtype == STC_F32 ? 1 : 0, mb};
+  const int rc = rht ? launch_encode_rht(a, stream) : launch_encode_eigen(a, stream);
+  if (rc) return fail(STC_EDEVICE, "encode_kv launch: %s", hipGetErrorString(hipGetLastError()));
+  return ok();
+}
+
+stc_status stc_decode_kv_batched(const void* states_dev, int64_t n_states, const int32_t* map,
+                                 const stc_head_info* infos, int64_t n_streams, int64_t n_tokens,
+                                 const void* packed_dev, int64_t packed_stream_stride, const float* norms_dev,
+                                 void* x_out_dev, int32_t dtype, int64_t ld, int64_t x_stream_stride,
+                                 stc_stream_t stream) {
+  bool rht = false;
+  int mb = 0;
+  if (stc_status s = check_batch("decode_kv", states_dev, n_states, infos, n_streams, n_tokens,
+                                 packed_stream_stride, &rht, &mb)) return s;
+  if (dtype != STC_F32 && dtype != STC_BF16) return fail(STC_EUNSUPPORTED, "decode_kv: dtype %d", dtype);
+  if (n_tokens == 0) return ok();
+  if (!x_out_dev || !packed_dev) return fail(STC_EINVAL, "decode_kv: NULL buffer");
+  if (rht && !norms_dev) return fail(STC_EINVAL, "decode_kv: RHT states need the norms");
+  const int es = elem_size(dtype);
+  if (ld < D || !aligned(x_out_dev, 16) || (ld * es) % 16 || (x_stream_stride * es) % 16)
+    return fail(STC_EINVAL, "decode_kv: output rows must be >= 128 elements and 16-byte aligned");
+  if (n_streams > 1 && x_stream_stride < (n_tokens - 1) * ld + D)
+    return fail(STC_EINVAL, "decode_kv: output stream stride too small");
+  if (!aligned(packed_dev, 16)) return fail(STC_EINVAL, "decode_kv: packed buffer must be 16-byte aligned");
+  DecodeLaunch a{static_cast<const unsigned char*>(states_dev), map, n_states, n_streams, n_tokens, ld,
+                 x_stream_stride, packed_stream_stride, static_cast<const unsigned char*>(packed_dev), norms_dev,
+                 x_out_dev, dtype == STC_F32 ? 1 : 0, mb};
+  const int rc = rht ? launch_decode_rht(a, stream) : launch_decode_eigen(a, stream);
+  if (rc) return fail(STC_EDEVICE, "decode_kv launch: %s", hipGetErrorString(hipGetLastError()));
+  return ok();
+}
+
+stc_status stc_encode_kv(const stc_head_info* info, const void* state_dev, int64_t n_tokens, const void* x_dev,
+                         int32_t dtype, int64_t ld, void* packed_dev, float* norms_dev, stc_stream_t stream) {
+  return stc_encode_kv_batched(state_dev, 1, nullptr, info, 1, n_tokens, x_dev, dtype, ld, 0, packed_dev,
+                               (int64_t)packed_bytes(info ? info->total_bits : 0, n_tokens), norms_dev, stream);
+}
+
+stc_status stc_decode_kv(const stc_head_info* info, const void* state_dev, int64_t n_tokens, const void* packed_dev,
+                         const float* norms_dev, void* x_out_dev, int32_t dtype, int64_t ld, stc_stream_t stream) {
+  return stc_decode_kv_batched(state_dev, 1, nullptr, info, 1, n_tokens, packed_dev,
+                               (int64_t)packed_bytes(info ? info->total_bits : 0, n_tokens), norms_dev, x_out_dev,
+                               dtype, ld, 0, stream);
+}
+
+stc_status stc_quantize_pack_f32(const stc_head_info* info, const void* state_dev, int64_t n_tokens,
+                                 const float* coeffs_dev, void* packed_dev, stc_stream_t stream) {
+  bool rht = false;
+  int mb = 0;
+  if (stc_status s = check_batch("quantize_pack_f32", state_dev, 1, info, 1, n_tokens,
+                                 (int64_t)packed_bytes(info ? info->total_bits : 0, n_tokens), &rht, &mb)) return s;
+  if (rht) return fail(STC_EUNSUPPORTED, "quantize_pack_f32: eigen/identity states only");
+  if (n_tokens == 0) return ok();
+  if (!coeffs_dev || !packed_dev || !aligned(coeffs_dev, 16) || !aligned(packed_dev, 16))
+    return fail(STC_EINVAL, "quantize_pack_f32: NULL or misaligned buffer");
+  EncodeLaunch a{static_cast<const unsigned char*>(state_dev), nullptr, 1, 1, n_tokens, D, 0,
+                 (int64_t)packed_bytes(mb, n_tokens), coeffs_dev, static_cast<unsigned char*>(packed_dev),
+                 nullptr, 2, mb};
+  if (launch_encode_eigen(a, stream)) return fail(STC_EDEVICE, "quantize_pack launch: %s", hipGetErrorString(hipGetLastError()));
+  return ok();
+}
+
+stc_status stc_attend_compressed_batched(const void* states_dev, int64_t n_states, const int32_t* k_map,
+                                         const int32_t* v_map, const stc_head_info* infos, int64_t n_pairs,
+                                         int64_t n_tokens, const void* k_packed_dev, const void* v_packed_dev,
+                                         int64_t packed_pair_stride, int32_t group, const float* q_dev,
+                                         float* out_dev, float scale, void* ws_dev, size_t ws_bytes,
+                                         stc_stream_t stream) {
+  bool rht = false;
+  int mb = 0;
+  if (stc_status s = check_batch("attend_compressed", states_dev, n_states, infos, n_pairs, n_tokens,
+                                 packed_pair_stride, &rht, &mb)) return s;
+  if (rht) return fail(STC_EUNSUPPORTED, "attend_compressed: eigen/identity states only");
+  if (group < 1 || group > 16) return fail(STC_EUNSUPPORTED, "attend_compressed: group %d outside 1..16", group);
+  if (n_tokens <= 0) return fail(STC_EINVAL, "attend_compressed: need at least one cached token");
+  if (!k_packed_dev || !v_packed_dev || !q_dev || !out_dev || !ws_dev)
+    return fail(STC_EINVAL, "attend_compressed: NULL buffer");
+  if (!aligned(k_packed_dev, 16) || !aligned(v_packed_dev, 16) || !aligned(q_dev, 16) || !aligned(out_dev, 16) ||
+      !aligned(ws_dev, 256))
+    return fail(STC_EINVAL, "attend_compressed: misaligned buffer");
+  if (!std::isfinite(scale)) return fail(STC_EINVAL, "attend_compressed: scale must be finite");
+  const size_t need = stc_attend_workspace_bytes(n_pairs, group, n_tokens);
+  if (ws_bytes < need) return fail(STC_EWORKSPACE, "attend_compressed: workspace %zu < %zu", ws_bytes, need);
+  const unsigned char* st = static_cast<const unsigned char*>(states_dev);
+  AttendLaunch a{st, k_map, st, v_map, n_states, n_pairs, n_tokens, packed_pair_stride,
+                 static_cast<const unsigned char*>(k_packed_dev), static_cast<const unsigned char*>(v_packed_dev),
+                 group, q_dev, out_dev, scale, static_cast<unsigned char*>(ws_dev), mb};
+  if (launch_attend(a, stream)) return fail(STC_EDEVICE, "attend launch: %s", hipGetErrorString(hipGetLastError()));
+  return ok();
+}
+
+stc_status stc_attend_compressed(const stc_head_info* k_info, const void* k_state_dev, const stc_head_info* v_info,
+                                 const void* v_state_dev, int64_t n_tokens, const void* k_packed_dev,
+                                 const void* v_packed_dev, int32_t group, const float* q_dev, float* out_dev,
+                                 float scale, void* ws_dev, size_t ws_bytes, stc_stream_t stream) {
+  if (!k_info || !v_info) return fail(STC_EINVAL, "attend_compressed: NULL info");
+  bool rht = false;
+  int mbk = 0, mbv = 0;
+  const int64_t stride = 0;
+  if (stc_status s = check_batch("attend_compressed", k_state_dev, 1, k_info, 1, n_tokens, stride, &rht, &mbk)) return s;
+  if (rht) return fail(STC_EUNSUPPORTED, "attend_compressed: eigen/identity states only");
+  if (stc_status s = check_batch("attend_compressed", v_state_dev, 1, v_info, 1, n_tokens, stride, &rht, &mbv)) return s;
+  if (rht) return fail(STC_EUNSUPPORTED, "attend_compressed: eigen/identity states only");
+  if (group < 1 || group > 16) return fail(STC_EUNSUPPORTED, "attend_compressed: group %d outside 1..16", group);
+  if (n_tokens <= 0) return fail(STC_EINVAL, "attend_compressed: need at least one cached token");
+  if (!k_packed_dev || !v_packed_dev || !q_dev || !out_dev || !ws_dev)
+    return fail(STC_EINVAL, "attend_compressed: NULL buffer");
+  if (!aligned(k_packed_dev, 16) || !aligned(v_packed_dev, 16) || !aligned(q_dev, 16) || !aligned(out_dev, 16) ||
+      !aligned(ws_dev, 256))
+    return fail(STC_EINVAL, "attend_compressed: misaligned buffer");
+  if (!std::isfinite(scale)) return fail(STC_EINVAL, "attend_compressed: scale must be finite");
+  const size_t need = stc_attend_workspace_bytes(1, group, n_tokens);
+  if (ws_bytes < need) return fail(STC_EWORKSPACE, "attend_compressed: workspace %zu < %zu", ws_bytes, need);
+  AttendLaunch a{static_cast<const unsigned char*>(k_state_dev), nullptr, static_cast<const unsigned char*>(v_state_dev),
+                 nullptr, 1, 1, n_tokens, 0, static_cast<const unsigned char*>(k_packed_dev),
+                 static_cast<const unsigned char*>(v_packed_dev), group, q_dev, out_dev, scale,
+                 static_cast<unsigned char*>(ws_dev), std::max(mbk, mbv)};
+  if (launch_attend(a, stream)) return fail(STC_EDEVICE, "attend launch: %s", hipGetErrorString(hipGetLastError()));
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,130 @@
+// Internal layout of the device state blob and helpers shared by the host
+// code and the HIP kernels of libstc. Not part of the public ABI.
+#pragma once
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/stc.h"
+
+namespace stc {
+
+constexpr int D = STC_D;
+constexpr size_t STATE_BYTES = 512u * 1024u;
+
+// Byte offsets of the regions of one state blob.
+constexpr size_t OFF_HDR = 0;                        // DevHdr
+constexpr size_t OFF_U32 = 8192;                     // float U[i][j], row-major (64 KiB)
+constexpr size_t OFF_UT_HI = OFF_U32 + 65536;        // bf16 U^T[j][i] high part (32 KiB)
+constexpr size_t OFF_UT_LO = OFF_UT_HI + 32768;      // bf16 U^T[j][i] low part
+constexpr size_t OFF_W_HI = OFF_UT_LO + 32768;       // bf16 W[perm row][j], W = U diag(step)
+constexpr size_t OFF_W_LO = OFF_W_HI + 32768;
+constexpr size_t OFF_THR = OFF_W_LO + 32768;         // float thresholds, up to 128*255
+constexpr size_t OFF_GRAM = OFF_THR + 131072;        // double second moment [i][j]
+static_assert(OFF_GRAM + 131072 <= STATE_BYTES, "state layout overflows the blob");
+
+// Quantizer fast path: y = c / step + L/2 + EPS; codes are exact when
+// fract(y) >= 2*EPS, otherwise the thresholds decide (see the encode kernel).
+constexpr float QEPS = 1.0f / 8192.0f;
+constexpr float QFLAG = 2.0f * QEPS;
+
+struct alignas(16) DevHdr {
+  int32_t xform;
+  int32_t total_bits;
+  int32_t n_kept;
+  int32_t nmax16;       // 16 * ceil((last kept channel + 1) / 16): encode N extent
+  int32_t kmax32;       // 32 * ceil((last kept channel + 1) / 32): decode K extent
+  int32_t pad[3];
+  uint8_t bits[D];
+  uint16_t off[D];      // bit offset of channel j inside a token record
+  float inv_step[D];    // fl32(1 / step_j); 0 for a dropped channel or a zero step
+  float ybias[D];       // L_j/2 + QEPS for a kept channel, 0.5 for a dropped one
+  int32_t lm1[D];       // L_j - 1 (0 if dropped)
+  int32_t thr_base[D];  // index of t_1 of channel j in the threshold table
+  float bias[D];        // decode: sum_j U_ij step_j (L_j - 1)/2, natural dim order
+  float step32[D];      // fl32(step_j)
+  float halfspan[D];    // (L_j - 1) / 2
+  float sign[D];        // Walsh-Hadamard diagonal (+-1)
+  float cb[8];          // Walsh-Hadamard codebook
+  float cb_thr[8];      // its 7 midpoint thresholds (last entry unused)
+};
+static_assert(sizeof(DevHdr) <= OFF_U32, "header too large");
+
+// Decode rows of W are stored permuted so that one lane of the decode MFMA
+// epilogue owns 8 consecutive output dims: stored row R = 16*mt + m with
+// mt = 2p + s, m = 4g + r holds output dim 32p + 8g + 4s + r.
+inline constexpr int w_row_dim(int R) {
+  return 32 * ((R >> 4) >> 1) + 8 * ((R & 15) >> 2) + 4 * ((R >> 4) & 1) + (R & 3);
+}
+
+inline size_t packed_bytes(int64_t total_bits, int64_t n) {
+  int64_t nb = (n * total_bits + 7) / 8;
+  return (size_t)((nb + 15) / 16 * 16);
+}
+
+// Attention split geometry (tokens per workgroup) as a function of the call's
+// shape; shared by the workspace-size query and the launcher.
+constexpr int ATT_TILE = 256;
+inline int64_t att_split_tokens(int64_t n_pairs, int64_t n_tokens) {
+  // aim for >= ~2048 workgroups in total, splits of 256..4096 tokens
+  int64_t target = 2048;
+  int64_t per = (n_pairs * n_tokens + target - 1) / target;
+  per = (per + ATT_TILE - 1) / ATT_TILE * ATT_TILE;
+  if (per < ATT_TILE) per = ATT_TILE;
+  if (per > 16 * ATT_TILE) per = 16 * ATT_TILE;
+  return per;
+}
+inline int64_t att_n_splits(int64_t n_pairs, int64_t n_tokens) {
+  int64_t s = att_split_tokens(n_pairs, n_tokens);
+  return (n_tokens + s - 1) / s;
+}
+constexpr size_t ATT_QTAB_BYTES = 16 * D * 2 * 2;   // per pair: a_hi, a_lo bf16 [16][128]
+constexpr int ATT_PART_FLOATS = D + 2;              // per (pair, split, head): acc[128], m, l
+
+// Host-side launchers implemented in stc_kernels.hip.
+struct EncodeLaunch {
+  const unsigned char* states;
+  const int32_t* map;
+  int64_t n_states;
+  int64_t n_streams, n_tokens, ld, x_stride, packed_stride;
+  const void* x;
+  unsigned char* packed;
+  float* norms;
+  int mode;       // 0 bf16 tokens, 1 fp32 tokens, 2 fp32 latent coefficients
+  int max_bits;   // largest total_bits of the states used
+};
+struct DecodeLaunch {
+  const unsigned char* states;
+  const int32_t* map;
+  int64_t n_states;
+  int64_t n_streams, n_tokens, ld, x_stride, packed_stride;
+  const unsigned char* packed;
+  const float* norms;
+  void* x;
+  int f32out;
+  int max_bits;
+};
+struct AttendLaunch {
+  const unsigned char* k_states;
+  const int32_t* k_map;
+  const unsigned char* v_states;
+  const int32_t* v_map;
+  int64_t n_states;
+  int64_t n_pairs, n_tokens, packed_stride;
+  const unsigned char* k_packed;
+  const unsigned char* v_packed;
+  int group;
+  const float* q;
+  float* out;
+  float scale;
+  unsigned char* ws;
+  int max_bits;
+};
+
+int launch_gram(const void* x, int dtype, int64_t ld, int64_t n_calib, double* gram, void* stream);
+int launch_encode_eigen(const EncodeLaunch& a, void* stream);
+int launch_decode_eigen(const DecodeLaunch& a, void* stream);
+int launch_encode_rht(const EncodeLaunch& a, void* stream);
+int launch_decode_rht(const DecodeLaunch& a, void* stream);
+int launch_attend(const AttendLaunch& a, void* stream);
+
+}  // namespace stc

@@ -1,0 +1,318 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C ABI.
+
+Bars (floating point tolerances are the ones the target states):
+  - quantize+pack fed the oracle's fp32 coefficients and the oracle's state:
+    byte-identical streams;
+  - end-to-end codes (GPU calibration and projection): at most 1e-4 of codes
+    differ, each by one level; calibrated widths identical;
+  - reconstruction relMSE within 1e-3 (relative) of the oracle's;
+  - attention: max |o - o*| <= 2e-3 max |o*|.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import codec, rht
+
+pytestmark = pytest.mark.gpu
+
+stc = pytest.importorskip("spectral_transform_codec_amd")
+
+DEV = "cuda"
+
+
+def dev_tensor(x32: np.ndarray, dtype: str) -> torch.Tensor:
+    t = torch.from_numpy(np.ascontiguousarray(x32, dtype=np.float32))
+    return (t.to(torch.bfloat16) if dtype == "bf16" else t).to(DEV)
+
+
+def gpu_state(st) -> "stc.State":
+    if st["xform"] == codec.XFORM_IDENTITY:
+        return stc.state_init(None, st["lam"], st["bits"], st["steps"], xform=stc.XFORM_IDENTITY)
+    return stc.state_init(st["U"], st["lam"], st["bits"], st["steps"], xform=stc.XFORM_EIGEN)
+
+
+def codes(packed, bits, n):
+    p = packed.cpu().numpy() if isinstance(packed, torch.Tensor) else packed
+    return codec.unpack(p, bits, n)
+
+
+def rel_err(a, b):
+    return float(np.abs(np.asarray(a, np.float64) - np.asarray(b, np.float64)).max() / np.abs(b).max())
+
+
+def stream_case(cfg, n, head=0, kind=0, layer=0):
+    w = synth.WORKLOADS[cfg]
+    return w, synth.stream(w, layer, 0, head, kind, n=n)
+
+
+# ------------------------------------------------------------ G1: bit-exact
+G1_CASES = [
+    ("cfg1_2.0", 1, 1000, 2.0, codec.XFORM_EIGEN, None),
+    ("cfg2_4.0", 2, 4133, 4.0, codec.XFORM_EIGEN, None),
+    ("cfg2_2.0", 2, 2600, 2.0, codec.XFORM_EIGEN, None),
+    ("cfg2_1.33", 2, 2600, 1.33, codec.XFORM_EIGEN, None),
+    ("identity_3.0", 2, 700, 3.0, codec.XFORM_IDENTITY, None),
+    ("all8", 2, 300, 8.0, codec.XFORM_EIGEN, None),
+    ("tiny_budget_odd", 2, 513, 0.1, codec.XFORM_EIGEN, None),
+    ("uniform2", 2, 600, 2.0, codec.XFORM_EIGEN, np.full(128, 2, np.uint8)),
+]
+
+
+@pytest.mark.parametrize("name,cfg,n,avg,xform,bits", G1_CASES, ids=[c[0] for c in G1_CASES])
+def test_quantize_pack_bitexact(name, cfg, n, avg, xform, bits):
+    w, x = stream_case(cfg, n)
+    n_c = min(w.n_calib, n)
+    st = codec.calibrate_head(x, n_c, avg, bits=bits, xform=xform)
+    c32 = codec.project(st, x).astype(np.float32)
+    # edge values: exact thresholds, neighbours, NaN, +-Inf, huge
+    kept = np.flatnonzero(st["bits"])
+    for i, j in enumerate(kept[:40]):
+        t = st["thresholds"][j]
+        c32[0, j] = t[len(t) // 2]
+        c32[1, j] = np.nextafter(t[0], np.float32(-np.inf))
+        c32[2, j] = t[-1]
+    c32[3, :] = np.nan
+    c32[4, :] = np.inf
+    c32[5, :] = -np.inf
+    c32[6, :] = 3e38
+    c32[7, :] = -0.0
+    gst = gpu_state(st)
+    got = stc.quantize_pack_f32(gst, torch.from_numpy(c32).to(DEV)).cpu().numpy()
+    want = codec.quantize_pack(st, c32.astype(np.float64))
+    assert got.shape == want.shape
+    assert np.array_equal(got, want), f"{np.count_nonzero(got != want)} bytes differ"
+
+
+def test_quantize_pack_zero_step_channel():
+    """A kept channel with a zero step (variance <= 0): every threshold is 0."""
+    lam = np.linspace(2.0, 0.5, 128)
+    lam[5] = 0.0
+    bits = np.full(128, 8, np.uint8)
+    st = codec.make_state(np.eye(128), lam, bits, codec.XFORM_IDENTITY)
+    c = np.random.default_rng(50).standard_normal((300, 128)).astype(np.float32)
+    c[:4, 5] = [0.0, -0.0, -1e-30, 1e-30]
+    gst = stc.state_init(None, lam, bits, st["steps"], xform=stc.XFORM_IDENTITY)
+    got = stc.quantize_pack_f32(gst, torch.from_numpy(c).to(DEV)).cpu().numpy()
+    assert np.array_equal(got, codec.quantize_pack(st, c.astype(np.float64)))
+
+
+def test_zero_tokens_is_a_noop():
+    w, x = stream_case(2, 64)
+    st = codec.calibrate_head(x, 64, 2.0)
+    gst = gpu_state(st)
+    packed, _ = stc.encode_kv(gst, dev_tensor(x[:0], "bf16"))
+    assert packed.numel() == 0
+
+
+# ------------------------------------------------------ G2: end-to-end codes
+E2E_CASES = [(1, 4096, 2.0, "f32"), (2, 8192, 4.0, "bf16"), (2, 8192, 2.0, "bf16"), (2, 8192, 1.33, "bf16"),
+             (5, 4500, 1.33, "bf16")]
+
+
+@pytest.mark.parametrize("cfg,n,avg,dtype", E2E_CASES)
+def test_encode_end_to_end(cfg, n, avg, dtype):
+    w, x = stream_case(cfg, n, head=1, kind=1)
+    n_c = w.n_calib
+    xd = dev_tensor(x, dtype)
+    gst = stc.calibrate_head(xd, n_c, avg)
+    ost = codec.calibrate_head(x, n_c, avg)
+    assert np.array_equal(gst.bits, ost["bits"])
+    assert np.abs(gst.lam - ost["lam"]).max() <= 1e-11 * ost["lam"][0]
+    assert np.abs(gst.basis() - ost["U"]).max() <= 1e-6
+    packed, _ = stc.encode_kv(gst, xd)
+    assert packed.numel() == codec.packed_bytes(ost["total_bits"], n)
+    qg = codes(packed, ost["bits"], n)
+    qo = codec.quantize(ost, codec.project(ost, x))
+    diff = qg != qo
+    frac = diff.sum() / max(1, n * int((ost["bits"] > 0).sum()))
+    assert frac <= 1e-4, frac
+    assert np.abs(qg - qo).max() <= 1
+
+
+def test_encode_with_oracle_state_isolates_projection():
+    w, x = stream_case(2, 5000, head=2)
+    ost = codec.calibrate_head(x, 2048, 2.0)
+    packed, _ = stc.encode_kv(gpu_state(ost), dev_tensor(x, "bf16"))
+    qg = codes(packed, ost["bits"], 5000)
+    qo = codec.quantize(ost, codec.project(ost, x))
+    assert (qg != qo).mean() <= 1e-4 and np.abs(qg - qo).max() <= 1
+
+
+# ---------------------------------------------------------- G3: reconstruction
+@pytest.mark.parametrize("cfg,n,avg,dtype", E2E_CASES + [(2, 777, 8.0, "bf16")])
+def test_decode_matches_oracle(cfg, n, avg, dtype):
+    w, x = stream_case(cfg, n, head=3)
+    ost = codec.calibrate_head(x, min(w.n_calib, n), avg)
+    po = codec.encode_kv(ost, x)
+    out = stc.decode_kv(gpu_state(ost), torch.from_numpy(po).to(DEV), n,
+                        dtype=torch.float32 if dtype == "f32" else torch.bfloat16)
+    xg = out.float().cpu().numpy().astype(np.float64)
+    xo = codec.decode_kv(ost, po, n, dtype)
+    r_o, r_g = codec.rel_mse(x, xo), codec.rel_mse(x, xg)
+    assert abs(r_g - r_o) <= 1e-3 * r_o, (r_g, r_o)
+    # element-wise: one rounding step of the output dtype apart, plus the
+    # error of the GPU's arithmetic before rounding. Each basis-times-step
+    # entry is held as a bf16 pair (relative error <= 2^-17) and the codes are
+    # summed in fp32, so that error is below 2^-15 sum_j |U_ij| step_j (L_j-1).
+    exact = codec.reconstruct_exact(ost, po, n)
+    ulp = np.abs(exact) * (2.0 ** -7 if dtype == "bf16" else 2.0 ** -23)
+    levels_m1 = np.where(ost["bits"] > 0, (1 << ost["bits"].astype(np.int64)) - 1, 0)
+    arith = 2.0 ** -15 * (np.abs(ost["U"]) @ (ost["steps"] * levels_m1))
+    assert np.all(np.abs(xg - xo) <= ulp + arith[None, :])
+
+
+@pytest.mark.parametrize("cfg,n,avg,dtype", [(1, 4096, 2.0, "f32"), (2, 8192, 2.0, "bf16")])
+def test_relmse_end_to_end(cfg, n, avg, dtype):
+    w, x = stream_case(cfg, n, head=4, kind=1)
+    xd = dev_tensor(x, dtype)
+    gst = stc.calibrate_head(xd, w.n_calib, avg)
+    packed, _ = stc.encode_kv(gst, xd)
+    xg = stc.decode_kv(gst, packed, n, dtype=xd.dtype).float().cpu().numpy()
+    ost = codec.calibrate_head(x, w.n_calib, avg)
+    xo = codec.decode_kv(ost, codec.encode_kv(ost, x), n, dtype)
+    r_o, r_g = codec.rel_mse(x, xo), codec.rel_mse(x, xg)
+    assert abs(r_g - r_o) <= 1e-3 * r_o, (r_g, r_o)
+
+
+# --------------------------------------------------------------- G4: attention
+@pytest.mark.parametrize("cfg,n,avg", [(1, 4096, 2.0), (2, 32768, 2.0), (2, 9000, 4.0), (2, 3000, 1.33),
+                                       (5, 2500, 1.33), (2, 1, 2.0), (2, 300, 2.0)])
+def test_attention_matches_oracle(cfg, n, avg):
+    w = synth.WORKLOADS[cfg]
+    k = synth.stream(w, 0, 0, 1, 0, n=n)
+    v = synth.stream(w, 0, 0, 1, 1, n=n)
+    n_c = min(w.n_calib, n)
+    ks, vs = codec.calibrate_head(k, n_c, avg), codec.calibrate_head(v, n_c, avg)
+    kp, vp = codec.encode_kv(ks, k), codec.encode_kv(vs, v)
+    q = synth.queries(w, 0, 0, 1)
+    want = codec.attend_compressed(ks, vs, kp, vp, n, q.astype(np.float64))
+    got = stc.attend_compressed(gpu_state(ks), gpu_state(vs), torch.from_numpy(kp).to(DEV),
+                                torch.from_numpy(vp).to(DEV), n, torch.from_numpy(q).to(DEV)).cpu().numpy()
+    assert rel_err(got, want) <= 2e-3, rel_err(got, want)
+
+
+def test_attention_end_to_end_gpu_codes():
+    w = synth.WORKLOADS[2]
+    n = 8192
+    k = synth.stream(w, 0, 0, 5, 0, n=n)
+    v = synth.stream(w, 0, 0, 5, 1, n=n)
+    kd, vd = dev_tensor(k, "bf16"), dev_tensor(v, "bf16")
+    gk, gv = stc.calibrate_head(kd, 2048, 2.0), stc.calibrate_head(vd, 2048, 2.0)
+    kp, _ = stc.encode_kv(gk, kd)
+    vp, _ = stc.encode_kv(gv, vd)
+    q = synth.queries(w, 0, 0, 5)
+    got = stc.attend_compressed(gk, gv, kp, vp, n, torch.from_numpy(q).to(DEV)).cpu().numpy()
+    ks, vs = codec.calibrate_head(k, 2048, 2.0), codec.calibrate_head(v, 2048, 2.0)
+    want = codec.attend_compressed(ks, vs, codec.encode_kv(ks, k), codec.encode_kv(vs, v), n, q.astype(np.float64))
+    assert rel_err(got, want) <= 2e-3
+
+
+def test_attention_batched_gqa7():
+    w = synth.WORKLOADS[5]
+    n, pairs = 2100, 3
+    states, kps, vps, qs, wants = [], [], [], [], []
+    for hd in range(pairs):
+        k = synth.stream(w, 0, 0, hd, 0, n=n)
+        v = synth.stream(w, 0, 0, hd, 1, n=n)
+        ks, vs = codec.calibrate_head(k, 2048, 1.33), codec.calibrate_head(v, 2048, 1.33)
+        kp, vp = codec.encode_kv(ks, k), codec.encode_kv(vs, v)
+        q = synth.queries(w, 0, 0, hd)
+        wants.append(codec.attend_compressed(ks, vs, kp, vp, n, q.astype(np.float64)))
+        states += [gpu_state(ks), gpu_state(vs)]
+        kps.append(kp); vps.append(vp); qs.append(q)
+    arr = stc.StateArray(states)
+    stride = stc.packed_bytes(arr.max_bits, n)
+    kb = np.zeros((pairs, stride), np.uint8); vb = np.zeros((pairs, stride), np.uint8)
+    for i in range(pairs):
+        kb[i, :kps[i].shape[0]] = kps[i]; vb[i, :vps[i].shape[0]] = vps[i]
+    kmap = torch.tensor([0, 2, 4], dtype=torch.int32, device=DEV)
+    vmap = torch.tensor([1, 3, 5], dtype=torch.int32, device=DEV)
+    out = stc.attend_compressed_batched(arr, kmap, vmap, torch.from_numpy(kb).to(DEV), torch.from_numpy(vb).to(DEV),
+                                        n, torch.from_numpy(np.stack(qs)).to(DEV)).cpu().numpy()
+    for i in range(pairs):
+        assert rel_err(out[i], wants[i]) <= 2e-3
+
+
+# ---------------------------------------------------------- batched codec
+def test_batched_encode_decode_shared_states():
+    w = synth.WORKLOADS[5]
+    n = 3000
+    xs = [synth.stream(w, 0, b, 0, 0, n=n) for b in range(4)]
+    st0 = codec.calibrate_head(xs[0], 2048, 1.33)
+    st1 = codec.calibrate_head(synth.stream(w, 0, 0, 1, 0, n=n), 2048, 1.33)
+    arr = stc.StateArray([gpu_state(st0), gpu_state(st1)])
+    smap = [0, 1, 1, 0]
+    x = torch.stack([dev_tensor(xi, "bf16") for xi in xs])
+    packed, _ = stc.encode_kv_batched(arr, x, torch.tensor(smap, dtype=torch.int32, device=DEV))
+    dec = stc.decode_kv_batched(arr, packed, n, state_of_stream=torch.tensor(smap, dtype=torch.int32, device=DEV))
+    for i, si in enumerate(smap):
+        st = st0 if si == 0 else st1
+        qg = codes(packed[i, :codec.packed_bytes(st["total_bits"], n)], st["bits"], n)
+        qo = codec.quantize(st, codec.project(st, xs[i]))
+        assert (qg != qo).mean() <= 1e-4 and np.abs(qg - qo).max() <= 1
+        single, _ = stc.encode_kv(gpu_state(st), dev_tensor(xs[i], "bf16"))
+        assert torch.equal(single, packed[i, :single.numel()])
+        xo = codec.decode_kv(st, codec.pack(qg, st["bits"]), n, "bf16")
+        xg = dec[i].float().cpu().numpy()
+        assert abs(codec.rel_mse(xs[i], xg) - codec.rel_mse(xs[i], xo)) <= 1e-3 * codec.rel_mse(xs[i], xo)
+
+
+# ----------------------------------------------------------------- RHT path
+@pytest.fixture(scope="module")
+def rht_codebook():
+    c, _ = rht.lloyd_max(synth.sphere_coordinate_samples(100000))
+    return rht.codebook_fp32(c)
+
+
+@pytest.mark.parametrize("n", [1, 1000, 32768])
+def test_rht_encode_matches_oracle(rht_codebook, n):
+    w = synth.WORKLOADS[3]
+    x = synth.stream(w, 0, 0, 2, 0, n=n)
+    signs = synth.random_signs(3, 0, 0, 2, 0)
+    ost = rht.make_state(signs, rht_codebook)
+    gst = stc.rht_state_init(signs, rht_codebook)
+    packed, norms = stc.encode_kv(gst, dev_tensor(x, "bf16"))
+    po, no = rht.encode_kv(ost, x)
+    assert packed.numel() == po.shape[0]
+    qg, qo = codes(packed, ost["bits"], n), codec.unpack(po, ost["bits"], n)
+    assert (qg != qo).mean() <= 1e-4 and np.abs(qg - qo).max() <= 1
+    # fp32 sum of 128 squares then sqrt: relative error <= (127/2 + 1) 2^-24
+    ng = norms.cpu().numpy()
+    assert np.all(np.abs(ng - no) <= 4e-6 * no)
+
+
+def test_rht_decode_matches_oracle(rht_codebook):
+    w = synth.WORKLOADS[3]
+    n = 5000
+    x = synth.stream(w, 0, 0, 3, 1, n=n)
+    signs = synth.random_signs(3, 0, 0, 3, 1)
+    ost = rht.make_state(signs, rht_codebook)
+    po, no = rht.encode_kv(ost, x)
+    gst = stc.rht_state_init(signs, rht_codebook)
+    xg = stc.decode_kv(gst, torch.from_numpy(po).to(DEV), n, torch.from_numpy(no).to(DEV)).float().cpu().numpy()
+    xo = rht.decode_kv(ost, po, no, n, "bf16")
+    r_o, r_g = codec.rel_mse(x, xo), codec.rel_mse(x, xg)
+    assert abs(r_g - r_o) <= 1e-3 * r_o
+    exact = rht.reconstruct_exact(ost, po, no, n)
+    assert np.all(np.abs(xg - xo) <= 1.01 * np.abs(exact) * 2.0 ** -7 + 1e-6 * np.abs(exact).max())
+
+
+def test_rht_batched(rht_codebook):
+    w = synth.WORKLOADS[3]
+    n = 2000
+    xs = [synth.stream(w, 0, 0, h, 0, n=n) for h in range(3)]
+    sg = [synth.random_signs(3, 0, 0, h, 0) for h in range(3)]
+    arr = stc.StateArray([stc.rht_state_init(s, rht_codebook) for s in sg])
+    packed, norms = stc.encode_kv_batched(arr, torch.stack([dev_tensor(xi, "bf16") for xi in xs]))
+    dec = stc.decode_kv_batched(arr, packed, n, norms=norms)
+    for i in range(3):
+        ost = rht.make_state(sg[i], rht_codebook)
+        po, no = rht.encode_kv(ost, xs[i])
+        qg, qo = codes(packed[i], ost["bits"], n), codec.unpack(po, ost["bits"], n)
+        assert (qg != qo).mean() <= 1e-4
+        r_o = codec.rel_mse(xs[i], rht.decode_kv(ost, po, no, n, "bf16"))
+        assert abs(codec.rel_mse(xs[i], dec[i].float().cpu().numpy()) - r_o) <= 1e-3 * r_o
