@@ -179,6 +179,29 @@ void sort_and_fix_signs(int n, const std::vector<double>& diag, const std::vecto
   }
 }
 
+// ------------------------------------------------------ unpack plan
+// For each quarter of 32 channels and each group of 4 consecutive channels,
+// where the group's codes sit relative to the quarter's first code bit: the
+// quarter-relative 32-bit word k holding its first bit, the shift s inside
+// it, and the 4 widths. 4 codes span at most 32 bits, so one 64-bit window
+// (words k, k+1) always holds the whole group.
+void fill_unpack_plan(DevHdr* h) {
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t q0 = h->off[32 * q];
+    h->qoff[q] = q0;
+    uint32_t kmax = 0;
+    for (int i = 0; i < 8; ++i) {
+      const int c = 32 * q + 4 * i;
+      const uint32_t rel = h->off[c] - q0;
+      const uint32_t k = rel >> 5, sft = rel & 31;
+      kmax = std::max(kmax, k);
+      h->plan[q][i] = k | sft << 5 | (uint32_t)h->bits[c] << 10 | (uint32_t)h->bits[c + 1] << 14 |
+                      (uint32_t)h->bits[c + 2] << 18 | (uint32_t)h->bits[c + 3] << 22;
+    }
+    h->qwords[q] = kmax + 2;
+  }
+}
+
 // ------------------------------------------------------ state construction
 stc_status build_eigen_blob(int d, int xform, const double* u, const double* lambda,
                             const uint8_t* bits, const double* steps_in, stc_head_info* info,
@@ -247,6 +270,8 @@ stc_status build_eigen_blob(int d, int xform, const double* u, const double* lam
     }
     h->bias[i] = (float)bias;
   }
+  for (int j = 0; j < d; ++j) h->bits4[j / 8] |= (uint32_t)bits[j] << (4 * (j % 8));
+  fill_unpack_plan(h);
   for (int R = 0; R < D; ++R) {
     const int i = w_row_dim(R);
     for (int j = 0; j < d; ++j) split_bf16(ud[(size_t)i * d + j] * steps[j], &w_hi[R * D + j], &w_lo[R * D + j]);
@@ -435,9 +460,11 @@ stc_status stc_rht_state_init(int32_t d, const int8_t* signs, const float* codeb
   h->kmax32 = d;
   for (int j = 0; j < d; ++j) {
     h->bits[j] = STC_RHT_BITS;
+    h->bits4[j / 8] |= (uint32_t)STC_RHT_BITS << (4 * (j % 8));
     h->off[j] = (uint16_t)(STC_RHT_BITS * j);
     h->sign[j] = (float)signs[j];
   }
+  fill_unpack_plan(h);
   for (int k = 0; k < 8; ++k) h->cb[k] = codebook[k];
   for (int k = 0; k < 7; ++k) h->cb_thr[k] = (float)(0.5 * ((double)codebook[k] + (double)codebook[k + 1]));
   info->d = d;

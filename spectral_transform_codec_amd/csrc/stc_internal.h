@@ -46,6 +46,15 @@ struct alignas(16) DevHdr {
   float sign[D];        // Walsh-Hadamard diagonal (+-1)
   float cb[8];          // Walsh-Hadamard codebook
   float cb_thr[8];      // its 7 midpoint thresholds (last entry unused)
+  uint32_t bits4[D / 8];  // widths again, 4 bits each: channel j in bits 4(j%8).. of word j/8
+  // Unpack plan. Quarter q covers channels [32q, 32q+32); its codes start at
+  // record bit qoff[q]. Output dword i of quarter q (channels 32q+4i..+3)
+  // reads the 64-bit window of quarter-relative words k, k+1 at bit s:
+  //   plan[q][i] = k | s << 5 | b0 << 10 | b1 << 14 | b2 << 18 | b3 << 22.
+  // qwords[q] = record-aligned words a quarter needs (max k + 2).
+  uint32_t plan[4][8];
+  uint32_t qoff[4];
+  uint32_t qwords[4];
 };
 static_assert(sizeof(DevHdr) <= OFF_U32, "header too large");
 
@@ -65,13 +74,13 @@ inline size_t packed_bytes(int64_t total_bits, int64_t n) {
 // shape; shared by the workspace-size query and the launcher.
 constexpr int ATT_TILE = 256;
 inline int64_t att_split_tokens(int64_t n_pairs, int64_t n_tokens) {
-  // aim for >= ~2048 workgroups in total, splits of 256..4096 tokens
-  int64_t target = 2048;
-  int64_t per = (n_pairs * n_tokens + target - 1) / target;
-  per = (per + ATT_TILE - 1) / ATT_TILE * ATT_TILE;
-  if (per < ATT_TILE) per = ATT_TILE;
-  if (per > 16 * ATT_TILE) per = 16 * ATT_TILE;
-  return per;
+  // about 512 workgroups in total (two per CU), splits of 1..256 tiles
+  const int64_t target = 512;
+  int64_t tiles = (n_tokens + ATT_TILE - 1) / ATT_TILE;
+  int64_t per = (n_pairs * tiles + target - 1) / target;
+  if (per < 1) per = 1;
+  if (per > 256) per = 256;
+  return per * ATT_TILE;
 }
 inline int64_t att_n_splits(int64_t n_pairs, int64_t n_tokens) {
   int64_t s = att_split_tokens(n_pairs, n_tokens);

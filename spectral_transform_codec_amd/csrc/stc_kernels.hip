@@ -79,18 +79,17 @@ __device__ __forceinline__ f16x8 bytes_to_f16x8(u32x2 v) {
 // forced into scalar registers: the pack/unpack loops branch on them, and a
 // per-channel vector load there would serialise a cache round trip per channel.
 struct HalfW {
-  unsigned w[16];  // byte k of w[i] = width of channel 64h + 4i + k
+  unsigned w[8];   // bits 4k..4k+3 of w[i] = width of channel 64h + 8i + k
   unsigned off;    // record bit offset of channel 64h
 };
 __device__ __forceinline__ HalfW load_half_widths(const DevHdr* hdr, int h) {
   HalfW r;
-  const unsigned* bw = reinterpret_cast<const unsigned*>(hdr->bits) + 16 * h;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) r.w[i] = __builtin_amdgcn_readfirstlane(bw[i]);
+  for (int i = 0; i < 8; ++i) r.w[i] = __builtin_amdgcn_readfirstlane(hdr->bits4[8 * h + i]);
   r.off = __builtin_amdgcn_readfirstlane((unsigned)hdr->off[64 * h]);
   return r;
 }
-__device__ __forceinline__ int width_of(const HalfW& W, int jj) { return (W.w[jj >> 2] >> (8 * (jj & 3))) & 0xff; }
+__device__ __forceinline__ int width_of(const HalfW& W, int jj) { return (W.w[jj >> 3] >> (4 * (jj & 7))) & 0xf; }
 
 // OR a 32-bit record word into an LDS bit stream at bit (32*d + sh).
 __device__ __forceinline__ void stage_or(unsigned* stage, unsigned d, unsigned sh, unsigned w) {
@@ -212,6 +211,24 @@ __global__ void __launch_bounds__(ENC_THREADS, 1) k_encode_eigen(EncK a) {
   int nt_cnt = 0, B = 0;
   HalfW HW = {};
 
+  // A fragments (tokens) of the next tile, loaded while the current one is
+  // processed (bf16 tokens only).
+  bf16x8 pf[2][4];
+  auto load_frags = [&](long long tile) {
+    const long long s = tile / a.tiles_per_stream;
+    const long long tt = tile - s * a.tiles_per_stream;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      long long tok = tt * ENC_T + 32 * wave + 16 * mt + r16;
+      if (tok > n - 1) tok = n - 1;
+      const unsigned short* row = static_cast<const unsigned short*>(a.x) + s * a.x_stride + tok * a.ld;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        pf[mt][ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(row + 32 * ks + 8 * g4));
+    }
+  };
+  if (MODE == 0 && t_begin < t_end) load_frags(t_begin);
+
   for (long long tile = t_begin; tile < t_end; ++tile) {
     const long long s = tile / a.tiles_per_stream;
     const long long tt = tile - s * a.tiles_per_stream;
@@ -244,7 +261,10 @@ __global__ void __launch_bounds__(ENC_THREADS, 1) k_encode_eigen(EncK a) {
       }
       __syncthreads();
     }
-    if (B == 0) continue;
+    if (B == 0) {
+      if (MODE == 0 && tile + 1 < t_end) load_frags(tile + 1);
+      continue;
+    }
     const long long tok0 = tt * ENC_T;
 
     // ---------------- phase A: project + quantize, codes -> LDS rows
@@ -257,18 +277,19 @@ __global__ void __launch_bounds__(ENC_THREADS, 1) k_encode_eigen(EncK a) {
         for (int r = 0; r < 4; ++r) cw[mt][h][r] = 0u;
     {
       bf16x8 ah[2][4], al[2][4];
-      if (MODE != 2) {
+      if (MODE == 0) {
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) ah[mt][ks] = pf[mt][ks];
+        if (tile + 1 < t_end) load_frags(tile + 1);
+      }
+      if (MODE == 1) {
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
           long long tok = tok0 + 32 * wave + 16 * mt + r16;
           if (tok > n - 1) tok = n - 1;
-          if (MODE == 0) {
-            const unsigned short* row =
-                static_cast<const unsigned short*>(a.x) + s * a.x_stride + tok * a.ld;
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks)
-              ah[mt][ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(row + 32 * ks + 8 * g4));
-          } else {
+          {
             const float* row = static_cast<const float*>(a.x) + s * a.x_stride + tok * a.ld;
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
@@ -452,17 +473,85 @@ int launch_encode_eigen(const EncodeLaunch& L, void* stream) {
 }
 
 // ======================================================================
+// Variable-width unpack, one quarter record (32 channels) per lane.
+// Stage: the lane loads the HBM dwords covering its quarter record, aligns
+// them to the record's first bit and stores them in a column of an LDS array
+// (word k of task t at col[k * ntask + t]: consecutive lanes hit consecutive
+// banks). Unpack: for each group of 4 channels the state's plan names the
+// word pair and bit shift holding the group; one 64-bit window read gives 4
+// codes. No read depends on another, so they pipeline; the plan is uniform.
+// ======================================================================
+constexpr int QW_MAX = 9;    // record-aligned words a quarter can need (256 bits + shift)
+
+struct QPlan {
+  unsigned e[8];
+  unsigned off;
+  unsigned nw;
+};
+__device__ __forceinline__ QPlan load_qplan(const DevHdr* hdr, int q) {
+  QPlan r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r.e[i] = __builtin_amdgcn_readfirstlane(hdr->plan[q][i]);
+  r.off = __builtin_amdgcn_readfirstlane(hdr->qoff[q]);
+  r.nw = __builtin_amdgcn_readfirstlane(hdr->qwords[q]);
+  return r;
+}
+
+// HBM dwords [d0, d0 + nw] of a stream of sdw >= 1 dwords (zero past the end
+// or when !valid). Addresses are clamped instead of branched on, so the loads
+// issue back to back.
+__device__ __forceinline__ void load_quarter_raw(const unsigned* g, unsigned long long d0, unsigned long long sdw,
+                                                 bool valid, unsigned nw, unsigned raw[QW_MAX + 1]) {
+  const unsigned long long last = sdw - 1;
+#pragma unroll
+  for (int k = 0; k <= QW_MAX; ++k) {
+    if ((unsigned)k <= nw) {
+      const unsigned long long idx = d0 + k;
+      const unsigned v = g[idx < last ? idx : last];
+      raw[k] = (valid && idx <= last) ? v : 0u;
+    } else {
+      raw[k] = 0u;
+    }
+  }
+}
+
+__device__ __forceinline__ void stage_quarter(const unsigned raw[QW_MAX + 1], unsigned sh, unsigned nw, unsigned* col,
+                                              int ntask) {
+#pragma unroll
+  for (int k = 0; k < QW_MAX; ++k)
+    if ((unsigned)k < nw) col[k * ntask] = __builtin_amdgcn_alignbit(raw[k + 1], raw[k], sh);
+}
+
+__device__ __forceinline__ void unpack_quarter(const unsigned* col, int ntask, const QPlan& P, unsigned out[8]) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const unsigned e = P.e[i];
+    const unsigned k = e & 31u, sft = (e >> 5) & 31u;
+    const unsigned b0 = (e >> 10) & 15u, b1 = (e >> 14) & 15u, b2 = (e >> 18) & 15u, b3 = (e >> 22) & 15u;
+    const unsigned lo = col[k * ntask], hi = col[(k + 1) * ntask];
+    const unsigned w = __builtin_amdgcn_alignbit(hi, lo, sft);
+    unsigned v = __builtin_amdgcn_ubfe(w, 0u, b0);
+    v |= __builtin_amdgcn_ubfe(w, b0, b1) << 8;
+    v |= __builtin_amdgcn_ubfe(w, b0 + b1, b2) << 16;
+    v |= __builtin_amdgcn_ubfe(w, b0 + b1 + b2, b3) << 24;
+    out[i] = v;
+  }
+}
+
+// ======================================================================
 // Decode (eigen / identity): unpack -> MFMA with W = U diag(step) -> bias.
 // x_hat_i = sum_j W_ij q_j - bias_i,  bias_i = sum_j W_ij (L_j - 1)/2,
 // i.e. sum_j U_ij step_j (q_j - (L_j - 1)/2) with q the raw codes.
-// Phase A: the tile's packed bytes -> LDS. Phase B: one half record per lane
-// unpacks codes (uniform widths) to LDS rows. Phase C: each wave rebuilds 32
-// tokens x 128 dims (A = W rows from LDS, B = codes), then stores bf16/fp32.
+// 16 waves per workgroup, 256-token tiles. Each lane unpacks one quarter
+// record (task = 4 quarters x 256 tokens) into LDS code rows; then wave w
+// rebuilds tokens 32(w%8)..+31 for output dims 64(w/8)..+63 (A = W rows
+// staged in LDS, B = codes) and stores them. The next tile's HBM words are
+// loaded while the current tile is reconstructed.
 // ======================================================================
 constexpr int DEC_T = 256;
-constexpr int DEC_THREADS = 512;
-constexpr int PK_BYTES = 32 * 1024 + 64;
-constexpr size_t DEC_LDS = 2 * 128 * UROW + DEC_T * CROW + PK_BYTES;
+constexpr int DEC_THREADS = 1024;
+constexpr int DCROW = 132;  // code row bytes (33 dwords: lanes of a wave hit distinct banks)
+constexpr size_t DEC_LDS = 2 * 128 * UROW + DEC_T * DCROW + (size_t)QW_MAX * DEC_THREADS * 4;
 
 struct DecK {
   const unsigned char* states;
@@ -476,31 +565,29 @@ struct DecK {
 
 // Unpack the 64 codes of channels [64h, 64h+64) of token tl from the LDS
 // stream `P32` (bit 0 = first bit of the tile) into 16 dwords, natural order.
+// Every code is read through its own 64-bit window at its bit address, so the
+// LDS reads are independent of each other and pipeline freely (a running
+// window would serialise one LDS round trip per 32 bits of record).
+// Reads P32[.. (tl*B + off + 64-channel span) / 32 + 1].
 __device__ __forceinline__ void unpack_half(const unsigned* P32, const HalfW& W, unsigned tl, int B,
                                             unsigned cw[16]) {
 #pragma unroll
   for (int i = 0; i < 16; ++i) cw[i] = 0u;
-  const unsigned S = tl * (unsigned)B + W.off;
-  const unsigned d0 = S >> 5, sh = S & 31u;
-  const unsigned r0 = P32[d0], r1 = P32[d0 + 1], r2 = P32[d0 + 2];
-  unsigned cur = __builtin_amdgcn_alignbit(r1, r0, sh);
-  unsigned nxt = __builtin_amdgcn_alignbit(r2, r1, sh);
-  unsigned raw = r2, k = d0 + 3;
-  int pos = 0;
+  unsigned S = tl * (unsigned)B + W.off;
+  // opaque to the optimiser: keeps the 64 per-channel addresses from being
+  // hoisted out of the caller's tile loop (they would pin ~64 registers)
+  asm volatile("" : "+v"(S));
+  unsigned pos = 0;
 #pragma unroll
   for (int jj = 0; jj < 64; ++jj) {
-    // bits [pos, pos + bw) of the 64-bit window nxt:cur (bw = 0 gives 0)
-    const int bw = width_of(W, jj);
-    const unsigned code = __builtin_amdgcn_ubfe(__builtin_amdgcn_alignbit(nxt, cur, (unsigned)pos), 0u, (unsigned)bw);
+    const unsigned bw = (unsigned)width_of(W, jj);
+    const unsigned bit = S + pos;
+    const unsigned d = bit >> 5;
+    const unsigned code = __builtin_amdgcn_ubfe(__builtin_amdgcn_alignbit(P32[d + 1], P32[d], bit), 0u, bw);
     cw[jj >> 2] |= code << (8 * (jj & 3));
     pos += bw;
-    if (pos >= 32) {
-      pos -= 32;
-      cur = nxt;
-      const unsigned rn = P32[k++];
-      nxt = __builtin_amdgcn_alignbit(rn, raw, sh);
-      raw = rn;
-    }
+    // keep at most 16 channels' reads in flight (register pressure)
+    if ((jj & 15) == 15) __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -510,21 +597,45 @@ __global__ void __launch_bounds__(DEC_THREADS, 1) k_decode_eigen(DecK a) {
   unsigned char* sWhi = smem;
   unsigned char* sWlo = smem + 128 * UROW;
   unsigned char* sCode = smem + 2 * 128 * UROW;
-  unsigned* sPk = reinterpret_cast<unsigned*>(smem + 2 * 128 * UROW + DEC_T * CROW);
+  unsigned* sCol = reinterpret_cast<unsigned*>(smem + 2 * 128 * UROW + DEC_T * DCROW);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r16 = lane & 15, g4 = lane >> 4;
+  const int q = wave >> 2;          // quarter record of this lane's unpack task
+  const int tl = tid & 255;         // token of this lane's unpack task
+  const int dh = wave >> 3;         // output-dim half of this wave's reconstruction
+  const int tw = wave & 7;          // token group of this wave's reconstruction
   const int lw = xcd_logical(blockIdx.x, a.grid);
   const long long t_begin = (long long)lw * a.tiles_per_wg;
   long long t_end = t_begin + a.tiles_per_wg;
   if (t_end > a.total_tiles) t_end = a.total_tiles;
   const long long n = a.n_tokens;
 
+  unsigned raw[QW_MAX + 1] = {};
+  unsigned raw_sh = 0;
+  // issue the HBM loads of this lane's quarter record of `tile`
+  auto load_raw = [&](long long tile) {
+    const long long s2 = tile / a.tiles_per_stream;
+    const long long tt2 = tile - s2 * a.tiles_per_stream;
+    const DevHdr* h2 =
+        reinterpret_cast<const DevHdr*>(a.states + (size_t)state_index(a.map, s2, a.n_states) * STATE_BYTES);
+    const unsigned long long B2 = (unsigned)h2->total_bits;
+    const unsigned nw = __builtin_amdgcn_readfirstlane(h2->qwords[q]);
+    const unsigned qo = __builtin_amdgcn_readfirstlane(h2->qoff[q]);
+    const unsigned long long tg = (unsigned long long)(tt2 * DEC_T + tl);
+    const unsigned long long S = tg * B2 + qo;
+    raw_sh = (unsigned)(S & 31u);
+    const unsigned long long sdw = (unsigned long long)packed_len((long long)B2, n) >> 2;
+    const unsigned* g = reinterpret_cast<const unsigned*>(a.packed + s2 * a.packed_stride);
+    if (B2 > 0) load_quarter_raw(g, S >> 5, sdw, tg < (unsigned long long)n, nw, raw);
+  };
+  if (t_begin < t_end) load_raw(t_begin);
+
   long long cur = -1;
   const DevHdr* hdr = nullptr;
   int ks_cnt = 0, B = 0;
-  HalfW HW = {};
+  QPlan QP = {};
 
   for (long long tile = t_begin; tile < t_end; ++tile) {
     const long long s = tile / a.tiles_per_stream;
@@ -535,7 +646,7 @@ __global__ void __launch_bounds__(DEC_THREADS, 1) k_decode_eigen(DecK a) {
       hdr = reinterpret_cast<const DevHdr*>(st + OFF_HDR);
       ks_cnt = hdr->kmax32 >> 5;
       B = hdr->total_bits;
-      HW = load_half_widths(hdr, wave >> 2);
+      QP = load_qplan(hdr, q);
       __syncthreads();
       const u32x4* ghi = reinterpret_cast<const u32x4*>(st + OFF_W_HI);
       const u32x4* glo = reinterpret_cast<const u32x4*>(st + OFF_W_LO);
@@ -548,36 +659,25 @@ __global__ void __launch_bounds__(DEC_THREADS, 1) k_decode_eigen(DecK a) {
       __syncthreads();
     }
     const long long tok0 = tt * DEC_T;
-    // ---------------- phase A: packed tile -> LDS
+    // ---- stage this lane's quarter record (its own LDS column)
+    stage_quarter(raw, raw_sh, QP.nw, sCol + tid, DEC_THREADS);
+    __syncthreads();  // previous tile's reconstruction is done with the code rows
+    // ---- unpack to code rows (natural channel order)
     {
-      const long long P = packed_len(B, n);
-      const long long start = tt * 32LL * B;
-      long long nb = 32LL * B;
-      if (nb > P - start) nb = P - start;
-      const u32x4* src = reinterpret_cast<const u32x4*>(a.packed + s * a.packed_stride + start);
-      u32x4* dst = reinterpret_cast<u32x4*>(sPk);
-      const int nchunk = (int)(nb >> 4);
-      const int zend = 2 * B + 2;
-      for (int i = tid; i < zend; i += DEC_THREADS) dst[i] = i < nchunk ? src[i] : (u32x4){0u, 0u, 0u, 0u};
-    }
-    __syncthreads();
-    // ---------------- phase B: unpack to code rows (natural channel order)
-    {
-      const int h = wave >> 2;
-      const int tl = 64 * (wave & 3) + lane;
-      unsigned cw[16];
+      unsigned out[8];
       if (tok0 + tl < n && B > 0) {
-        unpack_half(sPk, HW, (unsigned)tl, B, cw);
+        unpack_quarter(sCol + tid, DEC_THREADS, QP, out);
       } else {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) cw[i] = 0u;
+        for (int i = 0; i < 8; ++i) out[i] = 0u;
       }
-      u32x4* crow = reinterpret_cast<u32x4*>(sCode + tl * CROW + 64 * h);
+      unsigned* crow = reinterpret_cast<unsigned*>(sCode + tl * DCROW + 32 * q);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) crow[i] = (u32x4){cw[4 * i], cw[4 * i + 1], cw[4 * i + 2], cw[4 * i + 3]};
+      for (int i = 0; i < 8; ++i) crow[i] = out[i];
     }
+    if (tile + 1 < t_end) load_raw(tile + 1);
     __syncthreads();
-    // ---------------- phase C: MFMA reconstruction + store
+    // ---- reconstruct tokens 32*tw..+31, dims 64*dh..+63
     {
       bf16x8 bfr[2][4];
 #pragma unroll
@@ -585,12 +685,14 @@ __global__ void __launch_bounds__(DEC_THREADS, 1) k_decode_eigen(DecK a) {
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
           if (ks < ks_cnt) {
-            const u32x2 v = *reinterpret_cast<const u32x2*>(sCode + (32 * wave + 16 * nt2 + r16) * CROW + 32 * ks + 8 * g4);
-            bfr[nt2][ks] = bytes_to_bf16x8(v);
+            const unsigned* cp =
+                reinterpret_cast<const unsigned*>(sCode + (32 * tw + 16 * nt2 + r16) * DCROW + 32 * ks + 8 * g4);
+            bfr[nt2][ks] = bytes_to_bf16x8((u32x2){cp[0], cp[1]});
           }
         }
 #pragma unroll
-      for (int p = 0; p < 4; ++p) {
+      for (int pp = 0; pp < 2; ++pp) {
+        const int p = 2 * dh + pp;
         f32x4 acc[2][2];
 #pragma unroll
         for (int sI = 0; sI < 2; ++sI)
@@ -618,7 +720,7 @@ __global__ void __launch_bounds__(DEC_THREADS, 1) k_decode_eigen(DecK a) {
         const f32x4 b1 = *reinterpret_cast<const f32x4*>(hdr->bias + dbase + 4);
 #pragma unroll
         for (int nt2 = 0; nt2 < 2; ++nt2) {
-          const long long tok = tok0 + 32 * wave + 16 * nt2 + r16;
+          const long long tok = tok0 + 32 * tw + 16 * nt2 + r16;
           if (tok < n) {
             float v[8];
 #pragma unroll
@@ -645,7 +747,6 @@ __global__ void __launch_bounds__(DEC_THREADS, 1) k_decode_eigen(DecK a) {
         }
       }
     }
-    __syncthreads();
   }
 }
 
@@ -875,33 +976,40 @@ struct AttK {
   long long split_tokens, n_splits;
 };
 
-__global__ void __launch_bounds__(256) k_att_prologue(AttK a) {
-  const long long p = blockIdx.x;
+// a_hj = (U_K^T q_h)_j step_j scale log2(e), split into bf16 high and low
+// parts; one workgroup per (pair, padded head), one channel per thread.
+__global__ void __launch_bounds__(128) k_att_prologue(AttK a) {
+  const long long p = blockIdx.x >> 4;
+  const int h = blockIdx.x & 15;
+  const int j = threadIdx.x;
   const unsigned char* st = a.k_states + (size_t)state_index(a.k_map, p, a.n_states) * STATE_BYTES;
   const DevHdr* hk = reinterpret_cast<const DevHdr*>(st);
   const float* u = reinterpret_cast<const float*>(st + OFF_U32);
-  const float* q = a.q + p * a.group * 128;
   unsigned short* tab = reinterpret_cast<unsigned short*>(a.ws + p * ATT_QTAB_BYTES);
-  for (int e = threadIdx.x; e < 16 * 128; e += 256) {
-    const int h = e >> 7, j = e & 127;
-    float val = 0.0f;
-    if (h < a.group && hk->bits[j] > 0) {
-      float acc = 0.0f;
-      for (int i = 0; i < 128; ++i) acc = __builtin_fmaf(u[i * 128 + j], q[h * 128 + i], acc);
-      val = acc * hk->step32[j] * a.scale * LOG2E;
-    }
-    const __bf16 hi = (__bf16)val;
-    const __bf16 lo = (__bf16)(val - (float)hi);
-    tab[e] = __builtin_bit_cast(unsigned short, hi);
-    tab[16 * 128 + e] = __builtin_bit_cast(unsigned short, lo);
+  float val = 0.0f;
+  if (h < a.group && hk->bits[j] > 0) {
+    const float* q = a.q + (p * a.group + h) * 128;
+    float acc = 0.0f;
+#pragma unroll 8
+    for (int i = 0; i < 128; ++i) acc = __builtin_fmaf(u[i * 128 + j], q[i], acc);
+    val = acc * hk->step32[j] * a.scale * LOG2E;
   }
+  const __bf16 hi = (__bf16)val;
+  const __bf16 lo = (__bf16)(val - (float)hi);
+  tab[h * 128 + j] = __builtin_bit_cast(unsigned short, hi);
+  tab[16 * 128 + h * 128 + j] = __builtin_bit_cast(unsigned short, lo);
 }
 
-constexpr int ATT_THREADS = 256;
-constexpr int AKP = 32 * 1024 + 64;     // packed K tile bytes (max)
+constexpr int ATT_THREADS = 1024;
 constexpr int VCROW = ATT_TILE + 16;    // bytes per LDS row of transposed V codes
-constexpr int PROW = 72;                // fp16 per LDS row of P (64 tokens + pad)
-constexpr size_t ATT_LDS = 2 * (size_t)AKP + ATT_TILE * CROW + 128 * VCROW + 4 * 16 * PROW * 2;
+constexpr int PROW = 20;                // fp16 per LDS row of P (16 tokens + pad)
+constexpr size_t ATT_LDS = (size_t)ATT_TILE * CROW + 128 * VCROW + (size_t)QW_MAX * ATT_THREADS * 4 +
+                           16 * 16 * PROW * 2 + ATT_QTAB_BYTES;
+// the end-of-split merge scratch (80 KiB, then 8 x 16 x 130 floats) reuses the front of this space
+static_assert(8 * 40 * 64 * 4 <= ATT_LDS && 8 * 16 * ATT_PART_FLOATS * 4 <= ATT_LDS, "merge scratch");
+
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float grp16_max(float v) {
   v = fmaxf(v, __shfl_xor(v, 1));
@@ -918,53 +1026,64 @@ __device__ __forceinline__ float grp16_sum(float v) {
   return v;
 }
 
-__device__ __forceinline__ void load_tile_bytes(const unsigned char* src_stream, long long total_bits, long long n,
-                                                long long tt, unsigned* dst32, int tid, int nthreads) {
-  const long long P = packed_len(total_bits, n);
-  const long long start = tt * 32LL * total_bits;
-  long long nb = 32LL * total_bits;
-  if (nb > P - start) nb = P - start;
-  const u32x4* src = reinterpret_cast<const u32x4*>(src_stream + start);
-  u32x4* dst = reinterpret_cast<u32x4*>(dst32);
-  const int nchunk = (int)(nb >> 4);
-  const int zend = (int)(2 * total_bits + 2);
-  for (int i = tid; i < zend; i += nthreads) dst[i] = i < nchunk ? src[i] : (u32x4){0u, 0u, 0u, 0u};
+// 4 unsigned byte codes -> 4 fp16 (exact): 0x64xx is 1024 + xx in fp16.
+__device__ __forceinline__ f16x4 bytes_to_f16x4(unsigned v) {
+  const unsigned lo = __builtin_amdgcn_perm(v, 0x64646464u, 0x00050004u);
+  const unsigned hi = __builtin_amdgcn_perm(v, 0x64646464u, 0x00070006u);
+  const f16x2 off = {(_Float16)1024.0f, (_Float16)1024.0f};
+  const f16x2 a = __builtin_bit_cast(f16x2, lo) - off;
+  const f16x2 b = __builtin_bit_cast(f16x2, hi) - off;
+  return (f16x4){a[0], a[1], b[0], b[1]};
 }
 
+// 4x4 byte transpose across the 4 lanes of a quad: lane e holds byte c of
+// token e in byte c; afterwards lane e holds byte e of tokens 0..3.
+__device__ __forceinline__ unsigned quad_transpose_bytes(unsigned x, int e) {
+  const unsigned p1 = (unsigned)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, false);  // lane e^1
+  const unsigned y = __builtin_amdgcn_perm(p1, x, (e & 1) ? 0x03070105u : 0x06020400u);
+  const unsigned p2 = (unsigned)__builtin_amdgcn_mov_dpp((int)y, 0x4E, 0xF, 0xF, false);  // lane e^2
+  return __builtin_amdgcn_perm(p2, y, (e & 2) ? 0x03020706u : 0x05040100u);
+}
+
+// One workgroup (16 waves) per (split, pair); 256-token tiles.
+//  B: lane (token tl, quarter q) unpacks quarter q of the K record into the
+//     K code rows and quarter q of the V record, transposed across each
+//     quad of lanes, into the [channel][token] V code array.
+//  C: wave w scores tokens 16w..16w+15 (MFMA: a x K codes), updates its
+//     online softmax and accumulates P x V codes (MFMA, fp16).
+// The HBM words of the next tile are loaded while the current one computes.
+// At the end the 16 waves' (acc, m, l) are merged into the split's partial.
 __global__ void __launch_bounds__(ATT_THREADS, 1) k_att_main(AttK a) {
   extern __shared__ __align__(16) unsigned char smem[];
-  unsigned* sKp = reinterpret_cast<unsigned*>(smem);
-  unsigned* sVp = reinterpret_cast<unsigned*>(smem + AKP);
-  unsigned char* sKc = smem + 2 * AKP;
+  unsigned char* sKc = smem;
   unsigned char* sVc = sKc + ATT_TILE * CROW;
-  _Float16* sP = reinterpret_cast<_Float16*>(sVc + 128 * VCROW);
+  unsigned* sCol = reinterpret_cast<unsigned*>(sVc + 128 * VCROW);
+  _Float16* sP = reinterpret_cast<_Float16*>(sCol + QW_MAX * ATT_THREADS);
+  unsigned char* sA = reinterpret_cast<unsigned char*>(sP + 16 * 16 * PROW);  // a hi [16][128], lo [16][128]
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r16 = lane & 15, g4 = lane >> 4;
+  const int tl = tid & 255, q = wave >> 2;
   const long long sp = blockIdx.x, p = blockIdx.y;
   const long long n = a.n_tokens;
   const unsigned char* kst = a.k_states + (size_t)state_index(a.k_map, p, a.n_states) * STATE_BYTES;
   const unsigned char* vst = a.v_states + (size_t)state_index(a.v_map, p, a.n_states) * STATE_BYTES;
   const DevHdr* hk = reinterpret_cast<const DevHdr*>(kst);
   const DevHdr* hv = reinterpret_cast<const DevHdr*>(vst);
-  const int Bk = hk->total_bits, Bv = hv->total_bits;
+  const unsigned long long Bk = (unsigned)hk->total_bits, Bv = (unsigned)hv->total_bits;
   const int ksK = hk->kmax32 >> 5;
   const int ntV = hv->nmax16 >> 4;
-  const unsigned char* kpk = a.k_packed + p * a.packed_stride;
-  const unsigned char* vpk = a.v_packed + p * a.packed_stride;
-  const HalfW KW0 = load_half_widths(hk, 0), KW1 = load_half_widths(hk, 1);
-  const HalfW VW0 = load_half_widths(hv, 0), VW1 = load_half_widths(hv, 1);
+  const QPlan QK = load_qplan(hk, q), QV = load_qplan(hv, q);
+  const unsigned* gk = reinterpret_cast<const unsigned*>(a.k_packed + p * a.packed_stride);
+  const unsigned* gv = reinterpret_cast<const unsigned*>(a.v_packed + p * a.packed_stride);
+  const unsigned long long sdwK = (unsigned long long)packed_len((long long)Bk, n) >> 2;
+  const unsigned long long sdwV = (unsigned long long)packed_len((long long)Bv, n) >> 2;
 
-  // score A operand: a (bf16 hi/lo), rows = query heads (padded to 16)
-  bf16x8 ahi[4], alo[4];
+  // score A operand: a (bf16 hi/lo), rows = query heads (padded to 16), staged in LDS
   {
-    const unsigned short* tab = reinterpret_cast<const unsigned short*>(a.ws + p * ATT_QTAB_BYTES);
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      ahi[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(tab + r16 * 128 + 32 * ks + 8 * g4));
-      alo[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(tab + 2048 + r16 * 128 + 32 * ks + 8 * g4));
-    }
+    const u32x4* tab = reinterpret_cast<const u32x4*>(a.ws + p * ATT_QTAB_BYTES);
+    for (int i = tid; i < (int)(ATT_QTAB_BYTES / 16); i += ATT_THREADS) reinterpret_cast<u32x4*>(sA)[i] = tab[i];
   }
   float m_run[4], l_run[4];
   f32x4 acc_o[8];
@@ -977,103 +1096,134 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_att_main(AttK a) {
   long long t_end = t_begin + a.split_tokens;
   if (t_end > n) t_end = n;
 
+  unsigned rawk[QW_MAX + 1] = {}, rawv[QW_MAX + 1] = {};
+  unsigned shk = 0, shv = 0;
+  auto load_raw = [&](long long tok0) {
+    const unsigned long long tg = (unsigned long long)(tok0 + tl);
+    const bool ok = (long long)tg < t_end;
+    const unsigned long long SK = tg * Bk + QK.off, SV = tg * Bv + QV.off;
+    shk = (unsigned)(SK & 31u);
+    shv = (unsigned)(SV & 31u);
+    if (Bk) load_quarter_raw(gk, SK >> 5, sdwK, ok, QK.nw, rawk);
+    if (Bv) load_quarter_raw(gv, SV >> 5, sdwV, ok, QV.nw, rawv);
+  };
+  if (t_begin < t_end) load_raw(t_begin);
+
   for (long long tok0 = t_begin; tok0 < t_end; tok0 += ATT_TILE) {
-    const long long tt = tok0 / ATT_TILE;
-    if (Bk > 0) load_tile_bytes(kpk, Bk, n, tt, sKp, tid, ATT_THREADS);
-    if (Bv > 0) load_tile_bytes(vpk, Bv, n, tt, sVp, tid, ATT_THREADS);
-    __syncthreads();
-    // unpack one token per thread
+    const bool valid = tok0 + tl < t_end;
+    __syncthreads();  // previous tile's compute is done with the code arrays
+    // ---- B: unpack this lane's K and V quarter records
     {
-      const int tl = tid;
-      const bool valid = tok0 + tl < t_end;
+      unsigned out[8];
+      stage_quarter(rawk, shk, QK.nw, sCol + tid, ATT_THREADS);
+      if (valid && Bk) unpack_quarter(sCol + tid, ATT_THREADS, QK, out);
+      else {
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        unsigned cw[16];
-        if (valid && Bk > 0) unpack_half(sKp, h ? KW1 : KW0, (unsigned)tl, Bk, cw);
-        else {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) cw[i] = 0u;
-        }
-        u32x4* krow = reinterpret_cast<u32x4*>(sKc + tl * CROW + 64 * h);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) krow[i] = (u32x4){cw[4 * i], cw[4 * i + 1], cw[4 * i + 2], cw[4 * i + 3]};
+        for (int i = 0; i < 8; ++i) out[i] = 0u;
       }
+      u32x4* krow = reinterpret_cast<u32x4*>(sKc + tl * CROW + 32 * q);
+      krow[0] = (u32x4){out[0], out[1], out[2], out[3]};
+      krow[1] = (u32x4){out[4], out[5], out[6], out[7]};
+      stage_quarter(rawv, shv, QV.nw, sCol + tid, ATT_THREADS);
+      if (valid && Bv) unpack_quarter(sCol + tid, ATT_THREADS, QV, out);
+      else {
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        unsigned cw[16];
-        if (valid && Bv > 0) unpack_half(sVp, h ? VW1 : VW0, (unsigned)tl, Bv, cw);
-        else {
+        for (int i = 0; i < 8; ++i) out[i] = 0u;
+      }
+      const int e = tl & 3;
 #pragma unroll
-          for (int i = 0; i < 16; ++i) cw[i] = 0u;
-        }
-#pragma unroll
-        for (int jj = 0; jj < 64; ++jj) sVc[(64 * h + jj) * VCROW + tl] = (unsigned char)((cw[jj >> 2] >> (8 * (jj & 3))) & 0xffu);
+      for (int i = 0; i < 8; ++i) {
+        const unsigned t4 = quad_transpose_bytes(out[i], e);
+        *reinterpret_cast<unsigned*>(sVc + (32 * q + 4 * i + e) * VCROW + (tl & ~3)) = t4;
       }
     }
+    if (tok0 + ATT_TILE < t_end) load_raw(tok0 + ATT_TILE);
     __syncthreads();
-    // scores for this wave's 64 tokens
-    f32x4 sc[4];
+    // ---- C: scores for tokens 16*wave..+15
+    f32x4 sc = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      sc[nt] = (f32x4){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        if (ks < ksK) {
-          const u32x2 v = *reinterpret_cast<const u32x2*>(sKc + (64 * wave + 16 * nt + r16) * CROW + 32 * ks + 8 * g4);
-          const bf16x8 b = bytes_to_bf16x8(v);
-          sc[nt] = mfma_bf16(ahi[ks], b, sc[nt]);
-          sc[nt] = mfma_bf16(alo[ks], b, sc[nt]);
-        }
+    for (int ks = 0; ks < 4; ++ks) {
+      if (ks < ksK) {
+        const u32x2 v = *reinterpret_cast<const u32x2*>(sKc + (16 * wave + r16) * CROW + 32 * ks + 8 * g4);
+        const bf16x8 b = bytes_to_bf16x8(v);
+        const bf16x8 ah = *reinterpret_cast<const bf16x8*>(sA + (r16 * 128 + 32 * ks + 8 * g4) * 2);
+        const bf16x8 al = *reinterpret_cast<const bf16x8*>(sA + 4096 + (r16 * 128 + 32 * ks + 8 * g4) * 2);
+        sc = mfma_bf16(ah, b, sc);
+        sc = mfma_bf16(al, b, sc);
       }
-      const long long tok = tok0 + 64 * wave + 16 * nt + r16;
-      if (tok >= t_end) sc[nt] = (f32x4){-INFINITY, -INFINITY, -INFINITY, -INFINITY};
     }
-    // online softmax (per wave); lane rows are heads 4*g4 + r
+    if (tok0 + 16 * wave + r16 >= t_end) sc = (f32x4){-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    // online softmax; lane rows are heads 4*g4 + r, column = token r16
     _Float16* myP = sP + wave * 16 * PROW;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      float mt = fmaxf(fmaxf(sc[0][r], sc[1][r]), fmaxf(sc[2][r], sc[3][r]));
-      mt = grp16_max(mt);
+      const float mt = grp16_max(sc[r]);
       const float mnew = fmaxf(m_run[r], mt);
       const float alpha = (mnew == -INFINITY) ? 1.0f : exp2f(m_run[r] - mnew);
-      float ls = 0.0f;
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        const float pv = (mnew == -INFINITY) ? 0.0f : exp2f(sc[nt][r] - mnew);
-        const _Float16 ph = (_Float16)pv;
-        ls += (float)ph;
-        myP[(4 * g4 + r) * PROW + 16 * nt + r16] = ph;
-      }
-      l_run[r] = l_run[r] * alpha + ls;
+      const float pv = (mnew == -INFINITY) ? 0.0f : exp2f(sc[r] - mnew);
+      const _Float16 ph = (_Float16)pv;
+      l_run[r] = l_run[r] * alpha + (float)ph;
       m_run[r] = mnew;
+      myP[(4 * g4 + r) * PROW + r16] = ph;
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc_o[i][r] *= alpha;
     }
-    __syncthreads();
-    // P x V codes
-#pragma unroll
-    for (int ks2 = 0; ks2 < 2; ++ks2) {
-      const f16x8 pa = *reinterpret_cast<const f16x8*>(myP + r16 * PROW + 32 * ks2 + 8 * g4);
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's P writes have landed
+    __builtin_amdgcn_wave_barrier();
+    // P (heads x 16 tokens) x V codes (16 tokens x channels)
+    {
+      const f16x4 pa = *reinterpret_cast<const f16x4*>(myP + r16 * PROW + 4 * g4);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         if (i < ntV) {
-          const u32x2 v = *reinterpret_cast<const u32x2*>(sVc + (16 * i + r16) * VCROW + 64 * wave + 32 * ks2 + 8 * g4);
-          acc_o[i] = mfma_f16(pa, bytes_to_f16x8(v), acc_o[i]);
+          const unsigned v = *reinterpret_cast<const unsigned*>(sVc + (16 * i + r16) * VCROW + 16 * wave + 4 * g4);
+          acc_o[i] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, bytes_to_f16x4(v), acc_o[i], 0, 0, 0);
         }
+      }
+    }
+  }
+  __syncthreads();
+  // fold waves 8..15 into waves 0..7 (same lane positions), through LDS:
+  // [8 waves][40 values][64 lanes] = 80 KiB over the code arrays
+  {
+    float* xs = reinterpret_cast<float*>(smem) + (wave & 7) * 40 * 64 + lane;
+    if (wave >= 8) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        xs[r * 64] = m_run[r];
+        xs[(4 + r) * 64] = l_run[r];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) xs[(8 + 4 * i + r) * 64] = acc_o[i][r];
+      }
+    }
+    __syncthreads();
+    if (wave < 8) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float m2 = xs[r * 64];
+        const float mnew = fmaxf(m_run[r], m2);
+        const float f1 = (m_run[r] == -INFINITY) ? 0.0f : exp2f(m_run[r] - mnew);
+        const float f2 = (m2 == -INFINITY) ? 0.0f : exp2f(m2 - mnew);
+        l_run[r] = l_run[r] * f1 + xs[(4 + r) * 64] * f2;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc_o[i][r] = acc_o[i][r] * f1 + xs[(8 + 4 * i + r) * 64] * f2;
+        m_run[r] = mnew;
       }
     }
     __syncthreads();
   }
-  // merge the four waves: reuse the K code rows as scratch
-  float* red = reinterpret_cast<float*>(sKc);  // [4 waves][16 heads][130]
+  // merge the eight remaining waves: scratch [8 waves][16 heads][130]
+  float* red = reinterpret_cast<float*>(smem);
+  if (wave < 8) {
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const float lsum = grp16_sum(l_run[r]);
-    const int hrow = 4 * g4 + r;
-    float* base = red + (wave * 16 + hrow) * ATT_PART_FLOATS;
+    for (int r = 0; r < 4; ++r) {
+      const float lsum = grp16_sum(l_run[r]);
+      const int hrow = 4 * g4 + r;
+      float* base = red + (wave * 16 + hrow) * ATT_PART_FLOATS;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) base[16 * i + r16] = acc_o[i][r];
-    if (r16 == 0) { base[128] = m_run[r]; base[129] = lsum; }
+      for (int i = 0; i < 8; ++i) base[16 * i + r16] = acc_o[i][r];
+      if (r16 == 0) { base[128] = m_run[r]; base[129] = lsum; }
+    }
   }
   __syncthreads();
   float* part = reinterpret_cast<float*>(a.ws + a.n_pairs * ATT_QTAB_BYTES) +
@@ -1082,10 +1232,10 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_att_main(AttK a) {
     const int h = e >> 7, j = e & 127;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, red[(w * 16 + h) * ATT_PART_FLOATS + 128]);
+    for (int w = 0; w < 8; ++w) M = fmaxf(M, red[(w * 16 + h) * ATT_PART_FLOATS + 128]);
     float A = 0.0f, Ls = 0.0f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < 8; ++w) {
       const float mw = red[(w * 16 + h) * ATT_PART_FLOATS + 128];
       const float f = (mw == -INFINITY) ? 0.0f : exp2f(mw - M);
       A += f * red[(w * 16 + h) * ATT_PART_FLOATS + j];
@@ -1097,13 +1247,17 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_att_main(AttK a) {
 }
 
 // One workgroup per (pair, query head): merge the splits' (acc, m, l) with
-// log-sum-exp weights (fp32 weights, fp64 sums), take the softmax-weighted
-// mean code of every V channel, dequantize it and rotate back with U_V.
-__global__ void __launch_bounds__(128) k_att_combine(AttK a) {
+// log-sum-exp weights (fp32 weights, fp64 sums; 4 groups of threads take
+// every 4th split), take the softmax-weighted mean code of every V channel,
+// dequantize it and rotate back with U_V.
+__global__ void __launch_bounds__(512) k_att_combine(AttK a) {
+  __shared__ float red_m[4];
+  __shared__ double red_a[4][128];
+  __shared__ double red_l[4];
   __shared__ float chat[128];
   const long long p = blockIdx.x / a.group;
   const int h = (int)(blockIdx.x - p * a.group);
-  const int j = threadIdx.x;
+  const int j = threadIdx.x & 127, grp = threadIdx.x >> 7;
   const unsigned char* vst = a.v_states + (size_t)state_index(a.v_map, p, a.n_states) * STATE_BYTES;
   const DevHdr* hv = reinterpret_cast<const DevHdr*>(vst);
   const float* u = reinterpret_cast<const float*>(vst + OFF_U32);
@@ -1111,21 +1265,33 @@ __global__ void __launch_bounds__(128) k_att_combine(AttK a) {
                      ((p * a.n_splits) * a.group + h) * ATT_PART_FLOATS;
   const long long sstride = (long long)a.group * ATT_PART_FLOATS;
   float M = -INFINITY;
-  for (long long s = 0; s < a.n_splits; ++s) M = fmaxf(M, ps0[s * sstride + 128]);
+  for (long long s = grp; s < a.n_splits; s += 4) M = fmaxf(M, ps0[s * sstride + 128]);
+  if (j == 0) red_m[grp] = M;
+  __syncthreads();
+  M = fmaxf(fmaxf(red_m[0], red_m[1]), fmaxf(red_m[2], red_m[3]));
   double A = 0.0, L = 0.0;
-  for (long long s = 0; s < a.n_splits; ++s) {
+  for (long long s = grp; s < a.n_splits; s += 4) {
     const float* ps = ps0 + s * sstride;
     const float ms = ps[128];
     const float f = (ms == -INFINITY) ? 0.0f : exp2f(ms - M);
     A += (double)(f * ps[j]);
     L += (double)(f * ps[129]);
   }
-  chat[j] = hv->bits[j] ? (float)((double)hv->step32[j] * (A / L - (double)hv->halfspan[j])) : 0.0f;
+  red_a[grp][j] = A;
+  if (j == 0) red_l[grp] = L;
   __syncthreads();
-  float o = 0.0f;
+  if (grp == 0) {
+    A = (red_a[0][j] + red_a[1][j]) + (red_a[2][j] + red_a[3][j]);
+    L = (red_l[0] + red_l[1]) + (red_l[2] + red_l[3]);
+    chat[j] = hv->bits[j] ? (float)((double)hv->step32[j] * (A / L - (double)hv->halfspan[j])) : 0.0f;
+  }
+  __syncthreads();
+  if (grp == 0) {
+    float o = 0.0f;
 #pragma unroll 8
-  for (int k = 0; k < 128; ++k) o = __builtin_fmaf(u[j * 128 + k], chat[k], o);
-  a.out[(p * a.group + h) * 128 + j] = o;
+    for (int k = 0; k < 128; ++k) o = __builtin_fmaf(u[j * 128 + k], chat[k], o);
+    a.out[(p * a.group + h) * 128 + j] = o;
+  }
 }
 
 int launch_attend(const AttendLaunch& L, void* stream) {
@@ -1152,9 +1318,9 @@ int launch_attend(const AttendLaunch& L, void* stream) {
   a.split_tokens = att_split_tokens(L.n_pairs, L.n_tokens);
   a.n_splits = att_n_splits(L.n_pairs, L.n_tokens);
   hipStream_t s = (hipStream_t)stream;
-  hipLaunchKernelGGL(k_att_prologue, dim3((unsigned)L.n_pairs), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(k_att_prologue, dim3((unsigned)(L.n_pairs * 16)), dim3(128), 0, s, a);
   hipLaunchKernelGGL(k_att_main, dim3((unsigned)a.n_splits, (unsigned)L.n_pairs), dim3(ATT_THREADS), ATT_LDS, s, a);
-  hipLaunchKernelGGL(k_att_combine, dim3((unsigned)(L.n_pairs * L.group)), dim3(128), 0, s, a);
+  hipLaunchKernelGGL(k_att_combine, dim3((unsigned)(L.n_pairs * L.group)), dim3(512), 0, s, a);
   return hipGetLastError() != hipSuccess;
 }
 
