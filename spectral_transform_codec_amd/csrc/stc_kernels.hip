@@ -690,14 +690,14 @@ __global__ void __launch_bounds__(DEC_THREADS, 1) k_decode_eigen(DecK a) {
             bfr[nt2][ks] = bytes_to_bf16x8((u32x2){cp[0], cp[1]});
           }
         }
+      f32x4 acc[2][2][2];  // [pp][sI][nt2]
 #pragma unroll
       for (int pp = 0; pp < 2; ++pp) {
         const int p = 2 * dh + pp;
-        f32x4 acc[2][2];
 #pragma unroll
         for (int sI = 0; sI < 2; ++sI)
 #pragma unroll
-          for (int nt2 = 0; nt2 < 2; ++nt2) acc[sI][nt2] = (f32x4){0.f, 0.f, 0.f, 0.f};
+          for (int nt2 = 0; nt2 < 2; ++nt2) acc[pp][sI][nt2] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int sI = 0; sI < 2; ++sI) {
           const int mt = 2 * p + sI;
@@ -709,41 +709,64 @@ __global__ void __launch_bounds__(DEC_THREADS, 1) k_decode_eigen(DecK a) {
               const bf16x8 wl = *reinterpret_cast<const bf16x8*>(sWlo + off);
 #pragma unroll
               for (int nt2 = 0; nt2 < 2; ++nt2) {
-                acc[sI][nt2] = mfma_bf16(wh, bfr[nt2][ks], acc[sI][nt2]);
-                acc[sI][nt2] = mfma_bf16(wl, bfr[nt2][ks], acc[sI][nt2]);
+                acc[pp][sI][nt2] = mfma_bf16(wh, bfr[nt2][ks], acc[pp][sI][nt2]);
+                acc[pp][sI][nt2] = mfma_bf16(wl, bfr[nt2][ks], acc[pp][sI][nt2]);
               }
             }
           }
         }
-        const int dbase = 32 * p + 8 * g4;
-        const f32x4 b0 = *reinterpret_cast<const f32x4*>(hdr->bias + dbase);
-        const f32x4 b1 = *reinterpret_cast<const f32x4*>(hdr->bias + dbase + 4);
+      }
+      // lane (g4, r16) holds, for token 16*nt2 + r16 of its group, dims
+      // 32p + 8g4 + 0..7 for p = 2dh (chunk A) and p = 2dh + 1 (chunk B).
+      float bias8[2][8];
 #pragma unroll
-        for (int nt2 = 0; nt2 < 2; ++nt2) {
+      for (int pp = 0; pp < 2; ++pp) {
+        const f32x4 b0 = *reinterpret_cast<const f32x4*>(hdr->bias + 32 * (2 * dh + pp) + 8 * g4);
+        const f32x4 b1 = *reinterpret_cast<const f32x4*>(hdr->bias + 32 * (2 * dh + pp) + 8 * g4 + 4);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) { bias8[pp][r] = b0[r]; bias8[pp][4 + r] = b1[r]; }
+      }
+#pragma unroll
+      for (int nt2 = 0; nt2 < 2; ++nt2) {
+        if (F32OUT) {
           const long long tok = tok0 + 32 * tw + 16 * nt2 + r16;
           if (tok < n) {
-            float v[8];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              v[r] = acc[0][nt2][r] - b0[r];
-              v[4 + r] = acc[1][nt2][r] - b1[r];
-            }
-            if (F32OUT) {
-              float* o = static_cast<float*>(a.x) + s * a.x_stride + tok * a.ld + dbase;
-              *reinterpret_cast<f32x4*>(o) = (f32x4){v[0], v[1], v[2], v[3]};
-              *reinterpret_cast<f32x4*>(o + 4) = (f32x4){v[4], v[5], v[6], v[7]};
-            } else {
-              unsigned short* o = static_cast<unsigned short*>(a.x) + s * a.x_stride + tok * a.ld + dbase;
-              u32x4 w;
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                const unsigned lo = __builtin_bit_cast(unsigned short, (__bf16)v[2 * e]);
-                const unsigned hi = __builtin_bit_cast(unsigned short, (__bf16)v[2 * e + 1]);
-                w[e] = lo | (hi << 16);
-              }
-              *reinterpret_cast<u32x4*>(o) = w;
+            for (int pp = 0; pp < 2; ++pp) {
+              float* o = static_cast<float*>(a.x) + s * a.x_stride + tok * a.ld + 32 * (2 * dh + pp) + 8 * g4;
+              *reinterpret_cast<f32x4*>(o) = (f32x4){acc[pp][0][nt2][0] - bias8[pp][0], acc[pp][0][nt2][1] - bias8[pp][1],
+                                                     acc[pp][0][nt2][2] - bias8[pp][2], acc[pp][0][nt2][3] - bias8[pp][3]};
+              *reinterpret_cast<f32x4*>(o + 4) = (f32x4){acc[pp][1][nt2][0] - bias8[pp][4], acc[pp][1][nt2][1] - bias8[pp][5],
+                                                         acc[pp][1][nt2][2] - bias8[pp][6], acc[pp][1][nt2][3] - bias8[pp][7]};
             }
           }
+        } else {
+          // bf16: chunk A/B = 8 dims = 16 bytes. Lanes r16 and r16^1 swap so
+          // that each store instruction writes whole 128-byte rows of 8 tokens:
+          // first the even tokens (even lane: own A, odd lane: partner's B),
+          // then the odd tokens (even lane: partner's A, odd lane: own B).
+          u32x4 ch[2];
+#pragma unroll
+          for (int pp = 0; pp < 2; ++pp)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int sI = e >> 1, r = 2 * (e & 1);
+              const float v0 = acc[pp][sI][nt2][r] - bias8[pp][2 * e];
+              const float v1 = acc[pp][sI][nt2][r + 1] - bias8[pp][2 * e + 1];
+              ch[pp][e] = (unsigned)__builtin_bit_cast(unsigned short, (__bf16)v0) |
+                          ((unsigned)__builtin_bit_cast(unsigned short, (__bf16)v1) << 16);
+            }
+          const bool odd = r16 & 1;
+          u32x4 recv;
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            recv[e] = (unsigned)__builtin_amdgcn_mov_dpp((int)(odd ? ch[0][e] : ch[1][e]), 0xB1, 0xF, 0xF, false);
+          const long long tokA = tok0 + 32 * tw + 16 * nt2 + (r16 & ~1);
+          const long long tokB = tokA + 1;
+          unsigned short* oA = static_cast<unsigned short*>(a.x) + s * a.x_stride + tokA * a.ld + 64 * dh + 8 * g4;
+          unsigned short* oB = static_cast<unsigned short*>(a.x) + s * a.x_stride + tokB * a.ld + 64 * dh + 8 * g4;
+          if (tokA < n) *reinterpret_cast<u32x4*>(oA + (odd ? 32 : 0)) = odd ? recv : ch[0];
+          if (tokB < n) *reinterpret_cast<u32x4*>(oB + (odd ? 32 : 0)) = odd ? ch[1] : recv;
         }
       }
     }
@@ -861,53 +884,72 @@ __global__ void __launch_bounds__(256) k_rht_encode(RhtK a) {
   a.norms[s * a.n_tokens + tok] = nu;
 }
 
-__global__ void __launch_bounds__(256) k_rht_decode(RhtK a) {
+// 128 tokens per workgroup; the reconstructed rows go through LDS so that the
+// HBM stores are whole consecutive rows (per-lane row stores leave cache
+// lines partly written and multiply the write traffic).
+constexpr int RHTD_T = 128;
+__global__ void __launch_bounds__(RHTD_T) k_rht_decode(RhtK a) {
+  extern __shared__ __align__(16) unsigned char smem[];
   __shared__ float scb[8];
   const long long s = blockIdx.y;
+  const int t = threadIdx.x;
   const DevHdr* hdr =
       reinterpret_cast<const DevHdr*>(a.states + (size_t)state_index(a.map, s, a.n_states) * STATE_BYTES);
-  if (threadIdx.x < 8) scb[threadIdx.x] = hdr->cb[threadIdx.x];
+  if (t < 8) scb[t] = hdr->cb[t];
   __syncthreads();
-  const long long tok = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (tok >= a.n_tokens) return;
-  const u32x4* src = reinterpret_cast<const u32x4*>(a.packed_in + s * a.packed_stride + tok * 48);
-  unsigned w[12];
-  {
-    const u32x4 w0 = src[0], w1 = src[1], w2 = src[2];
+  const long long tok0 = (long long)blockIdx.x * RHTD_T;
+  const long long tok = tok0 + t;
+  const int rowb = a.f32out ? 512 + 16 : 256 + 16;  // LDS row bytes
+  if (tok < a.n_tokens) {
+    const u32x4* src = reinterpret_cast<const u32x4*>(a.packed_in + s * a.packed_stride + tok * 48);
+    unsigned w[12];
+    {
+      const u32x4 w0 = src[0], w1 = src[1], w2 = src[2];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) { w[e] = w0[e]; w[4 + e] = w1[e]; w[8 + e] = w2[e]; }
-  }
-  float v[128];
-#pragma unroll
-  for (int i = 0; i < 128; ++i) {
-    const int bp = 3 * i;
-    unsigned q = w[bp >> 5] >> (bp & 31);
-    if ((bp & 31) > 29) q |= w[(bp >> 5) + 1] << (32 - (bp & 31));
-    v[i] = scb[q & 7u];
-  }
-  fwht128(v);
-  const float m = a.norms_in[s * a.n_tokens + tok] * 0.08838834764831845f;  // |x| / sqrt(128)
-  if (a.f32out) {
-    float* o = static_cast<float*>(a.xo) + s * a.x_stride + tok * a.ld;
-#pragma unroll
-    for (int c = 0; c < 32; ++c)
-      *reinterpret_cast<f32x4*>(o + 4 * c) =
-          (f32x4){v[4 * c] * m * hdr->sign[4 * c], v[4 * c + 1] * m * hdr->sign[4 * c + 1],
-                  v[4 * c + 2] * m * hdr->sign[4 * c + 2], v[4 * c + 3] * m * hdr->sign[4 * c + 3]};
-  } else {
-    unsigned short* o = static_cast<unsigned short*>(a.xo) + s * a.x_stride + tok * a.ld;
-#pragma unroll
-    for (int c = 0; c < 16; ++c) {
-      u32x4 pk;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int i = 8 * c + 2 * e;
-        const unsigned lo = __builtin_bit_cast(unsigned short, (__bf16)(v[i] * m * hdr->sign[i]));
-        const unsigned hi = __builtin_bit_cast(unsigned short, (__bf16)(v[i + 1] * m * hdr->sign[i + 1]));
-        pk[e] = lo | (hi << 16);
-      }
-      *reinterpret_cast<u32x4*>(o + 8 * c) = pk;
+      for (int e = 0; e < 4; ++e) { w[e] = w0[e]; w[4 + e] = w1[e]; w[8 + e] = w2[e]; }
     }
+    float v[128];
+#pragma unroll
+    for (int i = 0; i < 128; ++i) {
+      const int bp = 3 * i;
+      unsigned q = w[bp >> 5] >> (bp & 31);
+      if ((bp & 31) > 29) q |= w[(bp >> 5) + 1] << (32 - (bp & 31));
+      v[i] = scb[q & 7u];
+    }
+    fwht128(v);
+    const float m = a.norms_in[s * a.n_tokens + tok] * 0.08838834764831845f;  // |x| / sqrt(128)
+    unsigned char* row = smem + t * rowb;
+    if (a.f32out) {
+#pragma unroll
+      for (int c = 0; c < 32; ++c)
+        *reinterpret_cast<f32x4*>(row + 16 * c) =
+            (f32x4){v[4 * c] * m * hdr->sign[4 * c], v[4 * c + 1] * m * hdr->sign[4 * c + 1],
+                    v[4 * c + 2] * m * hdr->sign[4 * c + 2], v[4 * c + 3] * m * hdr->sign[4 * c + 3]};
+    } else {
+#pragma unroll
+      for (int c = 0; c < 16; ++c) {
+        u32x4 pk;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 8 * c + 2 * e;
+          const unsigned lo = __builtin_bit_cast(unsigned short, (__bf16)(v[i] * m * hdr->sign[i]));
+          const unsigned hi = __builtin_bit_cast(unsigned short, (__bf16)(v[i + 1] * m * hdr->sign[i + 1]));
+          pk[e] = lo | (hi << 16);
+        }
+        *reinterpret_cast<u32x4*>(row + 16 * c) = pk;
+      }
+    }
+  }
+  __syncthreads();
+  // whole rows out: consecutive threads take consecutive 16-byte chunks of a row
+  const int cpr = a.f32out ? 32 : 16;
+  const long long ntok = (a.n_tokens - tok0) < RHTD_T ? (a.n_tokens - tok0) : RHTD_T;
+  const int esz = a.f32out ? 4 : 2;
+  unsigned char* obase = static_cast<unsigned char*>(a.xo) + (s * a.x_stride + tok0 * a.ld) * esz;
+  for (int i = t; i < ntok * cpr; i += RHTD_T) {
+    const int r = i / cpr, c = i - r * cpr;
+    *reinterpret_cast<u32x4*>(obase + ((long long)r * a.ld) * esz + 16 * c) =
+        *reinterpret_cast<const u32x4*>(smem + r * rowb + 16 * c);
   }
 }
 
@@ -941,8 +983,15 @@ int launch_decode_rht(const DecodeLaunch& L, void* stream) {
   a.norms_in = L.norms;
   a.xo = L.x;
   a.f32out = L.f32out;
-  dim3 grid((unsigned)((L.n_tokens + 255) / 256), (unsigned)L.n_streams);
-  hipLaunchKernelGGL(k_rht_decode, grid, dim3(256), 0, (hipStream_t)stream, a);
+  dim3 grid((unsigned)((L.n_tokens + RHTD_T - 1) / RHTD_T), (unsigned)L.n_streams);
+  const size_t lds = (size_t)RHTD_T * (L.f32out ? 512 + 16 : 256 + 16);
+  static bool attr = false;
+  if (!attr) {
+    (void)hipFuncSetAttribute((const void*)k_rht_decode, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              RHTD_T * (512 + 16));
+    attr = true;
+  }
+  hipLaunchKernelGGL(k_rht_decode, grid, dim3(RHTD_T), lds, (hipStream_t)stream, a);
   return hipGetLastError() != hipSuccess;
 }
 
