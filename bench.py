@@ -39,7 +39,60 @@ def parse():
     ap.add_argument("--tokens", type=int, default=None, help="override tokens per stream (testing only)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="before the workload, copy a buffer of this many MiB three times (untimed): "
+                         "the reference kernel for scaling the FETCH_SIZE / WRITE_SIZE counters")
+    ap.add_argument("--summarize", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"), default=None,
+                    help="no GPU work: turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of "
+                         "`bench.py --copy-mib N` into a traffic summary for --kernel")
+    ap.add_argument("--summarize-trace", metavar="TRACE_DIR", default=None,
+                    help="no GPU work: print the kernel statistics of a rocprofv3 --kernel-trace --stats run")
+    ap.add_argument("--kernel", default=None, help="kernel name prefix for --summarize")
+    ap.add_argument("--command", default="", help="command line recorded in a summary")
     return ap.parse_args()
+
+
+# Kernel launched by each timed op that is a single kernel; the roofline is
+# reported for the kernel with the largest share of the step.
+KERNEL_OF_OP = {"encode": "k_encode_eigen<bf16>", "decode": "k_decode_eigen<bf16>",
+                "rht_encode": "k_rht_encode", "rht_decode": "k_rht_decode"}
+# rocprofv3 kernel names of the same kernels
+PROFILE_NAME = {"k_encode_eigen<bf16>": "void stc::k_encode_eigen<0>(stc::EncK)",
+                "k_decode_eigen<bf16>": "void stc::k_decode_eigen<0>(stc::DecK)",
+                "k_rht_encode": "stc::k_rht_encode(stc::RhtK)",
+                "k_rht_decode": "stc::k_rht_decode(stc::RhtK)"}
+KERNEL_SOURCE = os.path.join(ROOT, "spectral_transform_codec_amd", "csrc", "stc_kernels.hip")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def kernel_of(op_name):
+    base = op_name.split("@")[0]
+    return KERNEL_OF_OP.get(base)
+
+
+def source_digest():
+    import hashlib
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def stored_traffic(kernel):
+    """HBM bytes per launch of `kernel` from a committed counter summary, or
+    None if there is none or the kernel source changed since it was taken."""
+    path = os.path.join(PROFILES, "traffic_" + kernel.replace("<", "_").replace(">", "") + "_cfg2.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line and not line.startswith(" "):
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256_16") != source_digest():
+        return None
+    try:
+        return float(vals["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def algorithmic_bytes(total_bits, n, streams, elem=2):
@@ -49,6 +102,9 @@ def algorithmic_bytes(total_bits, n, streams, elem=2):
 
 def main():
     args = parse()
+    if args.summarize or args.summarize_trace:
+        summarize(args)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py: this build runs on one GPU only (no collectives or sharding); "
               "run it with --gpus 1", file=sys.stderr)
@@ -126,6 +182,13 @@ def main():
                 S * n * (256 + 48 + 4)))
 
     stream = torch.cuda.current_stream()
+    if args.copy_mib:
+        src = torch.ones(args.copy_mib << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for _ in range(args.warmup):
         for _, fn, _ in ops:
             fn()
@@ -157,10 +220,21 @@ def main():
                         "bytes": int(nbytes)}
     step_bytes = sum(o[2] for o in ops)
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
-    dominant = max(ops, key=lambda o: per_op[o[0]]["ms"])
-    dname = dominant[0]
-    d_ms = per_op[dname]["ms"]
-    achieved = dominant[2] / (d_ms * 1e-3) / 1e9
+    # roofline of the single-kernel op family with the largest time share:
+    # algorithmic bytes per launch / average launch duration (HIP events on
+    # the launch stream), averaged over the family's launches in a step
+    fam = {}
+    for name, _, nbytes in ops:
+        kname = kernel_of(name)
+        if kname:
+            t = fam.setdefault(kname, [0.0, 0.0, 0])
+            t[0] += per_op[name]["ms"]
+            t[1] += nbytes
+            t[2] += 1
+    dname = max(fam, key=lambda k: fam[k][0])
+    d_ms, d_bytes, d_n = fam[dname]
+    achieved = d_bytes / (d_ms * 1e-3) / 1e9
+    traffic = stored_traffic(dname)
     codec_names = [o[0] for o in ops if o[0].startswith(("encode", "decode"))]
     codec_bytes = sum(o[2] for o in ops if o[0] in codec_names)
     codec_ms = sum(per_op[nm]["ms"] for nm in codec_names)
@@ -193,13 +267,113 @@ def main():
         "codec_GBps": round(codec_bytes / (codec_ms * 1e-3) / 1e9, 1),
         "attn_tokens_per_s": {nm: round(1e3 / per_op[nm]["ms"], 1) for nm in attn_names},
         "breakdown": per_op,
-        "roofline": {"bound": "hbm", "kernel": dname, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None},
+        "roofline": {"bound": "hbm", "kernel": dname, "launches_per_step": d_n,
+                     "algorithmic_bytes_per_launch": int(d_bytes / d_n),
+                     "avg_launch_us": round(1e3 * d_ms / d_n, 2),
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": None if traffic is None else int(traffic)},
         "cpu_baseline": cpu,
         "setup_s": round(setup_s, 2),
         "calibrate_s": round(cal_s, 2),
     }
     print(json.dumps(line), flush=True)
+
+
+def _profile_rows(d, want_counters):
+    """(kernel name, dispatch id, value) rows of a rocprofv3 output folder:
+    counter values of a --pmc run, or durations (ns) of a kernel trace. Reads
+    the rocpd database, or the CSV files when that is what the run wrote."""
+    import csv
+    import glob
+    import sqlite3
+    dbs = sorted(glob.glob(os.path.join(d, "**", "*.db"), recursive=True))
+    rows = []
+    if dbs:
+        for db in dbs:
+            con = sqlite3.connect(db)
+            if want_counters:
+                q = "select name, dispatch_id, counter_name, counter_value from pmc_events"
+                rows += [(r[0], r[1], r[2], float(r[3])) for r in con.execute(q)]
+            else:
+                rows += [(r[0], None, None, float(r[1] - r[2]))
+                         for r in con.execute("select name, end, start from kernels")]
+        return rows
+    pat = "*counter_collection.csv" if want_counters else "*kernel_trace.csv"
+    for fn in sorted(glob.glob(os.path.join(d, "**", pat), recursive=True)):
+        for r in csv.DictReader(open(fn)):
+            if want_counters:
+                rows.append((r["Kernel_Name"], r["Dispatch_Id"], r["Counter_Name"], float(r["Counter_Value"])))
+            else:
+                rows.append((r["Kernel_Name"], None, None,
+                             float(r["End_Timestamp"]) - float(r["Start_Timestamp"])))
+    return rows
+
+
+def summarize(args):
+    """Text summaries for profiles/: kernel statistics of a trace run, or the
+    HBM traffic per launch of one kernel from FETCH_SIZE and WRITE_SIZE runs,
+    each counter scaled by what it reads for a plain device copy of known size
+    (`bench.py --copy-mib N` runs one before the workload)."""
+    import collections
+    out = []
+    if args.command:
+        out.append("command: " + args.command)
+    if args.summarize_trace:
+        agg = collections.defaultdict(list)
+        for name, _, _, ns in _profile_rows(args.summarize_trace, False):
+            agg[name].append(ns)
+        tot = sum(sum(v) for v in agg.values())
+        out.append(f"{'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'share%':>7}  kernel")
+        for name, v in sorted(agg.items(), key=lambda kv: -sum(kv[1])):
+            out.append(f"{len(v):6d} {sum(v) / len(v) / 1e3:10.2f} {min(v) / 1e3:10.2f} {max(v) / 1e3:10.2f} "
+                       f"{100 * sum(v) / tot:7.2f}  {name}")
+        print("\n".join(out))
+        return
+    fetch_dir, write_dir = args.summarize
+    kernel = args.kernel
+    pname = PROFILE_NAME.get(kernel, kernel)
+
+    def per_kernel(d, counter):
+        vals = collections.defaultdict(lambda: collections.defaultdict(float))
+        for name, disp, cname, v in _profile_rows(d, True):
+            if cname == counter:
+                vals[name][disp] += v       # sums the per-instance values of a dispatch
+        return {k: list(v.values()) for k, v in vals.items()}
+
+    fetch = per_kernel(fetch_dir, "FETCH_SIZE")
+    write = per_kernel(write_dir, "WRITE_SIZE")
+    copy_name = max((k for k in fetch if "copy" in k.lower() or "elementwise" in k.lower()),
+                    key=lambda k: max(fetch[k]))
+    copy_bytes = args.copy_mib << 20
+    f_copy = max(fetch[copy_name]) * 1024.0
+    w_copy = max(write[copy_name]) * 1024.0
+    f_scale, w_scale = copy_bytes / f_copy, copy_bytes / w_copy
+    fk, wk = fetch[pname], write[pname]
+    f_avg = sum(fk) / len(fk) * 1024.0
+    w_avg = sum(wk) / len(wk) * 1024.0
+    traffic = f_avg * f_scale + w_avg * w_scale
+    out += [
+        f"kernel: {kernel}",
+        f"profiled_name: {pname}",
+        f"kernel_source_sha256_16: {source_digest()}",
+        f"copy_kernel: {copy_name}",
+        f"copy_bytes: {copy_bytes}",
+        f"copy_FETCH_SIZE_bytes: {f_copy:.0f}",
+        f"copy_WRITE_SIZE_bytes: {w_copy:.0f}",
+        f"fetch_scale: {f_scale:.4f}",
+        f"write_scale: {w_scale:.4f}",
+        f"launches: {len(fk)} (FETCH run), {len(wk)} (WRITE run)",
+        f"FETCH_SIZE_bytes_per_launch: {f_avg:.0f}",
+        f"WRITE_SIZE_bytes_per_launch: {w_avg:.0f}",
+        f"traffic_bytes_per_launch: {traffic:.0f}",
+        "  (= FETCH_SIZE * fetch_scale + WRITE_SIZE * write_scale, averaged over the launches)",
+        "per launch (FETCH KiB, scaled read bytes):",
+    ]
+    out += [f"  {v:.1f} KiB -> {v * 1024 * f_scale:.0f}" for v in fk]
+    out.append("per launch (WRITE KiB, scaled write bytes):")
+    out += [f"  {v:.1f} KiB -> {v * 1024 * w_scale:.0f}" for v in wk]
+    print("\n".join(out))
 
 
 def cpu_baseline(seconds):

@@ -183,6 +183,7 @@ class StateArray:
         self.infos = (HeadInfo * len(states))()
         for i, s in enumerate(states):
             ctypes.memmove(ctypes.byref(self.infos[i]), ctypes.byref(s.info), ctypes.sizeof(HeadInfo))
+        self.states = list(states)
         self.n = len(states)
         self.max_bits = max(int(s.info.total_bits) for s in states)
         self.xform = int(states[0].info.xform)
