@@ -195,21 +195,28 @@ def main():
     torch.cuda.synchronize()
 
     # ------------------------------------------------------- timed region
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in ops]
-          for _ in range(args.steps)]
+    # (1) the step as a whole: events only around the K steps
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0.record(stream)
     for k in range(args.steps):
-        for i, (_, fn, _) in enumerate(ops):
-            ev[k][i][0].record(stream)
+        for _, fn, _ in ops:
             fn()
-            ev[k][i][1].record(stream)
     t1.record(stream)
     torch.cuda.synchronize()
     total_ms = t0.elapsed_time(t1)
     ms_per_step = total_ms / args.steps
+    # (2) per-op durations: events on the launch stream around every op
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in ops]
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for k in range(args.steps):
+        for i, (_, fn, _) in enumerate(ops):
+            ev[k][i][0].record(stream)
+            fn()
+            ev[k][i][1].record(stream)
+    torch.cuda.synchronize()
 
     per_op = {}
     for i, (name, _, nbytes) in enumerate(ops):

@@ -245,7 +245,7 @@ stc_status build_eigen_blob(int d, int xform, const double* u, const double* lam
     if (b > 0) {
       const int L = 1 << b;
       h->inv_step[j] = steps[j] > 0.0 ? (float)(1.0 / steps[j]) : 0.0f;
-      h->ybias[j] = (float)(L / 2) + QEPS;
+      h->ybias[j] = (float)(L / 2) + quant_eps(L);
       h->lm1[j] = L - 1;
       h->thr_base[j] = nthr;
       for (int k = 1; k < L; ++k) thr[nthr++] = (float)(((double)k - (double)(L / 2)) * steps[j]);
@@ -265,10 +265,13 @@ stc_status build_eigen_blob(int d, int xform, const double* u, const double* lam
     for (int j = 0; j < d; ++j) {
       const double uij = ud[(size_t)i * d + j];
       u32[i * D + j] = (float)uij;
-      split_bf16(uij, &ut_hi[j * D + i], &ut_lo[j * D + i]);
       if (bits[j] > 0) bias += uij * steps[j] * 0.5 * (double)((1 << bits[j]) - 1);
     }
     h->bias[i] = (float)bias;
+  }
+  for (int R = 0; R < D; ++R) {
+    const int j = enc_row_channel(R);
+    for (int i = 0; i < d; ++i) split_bf16(ud[(size_t)i * d + j], &ut_hi[R * D + i], &ut_lo[R * D + i]);
   }
   for (int j = 0; j < d; ++j) h->bits4[j / 8] |= (uint32_t)bits[j] << (4 * (j % 8));
   fill_unpack_plan(h);
@@ -334,9 +337,8 @@ size_t stc_packed_bytes(int32_t total_bits, int64_t n_tokens) {
 size_t stc_attend_workspace_bytes(int64_t n_pairs, int32_t group, int64_t n_tokens) {
   if (n_pairs <= 0 || n_tokens <= 0 || group <= 0) return 256;
   const int64_t splits = att_n_splits(n_pairs, n_tokens);
-  size_t q = (size_t)n_pairs * ATT_QTAB_BYTES;
   size_t parts = (size_t)n_pairs * splits * group * ATT_PART_FLOATS * sizeof(float);
-  return (q + parts + 255) / 256 * 256;
+  return (parts + 255) / 256 * 256;
 }
 
 int32_t stc_total_bits(float avg_bits, int32_t d) {

@@ -14,18 +14,22 @@ constexpr size_t STATE_BYTES = 512u * 1024u;
 // Byte offsets of the regions of one state blob.
 constexpr size_t OFF_HDR = 0;                        // DevHdr
 constexpr size_t OFF_U32 = 8192;                     // float U[i][j], row-major (64 KiB)
-constexpr size_t OFF_UT_HI = OFF_U32 + 65536;        // bf16 U^T[j][i] high part (32 KiB)
-constexpr size_t OFF_UT_LO = OFF_UT_HI + 32768;      // bf16 U^T[j][i] low part
+constexpr size_t OFF_UT_HI = OFF_U32 + 65536;        // bf16 U[i][enc_row_channel(R)] at [R][i], high part
+constexpr size_t OFF_UT_LO = OFF_UT_HI + 32768;      // the low parts
 constexpr size_t OFF_W_HI = OFF_UT_LO + 32768;       // bf16 W[perm row][j], W = U diag(step)
 constexpr size_t OFF_W_LO = OFF_W_HI + 32768;
 constexpr size_t OFF_THR = OFF_W_LO + 32768;         // float thresholds, up to 128*255
 constexpr size_t OFF_GRAM = OFF_THR + 131072;        // double second moment [i][j]
 static_assert(OFF_GRAM + 131072 <= STATE_BYTES, "state layout overflows the blob");
 
-// Quantizer fast path: y = c / step + L/2 + EPS; codes are exact when
-// fract(y) >= 2*EPS, otherwise the thresholds decide (see the encode kernel).
-constexpr float QEPS = 1.0f / 8192.0f;
-constexpr float QFLAG = 2.0f * QEPS;
+// Quantizer fast path for a channel with L levels: y = c * fl(1/step) +
+// (L/2 + eps_L) in fp32 with eps_L = L * 2^-21. Against the exact count of
+// fp32 thresholds t_k = fl((k - L/2) step) <= c, y deviates by less than
+// L * 2^-21.5 (fp32 rounding of 1/step, of the fma, and of t_k, each relative
+// 2^-24 on magnitudes <= 2L), so floor(y) clamped to [0, L-1] is exact
+// whenever fract(y) >= 2 eps_L; otherwise the thresholds decide. Ties
+// (c == t_k) give y ~ k + eps_L and so go up, as the count does.
+inline constexpr float quant_eps(int levels) { return (float)levels * (1.0f / 2097152.0f); }
 
 struct alignas(16) DevHdr {
   int32_t xform;
@@ -37,7 +41,7 @@ struct alignas(16) DevHdr {
   uint8_t bits[D];
   uint16_t off[D];      // bit offset of channel j inside a token record
   float inv_step[D];    // fl32(1 / step_j); 0 for a dropped channel or a zero step
-  float ybias[D];       // L_j/2 + QEPS for a kept channel, 0.5 for a dropped one
+  float ybias[D];       // L_j/2 + quant_eps(L_j) for a kept channel, 0.5 for a dropped one
   int32_t lm1[D];       // L_j - 1 (0 if dropped)
   int32_t thr_base[D];  // index of t_1 of channel j in the threshold table
   float bias[D];        // decode: sum_j U_ij step_j (L_j - 1)/2, natural dim order
@@ -65,6 +69,15 @@ inline constexpr int w_row_dim(int R) {
   return 32 * ((R >> 4) >> 1) + 8 * ((R & 15) >> 2) + 4 * ((R >> 4) & 1) + (R & 3);
 }
 
+// Encode basis rows (bf16 U^T hi/lo) are stored permuted for the 32x32
+// encode MFMA (A = basis rows, M = channels): output row 8i + 4h + j of row
+// block b lands in lane half h, register 4i + j. Stored row R = 32b + 8i +
+// 4h + j holds latent channel 64h + 16b + 4i + j, so lane half h holds
+// channels [64h, 64h + 64) of its token, four consecutive channels per i.
+inline constexpr int enc_row_channel(int R) {
+  return 64 * ((R >> 2) & 1) + 16 * (R >> 5) + 4 * ((R >> 3) & 3) + (R & 3);
+}
+
 inline size_t packed_bytes(int64_t total_bits, int64_t n) {
   int64_t nb = (n * total_bits + 7) / 8;
   return (size_t)((nb + 15) / 16 * 16);
@@ -74,19 +87,17 @@ inline size_t packed_bytes(int64_t total_bits, int64_t n) {
 // shape; shared by the workspace-size query and the launcher.
 constexpr int ATT_TILE = 256;
 inline int64_t att_split_tokens(int64_t n_pairs, int64_t n_tokens) {
-  // about 512 workgroups in total (two per CU), splits of 1..256 tiles
-  const int64_t target = 512;
+  // about one workgroup per CU in total; a pair has at most that many splits
+  const int64_t target = 256;
   int64_t tiles = (n_tokens + ATT_TILE - 1) / ATT_TILE;
   int64_t per = (n_pairs * tiles + target - 1) / target;
   if (per < 1) per = 1;
-  if (per > 256) per = 256;
   return per * ATT_TILE;
 }
 inline int64_t att_n_splits(int64_t n_pairs, int64_t n_tokens) {
   int64_t s = att_split_tokens(n_pairs, n_tokens);
   return (n_tokens + s - 1) / s;
 }
-constexpr size_t ATT_QTAB_BYTES = 16 * D * 2 * 2;   // per pair: a_hi, a_lo bf16 [16][128]
 constexpr int ATT_PART_FLOATS = D + 2;              // per (pair, split, head): acc[128], m, l
 
 // Host-side launchers implemented in stc_kernels.hip.

@@ -40,6 +40,10 @@ constexpr float LOG2E = 1.4426950408889634f;
 __device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+__device__ __forceinline__ f32x16 mfma32_bf16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
 __device__ __forceinline__ f32x4 mfma_f16(f16x8 a, f16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
@@ -159,19 +163,29 @@ int launch_gram(const void* x, int dtype, int64_t ld, int64_t n_calib, double* g
 
 // ======================================================================
 // Encode (eigen / identity): project -> quantize -> pack.
-// One persistent workgroup of 8 waves per CU; a tile is 256 tokens of one
-// stream. Phase A: each wave projects 32 tokens onto the kept channels with
-// MFMA (B operand = basis rows staged in LDS) and quantizes in the MFMA
-// output layout (one channel per lane). Phase B: one token (half record) per
-// lane packs its codes with the widths in scalar registers into an LDS bit
-// stream. Phase C: the tile's bytes go to HBM as 128-bit stores.
+// A workgroup of 16 waves shares the basis (bf16 hi/lo rows, permuted) and
+// the quantizer tables in LDS; each wave encodes blocks of 32 tokens on its
+// own, with no workgroup barrier between blocks (four waves per SIMD hide
+// each other's memory and MFMA latency).
+//  1. MFMA 32x32x16 with A = basis rows (M = channels), B = the block's
+//     tokens: lane (h, t) receives channels [64h, 64h + 64) of token t,
+//     sixteen per row block, four consecutive channels per register group.
+//  2. Each value is quantized in registers and shifted to its bit offset
+//     inside its group of four channels (adjacent in the record): one word
+//     per group.
+//  3. Each group word is ORed into the wave's LDS bit stream at bit
+//     t*B + offset (one pad word per 32 keeps lanes on distinct banks; a
+//     spill past a 32-word block lands in that pad word and is folded back
+//     on the way out).
+//  4. The wave copies its stream (32 records, 4B bytes) to HBM and clears it.
 // ======================================================================
-constexpr int ENC_T = 256;
-constexpr int ENC_THREADS = 512;
-constexpr int UROW = 272;  // bytes per LDS basis row (256 + 16 pad against bank conflicts)
-constexpr int CROW = 144;  // bytes per LDS code row (128 + 16 pad)
-constexpr int STAGE_BYTES = 32 * 1024 + 64;
-constexpr size_t ENC_LDS = 2 * 128 * UROW + ENC_T * CROW + STAGE_BYTES;
+constexpr int ENC_WAVES = 16;
+constexpr int ENC_THREADS = 64 * ENC_WAVES;
+constexpr int ENC_BT = 32;                       // tokens per wave block
+constexpr int UROW = 272;                        // bytes per LDS basis row (256 + 16 pad)
+constexpr int CROW = 144;                        // bytes per LDS code row (128 + 16 pad)
+constexpr int EST_WORDS = 32 * 33 + 8;           // wave stream: 32 x 1024 bits + pad words + tail
+constexpr size_t ENC_LDS = 2 * 128 * UROW + 6 * 128 * 4 + (size_t)ENC_WAVES * EST_WORDS * 4;
 
 struct EncK {
   const unsigned char* states;
@@ -179,261 +193,233 @@ struct EncK {
   long long n_states, n_tokens, ld, x_stride, packed_stride;
   const void* x;
   unsigned char* packed;
-  long long tiles_per_stream, total_tiles, tiles_per_wg;
+  long long blocks_per_stream, total_blocks, blocks_per_wg;
   int grid;
 };
+
+__device__ __forceinline__ unsigned est_idx(unsigned w) { return w + (w >> 5); }
+
+// LDS (address space 3) byte pointers, used where a per-lane base must stay
+// one register so that reads can take constant offsets.
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+__device__ __forceinline__ unsigned lds_offset(unsigned char* p) {
+  return (unsigned)(uintptr_t)(lds_u8*)p;
+}
+__device__ __forceinline__ const lds_u8* lds_ptr(unsigned off) { return (const lds_u8*)(uintptr_t)off; }
+#define LDS_AT(T, p) (*(const __attribute__((address_space(3))) T*)(p))
+
+// Copy a wave stream of `nbytes` bytes (a multiple of 4*CW) to dst with
+// CW-word stores, folding the pad words back in; then clear `clear` words.
+template <int CW>
+__device__ __forceinline__ void est_copy_out(unsigned* str, unsigned char* dst, long long nbytes, unsigned clear,
+                                             int lane) {
+  typedef unsigned vec __attribute__((ext_vector_type(CW)));
+  const int nchunk = (int)(nbytes / (4 * CW));
+  for (int c = lane; c < nchunk; c += 64) {
+    vec v;
+#pragma unroll
+    for (int e = 0; e < CW; ++e) {
+      const unsigned w = (unsigned)(CW * c + e);
+      unsigned x = str[est_idx(w)];
+      if ((w & 31u) == 0u && w > 0u) x |= str[est_idx(w - 1) + 1];
+      v[e] = x;
+    }
+    reinterpret_cast<vec*>(dst)[c] = v;
+  }
+  __builtin_amdgcn_s_waitcnt(0xc07f);
+  __builtin_amdgcn_wave_barrier();
+  for (unsigned i = lane; i < clear; i += 64) str[i] = 0u;
+}
 
 // MODE 0: bf16 tokens, 1: fp32 tokens, 2: fp32 latent coefficients [n][128].
 template <int MODE>
 __global__ void __launch_bounds__(ENC_THREADS, 1) k_encode_eigen(EncK a) {
   extern __shared__ __align__(16) unsigned char smem[];
   unsigned char* sUhi = smem;
-  unsigned char* sUlo = smem + 128 * UROW;
-  unsigned char* sCode = smem + 2 * 128 * UROW;
-  unsigned* sStage = reinterpret_cast<unsigned*>(smem + 2 * 128 * UROW + ENC_T * CROW);
+  float* sInv = reinterpret_cast<float*>(smem + 2 * 128 * UROW);  // then yb, L-1, pos, band, group offset
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int r16 = lane & 15, g4 = lane >> 4;
+  const int t32 = lane & 31, h = lane >> 5;
+  unsigned* sStr = reinterpret_cast<unsigned*>(sInv + 6 * 128) + wave * EST_WORDS;
   const int lw = xcd_logical(blockIdx.x, a.grid);
-  const long long t_begin = (long long)lw * a.tiles_per_wg;
-  long long t_end = t_begin + a.tiles_per_wg;
-  if (t_end > a.total_tiles) t_end = a.total_tiles;
+  const long long b_begin = (long long)lw * a.blocks_per_wg;
+  long long b_end = b_begin + a.blocks_per_wg;
+  if (b_end > a.total_blocks) b_end = a.total_blocks;
   const long long n = a.n_tokens;
 
-  for (int i = tid; i < STAGE_BYTES / 4; i += ENC_THREADS) sStage[i] = 0u;
+  for (int i = lane; i < EST_WORDS; i += 64) sStr[i] = 0u;
 
-  long long cur = -1;
-  const DevHdr* hdr = nullptr;
-  const float* thr = nullptr;
-  float p_inv[8], p_yb[8];
-  int p_lm1[8], p_tb[8];
-  int nt_cnt = 0, B = 0;
-  HalfW HW = {};
-
-  // A fragments (tokens) of the next tile, loaded while the current one is
-  // processed (bf16 tokens only).
-  bf16x8 pf[2][4];
-  auto load_frags = [&](long long tile) {
-    const long long s = tile / a.tiles_per_stream;
-    const long long tt = tile - s * a.tiles_per_stream;
+  // B fragments (tokens) of a block: pf[ks] = token t (row clamped to n - 1),
+  // dims 16ks + 8h .. +7
+  bf16x8 pf[8];
+  auto load_frags = [&](long long s2, long long tt2) {
+    const long long tok0 = tt2 * ENC_BT;
+    const unsigned short* base = static_cast<const unsigned short*>(a.x) + s2 * a.x_stride + tok0 * a.ld;
+    const unsigned last = (unsigned)(n - 1 - tok0);
+    const unsigned r = (unsigned)t32 < last ? (unsigned)t32 : last;
+    const unsigned ro = r * (unsigned)a.ld + 8u * (unsigned)h;
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      long long tok = tt * ENC_T + 32 * wave + 16 * mt + r16;
-      if (tok > n - 1) tok = n - 1;
-      const unsigned short* row = static_cast<const unsigned short*>(a.x) + s * a.x_stride + tok * a.ld;
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        pf[mt][ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(row + 32 * ks + 8 * g4));
-    }
+    for (int ks = 0; ks < 8; ++ks)
+      pf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(base + ro + 16 * ks));
   };
-  if (MODE == 0 && t_begin < t_end) load_frags(t_begin);
 
-  for (long long tile = t_begin; tile < t_end; ++tile) {
-    const long long s = tile / a.tiles_per_stream;
-    const long long tt = tile - s * a.tiles_per_stream;
-    if (s != cur) {
-      cur = s;
-      const unsigned char* st = a.states + (size_t)state_index(a.map, s, a.n_states) * STATE_BYTES;
-      hdr = reinterpret_cast<const DevHdr*>(st + OFF_HDR);
-      thr = reinterpret_cast<const float*>(st + OFF_THR);
-      nt_cnt = hdr->nmax16 >> 4;
-      B = hdr->total_bits;
-      HW = load_half_widths(hdr, wave >> 2);
-      __syncthreads();  // every wave is done with the previous basis
-      if (MODE != 2) {
-        const u32x4* ghi = reinterpret_cast<const u32x4*>(st + OFF_UT_HI);
-        const u32x4* glo = reinterpret_cast<const u32x4*>(st + OFF_UT_LO);
-        const int chunks = hdr->nmax16 * 16;
-        for (int i = tid; i < chunks; i += ENC_THREADS) {
-          const int row = i >> 4, c = i & 15;
-          *reinterpret_cast<u32x4*>(sUhi + row * UROW + c * 16) = ghi[i];
-          *reinterpret_cast<u32x4*>(sUlo + row * UROW + c * 16) = glo[i];
-        }
+  for (long long seg = b_begin; seg < b_end;) {
+    const long long s = seg / a.blocks_per_stream;
+    long long seg_end = (s + 1) * a.blocks_per_stream;
+    if (seg_end > b_end) seg_end = b_end;
+    const unsigned char* st = a.states + (size_t)state_index(a.map, s, a.n_states) * STATE_BYTES;
+    const DevHdr* hdr = reinterpret_cast<const DevHdr*>(st + OFF_HDR);
+    const float* thr = reinterpret_cast<const float*>(st + OFF_THR);
+    const unsigned B = (unsigned)__builtin_amdgcn_readfirstlane(hdr->total_bits);
+    __syncthreads();  // every wave is done with the previous basis
+    if (MODE != 2) {
+      const u32x4* ghi = reinterpret_cast<const u32x4*>(st + OFF_UT_HI);
+      const u32x4* glo = reinterpret_cast<const u32x4*>(st + OFF_UT_LO);
+      for (int i = tid; i < 128 * 16; i += ENC_THREADS) {
+        const int row = i >> 4, c = i & 15;
+        *reinterpret_cast<u32x4*>(sUhi + row * UROW + c * 16) = ghi[i];
+        *reinterpret_cast<u32x4*>(sUhi + 128 * UROW + row * UROW + c * 16) = glo[i];
       }
-#pragma unroll
-      for (int nt = 0; nt < 8; ++nt) {
-        const int j = 16 * nt + r16;
-        p_inv[nt] = hdr->inv_step[j];
-        p_yb[nt] = hdr->ybias[j];
-        p_lm1[nt] = hdr->lm1[j];
-        p_tb[nt] = hdr->thr_base[j];
-      }
-      __syncthreads();
     }
-    if (B == 0) {
-      if (MODE == 0 && tile + 1 < t_end) load_frags(tile + 1);
-      continue;
+    if (tid < 128) {
+      sInv[tid] = hdr->inv_step[tid];
+      sInv[128 + tid] = hdr->ybias[tid];
+      sInv[256 + tid] = (float)hdr->lm1[tid];
+      reinterpret_cast<unsigned*>(sInv)[384 + tid] = (unsigned)hdr->off[tid] - (unsigned)hdr->off[tid & ~3];
+      sInv[512 + tid] = 2.0f * quant_eps(hdr->lm1[tid] + 1);  // guard band of the fast path
+      reinterpret_cast<unsigned*>(sInv)[640 + tid] = (unsigned)hdr->off[tid & ~3];  // record offset of the group
     }
-    const long long tok0 = tt * ENC_T;
-
-    // ---------------- phase A: project + quantize, codes -> LDS rows
-    unsigned cw[2][2][4];
+    __syncthreads();
+    if (B > 0) {
+      const long long P_len = packed_len((long long)B, n);
+      const unsigned cw_kind = (B & 3u) == 0u ? 4u : ((B & 1u) == 0u ? 2u : 1u);
+      const unsigned clear = est_idx(B + 4u) + 2u;
+      for (long long blk = seg + wave; blk < seg_end; blk += ENC_WAVES) {
+        const long long tt = blk - s * a.blocks_per_stream;
+        const long long tok0 = tt * ENC_BT;
+        const unsigned last_row = (unsigned)(n - 1 - tok0);
+        const unsigned trow = (unsigned)t32 < last_row ? (unsigned)t32 : last_row;
+        bf16x8 xl[8];
+        auto& xh = pf;
+        if (MODE == 0) load_frags(s, tt);
+        if (MODE == 1) {
+          const float* row = static_cast<const float*>(a.x) + s * a.x_stride + tok0 * a.ld + trow * (unsigned)a.ld;
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+          for (int ks = 0; ks < 8; ++ks) {
+            const f32x4 v0 = *reinterpret_cast<const f32x4*>(row + 16 * ks + 8 * h);
+            const f32x4 v1 = *reinterpret_cast<const f32x4*>(row + 16 * ks + 8 * h + 4);
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) cw[mt][h][r] = 0u;
-    {
-      bf16x8 ah[2][4], al[2][4];
-      if (MODE == 0) {
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-          for (int ks = 0; ks < 4; ++ks) ah[mt][ks] = pf[mt][ks];
-        if (tile + 1 < t_end) load_frags(tile + 1);
-      }
-      if (MODE == 1) {
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-          long long tok = tok0 + 32 * wave + 16 * mt + r16;
-          if (tok > n - 1) tok = n - 1;
-          {
-            const float* row = static_cast<const float*>(a.x) + s * a.x_stride + tok * a.ld;
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-              const f32x4 v0 = *reinterpret_cast<const f32x4*>(row + 32 * ks + 8 * g4);
-              const f32x4 v1 = *reinterpret_cast<const f32x4*>(row + 32 * ks + 8 * g4 + 4);
-#pragma unroll
-              for (int e = 0; e < 8; ++e) {
-                const float f = e < 4 ? v0[e] : v1[e - 4];
-                const __bf16 hi = (__bf16)f;
-                ah[mt][ks][e] = hi;
-                al[mt][ks][e] = (__bf16)(f - (float)hi);
-              }
+            for (int e = 0; e < 8; ++e) {
+              const float f = e < 4 ? v0[e] : v1[e - 4];
+              const __bf16 hi = (__bf16)f;
+              xh[ks][e] = hi;
+              xl[ks][e] = (__bf16)(f - (float)hi);
             }
           }
         }
-      }
+        // opaque per-lane LDS bases: every table read is base + constant
+        unsigned ub = lds_offset(sUhi + t32 * UROW + 16 * h);
+        unsigned pb = lds_offset(reinterpret_cast<unsigned char*>(sInv + 64 * h));
+        asm volatile("" : "+v"(ub), "+v"(pb));
+        const lds_u8* uL = lds_ptr(ub);
+        const lds_u8* pL = lds_ptr(pb);
+        const bool tok_ok = tok0 + t32 < n;
+        const unsigned tB = (unsigned)t32 * B;
 #pragma unroll
-      for (int nt = 0; nt < 8; ++nt) {
-        if (nt < nt_cnt) {
-          f32x4 acc[2];
+        for (int mb = 0; mb < 4; ++mb) {
+          // ---- 1: channels 64h + 16mb + 4i + j of token t in acc[4i + j]
+          f32x16 acc;
           if (MODE == 2) {
-            const float* cf = static_cast<const float*>(a.x);
+            const float* cf = static_cast<const float*>(a.x) + (tok0 + trow) * 128 + 64 * h + 16 * mb;
 #pragma unroll
-            for (int mt = 0; mt < 2; ++mt)
+            for (int i = 0; i < 4; ++i) {
+              const f32x4 v = *reinterpret_cast<const f32x4*>(cf + 4 * i);
 #pragma unroll
-              for (int r = 0; r < 4; ++r) {
-                long long tok = tok0 + 32 * wave + 16 * mt + 4 * g4 + r;
-                if (tok > n - 1) tok = n - 1;
-                acc[mt][r] = cf[tok * 128 + 16 * nt + r16];
-              }
+              for (int j = 0; j < 4; ++j) acc[4 * i + j] = v[j];
+            }
           } else {
 #pragma unroll
-            for (int mt = 0; mt < 2; ++mt) acc[mt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+            for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-              const int off = (16 * nt + r16) * UROW + (32 * ks + 8 * g4) * 2;
-              const bf16x8 bh = *reinterpret_cast<const bf16x8*>(sUhi + off);
-              const bf16x8 bl = *reinterpret_cast<const bf16x8*>(sUlo + off);
+            for (int ks = 0; ks < 8; ++ks) {
+              const int off = 32 * mb * UROW + 32 * ks;
+              const bf16x8 ah = LDS_AT(bf16x8, uL + off);
+              const bf16x8 al = LDS_AT(bf16x8, uL + 128 * UROW + off);
+              acc = mfma32_bf16(ah, xh[ks], acc);
+              acc = mfma32_bf16(al, xh[ks], acc);
+              if (MODE == 1) acc = mfma32_bf16(ah, xl[ks], acc);
+            }
+          }
+          // ---- 2 + 3 per group of four channels
 #pragma unroll
-              for (int mt = 0; mt < 2; ++mt) {
-                acc[mt] = mfma_bf16(ah[mt][ks], bh, acc[mt]);
-                acc[mt] = mfma_bf16(ah[mt][ks], bl, acc[mt]);
-                if (MODE == 1) acc[mt] = mfma_bf16(al[mt][ks], bh, acc[mt]);
+          for (int i = 0; i < 4; ++i) {
+            // y = c/step + L/2 + eps_L; outside the guard band next to an
+            // integer, floor(y) clamped to [0, L-1] is the exact threshold
+            // count; inside it, or for NaN or a zero step, the fp32
+            // thresholds decide.
+            const int coff = 4 * (16 * mb + 4 * i);  // byte offset of the group in a table
+            const f32x4 inv = LDS_AT(f32x4, pL + coff);
+            const f32x4 yb = LDS_AT(f32x4, pL + 512 + coff);
+            const f32x4 lm = LDS_AT(f32x4, pL + 1024 + coff);
+            const u32x4 pos = LDS_AT(u32x4, pL + 1536 + coff);
+            const f32x4 band = LDS_AT(f32x4, pL + 2048 + coff);
+            unsigned q[4];
+            bool need = false;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const float y = __builtin_fmaf(acc[4 * i + j], inv[j], yb[j]);
+              q[j] = (unsigned)__builtin_amdgcn_fmed3f(y, 0.0f, lm[j]);
+              need |= !(__builtin_amdgcn_fractf(y) >= band[j]);
+            }
+            if (__any(need)) {
+              // exact decision against the fp32 thresholds t_k (k = 1..L-1);
+              // the fast result is off by at most one level here
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                const float c = acc[4 * i + j];
+                const float y = __builtin_fmaf(c, inv[j], yb[j]);
+                if (!(__builtin_amdgcn_fractf(y) >= band[j])) {
+                  const int lm1 = (int)lm[j];
+                  int qq = (int)q[j];
+                  if (c != c) {
+                    qq = 0;
+                  } else if (inv[j] == 0.0f) {
+                    qq = c >= 0.0f ? lm1 : 0;  // zero step: every threshold is 0
+                  } else {
+                    const int ch = 64 * h + 16 * mb + 4 * i + j;
+                    const volatile float* tc = thr + *(const volatile int*)&hdr->thr_base[ch];
+                    if (qq > 0 && c < tc[qq - 1]) qq -= 1;
+                    else if (qq < lm1 && c >= tc[qq]) qq += 1;
+                  }
+                  q[j] = (unsigned)qq;
+                }
               }
             }
-          }
-          // Quantize. y = c/step + L/2 + EPS; away from integers floor(y) is
-          // the exact threshold count (the fp32 error of y is < 2^-15 while
-          // the guard band is 2^-13 wide); near an integer, or for NaN or a
-          // zero step, the exact thresholds decide.
-          const float inv = p_inv[nt], yb = p_yb[nt];
-          const int lm1 = p_lm1[nt];
-          int q[2][4];
-          unsigned flags = 0u;
-#pragma unroll
-          for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const float y = __builtin_fmaf(acc[mt][r], inv, yb);
-              const float yc = fminf(fmaxf(y, -1.0f), 511.0f);
-              int q0 = (int)floorf(yc);
-              q0 = q0 < 0 ? 0 : (q0 > lm1 ? lm1 : q0);
-              q[mt][r] = q0;
-              const float fr = __builtin_amdgcn_fractf(y);
-              if (!(fr >= QFLAG)) flags |= 1u << (4 * mt + r);
-            }
-          if (__any(flags != 0u)) {
-            const float* tc = thr + p_tb[nt];
-#pragma unroll
-            for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-              for (int r = 0; r < 4; ++r)
-                if (flags & (1u << (4 * mt + r))) q[mt][r] = quant_slow(acc[mt][r], inv, lm1, q[mt][r], tc);
-          }
-#pragma unroll
-          for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) cw[mt][nt >> 2][r] |= (unsigned)q[mt][r] << (8 * (nt & 3));
-        }
-      }
-    }
-    // code row of a token: dword (16h + c) holds channels 64h + 16k + c in byte k
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int tl = 32 * wave + 16 * mt + 4 * g4 + r;
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-          *reinterpret_cast<unsigned*>(sCode + tl * CROW + 4 * (16 * h + r16)) = cw[mt][h][r];
-      }
-    __syncthreads();
-
-    // ---------------- phase B: pack (half a record per lane) into the LDS stream
-    {
-      const int h = wave >> 2;
-      const int tl = 64 * (wave & 3) + lane;
-      if (tok0 + tl < n) {
-        unsigned c16[16];
-        const unsigned* crow = reinterpret_cast<const unsigned*>(sCode + tl * CROW + 64 * h);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const u32x4 v = *reinterpret_cast<const u32x4*>(crow + 4 * i);
-          c16[4 * i] = v[0]; c16[4 * i + 1] = v[1]; c16[4 * i + 2] = v[2]; c16[4 * i + 3] = v[3];
-        }
-        const unsigned S = (unsigned)tl * (unsigned)B + HW.off;
-        const unsigned d0 = S >> 5, sh = S & 31u;
-        unsigned acc = 0u, k = 0u;
-        int pos = 0;
-#pragma unroll
-        for (int jj = 0; jj < 64; ++jj) {
-          const int bw = width_of(HW, jj);
-          if (bw) {
-            const unsigned code = (c16[jj & 15] >> (8 * (jj >> 4))) & 0xffu;
-            acc |= code << pos;
-            if (pos + bw >= 32) {
-              stage_or(sStage, d0 + k, sh, acc);
-              ++k;
-              acc = code >> (32 - pos);
-              pos += bw - 32;
-            } else {
-              pos += bw;
+            const unsigned word = q[0] | (q[1] << pos[1]) | (q[2] << pos[2]) | (q[3] << pos[3]);
+            if (tok_ok) {
+              const unsigned P = tB + LDS_AT(unsigned, pL + 2560 + coff);  // record bit of the group
+              const unsigned long long v = (unsigned long long)word << (P & 31u);
+              unsigned* dst = sStr + est_idx(P >> 5);
+              __hip_atomic_fetch_or(dst, (unsigned)v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+              __hip_atomic_fetch_or(dst + 1, (unsigned)(v >> 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
             }
           }
         }
-        if (pos > 0) stage_or(sStage, d0 + k, sh, acc);
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's ORs have landed
+        __builtin_amdgcn_wave_barrier();
+        // ---- 4: stream -> HBM, then clear it. The last block of a stream
+        // also writes the zero padding up to the 16-byte boundary.
+        const long long start = tt * 4LL * (long long)B;
+        long long nbytes = 4LL * (long long)B;
+        if (tt == a.blocks_per_stream - 1 || nbytes > P_len - start) nbytes = P_len - start;
+        unsigned char* dst = a.packed + s * a.packed_stride + start;
+        if (cw_kind == 4u) est_copy_out<4>(sStr, dst, nbytes, clear, lane);
+        else if (cw_kind == 2u) est_copy_out<2>(sStr, dst, nbytes, clear, lane);
+        else est_copy_out<1>(sStr, dst, nbytes, clear, lane);
       }
     }
-    __syncthreads();
-
-    // ---------------- phase C: tile bytes -> HBM, then clear the stage
-    {
-      const long long P = packed_len(B, n);
-      const long long start = tt * 32LL * B;
-      long long nb = 32LL * B;
-      if (nb > P - start) nb = P - start;
-      u32x4* dst = reinterpret_cast<u32x4*>(a.packed + s * a.packed_stride + start);
-      u32x4* src = reinterpret_cast<u32x4*>(sStage);
-      const int nchunk = (int)(nb >> 4);
-      for (int i = tid; i < nchunk; i += ENC_THREADS) dst[i] = src[i];
-      const int zchunk = 2 * B + 1;
-      for (int i = tid; i < zchunk; i += ENC_THREADS) src[i] = (u32x4){0u, 0u, 0u, 0u};
-    }
-    __syncthreads();
+    seg = seg_end;
   }
 }
 
@@ -456,14 +442,15 @@ int launch_encode_eigen(const EncodeLaunch& L, void* stream) {
   a.packed_stride = L.packed_stride;
   a.x = L.x;
   a.packed = L.packed;
-  a.tiles_per_stream = (L.n_tokens + ENC_T - 1) / ENC_T;
-  a.total_tiles = a.tiles_per_stream * L.n_streams;
+  a.blocks_per_stream = (L.n_tokens + ENC_BT - 1) / ENC_BT;
+  a.total_blocks = a.blocks_per_stream * L.n_streams;
   int dev = 0, cus = 256;
   (void)hipGetDevice(&dev);
   (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  long long grid = a.total_tiles < cus ? a.total_tiles : cus;
-  a.tiles_per_wg = (a.total_tiles + grid - 1) / grid;
-  grid = (a.total_tiles + a.tiles_per_wg - 1) / a.tiles_per_wg;
+  long long grid = (a.total_blocks + ENC_WAVES - 1) / ENC_WAVES;
+  if (grid > cus) grid = cus;
+  a.blocks_per_wg = (a.total_blocks + grid - 1) / grid;
+  grid = (a.total_blocks + a.blocks_per_wg - 1) / a.blocks_per_wg;
   a.grid = (int)grid;
   hipStream_t s = (hipStream_t)stream;
   if (L.mode == 0) hipLaunchKernelGGL(k_encode_eigen<0>, dim3(grid), dim3(ENC_THREADS), ENC_LDS, s, a);
@@ -1003,11 +990,12 @@ int launch_decode_rht(const DecodeLaunch& L, void* stream) {
 // softmax. Values: the softmax-weighted average of the raw V codes is
 // accumulated per split, merged across splits with log-sum-exp, then
 // dequantized and rotated back once: o = U_V (step * (avg code - halfspan)).
-//  k_att_prologue: a -> bf16 hi/lo table per pair.
-//  k_att_main: one workgroup per (split, pair); 256-token tiles; K and V
-//   records unpacked one token per lane into LDS; scores = MFMA(a, K codes);
-//   online softmax per wave; P (fp16) x V codes (fp16) on MFMA.
-//  k_att_combine: merge splits, dequantize, rotate back (fp64).
+//  k_att_main: one workgroup per (split, pair); builds the a table (bf16
+//   hi/lo) in LDS, then 256-token tiles: K and V quarter records unpacked
+//   one per lane; scores = MFMA(a, K codes); online softmax per wave;
+//   P (fp16) x V codes (fp16) on MFMA; the split's (acc, m, l) to workspace.
+//  k_att_combine: one workgroup per pair: merge splits, dequantize, rotate
+//   back.
 // ======================================================================
 struct AttK {
   const unsigned char* k_states;
@@ -1025,37 +1013,16 @@ struct AttK {
   long long split_tokens, n_splits;
 };
 
-// a_hj = (U_K^T q_h)_j step_j scale log2(e), split into bf16 high and low
-// parts; one workgroup per (pair, padded head), one channel per thread.
-__global__ void __launch_bounds__(128) k_att_prologue(AttK a) {
-  const long long p = blockIdx.x >> 4;
-  const int h = blockIdx.x & 15;
-  const int j = threadIdx.x;
-  const unsigned char* st = a.k_states + (size_t)state_index(a.k_map, p, a.n_states) * STATE_BYTES;
-  const DevHdr* hk = reinterpret_cast<const DevHdr*>(st);
-  const float* u = reinterpret_cast<const float*>(st + OFF_U32);
-  unsigned short* tab = reinterpret_cast<unsigned short*>(a.ws + p * ATT_QTAB_BYTES);
-  float val = 0.0f;
-  if (h < a.group && hk->bits[j] > 0) {
-    const float* q = a.q + (p * a.group + h) * 128;
-    float acc = 0.0f;
-#pragma unroll 8
-    for (int i = 0; i < 128; ++i) acc = __builtin_fmaf(u[i * 128 + j], q[i], acc);
-    val = acc * hk->step32[j] * a.scale * LOG2E;
-  }
-  const __bf16 hi = (__bf16)val;
-  const __bf16 lo = (__bf16)(val - (float)hi);
-  tab[h * 128 + j] = __builtin_bit_cast(unsigned short, hi);
-  tab[16 * 128 + h * 128 + j] = __builtin_bit_cast(unsigned short, lo);
-}
-
 constexpr int ATT_THREADS = 1024;
 constexpr int VCROW = ATT_TILE + 16;    // bytes per LDS row of transposed V codes
 constexpr int PROW = 20;                // fp16 per LDS row of P (16 tokens + pad)
+constexpr int AROW = 272;                // bytes per LDS row of the a table (256 + 16 pad)
 constexpr size_t ATT_LDS = (size_t)ATT_TILE * CROW + 128 * VCROW + (size_t)QW_MAX * ATT_THREADS * 4 +
-                           16 * 16 * PROW * 2 + ATT_QTAB_BYTES;
+                           16 * 16 * PROW * 2 + 2 * 16 * AROW;
 // the end-of-split merge scratch (80 KiB, then 8 x 16 x 130 floats) reuses the front of this space
 static_assert(8 * 40 * 64 * 4 <= ATT_LDS && 8 * 16 * ATT_PART_FLOATS * 4 <= ATT_LDS, "merge scratch");
+static_assert((16 + 8 * 16) * 128 * 4 <= ATT_TILE * CROW + 128 * VCROW + QW_MAX * ATT_THREADS * 4,
+              "a-table scratch must fit in front of sP");
 
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
@@ -1108,7 +1075,7 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_att_main(AttK a) {
   unsigned char* sVc = sKc + ATT_TILE * CROW;
   unsigned* sCol = reinterpret_cast<unsigned*>(sVc + 128 * VCROW);
   _Float16* sP = reinterpret_cast<_Float16*>(sCol + QW_MAX * ATT_THREADS);
-  unsigned char* sA = reinterpret_cast<unsigned char*>(sP + 16 * 16 * PROW);  // a hi [16][128], lo [16][128]
+  unsigned char* sA = reinterpret_cast<unsigned char*>(sP + 16 * 16 * PROW);  // a hi [16][AROW], lo [16][AROW]
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1129,18 +1096,6 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_att_main(AttK a) {
   const unsigned long long sdwK = (unsigned long long)packed_len((long long)Bk, n) >> 2;
   const unsigned long long sdwV = (unsigned long long)packed_len((long long)Bv, n) >> 2;
 
-  // score A operand: a (bf16 hi/lo), rows = query heads (padded to 16), staged in LDS
-  {
-    const u32x4* tab = reinterpret_cast<const u32x4*>(a.ws + p * ATT_QTAB_BYTES);
-    for (int i = tid; i < (int)(ATT_QTAB_BYTES / 16); i += ATT_THREADS) reinterpret_cast<u32x4*>(sA)[i] = tab[i];
-  }
-  float m_run[4], l_run[4];
-  f32x4 acc_o[8];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) { m_run[r] = -INFINITY; l_run[r] = 0.0f; }
-#pragma unroll
-  for (int i = 0; i < 8; ++i) acc_o[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
-
   const long long t_begin = sp * a.split_tokens;
   long long t_end = t_begin + a.split_tokens;
   if (t_end > n) t_end = n;
@@ -1157,6 +1112,56 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_att_main(AttK a) {
     if (Bv) load_quarter_raw(gv, SV >> 5, sdwV, ok, QV.nw, rawv);
   };
   if (t_begin < t_end) load_raw(t_begin);
+
+  // Score A operand, built while the first tile's words are in flight:
+  // a_hj = (U_K^T q_h)_j step_j scale log2(e) as bf16 high and low parts,
+  // rows = query heads (padded to 16). Thread (part, j) sums rows
+  // 16*part..+15 of column j of U_K; the 8 parts are added through LDS
+  // scratch that the tile loop reuses afterwards.
+  {
+    float* sq = reinterpret_cast<float*>(smem);              // q [16][128]
+    float* red = sq + 16 * 128;                               // [8][16][128]
+    const int j = tid & 127, part = tid >> 7;
+    const int g = a.group;
+    const float* u = reinterpret_cast<const float*>(kst + OFF_U32);
+    float uc[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) uc[r] = u[(16 * part + r) * 128 + j];
+    const float* qp = a.q + p * g * 128;
+    for (int e = tid; e < g * 128; e += ATT_THREADS) sq[e] = qp[e];
+    __syncthreads();
+#pragma unroll
+    for (int h = 0; h < 16; ++h) {
+      if (h < g) {
+        float acc = 0.0f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc = __builtin_fmaf(uc[r], sq[h * 128 + 16 * part + r], acc);
+        red[(part * 16 + h) * 128 + j] = acc;
+      }
+    }
+    __syncthreads();
+    for (int e = tid; e < 16 * 128; e += ATT_THREADS) {
+      const int h = e >> 7, c = e & 127;
+      float val = 0.0f;
+      if (h < g && hk->bits[c] > 0) {
+        float sum = 0.0f;
+#pragma unroll
+        for (int pt = 0; pt < 8; ++pt) sum += red[(pt * 16 + h) * 128 + c];
+        val = sum * hk->step32[c] * a.scale * LOG2E;
+      }
+      const __bf16 hi = (__bf16)val;
+      const __bf16 lo = (__bf16)(val - (float)hi);
+      *reinterpret_cast<__bf16*>(sA + h * AROW + 2 * c) = hi;
+      *reinterpret_cast<__bf16*>(sA + (16 + h) * AROW + 2 * c) = lo;
+    }
+    // the tile loop starts with a barrier: sA is complete and the scratch free
+  }
+  float m_run[4], l_run[4];
+  f32x4 acc_o[8];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) { m_run[r] = -INFINITY; l_run[r] = 0.0f; }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc_o[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
   for (long long tok0 = t_begin; tok0 < t_end; tok0 += ATT_TILE) {
     const bool valid = tok0 + tl < t_end;
@@ -1195,8 +1200,8 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_att_main(AttK a) {
       if (ks < ksK) {
         const u32x2 v = *reinterpret_cast<const u32x2*>(sKc + (16 * wave + r16) * CROW + 32 * ks + 8 * g4);
         const bf16x8 b = bytes_to_bf16x8(v);
-        const bf16x8 ah = *reinterpret_cast<const bf16x8*>(sA + (r16 * 128 + 32 * ks + 8 * g4) * 2);
-        const bf16x8 al = *reinterpret_cast<const bf16x8*>(sA + 4096 + (r16 * 128 + 32 * ks + 8 * g4) * 2);
+        const bf16x8 ah = *reinterpret_cast<const bf16x8*>(sA + r16 * AROW + (32 * ks + 8 * g4) * 2);
+        const bf16x8 al = *reinterpret_cast<const bf16x8*>(sA + (16 + r16) * AROW + (32 * ks + 8 * g4) * 2);
         sc = mfma_bf16(ah, b, sc);
         sc = mfma_bf16(al, b, sc);
       }
@@ -1275,7 +1280,7 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_att_main(AttK a) {
     }
   }
   __syncthreads();
-  float* part = reinterpret_cast<float*>(a.ws + a.n_pairs * ATT_QTAB_BYTES) +
+  float* part = reinterpret_cast<float*>(a.ws) +
                 ((p * a.n_splits + sp) * a.group) * ATT_PART_FLOATS;
   for (int e = tid; e < a.group * 128; e += ATT_THREADS) {
     const int h = e >> 7, j = e & 127;
@@ -1295,57 +1300,122 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_att_main(AttK a) {
   }
 }
 
-// One workgroup per (pair, query head): merge the splits' (acc, m, l) with
-// log-sum-exp weights (fp32 weights, fp64 sums; 4 groups of threads take
-// every 4th split), take the softmax-weighted mean code of every V channel,
-// dequantize it and rotate back with U_V.
-__global__ void __launch_bounds__(512) k_att_combine(AttK a) {
-  __shared__ float red_m[4];
-  __shared__ double red_a[4][128];
-  __shared__ double red_l[4];
-  __shared__ float chat[128];
-  const long long p = blockIdx.x / a.group;
-  const int h = (int)(blockIdx.x - p * a.group);
-  const int j = threadIdx.x & 127, grp = threadIdx.x >> 7;
+// One workgroup of 1024 threads per pair: merge the splits' (acc, m, l) of
+// every query head with log-sum-exp weights (fp32 weights, fp64 sums), take
+// the softmax-weighted mean code of every V channel, dequantize it and
+// rotate back with U_V (staged in LDS, rows padded to 129 floats).
+constexpr int CMB_THREADS = 1024;
+constexpr int CMB_UROW = 129;
+constexpr int CMB_MAX_SPLITS = 256;  // att_split_tokens keeps n_splits <= 256
+__global__ void __launch_bounds__(CMB_THREADS, 1) k_att_combine(AttK a) {
+  extern __shared__ __align__(16) float cs[];
+  float* sU = cs;                          // [128][129]
+  float* sC = sU + 128 * CMB_UROW;         // per head: 128 weighted code sums, M, L
+  float* sF = sC + 16 * ATT_PART_FLOATS;   // weights [split][head]
+  const long long p = blockIdx.x;
+  const int t = threadIdx.x;
+  const int g = a.group;
+  const long long S = a.n_splits;
+  const float* ps0 = reinterpret_cast<const float*>(a.ws) + p * S * g * ATT_PART_FLOATS;
+  // Reads that depend on nothing are issued first: this thread's values of
+  // its first (head, j) entry for up to 32 splits and the split maxima; then
+  // the state (one dependent read of the map) with U_V and the quantizer
+  // fields of channel t & 127.
+  constexpr int CB = 32;
+  const int h0 = t / ATT_PART_FLOATS, j0 = t - h0 * ATT_PART_FLOATS;
+  const bool has0 = t < g * ATT_PART_FLOATS && j0 != 128;
+  const int nb0 = S < CB ? (int)S : CB;
+  float v0[CB];
+#pragma unroll
+  for (int r = 0; r < CB; ++r) v0[r] = (has0 && r < nb0) ? ps0[((long long)r * g + h0) * ATT_PART_FLOATS + j0] : 0.0f;
+  float mx[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const long long e = t + (long long)r * CMB_THREADS;
+    mx[r] = e < S * g ? ps0[e * ATT_PART_FLOATS + 128] : 0.0f;
+  }
   const unsigned char* vst = a.v_states + (size_t)state_index(a.v_map, p, a.n_states) * STATE_BYTES;
   const DevHdr* hv = reinterpret_cast<const DevHdr*>(vst);
   const float* u = reinterpret_cast<const float*>(vst + OFF_U32);
-  const float* ps0 = reinterpret_cast<const float*>(a.ws + a.n_pairs * ATT_QTAB_BYTES) +
-                     ((p * a.n_splits) * a.group + h) * ATT_PART_FLOATS;
-  const long long sstride = (long long)a.group * ATT_PART_FLOATS;
-  float M = -INFINITY;
-  for (long long s = grp; s < a.n_splits; s += 4) M = fmaxf(M, ps0[s * sstride + 128]);
-  if (j == 0) red_m[grp] = M;
-  __syncthreads();
-  M = fmaxf(fmaxf(red_m[0], red_m[1]), fmaxf(red_m[2], red_m[3]));
-  double A = 0.0, L = 0.0;
-  for (long long s = grp; s < a.n_splits; s += 4) {
-    const float* ps = ps0 + s * sstride;
-    const float ms = ps[128];
-    const float f = (ms == -INFINITY) ? 0.0f : exp2f(ms - M);
-    A += (double)(f * ps[j]);
-    L += (double)(f * ps[129]);
+  const int jc = t & 127;
+  const bool keptc = hv->bits[jc] > 0;
+  const double stepc = (double)hv->step32[jc], halfc = (double)hv->halfspan[jc];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const long long e = t + (long long)r * CMB_THREADS;
+    if (e < S * g) sF[e] = mx[r];
   }
-  red_a[grp][j] = A;
-  if (j == 0) red_l[grp] = L;
-  __syncthreads();
-  if (grp == 0) {
-    A = (red_a[0][j] + red_a[1][j]) + (red_a[2][j] + red_a[3][j]);
-    L = (red_l[0] + red_l[1]) + (red_l[2] + red_l[3]);
-    chat[j] = hv->bits[j] ? (float)((double)hv->step32[j] * (A / L - (double)hv->halfspan[j])) : 0.0f;
+  {
+    f32x4 uv[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) uv[r] = reinterpret_cast<const f32x4*>(u)[t + r * CMB_THREADS];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int e = 4 * (t + r * CMB_THREADS);
+      const int row = e >> 7, col = e & 127;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) sU[row * CMB_UROW + col + c] = uv[r][c];
+    }
   }
   __syncthreads();
-  if (grp == 0) {
-    float o = 0.0f;
-#pragma unroll 8
-    for (int k = 0; k < 128; ++k) o = __builtin_fmaf(u[j * 128 + k], chat[k], o);
-    a.out[(p * a.group + h) * 128 + j] = o;
+  // per-head maximum, then split weights
+  if (t < g) {
+    float M = -INFINITY;
+    for (long long s2 = 0; s2 < S; ++s2) M = fmaxf(M, sF[s2 * g + t]);
+    sC[t * ATT_PART_FLOATS + 128] = M;
+  }
+  __syncthreads();
+  for (long long e = t; e < S * g; e += CMB_THREADS) {
+    const int h = (int)(e % g);
+    const float ms = sF[e];
+    sF[e] = (ms == -INFINITY) ? 0.0f : exp2f(ms - sC[h * ATT_PART_FLOATS + 128]);
+  }
+  __syncthreads();
+  // weighted sums over the splits of the code sums (j < 128) and of l
+  // (j = 129), fp64; thread per (head, j)
+  for (int e = t; e < g * ATT_PART_FLOATS; e += CMB_THREADS) {
+    const int h = e / ATT_PART_FLOATS, j = e - h * ATT_PART_FLOATS;
+    if (j == 128) continue;
+    double A = 0.0;
+    long long s2 = 0;
+    if (e == t) {
+#pragma unroll
+      for (int r = 0; r < CB; ++r)
+        if (r < nb0) A += (double)(sF[r * g + h] * v0[r]);
+      s2 = nb0;
+    }
+    for (; s2 + 8 <= S; s2 += 8) {
+      float v[8];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) v[r] = ps0[((s2 + r) * g + h) * ATT_PART_FLOATS + j];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) A += (double)(sF[(s2 + r) * g + h] * v[r]);
+    }
+    for (; s2 < S; ++s2) A += (double)(sF[s2 * g + h] * ps0[(s2 * g + h) * ATT_PART_FLOATS + j]);
+    sC[e] = (float)A;
+  }
+  __syncthreads();
+  for (int hj = t; hj < g * 128; hj += CMB_THREADS) {   // j = hj & 127 = t & 127
+    float* c = sC + (hj >> 7) * ATT_PART_FLOATS + jc;
+    c[0] = keptc ? (float)(stepc * ((double)c[0] / (double)sC[(hj >> 7) * ATT_PART_FLOATS + 129] - halfc)) : 0.0f;
+  }
+  __syncthreads();
+  {
+    const int i = t & 127;
+    for (int h = t >> 7; h < g; h += CMB_THREADS / 128) {
+      float o = 0.0f;
+#pragma unroll 16
+      for (int k = 0; k < 128; ++k) o = __builtin_fmaf(sU[i * CMB_UROW + k], sC[h * ATT_PART_FLOATS + k], o);
+      a.out[(p * g + h) * 128 + i] = o;
+    }
   }
 }
 
 int launch_attend(const AttendLaunch& L, void* stream) {
   if (!g_att_attr_done) {
     (void)hipFuncSetAttribute((const void*)k_att_main, hipFuncAttributeMaxDynamicSharedMemorySize, (int)ATT_LDS);
+    (void)hipFuncSetAttribute((const void*)k_att_combine, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)((128 * CMB_UROW + 16 * ATT_PART_FLOATS) * 4 + CMB_MAX_SPLITS * 16 * 4));
     g_att_attr_done = true;
   }
   AttK a;
@@ -1367,9 +1437,9 @@ int launch_attend(const AttendLaunch& L, void* stream) {
   a.split_tokens = att_split_tokens(L.n_pairs, L.n_tokens);
   a.n_splits = att_n_splits(L.n_pairs, L.n_tokens);
   hipStream_t s = (hipStream_t)stream;
-  hipLaunchKernelGGL(k_att_prologue, dim3((unsigned)(L.n_pairs * 16)), dim3(128), 0, s, a);
+  const size_t cmb_lds = (size_t)(128 * CMB_UROW + 16 * ATT_PART_FLOATS) * 4 + (size_t)a.n_splits * L.group * 4;
   hipLaunchKernelGGL(k_att_main, dim3((unsigned)a.n_splits, (unsigned)L.n_pairs), dim3(ATT_THREADS), ATT_LDS, s, a);
-  hipLaunchKernelGGL(k_att_combine, dim3((unsigned)(L.n_pairs * L.group)), dim3(512), 0, s, a);
+  hipLaunchKernelGGL(k_att_combine, dim3((unsigned)L.n_pairs), dim3(CMB_THREADS), cmb_lds, s, a);
   return hipGetLastError() != hipSuccess;
 }
 
