@@ -276,7 +276,7 @@ stc_status build_eigen_blob(int d, int xform, const double* u, const double* lam
   for (int j = 0; j < d; ++j) h->bits4[j / 8] |= (uint32_t)bits[j] << (4 * (j % 8));
   fill_unpack_plan(h);
   for (int R = 0; R < D; ++R) {
-    const int i = w_row_dim(R);
+    const int i = enc_row_channel(R);  // output dim of stored row R (same permutation as the encode basis)
     for (int j = 0; j < d; ++j) split_bf16(ud[(size_t)i * d + j] * steps[j], &w_hi[R * D + j], &w_lo[R * D + j]);
   }
   if (info) {

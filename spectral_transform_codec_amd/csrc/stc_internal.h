@@ -16,7 +16,7 @@ constexpr size_t OFF_HDR = 0;                        // DevHdr
 constexpr size_t OFF_U32 = 8192;                     // float U[i][j], row-major (64 KiB)
 constexpr size_t OFF_UT_HI = OFF_U32 + 65536;        // bf16 U[i][enc_row_channel(R)] at [R][i], high part
 constexpr size_t OFF_UT_LO = OFF_UT_HI + 32768;      // the low parts
-constexpr size_t OFF_W_HI = OFF_UT_LO + 32768;       // bf16 W[perm row][j], W = U diag(step)
+constexpr size_t OFF_W_HI = OFF_UT_LO + 32768;       // bf16 W[enc_row_channel(R)][j] at [R][j], W = U diag(step)
 constexpr size_t OFF_W_LO = OFF_W_HI + 32768;
 constexpr size_t OFF_THR = OFF_W_LO + 32768;         // float thresholds, up to 128*255
 constexpr size_t OFF_GRAM = OFF_THR + 131072;        // double second moment [i][j]
@@ -62,12 +62,6 @@ struct alignas(16) DevHdr {
 };
 static_assert(sizeof(DevHdr) <= OFF_U32, "header too large");
 
-// Decode rows of W are stored permuted so that one lane of the decode MFMA
-// epilogue owns 8 consecutive output dims: stored row R = 16*mt + m with
-// mt = 2p + s, m = 4g + r holds output dim 32p + 8g + 4s + r.
-inline constexpr int w_row_dim(int R) {
-  return 32 * ((R >> 4) >> 1) + 8 * ((R & 15) >> 2) + 4 * ((R >> 4) & 1) + (R & 3);
-}
 
 // Encode basis rows (bf16 U^T hi/lo) are stored permuted for the 32x32
 // encode MFMA (A = basis rows, M = channels): output row 8i + 4h + j of row

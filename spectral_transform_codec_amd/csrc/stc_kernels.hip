@@ -79,38 +79,6 @@ __device__ __forceinline__ f16x8 bytes_to_f16x8(u32x2 v) {
   return r;
 }
 
-// Widths (and the record offset) of the 64 channels [64h, 64h+64) of a state,
-// forced into scalar registers: the pack/unpack loops branch on them, and a
-// per-channel vector load there would serialise a cache round trip per channel.
-struct HalfW {
-  unsigned w[8];   // bits 4k..4k+3 of w[i] = width of channel 64h + 8i + k
-  unsigned off;    // record bit offset of channel 64h
-};
-__device__ __forceinline__ HalfW load_half_widths(const DevHdr* hdr, int h) {
-  HalfW r;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) r.w[i] = __builtin_amdgcn_readfirstlane(hdr->bits4[8 * h + i]);
-  r.off = __builtin_amdgcn_readfirstlane((unsigned)hdr->off[64 * h]);
-  return r;
-}
-__device__ __forceinline__ int width_of(const HalfW& W, int jj) { return (W.w[jj >> 3] >> (4 * (jj & 7))) & 0xf; }
-
-// OR a 32-bit record word into an LDS bit stream at bit (32*d + sh).
-__device__ __forceinline__ void stage_or(unsigned* stage, unsigned d, unsigned sh, unsigned w) {
-  atomicOr(&stage[d], w << sh);
-  if (sh) atomicOr(&stage[d + 1], w >> (32u - sh));
-}
-
-// Exact code of a flagged element: the count of thresholds t_k <= c, found
-// from the fast estimate q (off by at most one level) with two comparisons.
-__device__ __noinline__ int quant_slow(float c, float inv, int lm1, int q, const float* thr) {
-  if (c != c) return 0;
-  if (inv == 0.0f) return c >= 0.0f ? lm1 : 0;  // zero step: every threshold is 0
-  if (q > 0 && c < thr[q - 1]) return q - 1;
-  if (q < lm1 && c >= thr[q]) return q + 1;
-  return q;
-}
-
 // ======================================================================
 // Second moment (calibration): one workgroup per stream, fp64 accumulation
 // of exact fp32 products in token order. Thread (ti, tj) owns entries
@@ -529,16 +497,24 @@ __device__ __forceinline__ void unpack_quarter(const unsigned* col, int ntask, c
 // Decode (eigen / identity): unpack -> MFMA with W = U diag(step) -> bias.
 // x_hat_i = sum_j W_ij q_j - bias_i,  bias_i = sum_j W_ij (L_j - 1)/2,
 // i.e. sum_j U_ij step_j (q_j - (L_j - 1)/2) with q the raw codes.
-// 16 waves per workgroup, 256-token tiles. Each lane unpacks one quarter
-// record (task = 4 quarters x 256 tokens) into LDS code rows; then wave w
-// rebuilds tokens 32(w%8)..+31 for output dims 64(w/8)..+63 (A = W rows
-// staged in LDS, B = codes) and stores them. The next tile's HBM words are
-// loaded while the current tile is reconstructed.
+// A workgroup of 16 waves shares W (bf16 hi/lo rows, permuted) and the unpack
+// tables in LDS; each wave decodes blocks of 32 tokens on its own:
+//  1. The block's records (32 B bits) go from HBM into the wave's LDS stream
+//     (word w at w + w/32; the pad slot after each 32 words repeats the next
+//     word, so the word after k is always at idx(k) + 1).
+//  2. Lane (h, t) takes channels [64h, 64h + 64) of token t: per group of four
+//     channels one 64-bit window at the group's record bit holds the four
+//     codes (offsets and widths from the tables); codes are exact in bf16.
+//  3. MFMA 32x32x16 with A = W rows (M = output dims, stored so that lane half
+//     h receives dims [64h, 64h + 64)) and B = codes (K = channels; lane half
+//     h supplies the channels of its own half record), minus the bias, rounded
+//     to the output dtype: each lane stores one 128-byte (bf16) or two
+//     (fp32) whole row halves.
 // ======================================================================
-constexpr int DEC_T = 256;
-constexpr int DEC_THREADS = 1024;
-constexpr int DCROW = 132;  // code row bytes (33 dwords: lanes of a wave hit distinct banks)
-constexpr size_t DEC_LDS = 2 * 128 * UROW + DEC_T * DCROW + (size_t)QW_MAX * DEC_THREADS * 4;
+constexpr int DEC_WAVES = 16;
+constexpr int DEC_THREADS = 64 * DEC_WAVES;
+constexpr int DEC_BT = 32;
+constexpr size_t DEC_LDS = 2 * 128 * UROW + 4 * 128 * 4 + (size_t)DEC_WAVES * EST_WORDS * 4;
 
 struct DecK {
   const unsigned char* states;
@@ -546,35 +522,25 @@ struct DecK {
   long long n_states, n_tokens, ld, x_stride, packed_stride;
   const unsigned char* packed;
   void* x;
-  long long tiles_per_stream, total_tiles, tiles_per_wg;
+  long long blocks_per_stream, total_blocks, blocks_per_wg;
   int grid;
 };
 
-// Unpack the 64 codes of channels [64h, 64h+64) of token tl from the LDS
-// stream `P32` (bit 0 = first bit of the tile) into 16 dwords, natural order.
-// Every code is read through its own 64-bit window at its bit address, so the
-// LDS reads are independent of each other and pipeline freely (a running
-// window would serialise one LDS round trip per 32 bits of record).
-// Reads P32[.. (tl*B + off + 64-channel span) / 32 + 1].
-__device__ __forceinline__ void unpack_half(const unsigned* P32, const HalfW& W, unsigned tl, int B,
-                                            unsigned cw[16]) {
+// HBM bytes [0, nbytes) of a block -> wave stream (CW-word loads), with the
+// word following each 32-word run repeated in the pad slot before it.
+template <int CW>
+__device__ __forceinline__ void est_copy_in(unsigned* str, const unsigned char* src, long long nbytes, int lane) {
+  typedef unsigned vec __attribute__((ext_vector_type(CW)));
+  const int nchunk = (int)(nbytes / (4 * CW));
+  for (int c = lane; c < nchunk; c += 64) {
+    const vec v = reinterpret_cast<const vec*>(src)[c];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) cw[i] = 0u;
-  unsigned S = tl * (unsigned)B + W.off;
-  // opaque to the optimiser: keeps the 64 per-channel addresses from being
-  // hoisted out of the caller's tile loop (they would pin ~64 registers)
-  asm volatile("" : "+v"(S));
-  unsigned pos = 0;
-#pragma unroll
-  for (int jj = 0; jj < 64; ++jj) {
-    const unsigned bw = (unsigned)width_of(W, jj);
-    const unsigned bit = S + pos;
-    const unsigned d = bit >> 5;
-    const unsigned code = __builtin_amdgcn_ubfe(__builtin_amdgcn_alignbit(P32[d + 1], P32[d], bit), 0u, bw);
-    cw[jj >> 2] |= code << (8 * (jj & 3));
-    pos += bw;
-    // keep at most 16 channels' reads in flight (register pressure)
-    if ((jj & 15) == 15) __builtin_amdgcn_sched_barrier(0);
+    for (int e = 0; e < CW; ++e) {
+      const unsigned w = (unsigned)(CW * c + e);
+      const unsigned ix = est_idx(w);
+      str[ix] = v[e];
+      if ((w & 31u) == 0u && w > 0u) str[ix - 1] = v[e];
+    }
   }
 }
 
@@ -582,181 +548,157 @@ template <int F32OUT>
 __global__ void __launch_bounds__(DEC_THREADS, 1) k_decode_eigen(DecK a) {
   extern __shared__ __align__(16) unsigned char smem[];
   unsigned char* sWhi = smem;
-  unsigned char* sWlo = smem + 128 * UROW;
-  unsigned char* sCode = smem + 2 * 128 * UROW;
-  unsigned* sCol = reinterpret_cast<unsigned*>(smem + 2 * 128 * UROW + DEC_T * DCROW);
+  unsigned* sTab = reinterpret_cast<unsigned*>(smem + 2 * 128 * UROW);  // goff, pos, width, bias
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int r16 = lane & 15, g4 = lane >> 4;
-  const int q = wave >> 2;          // quarter record of this lane's unpack task
-  const int tl = tid & 255;         // token of this lane's unpack task
-  const int dh = wave >> 3;         // output-dim half of this wave's reconstruction
-  const int tw = wave & 7;          // token group of this wave's reconstruction
+  const int t32 = lane & 31, h = lane >> 5;
+  unsigned* sStr = sTab + 4 * 128 + wave * EST_WORDS;
   const int lw = xcd_logical(blockIdx.x, a.grid);
-  const long long t_begin = (long long)lw * a.tiles_per_wg;
-  long long t_end = t_begin + a.tiles_per_wg;
-  if (t_end > a.total_tiles) t_end = a.total_tiles;
+  const long long b_begin = (long long)lw * a.blocks_per_wg;
+  long long b_end = b_begin + a.blocks_per_wg;
+  if (b_end > a.total_blocks) b_end = a.total_blocks;
   const long long n = a.n_tokens;
 
-  unsigned raw[QW_MAX + 1] = {};
-  unsigned raw_sh = 0;
-  // issue the HBM loads of this lane's quarter record of `tile`
-  auto load_raw = [&](long long tile) {
-    const long long s2 = tile / a.tiles_per_stream;
-    const long long tt2 = tile - s2 * a.tiles_per_stream;
-    const DevHdr* h2 =
-        reinterpret_cast<const DevHdr*>(a.states + (size_t)state_index(a.map, s2, a.n_states) * STATE_BYTES);
-    const unsigned long long B2 = (unsigned)h2->total_bits;
-    const unsigned nw = __builtin_amdgcn_readfirstlane(h2->qwords[q]);
-    const unsigned qo = __builtin_amdgcn_readfirstlane(h2->qoff[q]);
-    const unsigned long long tg = (unsigned long long)(tt2 * DEC_T + tl);
-    const unsigned long long S = tg * B2 + qo;
-    raw_sh = (unsigned)(S & 31u);
-    const unsigned long long sdw = (unsigned long long)packed_len((long long)B2, n) >> 2;
-    const unsigned* g = reinterpret_cast<const unsigned*>(a.packed + s2 * a.packed_stride);
-    if (B2 > 0) load_quarter_raw(g, S >> 5, sdw, tg < (unsigned long long)n, nw, raw);
-  };
-  if (t_begin < t_end) load_raw(t_begin);
-
-  long long cur = -1;
-  const DevHdr* hdr = nullptr;
-  int ks_cnt = 0, B = 0;
-  QPlan QP = {};
-
-  for (long long tile = t_begin; tile < t_end; ++tile) {
-    const long long s = tile / a.tiles_per_stream;
-    const long long tt = tile - s * a.tiles_per_stream;
-    if (s != cur) {
-      cur = s;
-      const unsigned char* st = a.states + (size_t)state_index(a.map, s, a.n_states) * STATE_BYTES;
-      hdr = reinterpret_cast<const DevHdr*>(st + OFF_HDR);
-      ks_cnt = hdr->kmax32 >> 5;
-      B = hdr->total_bits;
-      QP = load_qplan(hdr, q);
-      __syncthreads();
+  for (long long seg = b_begin; seg < b_end;) {
+    const long long s = seg / a.blocks_per_stream;
+    long long seg_end = (s + 1) * a.blocks_per_stream;
+    if (seg_end > b_end) seg_end = b_end;
+    const unsigned char* st = a.states + (size_t)state_index(a.map, s, a.n_states) * STATE_BYTES;
+    const DevHdr* hdr = reinterpret_cast<const DevHdr*>(st + OFF_HDR);
+    const unsigned B = (unsigned)__builtin_amdgcn_readfirstlane(hdr->total_bits);
+    __syncthreads();  // every wave is done with the previous state
+    {
       const u32x4* ghi = reinterpret_cast<const u32x4*>(st + OFF_W_HI);
       const u32x4* glo = reinterpret_cast<const u32x4*>(st + OFF_W_LO);
-      const int cpr = hdr->kmax32 / 8;  // 16-byte chunks per row used
-      for (int i = tid; i < 128 * cpr; i += DEC_THREADS) {
-        const int row = i / cpr, c = i - row * cpr;
-        *reinterpret_cast<u32x4*>(sWhi + row * UROW + c * 16) = ghi[row * 16 + c];
-        *reinterpret_cast<u32x4*>(sWlo + row * UROW + c * 16) = glo[row * 16 + c];
+      for (int i = tid; i < 128 * 16; i += DEC_THREADS) {
+        const int row = i >> 4, c = i & 15;
+        *reinterpret_cast<u32x4*>(sWhi + row * UROW + c * 16) = ghi[i];
+        *reinterpret_cast<u32x4*>(sWhi + 128 * UROW + row * UROW + c * 16) = glo[i];
       }
-      __syncthreads();
     }
-    const long long tok0 = tt * DEC_T;
-    // ---- stage this lane's quarter record (its own LDS column)
-    stage_quarter(raw, raw_sh, QP.nw, sCol + tid, DEC_THREADS);
-    __syncthreads();  // previous tile's reconstruction is done with the code rows
-    // ---- unpack to code rows (natural channel order)
-    {
-      unsigned out[8];
-      if (tok0 + tl < n && B > 0) {
-        unpack_quarter(sCol + tid, DEC_THREADS, QP, out);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) out[i] = 0u;
-      }
-      unsigned* crow = reinterpret_cast<unsigned*>(sCode + tl * DCROW + 32 * q);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) crow[i] = out[i];
+    if (tid < 128) {
+      sTab[tid] = (unsigned)hdr->off[tid & ~3];                              // group record offset
+      sTab[128 + tid] = (unsigned)hdr->off[tid] - (unsigned)hdr->off[tid & ~3];  // offset in the group
+      sTab[256 + tid] = (unsigned)hdr->bits[tid];                            // width
+      reinterpret_cast<float*>(sTab)[384 + tid] = -hdr->bias[tid];          // -bias, natural dim order
     }
-    if (tile + 1 < t_end) load_raw(tile + 1);
     __syncthreads();
-    // ---- reconstruct tokens 32*tw..+31, dims 64*dh..+63
-    {
-      bf16x8 bfr[2][4];
-#pragma unroll
-      for (int nt2 = 0; nt2 < 2; ++nt2)
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          if (ks < ks_cnt) {
-            const unsigned* cp =
-                reinterpret_cast<const unsigned*>(sCode + (32 * tw + 16 * nt2 + r16) * DCROW + 32 * ks + 8 * g4);
-            bfr[nt2][ks] = bytes_to_bf16x8((u32x2){cp[0], cp[1]});
-          }
-        }
-      f32x4 acc[2][2][2];  // [pp][sI][nt2]
-#pragma unroll
-      for (int pp = 0; pp < 2; ++pp) {
-        const int p = 2 * dh + pp;
-#pragma unroll
-        for (int sI = 0; sI < 2; ++sI)
-#pragma unroll
-          for (int nt2 = 0; nt2 < 2; ++nt2) acc[pp][sI][nt2] = (f32x4){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int sI = 0; sI < 2; ++sI) {
-          const int mt = 2 * p + sI;
-#pragma unroll
-          for (int ks = 0; ks < 4; ++ks) {
-            if (ks < ks_cnt) {
-              const int off = (16 * mt + r16) * UROW + (32 * ks + 8 * g4) * 2;
-              const bf16x8 wh = *reinterpret_cast<const bf16x8*>(sWhi + off);
-              const bf16x8 wl = *reinterpret_cast<const bf16x8*>(sWlo + off);
-#pragma unroll
-              for (int nt2 = 0; nt2 < 2; ++nt2) {
-                acc[pp][sI][nt2] = mfma_bf16(wh, bfr[nt2][ks], acc[pp][sI][nt2]);
-                acc[pp][sI][nt2] = mfma_bf16(wl, bfr[nt2][ks], acc[pp][sI][nt2]);
-              }
-            }
-          }
-        }
+    const long long P_len = packed_len((long long)B, n);
+    const unsigned cw_kind = (B & 3u) == 0u ? 4u : ((B & 1u) == 0u ? 2u : 1u);
+    for (long long blk = seg + wave; blk < seg_end; blk += DEC_WAVES) {
+      const long long tt = blk - s * a.blocks_per_stream;
+      const long long tok0 = tt * DEC_BT;
+      // ---- 1: records -> LDS stream
+      if (B > 0) {
+        const long long start = tt * 4LL * (long long)B;
+        long long nbytes = 4LL * (long long)B;
+        if (nbytes > P_len - start) nbytes = P_len - start;
+        const unsigned char* src = a.packed + s * a.packed_stride + start;
+        if (cw_kind == 4u) est_copy_in<4>(sStr, src, nbytes, lane);
+        else if (cw_kind == 2u) est_copy_in<2>(sStr, src, nbytes, lane);
+        else est_copy_in<1>(sStr, src, nbytes, lane);
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+        __builtin_amdgcn_wave_barrier();
       }
-      // lane (g4, r16) holds, for token 16*nt2 + r16 of its group, dims
-      // 32p + 8g4 + 0..7 for p = 2dh (chunk A) and p = 2dh + 1 (chunk B).
-      float bias8[2][8];
+      // ---- 2: codes of channels 64h + 8ks + i as bf16 (B fragments)
+      unsigned tb = lds_offset(reinterpret_cast<unsigned char*>(sTab + 64 * h));
+      unsigned wb = lds_offset(sWhi + t32 * UROW + 128 * h);
+      asm volatile("" : "+v"(tb), "+v"(wb));
+      const lds_u8* tL = lds_ptr(tb);
+      const lds_u8* wL = lds_ptr(wb);
+      const unsigned tB = (unsigned)t32 * B;
+      bf16x8 cf[8];
 #pragma unroll
-      for (int pp = 0; pp < 2; ++pp) {
-        const f32x4 b0 = *reinterpret_cast<const f32x4*>(hdr->bias + 32 * (2 * dh + pp) + 8 * g4);
-        const f32x4 b1 = *reinterpret_cast<const f32x4*>(hdr->bias + 32 * (2 * dh + pp) + 8 * g4 + 4);
+      for (int g = 0; g < 16; ++g) {  // group: channels 64h + 4g .. +3
+        unsigned code[4] = {0u, 0u, 0u, 0u};
+        if (B > 0) {
+          const unsigned P = tB + LDS_AT(unsigned, tL + 16 * g);
+          const unsigned ix = est_idx(P >> 5);
+          const unsigned w = __builtin_amdgcn_alignbit(sStr[ix + 1], sStr[ix], P & 31u);
+          const u32x4 pos = LDS_AT(u32x4, tL + 512 + 16 * g);
+          const u32x4 wid = LDS_AT(u32x4, tL + 1024 + 16 * g);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) { bias8[pp][r] = b0[r]; bias8[pp][4 + r] = b1[r]; }
+          for (int j = 0; j < 4; ++j) code[j] = __builtin_amdgcn_ubfe(w, pos[j], wid[j]);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) cf[g >> 1][4 * (g & 1) + j] = (__bf16)(float)code[j];
       }
+      // ---- 3: reconstruct dims 64h + 16ob + r of token t
+      const long long tok = tok0 + t32;
+      const bool tok_ok = tok < n;
+      u32x4 pk[4][2];  // bf16 output, dims 64h + 16ob + 8c .. +7 in pk[ob][c]
 #pragma unroll
-      for (int nt2 = 0; nt2 < 2; ++nt2) {
+      for (int ob = 0; ob < 4; ++ob) {
+        // the accumulator starts at -bias
+        f32x16 acc;
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const f32x4 nb = LDS_AT(f32x4, tL + 1536 + 64 * ob + 16 * q4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[4 * q4 + e] = nb[e];
+        }
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+          const int off = 32 * ob * UROW + 16 * ks;
+          const bf16x8 wh = LDS_AT(bf16x8, wL + off);
+          const bf16x8 wl = LDS_AT(bf16x8, wL + 128 * UROW + off);
+          acc = mfma32_bf16(wh, cf[ks], acc);
+          acc = mfma32_bf16(wl, cf[ks], acc);
+        }
         if (F32OUT) {
-          const long long tok = tok0 + 32 * tw + 16 * nt2 + r16;
-          if (tok < n) {
+          if (tok_ok) {
+            float* o = static_cast<float*>(a.x) + s * a.x_stride + tok * a.ld + 64 * h + 16 * ob;
 #pragma unroll
-            for (int pp = 0; pp < 2; ++pp) {
-              float* o = static_cast<float*>(a.x) + s * a.x_stride + tok * a.ld + 32 * (2 * dh + pp) + 8 * g4;
-              *reinterpret_cast<f32x4*>(o) = (f32x4){acc[pp][0][nt2][0] - bias8[pp][0], acc[pp][0][nt2][1] - bias8[pp][1],
-                                                     acc[pp][0][nt2][2] - bias8[pp][2], acc[pp][0][nt2][3] - bias8[pp][3]};
-              *reinterpret_cast<f32x4*>(o + 4) = (f32x4){acc[pp][1][nt2][0] - bias8[pp][4], acc[pp][1][nt2][1] - bias8[pp][5],
-                                                         acc[pp][1][nt2][2] - bias8[pp][6], acc[pp][1][nt2][3] - bias8[pp][7]};
-            }
+            for (int q4 = 0; q4 < 4; ++q4)
+              reinterpret_cast<f32x4*>(o)[q4] = (f32x4){acc[4 * q4], acc[4 * q4 + 1], acc[4 * q4 + 2], acc[4 * q4 + 3]};
           }
         } else {
-          // bf16: chunk A/B = 8 dims = 16 bytes. Lanes r16 and r16^1 swap so
-          // that each store instruction writes whole 128-byte rows of 8 tokens:
-          // first the even tokens (even lane: own A, odd lane: partner's B),
-          // then the odd tokens (even lane: partner's A, odd lane: own B).
-          u32x4 ch[2];
 #pragma unroll
-          for (int pp = 0; pp < 2; ++pp)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int sI = e >> 1, r = 2 * (e & 1);
-              const float v0 = acc[pp][sI][nt2][r] - bias8[pp][2 * e];
-              const float v1 = acc[pp][sI][nt2][r + 1] - bias8[pp][2 * e + 1];
-              ch[pp][e] = (unsigned)__builtin_bit_cast(unsigned short, (__bf16)v0) |
-                          ((unsigned)__builtin_bit_cast(unsigned short, (__bf16)v1) << 16);
-            }
-          const bool odd = r16 & 1;
-          u32x4 recv;
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            recv[e] = (unsigned)__builtin_amdgcn_mov_dpp((int)(odd ? ch[0][e] : ch[1][e]), 0xB1, 0xF, 0xF, false);
-          const long long tokA = tok0 + 32 * tw + 16 * nt2 + (r16 & ~1);
-          const long long tokB = tokA + 1;
-          unsigned short* oA = static_cast<unsigned short*>(a.x) + s * a.x_stride + tokA * a.ld + 64 * dh + 8 * g4;
-          unsigned short* oB = static_cast<unsigned short*>(a.x) + s * a.x_stride + tokB * a.ld + 64 * dh + 8 * g4;
-          if (tokA < n) *reinterpret_cast<u32x4*>(oA + (odd ? 32 : 0)) = odd ? recv : ch[0];
-          if (tokB < n) *reinterpret_cast<u32x4*>(oB + (odd ? 32 : 0)) = odd ? ch[1] : recv;
+          for (int e = 0; e < 8; ++e) {
+            const float v0 = acc[2 * e];
+            const float v1 = acc[2 * e + 1];
+            pk[ob][e >> 2][e & 3] = (unsigned)__builtin_bit_cast(unsigned short, (__bf16)v0) |
+                                    ((unsigned)__builtin_bit_cast(unsigned short, (__bf16)v1) << 16);
+          }
         }
       }
+      if (!F32OUT) {
+        // Two rounds through the LDS stream (free once the codes are out):
+        // the lanes of half r put their 128-byte row halves (one cache line
+        // each) into rows of 33 words, then the wave writes the 32 lines with
+        // 16-byte stores, eight lanes per line.
+        const int nrow = (int)(n - tok0 < DEC_BT ? n - tok0 : DEC_BT);
+        unsigned short* obase = static_cast<unsigned short*>(a.x) + s * a.x_stride + tok0 * a.ld;
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+          __builtin_amdgcn_s_waitcnt(0xc07f);
+          __builtin_amdgcn_wave_barrier();
+          if (h == r) {
+#pragma unroll
+            for (int ob = 0; ob < 4; ++ob)
+#pragma unroll
+              for (int c = 0; c < 2; ++c)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sStr[33 * t32 + 8 * ob + 4 * c + e] = pk[ob][c][e];
+          }
+          __builtin_amdgcn_s_waitcnt(0xc07f);
+          __builtin_amdgcn_wave_barrier();
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const int row = 8 * k + (lane >> 3), c = lane & 7;
+            if (row < nrow) {
+              const u32x4 v = (u32x4){sStr[33 * row + 4 * c], sStr[33 * row + 4 * c + 1], sStr[33 * row + 4 * c + 2],
+                                      sStr[33 * row + 4 * c + 3]};
+              *reinterpret_cast<u32x4*>(obase + row * a.ld + 64 * r + 8 * c) = v;
+            }
+          }
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+        __builtin_amdgcn_wave_barrier();
+      }
     }
+    seg = seg_end;
   }
 }
 
@@ -776,14 +718,15 @@ int launch_decode_eigen(const DecodeLaunch& L, void* stream) {
   a.packed_stride = L.packed_stride;
   a.packed = L.packed;
   a.x = L.x;
-  a.tiles_per_stream = (L.n_tokens + DEC_T - 1) / DEC_T;
-  a.total_tiles = a.tiles_per_stream * L.n_streams;
+  a.blocks_per_stream = (L.n_tokens + DEC_BT - 1) / DEC_BT;
+  a.total_blocks = a.blocks_per_stream * L.n_streams;
   int dev = 0, cus = 256;
   (void)hipGetDevice(&dev);
   (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  long long grid = a.total_tiles < cus ? a.total_tiles : cus;
-  a.tiles_per_wg = (a.total_tiles + grid - 1) / grid;
-  grid = (a.total_tiles + a.tiles_per_wg - 1) / a.tiles_per_wg;
+  long long grid = (a.total_blocks + DEC_WAVES - 1) / DEC_WAVES;
+  if (grid > cus) grid = cus;
+  a.blocks_per_wg = (a.total_blocks + grid - 1) / grid;
+  grid = (a.total_blocks + a.blocks_per_wg - 1) / a.blocks_per_wg;
   a.grid = (int)grid;
   hipStream_t s = (hipStream_t)stream;
   if (L.f32out) hipLaunchKernelGGL(k_decode_eigen<1>, dim3(grid), dim3(DEC_THREADS), DEC_LDS, s, a);
