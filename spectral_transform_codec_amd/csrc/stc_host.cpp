@@ -250,6 +250,7 @@ stc_status build_eigen_blob(int d, int xform, const double* u, const double* lam
       h->thr_base[j] = nthr;
       for (int k = 1; k < L; ++k) thr[nthr++] = (float)(((double)k - (double)(L / 2)) * steps[j]);
       h->step32[j] = (float)steps[j];
+      h->step64[j] = steps[j];
       h->halfspan[j] = 0.5f * (float)(L - 1);
     } else {
       h->inv_step[j] = 0.0f;

@@ -59,6 +59,7 @@ struct alignas(16) DevHdr {
   uint32_t plan[4][8];
   uint32_t qoff[4];
   uint32_t qwords[4];
+  double step64[D];     // step_j in fp64: thresholds are fl32((k - L/2) * step64[j])
 };
 static_assert(sizeof(DevHdr) <= OFF_U32, "header too large");
 

@@ -153,7 +153,7 @@ constexpr int ENC_BT = 32;                       // tokens per wave block
 constexpr int UROW = 272;                        // bytes per LDS basis row (256 + 16 pad)
 constexpr int CROW = 144;                        // bytes per LDS code row (128 + 16 pad)
 constexpr int EST_WORDS = 32 * 33 + 8;           // wave stream: 32 x 1024 bits + pad words + tail
-constexpr size_t ENC_LDS = 2 * 128 * UROW + 6 * 128 * 4 + (size_t)ENC_WAVES * EST_WORDS * 4;
+constexpr size_t ENC_LDS = 2 * 128 * UROW + 8 * 128 * 4 + (size_t)ENC_WAVES * EST_WORDS * 4;
 
 struct EncK {
   const unsigned char* states;
@@ -204,12 +204,12 @@ template <int MODE>
 __global__ void __launch_bounds__(ENC_THREADS, 1) k_encode_eigen(EncK a) {
   extern __shared__ __align__(16) unsigned char smem[];
   unsigned char* sUhi = smem;
-  float* sInv = reinterpret_cast<float*>(smem + 2 * 128 * UROW);  // then yb, L-1, pos, band, group offset
+  float* sInv = reinterpret_cast<float*>(smem + 2 * 128 * UROW);  // then yb, L-1, pos, band, group offset, fp64 step
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int t32 = lane & 31, h = lane >> 5;
-  unsigned* sStr = reinterpret_cast<unsigned*>(sInv + 6 * 128) + wave * EST_WORDS;
+  unsigned* sStr = reinterpret_cast<unsigned*>(sInv + 8 * 128) + wave * EST_WORDS;
   const int lw = xcd_logical(blockIdx.x, a.grid);
   const long long b_begin = (long long)lw * a.blocks_per_wg;
   long long b_end = b_begin + a.blocks_per_wg;
@@ -238,7 +238,6 @@ __global__ void __launch_bounds__(ENC_THREADS, 1) k_encode_eigen(EncK a) {
     if (seg_end > b_end) seg_end = b_end;
     const unsigned char* st = a.states + (size_t)state_index(a.map, s, a.n_states) * STATE_BYTES;
     const DevHdr* hdr = reinterpret_cast<const DevHdr*>(st + OFF_HDR);
-    const float* thr = reinterpret_cast<const float*>(st + OFF_THR);
     const unsigned B = (unsigned)__builtin_amdgcn_readfirstlane(hdr->total_bits);
     __syncthreads();  // every wave is done with the previous basis
     if (MODE != 2) {
@@ -257,6 +256,7 @@ __global__ void __launch_bounds__(ENC_THREADS, 1) k_encode_eigen(EncK a) {
       reinterpret_cast<unsigned*>(sInv)[384 + tid] = (unsigned)hdr->off[tid] - (unsigned)hdr->off[tid & ~3];
       sInv[512 + tid] = 2.0f * quant_eps(hdr->lm1[tid] + 1);  // guard band of the fast path
       reinterpret_cast<unsigned*>(sInv)[640 + tid] = (unsigned)hdr->off[tid & ~3];  // record offset of the group
+      reinterpret_cast<double*>(sInv + 768)[tid] = hdr->step64[tid];
     }
     __syncthreads();
     if (B > 0) {
@@ -341,8 +341,10 @@ __global__ void __launch_bounds__(ENC_THREADS, 1) k_encode_eigen(EncK a) {
               need |= !(__builtin_amdgcn_fractf(y) >= band[j]);
             }
             if (__any(need)) {
-              // exact decision against the fp32 thresholds t_k (k = 1..L-1);
-              // the fast result is off by at most one level here
+              // exact decision against the thresholds t_k = fl32((k - L/2) step),
+              // k = 1..L-1, rebuilt here from the fp64 step exactly as the
+              // state builder forms them; the fast result is off by at most
+              // one level
 #pragma unroll
               for (int j = 0; j < 4; ++j) {
                 const float c = acc[4 * i + j];
@@ -355,10 +357,11 @@ __global__ void __launch_bounds__(ENC_THREADS, 1) k_encode_eigen(EncK a) {
                   } else if (inv[j] == 0.0f) {
                     qq = c >= 0.0f ? lm1 : 0;  // zero step: every threshold is 0
                   } else {
-                    const int ch = 64 * h + 16 * mb + 4 * i + j;
-                    const volatile float* tc = thr + *(const volatile int*)&hdr->thr_base[ch];
-                    if (qq > 0 && c < tc[qq - 1]) qq -= 1;
-                    else if (qq < lm1 && c >= tc[qq]) qq += 1;
+                    // fp64 table entry of channel 64h + 16mb + 4i + j (pL covers 64h floats)
+                    const double s64 = LDS_AT(double, pL + 3072 + 256 * h + 2 * coff + 8 * j);
+                    const double half = (double)((lm1 + 1) >> 1);
+                    if (qq > 0 && c < (float)(((double)qq - half) * s64)) qq -= 1;
+                    else if (qq < lm1 && c >= (float)(((double)(qq + 1) - half) * s64)) qq += 1;
                   }
                   q[j] = (unsigned)qq;
                 }
