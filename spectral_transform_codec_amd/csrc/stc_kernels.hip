@@ -936,10 +936,13 @@ int launch_decode_rht(const DecodeLaunch& L, void* stream) {
 // softmax. Values: the softmax-weighted average of the raw V codes is
 // accumulated per split, merged across splits with log-sum-exp, then
 // dequantized and rotated back once: o = U_V (step * (avg code - halfspan)).
-//  k_att_main: one workgroup per (split, pair); builds the a table (bf16
-//   hi/lo) in LDS, then 256-token tiles: K and V quarter records unpacked
-//   one per lane; scores = MFMA(a, K codes); online softmax per wave;
-//   P (fp16) x V codes (fp16) on MFMA; the split's (acc, m, l) to workspace.
+//  k_att_main: one workgroup per (split, pair). It builds the a table (bf16
+//   hi/lo) in LDS; then each wave takes 32-token blocks of the split on its
+//   own: K and V records to LDS, K half records extracted per lane, scores
+//   by one MFMA chain (hi rows 0..15 and lo rows 16..31 of the table
+//   against the K codes), online softmax, P (fp16) x V codes (fp16) on MFMA
+//   with the V codes byte-transposed into a [channel][token] buffer. At the
+//   end the waves' (acc, m, l) are merged into the split's partial.
 //  k_att_combine: one workgroup per pair: merge splits, dequantize, rotate
 //   back.
 // ======================================================================
@@ -957,36 +960,27 @@ struct AttK {
   float scale;
   unsigned char* ws;
   long long split_tokens, n_splits;
+  int stream_words, region_words;
 };
 
-constexpr int ATT_THREADS = 1024;
-constexpr int VCROW = ATT_TILE + 16;    // bytes per LDS row of transposed V codes
-constexpr int PROW = 20;                // fp16 per LDS row of P (16 tokens + pad)
-constexpr int AROW = 272;                // bytes per LDS row of the a table (256 + 16 pad)
-constexpr size_t ATT_LDS = (size_t)ATT_TILE * CROW + 128 * VCROW + (size_t)QW_MAX * ATT_THREADS * 4 +
-                           16 * 16 * PROW * 2 + 2 * 16 * AROW;
-// the end-of-split merge scratch (80 KiB, then 8 x 16 x 130 floats) reuses the front of this space
-static_assert(8 * 40 * 64 * 4 <= ATT_LDS && 8 * 16 * ATT_PART_FLOATS * 4 <= ATT_LDS, "merge scratch");
-static_assert((16 + 8 * 16) * 128 * 4 <= ATT_TILE * CROW + 128 * VCROW + QW_MAX * ATT_THREADS * 4,
-              "a-table scratch must fit in front of sP");
+constexpr int ATT_WAVES_MAX = 16;
+constexpr int ATT_THREADS = 64 * ATT_WAVES_MAX;
+constexpr int ATT_BT = 32;                       // tokens per wave block
+constexpr int AROW = 272;                        // bytes per a-table row (rows 0..15 hi, 16..31 lo)
+constexpr int VT_ROW = 9;                        // dwords per row of the [channel][token] V bytes
+constexpr int VT_WORDS = 128 * VT_ROW;
+constexpr int P_ROWH = 36;                       // fp16 per row of P [head][token]
+constexpr int P_WORDS = 16 * P_ROWH / 2;
+constexpr int ATT_FIXED_BYTES = 32 * AROW + 6 * 128 * 4;
+// Words of one wave's region: the K and V record streams (reused for the
+// transposed V codes once both are extracted), P, and per-head alpha.
+__host__ __device__ constexpr int att_stream_words(int max_bits) { return max_bits + (max_bits >> 5) + 8; }
+__host__ __device__ constexpr int att_region_words(int max_bits) {
+  return (2 * att_stream_words(max_bits) > VT_WORDS ? 2 * att_stream_words(max_bits) : VT_WORDS) + P_WORDS + 16;
+}
 
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ float grp16_max(float v) {
-  v = fmaxf(v, __shfl_xor(v, 1));
-  v = fmaxf(v, __shfl_xor(v, 2));
-  v = fmaxf(v, __shfl_xor(v, 4));
-  v = fmaxf(v, __shfl_xor(v, 8));
-  return v;
-}
-__device__ __forceinline__ float grp16_sum(float v) {
-  v += __shfl_xor(v, 1);
-  v += __shfl_xor(v, 2);
-  v += __shfl_xor(v, 4);
-  v += __shfl_xor(v, 8);
-  return v;
-}
 
 // 4 unsigned byte codes -> 4 fp16 (exact): 0x64xx is 1024 + xx in fp16.
 __device__ __forceinline__ f16x4 bytes_to_f16x4(unsigned v) {
@@ -1007,242 +1001,325 @@ __device__ __forceinline__ unsigned quad_transpose_bytes(unsigned x, int e) {
   return __builtin_amdgcn_perm(p2, y, (e & 2) ? 0x03020706u : 0x05040100u);
 }
 
-// One workgroup (16 waves) per (split, pair); 256-token tiles.
-//  B: lane (token tl, quarter q) unpacks quarter q of the K record into the
-//     K code rows and quarter q of the V record, transposed across each
-//     quad of lanes, into the [channel][token] V code array.
-//  C: wave w scores tokens 16w..16w+15 (MFMA: a x K codes), updates its
-//     online softmax and accumulates P x V codes (MFMA, fp16).
-// The HBM words of the next tile are loaded while the current one computes.
-// At the end the 16 waves' (acc, m, l) are merged into the split's partial.
+// Max / sum over the 32 lanes of each half wave (DPP within 16-lane rows,
+// then a row swap).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+// Both 16-lane rows of each half wave side by side: element 0 holds the
+// value of row 2k, element 1 that of row 2k + 1, in every lane of the half.
+__device__ __forceinline__ auto row_swap(float x) {
+  const unsigned a = __builtin_bit_cast(unsigned, x);
+  return __builtin_amdgcn_permlane16_swap(a, a, false, false);
+}
+__device__ __forceinline__ float half_max(float x) {
+  x = fmaxf(x, dpp_f<0xB1>(x));   // quad_perm [1,0,3,2]
+  x = fmaxf(x, dpp_f<0x4E>(x));   // quad_perm [2,3,0,1]
+  x = fmaxf(x, dpp_f<0x141>(x));  // row_half_mirror
+  x = fmaxf(x, dpp_f<0x140>(x));  // row_mirror
+  const auto r = row_swap(x);
+  const unsigned r0 = r[0], r1 = r[1];  // (a bit cast of a vector element reads element 0)
+  return fmaxf(__builtin_bit_cast(float, r0), __builtin_bit_cast(float, r1));
+}
+__device__ __forceinline__ float half_sum(float x) {
+  x += dpp_f<0xB1>(x);
+  x += dpp_f<0x4E>(x);
+  x += dpp_f<0x141>(x);
+  x += dpp_f<0x140>(x);
+  const auto r = row_swap(x);
+  const unsigned r0 = r[0], r1 = r[1];
+  return __builtin_bit_cast(float, r0) + __builtin_bit_cast(float, r1);
+}
+
+// Per-lane unpack tables of a state: group record offset, offset inside the
+// group, width (128 each).
+__device__ __forceinline__ void att_tables(const DevHdr* hd, unsigned* tab, int c) {
+  tab[c] = (unsigned)hd->off[c & ~3];
+  tab[128 + c] = (unsigned)hd->off[c] - (unsigned)hd->off[c & ~3];
+  tab[256 + c] = (unsigned)hd->bits[c];
+}
+
+// The four codes of group g (channels 64h + 4g .. +3) of the record at bit
+// tB of an LDS stream, as bytes of one word.
+__device__ __forceinline__ unsigned att_group_bytes(const unsigned* str, const lds_u8* tL, unsigned tB, int g) {
+  const unsigned P = tB + LDS_AT(unsigned, tL + 16 * g);
+  const unsigned ix = est_idx(P >> 5);
+  const unsigned w = __builtin_amdgcn_alignbit(str[ix + 1], str[ix], P & 31u);
+  const u32x4 pos = LDS_AT(u32x4, tL + 512 + 16 * g);
+  const u32x4 wid = LDS_AT(u32x4, tL + 1024 + 16 * g);
+  unsigned v = __builtin_amdgcn_ubfe(w, pos[0], wid[0]);
+  v |= __builtin_amdgcn_ubfe(w, pos[1], wid[1]) << 8;
+  v |= __builtin_amdgcn_ubfe(w, pos[2], wid[2]) << 16;
+  v |= __builtin_amdgcn_ubfe(w, pos[3], wid[3]) << 24;
+  return v;
+}
+
 __global__ void __launch_bounds__(ATT_THREADS, 1) k_att_main(AttK a) {
   extern __shared__ __align__(16) unsigned char smem[];
-  unsigned char* sKc = smem;
-  unsigned char* sVc = sKc + ATT_TILE * CROW;
-  unsigned* sCol = reinterpret_cast<unsigned*>(sVc + 128 * VCROW);
-  _Float16* sP = reinterpret_cast<_Float16*>(sCol + QW_MAX * ATT_THREADS);
-  unsigned char* sA = reinterpret_cast<unsigned char*>(sP + 16 * 16 * PROW);  // a hi [16][AROW], lo [16][AROW]
+  unsigned char* sA = smem;                                        // a table [32][AROW]
+  unsigned* sTab = reinterpret_cast<unsigned*>(smem + 32 * AROW);  // K tables, then V tables
+  unsigned* sReg0 = sTab + 6 * 128;                                // wave regions
+  const int nwav = (int)(blockDim.x >> 6);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int r16 = lane & 15, g4 = lane >> 4;
-  const int tl = tid & 255, q = wave >> 2;
+  const int t32 = lane & 31, h = lane >> 5;
+  const int c16 = lane & 15, g4 = lane >> 4;
   const long long sp = blockIdx.x, p = blockIdx.y;
   const long long n = a.n_tokens;
+  const int g = a.group;
   const unsigned char* kst = a.k_states + (size_t)state_index(a.k_map, p, a.n_states) * STATE_BYTES;
   const unsigned char* vst = a.v_states + (size_t)state_index(a.v_map, p, a.n_states) * STATE_BYTES;
   const DevHdr* hk = reinterpret_cast<const DevHdr*>(kst);
   const DevHdr* hv = reinterpret_cast<const DevHdr*>(vst);
-  const unsigned long long Bk = (unsigned)hk->total_bits, Bv = (unsigned)hv->total_bits;
-  const int ksK = hk->kmax32 >> 5;
-  const int ntV = hv->nmax16 >> 4;
-  const QPlan QK = load_qplan(hk, q), QV = load_qplan(hv, q);
-  const unsigned* gk = reinterpret_cast<const unsigned*>(a.k_packed + p * a.packed_stride);
-  const unsigned* gv = reinterpret_cast<const unsigned*>(a.v_packed + p * a.packed_stride);
-  const unsigned long long sdwK = (unsigned long long)packed_len((long long)Bk, n) >> 2;
-  const unsigned long long sdwV = (unsigned long long)packed_len((long long)Bv, n) >> 2;
-
+  const unsigned Bk = (unsigned)__builtin_amdgcn_readfirstlane(hk->total_bits);
+  const unsigned Bv = (unsigned)__builtin_amdgcn_readfirstlane(hv->total_bits);
+  const int SW = a.stream_words;
+  unsigned* sKs = sReg0 + wave * a.region_words;  // K stream
+  unsigned* sVs = sKs + SW;                        // V stream
+  unsigned* sVT = sKs;                             // [channel][token] V bytes, after extraction
+  _Float16* sP = reinterpret_cast<_Float16*>(sKs + (2 * SW > VT_WORDS ? 2 * SW : VT_WORDS));
+  float* sAl = reinterpret_cast<float*>(sP + 16 * P_ROWH);  // alpha per head
   const long long t_begin = sp * a.split_tokens;
   long long t_end = t_begin + a.split_tokens;
   if (t_end > n) t_end = n;
 
-  unsigned rawk[QW_MAX + 1] = {}, rawv[QW_MAX + 1] = {};
-  unsigned shk = 0, shv = 0;
-  auto load_raw = [&](long long tok0) {
-    const unsigned long long tg = (unsigned long long)(tok0 + tl);
-    const bool ok = (long long)tg < t_end;
-    const unsigned long long SK = tg * Bk + QK.off, SV = tg * Bv + QV.off;
-    shk = (unsigned)(SK & 31u);
-    shv = (unsigned)(SV & 31u);
-    if (Bk) load_quarter_raw(gk, SK >> 5, sdwK, ok, QK.nw, rawk);
-    if (Bv) load_quarter_raw(gv, SV >> 5, sdwV, ok, QV.nw, rawv);
-  };
-  if (t_begin < t_end) load_raw(t_begin);
-
-  // Score A operand, built while the first tile's words are in flight:
-  // a_hj = (U_K^T q_h)_j step_j scale log2(e) as bf16 high and low parts,
-  // rows = query heads (padded to 16). Thread (part, j) sums rows
-  // 16*part..+15 of column j of U_K; the 8 parts are added through LDS
-  // scratch that the tile loop reuses afterwards.
+  if (tid < 128) {
+    att_tables(hk, sTab, tid);
+    att_tables(hv, sTab + 384, tid);
+  }
+  // Score A operand: a_hj = (U_K^T q_h)_j step_j scale log2(e) as bf16 high
+  // (rows 0..15) and low (rows 16..31) parts. Thread (part, j) sums rows
+  // part, part + 8, .. of column j of U_K; the parts are added through LDS
+  // scratch in the wave regions, which the blocks reuse afterwards.
   {
-    float* sq = reinterpret_cast<float*>(smem);              // q [16][128]
-    float* red = sq + 16 * 128;                               // [8][16][128]
+    float* sq = reinterpret_cast<float*>(sReg0);  // q [16][128]
+    float* red = sq + 16 * 128;                   // [8][16][128]
     const int j = tid & 127, part = tid >> 7;
-    const int g = a.group;
+    const int nparts = (int)(blockDim.x >> 7);
     const float* u = reinterpret_cast<const float*>(kst + OFF_U32);
-    float uc[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) uc[r] = u[(16 * part + r) * 128 + j];
     const float* qp = a.q + p * g * 128;
-    for (int e = tid; e < g * 128; e += ATT_THREADS) sq[e] = qp[e];
+    for (int e = tid; e < g * 128; e += blockDim.x) sq[e] = qp[e];
     __syncthreads();
+    float acc[16];
 #pragma unroll
-    for (int h = 0; h < 16; ++h) {
-      if (h < g) {
-        float acc = 0.0f;
+    for (int hh = 0; hh < 16; ++hh) acc[hh] = 0.0f;
+    for (int r = part; r < 128; r += nparts) {
+      const float ur = u[r * 128 + j];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc = __builtin_fmaf(uc[r], sq[h * 128 + 16 * part + r], acc);
-        red[(part * 16 + h) * 128 + j] = acc;
-      }
+      for (int hh = 0; hh < 16; ++hh)
+        if (hh < g) acc[hh] = __builtin_fmaf(ur, sq[hh * 128 + r], acc[hh]);
     }
-    __syncthreads();
-    for (int e = tid; e < 16 * 128; e += ATT_THREADS) {
-      const int h = e >> 7, c = e & 127;
-      float val = 0.0f;
-      if (h < g && hk->bits[c] > 0) {
-        float sum = 0.0f;
 #pragma unroll
-        for (int pt = 0; pt < 8; ++pt) sum += red[(pt * 16 + h) * 128 + c];
+    for (int hh = 0; hh < 16; ++hh)
+      if (hh < g) red[(part * 16 + hh) * 128 + j] = acc[hh];
+    __syncthreads();
+    for (int e = tid; e < 16 * 128; e += blockDim.x) {
+      const int hh = e >> 7, c = e & 127;
+      float val = 0.0f;
+      if (hh < g && hk->bits[c] > 0) {
+        float sum = 0.0f;
+        for (int pt = 0; pt < nparts; ++pt) sum += red[(pt * 16 + hh) * 128 + c];
         val = sum * hk->step32[c] * a.scale * LOG2E;
       }
       const __bf16 hi = (__bf16)val;
       const __bf16 lo = (__bf16)(val - (float)hi);
-      *reinterpret_cast<__bf16*>(sA + h * AROW + 2 * c) = hi;
-      *reinterpret_cast<__bf16*>(sA + (16 + h) * AROW + 2 * c) = lo;
+      *reinterpret_cast<__bf16*>(sA + hh * AROW + 2 * c) = hi;
+      *reinterpret_cast<__bf16*>(sA + (16 + hh) * AROW + 2 * c) = lo;
     }
-    // the tile loop starts with a barrier: sA is complete and the scratch free
+    __syncthreads();
   }
-  float m_run[4], l_run[4];
+
+  // per-wave online softmax state: heads H = 8i + 4h + j in the score
+  // layout (m replicated over the half, l partial per lane); the value
+  // accumulators in the P.V layout (heads 4*g4 + r, channel 16nb + c16)
+  float m_run[2][4], l_run[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) { m_run[i][j] = -INFINITY; l_run[i][j] = 0.0f; }
   f32x4 acc_o[8];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) { m_run[r] = -INFINITY; l_run[r] = 0.0f; }
-#pragma unroll
-  for (int i = 0; i < 8; ++i) acc_o[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  for (int nb = 0; nb < 8; ++nb) acc_o[nb] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-  for (long long tok0 = t_begin; tok0 < t_end; tok0 += ATT_TILE) {
-    const bool valid = tok0 + tl < t_end;
-    __syncthreads();  // previous tile's compute is done with the code arrays
-    // ---- B: unpack this lane's K and V quarter records
+  const long long PkL = packed_len((long long)Bk, n), PvL = packed_len((long long)Bv, n);
+  const unsigned char* gk = a.k_packed + p * a.packed_stride;
+  const unsigned char* gv = a.v_packed + p * a.packed_stride;
+  const unsigned cwk = (Bk & 3u) == 0u ? 4u : ((Bk & 1u) == 0u ? 2u : 1u);
+  const unsigned cwv = (Bv & 3u) == 0u ? 4u : ((Bv & 1u) == 0u ? 2u : 1u);
+  const bool two_rows = g > 8;
+
+  for (long long tok0 = t_begin + (long long)wave * ATT_BT; tok0 < t_end; tok0 += (long long)nwav * ATT_BT) {
+    // ---- records -> the wave's streams
     {
-      unsigned out[8];
-      stage_quarter(rawk, shk, QK.nw, sCol + tid, ATT_THREADS);
-      if (valid && Bk) unpack_quarter(sCol + tid, ATT_THREADS, QK, out);
-      else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) out[i] = 0u;
+      const long long blk = tok0 / ATT_BT;
+      if (Bk) {
+        const long long st0 = blk * 4LL * (long long)Bk;
+        long long nb_ = 4LL * (long long)Bk;
+        if (nb_ > PkL - st0) nb_ = PkL - st0;
+        if (cwk == 4u) est_copy_in<4>(sKs, gk + st0, nb_, lane);
+        else if (cwk == 2u) est_copy_in<2>(sKs, gk + st0, nb_, lane);
+        else est_copy_in<1>(sKs, gk + st0, nb_, lane);
       }
-      u32x4* krow = reinterpret_cast<u32x4*>(sKc + tl * CROW + 32 * q);
-      krow[0] = (u32x4){out[0], out[1], out[2], out[3]};
-      krow[1] = (u32x4){out[4], out[5], out[6], out[7]};
-      stage_quarter(rawv, shv, QV.nw, sCol + tid, ATT_THREADS);
-      if (valid && Bv) unpack_quarter(sCol + tid, ATT_THREADS, QV, out);
-      else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) out[i] = 0u;
+      if (Bv) {
+        const long long st0 = blk * 4LL * (long long)Bv;
+        long long nb_ = 4LL * (long long)Bv;
+        if (nb_ > PvL - st0) nb_ = PvL - st0;
+        if (cwv == 4u) est_copy_in<4>(sVs, gv + st0, nb_, lane);
+        else if (cwv == 2u) est_copy_in<2>(sVs, gv + st0, nb_, lane);
+        else est_copy_in<1>(sVs, gv + st0, nb_, lane);
       }
-      const int e = tl & 3;
+      __builtin_amdgcn_s_waitcnt(0xc07f);
+      __builtin_amdgcn_wave_barrier();
+    }
+    unsigned kb = lds_offset(reinterpret_cast<unsigned char*>(sTab + 64 * h));
+    unsigned ab = lds_offset(sA + t32 * AROW + 128 * h);
+    asm volatile("" : "+v"(kb), "+v"(ab));
+    const lds_u8* kL = lds_ptr(kb);
+    const lds_u8* vL = kL + 1536;
+    const lds_u8* aL = lds_ptr(ab);
+    const bool tok_ok = tok0 + t32 < t_end;
+    // ---- scores: channels 64h + 8ks + i of token t as bf16 B fragments
+    float sc[2][4];
+    {
+      f32x16 acc;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const unsigned t4 = quad_transpose_bytes(out[i], e);
-        *reinterpret_cast<unsigned*>(sVc + (32 * q + 4 * i + e) * VCROW + (tl & ~3)) = t4;
+      for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
+      const unsigned tB = (unsigned)t32 * Bk;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        bf16x8 bf;
+#pragma unroll
+        for (int hg = 0; hg < 2; ++hg) {
+          const unsigned v = Bk ? att_group_bytes(sKs, kL, tB, 2 * ks + hg) : 0u;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) bf[4 * hg + j] = (__bf16)(float)((v >> (8 * j)) & 0xffu);
+        }
+        acc = mfma32_bf16(LDS_AT(bf16x8, aL + 16 * ks), bf, acc);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int H = 8 * i + 4 * h + j;
+          sc[i][j] = (tok_ok && H < g) ? acc[4 * i + j] + acc[4 * (i + 2) + j] : -INFINITY;
+        }
+    }
+    // ---- V codes of the lane's 16 groups (bytes)
+    unsigned gvb[16];
+    {
+      const unsigned tB = (unsigned)t32 * Bv;
+#pragma unroll
+      for (int gg = 0; gg < 16; ++gg) gvb[gg] = Bv ? att_group_bytes(sVs, vL, tB, gg) : 0u;
+    }
+    // ---- online softmax; P (fp16) -> sP[head][token], alpha -> sAl
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      if (i == 1 && !two_rows) break;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int H = 8 * i + 4 * h + j;
+        const float mx = half_max(sc[i][j]);
+        const float mnew = fmaxf(m_run[i][j], mx);
+        const float alpha = (mnew == -INFINITY) ? 1.0f : exp2f(m_run[i][j] - mnew);
+        const float pv = (mnew == -INFINITY) ? 0.0f : exp2f(sc[i][j] - mnew);
+        const _Float16 ph = (_Float16)pv;
+        l_run[i][j] = l_run[i][j] * alpha + (float)ph;
+        m_run[i][j] = mnew;
+        sP[H * P_ROWH + t32] = ph;
+        if (t32 == 0) sAl[H] = alpha;
       }
     }
-    if (tok0 + ATT_TILE < t_end) load_raw(tok0 + ATT_TILE);
-    __syncthreads();
-    // ---- C: scores for tokens 16*wave..+15
-    f32x4 sc = (f32x4){0.f, 0.f, 0.f, 0.f};
+    if (!two_rows) {
+      // rows 8..15 of P are never read into a live accumulator row, but
+      // keep them finite
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      if (ks < ksK) {
-        const u32x2 v = *reinterpret_cast<const u32x2*>(sKc + (16 * wave + r16) * CROW + 32 * ks + 8 * g4);
-        const bf16x8 b = bytes_to_bf16x8(v);
-        const bf16x8 ah = *reinterpret_cast<const bf16x8*>(sA + r16 * AROW + (32 * ks + 8 * g4) * 2);
-        const bf16x8 al = *reinterpret_cast<const bf16x8*>(sA + (16 + r16) * AROW + (32 * ks + 8 * g4) * 2);
-        sc = mfma_bf16(ah, b, sc);
-        sc = mfma_bf16(al, b, sc);
+      for (int j = 0; j < 4; ++j) sP[(8 + 4 * h + j) * P_ROWH + t32] = (_Float16)0.0f;
+      if (t32 == 0) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sAl[8 + 4 * h + j] = 1.0f;
       }
     }
-    if (tok0 + 16 * wave + r16 >= t_end) sc = (f32x4){-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-    // online softmax; lane rows are heads 4*g4 + r, column = token r16
-    _Float16* myP = sP + wave * 16 * PROW;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float mt = grp16_max(sc[r]);
-      const float mnew = fmaxf(m_run[r], mt);
-      const float alpha = (mnew == -INFINITY) ? 1.0f : exp2f(m_run[r] - mnew);
-      const float pv = (mnew == -INFINITY) ? 0.0f : exp2f(sc[r] - mnew);
-      const _Float16 ph = (_Float16)pv;
-      l_run[r] = l_run[r] * alpha + (float)ph;
-      m_run[r] = mnew;
-      myP[(4 * g4 + r) * PROW + r16] = ph;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) acc_o[i][r] *= alpha;
-    }
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's P writes have landed
+    // ---- V bytes -> [channel][token] (quads of lanes = 4 consecutive tokens)
+    __builtin_amdgcn_s_waitcnt(0xc07f);
     __builtin_amdgcn_wave_barrier();
-    // P (heads x 16 tokens) x V codes (16 tokens x channels)
     {
-      const f16x4 pa = *reinterpret_cast<const f16x4*>(myP + r16 * PROW + 4 * g4);
+      const int e = t32 & 3;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        if (i < ntV) {
-          const unsigned v = *reinterpret_cast<const unsigned*>(sVc + (16 * i + r16) * VCROW + 16 * wave + 4 * g4);
-          acc_o[i] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, bytes_to_f16x4(v), acc_o[i], 0, 0, 0);
+      for (int gg = 0; gg < 16; ++gg) {
+        const unsigned tq = quad_transpose_bytes(gvb[gg], e);
+        sVT[(64 * h + 4 * gg + e) * VT_ROW + (t32 >> 2)] = tq;
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    __builtin_amdgcn_wave_barrier();
+    // ---- rescale and accumulate P x V: heads 4*g4 + r, channels 16nb + c16
+    {
+      const f32x4 al = *reinterpret_cast<const f32x4*>(sAl + 4 * g4);
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc_o[nb][r] *= al[r];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        const f16x4 pa = *reinterpret_cast<const f16x4*>(sP + c16 * P_ROWH + 16 * kt + 4 * g4);
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb) {
+          const unsigned vb = sVT[(16 * nb + c16) * VT_ROW + 4 * kt + g4];
+          acc_o[nb] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, bytes_to_f16x4(vb), acc_o[nb], 0, 0, 0);
         }
       }
     }
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    __builtin_amdgcn_wave_barrier();
   }
+  // ---- l over the half's tokens
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) l_run[i][j] = half_sum(l_run[i][j]);
+  // ---- merge the waves, four heads at a time: scratch [wave][4][130]
   __syncthreads();
-  // fold waves 8..15 into waves 0..7 (same lane positions), through LDS:
-  // [8 waves][40 values][64 lanes] = 80 KiB over the code arrays
-  {
-    float* xs = reinterpret_cast<float*>(smem) + (wave & 7) * 40 * 64 + lane;
-    if (wave >= 8) {
+  float* red = reinterpret_cast<float*>(sReg0);
+  float* part = reinterpret_cast<float*>(a.ws) + ((p * a.n_splits + sp) * g) * ATT_PART_FLOATS;
+  for (int c4 = 0; c4 * 4 < g; ++c4) {
+    float* mine = red + wave * 4 * ATT_PART_FLOATS;
+    // m, l of heads 4*c4 .. +3: H = 8i + 4h + j
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        xs[r * 64] = m_run[r];
-        xs[(4 + r) * 64] = l_run[r];
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) xs[(8 + 4 * i + r) * 64] = acc_o[i][r];
+      for (int j = 0; j < 4; ++j) {
+        const int H = 8 * i + 4 * h + j;
+        if (t32 == 0 && (H >> 2) == c4) {
+          mine[(H & 3) * ATT_PART_FLOATS + 128] = m_run[i][j];
+          mine[(H & 3) * ATT_PART_FLOATS + 129] = l_run[i][j];
+        }
       }
+    if (g4 == c4) {
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mine[r * ATT_PART_FLOATS + 16 * nb + c16] = acc_o[nb][r];
     }
     __syncthreads();
-    if (wave < 8) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float m2 = xs[r * 64];
-        const float mnew = fmaxf(m_run[r], m2);
-        const float f1 = (m_run[r] == -INFINITY) ? 0.0f : exp2f(m_run[r] - mnew);
-        const float f2 = (m2 == -INFINITY) ? 0.0f : exp2f(m2 - mnew);
-        l_run[r] = l_run[r] * f1 + xs[(4 + r) * 64] * f2;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) acc_o[i][r] = acc_o[i][r] * f1 + xs[(8 + 4 * i + r) * 64] * f2;
-        m_run[r] = mnew;
+    const int nh = g - 4 * c4 < 4 ? g - 4 * c4 : 4;
+    for (int e = tid; e < nh * 128; e += blockDim.x) {
+      const int hh = e >> 7, jj = e & 127;
+      float M = -INFINITY;
+      for (int w = 0; w < nwav; ++w) M = fmaxf(M, red[(w * 4 + hh) * ATT_PART_FLOATS + 128]);
+      float A = 0.0f, Ls = 0.0f;
+      for (int w = 0; w < nwav; ++w) {
+        const float* rw = red + (w * 4 + hh) * ATT_PART_FLOATS;
+        const float f = (rw[128] == -INFINITY) ? 0.0f : exp2f(rw[128] - M);
+        A += f * rw[jj];
+        Ls += f * rw[129];
       }
+      float* ph = part + (4 * c4 + hh) * ATT_PART_FLOATS;
+      ph[jj] = A;
+      if (jj == 0) { ph[128] = M; ph[129] = Ls; }
     }
     __syncthreads();
-  }
-  // merge the eight remaining waves: scratch [8 waves][16 heads][130]
-  float* red = reinterpret_cast<float*>(smem);
-  if (wave < 8) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float lsum = grp16_sum(l_run[r]);
-      const int hrow = 4 * g4 + r;
-      float* base = red + (wave * 16 + hrow) * ATT_PART_FLOATS;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) base[16 * i + r16] = acc_o[i][r];
-      if (r16 == 0) { base[128] = m_run[r]; base[129] = lsum; }
-    }
-  }
-  __syncthreads();
-  float* part = reinterpret_cast<float*>(a.ws) +
-                ((p * a.n_splits + sp) * a.group) * ATT_PART_FLOATS;
-  for (int e = tid; e < a.group * 128; e += ATT_THREADS) {
-    const int h = e >> 7, j = e & 127;
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < 8; ++w) M = fmaxf(M, red[(w * 16 + h) * ATT_PART_FLOATS + 128]);
-    float A = 0.0f, Ls = 0.0f;
-#pragma unroll
-    for (int w = 0; w < 8; ++w) {
-      const float mw = red[(w * 16 + h) * ATT_PART_FLOATS + 128];
-      const float f = (mw == -INFINITY) ? 0.0f : exp2f(mw - M);
-      A += f * red[(w * 16 + h) * ATT_PART_FLOATS + j];
-      Ls += f * red[(w * 16 + h) * ATT_PART_FLOATS + 129];
-    }
-    part[h * ATT_PART_FLOATS + j] = A;
-    if (j == 0) { part[h * ATT_PART_FLOATS + 128] = M; part[h * ATT_PART_FLOATS + 129] = Ls; }
   }
 }
 
@@ -1359,7 +1436,7 @@ __global__ void __launch_bounds__(CMB_THREADS, 1) k_att_combine(AttK a) {
 
 int launch_attend(const AttendLaunch& L, void* stream) {
   if (!g_att_attr_done) {
-    (void)hipFuncSetAttribute((const void*)k_att_main, hipFuncAttributeMaxDynamicSharedMemorySize, (int)ATT_LDS);
+    (void)hipFuncSetAttribute((const void*)k_att_main, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     (void)hipFuncSetAttribute((const void*)k_att_combine, hipFuncAttributeMaxDynamicSharedMemorySize,
                               (int)((128 * CMB_UROW + 16 * ATT_PART_FLOATS) * 4 + CMB_MAX_SPLITS * 16 * 4));
     g_att_attr_done = true;
@@ -1382,9 +1459,14 @@ int launch_attend(const AttendLaunch& L, void* stream) {
   a.ws = L.ws;
   a.split_tokens = att_split_tokens(L.n_pairs, L.n_tokens);
   a.n_splits = att_n_splits(L.n_pairs, L.n_tokens);
+  a.stream_words = att_stream_words(L.max_bits);
+  a.region_words = att_region_words(L.max_bits);
+  int waves = ATT_WAVES_MAX;
+  while (waves > 4 && ATT_FIXED_BYTES + (size_t)waves * a.region_words * 4 > 160 * 1024) waves -= 4;
+  const size_t att_lds = ATT_FIXED_BYTES + (size_t)waves * a.region_words * 4;
   hipStream_t s = (hipStream_t)stream;
   const size_t cmb_lds = (size_t)(128 * CMB_UROW + 16 * ATT_PART_FLOATS) * 4 + (size_t)a.n_splits * L.group * 4;
-  hipLaunchKernelGGL(k_att_main, dim3((unsigned)a.n_splits, (unsigned)L.n_pairs), dim3(ATT_THREADS), ATT_LDS, s, a);
+  hipLaunchKernelGGL(k_att_main, dim3((unsigned)a.n_splits, (unsigned)L.n_pairs), dim3(64 * waves), att_lds, s, a);
   hipLaunchKernelGGL(k_att_combine, dim3((unsigned)L.n_pairs), dim3(CMB_THREADS), cmb_lds, s, a);
   return hipGetLastError() != hipSuccess;
 }
