@@ -159,7 +159,7 @@ def main():
               for b in budgets}
     xhat = torch.empty((S, n, 128), dtype=torch.bfloat16, device=dev)
     attn_out = {b: torch.empty((heads, g, 128), dtype=torch.float32, device=dev) for b in budgets}
-    ws = torch.empty(stc.attend_workspace_bytes(heads, g, n), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(stc.attend_workspace_bytes(heads, g, n), dtype=torch.uint8, device=dev)
     rpacked = torch.empty((S, stc.packed_bytes(384, n)), dtype=torch.uint8, device=dev)
     rnorms = torch.empty((S, n), dtype=torch.float32, device=dev)
     setup_s = time.time() - t_setup

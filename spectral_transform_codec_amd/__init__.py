@@ -267,7 +267,7 @@ def attend_compressed(k_state: State, v_state: State, k_packed: torch.Tensor, v_
     out = torch.empty((g, D), dtype=torch.float32, device=q.device)
     need = attend_workspace_bytes(1, g, n)
     if ws is None or ws.numel() < need:
-        ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+        ws = torch.zeros(need, dtype=torch.uint8, device=q.device)  # zero-filled once
     check("stc_attend_compressed", lib().stc_attend_compressed(
         ctypes.byref(k_state.info), _ptr(k_state.blob), ctypes.byref(v_state.info), _ptr(v_state.blob), n,
         _ptr(k_packed), _ptr(v_packed), g, _ptr(q), _ptr(out), float(scale), _ptr(ws), ws.numel(), _stream()))
@@ -286,7 +286,7 @@ def attend_compressed_batched(states: StateArray, k_state_of_pair: torch.Tensor,
         out = torch.empty((Pn, g, D), dtype=torch.float32, device=q.device)
     need = attend_workspace_bytes(Pn, g, n)
     if ws is None or ws.numel() < need:
-        ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+        ws = torch.zeros(need, dtype=torch.uint8, device=q.device)  # zero-filled once
     check("stc_attend_compressed_batched", lib().stc_attend_compressed_batched(
         _ptr(states.blob), states.n, _ptr(_map_arg(k_state_of_pair)), _ptr(_map_arg(v_state_of_pair)),
         states.infos, Pn, n, _ptr(k_packed), _ptr(v_packed), k_packed.stride(0), g, _ptr(q), _ptr(out),

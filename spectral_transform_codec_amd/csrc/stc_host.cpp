@@ -337,9 +337,11 @@ size_t stc_packed_bytes(int32_t total_bits, int64_t n_tokens) {
 
 size_t stc_attend_workspace_bytes(int64_t n_pairs, int32_t group, int64_t n_tokens) {
   if (n_pairs <= 0 || n_tokens <= 0 || group <= 0) return 256;
-  const int64_t splits = att_n_splits(n_pairs, n_tokens);
-  size_t parts = (size_t)n_pairs * splits * group * ATT_PART_FLOATS * sizeof(float);
-  return (parts + 255) / 256 * 256;
+  // one launch covers at most ATT_MAX_PAIRS pairs; launches reuse the partials
+  const int64_t np = n_pairs < ATT_MAX_PAIRS ? n_pairs : ATT_MAX_PAIRS;
+  const int64_t splits = att_n_splits(np, n_tokens);
+  size_t parts = (size_t)np * splits * group * ATT_PART_FLOATS * sizeof(float);
+  return ATT_CNT_BYTES + (parts + 255) / 256 * 256;
 }
 
 int32_t stc_total_bits(float avg_bits, int32_t d) {

@@ -94,6 +94,11 @@ inline int64_t att_n_splits(int64_t n_pairs, int64_t n_tokens) {
   return (n_tokens + s - 1) / s;
 }
 constexpr int ATT_PART_FLOATS = D + 2;              // per (pair, split, head): acc[128], m, l
+// Attention workspace: a per-pair completion counter in a fixed area at the
+// front (zero before the first call, left at zero by every call), then the
+// split partials. A launch covers at most ATT_MAX_PAIRS pairs.
+constexpr size_t ATT_CNT_BYTES = 64 * 1024;
+constexpr int64_t ATT_MAX_PAIRS = (int64_t)(ATT_CNT_BYTES / 4);
 
 // Host-side launchers implemented in stc_kernels.hip.
 struct EncodeLaunch {

@@ -398,9 +398,9 @@ static bool g_enc_attr_done = false, g_dec_attr_done = false, g_att_attr_done = 
 
 int launch_encode_eigen(const EncodeLaunch& L, void* stream) {
   if (!g_enc_attr_done) {
-    (void)hipFuncSetAttribute((const void*)k_encode_eigen<0>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)ENC_LDS);
-    (void)hipFuncSetAttribute((const void*)k_encode_eigen<1>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)ENC_LDS);
-    (void)hipFuncSetAttribute((const void*)k_encode_eigen<2>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)ENC_LDS);
+    if (hipFuncSetAttribute((const void*)k_encode_eigen<0>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)ENC_LDS) != hipSuccess) return 1;
+    if (hipFuncSetAttribute((const void*)k_encode_eigen<1>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)ENC_LDS) != hipSuccess) return 1;
+    if (hipFuncSetAttribute((const void*)k_encode_eigen<2>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)ENC_LDS) != hipSuccess) return 1;
     g_enc_attr_done = true;
   }
   EncK a;
@@ -529,25 +529,42 @@ struct DecK {
   int grid;
 };
 
-// HBM bytes [0, nbytes) of a block -> wave stream (CW-word loads), with the
-// word following each 32-word run repeated in the pad slot before it.
-template <int CW>
-__device__ __forceinline__ void est_copy_in(unsigned* str, const unsigned char* src, long long nbytes, int lane) {
-  typedef unsigned vec __attribute__((ext_vector_type(CW)));
-  const int nchunk = (int)(nbytes / (4 * CW));
-  for (int c = lane; c < nchunk; c += 64) {
-    const vec v = reinterpret_cast<const vec*>(src)[c];
+// HBM bytes [0, nbytes) of a block (32 records of at most 64*NW bits, 4-byte
+// aligned) -> wave stream, in two steps so that every load of a block is in
+// flight at once: est_load issues dword loads (lane l takes words l, l + 64,
+// ..; 256 contiguous bytes per instruction, scalar base) into NW registers;
+// est_store writes them with the word following each 32-word run repeated in
+// the pad slot before it.
+__device__ __forceinline__ const unsigned* uniform_ptr(const unsigned char* p) {
+  const unsigned long long v = (unsigned long long)(uintptr_t)p;
+  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)v), hi = __builtin_amdgcn_readfirstlane((unsigned)(v >> 32));
+  return reinterpret_cast<const unsigned*>((uintptr_t)(((unsigned long long)hi << 32) | lo));
+}
+template <int NW>
+__device__ __forceinline__ void est_load(unsigned (&w)[NW], const unsigned char* src, long long nbytes, int lane) {
+  const int nw = (int)(nbytes >> 2);
+  const unsigned* s32 = uniform_ptr(src);
 #pragma unroll
-    for (int e = 0; e < CW; ++e) {
-      const unsigned w = (unsigned)(CW * c + e);
-      const unsigned ix = est_idx(w);
-      str[ix] = v[e];
-      if ((w & 31u) == 0u && w > 0u) str[ix - 1] = v[e];
+  for (int k = 0; k < NW; ++k) {
+    const int c = lane + 64 * k;
+    w[k] = c < nw ? s32[(unsigned)c] : 0u;
+  }
+}
+template <int NW>
+__device__ __forceinline__ void est_store(unsigned* str, const unsigned (&w)[NW], long long nbytes, int lane) {
+  const int nw = (int)(nbytes >> 2);
+#pragma unroll
+  for (int k = 0; k < NW; ++k) {
+    const unsigned c = (unsigned)(lane + 64 * k);
+    if ((int)c < nw) {
+      const unsigned ix = est_idx(c);
+      str[ix] = w[k];
+      if ((c & 31u) == 0u && c > 0u) str[ix - 1] = w[k];
     }
   }
 }
 
-template <int F32OUT>
+template <int F32OUT, int NW>
 __global__ void __launch_bounds__(DEC_THREADS, 1) k_decode_eigen(DecK a) {
   extern __shared__ __align__(16) unsigned char smem[];
   unsigned char* sWhi = smem;
@@ -598,9 +615,9 @@ __global__ void __launch_bounds__(DEC_THREADS, 1) k_decode_eigen(DecK a) {
         long long nbytes = 4LL * (long long)B;
         if (nbytes > P_len - start) nbytes = P_len - start;
         const unsigned char* src = a.packed + s * a.packed_stride + start;
-        if (cw_kind == 4u) est_copy_in<4>(sStr, src, nbytes, lane);
-        else if (cw_kind == 2u) est_copy_in<2>(sStr, src, nbytes, lane);
-        else est_copy_in<1>(sStr, src, nbytes, lane);
+        unsigned wr[NW];
+        est_load<NW>(wr, src, nbytes, lane);
+        est_store<NW>(sStr, wr, nbytes, lane);
         __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
         __builtin_amdgcn_wave_barrier();
       }
@@ -707,8 +724,10 @@ __global__ void __launch_bounds__(DEC_THREADS, 1) k_decode_eigen(DecK a) {
 
 int launch_decode_eigen(const DecodeLaunch& L, void* stream) {
   if (!g_dec_attr_done) {
-    (void)hipFuncSetAttribute((const void*)k_decode_eigen<0>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)DEC_LDS);
-    (void)hipFuncSetAttribute((const void*)k_decode_eigen<1>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)DEC_LDS);
+    if (hipFuncSetAttribute((const void*)k_decode_eigen<0, 8>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)DEC_LDS) != hipSuccess) return 1;
+    if (hipFuncSetAttribute((const void*)k_decode_eigen<1, 8>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)DEC_LDS) != hipSuccess) return 1;
+    if (hipFuncSetAttribute((const void*)k_decode_eigen<0, 16>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)DEC_LDS) != hipSuccess) return 1;
+    if (hipFuncSetAttribute((const void*)k_decode_eigen<1, 16>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)DEC_LDS) != hipSuccess) return 1;
     g_dec_attr_done = true;
   }
   DecK a;
@@ -732,8 +751,15 @@ int launch_decode_eigen(const DecodeLaunch& L, void* stream) {
   grid = (a.total_blocks + a.blocks_per_wg - 1) / a.blocks_per_wg;
   a.grid = (int)grid;
   hipStream_t s = (hipStream_t)stream;
-  if (L.f32out) hipLaunchKernelGGL(k_decode_eigen<1>, dim3(grid), dim3(DEC_THREADS), DEC_LDS, s, a);
-  else hipLaunchKernelGGL(k_decode_eigen<0>, dim3(grid), dim3(DEC_THREADS), DEC_LDS, s, a);
+  // records of up to 512 bits: 8 staging words per lane, else 16
+  const bool small = L.max_bits <= 512;
+  if (L.f32out) {
+    if (small) hipLaunchKernelGGL((k_decode_eigen<1, 8>), dim3(grid), dim3(DEC_THREADS), DEC_LDS, s, a);
+    else hipLaunchKernelGGL((k_decode_eigen<1, 16>), dim3(grid), dim3(DEC_THREADS), DEC_LDS, s, a);
+  } else {
+    if (small) hipLaunchKernelGGL((k_decode_eigen<0, 8>), dim3(grid), dim3(DEC_THREADS), DEC_LDS, s, a);
+    else hipLaunchKernelGGL((k_decode_eigen<0, 16>), dim3(grid), dim3(DEC_THREADS), DEC_LDS, s, a);
+  }
   return hipGetLastError() != hipSuccess;
 }
 
@@ -920,8 +946,8 @@ int launch_decode_rht(const DecodeLaunch& L, void* stream) {
   const size_t lds = (size_t)RHTD_T * (L.f32out ? 512 + 16 : 256 + 16);
   static bool attr = false;
   if (!attr) {
-    (void)hipFuncSetAttribute((const void*)k_rht_decode, hipFuncAttributeMaxDynamicSharedMemorySize,
-                              RHTD_T * (512 + 16));
+    if (hipFuncSetAttribute((const void*)k_rht_decode, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              RHTD_T * (512 + 16)) != hipSuccess) return 1;
     attr = true;
   }
   hipLaunchKernelGGL(k_rht_decode, grid, dim3(RHTD_T), lds, (hipStream_t)stream, a);
@@ -961,6 +987,7 @@ struct AttK {
   unsigned char* ws;
   long long split_tokens, n_splits;
   int stream_words, region_words;
+  long long pair_base;  // first pair of this launch (maps, caches, q, out); ws is per launch
 };
 
 constexpr int ATT_WAVES_MAX = 16;
@@ -976,7 +1003,7 @@ constexpr int ATT_FIXED_BYTES = 32 * AROW + 6 * 128 * 4;
 // transposed V codes once both are extracted), P, and per-head alpha.
 __host__ __device__ constexpr int att_stream_words(int max_bits) { return max_bits + (max_bits >> 5) + 8; }
 __host__ __device__ constexpr int att_region_words(int max_bits) {
-  return (2 * att_stream_words(max_bits) > VT_WORDS ? 2 * att_stream_words(max_bits) : VT_WORDS) + P_WORDS + 16;
+  return (2 * att_stream_words(max_bits) > VT_WORDS ? 2 * att_stream_words(max_bits) : VT_WORDS) + P_WORDS + 32;
 }
 
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
@@ -1055,6 +1082,86 @@ __device__ __forceinline__ unsigned att_group_bytes(const unsigned* str, const l
   return v;
 }
 
+// Run by the last workgroup of a pair to finish: merge the splits' (acc,
+// m, l) of every query head with log-sum-exp weights (fp32 weights, fp64
+// sums), take the softmax-weighted mean code of every V channel, dequantize
+// it and rotate back with U_V (staged in LDS, rows padded to 129 floats).
+// `cs` is LDS of at least att_combine_lds_bytes(); 512 or 1024 threads.
+constexpr int CMB_UROW = 129;
+constexpr int CMB_MAX_SPLITS = 256;  // att_split_tokens keeps n_splits <= 256
+__host__ __device__ constexpr size_t att_combine_lds_bytes(long long n_splits, int group) {
+  return (size_t)(128 * CMB_UROW + 16 * ATT_PART_FLOATS) * 4 + (size_t)n_splits * group * 4;
+}
+__device__ __forceinline__ void att_combine_pair(const AttK& a, long long p, float* cs) {
+  const long long pg = a.pair_base + p;
+  const int nt = (int)blockDim.x;
+  const int t = threadIdx.x;
+  const int g = a.group;
+  const long long S = a.n_splits;
+  float* sU = cs;                          // [128][129]
+  float* sC = sU + 128 * CMB_UROW;         // per head: 128 weighted code sums, M, L
+  float* sF = sC + 16 * ATT_PART_FLOATS;   // weights [split][head]
+  const float* ps0 = reinterpret_cast<const float*>(a.ws + ATT_CNT_BYTES) + p * S * g * ATT_PART_FLOATS;
+  const unsigned char* vst = a.v_states + (size_t)state_index(a.v_map, pg, a.n_states) * STATE_BYTES;
+  const DevHdr* hv = reinterpret_cast<const DevHdr*>(vst);
+  const f32x4* u4 = reinterpret_cast<const f32x4*>(vst + OFF_U32);
+  // split maxima and U_V into LDS
+  for (long long e = t; e < S * g; e += nt) sF[e] = ps0[e * ATT_PART_FLOATS + 128];
+  for (int e4 = t; e4 < 4096; e4 += nt) {
+    const f32x4 v = u4[e4];
+    const int row = e4 >> 5, col = 4 * (e4 & 31);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) sU[row * CMB_UROW + col + c] = v[c];
+  }
+  __syncthreads();
+  if (t < g) {
+    float M = -INFINITY;
+    for (long long s2 = 0; s2 < S; ++s2) M = fmaxf(M, sF[s2 * g + t]);
+    sC[t * ATT_PART_FLOATS + 128] = M;
+  }
+  __syncthreads();
+  for (long long e = t; e < S * g; e += nt) {
+    const float ms = sF[e];
+    sF[e] = (ms == -INFINITY) ? 0.0f : exp2f(ms - sC[(int)(e % g) * ATT_PART_FLOATS + 128]);
+  }
+  __syncthreads();
+  // weighted sums over the splits of the code sums (j < 128) and of l
+  // (j = 129), fp64; thread per (head, j), loads in batches of 8
+  for (int e = t; e < g * ATT_PART_FLOATS; e += nt) {
+    const int h = e / ATT_PART_FLOATS, j = e - h * ATT_PART_FLOATS;
+    if (j == 128) continue;
+    double A = 0.0;
+    long long s2 = 0;
+    for (; s2 + 8 <= S; s2 += 8) {
+      float v[8];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) v[r] = ps0[((s2 + r) * g + h) * ATT_PART_FLOATS + j];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) A += (double)(sF[(s2 + r) * g + h] * v[r]);
+    }
+    for (; s2 < S; ++s2) A += (double)(sF[s2 * g + h] * ps0[(s2 * g + h) * ATT_PART_FLOATS + j]);
+    sC[e] = (float)A;
+  }
+  __syncthreads();
+  // dequantize the mean codes: step * (A / L - (L_j - 1)/2)
+  for (int hj = t; hj < g * 128; hj += nt) {
+    const int h = hj >> 7, j = hj & 127;
+    float* c = sC + h * ATT_PART_FLOATS;
+    c[j] = hv->bits[j] ? (float)((double)hv->step32[j] * ((double)c[j] / (double)c[129] - (double)hv->halfspan[j]))
+                       : 0.0f;
+  }
+  __syncthreads();
+  // rotate back: o_i = sum_k U_ik chat_k
+  for (int hi = t; hi < g * 128; hi += nt) {
+    const int h = hi >> 7, i = hi & 127;
+    float o = 0.0f;
+#pragma unroll 16
+    for (int k = 0; k < 128; ++k) o = __builtin_fmaf(sU[i * CMB_UROW + k], sC[h * ATT_PART_FLOATS + k], o);
+    a.out[(pg * g + h) * 128 + i] = o;
+  }
+}
+
+template <int NW>
 __global__ void __launch_bounds__(ATT_THREADS, 1) k_att_main(AttK a) {
   extern __shared__ __align__(16) unsigned char smem[];
   unsigned char* sA = smem;                                        // a table [32][AROW]
@@ -1066,11 +1173,13 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_att_main(AttK a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int t32 = lane & 31, h = lane >> 5;
   const int c16 = lane & 15, g4 = lane >> 4;
-  const long long sp = blockIdx.x, p = blockIdx.y;
+  const long long sp = blockIdx.x, p = blockIdx.y;  // split, pair within this launch
+  const long long pg = a.pair_base + p;
   const long long n = a.n_tokens;
   const int g = a.group;
-  const unsigned char* kst = a.k_states + (size_t)state_index(a.k_map, p, a.n_states) * STATE_BYTES;
-  const unsigned char* vst = a.v_states + (size_t)state_index(a.v_map, p, a.n_states) * STATE_BYTES;
+  const bool two_rows = g > 8;  // query heads 8..15 in use
+  const unsigned char* kst = a.k_states + (size_t)state_index(a.k_map, pg, a.n_states) * STATE_BYTES;
+  const unsigned char* vst = a.v_states + (size_t)state_index(a.v_map, pg, a.n_states) * STATE_BYTES;
   const DevHdr* hk = reinterpret_cast<const DevHdr*>(kst);
   const DevHdr* hv = reinterpret_cast<const DevHdr*>(vst);
   const unsigned Bk = (unsigned)__builtin_amdgcn_readfirstlane(hk->total_bits);
@@ -1081,6 +1190,7 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_att_main(AttK a) {
   unsigned* sVT = sKs;                             // [channel][token] V bytes, after extraction
   _Float16* sP = reinterpret_cast<_Float16*>(sKs + (2 * SW > VT_WORDS ? 2 * SW : VT_WORDS));
   float* sAl = reinterpret_cast<float*>(sP + 16 * P_ROWH);  // alpha per head
+  float* sM = sAl + 16;                                     // running max per head
   const long long t_begin = sp * a.split_tokens;
   long long t_end = t_begin + a.split_tokens;
   if (t_end > n) t_end = n;
@@ -1094,26 +1204,38 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_att_main(AttK a) {
   // part, part + 8, .. of column j of U_K; the parts are added through LDS
   // scratch in the wave regions, which the blocks reuse afterwards.
   {
-    float* sq = reinterpret_cast<float*>(sReg0);  // q [16][128]
-    float* red = sq + 16 * 128;                   // [8][16][128]
+    float* sqT = reinterpret_cast<float*>(sReg0);  // q transposed [128][16], zero for heads >= g
+    float* red = sqT + 128 * 16;                    // [nparts][16][128]
     const int j = tid & 127, part = tid >> 7;
     const int nparts = (int)(blockDim.x >> 7);
     const float* u = reinterpret_cast<const float*>(kst + OFF_U32);
-    const float* qp = a.q + p * g * 128;
-    for (int e = tid; e < g * 128; e += blockDim.x) sq[e] = qp[e];
+    const float* qp = a.q + pg * g * 128;
+    const int rows = 128 / nparts;  // 16 (1024 threads) or 32 (512)
+    float ur[32];
+#pragma unroll
+    for (int k = 0; k < 32; ++k) ur[k] = k < rows ? u[(part + k * nparts) * 128 + j] : 0.0f;  // issued together
+    for (int e = tid; e < 128 * 16; e += blockDim.x) {
+      const int r = e >> 4, hh = e & 15;
+      sqT[e] = hh < g ? qp[hh * 128 + r] : 0.0f;
+    }
     __syncthreads();
     float acc[16];
 #pragma unroll
     for (int hh = 0; hh < 16; ++hh) acc[hh] = 0.0f;
-    for (int r = part; r < 128; r += nparts) {
-      const float ur = u[r * 128 + j];
 #pragma unroll
-      for (int hh = 0; hh < 16; ++hh)
-        if (hh < g) acc[hh] = __builtin_fmaf(ur, sq[hh * 128 + r], acc[hh]);
+    for (int k = 0; k < 32; ++k) {
+      if (k < rows) {
+        const f32x4* q4 = reinterpret_cast<const f32x4*>(sqT + (part + k * nparts) * 16);
+#pragma unroll
+        for (int c4 = 0; c4 < 4; ++c4) {
+          const f32x4 qv = q4[c4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[4 * c4 + e] = __builtin_fmaf(ur[k], qv[e], acc[4 * c4 + e]);
+        }
+      }
     }
 #pragma unroll
-    for (int hh = 0; hh < 16; ++hh)
-      if (hh < g) red[(part * 16 + hh) * 128 + j] = acc[hh];
+    for (int hh = 0; hh < 16; ++hh) red[(part * 16 + hh) * 128 + j] = acc[hh];
     __syncthreads();
     for (int e = tid; e < 16 * 128; e += blockDim.x) {
       const int hh = e >> 7, c = e & 127;
@@ -1134,42 +1256,40 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_att_main(AttK a) {
   // per-wave online softmax state: heads H = 8i + 4h + j in the score
   // layout (m replicated over the half, l partial per lane); the value
   // accumulators in the P.V layout (heads 4*g4 + r, channel 16nb + c16)
-  float m_run[2][4], l_run[2][4];
+  float l_run[2][4];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) { m_run[i][j] = -INFINITY; l_run[i][j] = 0.0f; }
+    for (int j = 0; j < 4; ++j) l_run[i][j] = 0.0f;
+  if (lane < 16) sM[lane] = -INFINITY;
+  if (!two_rows) {
+    // heads 8..15 unused: their P rows stay 0 and their alpha 1 (the
+    // blocks only write rows 0..7 then)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sP[(8 + 4 * h + j) * P_ROWH + t32] = (_Float16)0.0f;
+    if (lane < 8) sAl[8 + lane] = 1.0f;
+  }
   f32x4 acc_o[8];
 #pragma unroll
   for (int nb = 0; nb < 8; ++nb) acc_o[nb] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
   const long long PkL = packed_len((long long)Bk, n), PvL = packed_len((long long)Bv, n);
-  const unsigned char* gk = a.k_packed + p * a.packed_stride;
-  const unsigned char* gv = a.v_packed + p * a.packed_stride;
-  const unsigned cwk = (Bk & 3u) == 0u ? 4u : ((Bk & 1u) == 0u ? 2u : 1u);
-  const unsigned cwv = (Bv & 3u) == 0u ? 4u : ((Bv & 1u) == 0u ? 2u : 1u);
-  const bool two_rows = g > 8;
+  const unsigned char* gk = a.k_packed + pg * a.packed_stride;
+  const unsigned char* gv = a.v_packed + pg * a.packed_stride;
 
   for (long long tok0 = t_begin + (long long)wave * ATT_BT; tok0 < t_end; tok0 += (long long)nwav * ATT_BT) {
     // ---- records -> the wave's streams
     {
       const long long blk = tok0 / ATT_BT;
-      if (Bk) {
-        const long long st0 = blk * 4LL * (long long)Bk;
-        long long nb_ = 4LL * (long long)Bk;
-        if (nb_ > PkL - st0) nb_ = PkL - st0;
-        if (cwk == 4u) est_copy_in<4>(sKs, gk + st0, nb_, lane);
-        else if (cwk == 2u) est_copy_in<2>(sKs, gk + st0, nb_, lane);
-        else est_copy_in<1>(sKs, gk + st0, nb_, lane);
-      }
-      if (Bv) {
-        const long long st0 = blk * 4LL * (long long)Bv;
-        long long nb_ = 4LL * (long long)Bv;
-        if (nb_ > PvL - st0) nb_ = PvL - st0;
-        if (cwv == 4u) est_copy_in<4>(sVs, gv + st0, nb_, lane);
-        else if (cwv == 2u) est_copy_in<2>(sVs, gv + st0, nb_, lane);
-        else est_copy_in<1>(sVs, gv + st0, nb_, lane);
-      }
+      const long long stk = blk * 4LL * (long long)Bk, stv = blk * 4LL * (long long)Bv;
+      long long nbk = 4LL * (long long)Bk, nbv = 4LL * (long long)Bv;
+      if (nbk > PkL - stk) nbk = PkL - stk;
+      if (nbv > PvL - stv) nbv = PvL - stv;
+      unsigned wk[NW], wv[NW];
+      est_load<NW>(wk, gk + stk, Bk ? nbk : 0, lane);  // K and V loads in flight together
+      est_load<NW>(wv, gv + stv, Bv ? nbv : 0, lane);
+      est_store<NW>(sKs, wk, Bk ? nbk : 0, lane);
+      est_store<NW>(sVs, wv, Bv ? nbv : 0, lane);
       __builtin_amdgcn_s_waitcnt(0xc07f);
       __builtin_amdgcn_wave_barrier();
     }
@@ -1206,42 +1326,37 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_att_main(AttK a) {
           sc[i][j] = (tok_ok && H < g) ? acc[4 * i + j] + acc[4 * (i + 2) + j] : -INFINITY;
         }
     }
-    // ---- V codes of the lane's 16 groups (bytes)
+    // ---- online softmax; P (fp16) -> sP[head][token], alpha -> sAl
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      if (i == 1 && !two_rows) break;
+      const f32x4 mold = *reinterpret_cast<const f32x4*>(sM + 8 * i + 4 * h);
+      f32x4 mnw;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int H = 8 * i + 4 * h + j;
+        const float mx = half_max(sc[i][j]);
+        const float mnew = fmaxf(mold[j], mx);
+        const float alpha = (mnew == -INFINITY) ? 1.0f : exp2f(mold[j] - mnew);
+        const float pv = (mnew == -INFINITY) ? 0.0f : exp2f(sc[i][j] - mnew);
+        const _Float16 ph = (_Float16)pv;
+        l_run[i][j] = l_run[i][j] * alpha + (float)ph;
+        mnw[j] = mnew;
+        sP[H * P_ROWH + t32] = ph;
+        if (t32 == 0) sAl[H] = alpha;
+      }
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // every lane has read the old maxima
+      __builtin_amdgcn_wave_barrier();
+      if (t32 == 0) *reinterpret_cast<f32x4*>(sM + 8 * i + 4 * h) = mnw;
+    }
+    // ---- V codes of the lane's 16 groups (bytes), then -> [channel][token]
+    // (quads of lanes = 4 consecutive tokens)
     unsigned gvb[16];
     {
       const unsigned tB = (unsigned)t32 * Bv;
 #pragma unroll
       for (int gg = 0; gg < 16; ++gg) gvb[gg] = Bv ? att_group_bytes(sVs, vL, tB, gg) : 0u;
     }
-    // ---- online softmax; P (fp16) -> sP[head][token], alpha -> sAl
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      if (i == 1 && !two_rows) break;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int H = 8 * i + 4 * h + j;
-        const float mx = half_max(sc[i][j]);
-        const float mnew = fmaxf(m_run[i][j], mx);
-        const float alpha = (mnew == -INFINITY) ? 1.0f : exp2f(m_run[i][j] - mnew);
-        const float pv = (mnew == -INFINITY) ? 0.0f : exp2f(sc[i][j] - mnew);
-        const _Float16 ph = (_Float16)pv;
-        l_run[i][j] = l_run[i][j] * alpha + (float)ph;
-        m_run[i][j] = mnew;
-        sP[H * P_ROWH + t32] = ph;
-        if (t32 == 0) sAl[H] = alpha;
-      }
-    }
-    if (!two_rows) {
-      // rows 8..15 of P are never read into a live accumulator row, but
-      // keep them finite
-#pragma unroll
-      for (int j = 0; j < 4; ++j) sP[(8 + 4 * h + j) * P_ROWH + t32] = (_Float16)0.0f;
-      if (t32 == 0) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) sAl[8 + 4 * h + j] = 1.0f;
-      }
-    }
-    // ---- V bytes -> [channel][token] (quads of lanes = 4 consecutive tokens)
     __builtin_amdgcn_s_waitcnt(0xc07f);
     __builtin_amdgcn_wave_barrier();
     {
@@ -1274,15 +1389,19 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_att_main(AttK a) {
     __builtin_amdgcn_s_waitcnt(0xc07f);
     __builtin_amdgcn_wave_barrier();
   }
-  // ---- l over the half's tokens
+  // ---- l over the half's tokens; the maxima out of LDS before it is reused
+  float mfin[2][4];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) l_run[i][j] = half_sum(l_run[i][j]);
+    for (int j = 0; j < 4; ++j) {
+      l_run[i][j] = half_sum(l_run[i][j]);
+      mfin[i][j] = sM[8 * i + 4 * h + j];
+    }
   // ---- merge the waves, four heads at a time: scratch [wave][4][130]
   __syncthreads();
   float* red = reinterpret_cast<float*>(sReg0);
-  float* part = reinterpret_cast<float*>(a.ws) + ((p * a.n_splits + sp) * g) * ATT_PART_FLOATS;
+  float* part = reinterpret_cast<float*>(a.ws + ATT_CNT_BYTES) + ((p * a.n_splits + sp) * g) * ATT_PART_FLOATS;
   for (int c4 = 0; c4 * 4 < g; ++c4) {
     float* mine = red + wave * 4 * ATT_PART_FLOATS;
     // m, l of heads 4*c4 .. +3: H = 8i + 4h + j
@@ -1292,7 +1411,7 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_att_main(AttK a) {
       for (int j = 0; j < 4; ++j) {
         const int H = 8 * i + 4 * h + j;
         if (t32 == 0 && (H >> 2) == c4) {
-          mine[(H & 3) * ATT_PART_FLOATS + 128] = m_run[i][j];
+          mine[(H & 3) * ATT_PART_FLOATS + 128] = mfin[i][j];
           mine[(H & 3) * ATT_PART_FLOATS + 129] = l_run[i][j];
         }
       }
@@ -1321,124 +1440,36 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_att_main(AttK a) {
     }
     __syncthreads();
   }
-}
-
-// One workgroup of 1024 threads per pair: merge the splits' (acc, m, l) of
-// every query head with log-sum-exp weights (fp32 weights, fp64 sums), take
-// the softmax-weighted mean code of every V channel, dequantize it and
-// rotate back with U_V (staged in LDS, rows padded to 129 floats).
-constexpr int CMB_THREADS = 1024;
-constexpr int CMB_UROW = 129;
-constexpr int CMB_MAX_SPLITS = 256;  // att_split_tokens keeps n_splits <= 256
-__global__ void __launch_bounds__(CMB_THREADS, 1) k_att_combine(AttK a) {
-  extern __shared__ __align__(16) float cs[];
-  float* sU = cs;                          // [128][129]
-  float* sC = sU + 128 * CMB_UROW;         // per head: 128 weighted code sums, M, L
-  float* sF = sC + 16 * ATT_PART_FLOATS;   // weights [split][head]
-  const long long p = blockIdx.x;
-  const int t = threadIdx.x;
-  const int g = a.group;
-  const long long S = a.n_splits;
-  const float* ps0 = reinterpret_cast<const float*>(a.ws) + p * S * g * ATT_PART_FLOATS;
-  // Reads that depend on nothing are issued first: this thread's values of
-  // its first (head, j) entry for up to 32 splits and the split maxima; then
-  // the state (one dependent read of the map) with U_V and the quantizer
-  // fields of channel t & 127.
-  constexpr int CB = 32;
-  const int h0 = t / ATT_PART_FLOATS, j0 = t - h0 * ATT_PART_FLOATS;
-  const bool has0 = t < g * ATT_PART_FLOATS && j0 != 128;
-  const int nb0 = S < CB ? (int)S : CB;
-  float v0[CB];
-#pragma unroll
-  for (int r = 0; r < CB; ++r) v0[r] = (has0 && r < nb0) ? ps0[((long long)r * g + h0) * ATT_PART_FLOATS + j0] : 0.0f;
-  float mx[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const long long e = t + (long long)r * CMB_THREADS;
-    mx[r] = e < S * g ? ps0[e * ATT_PART_FLOATS + 128] : 0.0f;
-  }
-  const unsigned char* vst = a.v_states + (size_t)state_index(a.v_map, p, a.n_states) * STATE_BYTES;
-  const DevHdr* hv = reinterpret_cast<const DevHdr*>(vst);
-  const float* u = reinterpret_cast<const float*>(vst + OFF_U32);
-  const int jc = t & 127;
-  const bool keptc = hv->bits[jc] > 0;
-  const double stepc = (double)hv->step32[jc], halfc = (double)hv->halfspan[jc];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const long long e = t + (long long)r * CMB_THREADS;
-    if (e < S * g) sF[e] = mx[r];
-  }
-  {
-    f32x4 uv[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) uv[r] = reinterpret_cast<const f32x4*>(u)[t + r * CMB_THREADS];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int e = 4 * (t + r * CMB_THREADS);
-      const int row = e >> 7, col = e & 127;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) sU[row * CMB_UROW + col + c] = uv[r][c];
-    }
+  // ---- the last split of the pair to finish merges all of them. Every
+  // wave waits until its partial stores have reached L2; after the barrier
+  // one release per workgroup (thread 0's count) writes them back for the
+  // other XCDs, and only the waves of the last workgroup acquire. The counter
+  // of the pair is left at zero for the next call.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  unsigned* cnt = reinterpret_cast<unsigned*>(a.ws) + p;
+  unsigned* flag = reinterpret_cast<unsigned*>(smem);
+  if (tid == 0) {
+    const unsigned prev = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    *flag = prev == (unsigned)(a.n_splits - 1) ? 1u : 0u;
   }
   __syncthreads();
-  // per-head maximum, then split weights
-  if (t < g) {
-    float M = -INFINITY;
-    for (long long s2 = 0; s2 < S; ++s2) M = fmaxf(M, sF[s2 * g + t]);
-    sC[t * ATT_PART_FLOATS + 128] = M;
-  }
-  __syncthreads();
-  for (long long e = t; e < S * g; e += CMB_THREADS) {
-    const int h = (int)(e % g);
-    const float ms = sF[e];
-    sF[e] = (ms == -INFINITY) ? 0.0f : exp2f(ms - sC[h * ATT_PART_FLOATS + 128]);
-  }
-  __syncthreads();
-  // weighted sums over the splits of the code sums (j < 128) and of l
-  // (j = 129), fp64; thread per (head, j)
-  for (int e = t; e < g * ATT_PART_FLOATS; e += CMB_THREADS) {
-    const int h = e / ATT_PART_FLOATS, j = e - h * ATT_PART_FLOATS;
-    if (j == 128) continue;
-    double A = 0.0;
-    long long s2 = 0;
-    if (e == t) {
-#pragma unroll
-      for (int r = 0; r < CB; ++r)
-        if (r < nb0) A += (double)(sF[r * g + h] * v0[r]);
-      s2 = nb0;
-    }
-    for (; s2 + 8 <= S; s2 += 8) {
-      float v[8];
-#pragma unroll
-      for (int r = 0; r < 8; ++r) v[r] = ps0[((s2 + r) * g + h) * ATT_PART_FLOATS + j];
-#pragma unroll
-      for (int r = 0; r < 8; ++r) A += (double)(sF[(s2 + r) * g + h] * v[r]);
-    }
-    for (; s2 < S; ++s2) A += (double)(sF[s2 * g + h] * ps0[(s2 * g + h) * ATT_PART_FLOATS + j]);
-    sC[e] = (float)A;
-  }
-  __syncthreads();
-  for (int hj = t; hj < g * 128; hj += CMB_THREADS) {   // j = hj & 127 = t & 127
-    float* c = sC + (hj >> 7) * ATT_PART_FLOATS + jc;
-    c[0] = keptc ? (float)(stepc * ((double)c[0] / (double)sC[(hj >> 7) * ATT_PART_FLOATS + 129] - halfc)) : 0.0f;
-  }
-  __syncthreads();
-  {
-    const int i = t & 127;
-    for (int h = t >> 7; h < g; h += CMB_THREADS / 128) {
-      float o = 0.0f;
-#pragma unroll 16
-      for (int k = 0; k < 128; ++k) o = __builtin_fmaf(sU[i * CMB_UROW + k], sC[h * ATT_PART_FLOATS + k], o);
-      a.out[(p * g + h) * 128 + i] = o;
-    }
+  const unsigned last = *flag;
+  __syncthreads();  // read by every thread before the merge below reuses the LDS
+  if (last) {
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    att_combine_pair(a, p, reinterpret_cast<float*>(smem));
+    if (tid == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
 int launch_attend(const AttendLaunch& L, void* stream) {
   if (!g_att_attr_done) {
-    (void)hipFuncSetAttribute((const void*)k_att_main, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    (void)hipFuncSetAttribute((const void*)k_att_combine, hipFuncAttributeMaxDynamicSharedMemorySize,
-                              (int)((128 * CMB_UROW + 16 * ATT_PART_FLOATS) * 4 + CMB_MAX_SPLITS * 16 * 4));
+    if (hipFuncSetAttribute((const void*)k_att_main<8>, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) !=
+            hipSuccess ||
+        hipFuncSetAttribute((const void*)k_att_main<16>, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) !=
+            hipSuccess)
+      return 1;
     g_att_attr_done = true;
   }
   AttK a;
@@ -1457,17 +1488,25 @@ int launch_attend(const AttendLaunch& L, void* stream) {
   a.out = L.out;
   a.scale = L.scale;
   a.ws = L.ws;
-  a.split_tokens = att_split_tokens(L.n_pairs, L.n_tokens);
-  a.n_splits = att_n_splits(L.n_pairs, L.n_tokens);
   a.stream_words = att_stream_words(L.max_bits);
   a.region_words = att_region_words(L.max_bits);
   int waves = ATT_WAVES_MAX;
   while (waves > 4 && ATT_FIXED_BYTES + (size_t)waves * a.region_words * 4 > 160 * 1024) waves -= 4;
-  const size_t att_lds = ATT_FIXED_BYTES + (size_t)waves * a.region_words * 4;
   hipStream_t s = (hipStream_t)stream;
-  const size_t cmb_lds = (size_t)(128 * CMB_UROW + 16 * ATT_PART_FLOATS) * 4 + (size_t)a.n_splits * L.group * 4;
-  hipLaunchKernelGGL(k_att_main, dim3((unsigned)a.n_splits, (unsigned)L.n_pairs), dim3(64 * waves), att_lds, s, a);
-  hipLaunchKernelGGL(k_att_combine, dim3((unsigned)L.n_pairs), dim3(CMB_THREADS), cmb_lds, s, a);
+  for (long long c0 = 0; c0 < L.n_pairs; c0 += ATT_MAX_PAIRS) {
+    const long long np = L.n_pairs - c0 < ATT_MAX_PAIRS ? L.n_pairs - c0 : ATT_MAX_PAIRS;
+    a.pair_base = c0;
+    a.n_pairs = np;
+    a.split_tokens = att_split_tokens(np, L.n_tokens);
+    a.n_splits = att_n_splits(np, L.n_tokens);
+    size_t att_lds = ATT_FIXED_BYTES + (size_t)waves * a.region_words * 4;
+    const size_t cmb = att_combine_lds_bytes(a.n_splits, L.group);
+    if (att_lds < cmb) att_lds = cmb;
+    if (L.max_bits <= 512)
+      hipLaunchKernelGGL((k_att_main<8>), dim3((unsigned)a.n_splits, (unsigned)np), dim3(64 * waves), att_lds, s, a);
+    else
+      hipLaunchKernelGGL((k_att_main<16>), dim3((unsigned)a.n_splits, (unsigned)np), dim3(64 * waves), att_lds, s, a);
+  }
   return hipGetLastError() != hipSuccess;
 }
 

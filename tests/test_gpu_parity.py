@@ -316,3 +316,36 @@ def test_rht_batched(rht_codebook):
         assert (qg != qo).mean() <= 1e-4
         r_o = codec.rel_mse(xs[i], rht.decode_kv(ost, po, no, n, "bf16"))
         assert abs(codec.rel_mse(xs[i], dec[i].float().cpu().numpy()) - r_o) <= 1e-3 * r_o
+
+
+def test_attention_workspace_reused_across_shapes():
+    """One zero-filled workspace serves calls of different shapes in turn:
+    every call leaves its completion counters at zero."""
+    w = synth.WORKLOADS[2]
+    cases = [(3, 7, 2100, 2.0), (1, 4, 5000, 4.0), (3, 7, 2100, 2.0), (2, 16, 700, 1.33)]
+    need = max(stc.attend_workspace_bytes(pairs, g, n) for pairs, g, n, _ in cases)
+    ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
+    rng = np.random.default_rng(77)
+    for pairs, g, n, avg in cases:
+        states, kps, vps, qs, wants = [], [], [], [], []
+        for hd in range(pairs):
+            k = synth.stream(w, 0, 0, hd, 0, n=n)
+            v = synth.stream(w, 0, 0, hd, 1, n=n)
+            ks, vs = codec.calibrate_head(k, min(2048, n), avg), codec.calibrate_head(v, min(2048, n), avg)
+            kp, vp = codec.encode_kv(ks, k), codec.encode_kv(vs, v)
+            q = rng.standard_normal((g, 128)).astype(np.float32)
+            wants.append(codec.attend_compressed(ks, vs, kp, vp, n, q.astype(np.float64)))
+            states += [gpu_state(ks), gpu_state(vs)]
+            kps.append(kp); vps.append(vp); qs.append(q)
+        arr = stc.StateArray(states)
+        stride = stc.packed_bytes(arr.max_bits, n)
+        kb = np.zeros((pairs, stride), np.uint8); vb = np.zeros((pairs, stride), np.uint8)
+        for i in range(pairs):
+            kb[i, :kps[i].shape[0]] = kps[i]; vb[i, :vps[i].shape[0]] = vps[i]
+        kmap = torch.arange(0, 2 * pairs, 2, dtype=torch.int32, device=DEV)
+        vmap = kmap + 1
+        out = stc.attend_compressed_batched(arr, kmap, vmap, torch.from_numpy(kb).to(DEV),
+                                            torch.from_numpy(vb).to(DEV), n, torch.from_numpy(np.stack(qs)).to(DEV),
+                                            ws=ws).cpu().numpy()
+        for i in range(pairs):
+            assert rel_err(out[i], wants[i]) <= 2e-3, (pairs, g, n, i, rel_err(out[i], wants[i]))
