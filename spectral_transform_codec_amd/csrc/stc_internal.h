@@ -94,6 +94,11 @@ inline int64_t att_n_splits(int64_t n_pairs, int64_t n_tokens) {
   return (n_tokens + s - 1) / s;
 }
 constexpr int ATT_PART_FLOATS = D + 2;              // per (pair, split, head): acc[128], m, l
+// floats of one (pair, split) partial block: group x (acc, m, l), padded to
+// whole 128-byte lines so that no line is written by two workgroups
+__host__ __device__ inline int64_t att_part_stride(int group) {
+  return ((int64_t)group * ATT_PART_FLOATS + 31) / 32 * 32;
+}
 // Attention workspace: a per-pair completion counter in a fixed area at the
 // front (zero before the first call, left at zero by every call), then the
 // split partials. A launch covers at most ATT_MAX_PAIRS pairs.

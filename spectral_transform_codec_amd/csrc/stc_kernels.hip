@@ -1086,78 +1086,93 @@ __device__ __forceinline__ unsigned att_group_bytes(const unsigned* str, const l
 // m, l) of every query head with log-sum-exp weights (fp32 weights, fp64
 // sums), take the softmax-weighted mean code of every V channel, dequantize
 // it and rotate back with U_V (staged in LDS, rows padded to 129 floats).
+// One thread per (head, channel) reads every split's m, l and acc of its
+// item in batches of 32, all loads of a batch in flight together.
 // `cs` is LDS of at least att_combine_lds_bytes(); 512 or 1024 threads.
 constexpr int CMB_UROW = 129;
-constexpr int CMB_MAX_SPLITS = 256;  // att_split_tokens keeps n_splits <= 256
-__host__ __device__ constexpr size_t att_combine_lds_bytes(long long n_splits, int group) {
-  return (size_t)(128 * CMB_UROW + 16 * ATT_PART_FLOATS) * 4 + (size_t)n_splits * group * 4;
-}
+constexpr int CMB_BATCH = 32;
+__host__ __device__ constexpr size_t att_combine_lds_bytes() { return (size_t)(128 * CMB_UROW + 16 * 128) * 4; }
 __device__ __forceinline__ void att_combine_pair(const AttK& a, long long p, float* cs) {
   const long long pg = a.pair_base + p;
   const int nt = (int)blockDim.x;
   const int t = threadIdx.x;
   const int g = a.group;
-  const long long S = a.n_splits;
-  float* sU = cs;                          // [128][129]
-  float* sC = sU + 128 * CMB_UROW;         // per head: 128 weighted code sums, M, L
-  float* sF = sC + 16 * ATT_PART_FLOATS;   // weights [split][head]
-  const float* ps0 = reinterpret_cast<const float*>(a.ws + ATT_CNT_BYTES) + p * S * g * ATT_PART_FLOATS;
+  const int S = (int)a.n_splits;
+  const long long PS = att_part_stride(g);
+  float* sU = cs;                  // [128][129]
+  float* sC = sU + 128 * CMB_UROW;  // dequantized mean codes [head][128]
+  const float* ps0 = reinterpret_cast<const float*>(a.ws + ATT_CNT_BYTES) + p * (long long)S * PS;
   const unsigned char* vst = a.v_states + (size_t)state_index(a.v_map, pg, a.n_states) * STATE_BYTES;
   const DevHdr* hv = reinterpret_cast<const DevHdr*>(vst);
   const f32x4* u4 = reinterpret_cast<const f32x4*>(vst + OFF_U32);
-  // split maxima and U_V into LDS
-  for (long long e = t; e < S * g; e += nt) sF[e] = ps0[e * ATT_PART_FLOATS + 128];
-  for (int e4 = t; e4 < 4096; e4 += nt) {
-    const f32x4 v = u4[e4];
-    const int row = e4 >> 5, col = 4 * (e4 & 31);
+  {
+    f32x4 uv[8];  // 4096 float4 over 512 or 1024 threads, loads first
 #pragma unroll
-    for (int c = 0; c < 4; ++c) sU[row * CMB_UROW + col + c] = v[c];
-  }
-  __syncthreads();
-  if (t < g) {
-    float M = -INFINITY;
-    for (long long s2 = 0; s2 < S; ++s2) M = fmaxf(M, sF[s2 * g + t]);
-    sC[t * ATT_PART_FLOATS + 128] = M;
-  }
-  __syncthreads();
-  for (long long e = t; e < S * g; e += nt) {
-    const float ms = sF[e];
-    sF[e] = (ms == -INFINITY) ? 0.0f : exp2f(ms - sC[(int)(e % g) * ATT_PART_FLOATS + 128]);
-  }
-  __syncthreads();
-  // weighted sums over the splits of the code sums (j < 128) and of l
-  // (j = 129), fp64; thread per (head, j), loads in batches of 8
-  for (int e = t; e < g * ATT_PART_FLOATS; e += nt) {
-    const int h = e / ATT_PART_FLOATS, j = e - h * ATT_PART_FLOATS;
-    if (j == 128) continue;
-    double A = 0.0;
-    long long s2 = 0;
-    for (; s2 + 8 <= S; s2 += 8) {
-      float v[8];
-#pragma unroll
-      for (int r = 0; r < 8; ++r) v[r] = ps0[((s2 + r) * g + h) * ATT_PART_FLOATS + j];
-#pragma unroll
-      for (int r = 0; r < 8; ++r) A += (double)(sF[(s2 + r) * g + h] * v[r]);
+    for (int r = 0; r < 8; ++r) {
+      const int e4 = t + r * nt;
+      uv[r] = u4[e4 < 4096 ? e4 : 4095];
     }
-    for (; s2 < S; ++s2) A += (double)(sF[s2 * g + h] * ps0[(s2 * g + h) * ATT_PART_FLOATS + j]);
-    sC[e] = (float)A;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int e4 = t + r * nt;
+      if (e4 < 4096) {
+        const int row = e4 >> 5, col = 4 * (e4 & 31);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) sU[row * CMB_UROW + col + c] = uv[r][c];
+      }
+    }
   }
-  __syncthreads();
-  // dequantize the mean codes: step * (A / L - (L_j - 1)/2)
-  for (int hj = t; hj < g * 128; hj += nt) {
-    const int h = hj >> 7, j = hj & 127;
-    float* c = sC + h * ATT_PART_FLOATS;
-    c[j] = hv->bits[j] ? (float)((double)hv->step32[j] * ((double)c[j] / (double)c[129] - (double)hv->halfspan[j]))
-                       : 0.0f;
+  for (int it = t; it < g * 128; it += nt) {
+    const int hh = it >> 7, j = it & 127;
+    const float* ph = ps0 + hh * ATT_PART_FLOATS;
+    const unsigned bits = hv->bits[j];
+    const float step = hv->step32[j], hs = hv->halfspan[j];
+    float M = -INFINITY;
+    double A = 0.0, L = 0.0;
+    for (int s0 = 0; s0 < S; s0 += CMB_BATCH) {
+      float mv[CMB_BATCH], lv[CMB_BATCH], av[CMB_BATCH];
+#pragma unroll
+      for (int r = 0; r < CMB_BATCH; ++r) {
+        const long long s2 = s0 + r < S ? s0 + r : S - 1;
+        mv[r] = ph[s2 * PS + 128];
+        lv[r] = ph[s2 * PS + 129];
+        av[r] = ph[s2 * PS + j];
+      }
+      float Mc = M;
+#pragma unroll
+      for (int r = 0; r < CMB_BATCH; ++r) Mc = fmaxf(Mc, mv[r]);  // clamped repeats change no maximum
+      if (Mc != -INFINITY) {
+        if (M != -INFINITY && M != Mc) {
+          const double sc = (double)exp2f(M - Mc);
+          A *= sc;
+          L *= sc;
+        }
+#pragma unroll
+        for (int r = 0; r < CMB_BATCH; ++r) {
+          const float f = (s0 + r < S && mv[r] != -INFINITY) ? exp2f(mv[r] - Mc) : 0.0f;
+          A += (double)(f * av[r]);
+          L += (double)(f * lv[r]);
+        }
+        M = Mc;
+      }
+    }
+    // dequantize the mean code: step * (A / L - (L_j - 1)/2)
+    sC[hh * 128 + j] = bits ? (float)((double)step * (A / L - (double)hs)) : 0.0f;
   }
   __syncthreads();
   // rotate back: o_i = sum_k U_ik chat_k
   for (int hi = t; hi < g * 128; hi += nt) {
-    const int h = hi >> 7, i = hi & 127;
+    const int hh = hi >> 7, i = hi & 127;
+    const f32x4* c4 = reinterpret_cast<const f32x4*>(sC + hh * 128);
+    const float* ur = sU + i * CMB_UROW;
     float o = 0.0f;
-#pragma unroll 16
-    for (int k = 0; k < 128; ++k) o = __builtin_fmaf(sU[i * CMB_UROW + k], sC[h * ATT_PART_FLOATS + k], o);
-    a.out[(pg * g + h) * 128 + i] = o;
+#pragma unroll 8
+    for (int k4 = 0; k4 < 32; ++k4) {
+      const f32x4 c = c4[k4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o = __builtin_fmaf(ur[4 * k4 + e], c[e], o);
+    }
+    a.out[(pg * g + hh) * 128 + i] = o;
   }
 }
 
@@ -1401,7 +1416,7 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_att_main(AttK a) {
   // ---- merge the waves, four heads at a time: scratch [wave][4][130]
   __syncthreads();
   float* red = reinterpret_cast<float*>(sReg0);
-  float* part = reinterpret_cast<float*>(a.ws + ATT_CNT_BYTES) + ((p * a.n_splits + sp) * g) * ATT_PART_FLOATS;
+  float* part = reinterpret_cast<float*>(a.ws + ATT_CNT_BYTES) + (p * a.n_splits + sp) * att_part_stride(g);
   for (int c4 = 0; c4 * 4 < g; ++c4) {
     float* mine = red + wave * 4 * ATT_PART_FLOATS;
     // m, l of heads 4*c4 .. +3: H = 8i + 4h + j
@@ -1442,22 +1457,27 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_att_main(AttK a) {
   }
   // ---- the last split of the pair to finish merges all of them. Every
   // wave waits until its partial stores have reached L2; after the barrier
-  // one release per workgroup (thread 0's count) writes them back for the
-  // other XCDs, and only the waves of the last workgroup acquire. The counter
-  // of the pair is left at zero for the next call.
+  // thread 0 releases them with the pair's count (one L2 write-back per
+  // workgroup) and, in the last workgroup only, acquires the other splits'
+  // (one invalidate, complete before the barrier that the merge follows).
+  // The counter of the pair is left at zero for the next call.
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   unsigned* cnt = reinterpret_cast<unsigned*>(a.ws) + p;
   unsigned* flag = reinterpret_cast<unsigned*>(smem);
   if (tid == 0) {
     const unsigned prev = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-    *flag = prev == (unsigned)(a.n_splits - 1) ? 1u : 0u;
+    const unsigned is_last = prev == (unsigned)(a.n_splits - 1) ? 1u : 0u;
+    if (is_last) {
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    *flag = is_last;
   }
   __syncthreads();
   const unsigned last = *flag;
   __syncthreads();  // read by every thread before the merge below reuses the LDS
   if (last) {
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     att_combine_pair(a, p, reinterpret_cast<float*>(smem));
     if (tid == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
@@ -1500,7 +1520,7 @@ int launch_attend(const AttendLaunch& L, void* stream) {
     a.split_tokens = att_split_tokens(np, L.n_tokens);
     a.n_splits = att_n_splits(np, L.n_tokens);
     size_t att_lds = ATT_FIXED_BYTES + (size_t)waves * a.region_words * 4;
-    const size_t cmb = att_combine_lds_bytes(a.n_splits, L.group);
+    const size_t cmb = att_combine_lds_bytes();
     if (att_lds < cmb) att_lds = cmb;
     if (L.max_bits <= 512)
       hipLaunchKernelGGL((k_att_main<8>), dim3((unsigned)a.n_splits, (unsigned)np), dim3(64 * waves), att_lds, s, a);
