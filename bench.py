@@ -55,10 +55,11 @@ def parse():
 # Kernel launched by each timed op that is a single kernel; the roofline is
 # reported for the kernel with the largest share of the step.
 KERNEL_OF_OP = {"encode": "k_encode_eigen<bf16>", "decode": "k_decode_eigen<bf16>",
-                "rht_encode": "k_rht_encode", "rht_decode": "k_rht_decode"}
+                "attend": "k_att_main", "rht_encode": "k_rht_encode", "rht_decode": "k_rht_decode"}
 # rocprofv3 kernel names of the same kernels
 PROFILE_NAME = {"k_encode_eigen<bf16>": "void stc::k_encode_eigen<0>(stc::EncK)",
-                "k_decode_eigen<bf16>": "void stc::k_decode_eigen<0>(stc::DecK)",
+                "k_decode_eigen<bf16>": "void stc::k_decode_eigen<0, 8>(stc::DecK)",
+                "k_att_main": "void stc::k_att_main<8>(stc::AttK)",
                 "k_rht_encode": "stc::k_rht_encode(stc::RhtK)",
                 "k_rht_decode": "stc::k_rht_decode(stc::RhtK)"}
 KERNEL_SOURCE = os.path.join(ROOT, "spectral_transform_codec_amd", "csrc", "stc_kernels.hip")
@@ -242,6 +243,15 @@ def main():
     d_ms, d_bytes, d_n = fam[dname]
     achieved = d_bytes / (d_ms * 1e-3) / 1e9
     traffic = stored_traffic(dname)
+    # the same figures for every single-kernel family of the step
+    families = {}
+    for kname, (f_ms, f_bytes, f_n) in sorted(fam.items(), key=lambda kv: -kv[1][0]):
+        f_tr = stored_traffic(kname)
+        families[kname] = {"launches_per_step": f_n, "avg_launch_us": round(1e3 * f_ms / f_n, 2),
+                           "algorithmic_bytes_per_launch": int(f_bytes / f_n),
+                           "achieved": round(f_bytes / (f_ms * 1e-3) / 1e9, 1),
+                           "frac": round(f_bytes / (f_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                           "traffic": None if f_tr is None else int(f_tr)}
     codec_names = [o[0] for o in ops if o[0].startswith(("encode", "decode"))]
     codec_bytes = sum(o[2] for o in ops if o[0] in codec_names)
     codec_ms = sum(per_op[nm]["ms"] for nm in codec_names)
@@ -280,6 +290,7 @@ def main():
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": None if traffic is None else int(traffic)},
+        "roofline_by_kernel": families,
         "cpu_baseline": cpu,
         "setup_s": round(setup_s, 2),
         "calibrate_s": round(cal_s, 2),
