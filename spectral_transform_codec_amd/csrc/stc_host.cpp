@@ -252,6 +252,7 @@ stc_status build_eigen_blob(int d, int xform, const double* u, const double* lam
       h->step32[j] = (float)steps[j];
       h->step64[j] = steps[j];
       h->halfspan[j] = 0.5f * (float)(L - 1);
+      h->yhalf[j] = steps[j] > 0.0 ? (float)(L / 2) : (float)L - 0.5f;
     } else {
       h->inv_step[j] = 0.0f;
       h->ybias[j] = 0.5f;
@@ -272,7 +273,9 @@ stc_status build_eigen_blob(int d, int xform, const double* u, const double* lam
   }
   for (int R = 0; R < D; ++R) {
     const int j = enc_row_channel(R);
-    for (int i = 0; i < d; ++i) split_bf16(ud[(size_t)i * d + j], &ut_hi[R * D + i], &ut_lo[R * D + i]);
+    if (j >= d) continue;
+    const double ys = bits[j] == 0 ? 0.0 : (steps[j] > 0.0 ? 1.0 / steps[j] : 0x1p100);
+    for (int i = 0; i < d; ++i) split_bf16(ud[(size_t)i * d + j] * ys, &ut_hi[R * D + i], &ut_lo[R * D + i]);
   }
   for (int j = 0; j < d; ++j) h->bits4[j / 8] |= (uint32_t)bits[j] << (4 * (j % 8));
   fill_unpack_plan(h);

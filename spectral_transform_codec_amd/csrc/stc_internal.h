@@ -14,7 +14,7 @@ constexpr size_t STATE_BYTES = 512u * 1024u;
 // Byte offsets of the regions of one state blob.
 constexpr size_t OFF_HDR = 0;                        // DevHdr
 constexpr size_t OFF_U32 = 8192;                     // float U[i][j], row-major (64 KiB)
-constexpr size_t OFF_UT_HI = OFF_U32 + 65536;        // bf16 U[i][enc_row_channel(R)] at [R][i], high part
+constexpr size_t OFF_UT_HI = OFF_U32 + 65536;        // bf16 U[i][j] * yscale_j at [R][i], j = enc_row_channel(R), high part
 constexpr size_t OFF_UT_LO = OFF_UT_HI + 32768;      // the low parts
 constexpr size_t OFF_W_HI = OFF_UT_LO + 32768;       // bf16 W[enc_row_channel(R)][j] at [R][j], W = U diag(step)
 constexpr size_t OFF_W_LO = OFF_W_HI + 32768;
@@ -60,6 +60,12 @@ struct alignas(16) DevHdr {
   uint32_t qoff[4];
   uint32_t qwords[4];
   double step64[D];     // step_j in fp64: thresholds are fl32((k - L/2) * step64[j])
+  // Token encode: the basis rows are stored scaled by yscale_j = 1/step_j
+  // (2^100 for a zero step, 0 for a dropped channel), so that the projection
+  // gives the coordinate in quantizer cells directly; the code is
+  // clamp(floor(x.U_j yscale_j + yhalf_j), 0, L_j - 1), yhalf_j = L_j/2
+  // (L_j - 1/2 for a zero step, where every threshold is 0).
+  float yhalf[D];
 };
 static_assert(sizeof(DevHdr) <= OFF_U32, "header too large");
 

@@ -250,13 +250,20 @@ __global__ void __launch_bounds__(ENC_THREADS, 1) k_encode_eigen(EncK a) {
       }
     }
     if (tid < 128) {
-      sInv[tid] = hdr->inv_step[tid];
-      sInv[128 + tid] = hdr->ybias[tid];
-      sInv[256 + tid] = (float)hdr->lm1[tid];
-      reinterpret_cast<unsigned*>(sInv)[384 + tid] = (unsigned)hdr->off[tid] - (unsigned)hdr->off[tid & ~3];
-      sInv[512 + tid] = 2.0f * quant_eps(hdr->lm1[tid] + 1);  // guard band of the fast path
-      reinterpret_cast<unsigned*>(sInv)[640 + tid] = (unsigned)hdr->off[tid & ~3];  // record offset of the group
-      reinterpret_cast<double*>(sInv + 768)[tid] = hdr->step64[tid];
+      if (MODE == 2) {
+        sInv[tid] = hdr->inv_step[tid];
+        sInv[128 + tid] = hdr->ybias[tid];
+        sInv[256 + tid] = (float)hdr->lm1[tid];
+        reinterpret_cast<unsigned*>(sInv)[384 + tid] = (unsigned)hdr->off[tid] - (unsigned)hdr->off[tid & ~3];
+        sInv[512 + tid] = 2.0f * quant_eps(hdr->lm1[tid] + 1);  // guard band of the fast path
+        reinterpret_cast<unsigned*>(sInv)[640 + tid] = (unsigned)hdr->off[tid & ~3];  // record offset of the group
+        reinterpret_cast<double*>(sInv + 768)[tid] = hdr->step64[tid];
+      } else {
+        sInv[tid] = hdr->yhalf[tid];
+        sInv[128 + tid] = (float)hdr->lm1[tid];
+        reinterpret_cast<unsigned*>(sInv)[256 + tid] = (unsigned)hdr->off[tid] - (unsigned)hdr->off[tid & ~3];
+        reinterpret_cast<unsigned*>(sInv)[384 + tid] = (unsigned)hdr->off[tid & ~3];
+      }
     }
     __syncthreads();
     if (B > 0) {
@@ -322,54 +329,68 @@ __global__ void __launch_bounds__(ENC_THREADS, 1) k_encode_eigen(EncK a) {
           // ---- 2 + 3 per group of four channels
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            // y = c/step + L/2 + eps_L; outside the guard band next to an
-            // integer, floor(y) clamped to [0, L-1] is the exact threshold
-            // count; inside it, or for NaN or a zero step, the fp32
-            // thresholds decide.
             const int coff = 4 * (16 * mb + 4 * i);  // byte offset of the group in a table
-            const f32x4 inv = LDS_AT(f32x4, pL + coff);
-            const f32x4 yb = LDS_AT(f32x4, pL + 512 + coff);
-            const f32x4 lm = LDS_AT(f32x4, pL + 1024 + coff);
-            const u32x4 pos = LDS_AT(u32x4, pL + 1536 + coff);
-            const f32x4 band = LDS_AT(f32x4, pL + 2048 + coff);
             unsigned q[4];
-            bool need = false;
+            u32x4 pos;
+            unsigned goff;
+            if (MODE != 2) {
+              // acc = coordinate in quantizer cells (scaled basis rows):
+              // the code is floor(acc + L/2) clamped to [0, L-1]
+              const f32x4 yh = LDS_AT(f32x4, pL + coff);
+              const f32x4 lm = LDS_AT(f32x4, pL + 512 + coff);
+              pos = LDS_AT(u32x4, pL + 1024 + coff);
+              goff = LDS_AT(unsigned, pL + 1536 + coff);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const float y = __builtin_fmaf(acc[4 * i + j], inv[j], yb[j]);
-              q[j] = (unsigned)__builtin_amdgcn_fmed3f(y, 0.0f, lm[j]);
-              need |= !(__builtin_amdgcn_fractf(y) >= band[j]);
-            }
-            if (__any(need)) {
-              // exact decision against the thresholds t_k = fl32((k - L/2) step),
-              // k = 1..L-1, rebuilt here from the fp64 step exactly as the
-              // state builder forms them; the fast result is off by at most
-              // one level
-#pragma unroll
+              for (int j = 0; j < 4; ++j) q[j] = (unsigned)__builtin_amdgcn_fmed3f(acc[4 * i + j] + yh[j], 0.0f, lm[j]);
+            } else {
+              // y = c/step + L/2 + eps_L; outside the guard band next to an
+              // integer, floor(y) clamped to [0, L-1] is the exact threshold
+              // count; inside it, or for NaN or a zero step, the fp32
+              // thresholds decide.
+              const f32x4 inv = LDS_AT(f32x4, pL + coff);
+              const f32x4 yb = LDS_AT(f32x4, pL + 512 + coff);
+              const f32x4 lm = LDS_AT(f32x4, pL + 1024 + coff);
+              pos = LDS_AT(u32x4, pL + 1536 + coff);
+              const f32x4 band = LDS_AT(f32x4, pL + 2048 + coff);
+              goff = LDS_AT(unsigned, pL + 2560 + coff);
+              bool need = false;
+  #pragma unroll
               for (int j = 0; j < 4; ++j) {
-                const float c = acc[4 * i + j];
-                const float y = __builtin_fmaf(c, inv[j], yb[j]);
-                if (!(__builtin_amdgcn_fractf(y) >= band[j])) {
-                  const int lm1 = (int)lm[j];
-                  int qq = (int)q[j];
-                  if (c != c) {
-                    qq = 0;
-                  } else if (inv[j] == 0.0f) {
-                    qq = c >= 0.0f ? lm1 : 0;  // zero step: every threshold is 0
-                  } else {
-                    // fp64 table entry of channel 64h + 16mb + 4i + j (pL covers 64h floats)
-                    const double s64 = LDS_AT(double, pL + 3072 + 256 * h + 2 * coff + 8 * j);
-                    const double half = (double)((lm1 + 1) >> 1);
-                    if (qq > 0 && c < (float)(((double)qq - half) * s64)) qq -= 1;
-                    else if (qq < lm1 && c >= (float)(((double)(qq + 1) - half) * s64)) qq += 1;
+                const float y = __builtin_fmaf(acc[4 * i + j], inv[j], yb[j]);
+                q[j] = (unsigned)__builtin_amdgcn_fmed3f(y, 0.0f, lm[j]);
+                need |= !(__builtin_amdgcn_fractf(y) >= band[j]);
+              }
+              if (__any(need)) {
+                // exact decision against the thresholds t_k = fl32((k - L/2) step),
+                // k = 1..L-1, rebuilt here from the fp64 step exactly as the
+                // state builder forms them; the fast result is off by at most
+                // one level
+  #pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                  const float c = acc[4 * i + j];
+                  const float y = __builtin_fmaf(c, inv[j], yb[j]);
+                  if (!(__builtin_amdgcn_fractf(y) >= band[j])) {
+                    const int lm1 = (int)lm[j];
+                    int qq = (int)q[j];
+                    if (c != c) {
+                      qq = 0;
+                    } else if (inv[j] == 0.0f) {
+                      qq = c >= 0.0f ? lm1 : 0;  // zero step: every threshold is 0
+                    } else {
+                      // fp64 table entry of channel 64h + 16mb + 4i + j (pL covers 64h floats)
+                      const double s64 = LDS_AT(double, pL + 3072 + 256 * h + 2 * coff + 8 * j);
+                      const double half = (double)((lm1 + 1) >> 1);
+                      if (qq > 0 && c < (float)(((double)qq - half) * s64)) qq -= 1;
+                      else if (qq < lm1 && c >= (float)(((double)(qq + 1) - half) * s64)) qq += 1;
+                    }
+                    q[j] = (unsigned)qq;
                   }
-                  q[j] = (unsigned)qq;
                 }
               }
             }
             const unsigned word = q[0] | (q[1] << pos[1]) | (q[2] << pos[2]) | (q[3] << pos[3]);
             if (tok_ok) {
-              const unsigned P = tB + LDS_AT(unsigned, pL + 2560 + coff);  // record bit of the group
+              const unsigned P = tB + goff;  // record bit of the group
               const unsigned long long v = (unsigned long long)word << (P & 31u);
               unsigned* dst = sStr + est_idx(P >> 5);
               __hip_atomic_fetch_or(dst, (unsigned)v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
