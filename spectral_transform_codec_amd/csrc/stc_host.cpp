@@ -473,6 +473,16 @@ stc_status stc_rht_state_init(int32_t d, const int8_t* signs, const float* codeb
     h->sign[j] = (float)signs[j];
   }
   fill_unpack_plan(h);
+  // encode basis: row R holds output channel j = enc_row_channel(R) of
+  // H D, entries H[j][i] sign_i = +-1 (exact in bf16; no low part)
+  uint16_t* ut_hi = reinterpret_cast<uint16_t*>(blob.data() + OFF_UT_HI);
+  for (int R = 0; R < D; ++R) {
+    const int j = enc_row_channel(R);
+    for (int i = 0; i < D; ++i) {
+      const int hsign = (__builtin_popcount((unsigned)(i & j)) & 1) ? -1 : 1;
+      ut_hi[R * D + i] = hsign * signs[i] > 0 ? 0x3F80u : 0xBF80u;
+    }
+  }
   for (int k = 0; k < 8; ++k) h->cb[k] = codebook[k];
   for (int k = 0; k < 7; ++k) h->cb_thr[k] = (float)(0.5 * ((double)codebook[k] + (double)codebook[k + 1]));
   info->d = d;

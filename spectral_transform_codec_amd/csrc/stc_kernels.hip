@@ -785,10 +785,11 @@ int launch_decode_eigen(const DecodeLaunch& L, void* stream) {
 }
 
 // ======================================================================
-// Walsh-Hadamard path: one token per lane, the 128 values in registers.
-// Encode: signs -> norm -> FWHT butterflies -> scale by 1/(|x| sqrt(d)) ->
-// 3-bit codebook cell (count of midpoint thresholds <= y) -> 48-byte record.
-// Decode: codebook values -> FWHT -> scale by |x|/sqrt(d) -> signs.
+// Walsh-Hadamard path. Encode: the rotation x -> H D x is a dense +-1
+// matrix, exact in bf16, so it runs as MFMA chains like the eigen path, with
+// the 3-bit codebook in place of the per-channel uniform quantizer. Decode:
+// one token per lane, codebook values -> FWHT butterflies -> scale by
+// |x|/sqrt(d) -> signs.
 // ======================================================================
 struct RhtK {
   const unsigned char* states;
@@ -815,53 +816,107 @@ __device__ __forceinline__ void fwht128(float v[128]) {
       }
 }
 
-__global__ void __launch_bounds__(256) k_rht_encode(RhtK a) {
+// Encode: a wave takes blocks of 32 tokens. The rotation H D x is one
+// 32x32x16 MFMA chain per 32 channels against the +-1 rows of H D (exact in
+// bf16, so the products are exact and only the fp32 sums round); lane (h, t)
+// receives channels [64h, 64h + 64) of token t, whose 3-bit codes fill
+// words 6h .. 6h + 5 of the token's 48-byte record. The norm comes from the
+// lane's 64 input values and the other half's, and the code of a value c is
+// the count of scaled thresholds t_k |x| sqrt(d) <= c.
+constexpr int RHT_WAVES = 4;
+constexpr int RHT_BPW = 4;  // blocks per wave
+constexpr size_t RHT_LDS = 128 * UROW;
+
+__global__ void __launch_bounds__(64 * RHT_WAVES, 4) k_rht_encode(RhtK a) {
+  extern __shared__ __align__(16) unsigned char smem[];
   const long long s = blockIdx.y;
-  const long long tok = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (tok >= a.n_tokens) return;
-  const DevHdr* hdr =
-      reinterpret_cast<const DevHdr*>(a.states + (size_t)state_index(a.map, s, a.n_states) * STATE_BYTES);
-  const unsigned short* row = static_cast<const unsigned short*>(a.x) + s * a.x_stride + tok * a.ld;
-  float v[128];
-#pragma unroll
-  for (int c = 0; c < 16; ++c) {
-    const u32x4 w = *reinterpret_cast<const u32x4*>(row + 8 * c);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      v[8 * c + 2 * e] = __uint_as_float(w[e] << 16);
-      v[8 * c + 2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int t32 = lane & 31, h = lane >> 5;
+  const long long n = a.n_tokens;
+  const unsigned char* st = a.states + (size_t)state_index(a.map, s, a.n_states) * STATE_BYTES;
+  const DevHdr* hdr = reinterpret_cast<const DevHdr*>(st + OFF_HDR);
+  {
+    const u32x4* g = reinterpret_cast<const u32x4*>(st + OFF_UT_HI);
+    for (int i = tid; i < 128 * 16; i += 64 * RHT_WAVES) {
+      const int row = i >> 4, c = i & 15;
+      *reinterpret_cast<u32x4*>(smem + row * UROW + c * 16) = g[i];
     }
   }
-  float ss = 0.0f;
+  float thr[7];
 #pragma unroll
-  for (int i = 0; i < 128; ++i) {
-    v[i] *= hdr->sign[i];
-    ss = __builtin_fmaf(v[i], v[i], ss);
+  for (int k = 0; k < 7; ++k) thr[k] = hdr->cb_thr[k];
+  __syncthreads();
+  unsigned ub = lds_offset(smem + t32 * UROW + 16 * h);
+  asm volatile("" : "+v"(ub));
+  const lds_u8* uL = lds_ptr(ub);
+  const long long nblk = (n + ENC_BT - 1) / ENC_BT;
+  const long long b0 = ((long long)blockIdx.x * RHT_WAVES + wave) * RHT_BPW;
+  for (long long blk = b0; blk < b0 + RHT_BPW && blk < nblk; ++blk) {
+    const long long tok0 = blk * ENC_BT;
+    const unsigned last = (unsigned)(n - 1 - tok0);
+    const unsigned r = (unsigned)t32 < last ? (unsigned)t32 : last;
+    const unsigned short* row = static_cast<const unsigned short*>(a.x) + s * a.x_stride + (tok0 + r) * a.ld;
+    bf16x8 xf[8];
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+      xf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(row + 16 * ks + 8 * h));
+    // squared norm: this lane's 64 values, then the other half's
+    float ss = 0.0f;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const u32x4 w = __builtin_bit_cast(u32x4, xf[ks]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float lo = __uint_as_float(w[e] << 16), hi = __uint_as_float(w[e] & 0xffff0000u);
+        ss = __builtin_fmaf(lo, lo, ss);
+        ss = __builtin_fmaf(hi, hi, ss);
+      }
+    }
+    {
+      // element 0: the low half's sum, element 1: the high half's, in every lane
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(ss), __float_as_uint(ss), false, false);
+      const unsigned s_lo = sw[0], s_hi = sw[1];
+      ss = __uint_as_float(s_lo) + __uint_as_float(s_hi);
+    }
+    const float nu = sqrtf(ss);
+    const float sc = nu * 11.313708498984761f;
+    float T[7];
+#pragma unroll
+    for (int k = 0; k < 7; ++k) T[k] = nu > 0.0f ? thr[k] * sc : thr[k];
+    unsigned w[6] = {0u, 0u, 0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      f32x16 acc;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) acc = mfma32_bf16(LDS_AT(bf16x8, uL + 32 * mb * UROW + 32 * ks), xf[ks], acc);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float c = acc[e];
+        // count of thresholds <= c by binary search over the sorted T
+        const bool b2 = c >= T[3];
+        const float t1 = b2 ? T[5] : T[1];
+        const bool b1 = c >= t1;
+        const float t0 = b2 ? (b1 ? T[6] : T[4]) : (b1 ? T[2] : T[0]);
+        const bool b0 = c >= t0;
+        const unsigned q = (b2 ? 4u : 0u) + (b1 ? 2u : 0u) + (b0 ? 1u : 0u);
+        const int bp = 3 * (16 * mb + e);  // bit of channel 64h + 16mb + e in the half record
+        w[bp >> 5] |= q << (bp & 31);
+        if ((bp & 31) > 29) w[(bp >> 5) + 1] |= q >> (32 - (bp & 31));
+      }
+      __builtin_amdgcn_sched_barrier(0);  // one row block's accumulators live at a time
+    }
+    if (tok0 + t32 < n) {
+      u32x2* dst = reinterpret_cast<u32x2*>(a.packed + s * a.packed_stride + (tok0 + t32) * 48 + 24 * h);
+      dst[0] = (u32x2){w[0], w[1]};
+      dst[1] = (u32x2){w[2], w[3]};
+      dst[2] = (u32x2){w[4], w[5]};
+      if (h == 0) a.norms[s * n + tok0 + t32] = nu;
+    }
   }
-  fwht128(v);
-  const float nu = sqrtf(ss);
-  const float inv = nu > 0.0f ? 1.0f / (nu * 11.313708498984761f) : 0.0f;
-  float t[7];
-#pragma unroll
-  for (int k = 0; k < 7; ++k) t[k] = hdr->cb_thr[k];
-  unsigned w[12];
-#pragma unroll
-  for (int i = 0; i < 12; ++i) w[i] = 0u;
-#pragma unroll
-  for (int i = 0; i < 128; ++i) {
-    const float y = v[i] * inv;
-    unsigned q = 0;
-#pragma unroll
-    for (int k = 0; k < 7; ++k) q += (y >= t[k]) ? 1u : 0u;
-    const int bp = 3 * i;
-    w[bp >> 5] |= q << (bp & 31);
-    if ((bp & 31) > 29) w[(bp >> 5) + 1] |= q >> (32 - (bp & 31));
-  }
-  u32x4* dst = reinterpret_cast<u32x4*>(a.packed + s * a.packed_stride + tok * 48);
-  dst[0] = (u32x4){w[0], w[1], w[2], w[3]};
-  dst[1] = (u32x4){w[4], w[5], w[6], w[7]};
-  dst[2] = (u32x4){w[8], w[9], w[10], w[11]};
-  a.norms[s * a.n_tokens + tok] = nu;
 }
 
 // 128 tokens per workgroup; the reconstructed rows go through LDS so that the
@@ -945,8 +1000,9 @@ int launch_encode_rht(const EncodeLaunch& L, void* stream) {
   a.x = L.x;
   a.packed = L.packed;
   a.norms = L.norms;
-  dim3 grid((unsigned)((L.n_tokens + 255) / 256), (unsigned)L.n_streams);
-  hipLaunchKernelGGL(k_rht_encode, grid, dim3(256), 0, (hipStream_t)stream, a);
+  const long long nblk = (L.n_tokens + ENC_BT - 1) / ENC_BT;
+  dim3 grid((unsigned)((nblk + RHT_WAVES * RHT_BPW - 1) / (RHT_WAVES * RHT_BPW)), (unsigned)L.n_streams);
+  hipLaunchKernelGGL(k_rht_encode, grid, dim3(64 * RHT_WAVES), RHT_LDS, (hipStream_t)stream, a);
   return hipGetLastError() != hipSuccess;
 }
 
