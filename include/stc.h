@@ -193,6 +193,23 @@ stc_status stc_decode_kv_batched(const void* states_dev, int64_t n_states,
                                  void* x_out_dev, int32_t dtype, int64_t ld,
                                  int64_t x_stream_stride, stc_stream_t stream);
 
+/* Append m tokens to streams that already hold n_old (the cache is
+ * append-only, each token quantized on its own when it arrives: SPECTRA
+ * summary, "La Pipeline", steps 2-3). x row r of stream s is its token
+ * n_old + r; the records go to stream bits [(n_old + r) B, (n_old + r + 1) B).
+ * Bits of the first n_old records are kept, every byte from there up to
+ * packed_bytes(B, n_old + m) is rewritten (F1 zero padding included), so
+ * after the call the stream equals one encode of all n_old + m tokens.
+ * packed_stream_stride must hold n_old + m tokens; Walsh-Hadamard norms go to
+ * norms_dev + s*norms_stream_stride + n_old + r. Same layout rules and errors
+ * as stc_encode_kv_batched; m = 0 does nothing. */
+stc_status stc_append_kv_batched(const void* states_dev, int64_t n_states,
+                                 const int32_t* state_of_stream_dev, const stc_head_info* infos,
+                                 int64_t n_streams, int64_t n_old, int64_t m, const void* x_dev,
+                                 int32_t dtype, int64_t ld, int64_t x_stream_stride,
+                                 void* packed_dev, int64_t packed_stream_stride,
+                                 float* norms_dev, int64_t norms_stream_stride, stc_stream_t stream);
+
 /* One stream. */
 stc_status stc_encode_kv(const stc_head_info* info, const void* state_dev, int64_t n_tokens,
                          const void* x_dev, int32_t dtype, int64_t ld, void* packed_dev,
@@ -235,6 +252,25 @@ stc_status stc_attend_compressed(const stc_head_info* k_info, const void* k_stat
                                  const void* v_packed_dev, int32_t group, const float* q_dev,
                                  float* out_dev, float scale, void* ws_dev, size_t ws_bytes,
                                  stc_stream_t stream);
+
+/* One generation step for n_pairs KV heads: append the new K token
+ * k_new_dev[p][128] and V token v_new_dev[p][128] (dtype STC_BF16 or
+ * STC_F32, rows of 128 elements) to pair p's packed K and V streams, which
+ * hold n_old tokens and have room for n_old + 1, then attend as
+ * stc_attend_compressed_batched over all n_old + 1 tokens. The new token's
+ * records are those a full encode would write (the stream is append-only),
+ * and attention reads them back from the packed cache like every other
+ * token. EIGEN/IDENTITY states only; ws_dev as for
+ * stc_attend_compressed_batched with n_old + 1 tokens. Three launches on
+ * `stream`. */
+stc_status stc_decode_step_batched(const void* states_dev, int64_t n_states,
+                                   const int32_t* k_state_of_pair_dev,
+                                   const int32_t* v_state_of_pair_dev, const stc_head_info* infos,
+                                   int64_t n_pairs, int64_t n_old, const void* k_new_dev,
+                                   const void* v_new_dev, int32_t dtype, void* k_packed_dev,
+                                   void* v_packed_dev, int64_t packed_pair_stride, int32_t group,
+                                   const float* q_dev, float* out_dev, float scale, void* ws_dev,
+                                   size_t ws_bytes, stc_stream_t stream);
 
 /* ------------------------------------------------------ diagnostics */
 const char* stc_status_str(stc_status s);

@@ -224,6 +224,33 @@ def pack(codes: np.ndarray, bits: np.ndarray) -> np.ndarray:
     return (groups * weights[None, :]).sum(axis=1).astype(np.uint8)
 
 
+def append_pack(packed_old: np.ndarray, n_old: int, codes_new: np.ndarray, bits: np.ndarray) -> np.ndarray:
+    """Append-only cache (SPECTRA summary, "La Pipeline" steps 2-3: each new
+    token is quantized on arrival and its record appended): the stream of
+    n_old tokens followed by the records of codes_new [m][d], as F1 bytes of
+    n_old + m tokens. Written bit by bit from the F1 layout (record r of the
+    new tokens starts at stream bit (n_old + r) * B), independently of `pack`:
+    the old stream's first n_old * B bits are kept, every later bit is the
+    new records' or 0."""
+    codes_new = np.asarray(codes_new, dtype=np.int64)
+    bits = [int(b) for b in np.asarray(bits)]
+    total = sum(bits)
+    m = codes_new.shape[0]
+    out = np.zeros(packed_bytes(total, n_old + m), dtype=np.uint8)
+    old = np.asarray(packed_old, dtype=np.uint8)
+    for i in range(n_old * total):
+        if (int(old[i >> 3]) >> (i & 7)) & 1:
+            out[i >> 3] |= np.uint8(1 << (i & 7))
+    for r in range(m):
+        pos = (n_old + r) * total
+        for j, b in enumerate(bits):
+            for k in range(b):
+                if (int(codes_new[r, j]) >> k) & 1:
+                    out[pos >> 3] |= np.uint8(1 << (pos & 7))
+                pos += 1
+    return out
+
+
 def unpack(packed: np.ndarray, bits: np.ndarray, n: int) -> np.ndarray:
     """Inverse of `pack`: codes [n][d] (0 in dropped channels)."""
     packed = np.asarray(packed, dtype=np.uint8)

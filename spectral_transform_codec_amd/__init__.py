@@ -245,6 +245,46 @@ def encode_kv_batched(states: StateArray, x: torch.Tensor, state_of_stream: Opti
     return packed, norms
 
 
+def append_kv_batched(states: StateArray, x: torch.Tensor, n_old: int, packed: torch.Tensor,
+                      state_of_stream: Optional[torch.Tensor] = None, norms: Optional[torch.Tensor] = None):
+    """Append x [S][m][128] (tokens n_old .. n_old+m-1 of every stream) to packed [S][stride]
+    uint8 streams holding n_old tokens; stride must fit n_old + m. Walsh-Hadamard states write
+    norms [S][>= n_old + m] at columns n_old .. n_old+m-1. Returns packed."""
+    assert x.dim() == 3 and x.shape[2] == D and x.stride(2) == 1
+    S, m = x.shape[0], x.shape[1]
+    if states.xform == XFORM_RHT:
+        assert norms is not None and norms.dim() == 2 and norms.stride(1) == 1
+    ns = 0 if norms is None else norms.stride(0)
+    check("stc_append_kv_batched", lib().stc_append_kv_batched(
+        _ptr(states.blob), states.n, _ptr(_map_arg(state_of_stream)), states.infos, S, n_old, m, _ptr(x),
+        _dtype_code(x), x.stride(1), x.stride(0), _ptr(packed), packed.stride(0), _ptr(norms), ns, _stream()))
+    return packed
+
+
+def decode_step_batched(states: StateArray, k_state_of_pair: torch.Tensor, v_state_of_pair: torch.Tensor,
+                        n_old: int, k_new: torch.Tensor, v_new: torch.Tensor, k_packed: torch.Tensor,
+                        v_packed: torch.Tensor, q: torch.Tensor, scale: Optional[float] = None,
+                        ws: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None):
+    """One generation step: append k_new, v_new [P][128] to the P KV heads' packed K and V
+    streams (n_old tokens each, room for one more), then attend q fp32 [P][g][128] over
+    all n_old + 1 tokens. Returns out fp32 [P][g][128]."""
+    Pn, g = q.shape[0], q.shape[1]
+    assert k_new.shape == (Pn, D) and v_new.shape == (Pn, D) and k_new.dtype == v_new.dtype
+    assert k_new.is_contiguous() and v_new.is_contiguous() and q.is_contiguous()
+    assert k_packed.stride(0) == v_packed.stride(0)
+    scale = (1.0 / np.sqrt(D)) if scale is None else scale
+    if out is None:
+        out = torch.empty((Pn, g, D), dtype=torch.float32, device=q.device)
+    need = attend_workspace_bytes(Pn, g, n_old + 1)
+    if ws is None or ws.numel() < need:
+        ws = torch.zeros(need, dtype=torch.uint8, device=q.device)  # zero-filled once
+    check("stc_decode_step_batched", lib().stc_decode_step_batched(
+        _ptr(states.blob), states.n, _ptr(_map_arg(k_state_of_pair)), _ptr(_map_arg(v_state_of_pair)),
+        states.infos, Pn, n_old, _ptr(k_new), _ptr(v_new), _dtype_code(k_new), _ptr(k_packed), _ptr(v_packed),
+        k_packed.stride(0), g, _ptr(q), _ptr(out), float(scale), _ptr(ws), ws.numel(), _stream()))
+    return out
+
+
 def decode_kv_batched(states: StateArray, packed: torch.Tensor, n: int, norms: Optional[torch.Tensor] = None,
                       state_of_stream: Optional[torch.Tensor] = None, dtype=torch.bfloat16,
                       out: Optional[torch.Tensor] = None) -> torch.Tensor:

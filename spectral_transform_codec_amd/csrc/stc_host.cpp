@@ -582,33 +582,56 @@ static stc_status check_batch(const char* who, const void* states_dev, int64_t n
   return STC_OK;
 }
 
+// Encode tokens [n_old, n_old + m) of every stream (x row r = token n_old + r).
+static stc_status encode_impl(const char* who, const void* states_dev, int64_t n_states, const int32_t* map,
+                              const stc_head_info* infos, int64_t n_streams, int64_t n_old, int64_t m,
+                              const void* x_dev, int32_t dtype, int64_t ld, int64_t x_stream_stride,
+                              void* packed_dev, int64_t packed_stream_stride, float* norms_dev,
+                              int64_t norms_stream_stride, stc_stream_t stream) {
+  bool rht = false;
+  int mb = 0;
+  if (n_old < 0 || m < 0) return fail(STC_EINVAL, "%s: negative token count", who);
+  if (stc_status s = check_batch(who, states_dev, n_states, infos, n_streams, n_old + m, packed_stream_stride,
+                                 &rht, &mb)) return s;
+  if (dtype != STC_F32 && dtype != STC_BF16) return fail(STC_EUNSUPPORTED, "%s: dtype %d", who, dtype);
+  if (rht && dtype != STC_BF16) return fail(STC_EUNSUPPORTED, "%s: the RHT path takes bf16 tokens", who);
+  if (m == 0) return ok();
+  if (!x_dev || !packed_dev) return fail(STC_EINVAL, "%s: NULL buffer", who);
+  if (rht && !norms_dev) return fail(STC_EINVAL, "%s: RHT states need a norms buffer", who);
+  if (rht && n_streams > 1 && norms_stream_stride < n_old + m)
+    return fail(STC_EINVAL, "%s: norms stream stride %lld < %lld tokens", who, (long long)norms_stream_stride,
+                (long long)(n_old + m));
+  const int es = elem_size(dtype);
+  if (ld < D || !aligned(x_dev, 16) || (ld * es) % 16 || (x_stream_stride * es) % 16)
+    return fail(STC_EINVAL, "%s: x rows must be >= 128 elements and 16-byte aligned", who);
+  if (n_streams > 1 && x_stream_stride < (m - 1) * ld + D)
+    return fail(STC_EINVAL, "%s: x stream stride too small", who);
+  if (!aligned(packed_dev, 16)) return fail(STC_EINVAL, "%s: packed buffer must be 16-byte aligned", who);
+  if (rht && !aligned(norms_dev, 4)) return fail(STC_EINVAL, "%s: norms misaligned", who);
+  EncodeLaunch a{static_cast<const unsigned char*>(states_dev), map, n_states, n_streams, m, ld,
+                 x_stream_stride, packed_stream_stride, x_dev, static_cast<unsigned char*>(packed_dev), norms_dev,
+                 dtype == STC_F32 ? 1 : 0, mb, n_old, norms_stream_stride};
+  const int rc = rht ? launch_encode_rht(a, stream) : launch_encode_eigen(a, stream);
+  if (rc) return fail(STC_EDEVICE, "%s launch: %s", who, hipGetErrorString(hipGetLastError()));
+  return ok();
+}
+
 stc_status stc_encode_kv_batched(const void* states_dev, int64_t n_states, const int32_t* map,
                                  const stc_head_info* infos, int64_t n_streams, int64_t n_tokens,
                                  const void* x_dev, int32_t dtype, int64_t ld, int64_t x_stream_stride,
                                  void* packed_dev, int64_t packed_stream_stride, float* norms_dev,
                                  stc_stream_t stream) {
-  bool rht = false;
-  int mb = 0;
-  if (stc_status s = check_batch("encode_kv", states_dev, n_states, infos, n_streams, n_tokens,
-                                 packed_stream_stride, &rht, &mb)) return s;
-  if (dtype != STC_F32 && dtype != STC_BF16) return fail(STC_EUNSUPPORTED, "encode_kv: dtype %d", dtype);
-  if (rht && dtype != STC_BF16) return fail(STC_EUNSUPPORTED, "encode_kv: the RHT path takes bf16 tokens");
-  if (n_tokens == 0) return ok();
-  if (!x_dev || !packed_dev) return fail(STC_EINVAL, "encode_kv: NULL buffer");
-  if (rht && !norms_dev) return fail(STC_EINVAL, "encode_kv: RHT states need a norms buffer");
-  const int es = elem_size(dtype);
-  if (ld < D || !aligned(x_dev, 16) || (ld * es) % 16 || (x_stream_stride * es) % 16)
-    return fail(STC_EINVAL, "encode_kv: x rows must be >= 128 elements and 16-byte aligned");
-  if (n_streams > 1 && x_stream_stride < (n_tokens - 1) * ld + D)
-    return fail(STC_EINVAL, "encode_kv: x stream stride too small");
-  if (!aligned(packed_dev, 16)) return fail(STC_EINVAL, "encode_kv: packed buffer must be 16-byte aligned");
-  if (rht && !aligned(norms_dev, 4)) return fail(STC_EINVAL, "encode_kv: norms misaligned");
-  EncodeLaunch a{static_cast<const unsigned char*>(states_dev), map, n_states, n_streams, n_tokens, ld,
-                 x_stream_stride, packed_stream_stride, x_dev, static_cast<unsigned char*>(packed_dev), norms_dev,
-                 dtype == STC_F32 ? 1 : 0, mb};
-  const int rc = rht ? launch_encode_rht(a, stream) : launch_encode_eigen(a, stream);
-  if (rc) return fail(STC_EDEVICE, "encode_kv launch: %s", hipGetErrorString(hipGetLastError()));
-  return ok();
+  return encode_impl("encode_kv", states_dev, n_states, map, infos, n_streams, 0, n_tokens, x_dev, dtype, ld,
+                     x_stream_stride, packed_dev, packed_stream_stride, norms_dev, n_tokens, stream);
+}
+
+stc_status stc_append_kv_batched(const void* states_dev, int64_t n_states, const int32_t* map,
+                                 const stc_head_info* infos, int64_t n_streams, int64_t n_old, int64_t m,
+                                 const void* x_dev, int32_t dtype, int64_t ld, int64_t x_stream_stride,
+                                 void* packed_dev, int64_t packed_stream_stride, float* norms_dev,
+                                 int64_t norms_stream_stride, stc_stream_t stream) {
+  return encode_impl("append_kv", states_dev, n_states, map, infos, n_streams, n_old, m, x_dev, dtype, ld,
+                     x_stream_stride, packed_dev, packed_stream_stride, norms_dev, norms_stream_stride, stream);
 }
 
 stc_status stc_decode_kv_batched(const void* states_dev, int64_t n_states, const int32_t* map,
@@ -663,7 +686,7 @@ stc_status stc_quantize_pack_f32(const stc_head_info* info, const void* state_de
     return fail(STC_EINVAL, "quantize_pack_f32: NULL or misaligned buffer");
   EncodeLaunch a{static_cast<const unsigned char*>(state_dev), nullptr, 1, 1, n_tokens, D, 0,
                  (int64_t)packed_bytes(mb, n_tokens), coeffs_dev, static_cast<unsigned char*>(packed_dev),
-                 nullptr, 2, mb};
+                 nullptr, 2, mb, 0, 0};
   if (launch_encode_eigen(a, stream)) return fail(STC_EDEVICE, "quantize_pack launch: %s", hipGetErrorString(hipGetLastError()));
   return ok();
 }
@@ -725,6 +748,35 @@ stc_status stc_attend_compressed(const stc_head_info* k_info, const void* k_stat
                  static_cast<unsigned char*>(ws_dev), std::max(mbk, mbv)};
   if (launch_attend(a, stream)) return fail(STC_EDEVICE, "attend launch: %s", hipGetErrorString(hipGetLastError()));
   return ok();
+}
+
+stc_status stc_decode_step_batched(const void* states_dev, int64_t n_states, const int32_t* k_map,
+                                   const int32_t* v_map, const stc_head_info* infos, int64_t n_pairs,
+                                   int64_t n_old, const void* k_new_dev, const void* v_new_dev, int32_t dtype,
+                                   void* k_packed_dev, void* v_packed_dev, int64_t packed_pair_stride,
+                                   int32_t group, const float* q_dev, float* out_dev, float scale, void* ws_dev,
+                                   size_t ws_bytes, stc_stream_t stream) {
+  bool rht = false;
+  int mb = 0;
+  if (n_old < 0) return fail(STC_EINVAL, "decode_step: negative token count");
+  if (stc_status s = check_batch("decode_step", states_dev, n_states, infos, n_pairs, n_old + 1, packed_pair_stride,
+                                 &rht, &mb)) return s;
+  if (rht) return fail(STC_EUNSUPPORTED, "decode_step: eigen/identity states only");
+  if (group < 1 || group > 16) return fail(STC_EUNSUPPORTED, "decode_step: group %d outside 1..16", group);
+  if (!q_dev || !out_dev || !ws_dev) return fail(STC_EINVAL, "decode_step: NULL buffer");
+  if (!std::isfinite(scale)) return fail(STC_EINVAL, "decode_step: scale must be finite");
+  const size_t need = stc_attend_workspace_bytes(n_pairs, group, n_old + 1);
+  if (ws_bytes < need) return fail(STC_EWORKSPACE, "decode_step: workspace %zu < %zu", ws_bytes, need);
+  // the new K and V token of every KV head, then one attention step over all n_old + 1
+  if (stc_status s = encode_impl("decode_step (K append)", states_dev, n_states, k_map, infos, n_pairs, n_old, 1,
+                                 k_new_dev, dtype, D, D, k_packed_dev, packed_pair_stride, nullptr, 0, stream))
+    return s;
+  if (stc_status s = encode_impl("decode_step (V append)", states_dev, n_states, v_map, infos, n_pairs, n_old, 1,
+                                 v_new_dev, dtype, D, D, v_packed_dev, packed_pair_stride, nullptr, 0, stream))
+    return s;
+  return stc_attend_compressed_batched(states_dev, n_states, k_map, v_map, infos, n_pairs, n_old + 1, k_packed_dev,
+                                       v_packed_dev, packed_pair_stride, group, q_dev, out_dev, scale, ws_dev,
+                                       ws_bytes, stream);
 }
 
 }  // extern "C"

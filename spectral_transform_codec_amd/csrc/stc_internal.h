@@ -122,6 +122,8 @@ struct EncodeLaunch {
   float* norms;
   int mode;       // 0 bf16 tokens, 1 fp32 tokens, 2 fp32 latent coefficients
   int max_bits;   // largest total_bits of the states used
+  int64_t n_old = 0;         // tokens already in the streams (append); n_tokens new ones follow
+  int64_t norms_stride = 0;  // Walsh-Hadamard norms: elements between streams
 };
 struct DecodeLaunch {
   const unsigned char* states;

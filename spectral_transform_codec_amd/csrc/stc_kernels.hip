@@ -162,6 +162,8 @@ struct EncK {
   const void* x;
   unsigned char* packed;
   long long blocks_per_stream, total_blocks, blocks_per_wg;
+  long long n_old, blk0;  // tokens already in the streams; first (absolute) 32-token block
+  long long norms_stride;
   int grid;
 };
 
@@ -214,18 +216,27 @@ __global__ void __launch_bounds__(ENC_THREADS, 1) k_encode_eigen(EncK a) {
   const long long b_begin = (long long)lw * a.blocks_per_wg;
   long long b_end = b_begin + a.blocks_per_wg;
   if (b_end > a.total_blocks) b_end = a.total_blocks;
-  const long long n = a.n_tokens;
+  // the call writes tokens [n0, n) of each stream: x row r holds token n0 + r
+  const long long n0 = a.n_old, m = a.n_tokens, n = n0 + m;
 
   for (int i = lane; i < EST_WORDS; i += 64) sStr[i] = 0u;
 
-  // B fragments (tokens) of a block: pf[ks] = token t (row clamped to n - 1),
-  // dims 16ks + 8h .. +7
+  // x row of lane t in the block at token tok0: rbase + rlane (clamped to
+  // the call's rows [0, m))
+  auto x_row = [&](long long tok0, long long& rbase, unsigned& rlane) {
+    rbase = tok0 - n0 > 0 ? tok0 - n0 : 0;
+    long long r = tok0 + t32 - n0 - rbase;
+    if (r < 0) r = 0;
+    if (r > m - 1 - rbase) r = m - 1 - rbase;
+    rlane = (unsigned)r;
+  };
+  // B fragments (tokens) of a block: pf[ks] = token t, dims 16ks + 8h .. +7
   bf16x8 pf[8];
   auto load_frags = [&](long long s2, long long tt2) {
-    const long long tok0 = tt2 * ENC_BT;
-    const unsigned short* base = static_cast<const unsigned short*>(a.x) + s2 * a.x_stride + tok0 * a.ld;
-    const unsigned last = (unsigned)(n - 1 - tok0);
-    const unsigned r = (unsigned)t32 < last ? (unsigned)t32 : last;
+    long long rbase;
+    unsigned r;
+    x_row(tt2 * ENC_BT, rbase, r);
+    const unsigned short* base = static_cast<const unsigned short*>(a.x) + s2 * a.x_stride + rbase * a.ld;
     const unsigned ro = r * (unsigned)a.ld + 8u * (unsigned)h;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks)
@@ -271,15 +282,16 @@ __global__ void __launch_bounds__(ENC_THREADS, 1) k_encode_eigen(EncK a) {
       const unsigned cw_kind = (B & 3u) == 0u ? 4u : ((B & 1u) == 0u ? 2u : 1u);
       const unsigned clear = est_idx(B + 4u) + 2u;
       for (long long blk = seg + wave; blk < seg_end; blk += ENC_WAVES) {
-        const long long tt = blk - s * a.blocks_per_stream;
+        const long long tt = blk - s * a.blocks_per_stream + a.blk0;  // absolute block of the stream
         const long long tok0 = tt * ENC_BT;
-        const unsigned last_row = (unsigned)(n - 1 - tok0);
-        const unsigned trow = (unsigned)t32 < last_row ? (unsigned)t32 : last_row;
+        long long rbase;
+        unsigned trow;
+        x_row(tok0, rbase, trow);
         bf16x8 xl[8];
         auto& xh = pf;
         if (MODE == 0) load_frags(s, tt);
         if (MODE == 1) {
-          const float* row = static_cast<const float*>(a.x) + s * a.x_stride + tok0 * a.ld + trow * (unsigned)a.ld;
+          const float* row = static_cast<const float*>(a.x) + s * a.x_stride + rbase * a.ld + trow * (unsigned)a.ld;
 #pragma unroll
           for (int ks = 0; ks < 8; ++ks) {
             const f32x4 v0 = *reinterpret_cast<const f32x4*>(row + 16 * ks + 8 * h);
@@ -299,14 +311,14 @@ __global__ void __launch_bounds__(ENC_THREADS, 1) k_encode_eigen(EncK a) {
         asm volatile("" : "+v"(ub), "+v"(pb));
         const lds_u8* uL = lds_ptr(ub);
         const lds_u8* pL = lds_ptr(pb);
-        const bool tok_ok = tok0 + t32 < n;
+        const bool tok_ok = tok0 + t32 >= n0 && tok0 + t32 < n;
         const unsigned tB = (unsigned)t32 * B;
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) {
           // ---- 1: channels 64h + 16mb + 4i + j of token t in acc[4i + j]
           f32x16 acc;
           if (MODE == 2) {
-            const float* cf = static_cast<const float*>(a.x) + (tok0 + trow) * 128 + 64 * h + 16 * mb;
+            const float* cf = static_cast<const float*>(a.x) + (rbase + trow) * 128 + 64 * h + 16 * mb;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               const f32x4 v = *reinterpret_cast<const f32x4*>(cf + 4 * i);
@@ -404,8 +416,21 @@ __global__ void __launch_bounds__(ENC_THREADS, 1) k_encode_eigen(EncK a) {
         // also writes the zero padding up to the 16-byte boundary.
         const long long start = tt * 4LL * (long long)B;
         long long nbytes = 4LL * (long long)B;
-        if (tt == a.blocks_per_stream - 1 || nbytes > P_len - start) nbytes = P_len - start;
+        if (tok0 + ENC_BT >= n || nbytes > P_len - start) nbytes = P_len - start;
         unsigned char* dst = a.packed + s * a.packed_stride + start;
+        if (tok0 < n0) {
+          // an append's first block: the words holding bits of the records
+          // already in the stream keep them
+          const unsigned oldbits = (unsigned)((n0 - tok0) * (long long)B);
+          const unsigned wold = (oldbits + 31u) >> 5;
+          const unsigned* old = reinterpret_cast<const unsigned*>(dst);
+          for (unsigned w2 = lane; w2 < wold; w2 += 64) {
+            const unsigned rb = oldbits - 32u * w2;  // old bits in this word (all of them if >= 32)
+            sStr[est_idx(w2)] |= old[w2] & (rb >= 32u ? ~0u : (1u << rb) - 1u);
+          }
+          __builtin_amdgcn_s_waitcnt(0xc07f);
+          __builtin_amdgcn_wave_barrier();
+        }
         if (cw_kind == 4u) est_copy_out<4>(sStr, dst, nbytes, clear, lane);
         else if (cw_kind == 2u) est_copy_out<2>(sStr, dst, nbytes, clear, lane);
         else est_copy_out<1>(sStr, dst, nbytes, clear, lane);
@@ -434,7 +459,10 @@ int launch_encode_eigen(const EncodeLaunch& L, void* stream) {
   a.packed_stride = L.packed_stride;
   a.x = L.x;
   a.packed = L.packed;
-  a.blocks_per_stream = (L.n_tokens + ENC_BT - 1) / ENC_BT;
+  a.n_old = L.n_old;
+  a.blk0 = L.n_old / ENC_BT;
+  a.norms_stride = L.norms_stride;
+  a.blocks_per_stream = (L.n_old + L.n_tokens + ENC_BT - 1) / ENC_BT - a.blk0;
   a.total_blocks = a.blocks_per_stream * L.n_streams;
   int dev = 0, cus = 256;
   (void)hipGetDevice(&dev);
@@ -801,6 +829,7 @@ struct RhtK {
   const unsigned char* packed_in;
   float* norms;
   const float* norms_in;
+  long long n_old, norms_stride;  // encode: tokens already in the streams; norms row stride
   int f32out;
 };
 
@@ -834,7 +863,7 @@ __global__ void __launch_bounds__(64 * RHT_WAVES, 4) k_rht_encode(RhtK a) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int t32 = lane & 31, h = lane >> 5;
-  const long long n = a.n_tokens;
+  const long long n = a.n_tokens;  // x rows of the call; row j is token n_old + j of the stream
   const unsigned char* st = a.states + (size_t)state_index(a.map, s, a.n_states) * STATE_BYTES;
   const DevHdr* hdr = reinterpret_cast<const DevHdr*>(st + OFF_HDR);
   {
@@ -910,11 +939,12 @@ __global__ void __launch_bounds__(64 * RHT_WAVES, 4) k_rht_encode(RhtK a) {
       __builtin_amdgcn_sched_barrier(0);  // one row block's accumulators live at a time
     }
     if (tok0 + t32 < n) {
-      u32x2* dst = reinterpret_cast<u32x2*>(a.packed + s * a.packed_stride + (tok0 + t32) * 48 + 24 * h);
+      const long long tk = a.n_old + tok0 + t32;
+      u32x2* dst = reinterpret_cast<u32x2*>(a.packed + s * a.packed_stride + tk * 48 + 24 * h);
       dst[0] = (u32x2){w[0], w[1]};
       dst[1] = (u32x2){w[2], w[3]};
       dst[2] = (u32x2){w[4], w[5]};
-      if (h == 0) a.norms[s * n + tok0 + t32] = nu;
+      if (h == 0) a.norms[s * a.norms_stride + tk] = nu;
     }
   }
 }
@@ -1000,6 +1030,8 @@ int launch_encode_rht(const EncodeLaunch& L, void* stream) {
   a.x = L.x;
   a.packed = L.packed;
   a.norms = L.norms;
+  a.n_old = L.n_old;
+  a.norms_stride = L.norms_stride;
   const long long nblk = (L.n_tokens + ENC_BT - 1) / ENC_BT;
   dim3 grid((unsigned)((nblk + RHT_WAVES * RHT_BPW - 1) / (RHT_WAVES * RHT_BPW)), (unsigned)L.n_streams);
   hipLaunchKernelGGL(k_rht_encode, grid, dim3(64 * RHT_WAVES), RHT_LDS, (hipStream_t)stream, a);

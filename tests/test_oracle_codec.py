@@ -421,7 +421,38 @@ def test_pack_prefix_invariant():
             assert int(part[nb]) >> rem == 0
 
 
-# -------------------------------------------------------------- O8 rounding
+def test_append_pack_equals_pack_of_all():
+    """Appending records to a stream gives the stream of all tokens (F1 is
+    append-only), for record lengths on and off byte and word boundaries,
+    appends of one token and of many, and old streams whose padding is dirty
+    past the last record only where F1 allows none (it must stay ignored)."""
+    rng = np.random.default_rng(21)
+    for bits in (np.array([7, 5, 3, 3, 2, 1, 1, 0], np.uint8),      # B = 22
+                 np.array([4] * 8, np.uint8),                      # B = 32, word aligned
+                 np.array([3, 3, 2, 1, 0, 0, 0, 0], np.uint8)):    # B = 9
+        n = 41
+        codes = np.stack([rng.integers(0, 1 << int(b), n) for b in bits], axis=1)
+        full = codec.pack(codes, bits)
+        for n_old in (0, 1, 5, 16, 40):
+            old = codec.pack(codes[:n_old], bits)
+            got = codec.append_pack(old, n_old, codes[n_old:], bits)
+            assert np.array_equal(got, full), (int(bits.sum()), n_old)
+        # one token at a time
+        cur = codec.pack(codes[:0], bits)
+        for t in range(n):
+            cur = codec.append_pack(cur, t, codes[t:t + 1], bits)
+        assert np.array_equal(cur, full)
+        # bits of the old stream past its records are not carried over
+        old = codec.pack(codes[:3], bits).copy()
+        nb = old.shape[0]
+        tail_bit = 3 * int(bits.sum())
+        if tail_bit < nb * 8:
+            old[tail_bit >> 3] |= np.uint8(0xFF << (tail_bit & 7) & 0xFF)
+            old[(tail_bit >> 3) + 1:] = 0xFF
+        assert np.array_equal(codec.append_pack(old, 3, codes[3:], bits), full)
+
+
+# -------------------------------------------------------------- O8 rounding# -------------------------------------------------------------- O8 rounding
 def test_round_to_bf16():
     # agrees with the generator's bit-level fp32 -> bf16 RNE on fp32 inputs
     x = np.random.default_rng(13).standard_normal(20000).astype(np.float32) * 37
