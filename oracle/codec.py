@@ -389,6 +389,14 @@ def attend_compressed(k_state: Dict, v_state: Dict, k_packed: np.ndarray,
     [g][d] for the g query heads of this KV head."""
     khat = reconstruct_exact(k_state, k_packed, n)
     vhat = reconstruct_exact(v_state, v_packed, n)
+    return softmax_attention(q, khat, vhat, scale)
+
+
+def softmax_attention(q: np.ndarray, khat: np.ndarray, vhat: np.ndarray,
+                      scale: Optional[float] = None) -> np.ndarray:
+    """Standard attention of g query heads over n reconstructed keys and
+    values, fp64: s = q K^T * scale, softmax over the n tokens, o = p V.
+    READING: scale 1/sqrt(d), no mask, no positional rotation. fp32 [g][d]."""
     q = np.asarray(q, dtype=np.float64)
     d = khat.shape[1]
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)

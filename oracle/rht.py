@@ -121,9 +121,24 @@ def reconstruct_exact(state: Dict, packed: np.ndarray, norms: np.ndarray, n: int
     """x_hat = nu D H y_hat / sqrt(d) with y_hat the codebook values, fp64."""
     q = codec.unpack(packed, state["bits"], n)
     yhat = state["codebook"].astype(np.float64)[q]
-    nu = np.asarray(norms, dtype=np.float32).astype(np.float64)
+    nu = np.asarray(norms, dtype=np.float32).astype(np.float64)[:n]   # one norm per token of the n
     return unrotate(yhat, state["signs"]) * nu[:, None]
 
 
 def decode_kv(state: Dict, packed: np.ndarray, norms: np.ndarray, n: int, dtype: str) -> np.ndarray:
     return codec.round_to(reconstruct_exact(state, packed, norms, n), dtype)
+
+
+def attend_compressed(k_state: Dict, v_state: Dict, k_packed: np.ndarray, k_norms: np.ndarray,
+                      v_packed: np.ndarray, v_norms: np.ndarray, n: int, q: np.ndarray,
+                      scale=None) -> np.ndarray:
+    """One decode step over a Walsh-Hadamard (TurboQuant-style) cache, the
+    decode-time side of the SQ versus TQ comparison (ablation summary,
+    "Regime-Specifieke Prestaties en Kalibratiesensitiviteit" and "Opslag vs.
+    Kwaliteit"): keys and values are the exact fp64 reconstructions
+    nu D H y_hat / sqrt(d), then the same softmax attention as the eigen
+    cache. Returns fp32 [g][d]."""
+    khat = reconstruct_exact(k_state, k_packed, k_norms, n)
+    vhat = reconstruct_exact(v_state, v_packed, v_norms, n)
+    return codec.softmax_attention(q, khat, vhat, scale)
+

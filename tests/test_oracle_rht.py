@@ -146,3 +146,61 @@ def test_tq_beats_sq_on_heavy_tails(lloyd):
     sq = codec.calibrate_head(x, 2048, 3.0)
     r_sq = codec.rel_mse(x, codec.decode_kv(sq, codec.encode_kv(sq, x), 8192, "bf16"))
     assert r_tq < r_sq
+
+
+# ------------------------------------------- attention over the Walsh-Hadamard cache
+def _rht_pair(n=19, seed=33):
+    rng = np.random.default_rng(seed)
+    cb = rht.codebook_fp32(np.sort(rng.uniform(-0.25, 0.25, 8)))
+    ks = rht.make_state(np.where(rng.random(D) < 0.5, -1, 1), cb)
+    vs = rht.make_state(np.where(rng.random(D) < 0.5, -1, 1), cb)
+    k = rng.standard_t(3, (n, D))
+    v = rng.standard_t(3, (n, D))
+    kp, kn = rht.encode_kv(ks, k)
+    vp, vn = rht.encode_kv(vs, v)
+    return ks, vs, kp, kn, vp, vn, k, v
+
+
+def test_rht_attention_matches_plain_loops():
+    """Against a plain-loop softmax attention of the exact reconstructions,
+    written out independently of the oracle's vectorised core."""
+    ks, vs, kp, kn, vp, vn, k, _ = _rht_pair()
+    n = k.shape[0]
+    q = np.random.default_rng(34).standard_normal((3, D))
+    got = rht.attend_compressed(ks, vs, kp, kn, vp, vn, n, q)
+    khat = rht.reconstruct_exact(ks, kp, kn, n)
+    vhat = rht.reconstruct_exact(vs, vp, vn, n)
+    for h in range(3):
+        s = [sum(q[h, i] * khat[t, i] for i in range(D)) / math.sqrt(D) for t in range(n)]
+        m = max(s)
+        e = [math.exp(x - m) for x in s]
+        z = sum(e)
+        want = [sum(e[t] * vhat[t, i] for t in range(n)) / z for i in range(D)]
+        assert np.allclose(got[h], want, rtol=1e-6, atol=1e-6)
+
+
+def test_rht_attention_special_cases():
+    ks, vs, kp, kn, vp, vn, k, v = _rht_pair()
+    q = np.random.default_rng(35).standard_normal((2, D))
+    one = rht.attend_compressed(ks, vs, kp, kn, vp, vn, 1, q)
+    v1 = rht.reconstruct_exact(vs, vp, vn, 1)[0]
+    assert np.allclose(one, np.tile(v1, (2, 1)), rtol=1e-6, atol=1e-7)
+    # identical keys: uniform weights -> mean of V_hat
+    kp2, kn2 = rht.encode_kv(ks, np.tile(k[:1], (k.shape[0], 1)))
+    o = rht.attend_compressed(ks, vs, kp2, kn2, vp, vn, k.shape[0], q)
+    assert np.allclose(o, rht.reconstruct_exact(vs, vp, vn, k.shape[0]).mean(axis=0)[None, :], rtol=1e-6,
+                       atol=1e-6)
+
+
+def test_rht_latent_identity():
+    """q . K_hat_t = nu_t / sqrt(d) * (y_hat_t . H D q): scores can be taken in
+    the rotated basis (the form the GPU uses), with H from scipy."""
+    ks, vs, kp, kn, vp, vn, k, _ = _rht_pair()
+    n = k.shape[0]
+    q = np.random.default_rng(36).standard_normal(D)
+    khat = rht.reconstruct_exact(ks, kp, kn, n)
+    yhat = ks["codebook"].astype(np.float64)[codec.unpack(kp, ks["bits"], n)]
+    qt = linalg.hadamard(D) @ (ks["signs"] * q)
+    lhs = khat @ q
+    rhs = kn.astype(np.float64) / math.sqrt(D) * (yhat @ qt)
+    assert np.allclose(lhs, rhs, rtol=1e-12, atol=1e-12)
