@@ -241,6 +241,23 @@ def main():
         torch.cuda.synchronize()
         step_us[f"decode_step@{b}"] = round(1e3 * e0.elapsed_time(e1) / args.steps, 2)
 
+    # (4) one attention step over the Walsh-Hadamard caches of the same layer
+    rk, rv = rpacked[0::2], rpacked[1::2]
+    rkn, rvn = rnorms[0::2], rnorms[1::2]
+    rht_out = torch.empty((heads, g, 128), dtype=torch.float32, device=dev)
+    rfn = lambda: stc.attend_rht_batched(rht_arr, kmap, vmap, rk, rkn, rv, rvn, n, q, ws=ws, out=rht_out)
+    for _ in range(3):
+        rfn()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        rfn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    step_us["attend_rht"] = round(1e3 * e0.elapsed_time(e1) / args.steps, 2)
+
     per_op = {}
     for i, (name, _, nbytes) in enumerate(ops):
         ms = [ev[k][i][0].elapsed_time(ev[k][i][1]) for k in range(args.steps)]
@@ -305,7 +322,9 @@ def main():
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 1),
         "codec_GBps": round(codec_bytes / (codec_ms * 1e-3) / 1e9, 1),
         "attn_tokens_per_s": {nm: round(1e3 / per_op[nm]["ms"], 1) for nm in attn_names},
-        "decode_step_us": step_us,  # append 1 K/V token per KV head + attention over n (not in value)
+        # not in value: a generation step per budget (append one K/V token per KV head, then attend over
+        # n) and one attention step over the Walsh-Hadamard caches
+        "extra_us": step_us,
         "breakdown": per_op,
         "roofline": {"bound": "hbm", "kernel": dname, "launches_per_step": d_n,
                      "algorithmic_bytes_per_launch": int(d_bytes / d_n),

@@ -253,6 +253,25 @@ stc_status stc_attend_compressed(const stc_head_info* k_info, const void* k_stat
                                  float* out_dev, float scale, void* ws_dev, size_t ws_bytes,
                                  stc_stream_t stream);
 
+/* One decode step over Walsh-Hadamard caches (the TurboQuant-style
+ * comparison path; ablation summary, "Regime-Specifieke Prestaties"): as
+ * stc_attend_compressed_batched, with K_hat_t = |k_t| D H y_hat_t / sqrt(d)
+ * and V_hat_t likewise, y_hat the codebook values of the 3-bit codes. The
+ * per-token norms written by the RHT encode are k_norms_dev +
+ * p*norms_pair_stride (and v_norms_dev likewise), fp32. Scores are taken
+ * against H D q (never reconstructing K_hat), the softmax-weighted values are
+ * accumulated in the rotated basis and rotated back once. RHT states only
+ * (STC_EUNSUPPORTED otherwise); ws_dev as for stc_attend_compressed_batched. */
+stc_status stc_attend_rht_batched(const void* states_dev, int64_t n_states,
+                                  const int32_t* k_state_of_pair_dev,
+                                  const int32_t* v_state_of_pair_dev, const stc_head_info* infos,
+                                  int64_t n_pairs, int64_t n_tokens, const void* k_packed_dev,
+                                  const float* k_norms_dev, const void* v_packed_dev,
+                                  const float* v_norms_dev, int64_t packed_pair_stride,
+                                  int64_t norms_pair_stride, int32_t group, const float* q_dev,
+                                  float* out_dev, float scale, void* ws_dev, size_t ws_bytes,
+                                  stc_stream_t stream);
+
 /* One generation step for n_pairs KV heads: append the new K token
  * k_new_dev[p][128] and V token v_new_dev[p][128] (dtype STC_BF16 or
  * STC_F32, rows of 128 elements) to pair p's packed K and V streams, which

@@ -261,6 +261,28 @@ def append_kv_batched(states: StateArray, x: torch.Tensor, n_old: int, packed: t
     return packed
 
 
+def attend_rht_batched(states: StateArray, k_state_of_pair: torch.Tensor, v_state_of_pair: torch.Tensor,
+                       k_packed: torch.Tensor, k_norms: torch.Tensor, v_packed: torch.Tensor,
+                       v_norms: torch.Tensor, n: int, q: torch.Tensor, scale: Optional[float] = None,
+                       ws: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None):
+    """Attention over Walsh-Hadamard caches: k_packed, v_packed [P][stride] uint8 (same
+    stride), k_norms, v_norms fp32 [P][>= n] (same stride); q fp32 [P][g][128]."""
+    Pn, g = q.shape[0], q.shape[1]
+    assert k_packed.stride(0) == v_packed.stride(0) and k_norms.stride(0) == v_norms.stride(0)
+    assert k_norms.dtype == torch.float32 and k_norms.stride(1) == 1 and v_norms.stride(1) == 1
+    scale = (1.0 / np.sqrt(D)) if scale is None else scale
+    if out is None:
+        out = torch.empty((Pn, g, D), dtype=torch.float32, device=q.device)
+    need = attend_workspace_bytes(Pn, g, n)
+    if ws is None or ws.numel() < need:
+        ws = torch.zeros(need, dtype=torch.uint8, device=q.device)  # zero-filled once
+    check("stc_attend_rht_batched", lib().stc_attend_rht_batched(
+        _ptr(states.blob), states.n, _ptr(_map_arg(k_state_of_pair)), _ptr(_map_arg(v_state_of_pair)),
+        states.infos, Pn, n, _ptr(k_packed), _ptr(k_norms), _ptr(v_packed), _ptr(v_norms), k_packed.stride(0),
+        k_norms.stride(0), g, _ptr(q), _ptr(out), float(scale), _ptr(ws), ws.numel(), _stream()))
+    return out
+
+
 def decode_step_batched(states: StateArray, k_state_of_pair: torch.Tensor, v_state_of_pair: torch.Tensor,
                         n_old: int, k_new: torch.Tensor, v_new: torch.Tensor, k_packed: torch.Tensor,
                         v_packed: torch.Tensor, q: torch.Tensor, scale: Optional[float] = None,

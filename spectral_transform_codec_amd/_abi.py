@@ -49,6 +49,8 @@ SIGNATURES = {
                                               c_i64, c_i32, c_vp, c_vp, c_f32, c_vp, c_size, c_vp]),
     "stc_attend_compressed": (c_i32, [P(HeadInfo), c_vp, P(HeadInfo), c_vp, c_i64, c_vp, c_vp, c_i32, c_vp,
                                       c_vp, c_f32, c_vp, c_size, c_vp]),
+    "stc_attend_rht_batched": (c_i32, [c_vp, c_i64, c_vp, c_vp, P(HeadInfo), c_i64, c_i64, c_vp, c_vp, c_vp, c_vp,
+                                       c_i64, c_i64, c_i32, c_vp, c_vp, c_f32, c_vp, c_size, c_vp]),
     "stc_decode_step_batched": (c_i32, [c_vp, c_i64, c_vp, c_vp, P(HeadInfo), c_i64, c_i64, c_vp, c_vp, c_i32,
                                         c_vp, c_vp, c_i64, c_i32, c_vp, c_vp, c_f32, c_vp, c_size, c_vp]),
     "stc_status_str": (c_cp, [c_i32]),

@@ -58,6 +58,24 @@ uint16_t bf16_bits_rne(float f) {
   u += 0x7fffu + ((u >> 16) & 1u);
   return (uint16_t)(u >> 16);
 }
+// IEEE binary16 bits of fp32 f, round to nearest even (NaN stays NaN,
+// values from 65520 up become infinity, subnormal halves below 2^-14).
+uint16_t f16_bits_rne(float f) {
+  uint32_t u;
+  std::memcpy(&u, &f, 4);
+  const uint16_t sign = (uint16_t)((u >> 16) & 0x8000u);
+  const uint32_t a = u & 0x7fffffffu;
+  if (a > 0x7f800000u) return sign | 0x7e00u;
+  if (a >= 0x477ff000u) return sign | 0x7c00u;
+  if (a < 0x38800000u) {
+    float av;
+    std::memcpy(&av, &a, 4);
+    return sign | (uint16_t)std::nearbyint(av * 16777216.0f);  // units of 2^-24
+  }
+  uint32_t r = a - 0x38000000u;  // exponent bias 127 -> 15
+  r += 0xfffu + ((r >> 13) & 1u);
+  return sign | (uint16_t)(r >> 13);
+}
 double bf16_value(uint16_t b) {
   uint32_t u = (uint32_t)b << 16;
   float f;
@@ -483,6 +501,32 @@ stc_status stc_rht_state_init(int32_t d, const int8_t* signs, const float* codeb
       ut_hi[R * D + i] = hsign * signs[i] > 0 ? 0x3F80u : 0xBF80u;
     }
   }
+  // attention reads a Walsh-Hadamard cache through the eigen machinery:
+  // U = D H / sqrt(d) (U_ij = sign_i H[i][j] / sqrt(d); H is symmetric), unit
+  // steps and no level offset, so the latent code average is the average of
+  // codebook values and U rotates it back
+  float* u32 = reinterpret_cast<float*>(blob.data() + OFF_U32);
+  const double rs = 1.0 / std::sqrt((double)D);
+  for (int i = 0; i < D; ++i)
+    for (int j = 0; j < D; ++j) {
+      const int hsign = (__builtin_popcount((unsigned)(i & j)) & 1) ? -1 : 1;
+      u32[i * D + j] = (float)(hsign * signs[i] * rs);
+    }
+  for (int j = 0; j < D; ++j) {
+    h->step32[j] = 1.0f;
+    h->step64[j] = 1.0;
+    h->halfspan[j] = 0.0f;
+  }
+  for (int k = 0; k < 8; ++k) {
+    const uint16_t hi = bf16_bits_rne(codebook[k]);
+    const uint16_t lo = bf16_bits_rne(codebook[k] - bf16_value(hi));
+    const uint16_t hf = f16_bits_rne(codebook[k]);
+    const uint16_t v[3] = {hi, lo, hf};
+    for (int t = 0; t < 3; ++t) {
+      h->cbt[4 * t + (k >> 2)] |= (uint32_t)(v[t] & 0xFF) << (8 * (k & 3));
+      h->cbt[4 * t + 2 + (k >> 2)] |= (uint32_t)(v[t] >> 8) << (8 * (k & 3));
+    }
+  }
   for (int k = 0; k < 8; ++k) h->cb[k] = codebook[k];
   for (int k = 0; k < 7; ++k) h->cb_thr[k] = (float)(0.5 * ((double)codebook[k] + (double)codebook[k + 1]));
   info->d = d;
@@ -717,6 +761,39 @@ stc_status stc_attend_compressed_batched(const void* states_dev, int64_t n_state
                  static_cast<const unsigned char*>(k_packed_dev), static_cast<const unsigned char*>(v_packed_dev),
                  group, q_dev, out_dev, scale, static_cast<unsigned char*>(ws_dev), mb};
   if (launch_attend(a, stream)) return fail(STC_EDEVICE, "attend launch: %s", hipGetErrorString(hipGetLastError()));
+  return ok();
+}
+
+stc_status stc_attend_rht_batched(const void* states_dev, int64_t n_states, const int32_t* k_map,
+                                  const int32_t* v_map, const stc_head_info* infos, int64_t n_pairs,
+                                  int64_t n_tokens, const void* k_packed_dev, const float* k_norms_dev,
+                                  const void* v_packed_dev, const float* v_norms_dev, int64_t packed_pair_stride,
+                                  int64_t norms_pair_stride, int32_t group, const float* q_dev, float* out_dev,
+                                  float scale, void* ws_dev, size_t ws_bytes, stc_stream_t stream) {
+  bool rht = false;
+  int mb = 0;
+  if (stc_status s = check_batch("attend_rht", states_dev, n_states, infos, n_pairs, n_tokens, packed_pair_stride,
+                                 &rht, &mb)) return s;
+  if (!rht) return fail(STC_EUNSUPPORTED, "attend_rht: Walsh-Hadamard states only");
+  if (group < 1 || group > 16) return fail(STC_EUNSUPPORTED, "attend_rht: group %d outside 1..16", group);
+  if (n_tokens <= 0) return fail(STC_EINVAL, "attend_rht: need at least one cached token");
+  if (!k_packed_dev || !v_packed_dev || !k_norms_dev || !v_norms_dev || !q_dev || !out_dev || !ws_dev)
+    return fail(STC_EINVAL, "attend_rht: NULL buffer");
+  if (!aligned(k_packed_dev, 16) || !aligned(v_packed_dev, 16) || !aligned(q_dev, 16) || !aligned(out_dev, 16) ||
+      !aligned(ws_dev, 256) || !aligned(k_norms_dev, 4) || !aligned(v_norms_dev, 4))
+    return fail(STC_EINVAL, "attend_rht: misaligned buffer");
+  if (n_pairs > 1 && norms_pair_stride < n_tokens)
+    return fail(STC_EINVAL, "attend_rht: norms stride %lld < %lld tokens", (long long)norms_pair_stride,
+                (long long)n_tokens);
+  if (!std::isfinite(scale)) return fail(STC_EINVAL, "attend_rht: scale must be finite");
+  const size_t need = stc_attend_workspace_bytes(n_pairs, group, n_tokens);
+  if (ws_bytes < need) return fail(STC_EWORKSPACE, "attend_rht: workspace %zu < %zu", ws_bytes, need);
+  const unsigned char* st = static_cast<const unsigned char*>(states_dev);
+  AttendLaunch a{st, k_map, st, v_map, n_states, n_pairs, n_tokens, packed_pair_stride,
+                 static_cast<const unsigned char*>(k_packed_dev), static_cast<const unsigned char*>(v_packed_dev),
+                 group, q_dev, out_dev, scale, static_cast<unsigned char*>(ws_dev), mb,
+                 k_norms_dev, v_norms_dev, norms_pair_stride, true};
+  if (launch_attend(a, stream)) return fail(STC_EDEVICE, "attend_rht launch: %s", hipGetErrorString(hipGetLastError()));
   return ok();
 }
 

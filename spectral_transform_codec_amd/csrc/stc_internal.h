@@ -66,6 +66,11 @@ struct alignas(16) DevHdr {
   // clamp(floor(x.U_j yscale_j + yhalf_j), 0, L_j - 1), yhalf_j = L_j/2
   // (L_j - 1/2 for a zero step, where every threshold is 0).
   float yhalf[D];
+  // Walsh-Hadamard attention: the codebook as byte planes for v_perm lookups
+  // (code c selects byte c of the 8-byte plane held in words 2i, 2i+1):
+  // planes 0/1 low/high bytes of bf16(cb), 2/3 of bf16(cb - bf16(cb)),
+  // 4/5 of fp16(cb)
+  uint32_t cbt[12];
 };
 static_assert(sizeof(DevHdr) <= OFF_U32, "header too large");
 
@@ -151,6 +156,10 @@ struct AttendLaunch {
   float scale;
   unsigned char* ws;
   int max_bits;
+  const float* k_norms = nullptr;  // Walsh-Hadamard caches: per-token norms
+  const float* v_norms = nullptr;
+  int64_t norms_stride = 0;       // elements between pairs
+  bool rht = false;
 };
 
 int launch_gram(const void* x, int dtype, int64_t ld, int64_t n_calib, double* gram, void* stream);

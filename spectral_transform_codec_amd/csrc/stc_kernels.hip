@@ -1097,6 +1097,9 @@ struct AttK {
   long long split_tokens, n_splits;
   int stream_words, region_words;
   long long pair_base;  // first pair of this launch (maps, caches, q, out); ws is per launch
+  const float* k_norms;  // Walsh-Hadamard caches: per-token norms, pair stride norms_stride
+  const float* v_norms;
+  long long norms_stride;
 };
 
 constexpr int ATT_WAVES_MAX = 16;
@@ -1107,7 +1110,7 @@ constexpr int VT_ROW = 9;                        // dwords per row of the [chann
 constexpr int VT_WORDS = 128 * VT_ROW;
 constexpr int P_ROWH = 36;                       // fp16 per row of P [head][token]
 constexpr int P_WORDS = 16 * P_ROWH / 2;
-constexpr int ATT_FIXED_BYTES = 32 * AROW + 6 * 128 * 4;
+constexpr int ATT_FIXED_BYTES = 32 * AROW + 6 * 128 * 4 + 64;  // a table, unpack tables, codebook planes
 // Words of one wave's region: the K and V record streams (reused for the
 // transposed V codes once both are extracted), P, and per-head alpha.
 __host__ __device__ constexpr int att_stream_words(int max_bits) { return max_bits + (max_bits >> 5) + 8; }
@@ -1126,6 +1129,15 @@ __device__ __forceinline__ f16x4 bytes_to_f16x4(unsigned v) {
   const f16x2 a = __builtin_bit_cast(f16x2, lo) - off;
   const f16x2 b = __builtin_bit_cast(f16x2, hi) - off;
   return (f16x4){a[0], a[1], b[0], b[1]};
+}
+
+// Four codes (bytes of c, each 0..7) -> four 16-bit table entries, from the
+// low-byte plane (l0: entries 0..3, l1: 4..7) and the high-byte plane
+// (h0, h1): entries of codes 0, 1 in the first word, 2, 3 in the second.
+__device__ __forceinline__ u32x2 lut16x4(unsigned c, unsigned l0, unsigned l1, unsigned h0, unsigned h1) {
+  const unsigned lo = __builtin_amdgcn_perm(l1, l0, c);
+  const unsigned hi = __builtin_amdgcn_perm(h1, h0, c);
+  return (u32x2){__builtin_amdgcn_perm(hi, lo, 0x05010400u), __builtin_amdgcn_perm(hi, lo, 0x07030602u)};
 }
 
 // 4x4 byte transpose across the 4 lanes of a quad: lane e holds byte c of
@@ -1285,12 +1297,18 @@ __device__ __forceinline__ void att_combine_pair(const AttK& a, long long p, flo
   }
 }
 
-template <int NW>
+// RHT: a Walsh-Hadamard cache. Its state stores U = D H / sqrt(d) with unit
+// steps, so the score table and the split merge are the eigen ones; the
+// codes are looked up in the codebook (bf16 high and low parts for the
+// scores, fp16 for P.V), scores are scaled by the key's norm and P by the
+// value's norm over the largest value norm of the wave's block (the scale
+// is carried in the accumulators and restored at the merge).
+template <int NW, bool RHT>
 __global__ void __launch_bounds__(ATT_THREADS, 1) k_att_main(AttK a) {
   extern __shared__ __align__(16) unsigned char smem[];
   unsigned char* sA = smem;                                        // a table [32][AROW]
-  unsigned* sTab = reinterpret_cast<unsigned*>(smem + 32 * AROW);  // K tables, then V tables
-  unsigned* sReg0 = sTab + 6 * 128;                                // wave regions
+  unsigned* sTab = reinterpret_cast<unsigned*>(smem + 32 * AROW);  // K tables, V tables, codebook planes
+  unsigned* sReg0 = sTab + 6 * 128 + 16;                           // wave regions
   const int nwav = (int)(blockDim.x >> 6);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -1322,6 +1340,7 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_att_main(AttK a) {
   if (tid < 128) {
     att_tables(hk, sTab, tid);
     att_tables(hv, sTab + 384, tid);
+    if (RHT && tid < 12) sTab[768 + tid] = tid < 8 ? hk->cbt[tid] : hv->cbt[tid];  // K: bf16 hi/lo, V: fp16
   }
   // Score A operand: a_hj = (U_K^T q_h)_j step_j scale log2(e) as bf16 high
   // (rows 0..15) and low (rows 16..31) parts. Thread (part, j) sums rows
@@ -1396,6 +1415,7 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_att_main(AttK a) {
   f32x4 acc_o[8];
 #pragma unroll
   for (int nb = 0; nb < 8; ++nb) acc_o[nb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  float vscale = 1.0f;  // RHT: acc_o is in units of the current block's largest value norm
 
   const long long PkL = packed_len((long long)Bk, n), PvL = packed_len((long long)Bv, n);
   const unsigned char* gk = a.k_packed + pg * a.packed_stride;
@@ -1424,6 +1444,12 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_att_main(AttK a) {
     const lds_u8* vL = kL + 1536;
     const lds_u8* aL = lds_ptr(ab);
     const bool tok_ok = tok0 + t32 < t_end;
+    // RHT: the norms of the lane's token
+    float nk = 1.0f, nv = 0.0f;
+    if (RHT && tok_ok) {
+      nk = a.k_norms[pg * a.norms_stride + tok0 + t32];
+      nv = a.v_norms[pg * a.norms_stride + tok0 + t32];
+    }
     // ---- scores: channels 64h + 8ks + i of token t as bf16 B fragments
     float sc[2][4];
     {
@@ -1431,24 +1457,53 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_att_main(AttK a) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
       const unsigned tB = (unsigned)t32 * Bk;
+      u32x4 cbh, cbl;  // RHT: codebook planes (bf16 high parts, low parts)
+      if (RHT) {
+        cbh = LDS_AT(u32x4, kL - 64 * 4 * h + 768 * 4);
+        cbl = LDS_AT(u32x4, kL - 64 * 4 * h + 772 * 4);
+      }
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
-        bf16x8 bf;
+        if (RHT) {
+          u32x4 fh, fl;
 #pragma unroll
-        for (int hg = 0; hg < 2; ++hg) {
-          const unsigned v = Bk ? att_group_bytes(sKs, kL, tB, 2 * ks + hg) : 0u;
+          for (int hg = 0; hg < 2; ++hg) {
+            const unsigned v = att_group_bytes(sKs, kL, tB, 2 * ks + hg);
+            const u32x2 vh = lut16x4(v, cbh[0], cbh[1], cbh[2], cbh[3]);
+            const u32x2 vl = lut16x4(v, cbl[0], cbl[1], cbl[2], cbl[3]);
+            fh[2 * hg] = vh[0]; fh[2 * hg + 1] = vh[1];
+            fl[2 * hg] = vl[0]; fl[2 * hg + 1] = vl[1];
+          }
+          const bf16x8 at = LDS_AT(bf16x8, aL + 16 * ks);
+          acc = mfma32_bf16(at, __builtin_bit_cast(bf16x8, fh), acc);
+          acc = mfma32_bf16(at, __builtin_bit_cast(bf16x8, fl), acc);
+        } else {
+          bf16x8 bf;
 #pragma unroll
-          for (int j = 0; j < 4; ++j) bf[4 * hg + j] = (__bf16)(float)((v >> (8 * j)) & 0xffu);
+          for (int hg = 0; hg < 2; ++hg) {
+            const unsigned v = Bk ? att_group_bytes(sKs, kL, tB, 2 * ks + hg) : 0u;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) bf[4 * hg + j] = (__bf16)(float)((v >> (8 * j)) & 0xffu);
+          }
+          acc = mfma32_bf16(LDS_AT(bf16x8, aL + 16 * ks), bf, acc);
         }
-        acc = mfma32_bf16(LDS_AT(bf16x8, aL + 16 * ks), bf, acc);
       }
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int H = 8 * i + 4 * h + j;
-          sc[i][j] = (tok_ok && H < g) ? acc[4 * i + j] + acc[4 * (i + 2) + j] : -INFINITY;
+          sc[i][j] = (tok_ok && H < g) ? (acc[4 * i + j] + acc[4 * (i + 2) + j]) * nk : -INFINITY;
         }
+    }
+    // RHT: P is stored as p * |v_t| / (largest |v| of the block), at most 1
+    float pscale = 1.0f, vratio = 1.0f;
+    if (RHT) {
+      float vm = half_max(nv);
+      vm = vm > 0.0f ? vm : 1.0f;
+      pscale = nv / vm;
+      vratio = vscale / vm;  // rescales acc_o from the previous block's units
+      vscale = vm;
     }
     // ---- online softmax; P (fp16) -> sP[head][token], alpha -> sAl
 #pragma unroll
@@ -1463,8 +1518,8 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_att_main(AttK a) {
         const float mnew = fmaxf(mold[j], mx);
         const float alpha = (mnew == -INFINITY) ? 1.0f : exp2f(mold[j] - mnew);
         const float pv = (mnew == -INFINITY) ? 0.0f : exp2f(sc[i][j] - mnew);
-        const _Float16 ph = (_Float16)pv;
-        l_run[i][j] = l_run[i][j] * alpha + (float)ph;
+        const _Float16 ph = (_Float16)(RHT ? pv * pscale : pv);
+        l_run[i][j] = l_run[i][j] * alpha + (RHT ? pv : (float)ph);
         mnw[j] = mnew;
         sP[H * P_ROWH + t32] = ph;
         if (t32 == 0) sAl[H] = alpha;
@@ -1495,18 +1550,24 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_att_main(AttK a) {
     __builtin_amdgcn_wave_barrier();
     // ---- rescale and accumulate P x V: heads 4*g4 + r, channels 16nb + c16
     {
-      const f32x4 al = *reinterpret_cast<const f32x4*>(sAl + 4 * g4);
+      f32x4 al = *reinterpret_cast<const f32x4*>(sAl + 4 * g4);
+      if (RHT) al *= vratio;
 #pragma unroll
       for (int nb = 0; nb < 8; ++nb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc_o[nb][r] *= al[r];
+      u32x4 cbv;  // RHT: fp16 codebook planes
+      if (RHT) cbv = *reinterpret_cast<const u32x4*>(sTab + 776);
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
         const f16x4 pa = *reinterpret_cast<const f16x4*>(sP + c16 * P_ROWH + 16 * kt + 4 * g4);
 #pragma unroll
         for (int nb = 0; nb < 8; ++nb) {
           const unsigned vb = sVT[(16 * nb + c16) * VT_ROW + 4 * kt + g4];
-          acc_o[nb] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, bytes_to_f16x4(vb), acc_o[nb], 0, 0, 0);
+          f16x4 vf;
+          if (RHT) vf = __builtin_bit_cast(f16x4, lut16x4(vb, cbv[0], cbv[1], cbv[2], cbv[3]));
+          else vf = bytes_to_f16x4(vb);
+          acc_o[nb] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, vf, acc_o[nb], 0, 0, 0);
         }
       }
     }
@@ -1543,7 +1604,7 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_att_main(AttK a) {
 #pragma unroll
       for (int nb = 0; nb < 8; ++nb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) mine[r * ATT_PART_FLOATS + 16 * nb + c16] = acc_o[nb][r];
+        for (int r = 0; r < 4; ++r) mine[r * ATT_PART_FLOATS + 16 * nb + c16] = RHT ? acc_o[nb][r] * vscale : acc_o[nb][r];
     }
     __syncthreads();
     const int nh = g - 4 * c4 < 4 ? g - 4 * c4 : 4;
@@ -1594,10 +1655,12 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_att_main(AttK a) {
 
 int launch_attend(const AttendLaunch& L, void* stream) {
   if (!g_att_attr_done) {
-    if (hipFuncSetAttribute((const void*)k_att_main<8>, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) !=
-            hipSuccess ||
-        hipFuncSetAttribute((const void*)k_att_main<16>, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) !=
-            hipSuccess)
+    if (hipFuncSetAttribute((const void*)k_att_main<8, false>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            160 * 1024) != hipSuccess ||
+        hipFuncSetAttribute((const void*)k_att_main<16, false>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            160 * 1024) != hipSuccess ||
+        hipFuncSetAttribute((const void*)k_att_main<8, true>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            160 * 1024) != hipSuccess)
       return 1;
     g_att_attr_done = true;
   }
@@ -1617,6 +1680,9 @@ int launch_attend(const AttendLaunch& L, void* stream) {
   a.out = L.out;
   a.scale = L.scale;
   a.ws = L.ws;
+  a.k_norms = L.k_norms;
+  a.v_norms = L.v_norms;
+  a.norms_stride = L.norms_stride;
   a.stream_words = att_stream_words(L.max_bits);
   a.region_words = att_region_words(L.max_bits);
   int waves = ATT_WAVES_MAX;
@@ -1631,10 +1697,13 @@ int launch_attend(const AttendLaunch& L, void* stream) {
     size_t att_lds = ATT_FIXED_BYTES + (size_t)waves * a.region_words * 4;
     const size_t cmb = att_combine_lds_bytes();
     if (att_lds < cmb) att_lds = cmb;
-    if (L.max_bits <= 512)
-      hipLaunchKernelGGL((k_att_main<8>), dim3((unsigned)a.n_splits, (unsigned)np), dim3(64 * waves), att_lds, s, a);
+    const dim3 grid((unsigned)a.n_splits, (unsigned)np);
+    if (L.rht)
+      hipLaunchKernelGGL((k_att_main<8, true>), grid, dim3(64 * waves), att_lds, s, a);
+    else if (L.max_bits <= 512)
+      hipLaunchKernelGGL((k_att_main<8, false>), grid, dim3(64 * waves), att_lds, s, a);
     else
-      hipLaunchKernelGGL((k_att_main<16>), dim3((unsigned)a.n_splits, (unsigned)np), dim3(64 * waves), att_lds, s, a);
+      hipLaunchKernelGGL((k_att_main<16, false>), grid, dim3(64 * waves), att_lds, s, a);
   }
   return hipGetLastError() != hipSuccess;
 }
