@@ -467,8 +467,9 @@ int launch_encode_eigen(const EncodeLaunch& L, void* stream) {
   int dev = 0, cus = 256;
   (void)hipGetDevice(&dev);
   (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  long long grid = (a.total_blocks + ENC_WAVES - 1) / ENC_WAVES;
-  if (grid > cus) grid = cus;
+  // one workgroup per CU, or per block when there are fewer blocks than CUs
+  // (short appends: each workgroup then stages one state for one block)
+  long long grid = a.total_blocks < cus ? a.total_blocks : cus;
   a.blocks_per_wg = (a.total_blocks + grid - 1) / grid;
   grid = (a.total_blocks + a.blocks_per_wg - 1) / a.blocks_per_wg;
   a.grid = (int)grid;
@@ -794,8 +795,9 @@ int launch_decode_eigen(const DecodeLaunch& L, void* stream) {
   int dev = 0, cus = 256;
   (void)hipGetDevice(&dev);
   (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  long long grid = (a.total_blocks + DEC_WAVES - 1) / DEC_WAVES;
-  if (grid > cus) grid = cus;
+  // one workgroup per CU, or per block when there are fewer blocks than CUs
+  // (short appends: each workgroup then stages one state for one block)
+  long long grid = a.total_blocks < cus ? a.total_blocks : cus;
   a.blocks_per_wg = (a.total_blocks + grid - 1) / grid;
   grid = (a.total_blocks + a.blocks_per_wg - 1) / a.blocks_per_wg;
   a.grid = (int)grid;
