@@ -127,6 +127,31 @@ double stc_delta_star(int32_t bits);
  * to the lowest j). bits_out[d]. STC_EBUDGET if total_bits > 8 d or < 0. */
 stc_status stc_water_fill(int32_t d, const double* lambda, int32_t total_bits, uint8_t* bits_out);
 
+/* Allocation variants, all calibrate-time choices feeding the same
+ * quantizer, format and kernels (pass the result as `bits` to
+ * stc_calibrate_head / stc_state_init):
+ *  GREEDY       stc_water_fill (param unused);
+ *  OPERATIONAL  greedy on the quantizer's own distortion: each bit to
+ *               argmax lambda_j (eps(b_j) - eps(b_j + 1)), eps(b) the MSE of
+ *               the b-bit quantizer on a unit Gaussian, eps(0) = 1 (SPECTRA
+ *               summary, "La Pipeline" step 2; param unused);
+ *  GROUPED      one width per group of param adjacent channels (param
+ *               divides d), greedy on the group variance sums, param bits per
+ *               step while at least param bits remain ("Raggruppamento");
+ *  FLOOR        param bits on every channel, the rest greedy (ablation
+ *               summary, "Opslag vs. Kwaliteit": tail floor);
+ *  GAP          spectral-gap pruning: d_eff = 1 + the first j with
+ *               lambda_j >= param * lambda_{j+1} (param > 1; a positive
+ *               lambda_j before a non-positive one counts), channels from
+ *               d_eff on get 0 bits, the others share min(budget, 8 d_eff)
+ *               greedily (ablation summary, d_eff).
+ * Ties to the lowest index, lambda <= 0 counts as 0. Errors: STC_EBUDGET for
+ * a budget outside [0, 8d], STC_EINVAL for a bad variant or param. */
+enum { STC_ALLOC_GREEDY = 0, STC_ALLOC_OPERATIONAL = 1, STC_ALLOC_GROUPED = 2, STC_ALLOC_FLOOR = 3,
+       STC_ALLOC_GAP = 4 };
+stc_status stc_allocate_bits(int32_t d, const double* lambda, int32_t total_bits, int32_t variant,
+                             double param, uint8_t* bits_out);
+
 /* Symmetric eigendecomposition A = U diag(lambda) U^T (cyclic Jacobi, fp64),
  * lambda descending, columns sign-fixed as above. A, U row-major d*d. */
 stc_status stc_eigh(int32_t d, const double* a, double* u_out, double* lambda_out);

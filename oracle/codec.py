@@ -152,6 +152,99 @@ def delta_star(bits: int) -> float:
                                  xtol=1e-300, rtol=8.9e-16, maxiter=500))
 
 
+@functools.lru_cache(maxsize=None)
+def quantizer_mse(bits: int) -> float:
+    """eps(b): distortion of a unit-variance Gaussian channel at b bits, the
+    MSE of the 2^b-level quantizer with step delta*(b); eps(0) = 1 (the channel
+    is dropped and its whole variance is lost)."""
+    if bits == 0:
+        return 1.0
+    return uniform_gaussian_mse(delta_star(bits), 1 << bits)
+
+
+ALLOC_VARIANTS = ("greedy", "operational", "grouped", "floor", "gap")
+
+
+def allocate_bits(lam: np.ndarray, total_bits: int, variant: str = "greedy", param: float = 0.0,
+                  max_bits: int = MAX_BITS) -> np.ndarray:
+    """Bit allocation variants, all calibrate-time choices that feed the same
+    quantizer and format.
+
+    greedy      the default reverse water-filling (`water_fill`).
+    operational greedy on the quantizer's actual distortion: each bit goes
+                to argmax lam_j (eps(b_j) - eps(b_j + 1)) (SPECTRA summary,
+                "La Pipeline" step 2: bits follow the marginal variances;
+                READING: the rate-distortion model replaced by the uniform
+                quantizer's own MSE curve).
+    grouped     adjacent channels share one width (SPECTRA summary, "La
+                Pipeline" step 2, "Raggruppamento"): READING: groups of
+                G = param channels [kG, (k+1)G); greedy over groups on the
+                group variance sum Lam_k 4^-b_k, G bits per step, while at
+                least G bits remain (sum of bits = G floor(B / G)).
+    floor       a fixed floor of f = param bits on every channel (the
+                ablation summary's "tail floor", "Opslag vs. Kwaliteit"),
+                the rest of the budget by the default greedy.
+    gap         spectral-gap pruning of the effective dimension (ablation
+                summary, "Regime-Specifieke Prestaties en
+                Kalibratiesensitiviteit", d_eff): READING: d_eff = 1 + the
+                first j with lam_j >= r lam_{j+1} (r = param; d if none, and
+                a positive lam_j followed by lam_{j+1} <= 0 counts as a gap);
+                channels from d_eff on get 0 bits, the first d_eff channels
+                share the budget by the default greedy (at most max_bits
+                each, so the sum is min(B, max_bits d_eff)).
+    Ties go to the lowest index; lam <= 0 counts as 0."""
+    lam = np.asarray(lam, dtype=np.float64)
+    d = lam.shape[0]
+    if total_bits < 0 or total_bits > max_bits * d:
+        raise ValueError("budget out of range")
+    lam_pos = np.where(lam > 0.0, lam, 0.0)
+    if variant == "greedy":
+        return water_fill(lam, total_bits, max_bits)
+    if variant == "operational":
+        b = np.zeros(d, dtype=np.int64)
+        for _ in range(total_bits):
+            gain = np.array([lam_pos[j] * (quantizer_mse(int(b[j])) - quantizer_mse(int(b[j]) + 1))
+                             if b[j] < max_bits else -1.0 for j in range(d)])
+            b[int(np.argmax(gain))] += 1
+        return b.astype(np.uint8)
+    if variant == "grouped":
+        G = int(param)
+        if G < 1 or d % G:
+            raise ValueError("group size must divide d")
+        lam_g = lam_pos.reshape(d // G, G).sum(axis=1)
+        bg = np.zeros(d // G, dtype=np.int64)
+        left = total_bits
+        while left >= G:
+            gain = np.where(bg < max_bits, lam_g * np.ldexp(1.0, -2 * bg), -1.0)
+            if gain.max() < 0:
+                break
+            bg[int(np.argmax(gain))] += 1
+            left -= G
+        return np.repeat(bg, G).astype(np.uint8)
+    if variant == "floor":
+        f = int(param)
+        if f < 0 or f > max_bits or f * d > total_bits:
+            raise ValueError("floor out of range")
+        b = np.full(d, f, dtype=np.int64)
+        for _ in range(total_bits - f * d):
+            gain = np.where(b < max_bits, lam_pos * np.ldexp(1.0, -2 * b), -1.0)
+            b[int(np.argmax(gain))] += 1
+        return b.astype(np.uint8)
+    if variant == "gap":
+        r = float(param)
+        if not r > 1.0:
+            raise ValueError("gap ratio must exceed 1")
+        d_eff = d
+        for j in range(d - 1):
+            if lam_pos[j] > 0 and (lam_pos[j + 1] <= 0 or lam_pos[j] >= r * lam_pos[j + 1]):
+                d_eff = j + 1
+                break
+        b = np.zeros(d, dtype=np.int64)
+        b[:d_eff] = water_fill(lam[:d_eff], min(total_bits, max_bits * d_eff), max_bits)
+        return b.astype(np.uint8)
+    raise ValueError(f"unknown variant {variant}")
+
+
 def channel_offsets(bits: np.ndarray) -> np.ndarray:
     """Bit offset of each channel inside a token record (prefix sum)."""
     bits = np.asarray(bits, dtype=np.int64)

@@ -77,6 +77,18 @@ def water_fill(lam: np.ndarray, total: int) -> np.ndarray:
     return out
 
 
+ALLOC_VARIANTS = {"greedy": 0, "operational": 1, "grouped": 2, "floor": 3, "gap": 4}
+
+
+def allocate_bits(lam: np.ndarray, total: int, variant: str = "greedy", param: float = 0.0) -> np.ndarray:
+    lam = np.ascontiguousarray(lam, dtype=np.float64)
+    out = np.zeros(lam.shape[0], dtype=np.uint8)
+    check("stc_allocate_bits", lib().stc_allocate_bits(lam.shape[0], _np_ptr(lam, ctypes.c_double), int(total),
+                                                       ALLOC_VARIANTS[variant], float(param),
+                                                       _np_ptr(out, ctypes.c_uint8)))
+    return out
+
+
 def eigh(a: np.ndarray):
     a = np.ascontiguousarray(a, dtype=np.float64)
     d = a.shape[0]

@@ -29,6 +29,7 @@ SIGNATURES = {
     "stc_total_bits": (c_i32, [c_f32, c_i32]),
     "stc_delta_star": (c_f64, [c_i32]),
     "stc_water_fill": (c_i32, [c_i32, P(c_f64), c_i32, P(c_u8)]),
+    "stc_allocate_bits": (c_i32, [c_i32, P(c_f64), c_i32, c_i32, c_f64, P(c_u8)]),
     "stc_eigh": (c_i32, [c_i32, P(c_f64), P(c_f64), P(c_f64)]),
     "stc_lloyd_max": (c_i32, [P(c_f64), c_i64, c_i32, c_f64, c_i32, P(c_f64), P(c_i32)]),
     "stc_state_init": (c_i32, [c_i32, c_i32, P(c_f64), P(c_f64), P(c_u8), P(c_f64), P(HeadInfo), c_vp, c_vp]),

@@ -396,6 +396,114 @@ stc_status stc_water_fill(int32_t d, const double* lambda, int32_t total_bits, u
   return ok();
 }
 
+// MSE of the midrise uniform quantizer with `levels` levels and step delta
+// on N(0, 1): both halves of sum over cells of int (x - level)^2 phi(x) dx,
+// with int_a^b x^2 phi = [Q(x) ... ] written through Q = upper tail, phi.
+double gauss_uniform_mse(double delta, int levels) {
+  const double inv_sqrt2pi = 0.39894228040143267794;
+  const int half = levels / 2;
+  double acc = 0.0;
+  for (int i = 0; i < half; ++i) {
+    const double a = i * delta;
+    const bool last = (i == half - 1);
+    const double b = (i + 1) * delta;
+    const double y = (i + 0.5) * delta;
+    const double phia = inv_sqrt2pi * std::exp(-0.5 * a * a);
+    const double phib = last ? 0.0 : inv_sqrt2pi * std::exp(-0.5 * b * b);
+    const double qa = 0.5 * std::erfc(a / std::sqrt(2.0));
+    const double qb = last ? 0.0 : 0.5 * std::erfc(b / std::sqrt(2.0));
+    const double pr = qa - qb;                              // P(a <= x < b)
+    const double m1 = phia - phib;                          // int x phi
+    const double m2 = pr + a * phia - (last ? 0.0 : b * phib);  // int x^2 phi
+    acc += m2 - 2.0 * y * m1 + y * y * pr;
+  }
+  return 2.0 * acc;
+}
+
+// Distortion of a unit Gaussian channel at b bits (1 when dropped).
+static double eps_bits(int b) {
+  static double tab[STC_MAX_BITS + 1] = {-1.0};
+  if (tab[0] < 0.0) {
+    tab[0] = 1.0;
+    for (int k = 1; k <= STC_MAX_BITS; ++k) tab[k] = gauss_uniform_mse(delta_star_impl(k), 1 << k);
+  }
+  return tab[b];
+}
+
+stc_status stc_allocate_bits(int32_t d, const double* lambda, int32_t total_bits, int32_t variant, double param,
+                             uint8_t* bits_out) {
+  if (d <= 0 || !lambda || !bits_out) return fail(STC_EINVAL, "allocate_bits: bad arguments");
+  if (total_bits < 0 || total_bits > STC_MAX_BITS * d)
+    return fail(STC_EBUDGET, "allocate_bits: budget %d outside [0, %d]", total_bits, STC_MAX_BITS * d);
+  std::vector<double> lam(d);
+  for (int j = 0; j < d; ++j) lam[j] = lambda[j] > 0.0 ? lambda[j] : 0.0;
+  std::vector<int> b(d, 0);
+  // one bit at a time to the channel of largest gain (lowest index on ties)
+  auto greedy = [&](int first, int last, int nbits, auto gain) {
+    for (int it = 0; it < nbits; ++it) {
+      int best = -1;
+      double bestv = -1.0;
+      for (int j = first; j < last; ++j) {
+        if (b[j] >= STC_MAX_BITS) continue;
+        const double g = gain(j);
+        if (g > bestv) { bestv = g; best = j; }
+      }
+      if (best < 0) break;
+      b[best] += 1;
+    }
+  };
+  auto rd_gain = [&](int j) { return std::ldexp(lam[j], -2 * b[j]); };
+  switch (variant) {
+    case STC_ALLOC_GREEDY:
+      greedy(0, d, total_bits, rd_gain);
+      break;
+    case STC_ALLOC_OPERATIONAL:
+      greedy(0, d, total_bits, [&](int j) { return lam[j] * (eps_bits(b[j]) - eps_bits(b[j] + 1)); });
+      break;
+    case STC_ALLOC_GROUPED: {
+      const int G = (int)param;
+      if (param != (double)G || G < 1 || d % G) return fail(STC_EINVAL, "allocate_bits: group size %g", param);
+      const int ng = d / G;
+      std::vector<double> lg(ng, 0.0);
+      std::vector<int> bg(ng, 0);
+      for (int j = 0; j < d; ++j) lg[j / G] += lam[j];
+      for (int left = total_bits; left >= G; left -= G) {
+        int best = -1;
+        double bestv = -1.0;
+        for (int k = 0; k < ng; ++k) {
+          if (bg[k] >= STC_MAX_BITS) continue;
+          const double g = std::ldexp(lg[k], -2 * bg[k]);
+          if (g > bestv) { bestv = g; best = k; }
+        }
+        if (best < 0) break;
+        bg[best] += 1;
+      }
+      for (int j = 0; j < d; ++j) b[j] = bg[j / G];
+      break;
+    }
+    case STC_ALLOC_FLOOR: {
+      const int f = (int)param;
+      if (param != (double)f || f < 0 || f > STC_MAX_BITS || f * d > total_bits)
+        return fail(STC_EINVAL, "allocate_bits: floor %g with budget %d", param, total_bits);
+      for (int j = 0; j < d; ++j) b[j] = f;
+      greedy(0, d, total_bits - f * d, rd_gain);
+      break;
+    }
+    case STC_ALLOC_GAP: {
+      if (!(param > 1.0)) return fail(STC_EINVAL, "allocate_bits: gap ratio %g must exceed 1", param);
+      int d_eff = d;
+      for (int j = 0; j + 1 < d; ++j)
+        if (lam[j] > 0.0 && (lam[j + 1] <= 0.0 || lam[j] >= param * lam[j + 1])) { d_eff = j + 1; break; }
+      greedy(0, d_eff, std::min(total_bits, STC_MAX_BITS * d_eff), rd_gain);
+      break;
+    }
+    default:
+      return fail(STC_EINVAL, "allocate_bits: unknown variant %d", variant);
+  }
+  for (int j = 0; j < d; ++j) bits_out[j] = (uint8_t)b[j];
+  return ok();
+}
+
 stc_status stc_eigh(int32_t d, const double* a, double* u_out, double* lambda_out) {
   if (d <= 0 || !a || !u_out || !lambda_out) return fail(STC_EINVAL, "eigh: bad arguments");
   std::vector<double> m(a, a + (size_t)d * d), v;

@@ -163,3 +163,23 @@ def test_invalid_arguments_rejected_before_device_work():
                                    fake, fake, 0.1, fake, 1 << 20, None) == _abi.STC_EUNSUPPORTED
     assert L.stc_last_error()
     assert L.stc_status_str(_abi.STC_EBUDGET) == b"bit budget"
+
+
+def test_allocation_variants_match_oracle():
+    """The library's allocation variants equal the oracle's on random and
+    structured spectra (written independently on each side)."""
+    rng = np.random.default_rng(70)
+    spectra = [np.arange(1, 129, dtype=np.float64) ** -a for a in (0.8, 1.2, 2.0)]
+    spectra.append(np.sort(rng.exponential(1.0, 128))[::-1])
+    spectra.append(np.concatenate([np.linspace(3.0, 1.0, 20), np.full(108, 2e-4)]))
+    z = np.sort(rng.exponential(1.0, 128))[::-1]
+    z[100:] = 0.0
+    spectra.append(z)
+    cases = [("greedy", 0), ("operational", 0), ("grouped", 4), ("grouped", 8), ("floor", 1), ("gap", 50.0)]
+    for lam in spectra:
+        for B in (170, 256, 512):
+            for variant, param in cases:
+                want = codec.allocate_bits(lam, B, variant, param)
+                got = stc.allocate_bits(lam, B, variant, param)
+                assert np.array_equal(got, want), (variant, param, B)
+

@@ -591,3 +591,66 @@ def test_self_checks_on_cfg2_head():
         st = codec.calibrate_head(x, w.n_calib, avg)
         assert int(st["bits"].astype(int).sum()) == codec.total_bits_for(avg, 128)
         assert np.all(np.diff(st["bits"].astype(int)) <= 0)
+
+
+# ------------------------------------------------ allocation variants (next row)
+def _compositions(total, parts, cap):
+    if parts == 1:
+        if total <= cap:
+            yield (total,)
+        return
+    for first in range(min(total, cap) + 1):
+        for rest in _compositions(total - first, parts - 1, cap):
+            yield (first,) + rest
+
+
+def test_quantizer_mse_decreasing_convex_and_closed_form():
+    """eps(1) = 1 - 2/pi (levels +-sqrt(2/pi)); eps decreasing and convex in b,
+    which is what makes the marginal greedy optimal."""
+    eps = [codec.quantizer_mse(b) for b in range(9)]
+    assert abs(eps[1] - (1 - 2 / math.pi)) < 1e-12
+    assert all(eps[b + 1] < eps[b] for b in range(8))
+    assert all(eps[b] - eps[b + 1] > eps[b + 1] - eps[b + 2] for b in range(7))
+
+
+def test_operational_allocation_is_optimal_by_brute_force():
+    rng = np.random.default_rng(60)
+    for trial in range(4):
+        lam = np.sort(rng.exponential(1.0, 5))[::-1] * (1 + trial)
+        for B in (3, 7, 12):
+            got = codec.allocate_bits(lam, B, "operational")
+            assert got.sum() == B
+            cost = lambda b: sum(lam[j] * codec.quantizer_mse(int(b[j])) for j in range(5))
+            best = min(cost(c) for c in _compositions(B, 5, 8))
+            assert cost(got) <= best * (1 + 1e-12)
+
+
+def test_grouped_allocation_is_optimal_by_brute_force():
+    rng = np.random.default_rng(61)
+    lam = np.sort(rng.exponential(1.0, 8))[::-1]
+    G = 2
+    lam_g = lam.reshape(4, 2).sum(axis=1)
+    for B in (4, 9, 12, 17):
+        got = codec.allocate_bits(lam, B, "grouped", G)
+        assert got.sum() == G * (B // G)
+        assert np.all(got.reshape(4, 2)[:, 0] == got.reshape(4, 2)[:, 1])     # one width per group
+        cost = lambda bg: sum(lam_g[k] * 4.0 ** -int(bg[k]) for k in range(4))
+        best = min(cost(c) for c in _compositions(B // G, 4, 8))
+        assert cost(got.reshape(4, 2)[:, 0]) <= best * (1 + 1e-12)
+
+
+def test_floor_and_gap_allocations():
+    lam = np.arange(1, 129, dtype=np.float64) ** -1.2
+    f = codec.allocate_bits(lam, 300, "floor", 1)
+    assert f.sum() == 300 and f.min() >= 1
+    # the floor shifts the problem: the rest is the default greedy with 7-bit caps
+    assert np.array_equal(f - 1, codec.water_fill(lam, 300 - 128, 7))
+    # a planted spectral gap after channel 10 (ratio 1e4): nothing past it
+    lam2 = np.concatenate([np.linspace(2.0, 1.0, 10), np.full(118, 1e-4)])
+    g = codec.allocate_bits(lam2, 64, "gap", 100.0)
+    assert g[10:].sum() == 0 and g.sum() == 64
+    assert np.array_equal(g[:10], codec.water_fill(lam2[:10], 64))
+    # budget beyond the kept channels' capacity is not spent
+    assert codec.allocate_bits(lam2, 200, "gap", 100.0).sum() == 80
+    # no gap above the ratio: the default
+    assert np.array_equal(codec.allocate_bits(lam, 256, "gap", 100.0), codec.water_fill(lam, 256))
