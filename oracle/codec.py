@@ -486,14 +486,19 @@ def attend_compressed(k_state: Dict, v_state: Dict, k_packed: np.ndarray,
 
 
 def softmax_attention(q: np.ndarray, khat: np.ndarray, vhat: np.ndarray,
-                      scale: Optional[float] = None) -> np.ndarray:
+                      scale: Optional[float] = None, extra: Optional[np.ndarray] = None) -> np.ndarray:
     """Standard attention of g query heads over n reconstructed keys and
-    values, fp64: s = q K^T * scale, softmax over the n tokens, o = p V.
-    READING: scale 1/sqrt(d), no mask, no positional rotation. fp32 [g][d]."""
+    values, fp64: s = (q K^T + extra) * scale, softmax over the n tokens,
+    o = p V; `extra` [g][n] is an optional additive estimate of the part of
+    q . k the reconstruction misses. READING: scale 1/sqrt(d), no mask, no
+    positional rotation. fp32 [g][d]."""
     q = np.asarray(q, dtype=np.float64)
     d = khat.shape[1]
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    s = (q @ khat.T) * scale                       # [g][n]
+    s = q @ khat.T
+    if extra is not None:
+        s = s + extra
+    s = s * scale                                  # [g][n]
     s = s - s.max(axis=1, keepdims=True)
     p = np.exp(s)
     p = p / p.sum(axis=1, keepdims=True)

@@ -18,7 +18,8 @@ Value distributions follow the pages' description of the cache statistics:
 
 Seeds: ``np.random.default_rng([cfg, layer, batch, head, kind, purpose])`` with
 kind K=0 / V=1 and purpose 0 rotation, 1 samples, 2 outlier channels,
-3 queries, 4 random signs, 5 codebook training samples, 6 per-layer decay.
+3 queries, 4 random signs, 5 codebook training samples, 6 per-layer decay,
+7 the Gaussian matrix of the 1-bit residual sketch.
 """
 from __future__ import annotations
 
@@ -37,7 +38,7 @@ __all__ = [
 
 D = 128
 KIND_K, KIND_V = 0, 1
-P_ROT, P_SAMPLES, P_OUTLIER, P_QUERY, P_SIGNS, P_LLOYD, P_ALPHA = range(7)
+P_ROT, P_SAMPLES, P_OUTLIER, P_QUERY, P_SIGNS, P_LLOYD, P_ALPHA, P_SKETCH = range(8)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -166,6 +167,13 @@ def random_signs(cfg: int, layer: int, batch: int, head: int, kind: int) -> np.n
     """Seeded +-1 diagonal of the randomized Walsh-Hadamard transform, int8."""
     rng = rng_for(cfg, layer, batch, head, kind, P_SIGNS)
     return (rng.integers(0, 2, size=D) * 2 - 1).astype(np.int8)
+
+
+def sketch_matrix(cfg: int, layer: int, batch: int, head: int, kind: int, m: int = D) -> np.ndarray:
+    """Seeded Gaussian matrix S [m][128] (iid N(0, 1), fp32) of the 1-bit
+    Johnson-Lindenstrauss residual sketch of one stream."""
+    rng = rng_for(cfg, layer, batch, head, kind, P_SKETCH)
+    return rng.standard_normal((m, D)).astype(np.float32)
 
 
 def sphere_coordinate_samples(n: int = 1_000_000, d: int = D, seed_cfg: int = 3) -> np.ndarray:

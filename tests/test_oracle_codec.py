@@ -637,6 +637,9 @@ def test_grouped_allocation_is_optimal_by_brute_force():
         cost = lambda bg: sum(lam_g[k] * 4.0 ** -int(bg[k]) for k in range(4))
         best = min(cost(c) for c in _compositions(B // G, 4, 8))
         assert cost(got.reshape(4, 2)[:, 0]) <= best * (1 + 1e-12)
+    # a group's variance is the sum over its channels, not its largest one
+    got = codec.allocate_bits(np.array([1.0, 0.0, 0.6, 0.6]), 2, "grouped", 2)
+    assert np.array_equal(got, [0, 0, 1, 1])
 
 
 def test_floor_and_gap_allocations():

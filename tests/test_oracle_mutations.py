@@ -159,3 +159,63 @@ def test_rht_mutant_is_caught(monkeypatch, name, mutant, check):
     assert not _fails(check)
     monkeypatch.setattr(rht, name, mutant)
     assert _fails(check)
+
+
+# ------------------------------------------------------------ later rows
+import test_oracle_qjl as tq  # noqa: E402
+from oracle import qjl  # noqa: E402
+
+
+def _append_one_bit_late(packed_old, n_old, codes_new, bits):
+    full = _orig_append(packed_old, n_old, codes_new, bits)
+    out = np.zeros_like(full)
+    allbits = np.unpackbits(full, bitorder="little")
+    shifted = np.concatenate([[0], allbits[:-1]])
+    keep = n_old * int(np.asarray(bits, np.int64).sum())
+    shifted[:keep] = allbits[:keep]
+    return np.packbits(shifted, bitorder="little")[: out.shape[0]]
+
+
+_orig_append = codec.append_pack
+_orig_alloc = codec.allocate_bits
+
+
+def _alloc_operational_as_rd(lam, total_bits, variant="greedy", param=0.0, max_bits=8):
+    if variant == "operational":
+        return codec.water_fill(lam, total_bits, max_bits)
+    return _orig_alloc(lam, total_bits, variant, param, max_bits)
+
+
+def _alloc_grouped_by_max(lam, total_bits, variant="greedy", param=0.0, max_bits=8):
+    if variant == "grouped":
+        G = int(param)
+        lam_g = np.repeat(np.asarray(lam, np.float64).reshape(-1, G).max(axis=1), G)
+        return _orig_alloc(lam_g, total_bits, variant, param, max_bits)
+    return _orig_alloc(lam, total_bits, variant, param, max_bits)
+
+
+_orig_corr = qjl.score_correction
+
+
+def _corr_no_sqrt_pi_2(q, sketch, rnorm, S, n):
+    return _orig_corr(q, sketch, rnorm, S, n) / math.sqrt(math.pi / 2.0)
+
+
+def _check_append():
+    tc.test_append_pack_equals_pack_of_all()
+
+
+def _check_qjl_unbiased():
+    tq.test_sketch_estimate_is_unbiased_on_real_codes()
+
+
+@pytest.mark.parametrize("module,name,mutant,check", [
+    (codec, "append_pack", _append_one_bit_late, _check_append),
+    (codec, "allocate_bits", _alloc_operational_as_rd, tc.test_operational_allocation_is_optimal_by_brute_force),
+    (codec, "allocate_bits", _alloc_grouped_by_max, tc.test_grouped_allocation_is_optimal_by_brute_force),
+    (qjl, "score_correction", _corr_no_sqrt_pi_2, _check_qjl_unbiased),
+], ids=["append_one_bit_late", "operational_as_rd", "grouped_by_max", "qjl_no_sqrt_pi_2"])
+def test_later_row_mutant_is_caught(monkeypatch, module, name, mutant, check):
+    assert not _fails(check)
+    monkeypatch.setattr(module, name, mutant)
+    assert _fails(check)

@@ -1,0 +1,99 @@
+"""Pins of the 1-bit Johnson-Lindenstrauss residual sketch oracle: the
+estimator is unbiased with the closed-form variance of a Gaussian sketch,
+its zero-mean score noise is amplified by exp as Jensen's inequality says
+(E[exp(e)] = exp(var/2) for Gaussian e), a zero residual gives no
+correction, and on real codes the corrected scores average to the true ones."""
+import math
+
+import numpy as np
+
+import synth
+from oracle import codec, qjl, rht
+
+D = 128
+
+
+def _estimates(q, r, trials, m=qjl.SKETCH_BITS, seed=80):
+    rng = np.random.default_rng(seed)
+    est = np.empty(trials)
+    rn = float(np.sqrt(r @ r))
+    for t in range(trials):
+        S = rng.standard_normal((m, D))
+        z = np.where(S @ r >= 0, 1.0, -1.0)
+        est[t] = math.sqrt(math.pi / 2) / m * rn * float((S @ q) @ z)
+    return est
+
+
+def test_estimator_unbiased_with_closed_form_variance():
+    rng = np.random.default_rng(81)
+    q = rng.standard_normal(D)
+    r = 0.3 * rng.standard_normal(D)
+    est = _estimates(q, r, 4000)
+    rn = math.sqrt(r @ r)
+    var = rn * rn / qjl.SKETCH_BITS * (math.pi / 2 * (q @ q) - (q @ r / rn) ** 2)
+    se = math.sqrt(var / est.size)
+    assert abs(est.mean() - q @ r) < 4 * se
+    assert abs(est.var() / var - 1) < 0.1
+
+
+def test_jensen_amplification_of_score_noise():
+    """The estimator's error e is zero-mean and near-Gaussian, so the softmax
+    weight exp(s + e) is inflated on average by exp(var(e)/2)."""
+    rng = np.random.default_rng(82)
+    q = 0.5 * rng.standard_normal(D)
+    r = 0.2 * rng.standard_normal(D)
+    e = _estimates(q, r, 6000, seed=83) - q @ r
+    assert abs(e.mean()) < 4 * e.std() / math.sqrt(e.size)
+    ratio = np.exp(e).mean() / math.exp(e.var() / 2)
+    assert abs(ratio - 1) < 0.03
+    assert np.exp(e).mean() > 1.0
+
+
+def _rht_case(n=64, seed=84):
+    rng = np.random.default_rng(seed)
+    cb = rht.codebook_fp32(rht.lloyd_max(synth.sphere_coordinate_samples(20000))[0])
+    st = rht.make_state(np.where(rng.random(D) < 0.5, -1, 1), cb)
+    x = rng.standard_t(3, (n, D))
+    kp, kn = rht.encode_kv(st, x)
+    S = rng.standard_normal((qjl.SKETCH_BITS, D)).astype(np.float32)
+    return st, x, kp, kn, S
+
+
+def test_zero_residual_gives_no_correction():
+    st, x, kp, kn, S = _rht_case(n=5)
+    exact = rht.reconstruct_exact(st, kp, kn, 5)         # keys equal to their reconstruction
+    sk, rn = qjl.sketch_encode(st, exact, kp, kn, S)
+    assert np.all(rn == 0)
+    assert np.all(qjl.score_correction(np.ones((2, D)), sk, rn, S, 5) == 0)
+
+
+def test_sketch_estimate_is_unbiased_on_real_codes():
+    """On real codes the corrected score is an unbiased estimate of q . k:
+    averaged over independent sketch matrices it converges to the true score,
+    while any single sketch adds variance (at m = d about pi/2 times the
+    uncorrected error, which is the noise the pages' Jensen analysis is about)."""
+    st, x, kp, kn, _ = _rht_case()
+    n = x.shape[0]
+    q = np.random.default_rng(85).standard_normal((8, D))
+    true = q @ x.T
+    base = q @ rht.reconstruct_exact(st, kp, kn, n).T
+    rng = np.random.default_rng(86)
+    acc = np.zeros_like(base)
+    T = 400
+    for _ in range(T):
+        S = rng.standard_normal((qjl.SKETCH_BITS, D)).astype(np.float32)
+        sk, rn = qjl.sketch_encode(st, x, kp, kn, S)
+        acc += base + qjl.score_correction(q, sk, rn, S, n)
+    err_base = np.mean((base - true) ** 2)
+    assert np.mean((acc / T - true) ** 2) < 0.015 * err_base
+
+
+def test_sketch_bits_layout():
+    """One bit per sketch row, F1 layout with 1-bit channels: bit t*m + i is
+    row i of token t's sign (1 = non-negative)."""
+    st, x, kp, kn, S = _rht_case(n=3)
+    sk, _ = qjl.sketch_encode(st, x, kp, kn, S)
+    r = x - rht.reconstruct_exact(st, kp, kn, 3)
+    bits = np.unpackbits(sk, bitorder="little")[: 3 * qjl.SKETCH_BITS].reshape(3, -1)
+    assert np.array_equal(bits, (r @ S.astype(np.float64).T >= 0).astype(np.uint8))
+    assert sk.shape[0] == codec.packed_bytes(qjl.SKETCH_BITS, 3)
