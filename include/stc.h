@@ -89,6 +89,7 @@ enum { STC_XFORM_EIGEN = 0, STC_XFORM_IDENTITY = 1, STC_XFORM_RHT = 2 }; /* tran
 #define STC_D 128
 #define STC_MAX_BITS 8
 #define STC_RHT_BITS 3
+#define STC_SKETCH_BITS 128  /* bits of the key residual sketch per token (Walsh-Hadamard path) */
 
 /* Host-side summary of a state, written by the calls that build one. */
 typedef struct {
@@ -99,6 +100,7 @@ typedef struct {
   uint8_t bits[STC_D];  /* width of each latent channel (0..8) */
   double lambda[STC_D]; /* second-moment eigenvalues (EIGEN), diagonal (IDENTITY) */
   double steps[STC_D];  /* quantizer step of each kept channel (0 if dropped) */
+  int32_t sketch_bits;  /* RHT states: bits of the key residual sketch per token (0: none) */
 } stc_head_info;
 
 /* ------------------------------------------------------------ sizes */
@@ -180,6 +182,18 @@ stc_status stc_state_init(int32_t d, int32_t xform, const double* u, const doubl
 stc_status stc_rht_state_init(int32_t d, const int8_t* signs, const float* codebook,
                               stc_head_info* info, void* state_dev, stc_stream_t stream);
 
+/* A Walsh-Hadamard state whose keys also carry a 1-bit Johnson-Lindenstrauss
+ * sketch of their residual (TQ-QKV; ablation summary, "Experimentele
+ * Opstelling" and "Belangrijkste Bijdragen" 1): sketch[i*d + j] = S_ij, the
+ * STC_SKETCH_BITS x d Gaussian matrix of the stream (host fp32, finite). The
+ * encode then also writes z = sign(S r) of r = x - K_hat (STC_SKETCH_BITS
+ * bits per token, one per row, 1 = non-negative) and |r| (fp32), and the
+ * attention adds sqrt(pi/2)/m |r_t| (S q).z_t to each score. Synchronizes
+ * `stream`. */
+stc_status stc_rht_sketch_state_init(int32_t d, const int8_t* signs, const float* codebook,
+                                     const float* sketch, stc_head_info* info, void* state_dev,
+                                     stc_stream_t stream);
+
 /* Calibrate one stream: second moment of the first n_calib tokens of x_dev
  * ([n][ld] of dtype, row t at x_dev + t*ld elements) computed on the GPU in
  * fp64, eigendecomposition on the host (EIGEN) or its diagonal (IDENTITY),
@@ -235,6 +249,21 @@ stc_status stc_append_kv_batched(const void* states_dev, int64_t n_states,
                                  void* packed_dev, int64_t packed_stream_stride,
                                  float* norms_dev, int64_t norms_stream_stride, stc_stream_t stream);
 
+/* stc_append_kv_batched (n_old = 0: a plain encode) for Walsh-Hadamard
+ * states built by stc_rht_sketch_state_init, bf16 tokens, also writing each
+ * token's key residual sketch (STC_SKETCH_BITS / 8 bytes at sketch_dev +
+ * s*sketch_stream_stride + t*16, row i at bit i, 1 = non-negative,
+ * sign(0) = +1) and |r| (fp32 at rnorm_dev + s*rnorm_stream_stride + t).
+ * STC_EINVAL if a state has no sketch matrix. */
+stc_status stc_append_rht_sketch_batched(const void* states_dev, int64_t n_states,
+                                        const int32_t* state_of_stream_dev, const stc_head_info* infos,
+                                        int64_t n_streams, int64_t n_old, int64_t m, const void* x_dev,
+                                        int64_t ld, int64_t x_stream_stride, void* packed_dev,
+                                        int64_t packed_stream_stride, float* norms_dev,
+                                        int64_t norms_stream_stride, void* sketch_dev,
+                                        int64_t sketch_stream_stride, float* rnorm_dev,
+                                        int64_t rnorm_stream_stride, stc_stream_t stream);
+
 /* One stream. */
 stc_status stc_encode_kv(const stc_head_info* info, const void* state_dev, int64_t n_tokens,
                          const void* x_dev, int32_t dtype, int64_t ld, void* packed_dev,
@@ -285,7 +314,13 @@ stc_status stc_attend_compressed(const stc_head_info* k_info, const void* k_stat
  * per-token norms written by the RHT encode are k_norms_dev +
  * p*norms_pair_stride (and v_norms_dev likewise), fp32. Scores are taken
  * against H D q (never reconstructing K_hat), the softmax-weighted values are
- * accumulated in the rotated basis and rotated back once. RHT states only
+ * accumulated in the rotated basis and rotated back once. With k_sketch_dev
+ * (keys encoded by stc_append_rht_sketch_batched; their states built by
+ * stc_rht_sketch_state_init) each score gains the residual estimate
+ * sqrt(pi/2)/STC_SKETCH_BITS |r_t| (S q).z_t, the sketch of pair p at
+ * k_sketch_dev + p*sketch_pair_stride (16 bytes per token) and |r| at
+ * k_rnorm_dev + p*rnorm_pair_stride; NULL: no correction (a K state built
+ * without the sketch matrix contributes none either). RHT states only
  * (STC_EUNSUPPORTED otherwise); ws_dev as for stc_attend_compressed_batched. */
 stc_status stc_attend_rht_batched(const void* states_dev, int64_t n_states,
                                   const int32_t* k_state_of_pair_dev,
@@ -293,7 +328,9 @@ stc_status stc_attend_rht_batched(const void* states_dev, int64_t n_states,
                                   int64_t n_pairs, int64_t n_tokens, const void* k_packed_dev,
                                   const float* k_norms_dev, const void* v_packed_dev,
                                   const float* v_norms_dev, int64_t packed_pair_stride,
-                                  int64_t norms_pair_stride, int32_t group, const float* q_dev,
+                                  int64_t norms_pair_stride, const void* k_sketch_dev,
+                                  const float* k_rnorm_dev, int64_t sketch_pair_stride,
+                                  int64_t rnorm_pair_stride, int32_t group, const float* q_dev,
                                   float* out_dev, float scale, void* ws_dev, size_t ws_bytes,
                                   stc_stream_t stream);
 

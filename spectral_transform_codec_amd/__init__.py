@@ -173,6 +173,20 @@ def rht_state_init(signs: np.ndarray, codebook: np.ndarray, device="cuda") -> St
     return State(blob, info)
 
 
+def rht_sketch_state_init(signs: np.ndarray, codebook: np.ndarray, sketch: np.ndarray, device="cuda") -> State:
+    """Walsh-Hadamard state whose keys carry the residual sketch; sketch = S [128][128] fp32."""
+    info = HeadInfo()
+    blob = _new_blob(device)
+    sg = np.ascontiguousarray(signs, np.int8)
+    cb = np.ascontiguousarray(codebook, np.float32)
+    sk = np.ascontiguousarray(sketch, np.float32)
+    assert sk.shape == (128, D)
+    check("stc_rht_sketch_state_init", lib().stc_rht_sketch_state_init(
+        D, _np_ptr(sg, ctypes.c_int8), _np_ptr(cb, ctypes.c_float), _np_ptr(sk, ctypes.c_float), ctypes.byref(info),
+        _ptr(blob), _stream()))
+    return State(blob, info)
+
+
 def calibrate_head(x: torch.Tensor, n_calib: int, avg_bits: float, bits: Optional[np.ndarray] = None,
                    xform: int = XFORM_EIGEN) -> State:
     """x: [n][128] (row stride may exceed 128) bf16/fp32 on the GPU."""
@@ -276,9 +290,12 @@ def append_kv_batched(states: StateArray, x: torch.Tensor, n_old: int, packed: t
 def attend_rht_batched(states: StateArray, k_state_of_pair: torch.Tensor, v_state_of_pair: torch.Tensor,
                        k_packed: torch.Tensor, k_norms: torch.Tensor, v_packed: torch.Tensor,
                        v_norms: torch.Tensor, n: int, q: torch.Tensor, scale: Optional[float] = None,
-                       ws: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None):
+                       ws: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                       k_sketch: Optional[torch.Tensor] = None, k_rnorm: Optional[torch.Tensor] = None):
     """Attention over Walsh-Hadamard caches: k_packed, v_packed [P][stride] uint8 (same
-    stride), k_norms, v_norms fp32 [P][>= n] (same stride); q fp32 [P][g][128]."""
+    stride), k_norms, v_norms fp32 [P][>= n] (same stride); q fp32 [P][g][128]. With
+    k_sketch uint8 [P][>= 16 n] and k_rnorm fp32 [P][>= n] the key residual sketch corrects
+    the scores."""
     Pn, g = q.shape[0], q.shape[1]
     assert k_packed.stride(0) == v_packed.stride(0) and k_norms.stride(0) == v_norms.stride(0)
     assert k_norms.dtype == torch.float32 and k_norms.stride(1) == 1 and v_norms.stride(1) == 1
@@ -291,7 +308,9 @@ def attend_rht_batched(states: StateArray, k_state_of_pair: torch.Tensor, v_stat
     check("stc_attend_rht_batched", lib().stc_attend_rht_batched(
         _ptr(states.blob), states.n, _ptr(_map_arg(k_state_of_pair)), _ptr(_map_arg(v_state_of_pair)),
         states.infos, Pn, n, _ptr(k_packed), _ptr(k_norms), _ptr(v_packed), _ptr(v_norms), k_packed.stride(0),
-        k_norms.stride(0), g, _ptr(q), _ptr(out), float(scale), _ptr(ws), ws.numel(), _stream()))
+        k_norms.stride(0), _ptr(k_sketch), _ptr(k_rnorm), 0 if k_sketch is None else k_sketch.stride(0),
+        0 if k_rnorm is None else k_rnorm.stride(0), g, _ptr(q), _ptr(out), float(scale), _ptr(ws), ws.numel(),
+        _stream()))
     return out
 
 
@@ -317,6 +336,23 @@ def decode_step_batched(states: StateArray, k_state_of_pair: torch.Tensor, v_sta
         states.infos, Pn, n_old, _ptr(k_new), _ptr(v_new), _dtype_code(k_new), _ptr(k_packed), _ptr(v_packed),
         k_packed.stride(0), g, _ptr(q), _ptr(out), float(scale), _ptr(ws), ws.numel(), _stream()))
     return out
+
+
+def append_rht_sketch_batched(states: StateArray, x: torch.Tensor, n_old: int, packed: torch.Tensor,
+                              norms: torch.Tensor, sketch: torch.Tensor, rnorm: torch.Tensor,
+                              state_of_stream: Optional[torch.Tensor] = None):
+    """Walsh-Hadamard encode/append with the key residual sketch: x [S][m][128] bf16 are tokens
+    n_old .. n_old+m-1; packed [S][>= 48 (n_old+m)], norms and rnorm fp32 [S][>= n_old+m],
+    sketch uint8 [S][>= 16 (n_old+m)]."""
+    assert x.dim() == 3 and x.shape[2] == D and x.stride(2) == 1 and x.dtype == torch.bfloat16
+    S, m = x.shape[0], x.shape[1]
+    for t in (norms, rnorm):
+        assert t.dtype == torch.float32 and t.stride(1) == 1
+    check("stc_append_rht_sketch_batched", lib().stc_append_rht_sketch_batched(
+        _ptr(states.blob), states.n, _ptr(_map_arg(state_of_stream)), states.infos, S, n_old, m, _ptr(x),
+        x.stride(1), x.stride(0), _ptr(packed), packed.stride(0), _ptr(norms), norms.stride(0), _ptr(sketch),
+        sketch.stride(0), _ptr(rnorm), rnorm.stride(0), _stream()))
+    return packed
 
 
 def decode_kv_batched(states: StateArray, packed: torch.Tensor, n: int, norms: Optional[torch.Tensor] = None,

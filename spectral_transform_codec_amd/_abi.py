@@ -17,7 +17,7 @@ c_size, c_vp, c_cp = ctypes.c_size_t, ctypes.c_void_p, ctypes.c_char_p
 
 class HeadInfo(ctypes.Structure):
     _fields_ = [("d", c_i32), ("xform", c_i32), ("total_bits", c_i32), ("n_kept", c_i32),
-                ("bits", c_u8 * D), ("lam", c_f64 * D), ("steps", c_f64 * D)]
+                ("bits", c_u8 * D), ("lam", c_f64 * D), ("steps", c_f64 * D), ("sketch_bits", c_i32)]
 
 
 P = ctypes.POINTER
@@ -43,6 +43,9 @@ SIGNATURES = {
                                       c_i32, c_i64, c_i64, c_vp]),
     "stc_append_kv_batched": (c_i32, [c_vp, c_i64, c_vp, P(HeadInfo), c_i64, c_i64, c_i64, c_vp, c_i32, c_i64,
                                       c_i64, c_vp, c_i64, c_vp, c_i64, c_vp]),
+    "stc_append_rht_sketch_batched": (c_i32, [c_vp, c_i64, c_vp, P(HeadInfo), c_i64, c_i64, c_i64, c_vp, c_i64,
+                                              c_i64, c_vp, c_i64, c_vp, c_i64, c_vp, c_i64, c_vp, c_i64, c_vp]),
+    "stc_rht_sketch_state_init": (c_i32, [c_i32, P(ctypes.c_int8), P(c_f32), P(c_f32), P(HeadInfo), c_vp, c_vp]),
     "stc_encode_kv": (c_i32, [P(HeadInfo), c_vp, c_i64, c_vp, c_i32, c_i64, c_vp, c_vp, c_vp]),
     "stc_decode_kv": (c_i32, [P(HeadInfo), c_vp, c_i64, c_vp, c_vp, c_vp, c_i32, c_i64, c_vp]),
     "stc_quantize_pack_f32": (c_i32, [P(HeadInfo), c_vp, c_i64, c_vp, c_vp, c_vp]),
@@ -51,7 +54,8 @@ SIGNATURES = {
     "stc_attend_compressed": (c_i32, [P(HeadInfo), c_vp, P(HeadInfo), c_vp, c_i64, c_vp, c_vp, c_i32, c_vp,
                                       c_vp, c_f32, c_vp, c_size, c_vp]),
     "stc_attend_rht_batched": (c_i32, [c_vp, c_i64, c_vp, c_vp, P(HeadInfo), c_i64, c_i64, c_vp, c_vp, c_vp, c_vp,
-                                       c_i64, c_i64, c_i32, c_vp, c_vp, c_f32, c_vp, c_size, c_vp]),
+                                       c_i64, c_i64, c_vp, c_vp, c_i64, c_i64, c_i32, c_vp, c_vp, c_f32, c_vp,
+                                       c_size, c_vp]),
     "stc_decode_step_batched": (c_i32, [c_vp, c_i64, c_vp, c_vp, P(HeadInfo), c_i64, c_i64, c_vp, c_vp, c_i32,
                                         c_vp, c_vp, c_i64, c_i32, c_vp, c_vp, c_f32, c_vp, c_size, c_vp]),
     "stc_status_str": (c_cp, [c_i32]),

@@ -306,6 +306,7 @@ stc_status build_eigen_blob(int d, int xform, const double* u, const double* lam
     info->xform = xform;
     info->total_bits = total;
     info->n_kept = n_kept;
+    info->sketch_bits = 0;
     for (int j = 0; j < d; ++j) {
       info->bits[j] = bits[j];
       info->lambda[j] = lambda ? lambda[j] : 0.0;
@@ -575,8 +576,8 @@ stc_status stc_state_init(int32_t d, int32_t xform, const double* u, const doubl
   return ok();
 }
 
-stc_status stc_rht_state_init(int32_t d, const int8_t* signs, const float* codebook, stc_head_info* info,
-                              void* state_dev, stc_stream_t stream) {
+static stc_status rht_state_build(int32_t d, const int8_t* signs, const float* codebook, const float* sketch,
+                                  stc_head_info* info, void* state_dev, stc_stream_t stream) {
   if (d != D) return fail(STC_EUNSUPPORTED, "rht_state_init: d=%d (only %d is supported)", d, D);
   if (!signs || !codebook || !info) return fail(STC_EINVAL, "rht_state_init: NULL argument");
   if (stc_status s = check_state_ptr(state_dev, "state_dev")) return s;
@@ -637,10 +638,34 @@ stc_status stc_rht_state_init(int32_t d, const int8_t* signs, const float* codeb
   }
   for (int k = 0; k < 8; ++k) h->cb[k] = codebook[k];
   for (int k = 0; k < 7; ++k) h->cb_thr[k] = (float)(0.5 * ((double)codebook[k] + (double)codebook[k + 1]));
+  if (sketch) {
+    // key residual sketch: z = sign(S r), r = x - K_hat = |x| D H (y - y_hat) / sqrt(d),
+    // so S r = |x| P e with P = S D H / sqrt(d) and e = y - y_hat in the rotated
+    // basis; P rows permuted like the encode basis, S^T for the attention's S q
+    h->sketch_bits = STC_SKETCH_BITS;
+    uint16_t* p_hi = reinterpret_cast<uint16_t*>(blob.data() + OFF_SKP_HI);
+    uint16_t* p_lo = reinterpret_cast<uint16_t*>(blob.data() + OFF_SKP_LO);
+    float* st32 = reinterpret_cast<float*>(blob.data() + OFF_SKT32);
+    const double rs = 1.0 / std::sqrt((double)D);
+    for (int R = 0; R < STC_SKETCH_BITS; ++R) {
+      const int i = enc_row_channel(R);
+      for (int j = 0; j < D; ++j) {
+        double acc = 0.0;  // (S D H)_ij = sum_k S_ik sign_k H[k][j]
+        for (int k = 0; k < D; ++k) {
+          const int hsign = (__builtin_popcount((unsigned)(k & j)) & 1) ? -1 : 1;
+          acc += (double)sketch[i * D + k] * signs[k] * hsign;
+        }
+        split_bf16(acc * rs, &p_hi[R * D + j], &p_lo[R * D + j]);
+      }
+    }
+    for (int i = 0; i < STC_SKETCH_BITS; ++i)
+      for (int j = 0; j < D; ++j) st32[j * STC_SKETCH_BITS + i] = sketch[i * D + j];
+  }
   info->d = d;
   info->xform = STC_XFORM_RHT;
   info->total_bits = h->total_bits;
   info->n_kept = d;
+  info->sketch_bits = sketch ? STC_SKETCH_BITS : 0;
   for (int j = 0; j < d; ++j) {
     info->bits[j] = STC_RHT_BITS;
     info->lambda[j] = 0.0;
@@ -648,6 +673,19 @@ stc_status stc_rht_state_init(int32_t d, const int8_t* signs, const float* codeb
   }
   if (stc_status s = upload(blob, state_dev, stream)) return s;
   return ok();
+}
+
+stc_status stc_rht_state_init(int32_t d, const int8_t* signs, const float* codebook, stc_head_info* info,
+                              void* state_dev, stc_stream_t stream) {
+  return rht_state_build(d, signs, codebook, nullptr, info, state_dev, stream);
+}
+
+stc_status stc_rht_sketch_state_init(int32_t d, const int8_t* signs, const float* codebook, const float* sketch,
+                                     stc_head_info* info, void* state_dev, stc_stream_t stream) {
+  if (!sketch) return fail(STC_EINVAL, "rht_sketch_state_init: NULL sketch matrix");
+  for (int k = 0; k < STC_SKETCH_BITS * D; ++k)
+    if (!std::isfinite(sketch[k])) return fail(STC_EINVAL, "rht_sketch_state_init: sketch entry %d not finite", k);
+  return rht_state_build(d, signs, codebook, sketch, info, state_dev, stream);
 }
 
 stc_status stc_calibrate_head(int32_t d, int64_t n_calib, const void* x_dev, int32_t dtype, int64_t ld,
@@ -739,7 +777,9 @@ static stc_status encode_impl(const char* who, const void* states_dev, int64_t n
                               const stc_head_info* infos, int64_t n_streams, int64_t n_old, int64_t m,
                               const void* x_dev, int32_t dtype, int64_t ld, int64_t x_stream_stride,
                               void* packed_dev, int64_t packed_stream_stride, float* norms_dev,
-                              int64_t norms_stream_stride, stc_stream_t stream) {
+                              int64_t norms_stream_stride, stc_stream_t stream, void* sketch_dev = nullptr,
+                              int64_t sketch_stream_stride = 0, float* rnorm_dev = nullptr,
+                              int64_t rnorm_stream_stride = 0) {
   bool rht = false;
   int mb = 0;
   if (n_old < 0 || m < 0) return fail(STC_EINVAL, "%s: negative token count", who);
@@ -760,9 +800,21 @@ static stc_status encode_impl(const char* who, const void* states_dev, int64_t n
     return fail(STC_EINVAL, "%s: x stream stride too small", who);
   if (!aligned(packed_dev, 16)) return fail(STC_EINVAL, "%s: packed buffer must be 16-byte aligned", who);
   if (rht && !aligned(norms_dev, 4)) return fail(STC_EINVAL, "%s: norms misaligned", who);
+  if (sketch_dev) {
+    if (!rht) return fail(STC_EUNSUPPORTED, "%s: the residual sketch needs Walsh-Hadamard states", who);
+    for (int64_t i = 0; i < n_states; ++i)
+      if (infos[i].sketch_bits != STC_SKETCH_BITS)
+        return fail(STC_EINVAL, "%s: state %lld has no sketch matrix", who, (long long)i);
+    if (!rnorm_dev || !aligned(sketch_dev, 8) || !aligned(rnorm_dev, 4) || sketch_stream_stride % 8)
+      return fail(STC_EINVAL, "%s: sketch needs 8-byte aligned bytes and a norms buffer", who);
+    if (n_streams > 1 && (sketch_stream_stride < (n_old + m) * (STC_SKETCH_BITS / 8) ||
+                          rnorm_stream_stride < n_old + m))
+      return fail(STC_EINVAL, "%s: sketch or residual norm stride too small", who);
+  }
   EncodeLaunch a{static_cast<const unsigned char*>(states_dev), map, n_states, n_streams, m, ld,
                  x_stream_stride, packed_stream_stride, x_dev, static_cast<unsigned char*>(packed_dev), norms_dev,
-                 dtype == STC_F32 ? 1 : 0, mb, n_old, norms_stream_stride};
+                 dtype == STC_F32 ? 1 : 0, mb, n_old, norms_stream_stride,
+                 static_cast<unsigned char*>(sketch_dev), rnorm_dev, sketch_stream_stride, rnorm_stream_stride};
   const int rc = rht ? launch_encode_rht(a, stream) : launch_encode_eigen(a, stream);
   if (rc) return fail(STC_EDEVICE, "%s launch: %s", who, hipGetErrorString(hipGetLastError()));
   return ok();
@@ -775,6 +827,18 @@ stc_status stc_encode_kv_batched(const void* states_dev, int64_t n_states, const
                                  stc_stream_t stream) {
   return encode_impl("encode_kv", states_dev, n_states, map, infos, n_streams, 0, n_tokens, x_dev, dtype, ld,
                      x_stream_stride, packed_dev, packed_stream_stride, norms_dev, n_tokens, stream);
+}
+
+stc_status stc_append_rht_sketch_batched(const void* states_dev, int64_t n_states, const int32_t* map,
+                                        const stc_head_info* infos, int64_t n_streams, int64_t n_old, int64_t m,
+                                        const void* x_dev, int64_t ld, int64_t x_stream_stride, void* packed_dev,
+                                        int64_t packed_stream_stride, float* norms_dev, int64_t norms_stream_stride,
+                                        void* sketch_dev, int64_t sketch_stream_stride, float* rnorm_dev,
+                                        int64_t rnorm_stream_stride, stc_stream_t stream) {
+  if (!sketch_dev && m > 0) return fail(STC_EINVAL, "append_rht_sketch: NULL sketch buffer");
+  return encode_impl("append_rht_sketch", states_dev, n_states, map, infos, n_streams, n_old, m, x_dev, STC_BF16,
+                     ld, x_stream_stride, packed_dev, packed_stream_stride, norms_dev, norms_stream_stride, stream,
+                     sketch_dev, sketch_stream_stride, rnorm_dev, rnorm_stream_stride);
 }
 
 stc_status stc_append_kv_batched(const void* states_dev, int64_t n_states, const int32_t* map,
@@ -876,8 +940,10 @@ stc_status stc_attend_rht_batched(const void* states_dev, int64_t n_states, cons
                                   const int32_t* v_map, const stc_head_info* infos, int64_t n_pairs,
                                   int64_t n_tokens, const void* k_packed_dev, const float* k_norms_dev,
                                   const void* v_packed_dev, const float* v_norms_dev, int64_t packed_pair_stride,
-                                  int64_t norms_pair_stride, int32_t group, const float* q_dev, float* out_dev,
-                                  float scale, void* ws_dev, size_t ws_bytes, stc_stream_t stream) {
+                                  int64_t norms_pair_stride, const void* k_sketch_dev, const float* k_rnorm_dev,
+                                  int64_t sketch_pair_stride, int64_t rnorm_pair_stride, int32_t group,
+                                  const float* q_dev, float* out_dev, float scale, void* ws_dev, size_t ws_bytes,
+                                  stc_stream_t stream) {
   bool rht = false;
   int mb = 0;
   if (stc_status s = check_batch("attend_rht", states_dev, n_states, infos, n_pairs, n_tokens, packed_pair_stride,
@@ -894,13 +960,25 @@ stc_status stc_attend_rht_batched(const void* states_dev, int64_t n_states, cons
     return fail(STC_EINVAL, "attend_rht: norms stride %lld < %lld tokens", (long long)norms_pair_stride,
                 (long long)n_tokens);
   if (!std::isfinite(scale)) return fail(STC_EINVAL, "attend_rht: scale must be finite");
+  if (k_sketch_dev) {
+    // the K states need the sketch matrix (V states have none; the maps live on the device,
+    // so only its presence in the array is checked: a K state without one adds nothing)
+    bool any = false;
+    for (int64_t i = 0; i < n_states; ++i) any = any || infos[i].sketch_bits == STC_SKETCH_BITS;
+    if (!any) return fail(STC_EINVAL, "attend_rht: a sketch is given but no state has a sketch matrix");
+    if (!k_rnorm_dev || !aligned(k_sketch_dev, 8) || !aligned(k_rnorm_dev, 4) || sketch_pair_stride % 8)
+      return fail(STC_EINVAL, "attend_rht: sketch needs 8-byte aligned bytes and the residual norms");
+    if (n_pairs > 1 && (sketch_pair_stride < n_tokens * (STC_SKETCH_BITS / 8) || rnorm_pair_stride < n_tokens))
+      return fail(STC_EINVAL, "attend_rht: sketch or residual norm stride too small");
+  }
   const size_t need = stc_attend_workspace_bytes(n_pairs, group, n_tokens);
   if (ws_bytes < need) return fail(STC_EWORKSPACE, "attend_rht: workspace %zu < %zu", ws_bytes, need);
   const unsigned char* st = static_cast<const unsigned char*>(states_dev);
   AttendLaunch a{st, k_map, st, v_map, n_states, n_pairs, n_tokens, packed_pair_stride,
                  static_cast<const unsigned char*>(k_packed_dev), static_cast<const unsigned char*>(v_packed_dev),
                  group, q_dev, out_dev, scale, static_cast<unsigned char*>(ws_dev), mb,
-                 k_norms_dev, v_norms_dev, norms_pair_stride, true};
+                 k_norms_dev, v_norms_dev, norms_pair_stride, true,
+                 static_cast<const unsigned char*>(k_sketch_dev), k_rnorm_dev, sketch_pair_stride, rnorm_pair_stride};
   if (launch_attend(a, stream)) return fail(STC_EDEVICE, "attend_rht launch: %s", hipGetErrorString(hipGetLastError()));
   return ok();
 }

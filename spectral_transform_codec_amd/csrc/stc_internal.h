@@ -19,6 +19,12 @@ constexpr size_t OFF_UT_LO = OFF_UT_HI + 32768;      // the low parts
 constexpr size_t OFF_W_HI = OFF_UT_LO + 32768;       // bf16 W[enc_row_channel(R)][j] at [R][j], W = U diag(step)
 constexpr size_t OFF_W_LO = OFF_W_HI + 32768;
 constexpr size_t OFF_THR = OFF_W_LO + 32768;         // float thresholds, up to 128*255
+// Walsh-Hadamard states with a key residual sketch reuse the threshold area:
+// P = S D H / sqrt(d) as bf16 hi / lo rows (sketch row i at [R][j], i =
+// enc_row_channel(R)) and S^T fp32 ([j][i] = S_ij) for S q.
+constexpr size_t OFF_SKP_HI = OFF_THR;
+constexpr size_t OFF_SKP_LO = OFF_THR + 32768;
+constexpr size_t OFF_SKT32 = OFF_THR + 65536;
 constexpr size_t OFF_GRAM = OFF_THR + 131072;        // double second moment [i][j]
 static_assert(OFF_GRAM + 131072 <= STATE_BYTES, "state layout overflows the blob");
 
@@ -37,7 +43,8 @@ struct alignas(16) DevHdr {
   int32_t n_kept;
   int32_t nmax16;       // 16 * ceil((last kept channel + 1) / 16): encode N extent
   int32_t kmax32;       // 32 * ceil((last kept channel + 1) / 32): decode K extent
-  int32_t pad[3];
+  int32_t sketch_bits;  // Walsh-Hadamard states: key residual sketch bits per token (0: none)
+  int32_t pad[2];
   uint8_t bits[D];
   uint16_t off[D];      // bit offset of channel j inside a token record
   float inv_step[D];    // fl32(1 / step_j); 0 for a dropped channel or a zero step
@@ -129,6 +136,9 @@ struct EncodeLaunch {
   int max_bits;   // largest total_bits of the states used
   int64_t n_old = 0;         // tokens already in the streams (append); n_tokens new ones follow
   int64_t norms_stride = 0;  // Walsh-Hadamard norms: elements between streams
+  unsigned char* sketch = nullptr;  // Walsh-Hadamard key residual sketch (16 bytes per token) or null
+  float* rnorm = nullptr;           // |r| per token
+  int64_t sketch_stride = 0, rnorm_stride = 0;
 };
 struct DecodeLaunch {
   const unsigned char* states;
@@ -160,6 +170,9 @@ struct AttendLaunch {
   const float* v_norms = nullptr;
   int64_t norms_stride = 0;       // elements between pairs
   bool rht = false;
+  const unsigned char* k_sketch = nullptr;  // Walsh-Hadamard keys: residual sketch and |r|, or null
+  const float* k_rnorm = nullptr;
+  int64_t sketch_stride = 0, rnorm_stride = 0;
 };
 
 int launch_gram(const void* x, int dtype, int64_t ld, int64_t n_calib, double* gram, void* stream);

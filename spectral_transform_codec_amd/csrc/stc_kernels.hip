@@ -832,6 +832,9 @@ struct RhtK {
   float* norms;
   const float* norms_in;
   long long n_old, norms_stride;  // encode: tokens already in the streams; norms row stride
+  unsigned char* sketch;          // key residual sketch: 16 bytes per token, stream stride sketch_stride
+  float* rnorm;                   // |r| per token, stream stride rnorm_stride
+  long long sketch_stride, rnorm_stride;
   int f32out;
 };
 
@@ -857,8 +860,17 @@ __device__ __forceinline__ void fwht128(float v[128]) {
 constexpr int RHT_WAVES = 4;
 constexpr int RHT_BPW = 4;  // blocks per wave
 constexpr size_t RHT_LDS = 128 * UROW;
+// With the key residual sketch (SKETCH): 8 waves, and P = S D H / sqrt(d)
+// (bf16 hi / lo rows) plus the codebook next to the basis in LDS. Each value
+// leaves e' = c - y_hat |x| sqrt(d) = |x| sqrt(d) (y - y_hat) in the rotated
+// basis; S r = P e' / sqrt(d) has the sign of P e', and |r| = |e'| / sqrt(d).
+constexpr int RHTS_WAVES = 8;
+constexpr size_t RHTS_LDS = 3 * 128 * UROW + 32;
 
-__global__ void __launch_bounds__(64 * RHT_WAVES, 4) k_rht_encode(RhtK a) {
+template <bool SKETCH>
+__global__ void __launch_bounds__(SKETCH ? 64 * RHTS_WAVES : 64 * RHT_WAVES, SKETCH ? 2 : 4)
+    k_rht_encode(RhtK a) {
+  constexpr int NWV = SKETCH ? RHTS_WAVES : RHT_WAVES;
   extern __shared__ __align__(16) unsigned char smem[];
   const long long s = blockIdx.y;
   const int tid = threadIdx.x;
@@ -870,10 +882,15 @@ __global__ void __launch_bounds__(64 * RHT_WAVES, 4) k_rht_encode(RhtK a) {
   const DevHdr* hdr = reinterpret_cast<const DevHdr*>(st + OFF_HDR);
   {
     const u32x4* g = reinterpret_cast<const u32x4*>(st + OFF_UT_HI);
-    for (int i = tid; i < 128 * 16; i += 64 * RHT_WAVES) {
+    for (int i = tid; i < 128 * 16; i += 64 * NWV) {
       const int row = i >> 4, c = i & 15;
       *reinterpret_cast<u32x4*>(smem + row * UROW + c * 16) = g[i];
+      if (SKETCH) {
+        *reinterpret_cast<u32x4*>(smem + (128 + row) * UROW + c * 16) = reinterpret_cast<const u32x4*>(st + OFF_SKP_HI)[i];
+        *reinterpret_cast<u32x4*>(smem + (256 + row) * UROW + c * 16) = reinterpret_cast<const u32x4*>(st + OFF_SKP_LO)[i];
+      }
     }
+    if (SKETCH && tid < 8) reinterpret_cast<float*>(smem + 3 * 128 * UROW)[tid] = hdr->cb[tid];
   }
   float thr[7];
 #pragma unroll
@@ -882,8 +899,12 @@ __global__ void __launch_bounds__(64 * RHT_WAVES, 4) k_rht_encode(RhtK a) {
   unsigned ub = lds_offset(smem + t32 * UROW + 16 * h);
   asm volatile("" : "+v"(ub));
   const lds_u8* uL = lds_ptr(ub);
+  unsigned pb = lds_offset(smem + 128 * UROW + t32 * UROW + 128 * h);  // P rows: lane reads cols 64h + 8ks ..
+  asm volatile("" : "+v"(pb));
+  const lds_u8* pL = lds_ptr(pb);
+  const float* sCb = reinterpret_cast<const float*>(smem + 3 * 128 * UROW);
   const long long nblk = (n + ENC_BT - 1) / ENC_BT;
-  const long long b0 = ((long long)blockIdx.x * RHT_WAVES + wave) * RHT_BPW;
+  const long long b0 = ((long long)blockIdx.x * NWV + wave) * RHT_BPW;
   for (long long blk = b0; blk < b0 + RHT_BPW && blk < nblk; ++blk) {
     const long long tok0 = blk * ENC_BT;
     const unsigned last = (unsigned)(n - 1 - tok0);
@@ -917,6 +938,9 @@ __global__ void __launch_bounds__(64 * RHT_WAVES, 4) k_rht_encode(RhtK a) {
 #pragma unroll
     for (int k = 0; k < 7; ++k) T[k] = nu > 0.0f ? thr[k] * sc : thr[k];
     unsigned w[6] = {0u, 0u, 0u, 0u, 0u, 0u};
+    // SKETCH: e' of channels 64h + 8ks + i as bf16 hi / lo B fragments, |e'|^2
+    u32x4 eh[8], el[8];
+    float ee = 0.0f;
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
       f32x16 acc;
@@ -937,6 +961,22 @@ __global__ void __launch_bounds__(64 * RHT_WAVES, 4) k_rht_encode(RhtK a) {
         const int bp = 3 * (16 * mb + e);  // bit of channel 64h + 16mb + e in the half record
         w[bp >> 5] |= q << (bp & 31);
         if ((bp & 31) > 29) w[(bp >> 5) + 1] |= q >> (32 - (bp & 31));
+        if (SKETCH) {
+          const float ep = __builtin_fmaf(-sCb[q], sc, c);  // c - y_hat |x| sqrt(d)
+          ee = __builtin_fmaf(ep, ep, ee);
+          const __bf16 hi = (__bf16)ep;
+          const __bf16 lo = (__bf16)(ep - (float)hi);
+          // channel 64h + 16mb + e is element e % 8 of fragment 2mb + e / 8
+          const int ks = 2 * mb + (e >> 3), k2 = (e & 7) >> 1;
+          const unsigned hv = __builtin_bit_cast(unsigned short, hi), lv = __builtin_bit_cast(unsigned short, lo);
+          if (e & 1) {
+            eh[ks][k2] |= hv << 16;
+            el[ks][k2] |= lv << 16;
+          } else {
+            eh[ks][k2] = hv;
+            el[ks][k2] = lv;
+          }
+        }
       }
       __builtin_amdgcn_sched_barrier(0);  // one row block's accumulators live at a time
     }
@@ -947,6 +987,38 @@ __global__ void __launch_bounds__(64 * RHT_WAVES, 4) k_rht_encode(RhtK a) {
       dst[1] = (u32x2){w[2], w[3]};
       dst[2] = (u32x2){w[4], w[5]};
       if (h == 0) a.norms[s * a.norms_stride + tk] = nu;
+    }
+    if (SKETCH) {
+      // sign bits of P e' for sketch rows 64h + 16mb + e of token t
+      unsigned zw[2] = {0u, 0u};
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        f32x16 acc;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+          const bf16x8 ph = LDS_AT(bf16x8, pL + 32 * mb * UROW + 16 * ks);
+          const bf16x8 pl = LDS_AT(bf16x8, pL + 128 * UROW + 32 * mb * UROW + 16 * ks);
+          acc = mfma32_bf16(ph, __builtin_bit_cast(bf16x8, eh[ks]), acc);
+          acc = mfma32_bf16(ph, __builtin_bit_cast(bf16x8, el[ks]), acc);
+          acc = mfma32_bf16(pl, __builtin_bit_cast(bf16x8, eh[ks]), acc);
+        }
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if (acc[e] >= 0.0f) zw[mb >> 1] |= 1u << (16 * (mb & 1) + e);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(ee), __float_as_uint(ee), false, false);
+        const unsigned s_lo = sw[0], s_hi = sw[1];
+        ee = __uint_as_float(s_lo) + __uint_as_float(s_hi);
+      }
+      if (tok0 + t32 < n) {
+        const long long tk = a.n_old + tok0 + t32;
+        *reinterpret_cast<u32x2*>(a.sketch + s * a.sketch_stride + tk * 16 + 8 * h) = (u32x2){zw[0], zw[1]};
+        if (h == 0) a.rnorm[s * a.rnorm_stride + tk] = sqrtf(ee) * 0.08838834764831845f;
+      }
     }
   }
 }
@@ -1034,9 +1106,25 @@ int launch_encode_rht(const EncodeLaunch& L, void* stream) {
   a.norms = L.norms;
   a.n_old = L.n_old;
   a.norms_stride = L.norms_stride;
+  a.sketch = L.sketch;
+  a.rnorm = L.rnorm;
+  a.sketch_stride = L.sketch_stride;
+  a.rnorm_stride = L.rnorm_stride;
   const long long nblk = (L.n_tokens + ENC_BT - 1) / ENC_BT;
-  dim3 grid((unsigned)((nblk + RHT_WAVES * RHT_BPW - 1) / (RHT_WAVES * RHT_BPW)), (unsigned)L.n_streams);
-  hipLaunchKernelGGL(k_rht_encode, grid, dim3(64 * RHT_WAVES), RHT_LDS, (hipStream_t)stream, a);
+  if (L.sketch) {
+    static bool attr = false;
+    if (!attr) {
+      if (hipFuncSetAttribute((const void*)k_rht_encode<true>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)RHTS_LDS) != hipSuccess)
+        return 1;
+      attr = true;
+    }
+    dim3 grid((unsigned)((nblk + RHTS_WAVES * RHT_BPW - 1) / (RHTS_WAVES * RHT_BPW)), (unsigned)L.n_streams);
+    hipLaunchKernelGGL(k_rht_encode<true>, grid, dim3(64 * RHTS_WAVES), RHTS_LDS, (hipStream_t)stream, a);
+  } else {
+    dim3 grid((unsigned)((nblk + RHT_WAVES * RHT_BPW - 1) / (RHT_WAVES * RHT_BPW)), (unsigned)L.n_streams);
+    hipLaunchKernelGGL(k_rht_encode<false>, grid, dim3(64 * RHT_WAVES), RHT_LDS, (hipStream_t)stream, a);
+  }
   return hipGetLastError() != hipSuccess;
 }
 
@@ -1102,6 +1190,9 @@ struct AttK {
   const float* k_norms;  // Walsh-Hadamard caches: per-token norms, pair stride norms_stride
   const float* v_norms;
   long long norms_stride;
+  const unsigned char* k_sketch;  // key residual sketch (16 bytes per token) and |r|, or null
+  const float* k_rnorm;
+  long long sketch_stride, rnorm_stride;
 };
 
 constexpr int ATT_WAVES_MAX = 16;
@@ -1305,12 +1396,16 @@ __device__ __forceinline__ void att_combine_pair(const AttK& a, long long p, flo
 // scores, fp16 for P.V), scores are scaled by the key's norm and P by the
 // value's norm over the largest value norm of the wave's block (the scale
 // is carried in the accumulators and restored at the merge).
-template <int NW, bool RHT>
+// SKETCH (RHT only): keys carry the 1-bit residual sketch; a second table
+// holds S q scale log2(e) sqrt(pi/2)/m (hi / lo) and each score gains
+// |r_t| times its product with the token's signs, one more MFMA chain.
+template <int NW, bool RHT, bool SKETCH>
 __global__ void __launch_bounds__(ATT_THREADS, 1) k_att_main(AttK a) {
   extern __shared__ __align__(16) unsigned char smem[];
   unsigned char* sA = smem;                                        // a table [32][AROW]
   unsigned* sTab = reinterpret_cast<unsigned*>(smem + 32 * AROW);  // K tables, V tables, codebook planes
-  unsigned* sReg0 = sTab + 6 * 128 + 16;                           // wave regions
+  unsigned char* sA2 = reinterpret_cast<unsigned char*>(sTab + 6 * 128 + 16);  // SKETCH: sign table [32][AROW]
+  unsigned* sReg0 = sTab + 6 * 128 + 16 + (SKETCH ? 32 * AROW / 4 : 0);       // wave regions
   const int nwav = (int)(blockDim.x >> 6);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -1353,16 +1448,18 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_att_main(AttK a) {
     float* red = sqT + 128 * 16;                    // [nparts][16][128]
     const int j = tid & 127, part = tid >> 7;
     const int nparts = (int)(blockDim.x >> 7);
-    const float* u = reinterpret_cast<const float*>(kst + OFF_U32);
     const float* qp = a.q + pg * g * 128;
     const int rows = 128 / nparts;  // 16 (1024 threads) or 32 (512)
-    float ur[32];
-#pragma unroll
-    for (int k = 0; k < 32; ++k) ur[k] = k < rows ? u[(part + k * nparts) * 128 + j] : 0.0f;  // issued together
     for (int e = tid; e < 128 * 16; e += blockDim.x) {
       const int r = e >> 4, hh = e & 15;
       sqT[e] = hh < g ? qp[hh * 128 + r] : 0.0f;
     }
+    for (int tab = 0; tab < (SKETCH ? 2 : 1); ++tab) {
+    // tab 0: U_K (scores), tab 1: S^T (sketch products)
+    const float* u = reinterpret_cast<const float*>(kst + (tab == 0 ? OFF_U32 : OFF_SKT32));
+    float ur[32];
+#pragma unroll
+    for (int k = 0; k < 32; ++k) ur[k] = k < rows ? u[(part + k * nparts) * 128 + j] : 0.0f;  // issued together
     __syncthreads();
     float acc[16];
 #pragma unroll
@@ -1382,20 +1479,23 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_att_main(AttK a) {
 #pragma unroll
     for (int hh = 0; hh < 16; ++hh) red[(part * 16 + hh) * 128 + j] = acc[hh];
     __syncthreads();
+    unsigned char* dstA = tab == 0 ? sA : sA2;
     for (int e = tid; e < 16 * 128; e += blockDim.x) {
       const int hh = e >> 7, c = e & 127;
       float val = 0.0f;
-      if (hh < g && hk->bits[c] > 0) {
+      if (hh < g && (tab == 1 || hk->bits[c] > 0)) {
         float sum = 0.0f;
         for (int pt = 0; pt < nparts; ++pt) sum += red[(pt * 16 + hh) * 128 + c];
-        val = sum * hk->step32[c] * a.scale * LOG2E;
+        val = tab == 0 ? sum * hk->step32[c] * a.scale * LOG2E
+                       : sum * (a.scale * LOG2E * 1.2533141373155003f / (float)STC_SKETCH_BITS);  // sqrt(pi/2)/m
       }
       const __bf16 hi = (__bf16)val;
       const __bf16 lo = (__bf16)(val - (float)hi);
-      *reinterpret_cast<__bf16*>(sA + hh * AROW + 2 * c) = hi;
-      *reinterpret_cast<__bf16*>(sA + (16 + hh) * AROW + 2 * c) = lo;
+      *reinterpret_cast<__bf16*>(dstA + hh * AROW + 2 * c) = hi;
+      *reinterpret_cast<__bf16*>(dstA + (16 + hh) * AROW + 2 * c) = lo;
     }
     __syncthreads();
+    }
   }
 
   // per-wave online softmax state: heads H = 8i + 4h + j in the score
@@ -1497,6 +1597,35 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_att_main(AttK a) {
           const int H = 8 * i + 4 * h + j;
           sc[i][j] = (tok_ok && H < g) ? (acc[4 * i + j] + acc[4 * (i + 2) + j]) * nk : -INFINITY;
         }
+      if (SKETCH) {
+        // + |r_t| (S q) . z_t: the lane's 64 signs (rows 64h .. 64h + 63) as +-1 bf16
+        u32x2 zb = (u32x2){0u, 0u};
+        float rn = 0.0f;
+        if (tok_ok) {
+          zb = *reinterpret_cast<const u32x2*>(a.k_sketch + pg * a.sketch_stride + (tok0 + t32) * 16 + 8 * h);
+          rn = a.k_rnorm[pg * a.rnorm_stride + tok0 + t32];
+        }
+        unsigned zab = lds_offset(sA2 + t32 * AROW + 128 * h);
+        asm volatile("" : "+v"(zab));
+        const lds_u8* zL = lds_ptr(zab);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+          const unsigned byte = (zb[ks >> 2] >> (8 * (ks & 3))) & 0xffu;
+          u32x4 zf;
+#pragma unroll
+          for (int k2 = 0; k2 < 4; ++k2) {
+            const unsigned x2 = byte >> (2 * k2);
+            zf[k2] = 0xBF80BF80u - ((x2 & 1u) << 15) - ((x2 & 2u) << 30);  // bit 1 -> +1, 0 -> -1
+          }
+          acc = mfma32_bf16(LDS_AT(bf16x8, zL + 16 * ks), __builtin_bit_cast(bf16x8, zf), acc);
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) sc[i][j] += (acc[4 * i + j] + acc[4 * (i + 2) + j]) * rn;
+      }
     }
     // RHT: P is stored as p * |v_t| / (largest |v| of the block), at most 1
     float pscale = 1.0f, vratio = 1.0f;
@@ -1657,11 +1786,13 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_att_main(AttK a) {
 
 int launch_attend(const AttendLaunch& L, void* stream) {
   if (!g_att_attr_done) {
-    if (hipFuncSetAttribute((const void*)k_att_main<8, false>, hipFuncAttributeMaxDynamicSharedMemorySize,
+    if (hipFuncSetAttribute((const void*)k_att_main<8, false, false>, hipFuncAttributeMaxDynamicSharedMemorySize,
                             160 * 1024) != hipSuccess ||
-        hipFuncSetAttribute((const void*)k_att_main<16, false>, hipFuncAttributeMaxDynamicSharedMemorySize,
+        hipFuncSetAttribute((const void*)k_att_main<16, false, false>, hipFuncAttributeMaxDynamicSharedMemorySize,
                             160 * 1024) != hipSuccess ||
-        hipFuncSetAttribute((const void*)k_att_main<8, true>, hipFuncAttributeMaxDynamicSharedMemorySize,
+        hipFuncSetAttribute((const void*)k_att_main<8, true, false>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            160 * 1024) != hipSuccess ||
+        hipFuncSetAttribute((const void*)k_att_main<8, true, true>, hipFuncAttributeMaxDynamicSharedMemorySize,
                             160 * 1024) != hipSuccess)
       return 1;
     g_att_attr_done = true;
@@ -1685,10 +1816,16 @@ int launch_attend(const AttendLaunch& L, void* stream) {
   a.k_norms = L.k_norms;
   a.v_norms = L.v_norms;
   a.norms_stride = L.norms_stride;
+  a.k_sketch = L.k_sketch;
+  a.k_rnorm = L.k_rnorm;
+  a.sketch_stride = L.sketch_stride;
+  a.rnorm_stride = L.rnorm_stride;
   a.stream_words = att_stream_words(L.max_bits);
   a.region_words = att_region_words(L.max_bits);
+  const bool sketch = L.rht && L.k_sketch;
+  const size_t fixed = ATT_FIXED_BYTES + (sketch ? 32 * AROW : 0);
   int waves = ATT_WAVES_MAX;
-  while (waves > 4 && ATT_FIXED_BYTES + (size_t)waves * a.region_words * 4 > 160 * 1024) waves -= 4;
+  while (waves > 4 && fixed + (size_t)waves * a.region_words * 4 > 160 * 1024) waves -= 4;
   hipStream_t s = (hipStream_t)stream;
   for (long long c0 = 0; c0 < L.n_pairs; c0 += ATT_MAX_PAIRS) {
     const long long np = L.n_pairs - c0 < ATT_MAX_PAIRS ? L.n_pairs - c0 : ATT_MAX_PAIRS;
@@ -1696,16 +1833,18 @@ int launch_attend(const AttendLaunch& L, void* stream) {
     a.n_pairs = np;
     a.split_tokens = att_split_tokens(np, L.n_tokens);
     a.n_splits = att_n_splits(np, L.n_tokens);
-    size_t att_lds = ATT_FIXED_BYTES + (size_t)waves * a.region_words * 4;
+    size_t att_lds = fixed + (size_t)waves * a.region_words * 4;
     const size_t cmb = att_combine_lds_bytes();
     if (att_lds < cmb) att_lds = cmb;
     const dim3 grid((unsigned)a.n_splits, (unsigned)np);
-    if (L.rht)
-      hipLaunchKernelGGL((k_att_main<8, true>), grid, dim3(64 * waves), att_lds, s, a);
+    if (sketch)
+      hipLaunchKernelGGL((k_att_main<8, true, true>), grid, dim3(64 * waves), att_lds, s, a);
+    else if (L.rht)
+      hipLaunchKernelGGL((k_att_main<8, true, false>), grid, dim3(64 * waves), att_lds, s, a);
     else if (L.max_bits <= 512)
-      hipLaunchKernelGGL((k_att_main<8, false>), grid, dim3(64 * waves), att_lds, s, a);
+      hipLaunchKernelGGL((k_att_main<8, false, false>), grid, dim3(64 * waves), att_lds, s, a);
     else
-      hipLaunchKernelGGL((k_att_main<16, false>), grid, dim3(64 * waves), att_lds, s, a);
+      hipLaunchKernelGGL((k_att_main<16, false, false>), grid, dim3(64 * waves), att_lds, s, a);
   }
   return hipGetLastError() != hipSuccess;
 }

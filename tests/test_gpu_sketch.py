@@ -1,0 +1,124 @@
+"""Key residual sketch (1-bit JL on the Walsh-Hadamard key path) on the GPU
+against the oracle: sketch bits from the GPU's own codes (at most 1e-3 of
+bits differ, where S r is within rounding of 0), residual norms within 1e-4
+relative, appends equal one encode, and attention with the sketch within
+2e-3 of the oracle's."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import codec, qjl, rht
+
+pytestmark = pytest.mark.gpu
+
+stc = pytest.importorskip("spectral_transform_codec_amd")
+
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module")
+def cb():
+    c, _ = rht.lloyd_max(synth.sphere_coordinate_samples(100000))
+    return rht.codebook_fp32(c)
+
+
+def make(cb, heads, kind=0):
+    sig = [synth.random_signs(3, 0, 0, h, kind) for h in range(heads)]
+    S = [synth.sketch_matrix(3, 0, 0, h, kind) for h in range(heads)]
+    arr = stc.StateArray([stc.rht_sketch_state_init(sig[h], cb, S[h]) for h in range(heads)])
+    return sig, S, arr
+
+
+def gpu_encode(arr, x, n):
+    P = x.shape[0]
+    packed = torch.zeros((P, stc.packed_bytes(384, n)), dtype=torch.uint8, device=DEV)
+    norms = torch.zeros((P, n), dtype=torch.float32, device=DEV)
+    sk = torch.zeros((P, stc.packed_bytes(128, n)), dtype=torch.uint8, device=DEV)
+    rn = torch.zeros((P, n), dtype=torch.float32, device=DEV)
+    stc.append_rht_sketch_batched(arr, x, 0, packed, norms, sk, rn)
+    return packed, norms, sk, rn
+
+
+@pytest.mark.parametrize("n", [1, 777, 32768])
+def test_sketch_encode_matches_oracle(cb, n):
+    w = synth.WORKLOADS[3]
+    heads = 2
+    sig, S, arr = make(cb, heads)
+    xs = [synth.stream(w, 0, 0, h, 0, n=n) for h in range(heads)]
+    x = torch.stack([torch.from_numpy(xi) for xi in xs]).to(DEV, torch.bfloat16)
+    packed, norms, sk, rn = gpu_encode(arr, x, n)
+    plain, pnorms = stc.encode_kv_batched(stc.StateArray([stc.rht_state_init(sig[h], cb) for h in range(heads)]), x)
+    assert torch.equal(packed, plain) and torch.equal(norms, pnorms)     # codes unchanged by the sketch
+    for h in range(heads):
+        st = rht.make_state(sig[h], cb)
+        gp, gn = packed[h].cpu().numpy(), norms[h].cpu().numpy()
+        zs, zr = qjl.sketch_encode(st, xs[h], gp, gn, S[h])
+        gz = codec.unpack(sk[h].cpu().numpy(), qjl.sketch_bits_vector(), n)
+        oz = codec.unpack(zs, qjl.sketch_bits_vector(), n)
+        assert (gz != oz).mean() <= 1e-3, (gz != oz).mean()
+        grn = rn[h].cpu().numpy()
+        assert np.all(np.abs(grn - zr) <= 1e-4 * np.maximum(zr, 1e-30) + 1e-30)
+
+
+def test_sketch_append_equals_one_encode(cb):
+    w = synth.WORKLOADS[3]
+    n = 1000
+    sig, S, arr = make(cb, 2)
+    x = torch.stack([torch.from_numpy(synth.stream(w, 0, 0, h, 0, n=n)) for h in range(2)]).to(DEV, torch.bfloat16)
+    full = gpu_encode(arr, x, n)
+    bufs = [torch.full_like(t, 7) for t in full]
+    for a, b in zip([0, 1, 33, 100, 517], [1, 33, 100, 517, 1000]):
+        stc.append_rht_sketch_batched(arr, x[:, a:b], a, *bufs)
+    for got, want in zip(bufs, full):
+        assert torch.equal(got, want)
+
+
+def rel_err(a, b):
+    return float(np.abs(np.asarray(a, np.float64) - np.asarray(b, np.float64)).max() / np.abs(b).max())
+
+
+@pytest.mark.parametrize("n,g,gpu_codes", [(1, 4, False), (500, 4, False), (3000, 7, False), (32768, 4, True)])
+def test_attention_with_sketch_matches_oracle(cb, n, g, gpu_codes):
+    w = synth.WORKLOADS[3]
+    pairs = 2
+    ksig, kS, _ = make(cb, pairs, kind=0)
+    vsig = [synth.random_signs(3, 0, 0, h, 1) for h in range(pairs)]
+    states = []
+    for h in range(pairs):
+        states += [stc.rht_sketch_state_init(ksig[h], cb, kS[h]), stc.rht_state_init(vsig[h], cb)]
+    arr = stc.StateArray(states)
+    kx = [synth.stream(w, 0, 0, h, 0, n=n) for h in range(pairs)]
+    vx = [synth.stream(w, 0, 0, h, 1, n=n) for h in range(pairs)]
+    kst = [rht.make_state(ksig[h], cb) for h in range(pairs)]
+    vst = [rht.make_state(vsig[h], cb) for h in range(pairs)]
+    if gpu_codes:
+        karr = stc.StateArray([states[2 * h] for h in range(pairs)])
+        varr = stc.StateArray([states[2 * h + 1] for h in range(pairs)])
+        kp, kn, ks, kr = gpu_encode(karr, torch.stack([torch.from_numpy(t) for t in kx]).to(DEV, torch.bfloat16), n)
+        vp, vn = stc.encode_kv_batched(varr, torch.stack([torch.from_numpy(t) for t in vx]).to(DEV, torch.bfloat16))
+        host = [t.cpu().numpy() for t in (kp, kn, ks, kr, vp, vn)]
+    else:
+        host = [[], [], [], [], [], []]
+        for h in range(pairs):
+            p, nn = rht.encode_kv(kst[h], kx[h])
+            z, r = qjl.sketch_encode(kst[h], kx[h], p, nn, kS[h])
+            vp_, vn_ = rht.encode_kv(vst[h], vx[h])
+            for lst, val in zip(host, (p, nn, z, r, vp_, vn_)):
+                lst.append(val)
+        host = [np.stack(lst) for lst in host]
+        kp, kn, ks, kr, vp, vn = [torch.from_numpy(t).to(DEV) for t in host]
+    kmap = torch.arange(0, 2 * pairs, 2, dtype=torch.int32, device=DEV)
+    vmap = kmap + 1
+    q = np.random.default_rng(90 + n).standard_normal((pairs, g, 128)).astype(np.float32)
+    out = stc.attend_rht_batched(arr, kmap, vmap, kp, kn, vp, vn, n, torch.from_numpy(q).to(DEV),
+                                 k_sketch=ks, k_rnorm=kr).cpu().numpy()
+    hkp, hkn, hks, hkr, hvp, hvn = host
+    for h in range(pairs):
+        want = qjl.attend_compressed(kst[h], vst[h], hkp[h], hkn[h], hks[h], hkr[h], kS[h], hvp[h], hvn[h], n,
+                                     q[h].astype(np.float64))
+        assert rel_err(out[h], want) <= 2e-3, (h, rel_err(out[h], want))
+    # the correction matters: without it the result is the plain Walsh-Hadamard attention
+    plain = stc.attend_rht_batched(arr, kmap, vmap, kp, kn, vp, vn, n, torch.from_numpy(q).to(DEV)).cpu().numpy()
+    if n > 1:
+        assert rel_err(plain, out) > 1e-3
