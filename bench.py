@@ -258,6 +258,37 @@ def main():
     torch.cuda.synchronize()
     step_us["attend_rht"] = round(1e3 * e0.elapsed_time(e1) / args.steps, 2)
 
+    # (5) the key residual sketch on the same layer: sketch encode of the 8 K
+    # streams, then attention with the score correction
+    sk_states = []
+    for s_ in range(S):
+        sg = synth.random_signs(3, 0, 0, s_ // 2, s_ % 2)
+        sk_states.append(stc.rht_sketch_state_init(sg, cb32, synth.sketch_matrix(3, 0, 0, s_ // 2, 0))
+                         if s_ % 2 == 0 else stc.rht_state_init(sg, cb32))
+    sk_arr = stc.StateArray(sk_states)
+    kx3 = x3[0::2]
+    sk_packed = torch.empty((S, stc.packed_bytes(384, n)), dtype=torch.uint8, device=dev)[0::2]  # V's strides
+    sk_norms = torch.empty((S, n), dtype=torch.float32, device=dev)[0::2]
+    sk_bits = torch.empty((heads, stc.packed_bytes(128, n)), dtype=torch.uint8, device=dev)
+    sk_rn = torch.empty((heads, n), dtype=torch.float32, device=dev)
+    kmap_sk = torch.arange(0, S, 2, dtype=torch.int32, device=dev)
+    sfn = lambda: stc.append_rht_sketch_batched(sk_arr, kx3, 0, sk_packed, sk_norms, sk_bits, sk_rn,
+                                                state_of_stream=kmap_sk)
+    afn = lambda: stc.attend_rht_batched(sk_arr, kmap, vmap, sk_packed, sk_norms, rv, rvn, n, q, ws=ws,
+                                         out=rht_out, k_sketch=sk_bits, k_rnorm=sk_rn)
+    for name, fn in (("rht_sketch_encode_K", sfn), ("attend_rht_sketch", afn)):
+        for _ in range(3):
+            fn()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(args.steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        step_us[name] = round(1e3 * e0.elapsed_time(e1) / args.steps, 2)
+
     per_op = {}
     for i, (name, _, nbytes) in enumerate(ops):
         ms = [ev[k][i][0].elapsed_time(ev[k][i][1]) for k in range(args.steps)]
@@ -323,7 +354,8 @@ def main():
         "codec_GBps": round(codec_bytes / (codec_ms * 1e-3) / 1e9, 1),
         "attn_tokens_per_s": {nm: round(1e3 / per_op[nm]["ms"], 1) for nm in attn_names},
         # not in value: a generation step per budget (append one K/V token per KV head, then attend over
-        # n) and one attention step over the Walsh-Hadamard caches
+        # n), one attention step over the Walsh-Hadamard caches, and the key residual sketch (its
+        # encode of the 8 K streams, attention with the score correction)
         "extra_us": step_us,
         "breakdown": per_op,
         "roofline": {"bound": "hbm", "kernel": dname, "launches_per_step": d_n,

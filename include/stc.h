@@ -254,7 +254,9 @@ stc_status stc_append_kv_batched(const void* states_dev, int64_t n_states,
  * token's key residual sketch (STC_SKETCH_BITS / 8 bytes at sketch_dev +
  * s*sketch_stream_stride + t*16, row i at bit i, 1 = non-negative,
  * sign(0) = +1) and |r| (fp32 at rnorm_dev + s*rnorm_stream_stride + t).
- * STC_EINVAL if a state has no sketch matrix. */
+ * Streams whose state has no sketch matrix get codes and norms only (their
+ * sketch bytes and residual norms are not written); STC_EINVAL if no state
+ * of the array has one. */
 stc_status stc_append_rht_sketch_batched(const void* states_dev, int64_t n_states,
                                         const int32_t* state_of_stream_dev, const stc_head_info* infos,
                                         int64_t n_streams, int64_t n_old, int64_t m, const void* x_dev,

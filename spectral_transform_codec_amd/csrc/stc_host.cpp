@@ -802,9 +802,11 @@ static stc_status encode_impl(const char* who, const void* states_dev, int64_t n
   if (rht && !aligned(norms_dev, 4)) return fail(STC_EINVAL, "%s: norms misaligned", who);
   if (sketch_dev) {
     if (!rht) return fail(STC_EUNSUPPORTED, "%s: the residual sketch needs Walsh-Hadamard states", who);
-    for (int64_t i = 0; i < n_states; ++i)
-      if (infos[i].sketch_bits != STC_SKETCH_BITS)
-        return fail(STC_EINVAL, "%s: state %lld has no sketch matrix", who, (long long)i);
+    // the map lives on the device: streams whose state has no sketch matrix get codes and
+    // norms only (their sketch bytes and residual norms are left as they are)
+    bool any = false;
+    for (int64_t i = 0; i < n_states; ++i) any = any || infos[i].sketch_bits == STC_SKETCH_BITS;
+    if (!any) return fail(STC_EINVAL, "%s: no state has a sketch matrix", who);
     if (!rnorm_dev || !aligned(sketch_dev, 8) || !aligned(rnorm_dev, 4) || sketch_stream_stride % 8)
       return fail(STC_EINVAL, "%s: sketch needs 8-byte aligned bytes and a norms buffer", who);
     if (n_streams > 1 && (sketch_stream_stride < (n_old + m) * (STC_SKETCH_BITS / 8) ||

@@ -988,7 +988,7 @@ __global__ void __launch_bounds__(SKETCH ? 64 * RHTS_WAVES : 64 * RHT_WAVES, SKE
       dst[2] = (u32x2){w[4], w[5]};
       if (h == 0) a.norms[s * a.norms_stride + tk] = nu;
     }
-    if (SKETCH) {
+    if (SKETCH && hdr->sketch_bits != 0) {
       // sign bits of P e' for sketch rows 64h + 16mb + e of token t
       unsigned zw[2] = {0u, 0u};
 #pragma unroll
