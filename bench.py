@@ -59,8 +59,8 @@ KERNEL_OF_OP = {"encode": "k_encode_eigen<bf16>", "decode": "k_decode_eigen<bf16
 # rocprofv3 kernel names of the same kernels
 PROFILE_NAME = {"k_encode_eigen<bf16>": "void stc::k_encode_eigen<0>(stc::EncK)",
                 "k_decode_eigen<bf16>": "void stc::k_decode_eigen<0, 8>(stc::DecK)",
-                "k_att_main": "void stc::k_att_main<8>(stc::AttK)",
-                "k_rht_encode": "stc::k_rht_encode(stc::RhtK)",
+                "k_att_main": "void stc::k_att_main<8, false, false>(stc::AttK)",
+                "k_rht_encode": "void stc::k_rht_encode<false>(stc::RhtK)",
                 "k_rht_decode": "stc::k_rht_decode(stc::RhtK)"}
 KERNEL_SOURCE = os.path.join(ROOT, "spectral_transform_codec_amd", "csrc", "stc_kernels.hip")
 PROFILES = os.path.join(ROOT, "profiles")
@@ -80,7 +80,7 @@ def source_digest():
 def stored_traffic(kernel):
     """HBM bytes per launch of `kernel` from a committed counter summary, or
     None if there is none or the kernel source changed since it was taken."""
-    path = os.path.join(PROFILES, "traffic_" + kernel.replace("<", "_").replace(">", "") + "_cfg2.txt")
+    path = os.path.join(PROFILES, "traffic_" + kernel.replace("<", "_").replace(">", "") + "_llama_layer.txt")
     if not os.path.exists(path):
         return None
     vals = {}
