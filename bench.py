@@ -289,6 +289,25 @@ def main():
         torch.cuda.synchronize()
         step_us[name] = round(1e3 * e0.elapsed_time(e1) / args.steps, 2)
 
+    # (6) cold caches: each op of the step once more, after 1 GiB of writes
+    # has pushed the L2s and the 256 MiB memory-side cache out
+    scratch = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    cold = {}
+    for name, fn, nbytes in ops:
+        ms = []
+        for _ in range(3):
+            scratch.fill_(1.0)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms.append(e0.elapsed_time(e1))
+        cold[name] = {"us": round(1e3 * min(ms), 2),
+                      "pct_hbm_peak": round(100.0 * nbytes / (min(ms) * 1e-3) / 1e9 / HBM_PEAK_GBPS, 1)}
+    del scratch
+
     per_op = {}
     for i, (name, _, nbytes) in enumerate(ops):
         ms = [ev[k][i][0].elapsed_time(ev[k][i][1]) for k in range(args.steps)]
@@ -358,6 +377,7 @@ def main():
         # encode of the 8 K streams, attention with the score correction)
         "extra_us": step_us,
         "breakdown": per_op,
+        "breakdown_cold": cold,  # each op alone after 1 GiB of writes (not in value)
         "roofline": {"bound": "hbm", "kernel": dname, "launches_per_step": d_n,
                      "algorithmic_bytes_per_launch": int(d_bytes / d_n),
                      "avg_launch_us": round(1e3 * d_ms / d_n, 2),
