@@ -5,6 +5,14 @@ amplification of its score noise in "Statistische Validatie en Jensen's
 Ongelijkheid"). Test infrastructure only: the tests, the smoke check and the
 CPU baseline of the benchmark use it; the library never does.
 
+The eigen cache gets the "selective" sketch of SpectralQuant (ablation
+summary, "Experimentele Opstelling": a selective QJL sketch on the top
+effective dimensions). READING: it covers the quantization residual of the
+water-filled channels, r_j = c_j - c_hat_j for the kept channels with a
+positive step, in the latent basis (0 for dropped channels); the query is
+taken to the same basis, so the estimate of (U^T q) . r is
+sqrt(pi/2) / m ||r|| (S U^T q) . z.
+
 READINGs (the pages give no parameters): m = 128 sketch bits per token;
 S [m][d] iid N(0, 1), seeded per stream and passed in; the sketch of key k
 is z = sign(S r) of the residual r = k - K_hat (K_hat the exact
@@ -63,3 +71,35 @@ def attend_compressed(k_state: Dict, v_state: Dict, k_packed: np.ndarray, k_norm
     vhat = rht.reconstruct_exact(v_state, v_packed, v_norms, n)
     extra = score_correction(q, sketch, rnorm, S, n)
     return codec.softmax_attention(q, khat, vhat, scale, extra)
+
+
+# ------------------------------------------------------- eigen cache (selective)
+def latent_residual(state: Dict, x: np.ndarray) -> np.ndarray:
+    """r_j = c_j - c_hat_j on the kept channels with a positive step, 0
+    elsewhere, [n][d] fp64 (c = x U, c_hat the dequantized codes)."""
+    c = codec.project(state, x)
+    chat = codec.dequantize(state, codec.quantize(state, c))
+    keep = (np.asarray(state["bits"]) > 0) & (np.asarray(state["steps"]) > 0)
+    return np.where(keep[None, :], c - chat, 0.0)
+
+
+def sketch_encode_eigen(state: Dict, x: np.ndarray, S: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """Selective sketch of keys x [n][d] on the eigen cache: (packed sign bits
+    of S r, ||r|| fp32 [n])."""
+    r = latent_residual(state, x)
+    S = np.asarray(S, dtype=np.float32).astype(np.float64)
+    z = (r @ S.T >= 0.0).astype(np.int64)
+    return codec.pack(z, sketch_bits_vector(S.shape[0])), np.sqrt(np.sum(r * r, axis=1)).astype(np.float32)
+
+
+def attend_compressed_eigen(k_state: Dict, v_state: Dict, k_packed: np.ndarray, sketch: np.ndarray,
+                            rnorm: np.ndarray, S: np.ndarray, v_packed: np.ndarray, n: int, q: np.ndarray,
+                            scale=None) -> np.ndarray:
+    """Decode-step attention over an eigen cache whose keys carry the selective
+    sketch: q . K_hat_t plus sqrt(pi/2)/m ||r_t|| (S U^T q) . z_t. fp32 [g][d]."""
+    khat = codec.reconstruct_exact(k_state, k_packed, n)
+    vhat = codec.reconstruct_exact(v_state, v_packed, n)
+    qt = np.asarray(q, dtype=np.float64) @ k_state["U"]          # U^T q, [g][d]
+    extra = score_correction(qt, sketch, rnorm, S, n)
+    return codec.softmax_attention(q, khat, vhat, scale, extra)
+

@@ -97,3 +97,48 @@ def test_sketch_bits_layout():
     bits = np.unpackbits(sk, bitorder="little")[: 3 * qjl.SKETCH_BITS].reshape(3, -1)
     assert np.array_equal(bits, (r @ S.astype(np.float64).T >= 0).astype(np.uint8))
     assert sk.shape[0] == codec.packed_bytes(qjl.SKETCH_BITS, 3)
+
+
+# ----------------------------------------------------- selective sketch, eigen cache
+def _eigen_case(n=48, avg=1.33, seed=87):
+    w = synth.WORKLOADS[2]
+    x = synth.stream(w, 0, 0, 1, 0, n=2048)
+    st = codec.calibrate_head(x, 2048, avg)
+    S = np.random.default_rng(seed).standard_normal((qjl.SKETCH_BITS, D)).astype(np.float32)
+    return st, x[:n], S
+
+
+def test_latent_residual_identity():
+    """q . k - q . K_hat = (U^T q) . (c - c_hat) exactly; the selective
+    residual leaves out only the dropped channels' coefficients."""
+    st, x, _ = _eigen_case()
+    n = x.shape[0]
+    q = np.random.default_rng(88).standard_normal(D)
+    kp = codec.encode_kv(st, x)
+    miss = x @ q - codec.reconstruct_exact(st, kp, n) @ q
+    r = qjl.latent_residual(st, x)
+    c = codec.project(st, x)
+    dropped = np.asarray(st["bits"]) == 0
+    assert dropped.any()                                  # 1.33 bits drops channels
+    rest = c[:, dropped] @ (st["U"].T @ q)[dropped]
+    assert np.allclose(miss, r @ (st["U"].T @ q) + rest, rtol=0, atol=1e-9 * np.abs(miss).max())
+    assert np.all(r[:, dropped] == 0)
+
+
+def test_selective_sketch_unbiased():
+    """Over independent sketches the corrected score converges to
+    q . K_hat + (U^T q) . r (the dropped channels stay uncorrected)."""
+    st, x, _ = _eigen_case()
+    n = x.shape[0]
+    q = np.random.default_rng(89).standard_normal((4, D))
+    kp = codec.encode_kv(st, x)
+    base = q @ codec.reconstruct_exact(st, kp, n).T
+    target = base + (q @ st["U"]) @ qjl.latent_residual(st, x).T
+    rng = np.random.default_rng(90)
+    acc = np.zeros_like(base)
+    T = 300
+    for _ in range(T):
+        S = rng.standard_normal((qjl.SKETCH_BITS, D)).astype(np.float32)
+        sk, rn = qjl.sketch_encode_eigen(st, x, S)
+        acc += base + qjl.score_correction(q @ st["U"], sk, rn, S, n)
+    assert np.mean((acc / T - target) ** 2) < 0.02 * np.mean((base - target) ** 2)
