@@ -177,6 +177,19 @@ stc_status stc_state_init(int32_t d, int32_t xform, const double* u, const doubl
                           const uint8_t* bits, const double* steps, stc_head_info* info,
                           void* state_dev, stc_stream_t stream);
 
+/* stc_state_init plus a selective residual sketch of the keys (SpectralQuant:
+ * "a selective QJL sketch on the top effective dimensions", ablation summary,
+ * "Experimentele Opstelling"): sketch[i*d + j] = S_ij (host fp32, finite,
+ * STC_SKETCH_BITS x d). The sketch covers r = c - c_hat on the kept channels
+ * with a positive step (latent basis; 0 elsewhere): stc_sketch_kv_batched
+ * writes sign(S r) and |r| per token, stc_attend_compressed_sketch_batched
+ * adds sqrt(pi/2)/STC_SKETCH_BITS |r_t| (S U^T q).z_t to each score. The
+ * sketch matrices take the place of the state's fp32 threshold table (which
+ * no kernel reads). Synchronizes `stream`. */
+stc_status stc_state_init_sketch(int32_t d, int32_t xform, const double* u, const double* lambda,
+                                 const uint8_t* bits, const double* steps, const float* sketch,
+                                 stc_head_info* info, void* state_dev, stc_stream_t stream);
+
 /* Build a Walsh-Hadamard state: signs[d] in {-1,+1}, codebook[8] fp32
  * ascending. Fills *info and state_dev; synchronizes `stream`. */
 stc_status stc_rht_state_init(int32_t d, const int8_t* signs, const float* codebook,
@@ -266,6 +279,21 @@ stc_status stc_append_rht_sketch_batched(const void* states_dev, int64_t n_state
                                         int64_t sketch_stream_stride, float* rnorm_dev,
                                         int64_t rnorm_stream_stride, stc_stream_t stream);
 
+/* The selective residual sketch of tokens [n_old, n_old + m) of eigen /
+ * identity streams (bf16 tokens, x row r = token n_old + r) whose states
+ * were built by stc_state_init_sketch: recomputes the cells and codes the
+ * encode gives those tokens (it does not read the packed stream), then writes
+ * sign(S r) (STC_SKETCH_BITS / 8 bytes at sketch_dev + s*sketch_stream_stride
+ * + t*16, row i at bit i, 1 = non-negative) and |r| (fp32 at rnorm_dev +
+ * s*rnorm_stream_stride + t). Streams whose state has no sketch matrix are
+ * left untouched; STC_EINVAL if no state has one. */
+stc_status stc_sketch_kv_batched(const void* states_dev, int64_t n_states,
+                                const int32_t* state_of_stream_dev, const stc_head_info* infos,
+                                int64_t n_streams, int64_t n_old, int64_t m, const void* x_dev,
+                                int64_t ld, int64_t x_stream_stride, void* sketch_dev,
+                                int64_t sketch_stream_stride, float* rnorm_dev,
+                                int64_t rnorm_stream_stride, stc_stream_t stream);
+
 /* One stream. */
 stc_status stc_encode_kv(const stc_head_info* info, const void* state_dev, int64_t n_tokens,
                          const void* x_dev, int32_t dtype, int64_t ld, void* packed_dev,
@@ -300,6 +328,22 @@ stc_status stc_attend_compressed_batched(const void* states_dev, int64_t n_state
                                          int32_t group, const float* q_dev, float* out_dev,
                                          float scale, void* ws_dev, size_t ws_bytes,
                                          stc_stream_t stream);
+
+/* stc_attend_compressed_batched with the keys' selective residual sketch
+ * (from stc_sketch_kv_batched; pair p's at k_sketch_dev + p*sketch_pair_stride,
+ * 16 bytes per token, and |r| at k_rnorm_dev + p*rnorm_pair_stride): every
+ * score gains sqrt(pi/2)/STC_SKETCH_BITS |r_t| (S U_K^T q).z_t. */
+stc_status stc_attend_compressed_sketch_batched(const void* states_dev, int64_t n_states,
+                                                const int32_t* k_state_of_pair_dev,
+                                                const int32_t* v_state_of_pair_dev,
+                                                const stc_head_info* infos, int64_t n_pairs,
+                                                int64_t n_tokens, const void* k_packed_dev,
+                                                const void* v_packed_dev, int64_t packed_pair_stride,
+                                                const void* k_sketch_dev, const float* k_rnorm_dev,
+                                                int64_t sketch_pair_stride, int64_t rnorm_pair_stride,
+                                                int32_t group, const float* q_dev, float* out_dev,
+                                                float scale, void* ws_dev, size_t ws_bytes,
+                                                stc_stream_t stream);
 
 /* One KV head. */
 stc_status stc_attend_compressed(const stc_head_info* k_info, const void* k_state_dev,

@@ -149,17 +149,23 @@ def _new_blob(device) -> torch.Tensor:
 
 
 def state_init(u: Optional[np.ndarray], lam: np.ndarray, bits: np.ndarray, steps: Optional[np.ndarray] = None,
-               xform: int = XFORM_EIGEN, device="cuda") -> State:
+               xform: int = XFORM_EIGEN, device="cuda", sketch: Optional[np.ndarray] = None) -> State:
+    """sketch: S [128][128] fp32 to attach the keys' selective residual sketch."""
     info = HeadInfo()
     blob = _new_blob(device)
     lam = np.ascontiguousarray(lam, np.float64)
     bits = np.ascontiguousarray(bits, np.uint8)
     u_p = None if u is None else np.ascontiguousarray(u, np.float64)
     s_p = None if steps is None else np.ascontiguousarray(steps, np.float64)
-    check("stc_state_init", lib().stc_state_init(
-        D, xform, None if u_p is None else _np_ptr(u_p, ctypes.c_double), _np_ptr(lam, ctypes.c_double),
-        _np_ptr(bits, ctypes.c_uint8), None if s_p is None else _np_ptr(s_p, ctypes.c_double),
-        ctypes.byref(info), _ptr(blob), _stream()))
+    args = (D, xform, None if u_p is None else _np_ptr(u_p, ctypes.c_double), _np_ptr(lam, ctypes.c_double),
+            _np_ptr(bits, ctypes.c_uint8), None if s_p is None else _np_ptr(s_p, ctypes.c_double))
+    if sketch is None:
+        check("stc_state_init", lib().stc_state_init(*args, ctypes.byref(info), _ptr(blob), _stream()))
+    else:
+        sk = np.ascontiguousarray(sketch, np.float32)
+        assert sk.shape == (128, D)
+        check("stc_state_init_sketch", lib().stc_state_init_sketch(*args, _np_ptr(sk, ctypes.c_float),
+                                                                   ctypes.byref(info), _ptr(blob), _stream()))
     return State(blob, info)
 
 
@@ -353,6 +359,39 @@ def append_rht_sketch_batched(states: StateArray, x: torch.Tensor, n_old: int, p
         x.stride(1), x.stride(0), _ptr(packed), packed.stride(0), _ptr(norms), norms.stride(0), _ptr(sketch),
         sketch.stride(0), _ptr(rnorm), rnorm.stride(0), _stream()))
     return packed
+
+
+def sketch_kv_batched(states: StateArray, x: torch.Tensor, n_old: int, sketch: torch.Tensor, rnorm: torch.Tensor,
+                      state_of_stream: Optional[torch.Tensor] = None):
+    """Selective residual sketch of eigen keys: x [S][m][128] bf16 are tokens n_old .. n_old+m-1;
+    sketch uint8 [S][>= 16 (n_old+m)], rnorm fp32 [S][>= n_old+m]."""
+    assert x.dim() == 3 and x.shape[2] == D and x.stride(2) == 1 and x.dtype == torch.bfloat16
+    assert rnorm.dtype == torch.float32 and rnorm.stride(1) == 1
+    check("stc_sketch_kv_batched", lib().stc_sketch_kv_batched(
+        _ptr(states.blob), states.n, _ptr(_map_arg(state_of_stream)), states.infos, x.shape[0], n_old, x.shape[1],
+        _ptr(x), x.stride(1), x.stride(0), _ptr(sketch), sketch.stride(0), _ptr(rnorm), rnorm.stride(0), _stream()))
+    return sketch
+
+
+def attend_compressed_sketch_batched(states: StateArray, k_state_of_pair: torch.Tensor,
+                                     v_state_of_pair: torch.Tensor, k_packed: torch.Tensor, v_packed: torch.Tensor,
+                                     k_sketch: torch.Tensor, k_rnorm: torch.Tensor, n: int, q: torch.Tensor,
+                                     scale: Optional[float] = None, ws: Optional[torch.Tensor] = None,
+                                     out: Optional[torch.Tensor] = None):
+    Pn, g = q.shape[0], q.shape[1]
+    assert k_packed.stride(0) == v_packed.stride(0)
+    scale = (1.0 / np.sqrt(D)) if scale is None else scale
+    if out is None:
+        out = torch.empty((Pn, g, D), dtype=torch.float32, device=q.device)
+    need = attend_workspace_bytes(Pn, g, n)
+    if ws is None or ws.numel() < need:
+        ws = torch.zeros(need, dtype=torch.uint8, device=q.device)  # zero-filled once
+    check("stc_attend_compressed_sketch_batched", lib().stc_attend_compressed_sketch_batched(
+        _ptr(states.blob), states.n, _ptr(_map_arg(k_state_of_pair)), _ptr(_map_arg(v_state_of_pair)),
+        states.infos, Pn, n, _ptr(k_packed), _ptr(v_packed), k_packed.stride(0), _ptr(k_sketch), _ptr(k_rnorm),
+        k_sketch.stride(0), k_rnorm.stride(0), g, _ptr(q), _ptr(out), float(scale), _ptr(ws), ws.numel(),
+        _stream()))
+    return out
 
 
 def decode_kv_batched(states: StateArray, packed: torch.Tensor, n: int, norms: Optional[torch.Tensor] = None,

@@ -46,6 +46,13 @@ SIGNATURES = {
     "stc_append_rht_sketch_batched": (c_i32, [c_vp, c_i64, c_vp, P(HeadInfo), c_i64, c_i64, c_i64, c_vp, c_i64,
                                               c_i64, c_vp, c_i64, c_vp, c_i64, c_vp, c_i64, c_vp, c_i64, c_vp]),
     "stc_rht_sketch_state_init": (c_i32, [c_i32, P(ctypes.c_int8), P(c_f32), P(c_f32), P(HeadInfo), c_vp, c_vp]),
+    "stc_state_init_sketch": (c_i32, [c_i32, c_i32, P(c_f64), P(c_f64), P(c_u8), P(c_f64), P(c_f32), P(HeadInfo),
+                                      c_vp, c_vp]),
+    "stc_sketch_kv_batched": (c_i32, [c_vp, c_i64, c_vp, P(HeadInfo), c_i64, c_i64, c_i64, c_vp, c_i64, c_i64, c_vp,
+                                      c_i64, c_vp, c_i64, c_vp]),
+    "stc_attend_compressed_sketch_batched": (c_i32, [c_vp, c_i64, c_vp, c_vp, P(HeadInfo), c_i64, c_i64, c_vp, c_vp,
+                                                     c_i64, c_vp, c_vp, c_i64, c_i64, c_i32, c_vp, c_vp, c_f32, c_vp,
+                                                     c_size, c_vp]),
     "stc_encode_kv": (c_i32, [P(HeadInfo), c_vp, c_i64, c_vp, c_i32, c_i64, c_vp, c_vp, c_vp]),
     "stc_decode_kv": (c_i32, [P(HeadInfo), c_vp, c_i64, c_vp, c_vp, c_vp, c_i32, c_i64, c_vp]),
     "stc_quantize_pack_f32": (c_i32, [P(HeadInfo), c_vp, c_i64, c_vp, c_vp, c_vp]),

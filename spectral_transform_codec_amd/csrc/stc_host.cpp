@@ -576,6 +576,50 @@ stc_status stc_state_init(int32_t d, int32_t xform, const double* u, const doubl
   return ok();
 }
 
+stc_status stc_state_init_sketch(int32_t d, int32_t xform, const double* u, const double* lambda,
+                                 const uint8_t* bits, const double* steps, const float* sketch,
+                                 stc_head_info* info, void* state_dev, stc_stream_t stream) {
+  if (!sketch) return fail(STC_EINVAL, "state_init_sketch: NULL sketch matrix");
+  for (int k = 0; k < STC_SKETCH_BITS * D; ++k)
+    if (!std::isfinite(sketch[k])) return fail(STC_EINVAL, "state_init_sketch: sketch entry %d not finite", k);
+  if (d != D) return fail(STC_EUNSUPPORTED, "state_init_sketch: d=%d (only %d is supported)", d, D);
+  if (xform != STC_XFORM_EIGEN && xform != STC_XFORM_IDENTITY)
+    return fail(STC_EUNSUPPORTED, "state_init_sketch: xform %d", xform);
+  if (xform == STC_XFORM_EIGEN && !u) return fail(STC_EINVAL, "state_init_sketch: EIGEN needs a basis");
+  if (xform == STC_XFORM_IDENTITY && u) return fail(STC_EINVAL, "state_init_sketch: IDENTITY takes no basis");
+  if (!lambda || !bits || !info) return fail(STC_EINVAL, "state_init_sketch: NULL lambda/bits/info");
+  if (stc_status s = check_state_ptr(state_dev, "state_dev")) return s;
+  for (int j = 0; j < d; ++j)
+    if (bits[j] > STC_MAX_BITS) return fail(STC_EBUDGET, "state_init_sketch: width %d > 8 at channel %d", bits[j], j);
+  if (steps)
+    for (int j = 0; j < d; ++j)
+      if (bits[j] && !(steps[j] >= 0.0 && std::isfinite(steps[j])))
+        return fail(STC_EINVAL, "state_init_sketch: bad step at channel %d", j);
+  std::vector<unsigned char> blob;
+  build_eigen_blob(d, xform, u, lambda, bits, steps, info, blob);
+  // the sketch replaces the fp32 threshold table (which no kernel reads): S rows
+  // (latent channel order) permuted like the encode basis, bf16 hi / lo, and
+  // M^T = (S U^T)^T fp32 for the attention's S U^T q
+  DevHdr* h = reinterpret_cast<DevHdr*>(blob.data() + OFF_HDR);
+  h->sketch_bits = STC_SKETCH_BITS;
+  uint16_t* p_hi = reinterpret_cast<uint16_t*>(blob.data() + OFF_SKP_HI);
+  uint16_t* p_lo = reinterpret_cast<uint16_t*>(blob.data() + OFF_SKP_LO);
+  float* mt = reinterpret_cast<float*>(blob.data() + OFF_SKT32);
+  for (int R = 0; R < STC_SKETCH_BITS; ++R) {
+    const int i = enc_row_channel(R);
+    for (int j = 0; j < D; ++j) split_bf16((double)sketch[i * D + j], &p_hi[R * D + j], &p_lo[R * D + j]);
+  }
+  for (int k = 0; k < D; ++k)
+    for (int i = 0; i < STC_SKETCH_BITS; ++i) {
+      double acc = 0.0;  // M_ik = sum_j S_ij U_kj
+      for (int j = 0; j < D; ++j) acc += (double)sketch[i * D + j] * (u ? u[(size_t)k * D + j] : (k == j ? 1.0 : 0.0));
+      mt[k * STC_SKETCH_BITS + i] = (float)acc;
+    }
+  info->sketch_bits = STC_SKETCH_BITS;
+  if (stc_status s = upload(blob, state_dev, stream)) return s;
+  return ok();
+}
+
 static stc_status rht_state_build(int32_t d, const int8_t* signs, const float* codebook, const float* sketch,
                                   stc_head_info* info, void* state_dev, stc_stream_t stream) {
   if (d != D) return fail(STC_EUNSUPPORTED, "rht_state_init: d=%d (only %d is supported)", d, D);
@@ -843,6 +887,37 @@ stc_status stc_append_rht_sketch_batched(const void* states_dev, int64_t n_state
                      sketch_dev, sketch_stream_stride, rnorm_dev, rnorm_stream_stride);
 }
 
+stc_status stc_sketch_kv_batched(const void* states_dev, int64_t n_states, const int32_t* map,
+                                const stc_head_info* infos, int64_t n_streams, int64_t n_old, int64_t m,
+                                const void* x_dev, int64_t ld, int64_t x_stream_stride, void* sketch_dev,
+                                int64_t sketch_stream_stride, float* rnorm_dev, int64_t rnorm_stream_stride,
+                                stc_stream_t stream) {
+  bool rht = false;
+  int mb = 0;
+  if (n_old < 0 || m < 0) return fail(STC_EINVAL, "sketch_kv: negative token count");
+  if (stc_status s = check_batch("sketch_kv", states_dev, n_states, infos, n_streams, n_old + m, (int64_t)1 << 40,
+                                 &rht, &mb))  // no packed stream here
+    return s;
+  if (rht) return fail(STC_EUNSUPPORTED, "sketch_kv: eigen/identity states (Walsh-Hadamard: append_rht_sketch)");
+  bool any = false;
+  for (int64_t i = 0; i < n_states; ++i) any = any || infos[i].sketch_bits == STC_SKETCH_BITS;
+  if (!any) return fail(STC_EINVAL, "sketch_kv: no state has a sketch matrix");
+  if (m == 0) return ok();
+  if (!x_dev || !sketch_dev || !rnorm_dev) return fail(STC_EINVAL, "sketch_kv: NULL buffer");
+  if (ld < D || !aligned(x_dev, 16) || (ld * 2) % 16 || (x_stream_stride * 2) % 16)
+    return fail(STC_EINVAL, "sketch_kv: x rows must be >= 128 bf16 and 16-byte aligned");
+  if (n_streams > 1 && x_stream_stride < (m - 1) * ld + D) return fail(STC_EINVAL, "sketch_kv: x stream stride too small");
+  if (!aligned(sketch_dev, 8) || !aligned(rnorm_dev, 4) || sketch_stream_stride % 8)
+    return fail(STC_EINVAL, "sketch_kv: misaligned sketch or norms");
+  if (n_streams > 1 && (sketch_stream_stride < (n_old + m) * (STC_SKETCH_BITS / 8) || rnorm_stream_stride < n_old + m))
+    return fail(STC_EINVAL, "sketch_kv: sketch or residual norm stride too small");
+  EncodeLaunch a{static_cast<const unsigned char*>(states_dev), map, n_states, n_streams, m, ld, x_stream_stride, 0,
+                 x_dev, nullptr, nullptr, 0, mb, n_old, 0,
+                 static_cast<unsigned char*>(sketch_dev), rnorm_dev, sketch_stream_stride, rnorm_stream_stride};
+  if (launch_sketch_eigen(a, stream)) return fail(STC_EDEVICE, "sketch_kv launch: %s", hipGetErrorString(hipGetLastError()));
+  return ok();
+}
+
 stc_status stc_append_kv_batched(const void* states_dev, int64_t n_states, const int32_t* map,
                                  const stc_head_info* infos, int64_t n_streams, int64_t n_old, int64_t m,
                                  const void* x_dev, int32_t dtype, int64_t ld, int64_t x_stream_stride,
@@ -935,6 +1010,43 @@ stc_status stc_attend_compressed_batched(const void* states_dev, int64_t n_state
                  static_cast<const unsigned char*>(k_packed_dev), static_cast<const unsigned char*>(v_packed_dev),
                  group, q_dev, out_dev, scale, static_cast<unsigned char*>(ws_dev), mb};
   if (launch_attend(a, stream)) return fail(STC_EDEVICE, "attend launch: %s", hipGetErrorString(hipGetLastError()));
+  return ok();
+}
+
+stc_status stc_attend_compressed_sketch_batched(const void* states_dev, int64_t n_states, const int32_t* k_map,
+                                                const int32_t* v_map, const stc_head_info* infos, int64_t n_pairs,
+                                                int64_t n_tokens, const void* k_packed_dev, const void* v_packed_dev,
+                                                int64_t packed_pair_stride, const void* k_sketch_dev,
+                                                const float* k_rnorm_dev, int64_t sketch_pair_stride,
+                                                int64_t rnorm_pair_stride, int32_t group, const float* q_dev,
+                                                float* out_dev, float scale, void* ws_dev, size_t ws_bytes,
+                                                stc_stream_t stream) {
+  bool rht = false;
+  int mb = 0;
+  if (stc_status s = check_batch("attend_sketch", states_dev, n_states, infos, n_pairs, n_tokens, packed_pair_stride,
+                                 &rht, &mb)) return s;
+  if (rht) return fail(STC_EUNSUPPORTED, "attend_sketch: eigen/identity states (Walsh-Hadamard: attend_rht)");
+  if (group < 1 || group > 16) return fail(STC_EUNSUPPORTED, "attend_sketch: group %d outside 1..16", group);
+  if (n_tokens <= 0) return fail(STC_EINVAL, "attend_sketch: need at least one cached token");
+  if (!k_packed_dev || !v_packed_dev || !q_dev || !out_dev || !ws_dev || !k_sketch_dev || !k_rnorm_dev)
+    return fail(STC_EINVAL, "attend_sketch: NULL buffer");
+  if (!aligned(k_packed_dev, 16) || !aligned(v_packed_dev, 16) || !aligned(q_dev, 16) || !aligned(out_dev, 16) ||
+      !aligned(ws_dev, 256) || !aligned(k_sketch_dev, 8) || !aligned(k_rnorm_dev, 4) || sketch_pair_stride % 8)
+    return fail(STC_EINVAL, "attend_sketch: misaligned buffer");
+  if (n_pairs > 1 && (sketch_pair_stride < n_tokens * (STC_SKETCH_BITS / 8) || rnorm_pair_stride < n_tokens))
+    return fail(STC_EINVAL, "attend_sketch: sketch or residual norm stride too small");
+  bool any = false;
+  for (int64_t i = 0; i < n_states; ++i) any = any || infos[i].sketch_bits == STC_SKETCH_BITS;
+  if (!any) return fail(STC_EINVAL, "attend_sketch: no state has a sketch matrix");
+  if (!std::isfinite(scale)) return fail(STC_EINVAL, "attend_sketch: scale must be finite");
+  const size_t need = stc_attend_workspace_bytes(n_pairs, group, n_tokens);
+  if (ws_bytes < need) return fail(STC_EWORKSPACE, "attend_sketch: workspace %zu < %zu", ws_bytes, need);
+  const unsigned char* st = static_cast<const unsigned char*>(states_dev);
+  AttendLaunch a{st, k_map, st, v_map, n_states, n_pairs, n_tokens, packed_pair_stride,
+                 static_cast<const unsigned char*>(k_packed_dev), static_cast<const unsigned char*>(v_packed_dev),
+                 group, q_dev, out_dev, scale, static_cast<unsigned char*>(ws_dev), mb, nullptr, nullptr, 0, false,
+                 static_cast<const unsigned char*>(k_sketch_dev), k_rnorm_dev, sketch_pair_stride, rnorm_pair_stride};
+  if (launch_attend(a, stream)) return fail(STC_EDEVICE, "attend_sketch launch: %s", hipGetErrorString(hipGetLastError()));
   return ok();
 }
 

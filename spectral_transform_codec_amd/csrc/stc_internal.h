@@ -179,6 +179,7 @@ int launch_gram(const void* x, int dtype, int64_t ld, int64_t n_calib, double* g
 int launch_encode_eigen(const EncodeLaunch& a, void* stream);
 int launch_decode_eigen(const DecodeLaunch& a, void* stream);
 int launch_encode_rht(const EncodeLaunch& a, void* stream);
+int launch_sketch_eigen(const EncodeLaunch& a, void* stream);
 int launch_decode_rht(const DecodeLaunch& a, void* stream);
 int launch_attend(const AttendLaunch& a, void* stream);
 

@@ -164,6 +164,9 @@ struct EncK {
   long long blocks_per_stream, total_blocks, blocks_per_wg;
   long long n_old, blk0;  // tokens already in the streams; first (absolute) 32-token block
   long long norms_stride;
+  unsigned char* sketch;  // selective residual sketch (16 bytes per token) and |r|
+  float* rnorm;
+  long long sketch_stride, rnorm_stride;
   int grid;
 };
 
@@ -438,6 +441,161 @@ __global__ void __launch_bounds__(ENC_THREADS, 1) k_encode_eigen(EncK a) {
     }
     seg = seg_end;
   }
+}
+
+// ======================================================================
+// Selective residual sketch of eigen / identity keys (tokens bf16): a wave
+// takes 32-token blocks, recomputes the cell coordinates y = x U/step + L/2
+// with the encode's scaled basis and its codes q = clamp(floor y), keeps
+// r = step (y - q - 1/2) = c - c_hat on the kept channels (the step table is
+// 0 elsewhere), and writes the signs of S r (rows permuted like the encode
+// basis, hi / lo MFMA chains against r hi / lo) and |r| per token.
+// ======================================================================
+constexpr int SKE_WAVES = 8;
+constexpr int SKE_BPW = 4;  // blocks per wave
+constexpr size_t SKE_LDS = 4 * 128 * UROW + 3 * 128 * 4;
+
+__global__ void __launch_bounds__(64 * SKE_WAVES, 2) k_sketch_eigen(EncK a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const long long s = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int t32 = lane & 31, h = lane >> 5;
+  const long long m = a.n_tokens;  // x rows of the call; row j is token n_old + j of the stream
+  const unsigned char* st = a.states + (size_t)state_index(a.map, s, a.n_states) * STATE_BYTES;
+  const DevHdr* hdr = reinterpret_cast<const DevHdr*>(st + OFF_HDR);
+  if (hdr->sketch_bits == 0) return;  // the whole workgroup: no sketch matrix for this stream
+  float* sTb = reinterpret_cast<float*>(smem + 4 * 128 * UROW);  // L/2, L - 1, step (per channel)
+  for (int i = tid; i < 128 * 16; i += 64 * SKE_WAVES) {
+    const int row = i >> 4, c = i & 15;
+    *reinterpret_cast<u32x4*>(smem + row * UROW + c * 16) = reinterpret_cast<const u32x4*>(st + OFF_UT_HI)[i];
+    *reinterpret_cast<u32x4*>(smem + (128 + row) * UROW + c * 16) = reinterpret_cast<const u32x4*>(st + OFF_UT_LO)[i];
+    *reinterpret_cast<u32x4*>(smem + (256 + row) * UROW + c * 16) = reinterpret_cast<const u32x4*>(st + OFF_SKP_HI)[i];
+    *reinterpret_cast<u32x4*>(smem + (384 + row) * UROW + c * 16) = reinterpret_cast<const u32x4*>(st + OFF_SKP_LO)[i];
+  }
+  if (tid < 128) {
+    sTb[tid] = hdr->yhalf[tid];
+    sTb[128 + tid] = (float)hdr->lm1[tid];
+    sTb[256 + tid] = hdr->step32[tid];
+  }
+  __syncthreads();
+  unsigned ub = lds_offset(smem + t32 * UROW + 16 * h);                // basis rows: cols 16ks + 8h ..
+  unsigned pb = lds_offset(smem + 256 * UROW + t32 * UROW + 128 * h);  // S rows: cols 64h + 8ks ..
+  unsigned tb = lds_offset(reinterpret_cast<unsigned char*>(sTb + 64 * h));
+  asm volatile("" : "+v"(ub), "+v"(pb), "+v"(tb));
+  const lds_u8* uL = lds_ptr(ub);
+  const lds_u8* pL = lds_ptr(pb);
+  const lds_u8* tL = lds_ptr(tb);
+  const long long nblk = (m + ENC_BT - 1) / ENC_BT;
+  const long long b0 = ((long long)blockIdx.x * SKE_WAVES + wave) * SKE_BPW;
+  for (long long blk = b0; blk < b0 + SKE_BPW && blk < nblk; ++blk) {
+    const long long tok0 = blk * ENC_BT;
+    const unsigned last = (unsigned)(m - 1 - tok0);
+    const unsigned r = (unsigned)t32 < last ? (unsigned)t32 : last;
+    const unsigned short* row = static_cast<const unsigned short*>(a.x) + s * a.x_stride + (tok0 + r) * a.ld;
+    bf16x8 xf[8];
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+      xf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(row + 16 * ks + 8 * h));
+    u32x4 rh[8], rl[8];  // r of channels 64h + 8ks + i, bf16 hi / lo
+    float ee = 0.0f;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      f32x16 acc;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const int off = 32 * mb * UROW + 32 * ks;
+        acc = mfma32_bf16(LDS_AT(bf16x8, uL + off), xf[ks], acc);
+        acc = mfma32_bf16(LDS_AT(bf16x8, uL + 128 * UROW + off), xf[ks], acc);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int coff = 4 * (16 * mb + 4 * i);
+        const f32x4 yh = LDS_AT(f32x4, tL + coff);
+        const f32x4 lm = LDS_AT(f32x4, tL + 512 + coff);
+        const f32x4 stp = LDS_AT(f32x4, tL + 1024 + coff);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int e = 4 * i + j;
+          const float y = acc[e] + yh[j];
+          const float q = (float)(unsigned)__builtin_amdgcn_fmed3f(y, 0.0f, lm[j]);
+          const float rv = stp[j] == 0.0f ? 0.0f : stp[j] * (y - q - 0.5f);
+          ee = __builtin_fmaf(rv, rv, ee);
+          const __bf16 hi = (__bf16)rv;
+          const __bf16 lo = (__bf16)(rv - (float)hi);
+          const int ks = 2 * mb + (e >> 3), k2 = (e & 7) >> 1;
+          const unsigned hv = __builtin_bit_cast(unsigned short, hi), lv = __builtin_bit_cast(unsigned short, lo);
+          if (e & 1) {
+            rh[ks][k2] |= hv << 16;
+            rl[ks][k2] |= lv << 16;
+          } else {
+            rh[ks][k2] = hv;
+            rl[ks][k2] = lv;
+          }
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    unsigned zw[2] = {0u, 0u};
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      f32x16 acc;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const bf16x8 ph = LDS_AT(bf16x8, pL + 32 * mb * UROW + 16 * ks);
+        const bf16x8 pl = LDS_AT(bf16x8, pL + 128 * UROW + 32 * mb * UROW + 16 * ks);
+        acc = mfma32_bf16(ph, __builtin_bit_cast(bf16x8, rh[ks]), acc);
+        acc = mfma32_bf16(ph, __builtin_bit_cast(bf16x8, rl[ks]), acc);
+        acc = mfma32_bf16(pl, __builtin_bit_cast(bf16x8, rh[ks]), acc);
+      }
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        if (acc[e] >= 0.0f) zw[mb >> 1] |= 1u << (16 * (mb & 1) + e);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(ee), __float_as_uint(ee), false, false);
+      const unsigned s_lo = sw[0], s_hi = sw[1];
+      ee = __uint_as_float(s_lo) + __uint_as_float(s_hi);
+    }
+    if (tok0 + t32 < m) {
+      const long long tk = a.n_old + tok0 + t32;
+      *reinterpret_cast<u32x2*>(a.sketch + s * a.sketch_stride + tk * 16 + 8 * h) = (u32x2){zw[0], zw[1]};
+      if (h == 0) a.rnorm[s * a.rnorm_stride + tk] = sqrtf(ee);
+    }
+  }
+}
+
+int launch_sketch_eigen(const EncodeLaunch& L, void* stream) {
+  static bool attr = false;
+  if (!attr) {
+    if (hipFuncSetAttribute((const void*)k_sketch_eigen, hipFuncAttributeMaxDynamicSharedMemorySize, (int)SKE_LDS) !=
+        hipSuccess)
+      return 1;
+    attr = true;
+  }
+  EncK a{};
+  a.states = L.states;
+  a.map = L.map;
+  a.n_states = L.n_states;
+  a.n_tokens = L.n_tokens;
+  a.ld = L.ld;
+  a.x_stride = L.x_stride;
+  a.x = L.x;
+  a.n_old = L.n_old;
+  a.sketch = L.sketch;
+  a.rnorm = L.rnorm;
+  a.sketch_stride = L.sketch_stride;
+  a.rnorm_stride = L.rnorm_stride;
+  const long long nblk = (L.n_tokens + ENC_BT - 1) / ENC_BT;
+  dim3 grid((unsigned)((nblk + SKE_WAVES * SKE_BPW - 1) / (SKE_WAVES * SKE_BPW)), (unsigned)L.n_streams);
+  hipLaunchKernelGGL(k_sketch_eigen, grid, dim3(64 * SKE_WAVES), SKE_LDS, (hipStream_t)stream, a);
+  return hipGetLastError() != hipSuccess;
 }
 
 static bool g_enc_attr_done = false, g_dec_attr_done = false, g_att_attr_done = false;
@@ -1793,6 +1951,10 @@ int launch_attend(const AttendLaunch& L, void* stream) {
         hipFuncSetAttribute((const void*)k_att_main<8, true, false>, hipFuncAttributeMaxDynamicSharedMemorySize,
                             160 * 1024) != hipSuccess ||
         hipFuncSetAttribute((const void*)k_att_main<8, true, true>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            160 * 1024) != hipSuccess ||
+        hipFuncSetAttribute((const void*)k_att_main<8, false, true>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            160 * 1024) != hipSuccess ||
+        hipFuncSetAttribute((const void*)k_att_main<16, false, true>, hipFuncAttributeMaxDynamicSharedMemorySize,
                             160 * 1024) != hipSuccess)
       return 1;
     g_att_attr_done = true;
@@ -1822,7 +1984,7 @@ int launch_attend(const AttendLaunch& L, void* stream) {
   a.rnorm_stride = L.rnorm_stride;
   a.stream_words = att_stream_words(L.max_bits);
   a.region_words = att_region_words(L.max_bits);
-  const bool sketch = L.rht && L.k_sketch;
+  const bool sketch = L.k_sketch != nullptr;
   const size_t fixed = ATT_FIXED_BYTES + (sketch ? 32 * AROW : 0);
   int waves = ATT_WAVES_MAX;
   while (waves > 4 && fixed + (size_t)waves * a.region_words * 4 > 160 * 1024) waves -= 4;
@@ -1837,8 +1999,12 @@ int launch_attend(const AttendLaunch& L, void* stream) {
     const size_t cmb = att_combine_lds_bytes();
     if (att_lds < cmb) att_lds = cmb;
     const dim3 grid((unsigned)a.n_splits, (unsigned)np);
-    if (sketch)
+    if (sketch && L.rht)
       hipLaunchKernelGGL((k_att_main<8, true, true>), grid, dim3(64 * waves), att_lds, s, a);
+    else if (sketch && L.max_bits <= 512)
+      hipLaunchKernelGGL((k_att_main<8, false, true>), grid, dim3(64 * waves), att_lds, s, a);
+    else if (sketch)
+      hipLaunchKernelGGL((k_att_main<16, false, true>), grid, dim3(64 * waves), att_lds, s, a);
     else if (L.rht)
       hipLaunchKernelGGL((k_att_main<8, true, false>), grid, dim3(64 * waves), att_lds, s, a);
     else if (L.max_bits <= 512)

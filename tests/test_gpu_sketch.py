@@ -122,3 +122,81 @@ def test_attention_with_sketch_matches_oracle(cb, n, g, gpu_codes):
     plain = stc.attend_rht_batched(arr, kmap, vmap, kp, kn, vp, vn, n, torch.from_numpy(q).to(DEV)).cpu().numpy()
     if n > 1:
         assert rel_err(plain, out) > 1e-3
+
+
+# ----------------------------------------------------- selective sketch, eigen cache
+def eigen_states(avg, pairs, sketch_k=True):
+    w = synth.WORKLOADS[2]
+    out = []
+    for h in range(pairs):
+        for kind in (0, 1):
+            st = codec.calibrate_head(synth.stream(w, 0, 0, h, kind, n=2048), 2048, avg)
+            S = synth.sketch_matrix(2, 0, 0, h, kind) if (kind == 0 and sketch_k) else None
+            out.append((st, S))
+    return out
+
+
+@pytest.mark.parametrize("avg,n", [(2.0, 777), (1.33, 32768), (4.0, 1)])
+def test_eigen_sketch_matches_oracle(avg, n):
+    w = synth.WORKLOADS[2]
+    sts = eigen_states(avg, 2)
+    arr = stc.StateArray([stc.state_init(st["U"], st["lam"], st["bits"], st["steps"], sketch=S) for st, S in sts])
+    kmap = torch.tensor([0, 2], dtype=torch.int32, device=DEV)
+    xs = [synth.stream(w, 0, 0, h, 0, n=n) for h in range(2)]
+    x = torch.stack([torch.from_numpy(t) for t in xs]).to(DEV, torch.bfloat16)
+    sk = torch.zeros((2, stc.packed_bytes(128, n)), dtype=torch.uint8, device=DEV)
+    rn = torch.zeros((2, n), dtype=torch.float32, device=DEV)
+    stc.sketch_kv_batched(arr, x, 0, sk, rn, state_of_stream=kmap)
+    for h in range(2):
+        st, S = sts[2 * h]
+        zs, zr = qjl.sketch_encode_eigen(st, xs[h], S)
+        gz = codec.unpack(sk[h].cpu().numpy(), qjl.sketch_bits_vector(), n)
+        oz = codec.unpack(zs, qjl.sketch_bits_vector(), n)
+        # a code that differs from the oracle's (<= 1e-4 of codes) changes its token's residual
+        assert (gz != oz).mean() <= 2e-3, (gz != oz).mean()
+        grn = rn[h].cpu().numpy()
+        close = np.abs(grn - zr) <= 1e-3 * np.maximum(zr, 1e-30)
+        assert close.mean() >= 0.999
+
+
+def test_eigen_sketch_append_equals_one_pass():
+    w = synth.WORKLOADS[2]
+    n = 1000
+    sts = eigen_states(2.0, 1)
+    arr = stc.StateArray([stc.state_init(st["U"], st["lam"], st["bits"], st["steps"], sketch=S) for st, S in sts])
+    x = torch.from_numpy(synth.stream(w, 0, 0, 0, 0, n=n))[None].to(DEV, torch.bfloat16)
+    sk = torch.zeros((1, stc.packed_bytes(128, n)), dtype=torch.uint8, device=DEV)
+    rn = torch.zeros((1, n), dtype=torch.float32, device=DEV)
+    stc.sketch_kv_batched(arr, x, 0, sk, rn)
+    sk2, rn2 = torch.full_like(sk, 3), torch.full_like(rn, 5.0)
+    for a, b in zip([0, 1, 33, 517], [1, 33, 517, 1000]):
+        stc.sketch_kv_batched(arr, x[:, a:b], a, sk2, rn2)
+    assert torch.equal(sk, sk2) and torch.equal(rn, rn2)
+
+
+@pytest.mark.parametrize("avg,n,g", [(2.0, 1, 4), (2.0, 2000, 4), (1.33, 3000, 7), (4.0, 32768, 4)])
+def test_eigen_attention_with_sketch_matches_oracle(avg, n, g):
+    w = synth.WORKLOADS[2]
+    pairs = 2
+    sts = eigen_states(avg, pairs)
+    arr = stc.StateArray([stc.state_init(st["U"], st["lam"], st["bits"], st["steps"], sketch=S) for st, S in sts])
+    kmap = torch.tensor([0, 2], dtype=torch.int32, device=DEV)
+    vmap = kmap + 1
+    kx = [synth.stream(w, 0, 0, h, 0, n=n) for h in range(pairs)]
+    vx = [synth.stream(w, 0, 0, h, 1, n=n) for h in range(pairs)]
+    stride = stc.packed_bytes(arr.max_bits, n)
+    kp = np.zeros((pairs, stride), np.uint8); vp = np.zeros((pairs, stride), np.uint8)
+    sk = np.zeros((pairs, stc.packed_bytes(128, n)), np.uint8); rn = np.zeros((pairs, n), np.float32)
+    for h in range(pairs):
+        (ks, S), (vs, _) = sts[2 * h], sts[2 * h + 1]
+        p = codec.encode_kv(ks, kx[h]); kp[h, :p.shape[0]] = p
+        p = codec.encode_kv(vs, vx[h]); vp[h, :p.shape[0]] = p
+        z, r = qjl.sketch_encode_eigen(ks, kx[h], S); sk[h] = z; rn[h] = r
+    q = np.random.default_rng(95 + n).standard_normal((pairs, g, 128)).astype(np.float32)
+    out = stc.attend_compressed_sketch_batched(
+        arr, kmap, vmap, torch.from_numpy(kp).to(DEV), torch.from_numpy(vp).to(DEV), torch.from_numpy(sk).to(DEV),
+        torch.from_numpy(rn).to(DEV), n, torch.from_numpy(q).to(DEV)).cpu().numpy()
+    for h in range(pairs):
+        (ks, S), (vs, _) = sts[2 * h], sts[2 * h + 1]
+        want = qjl.attend_compressed_eigen(ks, vs, kp[h], sk[h], rn[h], S, vp[h], n, q[h].astype(np.float64))
+        assert rel_err(out[h], want) <= 2e-3, (h, rel_err(out[h], want))
