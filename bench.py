@@ -47,6 +47,9 @@ def parse():
                          "`bench.py --copy-mib N` into a traffic summary for --kernel")
     ap.add_argument("--summarize-trace", metavar="TRACE_DIR", default=None,
                     help="no GPU work: print the kernel statistics of a rocprofv3 --kernel-trace --stats run")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="time only the step (no generation step, Walsh-Hadamard attention, sketch or cold "
+                         "passes); for counter runs whose per-launch averages must cover the step's launches only")
     ap.add_argument("--kernel", default=None, help="kernel name prefix for --summarize")
     ap.add_argument("--command", default="", help="command line recorded in a summary")
     return ap.parse_args()
@@ -219,94 +222,94 @@ def main():
             ev[k][i][1].record(stream)
     torch.cuda.synchronize()
 
-    # (3) one generation step per budget (append the last token's K and V to
-    # every KV head, then attend over all n): it rewrites record n - 1 with
-    # the same codes, so the caches stay as they are
-    kn = x2[0::2, n - 1].contiguous()
-    vn = x2[1::2, n - 1].contiguous()
-    step_us = {}
-    for b in budgets:
-        kp, vp = packed[b][0::2], packed[b][1::2]
-        fn = (lambda b=b, kp=kp, vp=vp: stc.decode_step_batched(arrays[b], kmap, vmap, n - 1, kn, vn, kp, vp, q,
-                                                                ws=ws, out=attn_out[b]))
-        for _ in range(3):
-            fn()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for _ in range(args.steps):
-            fn()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        step_us[f"decode_step@{b}"] = round(1e3 * e0.elapsed_time(e1) / args.steps, 2)
-
-    # (4) one attention step over the Walsh-Hadamard caches of the same layer
-    rk, rv = rpacked[0::2], rpacked[1::2]
-    rkn, rvn = rnorms[0::2], rnorms[1::2]
-    rht_out = torch.empty((heads, g, 128), dtype=torch.float32, device=dev)
-    rfn = lambda: stc.attend_rht_batched(rht_arr, kmap, vmap, rk, rkn, rv, rvn, n, q, ws=ws, out=rht_out)
-    for _ in range(3):
-        rfn()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for _ in range(args.steps):
-        rfn()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    step_us["attend_rht"] = round(1e3 * e0.elapsed_time(e1) / args.steps, 2)
-
-    # (5) the key residual sketch on the same layer: sketch encode of the 8 K
-    # streams, then attention with the score correction
-    sk_states = []
-    for s_ in range(S):
-        sg = synth.random_signs(3, 0, 0, s_ // 2, s_ % 2)
-        sk_states.append(stc.rht_sketch_state_init(sg, cb32, synth.sketch_matrix(3, 0, 0, s_ // 2, 0))
-                         if s_ % 2 == 0 else stc.rht_state_init(sg, cb32))
-    sk_arr = stc.StateArray(sk_states)
-    kx3 = x3[0::2]
-    sk_packed = torch.empty((S, stc.packed_bytes(384, n)), dtype=torch.uint8, device=dev)[0::2]  # V's strides
-    sk_norms = torch.empty((S, n), dtype=torch.float32, device=dev)[0::2]
-    sk_bits = torch.empty((heads, stc.packed_bytes(128, n)), dtype=torch.uint8, device=dev)
-    sk_rn = torch.empty((heads, n), dtype=torch.float32, device=dev)
-    kmap_sk = torch.arange(0, S, 2, dtype=torch.int32, device=dev)
-    sfn = lambda: stc.append_rht_sketch_batched(sk_arr, kx3, 0, sk_packed, sk_norms, sk_bits, sk_rn,
-                                                state_of_stream=kmap_sk)
-    afn = lambda: stc.attend_rht_batched(sk_arr, kmap, vmap, sk_packed, sk_norms, rv, rvn, n, q, ws=ws,
-                                         out=rht_out, k_sketch=sk_bits, k_rnorm=sk_rn)
-    for name, fn in (("rht_sketch_encode_K", sfn), ("attend_rht_sketch", afn)):
-        for _ in range(3):
-            fn()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for _ in range(args.steps):
-            fn()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        step_us[name] = round(1e3 * e0.elapsed_time(e1) / args.steps, 2)
-
-    # (6) cold caches: each op of the step once more, after 1 GiB of writes
-    # has pushed the L2s and the 256 MiB memory-side cache out
-    scratch = torch.empty(1 << 28, dtype=torch.float32, device=dev)
-    cold = {}
-    for name, fn, nbytes in ops:
-        ms = []
-        for _ in range(3):
-            scratch.fill_(1.0)
+    step_us, cold = {}, {}
+    if not args.no_extras:
+        # (3) one generation step per budget (append the last token's K and V to
+        # every KV head, then attend over all n): it rewrites record n - 1 with
+        # the same codes, so the caches stay as they are
+        kn = x2[0::2, n - 1].contiguous()
+        vn = x2[1::2, n - 1].contiguous()
+        for b in budgets:
+            kp, vp = packed[b][0::2], packed[b][1::2]
+            fn = (lambda b=b, kp=kp, vp=vp: stc.decode_step_batched(arrays[b], kmap, vmap, n - 1, kn, vn, kp, vp, q,
+                                                                    ws=ws, out=attn_out[b]))
+            for _ in range(3):
+                fn()
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
             e0.record(stream)
-            fn()
+            for _ in range(args.steps):
+                fn()
             e1.record(stream)
             torch.cuda.synchronize()
-            ms.append(e0.elapsed_time(e1))
-        cold[name] = {"us": round(1e3 * min(ms), 2),
-                      "pct_hbm_peak": round(100.0 * nbytes / (min(ms) * 1e-3) / 1e9 / HBM_PEAK_GBPS, 1)}
-    del scratch
+            step_us[f"decode_step@{b}"] = round(1e3 * e0.elapsed_time(e1) / args.steps, 2)
+
+        # (4) one attention step over the Walsh-Hadamard caches of the same layer
+        rk, rv = rpacked[0::2], rpacked[1::2]
+        rkn, rvn = rnorms[0::2], rnorms[1::2]
+        rht_out = torch.empty((heads, g, 128), dtype=torch.float32, device=dev)
+        rfn = lambda: stc.attend_rht_batched(rht_arr, kmap, vmap, rk, rkn, rv, rvn, n, q, ws=ws, out=rht_out)
+        for _ in range(3):
+            rfn()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(args.steps):
+            rfn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        step_us["attend_rht"] = round(1e3 * e0.elapsed_time(e1) / args.steps, 2)
+
+        # (5) the key residual sketch on the same layer: sketch encode of the 8 K
+        # streams, then attention with the score correction
+        sk_states = []
+        for s_ in range(S):
+            sg = synth.random_signs(3, 0, 0, s_ // 2, s_ % 2)
+            sk_states.append(stc.rht_sketch_state_init(sg, cb32, synth.sketch_matrix(3, 0, 0, s_ // 2, 0))
+                             if s_ % 2 == 0 else stc.rht_state_init(sg, cb32))
+        sk_arr = stc.StateArray(sk_states)
+        kx3 = x3[0::2]
+        sk_packed = torch.empty((S, stc.packed_bytes(384, n)), dtype=torch.uint8, device=dev)[0::2]  # V's strides
+        sk_norms = torch.empty((S, n), dtype=torch.float32, device=dev)[0::2]
+        sk_bits = torch.empty((heads, stc.packed_bytes(128, n)), dtype=torch.uint8, device=dev)
+        sk_rn = torch.empty((heads, n), dtype=torch.float32, device=dev)
+        kmap_sk = torch.arange(0, S, 2, dtype=torch.int32, device=dev)
+        sfn = lambda: stc.append_rht_sketch_batched(sk_arr, kx3, 0, sk_packed, sk_norms, sk_bits, sk_rn,
+                                                    state_of_stream=kmap_sk)
+        afn = lambda: stc.attend_rht_batched(sk_arr, kmap, vmap, sk_packed, sk_norms, rv, rvn, n, q, ws=ws,
+                                             out=rht_out, k_sketch=sk_bits, k_rnorm=sk_rn)
+        for name, fn in (("rht_sketch_encode_K", sfn), ("attend_rht_sketch", afn)):
+            for _ in range(3):
+                fn()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(args.steps):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            step_us[name] = round(1e3 * e0.elapsed_time(e1) / args.steps, 2)
+
+        # (6) cold caches: each op of the step once more, after 1 GiB of writes
+        # has pushed the L2s and the 256 MiB memory-side cache out
+        scratch = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        for name, fn, nbytes in ops:
+            ms = []
+            for _ in range(3):
+                scratch.fill_(1.0)
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                fn()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                ms.append(e0.elapsed_time(e1))
+            cold[name] = {"us": round(1e3 * min(ms), 2),
+                          "pct_hbm_peak": round(100.0 * nbytes / (min(ms) * 1e-3) / 1e9 / HBM_PEAK_GBPS, 1)}
+        del scratch
 
     per_op = {}
     for i, (name, _, nbytes) in enumerate(ops):
