@@ -316,11 +316,71 @@ __global__ void __launch_bounds__(ENC_THREADS, 1) k_encode_eigen(EncK a) {
         const lds_u8* pL = lds_ptr(pb);
         const bool tok_ok = tok0 + t32 >= n0 && tok0 + t32 < n;
         const unsigned tB = (unsigned)t32 * B;
+        // ---- 3: OR a group word into the stream at record bit tB + goff; a
+        // lane whose token is outside the call ORs zero (no branch, so that
+        // this work can overlap the next row block's MFMA chain)
+        auto put_group = [&](unsigned word, unsigned goff) {
+          const unsigned P = tB + goff;
+          const unsigned long long v = (unsigned long long)(tok_ok ? word : 0u) << (P & 31u);
+          unsigned* dst = sStr + est_idx(P >> 5);
+          __hip_atomic_fetch_or(dst, (unsigned)v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+          __hip_atomic_fetch_or(dst + 1, (unsigned)(v >> 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        };
+        if (MODE != 2) {
+          // ---- 1: channels 64h + 16mb + 4i + j of token t in acc[4i + j].
+          // The chain starts from yhalf_j, so that it ends on the cell
+          // coordinate x.U_j yscale_j + yhalf_j itself.
+          auto chain_init = [&](const int mb, f32x16& acc) {
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb) {
-          // ---- 1: channels 64h + 16mb + 4i + j of token t in acc[4i + j]
-          f32x16 acc;
-          if (MODE == 2) {
+            for (int i = 0; i < 4; ++i) {
+              const f32x4 yh = LDS_AT(f32x4, pL + 4 * (16 * mb + 4 * i));
+#pragma unroll
+              for (int j = 0; j < 4; ++j) acc[4 * i + j] = yh[j];
+            }
+          };
+          auto chain_step = [&](const int mb, const int ks, f32x16& acc) {
+            const int off = 32 * mb * UROW + 32 * ks;
+            const bf16x8 ah = LDS_AT(bf16x8, uL + off);
+            const bf16x8 al = LDS_AT(bf16x8, uL + 128 * UROW + off);
+            acc = mfma32_bf16(ah, xh[ks], acc);
+            acc = mfma32_bf16(al, xh[ks], acc);
+            if (MODE == 1) acc = mfma32_bf16(ah, xl[ks], acc);
+          };
+          // ---- 2: the code is floor(acc) clamped to [0, L-1], per group of
+          // four channels
+          auto quant_group = [&](const int mb, const int i, const f32x16& acc) {
+            const int coff = 4 * (16 * mb + 4 * i);  // byte offset of the group in a table
+            const f32x4 lm = LDS_AT(f32x4, pL + 512 + coff);
+            const u32x4 pos = LDS_AT(u32x4, pL + 1024 + coff);
+            const unsigned goff = LDS_AT(unsigned, pL + 1536 + coff);
+            unsigned q[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) q[j] = (unsigned)__builtin_amdgcn_fmed3f(acc[4 * i + j], 0.0f, lm[j]);
+            put_group(q[0] | (q[1] << pos[1]) | (q[2] << pos[2]) | (q[3] << pos[3]), goff);
+          };
+          // Two accumulators, interleaved in program order: while the chain
+          // of row block mb + 1 runs on the MFMA unit, row block mb is
+          // quantized (one group of four channels per two steps).
+          f32x16 acc0, acc1;
+          chain_init(0, acc0);
+#pragma unroll
+          for (int ks = 0; ks < 8; ++ks) chain_step(0, ks, acc0);
+#pragma unroll
+          for (int mb = 0; mb < 4; ++mb) {
+            f32x16& cur = (mb & 1) ? acc1 : acc0;
+            f32x16& nxt = (mb & 1) ? acc0 : acc1;
+            if (mb < 3) chain_init(mb + 1, nxt);
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks) {
+              if (mb < 3) chain_step(mb + 1, ks, nxt);
+              if (ks & 1) quant_group(mb, ks >> 1, cur);
+            }
+          }
+        } else {
+#pragma unroll
+          for (int mb = 0; mb < 4; ++mb) {
+            // ---- 1: latent coefficients of channels 64h + 16mb + 4i + j
+            f32x16 acc;
             const float* cf = static_cast<const float*>(a.x) + (rbase + trow) * 128 + 64 * h + 16 * mb;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -328,36 +388,11 @@ __global__ void __launch_bounds__(ENC_THREADS, 1) k_encode_eigen(EncK a) {
 #pragma unroll
               for (int j = 0; j < 4; ++j) acc[4 * i + j] = v[j];
             }
-          } else {
+            // ---- 2: per group of four channels
 #pragma unroll
-            for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
-#pragma unroll
-            for (int ks = 0; ks < 8; ++ks) {
-              const int off = 32 * mb * UROW + 32 * ks;
-              const bf16x8 ah = LDS_AT(bf16x8, uL + off);
-              const bf16x8 al = LDS_AT(bf16x8, uL + 128 * UROW + off);
-              acc = mfma32_bf16(ah, xh[ks], acc);
-              acc = mfma32_bf16(al, xh[ks], acc);
-              if (MODE == 1) acc = mfma32_bf16(ah, xl[ks], acc);
-            }
-          }
-          // ---- 2 + 3 per group of four channels
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int coff = 4 * (16 * mb + 4 * i);  // byte offset of the group in a table
-            unsigned q[4];
-            u32x4 pos;
-            unsigned goff;
-            if (MODE != 2) {
-              // acc = coordinate in quantizer cells (scaled basis rows):
-              // the code is floor(acc + L/2) clamped to [0, L-1]
-              const f32x4 yh = LDS_AT(f32x4, pL + coff);
-              const f32x4 lm = LDS_AT(f32x4, pL + 512 + coff);
-              pos = LDS_AT(u32x4, pL + 1024 + coff);
-              goff = LDS_AT(unsigned, pL + 1536 + coff);
-#pragma unroll
-              for (int j = 0; j < 4; ++j) q[j] = (unsigned)__builtin_amdgcn_fmed3f(acc[4 * i + j] + yh[j], 0.0f, lm[j]);
-            } else {
+            for (int i = 0; i < 4; ++i) {
+              const int coff = 4 * (16 * mb + 4 * i);  // byte offset of the group in a table
+              unsigned q[4];
               // y = c/step + L/2 + eps_L; outside the guard band next to an
               // integer, floor(y) clamped to [0, L-1] is the exact threshold
               // count; inside it, or for NaN or a zero step, the fp32
@@ -365,11 +400,11 @@ __global__ void __launch_bounds__(ENC_THREADS, 1) k_encode_eigen(EncK a) {
               const f32x4 inv = LDS_AT(f32x4, pL + coff);
               const f32x4 yb = LDS_AT(f32x4, pL + 512 + coff);
               const f32x4 lm = LDS_AT(f32x4, pL + 1024 + coff);
-              pos = LDS_AT(u32x4, pL + 1536 + coff);
+              const u32x4 pos = LDS_AT(u32x4, pL + 1536 + coff);
               const f32x4 band = LDS_AT(f32x4, pL + 2048 + coff);
-              goff = LDS_AT(unsigned, pL + 2560 + coff);
+              const unsigned goff = LDS_AT(unsigned, pL + 2560 + coff);
               bool need = false;
-  #pragma unroll
+#pragma unroll
               for (int j = 0; j < 4; ++j) {
                 const float y = __builtin_fmaf(acc[4 * i + j], inv[j], yb[j]);
                 q[j] = (unsigned)__builtin_amdgcn_fmed3f(y, 0.0f, lm[j]);
@@ -380,7 +415,7 @@ __global__ void __launch_bounds__(ENC_THREADS, 1) k_encode_eigen(EncK a) {
                 // k = 1..L-1, rebuilt here from the fp64 step exactly as the
                 // state builder forms them; the fast result is off by at most
                 // one level
-  #pragma unroll
+#pragma unroll
                 for (int j = 0; j < 4; ++j) {
                   const float c = acc[4 * i + j];
                   const float y = __builtin_fmaf(c, inv[j], yb[j]);
@@ -402,14 +437,7 @@ __global__ void __launch_bounds__(ENC_THREADS, 1) k_encode_eigen(EncK a) {
                   }
                 }
               }
-            }
-            const unsigned word = q[0] | (q[1] << pos[1]) | (q[2] << pos[2]) | (q[3] << pos[3]);
-            if (tok_ok) {
-              const unsigned P = tB + goff;  // record bit of the group
-              const unsigned long long v = (unsigned long long)word << (P & 31u);
-              unsigned* dst = sStr + est_idx(P >> 5);
-              __hip_atomic_fetch_or(dst, (unsigned)v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-              __hip_atomic_fetch_or(dst + 1, (unsigned)(v >> 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+              put_group(q[0] | (q[1] << pos[1]) | (q[2] << pos[2]) | (q[3] << pos[3]), goff);
             }
           }
         }
@@ -502,9 +530,13 @@ __global__ void __launch_bounds__(64 * SKE_WAVES, 2) k_sketch_eigen(EncK a) {
     float ee = 0.0f;
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
-      f32x16 acc;
+      f32x16 acc;  // from yhalf, as the encode accumulates
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
+      for (int i = 0; i < 4; ++i) {
+        const f32x4 yh = LDS_AT(f32x4, tL + 4 * (16 * mb + 4 * i));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[4 * i + j] = yh[j];
+      }
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
         const int off = 32 * mb * UROW + 32 * ks;
@@ -514,13 +546,12 @@ __global__ void __launch_bounds__(64 * SKE_WAVES, 2) k_sketch_eigen(EncK a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int coff = 4 * (16 * mb + 4 * i);
-        const f32x4 yh = LDS_AT(f32x4, tL + coff);
         const f32x4 lm = LDS_AT(f32x4, tL + 512 + coff);
         const f32x4 stp = LDS_AT(f32x4, tL + 1024 + coff);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int e = 4 * i + j;
-          const float y = acc[e] + yh[j];
+          const float y = acc[e];
           const float q = (float)(unsigned)__builtin_amdgcn_fmed3f(y, 0.0f, lm[j]);
           const float rv = stp[j] == 0.0f ? 0.0f : stp[j] * (y - q - 0.5f);
           ee = __builtin_fmaf(rv, rv, ee);
