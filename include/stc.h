@@ -107,11 +107,10 @@ typedef struct {
 size_t stc_state_bytes(void);
 /* ceil(n_tokens * total_bits / 8) rounded up to a multiple of 16 (format F1). */
 size_t stc_packed_bytes(int32_t total_bits, int64_t n_tokens);
-/* Workspace of stc_attend_compressed_batched: a 64 KiB area of per-KV-head
- * completion counters followed by the per-split partial results. The
- * workspace must be zero-filled before its first use; every call leaves the
- * counters at zero again, so it can be reused by later calls of any shape
- * (not by calls that run at the same time). */
+/* Workspace of stc_attend_compressed_batched: the per-split partial results
+ * (written by one kernel, merged by the next). It needs no initialisation
+ * and can be reused by later calls of any shape in stream order (not by
+ * calls that run at the same time). */
 size_t stc_attend_workspace_bytes(int64_t n_pairs, int32_t group, int64_t n_tokens);
 
 /* ------------------------------------------------------- host math
@@ -317,8 +316,8 @@ stc_status stc_quantize_pack_f32(const stc_head_info* info, const void* state_de
  * of the packed codes (never materialised: scores are taken in the latent
  * basis and the weighted code average is rotated back once). q_dev, out_dev:
  * fp32 [n_pairs][group][128]. EIGEN/IDENTITY states only. ws_dev: at least
- * stc_attend_workspace_bytes(n_pairs, group, n_tokens) bytes, 256-aligned,
- * zero-filled before its first use (see stc_attend_workspace_bytes). */
+ * stc_attend_workspace_bytes(n_pairs, group, n_tokens) bytes, 256-aligned
+ * (see stc_attend_workspace_bytes). */
 stc_status stc_attend_compressed_batched(const void* states_dev, int64_t n_states,
                                          const int32_t* k_state_of_pair_dev,
                                          const int32_t* v_state_of_pair_dev,

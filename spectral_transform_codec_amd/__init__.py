@@ -310,7 +310,7 @@ def attend_rht_batched(states: StateArray, k_state_of_pair: torch.Tensor, v_stat
         out = torch.empty((Pn, g, D), dtype=torch.float32, device=q.device)
     need = attend_workspace_bytes(Pn, g, n)
     if ws is None or ws.numel() < need:
-        ws = torch.zeros(need, dtype=torch.uint8, device=q.device)  # zero-filled once
+        ws = torch.empty(need, dtype=torch.uint8, device=q.device)
     check("stc_attend_rht_batched", lib().stc_attend_rht_batched(
         _ptr(states.blob), states.n, _ptr(_map_arg(k_state_of_pair)), _ptr(_map_arg(v_state_of_pair)),
         states.infos, Pn, n, _ptr(k_packed), _ptr(k_norms), _ptr(v_packed), _ptr(v_norms), k_packed.stride(0),
@@ -336,7 +336,7 @@ def decode_step_batched(states: StateArray, k_state_of_pair: torch.Tensor, v_sta
         out = torch.empty((Pn, g, D), dtype=torch.float32, device=q.device)
     need = attend_workspace_bytes(Pn, g, n_old + 1)
     if ws is None or ws.numel() < need:
-        ws = torch.zeros(need, dtype=torch.uint8, device=q.device)  # zero-filled once
+        ws = torch.empty(need, dtype=torch.uint8, device=q.device)
     check("stc_decode_step_batched", lib().stc_decode_step_batched(
         _ptr(states.blob), states.n, _ptr(_map_arg(k_state_of_pair)), _ptr(_map_arg(v_state_of_pair)),
         states.infos, Pn, n_old, _ptr(k_new), _ptr(v_new), _dtype_code(k_new), _ptr(k_packed), _ptr(v_packed),
@@ -385,7 +385,7 @@ def attend_compressed_sketch_batched(states: StateArray, k_state_of_pair: torch.
         out = torch.empty((Pn, g, D), dtype=torch.float32, device=q.device)
     need = attend_workspace_bytes(Pn, g, n)
     if ws is None or ws.numel() < need:
-        ws = torch.zeros(need, dtype=torch.uint8, device=q.device)  # zero-filled once
+        ws = torch.empty(need, dtype=torch.uint8, device=q.device)
     check("stc_attend_compressed_sketch_batched", lib().stc_attend_compressed_sketch_batched(
         _ptr(states.blob), states.n, _ptr(_map_arg(k_state_of_pair)), _ptr(_map_arg(v_state_of_pair)),
         states.infos, Pn, n, _ptr(k_packed), _ptr(v_packed), k_packed.stride(0), _ptr(k_sketch), _ptr(k_rnorm),
@@ -416,7 +416,7 @@ def attend_compressed(k_state: State, v_state: State, k_packed: torch.Tensor, v_
     out = torch.empty((g, D), dtype=torch.float32, device=q.device)
     need = attend_workspace_bytes(1, g, n)
     if ws is None or ws.numel() < need:
-        ws = torch.zeros(need, dtype=torch.uint8, device=q.device)  # zero-filled once
+        ws = torch.empty(need, dtype=torch.uint8, device=q.device)
     check("stc_attend_compressed", lib().stc_attend_compressed(
         ctypes.byref(k_state.info), _ptr(k_state.blob), ctypes.byref(v_state.info), _ptr(v_state.blob), n,
         _ptr(k_packed), _ptr(v_packed), g, _ptr(q), _ptr(out), float(scale), _ptr(ws), ws.numel(), _stream()))
@@ -435,7 +435,7 @@ def attend_compressed_batched(states: StateArray, k_state_of_pair: torch.Tensor,
         out = torch.empty((Pn, g, D), dtype=torch.float32, device=q.device)
     need = attend_workspace_bytes(Pn, g, n)
     if ws is None or ws.numel() < need:
-        ws = torch.zeros(need, dtype=torch.uint8, device=q.device)  # zero-filled once
+        ws = torch.empty(need, dtype=torch.uint8, device=q.device)
     check("stc_attend_compressed_batched", lib().stc_attend_compressed_batched(
         _ptr(states.blob), states.n, _ptr(_map_arg(k_state_of_pair)), _ptr(_map_arg(v_state_of_pair)),
         states.infos, Pn, n, _ptr(k_packed), _ptr(v_packed), k_packed.stride(0), g, _ptr(q), _ptr(out),

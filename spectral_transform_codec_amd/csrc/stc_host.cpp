@@ -363,7 +363,7 @@ size_t stc_attend_workspace_bytes(int64_t n_pairs, int32_t group, int64_t n_toke
   const int64_t np = n_pairs < ATT_MAX_PAIRS ? n_pairs : ATT_MAX_PAIRS;
   const int64_t splits = att_n_splits(np, n_tokens);
   size_t parts = (size_t)np * splits * att_part_stride(group) * sizeof(float);
-  return ATT_CNT_BYTES + (parts + 255) / 256 * 256;
+  return (parts + 255) / 256 * 256;
 }
 
 int32_t stc_total_bits(float avg_bits, int32_t d) {

@@ -117,11 +117,9 @@ constexpr int ATT_PART_FLOATS = D + 2;              // per (pair, split, head): 
 __host__ __device__ inline int64_t att_part_stride(int group) {
   return ((int64_t)group * ATT_PART_FLOATS + 31) / 32 * 32;
 }
-// Attention workspace: a per-pair completion counter in a fixed area at the
-// front (zero before the first call, left at zero by every call), then the
-// split partials. A launch covers at most ATT_MAX_PAIRS pairs.
-constexpr size_t ATT_CNT_BYTES = 64 * 1024;
-constexpr int64_t ATT_MAX_PAIRS = (int64_t)(ATT_CNT_BYTES / 4);
+// Attention workspace: the split partials of one launch, which covers at
+// most ATT_MAX_PAIRS pairs (launches of one call reuse it in stream order).
+constexpr int64_t ATT_MAX_PAIRS = 16384;
 
 // Host-side launchers implemented in stc_kernels.hip.
 struct EncodeLaunch {

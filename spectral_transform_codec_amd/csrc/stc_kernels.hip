@@ -1357,8 +1357,9 @@ int launch_decode_rht(const DecodeLaunch& L, void* stream) {
 //   against the K codes), online softmax, P (fp16) x V codes (fp16) on MFMA
 //   with the V codes byte-transposed into a [channel][token] buffer. At the
 //   end the waves' (acc, m, l) are merged into the split's partial.
-//  k_att_combine: one workgroup per pair: merge splits, dequantize, rotate
-//   back.
+//  k_att_combine (the next launch on the stream, so every split's partial
+//   is in memory): one workgroup per (pair, query head): merge the splits,
+//   dequantize, rotate back.
 // ======================================================================
 struct AttK {
   const unsigned char* k_states;
@@ -1485,99 +1486,6 @@ __device__ __forceinline__ unsigned att_group_bytes(const unsigned* str, const l
   return v;
 }
 
-// Run by the last workgroup of a pair to finish: merge the splits' (acc,
-// m, l) of every query head with log-sum-exp weights (fp32 weights, fp64
-// sums), take the softmax-weighted mean code of every V channel, dequantize
-// it and rotate back with U_V (staged in LDS, rows padded to 129 floats).
-// One thread per (head, channel) reads every split's m, l and acc of its
-// item in batches of 32, all loads of a batch in flight together.
-// `cs` is LDS of at least att_combine_lds_bytes(); 512 or 1024 threads.
-constexpr int CMB_UROW = 129;
-constexpr int CMB_BATCH = 32;
-__host__ __device__ constexpr size_t att_combine_lds_bytes() { return (size_t)(128 * CMB_UROW + 16 * 128) * 4; }
-__device__ __forceinline__ void att_combine_pair(const AttK& a, long long p, float* cs) {
-  const long long pg = a.pair_base + p;
-  const int nt = (int)blockDim.x;
-  const int t = threadIdx.x;
-  const int g = a.group;
-  const int S = (int)a.n_splits;
-  const long long PS = att_part_stride(g);
-  float* sU = cs;                  // [128][129]
-  float* sC = sU + 128 * CMB_UROW;  // dequantized mean codes [head][128]
-  const float* ps0 = reinterpret_cast<const float*>(a.ws + ATT_CNT_BYTES) + p * (long long)S * PS;
-  const unsigned char* vst = a.v_states + (size_t)state_index(a.v_map, pg, a.n_states) * STATE_BYTES;
-  const DevHdr* hv = reinterpret_cast<const DevHdr*>(vst);
-  const f32x4* u4 = reinterpret_cast<const f32x4*>(vst + OFF_U32);
-  {
-    f32x4 uv[8];  // 4096 float4 over 512 or 1024 threads, loads first
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const int e4 = t + r * nt;
-      uv[r] = u4[e4 < 4096 ? e4 : 4095];
-    }
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const int e4 = t + r * nt;
-      if (e4 < 4096) {
-        const int row = e4 >> 5, col = 4 * (e4 & 31);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) sU[row * CMB_UROW + col + c] = uv[r][c];
-      }
-    }
-  }
-  for (int it = t; it < g * 128; it += nt) {
-    const int hh = it >> 7, j = it & 127;
-    const float* ph = ps0 + hh * ATT_PART_FLOATS;
-    const unsigned bits = hv->bits[j];
-    const float step = hv->step32[j], hs = hv->halfspan[j];
-    float M = -INFINITY;
-    double A = 0.0, L = 0.0;
-    for (int s0 = 0; s0 < S; s0 += CMB_BATCH) {
-      float mv[CMB_BATCH], lv[CMB_BATCH], av[CMB_BATCH];
-#pragma unroll
-      for (int r = 0; r < CMB_BATCH; ++r) {
-        const long long s2 = s0 + r < S ? s0 + r : S - 1;
-        mv[r] = ph[s2 * PS + 128];
-        lv[r] = ph[s2 * PS + 129];
-        av[r] = ph[s2 * PS + j];
-      }
-      float Mc = M;
-#pragma unroll
-      for (int r = 0; r < CMB_BATCH; ++r) Mc = fmaxf(Mc, mv[r]);  // clamped repeats change no maximum
-      if (Mc != -INFINITY) {
-        if (M != -INFINITY && M != Mc) {
-          const double sc = (double)exp2f(M - Mc);
-          A *= sc;
-          L *= sc;
-        }
-#pragma unroll
-        for (int r = 0; r < CMB_BATCH; ++r) {
-          const float f = (s0 + r < S && mv[r] != -INFINITY) ? exp2f(mv[r] - Mc) : 0.0f;
-          A += (double)(f * av[r]);
-          L += (double)(f * lv[r]);
-        }
-        M = Mc;
-      }
-    }
-    // dequantize the mean code: step * (A / L - (L_j - 1)/2)
-    sC[hh * 128 + j] = bits ? (float)((double)step * (A / L - (double)hs)) : 0.0f;
-  }
-  __syncthreads();
-  // rotate back: o_i = sum_k U_ik chat_k
-  for (int hi = t; hi < g * 128; hi += nt) {
-    const int hh = hi >> 7, i = hi & 127;
-    const f32x4* c4 = reinterpret_cast<const f32x4*>(sC + hh * 128);
-    const float* ur = sU + i * CMB_UROW;
-    float o = 0.0f;
-#pragma unroll 8
-    for (int k4 = 0; k4 < 32; ++k4) {
-      const f32x4 c = c4[k4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) o = __builtin_fmaf(ur[4 * k4 + e], c[e], o);
-    }
-    a.out[(pg * g + hh) * 128 + i] = o;
-  }
-}
 
 // RHT: a Walsh-Hadamard cache. Its state stores U = D H / sqrt(d) with unit
 // steps, so the score table and the split merge are the eigen ones; the
@@ -1588,6 +1496,96 @@ __device__ __forceinline__ void att_combine_pair(const AttK& a, long long p, flo
 // SKETCH (RHT only): keys carry the 1-bit residual sketch; a second table
 // holds S q scale log2(e) sqrt(pi/2)/m (hi / lo) and each score gains
 // |r_t| times its product with the token's signs, one more MFMA chain.
+// k_att_combine: one workgroup per (pair, query head), after k_att_main has
+// written every split's partial. Thread j merges the splits' (acc_j, m, l)
+// with log-sum-exp weights (fp32 weights, fp64 sums, batches of 32 splits
+// with all loads in flight) and dequantizes the mean code of V channel j;
+// meanwhile U_V is staged in LDS (rows padded to 129 floats); then thread i
+// rotates back: o_i = sum_k U_ik chat_k.
+constexpr int CMB_THREADS = 128;
+constexpr int CMB_UROW = 129;
+constexpr int CMB_BATCH = 32;
+constexpr size_t CMB_LDS = (size_t)(128 * CMB_UROW + 128) * 4;
+
+__global__ void __launch_bounds__(CMB_THREADS) k_att_combine(AttK a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  float* sU = reinterpret_cast<float*>(smem);  // [128][129]
+  float* sC = sU + 128 * CMB_UROW;             // dequantized mean codes
+  const long long p = blockIdx.x;
+  const int hh = blockIdx.y;
+  const long long pg = a.pair_base + p;
+  const int t = threadIdx.x;
+  const int g = a.group;
+  const int S = (int)a.n_splits;
+  const long long PS = att_part_stride(g);
+  const unsigned char* vst = a.v_states + (size_t)state_index(a.v_map, pg, a.n_states) * STATE_BYTES;
+  const DevHdr* hv = reinterpret_cast<const DevHdr*>(vst);
+  const f32x4* u4 = reinterpret_cast<const f32x4*>(vst + OFF_U32);
+  const float* ph = reinterpret_cast<const float*>(a.ws) + p * (long long)S * PS + hh * ATT_PART_FLOATS;
+  const int j = t;
+  const unsigned bits = hv->bits[j];
+  const float step = hv->step32[j], hs = hv->halfspan[j];
+  float M = -INFINITY;
+  double A = 0.0, L = 0.0;
+  for (int s0 = 0; s0 < S; s0 += CMB_BATCH) {
+    float mv[CMB_BATCH], lv[CMB_BATCH], av[CMB_BATCH];
+#pragma unroll
+    for (int r = 0; r < CMB_BATCH; ++r) {
+      const long long s2 = s0 + r < S ? s0 + r : S - 1;
+      mv[r] = ph[s2 * PS + 128];
+      lv[r] = ph[s2 * PS + 129];
+      av[r] = ph[s2 * PS + j];
+    }
+    if (s0 == 0) {
+      // U_V -> LDS: 4096 float4, 32 per thread, in four batches of 8
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        f32x4 uv[8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) uv[r] = u4[t + (8 * b + r) * CMB_THREADS];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          const int e4 = t + (8 * b + r) * CMB_THREADS;
+          const int row = e4 >> 5, col = 4 * (e4 & 31);
+#pragma unroll
+          for (int c = 0; c < 4; ++c) sU[row * CMB_UROW + col + c] = uv[r][c];
+        }
+      }
+    }
+    float Mc = M;
+#pragma unroll
+    for (int r = 0; r < CMB_BATCH; ++r) Mc = fmaxf(Mc, mv[r]);  // clamped repeats change no maximum
+    if (Mc != -INFINITY) {
+      if (M != -INFINITY && M != Mc) {
+        const double sc = (double)exp2f(M - Mc);
+        A *= sc;
+        L *= sc;
+      }
+#pragma unroll
+      for (int r = 0; r < CMB_BATCH; ++r) {
+        const float f = (s0 + r < S && mv[r] != -INFINITY) ? exp2f(mv[r] - Mc) : 0.0f;
+        A += (double)(f * av[r]);
+        L += (double)(f * lv[r]);
+      }
+      M = Mc;
+    }
+  }
+  // dequantize the mean code: step * (A / L - (L_j - 1)/2)
+  sC[j] = bits ? (float)((double)step * (A / L - (double)hs)) : 0.0f;
+  __syncthreads();
+  const int i = t;
+  const f32x4* c4 = reinterpret_cast<const f32x4*>(sC);
+  const float* ur = sU + i * CMB_UROW;
+  float o = 0.0f;
+#pragma unroll 8
+  for (int k4 = 0; k4 < 32; ++k4) {
+    const f32x4 c = c4[k4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o = __builtin_fmaf(ur[4 * k4 + e], c[e], o);
+  }
+  a.out[(pg * g + hh) * 128 + i] = o;
+}
+
 template <int NW, bool RHT, bool SKETCH>
 __global__ void __launch_bounds__(ATT_THREADS, 1) k_att_main(AttK a) {
   extern __shared__ __align__(16) unsigned char smem[];
@@ -1906,7 +1904,7 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_att_main(AttK a) {
   // ---- merge the waves, four heads at a time: scratch [wave][4][130]
   __syncthreads();
   float* red = reinterpret_cast<float*>(sReg0);
-  float* part = reinterpret_cast<float*>(a.ws + ATT_CNT_BYTES) + (p * a.n_splits + sp) * att_part_stride(g);
+  float* part = reinterpret_cast<float*>(a.ws) + (p * a.n_splits + sp) * att_part_stride(g);
   for (int c4 = 0; c4 * 4 < g; ++c4) {
     float* mine = red + wave * 4 * ATT_PART_FLOATS;
     // m, l of heads 4*c4 .. +3: H = 8i + 4h + j
@@ -1943,33 +1941,7 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_att_main(AttK a) {
       ph[jj] = A;
       if (jj == 0) { ph[128] = M; ph[129] = Ls; }
     }
-    __syncthreads();
-  }
-  // ---- the last split of the pair to finish merges all of them. Every
-  // wave waits until its partial stores have reached L2; after the barrier
-  // thread 0 releases them with the pair's count (one L2 write-back per
-  // workgroup) and, in the last workgroup only, acquires the other splits'
-  // (one invalidate, complete before the barrier that the merge follows).
-  // The counter of the pair is left at zero for the next call.
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  unsigned* cnt = reinterpret_cast<unsigned*>(a.ws) + p;
-  unsigned* flag = reinterpret_cast<unsigned*>(smem);
-  if (tid == 0) {
-    const unsigned prev = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-    const unsigned is_last = prev == (unsigned)(a.n_splits - 1) ? 1u : 0u;
-    if (is_last) {
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    }
-    *flag = is_last;
-  }
-  __syncthreads();
-  const unsigned last = *flag;
-  __syncthreads();  // read by every thread before the merge below reuses the LDS
-  if (last) {
-    att_combine_pair(a, p, reinterpret_cast<float*>(smem));
-    if (tid == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (4 * (c4 + 1) < g) __syncthreads();
   }
 }
 
@@ -1986,7 +1958,9 @@ int launch_attend(const AttendLaunch& L, void* stream) {
         hipFuncSetAttribute((const void*)k_att_main<8, false, true>, hipFuncAttributeMaxDynamicSharedMemorySize,
                             160 * 1024) != hipSuccess ||
         hipFuncSetAttribute((const void*)k_att_main<16, false, true>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            160 * 1024) != hipSuccess)
+                            160 * 1024) != hipSuccess ||
+        hipFuncSetAttribute((const void*)k_att_combine, hipFuncAttributeMaxDynamicSharedMemorySize, (int)CMB_LDS) !=
+            hipSuccess)
       return 1;
     g_att_attr_done = true;
   }
@@ -2026,9 +2000,7 @@ int launch_attend(const AttendLaunch& L, void* stream) {
     a.n_pairs = np;
     a.split_tokens = att_split_tokens(np, L.n_tokens);
     a.n_splits = att_n_splits(np, L.n_tokens);
-    size_t att_lds = fixed + (size_t)waves * a.region_words * 4;
-    const size_t cmb = att_combine_lds_bytes();
-    if (att_lds < cmb) att_lds = cmb;
+    const size_t att_lds = fixed + (size_t)waves * a.region_words * 4;
     const dim3 grid((unsigned)a.n_splits, (unsigned)np);
     if (sketch && L.rht)
       hipLaunchKernelGGL((k_att_main<8, true, true>), grid, dim3(64 * waves), att_lds, s, a);
@@ -2042,6 +2014,8 @@ int launch_attend(const AttendLaunch& L, void* stream) {
       hipLaunchKernelGGL((k_att_main<8, false, false>), grid, dim3(64 * waves), att_lds, s, a);
     else
       hipLaunchKernelGGL((k_att_main<16, false, false>), grid, dim3(64 * waves), att_lds, s, a);
+    // the splits' partials -> out, once every split has written its own
+    hipLaunchKernelGGL(k_att_combine, dim3((unsigned)np, (unsigned)L.group), dim3(CMB_THREADS), CMB_LDS, s, a);
   }
   return hipGetLastError() != hipSuccess;
 }
