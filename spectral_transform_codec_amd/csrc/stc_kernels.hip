@@ -1636,7 +1636,7 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_att_main(AttK a) {
     const int j = tid & 127, part = tid >> 7;
     const int nparts = (int)(blockDim.x >> 7);
     const float* qp = a.q + pg * g * 128;
-    const int rows = 128 / nparts;  // 16 (1024 threads) or 32 (512)
+    const int rows = (128 + nparts - 1) / nparts;  // rows per part: 16, 22 or 32 (1024, 768, 512 threads)
     for (int e = tid; e < 128 * 16; e += blockDim.x) {
       const int r = e >> 4, hh = e & 15;
       sqT[e] = hh < g ? qp[hh * 128 + r] : 0.0f;
@@ -1646,7 +1646,12 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_att_main(AttK a) {
     const float* u = reinterpret_cast<const float*>(kst + (tab == 0 ? OFF_U32 : OFF_SKT32));
     float ur[32];
 #pragma unroll
-    for (int k = 0; k < 32; ++k) ur[k] = k < rows ? u[(part + k * nparts) * 128 + j] : 0.0f;  // issued together
+    for (int k = 0; k < 32; ++k) {
+      // issued together: rows past the part's share load row 127 and count 0
+      const int row = part + k * nparts;
+      const float v = u[(row < 127 ? row : 127) * 128 + j];
+      ur[k] = (k < rows && row < 128) ? v : 0.0f;
+    }
     __syncthreads();
     float acc[16];
 #pragma unroll
@@ -1654,7 +1659,8 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_att_main(AttK a) {
 #pragma unroll
     for (int k = 0; k < 32; ++k) {
       if (k < rows) {
-        const f32x4* q4 = reinterpret_cast<const f32x4*>(sqT + (part + k * nparts) * 16);
+        const int row = part + k * nparts;
+        const f32x4* q4 = reinterpret_cast<const f32x4*>(sqT + (row < 127 ? row : 127) * 16);
 #pragma unroll
         for (int c4 = 0; c4 < 4; ++c4) {
           const f32x4 qv = q4[c4];
@@ -1992,7 +1998,8 @@ int launch_attend(const AttendLaunch& L, void* stream) {
   const bool sketch = L.k_sketch != nullptr;
   const size_t fixed = ATT_FIXED_BYTES + (sketch ? 32 * AROW : 0);
   int waves = ATT_WAVES_MAX;
-  while (waves > 4 && fixed + (size_t)waves * a.region_words * 4 > 160 * 1024) waves -= 4;
+  while (waves > 8 && fixed + (size_t)waves * a.region_words * 4 > 160 * 1024) waves -= 4;
+  if (fixed + (size_t)waves * a.region_words * 4 > 160 * 1024) return 1;  // (the a-table build needs >= 8 waves)
   hipStream_t s = (hipStream_t)stream;
   for (long long c0 = 0; c0 < L.n_pairs; c0 += ATT_MAX_PAIRS) {
     const long long np = L.n_pairs - c0 < ATT_MAX_PAIRS ? L.n_pairs - c0 : ATT_MAX_PAIRS;

@@ -195,6 +195,28 @@ def test_attention_matches_oracle(cfg, n, avg):
     assert rel_err(got, want) <= 2e-3, rel_err(got, want)
 
 
+@pytest.mark.parametrize("avg", [7.8, 8.0])
+def test_attention_wide_records_last_dims(avg):
+    """Records of 998 / 1024 bits leave room for 12 waves per workgroup only
+    (the a table is then built by 6 parts of 22 rows): a query that lives on
+    the last latent dimensions checks that every row of U_K is summed."""
+    w = synth.WORKLOADS[2]
+    n = 3000
+    k = synth.stream(w, 0, 0, 1, 0, n=n)
+    v = synth.stream(w, 0, 0, 1, 1, n=n)
+    ks, vs = codec.calibrate_head(k, 2048, avg), codec.calibrate_head(v, 2048, avg)
+    kp, vp = codec.encode_kv(ks, k), codec.encode_kv(vs, v)
+    rng = np.random.default_rng(5)
+    q = np.zeros((4, 128), np.float32)
+    q[:, 120:] = rng.standard_normal((4, 8)).astype(np.float32) * 3.0
+    q = (q + 0.01 * rng.standard_normal((4, 128))).astype(np.float32)
+    qr = (q.astype(np.float64) @ ks["U"].T).astype(np.float32)  # query along the last latent directions
+    want = codec.attend_compressed(ks, vs, kp, vp, n, qr.astype(np.float64))
+    got = stc.attend_compressed(gpu_state(ks), gpu_state(vs), torch.from_numpy(kp).to(DEV),
+                                torch.from_numpy(vp).to(DEV), n, torch.from_numpy(qr).to(DEV)).cpu().numpy()
+    assert rel_err(got, want) <= 2e-3, rel_err(got, want)
+
+
 def test_attention_end_to_end_gpu_codes():
     w = synth.WORKLOADS[2]
     n = 8192
