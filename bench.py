@@ -47,6 +47,8 @@ def parse():
                          "`bench.py --copy-mib N` into a traffic summary for --kernel")
     ap.add_argument("--summarize-trace", metavar="TRACE_DIR", default=None,
                     help="no GPU work: print the kernel statistics of a rocprofv3 --kernel-trace --stats run")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="PMC_DIR", default=None,
+                    help="no GPU work: per-kernel averages of the counters of rocprofv3 --pmc runs of the step")
     ap.add_argument("--no-extras", action="store_true",
                     help="time only the step (no generation step, Walsh-Hadamard attention, sketch or cold "
                          "passes); for counter runs whose per-launch averages must cover the step's launches only")
@@ -106,7 +108,7 @@ def algorithmic_bytes(total_bits, n, streams, elem=2):
 
 def main():
     args = parse()
-    if args.summarize or args.summarize_trace:
+    if args.summarize or args.summarize_trace or args.summarize_counters:
         summarize(args)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -222,7 +224,7 @@ def main():
             ev[k][i][1].record(stream)
     torch.cuda.synchronize()
 
-    step_us, cold = {}, {}
+    step_us, cold, achievable = {}, {}, {}
     if not args.no_extras:
         # (3) one generation step per budget (append the last token's K and V to
         # every KV head, then attend over all n): it rewrites record n - 1 with
@@ -341,6 +343,27 @@ def main():
                           "pct_hbm_peak": round(100.0 * nbytes / (min(ms) * 1e-3) / 1e9 / HBM_PEAK_GBPS, 1)}
         del scratch
 
+        # (7) what a plain device copy achieves (bytes read + written per
+        # second): at 1 GiB, and at the size of one encode launch's traffic
+        def copy_gbps(nbytes):
+            src = torch.ones(nbytes, dtype=torch.uint8, device=dev)
+            dst = torch.empty_like(src)
+            for _ in range(3):
+                dst.copy_(src)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(10):
+                dst.copy_(src)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return round(2 * nbytes * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
+        enc_bytes = int(ops[0][2])
+        achievable = {"copy_GBps_1GiB": copy_gbps(1 << 30),
+                      "copy_GBps_encode_size": copy_gbps(enc_bytes // 2),
+                      "encode_size_bytes": enc_bytes}
+
     per_op = {}
     for i, (name, _, nbytes) in enumerate(ops):
         ms = [ev[k][i][0].elapsed_time(ev[k][i][1]) for k in range(args.steps)]
@@ -411,6 +434,7 @@ def main():
         "extra_us": step_us,
         "breakdown": per_op,
         "breakdown_cold": cold,  # each op alone after 1 GiB of writes (not in value)
+        "achievable": achievable,  # plain device copies, read + write bytes per second (not in value)
         "roofline": {"bound": "hbm", "kernel": dname, "launches_per_step": d_n,
                      "algorithmic_bytes_per_launch": int(d_bytes / d_n),
                      "avg_launch_us": round(1e3 * d_ms / d_n, 2),
@@ -464,6 +488,47 @@ def summarize(args):
     out = []
     if args.command:
         out.append("command: " + args.command)
+    if args.summarize_counters:
+        # per kernel: the average over its dispatches of each counter (summed
+        # over the counter's instances within a dispatch)
+        per = collections.defaultdict(lambda: collections.defaultdict(list))
+        for d in args.summarize_counters:
+            acc = collections.defaultdict(lambda: collections.defaultdict(float))
+            for name, disp, cname, v in _profile_rows(d, True):
+                acc[(name, disp)][cname] += v
+            for (name, _), cs in acc.items():
+                for cname, v in cs.items():
+                    per[name][cname].append(v)
+        out.append(f"kernel_source_sha256_16: {source_digest()}")
+        # 32-token blocks per launch of the Llama-layer step: 16 streams x
+        # 32768 tokens for the codec kernels, 8 KV heads x 32768 for attention
+        blocks = {"k_att_main": 8 * 32768 // 32}
+        for kname, pname in PROFILE_NAME.items():
+            if pname not in per:
+                continue
+            cs = per[pname]
+            avg = {c: sum(v) / len(v) for c, v in cs.items()}
+            nb = blocks.get(kname, 16 * 32768 // 32)
+            out.append(f"== {kname}  ({pname}; {len(next(iter(cs.values())))} dispatches per counter)")
+            for c in sorted(avg):
+                out.append(f"   {c:40s} {avg[c]:18.1f}")
+            if "SQ_INSTS_VALU" in avg and "SQ_INSTS_MFMA" in avg:
+                out.append(f"   per 32-token block: VALU {avg['SQ_INSTS_VALU'] / nb:.1f} (MFMA included), "
+                           f"MFMA {avg['SQ_INSTS_MFMA'] / nb:.1f}, LDS {avg.get('SQ_INSTS_LDS', 0) / nb:.1f}, "
+                           f"VMEM read {avg.get('SQ_INSTS_VMEM_RD', 0) / nb:.2f}, "
+                           f"VMEM write {avg.get('SQ_INSTS_VMEM_WR', 0) / nb:.2f}")
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in avg:
+                out.append(f"   MFMA busy cycles per SIMD (1024 SIMDs): {avg['SQ_VALU_MFMA_BUSY_CYCLES'] / 1024:.0f}")
+            if "SQ_LDS_BANK_CONFLICT" in avg and "SQ_ACTIVE_INST_LDS" in avg:
+                out.append(f"   LDS bank-conflict cycles / LDS active cycles: "
+                           f"{avg['SQ_LDS_BANK_CONFLICT'] / max(1.0, avg['SQ_ACTIVE_INST_LDS']):.3f}")
+            if "SQ_WAVE_CYCLES" in avg:
+                for c in ("SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS", "SQ_WAIT_INST_ANY", "SQ_WAIT_INST_LDS",
+                          "SQ_WAIT_ANY"):
+                    if c in avg:
+                        out.append(f"   {c} / SQ_WAVE_CYCLES: {avg[c] / avg['SQ_WAVE_CYCLES']:.3f}")
+        print("\n".join(out))
+        return
     if args.summarize_trace:
         agg = collections.defaultdict(list)
         for name, _, _, ns in _profile_rows(args.summarize_trace, False):
