@@ -387,8 +387,8 @@ stc_status stc_attend_rht_batched(const void* states_dev, int64_t n_states,
  * records are those a full encode would write (the stream is append-only),
  * and attention reads them back from the packed cache like every other
  * token. EIGEN/IDENTITY states only; ws_dev as for
- * stc_attend_compressed_batched with n_old + 1 tokens. Three launches on
- * `stream`. */
+ * stc_attend_compressed_batched with n_old + 1 tokens. Four launches on
+ * `stream` (the two appends, attention, the split merge). */
 stc_status stc_decode_step_batched(const void* states_dev, int64_t n_states,
                                    const int32_t* k_state_of_pair_dev,
                                    const int32_t* v_state_of_pair_dev, const stc_head_info* infos,
