@@ -52,6 +52,10 @@ def parse():
     ap.add_argument("--no-extras", action="store_true",
                     help="time only the step (no generation step, Walsh-Hadamard attention, sketch or cold "
                          "passes); for counter runs whose per-launch averages must cover the step's launches only")
+    ap.add_argument("--workload", default="llama_layer", choices=["llama_layer", "llama_cache", "qwen_batch"],
+                    help="llama_layer: the step above (the bench line); llama_cache: 32 layers x 8 KV heads x "
+                         "131072 tokens at 2.0 bits; qwen_batch: 28 layers x 4 KV heads x batch 16 x 32768 tokens "
+                         "at 1.33 bits (both print their own line: prefill encode, decode and the attention step)")
     ap.add_argument("--kernel", default=None, help="kernel name prefix for --summarize")
     ap.add_argument("--command", default="", help="command line recorded in a summary")
     return ap.parse_args()
@@ -127,6 +131,9 @@ def main():
         sys.exit(2)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.workload != "llama_layer":
+        large_workload(args, dev)
+        return
 
     w = synth.WORKLOADS[WORKLOAD]
     w3 = synth.WORKLOADS[RHT_WORKLOAD]
@@ -445,6 +452,117 @@ def main():
         "cpu_baseline": cpu,
         "setup_s": round(setup_s, 2),
         "calibrate_s": round(cal_s, 2),
+    }
+    print(json.dumps(line), flush=True)
+
+
+def large_workload(args, dev):
+    """The full-size caches: every stream generated on the device from the
+    workload's recipe (per-stream Haar rotation and outlier channels from the
+    seeded numpy generators, lambda_i = i^-alpha per layer, Gaussian samples
+    from a seeded device generator), calibrated on its first 2048 tokens (the
+    Qwen batch: one state per layer, KV head and K/V from batch entry 0,
+    shared across the batch), then timed: one batched encode of every stream
+    (prefill), one batched decode, and the decode-attention step over all
+    layers (and batch entries) reading only the packed cache."""
+    import numpy as np
+    import torch
+
+    import synth
+    import spectral_transform_codec_amd as stc
+
+    w = synth.WORKLOADS[4 if args.workload == "llama_cache" else 5]
+    n = args.tokens or w.n_tokens
+    L, Bt, H, g = w.layers, w.batch, w.kv_heads, w.group
+    budget = w.budgets[0]
+    S = L * Bt * H * 2                      # streams ordered (layer, batch, head, K/V)
+    P = S // 2                              # KV heads attended per step
+    t_setup = time.time()
+    x = torch.empty((S, n, 128), dtype=torch.bfloat16, device=dev)
+    gen = torch.Generator(device=dev)
+    rot = {}
+    for l in range(L):
+        lam = torch.arange(1, 129, dtype=torch.float64, device=dev) ** (-synth.layer_alpha(w, l))
+        for b in range(Bt):
+            bs = 0 if w.share_over_batch else b
+            for h in range(H):
+                for kind in (0, 1):
+                    key = (l, bs, h, kind)
+                    if key not in rot:
+                        q = synth.haar_orthogonal(synth.rng_for(w.cfg, l, bs, h, kind, synth.P_ROT))
+                        idx = synth.rng_for(w.cfg, l, bs, h, kind, synth.P_OUTLIER).permutation(128)[:w.n_outliers]
+                        sc = np.ones(128)
+                        sc[idx] = w.outlier_scale
+                        # x = (z sqrt(lambda)) Q^T, then the outlier channels scaled
+                        m = (torch.from_numpy(q.T * sc[None, :]).to(dev) * lam.sqrt()[:, None]).float()
+                        rot[key] = m
+                    gen.manual_seed(((((w.cfg * 64 + l) * 64 + b) * 64 + h) * 2 + kind) * 8 + synth.P_SAMPLES)
+                    z = torch.randn((n, 128), generator=gen, device=dev, dtype=torch.float32)
+                    x[((l * Bt + b) * H + h) * 2 + kind] = (z @ rot[key]).to(torch.bfloat16)
+                    del z
+    torch.cuda.synchronize()
+    setup_s = time.time() - t_setup
+    # states: one per stream, or one per (layer, head, K/V) from batch entry 0
+    t_cal = time.time()
+    states, smap = [], []
+    for l in range(L):
+        for b in range(Bt):
+            for h in range(H):
+                for kind in (0, 1):
+                    s_ = ((l * Bt + b) * H + h) * 2 + kind
+                    if w.share_over_batch and b > 0:
+                        smap.append(smap[((l * Bt + 0) * H + h) * 2 + kind])
+                    else:
+                        states.append(stc.calibrate_head(x[s_], min(w.n_calib, n), budget))
+                        smap.append(len(states) - 1)
+    arr = stc.StateArray(states)
+    torch.cuda.synchronize()
+    cal_s = time.time() - t_cal
+    smap_t = torch.tensor(smap, dtype=torch.int32, device=dev)
+    kmap, vmap = smap_t[0::2].contiguous(), smap_t[1::2].contiguous()
+    B = arr.max_bits
+    packed = torch.empty((S, stc.packed_bytes(B, n)), dtype=torch.uint8, device=dev)
+    qs = torch.randn((P, g, 128), generator=gen.manual_seed(w.cfg * 8 + synth.P_QUERY), device=dev)
+    ws = torch.empty(stc.attend_workspace_bytes(P, g, n), dtype=torch.uint8, device=dev)
+    out = torch.empty((P, g, 128), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps  # ms
+
+    codec_bytes = S * n * (256 + B / 8.0)
+    enc_ms = timed(lambda: stc.encode_kv_batched(arr, x, state_of_stream=smap_t, packed=packed), args.steps)
+    xhat = x  # decode overwrites the inputs (they are not needed any more)
+    dec_ms = timed(lambda: stc.decode_kv_batched(arr, packed, n, state_of_stream=smap_t, out=xhat), args.steps)
+    stc.encode_kv_batched(arr, x, state_of_stream=smap_t, packed=packed)  # the cache of the reconstruction
+    kp, vp = packed[0::2], packed[1::2]
+    att_ms = timed(lambda: stc.attend_compressed_batched(arr, kmap, vmap, kp, vp, n, qs, ws=ws, out=out),
+                   args.steps)
+    att_bytes = P * n * 2 * B / 8.0
+    line = {
+        "workload": args.workload, "config": w.name, "streams": S, "tokens": n, "kv_heads_per_step": P,
+        "group": g, "batch": Bt, "budget_bits": budget, "total_bits": B, "steps": args.steps,
+        "data": "synthetic (device-generated, seeded)",
+        "encode": {"ms": round(enc_ms, 4), "GBps": round(codec_bytes / (enc_ms * 1e-3) / 1e9, 1),
+                   "pct_hbm_peak": round(100 * codec_bytes / (enc_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 1),
+                   "bytes": int(codec_bytes)},
+        "decode": {"ms": round(dec_ms, 4), "GBps": round(codec_bytes / (dec_ms * 1e-3) / 1e9, 1),
+                   "pct_hbm_peak": round(100 * codec_bytes / (dec_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 1)},
+        "attention": {"us_per_step": round(att_ms * 1e3, 1), "steps_per_s": round(1e3 / att_ms, 1),
+                      "tokens_per_s": round(Bt * 1e3 / att_ms, 1),
+                      "GBps": round(att_bytes / (att_ms * 1e-3) / 1e9, 1),
+                      "pct_hbm_peak": round(100 * att_bytes / (att_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 1),
+                      "bytes": int(att_bytes)},
+        "setup_s": round(setup_s, 1), "calibrate_s": round(cal_s, 1),
     }
     print(json.dumps(line), flush=True)
 
