@@ -779,6 +779,8 @@ __device__ __forceinline__ const unsigned* uniform_ptr(const unsigned char* p) {
   const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)v), hi = __builtin_amdgcn_readfirstlane((unsigned)(v >> 32));
   return reinterpret_cast<const unsigned*>((uintptr_t)(((unsigned long long)hi << 32) | lo));
 }
+// (The chunk tests are uniform; only a ragged last chunk tests per lane.
+// Word c = lane + 64k sits at est_idx(c) = est_idx(lane) + 66k.)
 template <int NW>
 __device__ __forceinline__ void est_load(unsigned (&w)[NW], const unsigned char* src, long long nbytes, int lane) {
   const int nw = (int)(nbytes >> 2);
@@ -786,19 +788,22 @@ __device__ __forceinline__ void est_load(unsigned (&w)[NW], const unsigned char*
 #pragma unroll
   for (int k = 0; k < NW; ++k) {
     const int c = lane + 64 * k;
-    w[k] = c < nw ? s32[(unsigned)c] : 0u;
+    if (64 * k + 64 <= nw) w[k] = s32[(unsigned)c];
+    else if (64 * k < nw) w[k] = c < nw ? s32[(unsigned)c] : 0u;
+    else w[k] = 0u;
   }
 }
 template <int NW>
 __device__ __forceinline__ void est_store(unsigned* str, const unsigned (&w)[NW], long long nbytes, int lane) {
   const int nw = (int)(nbytes >> 2);
+  unsigned* base = str + est_idx((unsigned)lane);
+  const bool pad = (lane & 31) == 0;  // lanes 0 and 32 start a 32-word run
 #pragma unroll
   for (int k = 0; k < NW; ++k) {
-    const unsigned c = (unsigned)(lane + 64 * k);
-    if ((int)c < nw) {
-      const unsigned ix = est_idx(c);
-      str[ix] = w[k];
-      if ((c & 31u) == 0u && c > 0u) str[ix - 1] = w[k];
+    if (64 * k >= nw) break;
+    if (64 * k + 64 <= nw || lane + 64 * k < nw) {
+      base[66 * k] = w[k];
+      if (pad && (lane != 0 || k > 0)) base[66 * k - 1] = w[k];
     }
   }
 }
@@ -1473,10 +1478,22 @@ __device__ __forceinline__ void att_tables(const DevHdr* hd, unsigned* tab, int 
 
 // The four codes of group g (channels 64h + 4g .. +3) of the record at bit
 // tB of an LDS stream, as bytes of one word.
+// 32-bit window of the lane's record at stream bit P (est_idx(w) = 33w >> 5)
+__device__ __forceinline__ unsigned att_window(const unsigned* str, unsigned P) {
+  const unsigned ix = __umul24(P >> 5, 33u) >> 5;  // P < 2^24
+  return __builtin_amdgcn_alignbit(str[ix + 1], str[ix], P & 31u);
+}
+// the four codes of group g as floats (exact)
+__device__ __forceinline__ void att_group_codes(const unsigned* str, const lds_u8* tL, unsigned tB, int g,
+                                                float c[4]) {
+  const unsigned w = att_window(str, tB + LDS_AT(unsigned, tL + 16 * g));
+  const u32x4 pos = LDS_AT(u32x4, tL + 512 + 16 * g);
+  const u32x4 wid = LDS_AT(u32x4, tL + 1024 + 16 * g);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) c[j] = (float)__builtin_amdgcn_ubfe(w, pos[j], wid[j]);
+}
 __device__ __forceinline__ unsigned att_group_bytes(const unsigned* str, const lds_u8* tL, unsigned tB, int g) {
-  const unsigned P = tB + LDS_AT(unsigned, tL + 16 * g);
-  const unsigned ix = est_idx(P >> 5);
-  const unsigned w = __builtin_amdgcn_alignbit(str[ix + 1], str[ix], P & 31u);
+  const unsigned w = att_window(str, tB + LDS_AT(unsigned, tL + 16 * g));
   const u32x4 pos = LDS_AT(u32x4, tL + 512 + 16 * g);
   const u32x4 wid = LDS_AT(u32x4, tL + 1024 + 16 * g);
   unsigned v = __builtin_amdgcn_ubfe(w, pos[0], wid[0]);
@@ -1773,12 +1790,15 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_att_main(AttK a) {
           acc = mfma32_bf16(at, __builtin_bit_cast(bf16x8, fh), acc);
           acc = mfma32_bf16(at, __builtin_bit_cast(bf16x8, fl), acc);
         } else {
+          // codes straight to bf16 (exact); a stream without kept channels
+          // (Bk = 0) reads its all-zero tables and gives code 0
           bf16x8 bf;
 #pragma unroll
           for (int hg = 0; hg < 2; ++hg) {
-            const unsigned v = Bk ? att_group_bytes(sKs, kL, tB, 2 * ks + hg) : 0u;
+            float c[4];
+            att_group_codes(sKs, kL, tB, 2 * ks + hg, c);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) bf[4 * hg + j] = (__bf16)(float)((v >> (8 * j)) & 0xffu);
+            for (int j = 0; j < 4; ++j) bf[4 * hg + j] = (__bf16)c[j];
           }
           acc = mfma32_bf16(LDS_AT(bf16x8, aL + 16 * ks), bf, acc);
         }
@@ -1840,8 +1860,9 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_att_main(AttK a) {
         const int H = 8 * i + 4 * h + j;
         const float mx = half_max(sc[i][j]);
         const float mnew = fmaxf(mold[j], mx);
-        const float alpha = (mnew == -INFINITY) ? 1.0f : exp2f(mold[j] - mnew);
-        const float pv = (mnew == -INFINITY) ? 0.0f : exp2f(sc[i][j] - mnew);
+        // arguments <= 0: the hardware exp2 (results below 2^-126 flush to 0)
+        const float alpha = (mnew == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(mold[j] - mnew);
+        const float pv = (mnew == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(sc[i][j] - mnew);
         const _Float16 ph = (_Float16)(RHT ? pv * pscale : pv);
         l_run[i][j] = l_run[i][j] * alpha + (RHT ? pv : (float)ph);
         mnw[j] = mnew;
@@ -1858,7 +1879,7 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_att_main(AttK a) {
     {
       const unsigned tB = (unsigned)t32 * Bv;
 #pragma unroll
-      for (int gg = 0; gg < 16; ++gg) gvb[gg] = Bv ? att_group_bytes(sVs, vL, tB, gg) : 0u;
+      for (int gg = 0; gg < 16; ++gg) gvb[gg] = att_group_bytes(sVs, vL, tB, gg);  // all 0 if Bv = 0 (zero widths)
     }
     __builtin_amdgcn_s_waitcnt(0xc07f);
     __builtin_amdgcn_wave_barrier();
@@ -1876,10 +1897,13 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_att_main(AttK a) {
     {
       f32x4 al = *reinterpret_cast<const f32x4*>(sAl + 4 * g4);
       if (RHT) al *= vratio;
+      // (once the running maxima settle, every alpha is 1: skip the rescale)
+      if (!__all(al[0] == 1.0f && al[1] == 1.0f && al[2] == 1.0f && al[3] == 1.0f)) {
 #pragma unroll
-      for (int nb = 0; nb < 8; ++nb)
+        for (int nb = 0; nb < 8; ++nb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc_o[nb][r] *= al[r];
+          for (int r = 0; r < 4; ++r) acc_o[nb][r] *= al[r];
+      }
       u32x4 cbv;  // RHT: fp16 codebook planes
       if (RHT) cbv = *reinterpret_cast<const u32x4*>(sTab + 776);
 #pragma unroll
