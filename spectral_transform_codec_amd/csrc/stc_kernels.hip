@@ -171,6 +171,9 @@ struct EncK {
 };
 
 __device__ __forceinline__ unsigned est_idx(unsigned w) { return w + (w >> 5); }
+// est_idx(P >> 5) for a stream bit P < 2^24 (a wave block's stream is at
+// most 32 x 1024 bits): w + floor(w / 32) = floor(33 w / 32)
+__device__ __forceinline__ unsigned est_idx_bit(unsigned P) { return __umul24(P >> 5, 33u) >> 5; }
 
 // LDS (address space 3) byte pointers, used where a per-lane base must stay
 // one register so that reads can take constant offsets.
@@ -322,7 +325,7 @@ __global__ void __launch_bounds__(ENC_THREADS, 1) k_encode_eigen(EncK a) {
         auto put_group = [&](unsigned word, unsigned goff) {
           const unsigned P = tB + goff;
           const unsigned long long v = (unsigned long long)(tok_ok ? word : 0u) << (P & 31u);
-          unsigned* dst = sStr + est_idx(P >> 5);
+          unsigned* dst = sStr + est_idx_bit(P);
           __hip_atomic_fetch_or(dst, (unsigned)v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
           __hip_atomic_fetch_or(dst + 1, (unsigned)(v >> 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         };
@@ -878,7 +881,7 @@ __global__ void __launch_bounds__(DEC_THREADS, 1) k_decode_eigen(DecK a) {
         unsigned code[4] = {0u, 0u, 0u, 0u};
         if (B > 0) {
           const unsigned P = tB + LDS_AT(unsigned, tL + 16 * g);
-          const unsigned ix = est_idx(P >> 5);
+          const unsigned ix = est_idx_bit(P);
           const unsigned w = __builtin_amdgcn_alignbit(sStr[ix + 1], sStr[ix], P & 31u);
           const u32x4 pos = LDS_AT(u32x4, tL + 512 + 16 * g);
           const u32x4 wid = LDS_AT(u32x4, tL + 1024 + 16 * g);
@@ -1480,7 +1483,7 @@ __device__ __forceinline__ void att_tables(const DevHdr* hd, unsigned* tab, int 
 // tB of an LDS stream, as bytes of one word.
 // 32-bit window of the lane's record at stream bit P (est_idx(w) = 33w >> 5)
 __device__ __forceinline__ unsigned att_window(const unsigned* str, unsigned P) {
-  const unsigned ix = __umul24(P >> 5, 33u) >> 5;  // P < 2^24
+  const unsigned ix = est_idx_bit(P);
   return __builtin_amdgcn_alignbit(str[ix + 1], str[ix], P & 31u);
 }
 // the four codes of group g as floats (exact)
