@@ -287,6 +287,10 @@ __global__ void __launch_bounds__(ENC_THREADS, 1) k_encode_eigen(EncK a) {
       const long long P_len = packed_len((long long)B, n);
       const unsigned cw_kind = (B & 3u) == 0u ? 4u : ((B & 1u) == 0u ? 2u : 1u);
       const unsigned clear = est_idx(B + 4u) + 2u;
+      // bf16 tokens: a block's fragments are requested as soon as the
+      // previous block's last MFMA has read its own (same registers), so the
+      // load runs under that block's last quantization and copy-out
+      if (MODE == 0 && seg + wave < seg_end) load_frags(s, seg + wave - s * a.blocks_per_stream + a.blk0);
       for (long long blk = seg + wave; blk < seg_end; blk += ENC_WAVES) {
         const long long tt = blk - s * a.blocks_per_stream + a.blk0;  // absolute block of the stream
         const long long tok0 = tt * ENC_BT;
@@ -295,7 +299,6 @@ __global__ void __launch_bounds__(ENC_THREADS, 1) k_encode_eigen(EncK a) {
         x_row(tok0, rbase, trow);
         bf16x8 xl[8];
         auto& xh = pf;
-        if (MODE == 0) load_frags(s, tt);
         if (MODE == 1) {
           const float* row = static_cast<const float*>(a.x) + s * a.x_stride + rbase * a.ld + trow * (unsigned)a.ld;
 #pragma unroll
@@ -378,6 +381,7 @@ __global__ void __launch_bounds__(ENC_THREADS, 1) k_encode_eigen(EncK a) {
               if (mb < 3) chain_step(mb + 1, ks, nxt);
               if (ks & 1) quant_group(mb, ks >> 1, cur);
             }
+            if (MODE == 0 && mb == 2 && blk + ENC_WAVES < seg_end) load_frags(s, tt + ENC_WAVES);
           }
         } else {
 #pragma unroll
