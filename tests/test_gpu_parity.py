@@ -259,6 +259,43 @@ def test_attention_batched_gqa7():
         assert rel_err(out[i], wants[i]) <= 2e-3
 
 
+def test_attention_zero_bit_streams():
+    """KV heads whose K or V keeps no channel (a 0.0-bit budget: empty
+    records): no K bits give equal scores, so the output is the mean of the
+    reconstructed V; no V bits give a zero output. Mixed in one batched call
+    with a regular pair; garbage-filled record bytes beyond each stream."""
+    w = synth.WORKLOADS[2]
+    n = 1700
+    budgets = [(0.0, 2.0), (2.0, 0.0), (2.0, 2.0), (0.0, 0.0)]
+    states, kps, vps, qs, wants = [], [], [], [], []
+    for hd, (bk, bv) in enumerate(budgets):
+        k = synth.stream(w, 0, 0, hd, 0, n=n)
+        v = synth.stream(w, 0, 0, hd, 1, n=n)
+        ks, vs = codec.calibrate_head(k, 1024, bk), codec.calibrate_head(v, 1024, bv)
+        kp, vp = codec.encode_kv(ks, k), codec.encode_kv(vs, v)
+        q = synth.queries(w, 0, 0, hd)
+        wants.append(codec.attend_compressed(ks, vs, kp, vp, n, q.astype(np.float64)))
+        states += [gpu_state(ks), gpu_state(vs)]
+        kps.append(kp); vps.append(vp); qs.append(q)
+    assert np.abs(wants[1]).max() == 0.0 and np.abs(wants[0] - wants[0][0]).max() == 0.0
+    arr = stc.StateArray(states)
+    stride = stc.packed_bytes(arr.max_bits, n)
+    rng = np.random.default_rng(3)
+    kb = rng.integers(0, 256, (len(budgets), stride), dtype=np.uint8)
+    vb = rng.integers(0, 256, (len(budgets), stride), dtype=np.uint8)
+    for i in range(len(budgets)):
+        kb[i, :kps[i].shape[0]] = kps[i]; vb[i, :vps[i].shape[0]] = vps[i]
+    kmap = torch.arange(0, 2 * len(budgets), 2, dtype=torch.int32, device=DEV)
+    out = stc.attend_compressed_batched(arr, kmap, kmap + 1, torch.from_numpy(kb).to(DEV),
+                                        torch.from_numpy(vb).to(DEV), n,
+                                        torch.from_numpy(np.stack(qs)).to(DEV)).cpu().numpy()
+    for i in range(len(budgets)):
+        if np.abs(wants[i]).max() == 0.0:
+            assert np.abs(out[i]).max() == 0.0, i
+        else:
+            assert rel_err(out[i], wants[i]) <= 2e-3, (i, rel_err(out[i], wants[i]))
+
+
 # ---------------------------------------------------------- batched codec
 def test_batched_encode_decode_shared_states():
     w = synth.WORKLOADS[5]
