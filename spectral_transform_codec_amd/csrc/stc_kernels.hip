@@ -172,8 +172,14 @@ struct EncK {
 
 __device__ __forceinline__ unsigned est_idx(unsigned w) { return w + (w >> 5); }
 // est_idx(P >> 5) for a stream bit P < 2^24 (a wave block's stream is at
-// most 32 x 1024 bits): w + floor(w / 32) = floor(33 w / 32)
-__device__ __forceinline__ unsigned est_idx_bit(unsigned P) { return __umul24(P >> 5, 33u) >> 5; }
+// most 32 x 1024 bits): w + floor(w / 32) = floor(33 w / 32), one 24-bit
+// multiply (written as such: the compiler would expand 33 w into shifts and
+// masks, two instructions more per group)
+__device__ __forceinline__ unsigned est_idx_bit(unsigned P) {
+  unsigned r;
+  asm("v_lshrrev_b32 %0, 5, %1\n\tv_mul_u32_u24 %0, 33, %0\n\tv_lshrrev_b32 %0, 5, %0" : "=&v"(r) : "v"(P));
+  return r;
+}
 
 // LDS (address space 3) byte pointers, used where a per-lane base must stay
 // one register so that reads can take constant offsets.
@@ -1485,13 +1491,14 @@ __device__ __forceinline__ void att_tables(const DevHdr* hd, unsigned* tab, int 
 
 // The four codes of group g (channels 64h + 4g .. +3) of the record at bit
 // tB of an LDS stream, as bytes of one word.
-// 32-bit window of the lane's record at stream bit P (est_idx(w) = 33w >> 5)
-__device__ __forceinline__ unsigned att_window(const unsigned* str, unsigned P) {
-  const unsigned ix = est_idx_bit(P);
-  return __builtin_amdgcn_alignbit(str[ix + 1], str[ix], P & 31u);
+// 32-bit window of the lane's record at stream bit P; sb = the stream's LDS
+// base as one register, so that the address is one shift-add
+__device__ __forceinline__ unsigned att_window(const lds_u8* sb, unsigned P) {
+  const lds_u8* p = sb + (est_idx_bit(P) << 2);
+  return __builtin_amdgcn_alignbit(LDS_AT(unsigned, p + 4), LDS_AT(unsigned, p), P & 31u);
 }
 // the four codes of group g as floats (exact)
-__device__ __forceinline__ void att_group_codes(const unsigned* str, const lds_u8* tL, unsigned tB, int g,
+__device__ __forceinline__ void att_group_codes(const lds_u8* str, const lds_u8* tL, unsigned tB, int g,
                                                 float c[4]) {
   const unsigned w = att_window(str, tB + LDS_AT(unsigned, tL + 16 * g));
   const u32x4 pos = LDS_AT(u32x4, tL + 512 + 16 * g);
@@ -1499,7 +1506,7 @@ __device__ __forceinline__ void att_group_codes(const unsigned* str, const lds_u
 #pragma unroll
   for (int j = 0; j < 4; ++j) c[j] = (float)__builtin_amdgcn_ubfe(w, pos[j], wid[j]);
 }
-__device__ __forceinline__ unsigned att_group_bytes(const unsigned* str, const lds_u8* tL, unsigned tB, int g) {
+__device__ __forceinline__ unsigned att_group_bytes(const lds_u8* str, const lds_u8* tL, unsigned tB, int g) {
   const unsigned w = att_window(str, tB + LDS_AT(unsigned, tL + 16 * g));
   const u32x4 pos = LDS_AT(u32x4, tL + 512 + 16 * g);
   const u32x4 wid = LDS_AT(u32x4, tL + 1024 + 16 * g);
@@ -1758,7 +1765,11 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_att_main(AttK a) {
     }
     unsigned kb = lds_offset(reinterpret_cast<unsigned char*>(sTab + 64 * h));
     unsigned ab = lds_offset(sA + t32 * AROW + 128 * h);
-    asm volatile("" : "+v"(kb), "+v"(ab));
+    unsigned ksb = lds_offset(reinterpret_cast<unsigned char*>(sKs));
+    unsigned vsb = lds_offset(reinterpret_cast<unsigned char*>(sVs));
+    asm volatile("" : "+v"(kb), "+v"(ab), "+v"(ksb), "+v"(vsb));
+    const lds_u8* kSL = lds_ptr(ksb);
+    const lds_u8* vSL = lds_ptr(vsb);
     const lds_u8* kL = lds_ptr(kb);
     const lds_u8* vL = kL + 1536;
     const lds_u8* aL = lds_ptr(ab);
@@ -1787,7 +1798,7 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_att_main(AttK a) {
           u32x4 fh, fl;
 #pragma unroll
           for (int hg = 0; hg < 2; ++hg) {
-            const unsigned v = att_group_bytes(sKs, kL, tB, 2 * ks + hg);
+            const unsigned v = att_group_bytes(kSL, kL, tB, 2 * ks + hg);
             const u32x2 vh = lut16x4(v, cbh[0], cbh[1], cbh[2], cbh[3]);
             const u32x2 vl = lut16x4(v, cbl[0], cbl[1], cbl[2], cbl[3]);
             fh[2 * hg] = vh[0]; fh[2 * hg + 1] = vh[1];
@@ -1803,7 +1814,7 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_att_main(AttK a) {
 #pragma unroll
           for (int hg = 0; hg < 2; ++hg) {
             float c[4];
-            att_group_codes(sKs, kL, tB, 2 * ks + hg, c);
+            att_group_codes(kSL, kL, tB, 2 * ks + hg, c);
 #pragma unroll
             for (int j = 0; j < 4; ++j) bf[4 * hg + j] = (__bf16)c[j];
           }
@@ -1886,7 +1897,7 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_att_main(AttK a) {
     {
       const unsigned tB = (unsigned)t32 * Bv;
 #pragma unroll
-      for (int gg = 0; gg < 16; ++gg) gvb[gg] = att_group_bytes(sVs, vL, tB, gg);  // all 0 if Bv = 0 (zero widths)
+      for (int gg = 0; gg < 16; ++gg) gvb[gg] = att_group_bytes(vSL, vL, tB, gg);  // all 0 if Bv = 0 (zero widths)
     }
     __builtin_amdgcn_s_waitcnt(0xc07f);
     __builtin_amdgcn_wave_barrier();
