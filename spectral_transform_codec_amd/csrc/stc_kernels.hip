@@ -787,17 +787,20 @@ struct DecK {
 // ..; 256 contiguous bytes per instruction, scalar base) into NW registers;
 // est_store writes them with the word following each 32-word run repeated in
 // the pad slot before it.
-__device__ __forceinline__ const unsigned* uniform_ptr(const unsigned char* p) {
+// (a global-memory pointer held in scalar registers: the loads take it as
+// their base and a 32-bit per-lane offset, with no 64-bit address math)
+typedef __attribute__((address_space(1))) const unsigned gbl_u32;
+__device__ __forceinline__ gbl_u32* uniform_ptr(const unsigned char* p) {
   const unsigned long long v = (unsigned long long)(uintptr_t)p;
   const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)v), hi = __builtin_amdgcn_readfirstlane((unsigned)(v >> 32));
-  return reinterpret_cast<const unsigned*>((uintptr_t)(((unsigned long long)hi << 32) | lo));
+  return reinterpret_cast<gbl_u32*>((uintptr_t)(((unsigned long long)hi << 32) | lo));
 }
 // (The chunk tests are uniform; only a ragged last chunk tests per lane.
 // Word c = lane + 64k sits at est_idx(c) = est_idx(lane) + 66k.)
 template <int NW>
 __device__ __forceinline__ void est_load(unsigned (&w)[NW], const unsigned char* src, long long nbytes, int lane) {
   const int nw = (int)(nbytes >> 2);
-  const unsigned* s32 = uniform_ptr(src);
+  gbl_u32* s32 = uniform_ptr(src);
 #pragma unroll
   for (int k = 0; k < NW; ++k) {
     const int c = lane + 64 * k;
