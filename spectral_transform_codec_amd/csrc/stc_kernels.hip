@@ -1875,6 +1875,26 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_att_main(AttK a) {
     for (int i = 0; i < 2; ++i) {
       if (i == 1 && !two_rows) break;
       const f32x4 mold = *reinterpret_cast<const f32x4*>(sM + 8 * i + 4 * h);
+      // When every score of the block is at most 2^8 above its head's running
+      // maximum, that maximum stays the reference (weights <= 2^8, exact
+      // enough in fp16; the merges use the same reference), so no block
+      // maximum, no alpha and no rescale are needed.
+      bool slow = false;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (8 * i + 4 * h + j < g) slow |= !(sc[i][j] <= mold[j] + 8.0f);
+      if (!__any(slow)) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int H = 8 * i + 4 * h + j;
+          const float pv = H < g ? __builtin_amdgcn_exp2f(sc[i][j] - mold[j]) : 0.0f;
+          const _Float16 ph = (_Float16)(RHT ? pv * pscale : pv);
+          l_run[i][j] += RHT ? pv : (float)ph;
+          sP[H * P_ROWH + t32] = ph;
+          if (t32 == 0) sAl[H] = 1.0f;
+        }
+        continue;
+      }
       f32x4 mnw;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
