@@ -1655,6 +1655,26 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_att_main(AttK a) {
   long long t_end = t_begin + a.split_tokens;
   if (t_end > n) t_end = n;
 
+  // the records of a wave block go HBM -> registers (wk, wv) -> the wave's
+  // streams; the wave's first block is requested before the a table is built
+  const long long PkL = packed_len((long long)Bk, n), PvL = packed_len((long long)Bv, n);
+  const unsigned char* gk = a.k_packed + pg * a.packed_stride;
+  const unsigned char* gv = a.v_packed + pg * a.packed_stride;
+  unsigned wk[NW], wv[NW];
+  long long nbk = 0, nbv = 0;
+  auto load_records = [&](long long tok0) {
+    const long long blk = tok0 / ATT_BT;
+    const long long stk = blk * 4LL * (long long)Bk, stv = blk * 4LL * (long long)Bv;
+    nbk = 4LL * (long long)Bk;
+    nbv = 4LL * (long long)Bv;
+    if (nbk > PkL - stk) nbk = PkL - stk;
+    if (nbv > PvL - stv) nbv = PvL - stv;
+    est_load<NW>(wk, gk + stk, Bk ? nbk : 0, lane);  // K and V loads in flight together
+    est_load<NW>(wv, gv + stv, Bv ? nbv : 0, lane);
+  };
+  const long long t_first = t_begin + (long long)wave * ATT_BT;
+  if (t_first < t_end) load_records(t_first);
+
   if (tid < 128) {
     att_tables(hk, sTab, tid);
     att_tables(hv, sTab + 384, tid);
@@ -1670,7 +1690,7 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_att_main(AttK a) {
     const int j = tid & 127, part = tid >> 7;
     const int nparts = (int)(blockDim.x >> 7);
     const float* qp = a.q + pg * g * 128;
-    const int rows = (128 + nparts - 1) / nparts;  // rows per part: 16, 22 or 32 (1024, 768, 512 threads)
+    const int rows = (128 + nparts - 1) / nparts;  // rows per part: 16 or 22 (1024 or 768 threads)
     for (int e = tid; e < 128 * 16; e += blockDim.x) {
       const int r = e >> 4, hh = e & 15;
       sqT[e] = hh < g ? qp[hh * 128 + r] : 0.0f;
@@ -1678,9 +1698,9 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_att_main(AttK a) {
     for (int tab = 0; tab < (SKETCH ? 2 : 1); ++tab) {
     // tab 0: U_K (scores), tab 1: S^T (sketch products)
     const float* u = reinterpret_cast<const float*>(kst + (tab == 0 ? OFF_U32 : OFF_SKT32));
-    float ur[32];
+    float ur[22];
 #pragma unroll
-    for (int k = 0; k < 32; ++k) {
+    for (int k = 0; k < 22; ++k) {
       // issued together: rows past the part's share load row 127 and count 0
       const int row = part + k * nparts;
       const float v = u[(row < 127 ? row : 127) * 128 + j];
@@ -1691,7 +1711,7 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_att_main(AttK a) {
 #pragma unroll
     for (int hh = 0; hh < 16; ++hh) acc[hh] = 0.0f;
 #pragma unroll
-    for (int k = 0; k < 32; ++k) {
+    for (int k = 0; k < 22; ++k) {
       if (k < rows) {
         const int row = part + k * nparts;
         const f32x4* q4 = reinterpret_cast<const f32x4*>(sqT + (row < 127 ? row : 127) * 16);
@@ -1746,26 +1766,19 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_att_main(AttK a) {
   for (int nb = 0; nb < 8; ++nb) acc_o[nb] = (f32x4){0.f, 0.f, 0.f, 0.f};
   float vscale = 1.0f;  // RHT: acc_o is in units of the current block's largest value norm
 
-  const long long PkL = packed_len((long long)Bk, n), PvL = packed_len((long long)Bv, n);
-  const unsigned char* gk = a.k_packed + pg * a.packed_stride;
-  const unsigned char* gv = a.v_packed + pg * a.packed_stride;
-
-  for (long long tok0 = t_begin + (long long)wave * ATT_BT; tok0 < t_end; tok0 += (long long)nwav * ATT_BT) {
+  if (t_first < t_end) {  // (the a-table build is done with the wave regions)
+    est_store<NW>(sKs, wk, Bk ? nbk : 0, lane);
+    est_store<NW>(sVs, wv, Bv ? nbv : 0, lane);
+  }
+  for (long long tok0 = t_first; tok0 < t_end; tok0 += (long long)nwav * ATT_BT) {
     // ---- records -> the wave's streams
-    {
-      const long long blk = tok0 / ATT_BT;
-      const long long stk = blk * 4LL * (long long)Bk, stv = blk * 4LL * (long long)Bv;
-      long long nbk = 4LL * (long long)Bk, nbv = 4LL * (long long)Bv;
-      if (nbk > PkL - stk) nbk = PkL - stk;
-      if (nbv > PvL - stv) nbv = PvL - stv;
-      unsigned wk[NW], wv[NW];
-      est_load<NW>(wk, gk + stk, Bk ? nbk : 0, lane);  // K and V loads in flight together
-      est_load<NW>(wv, gv + stv, Bv ? nbv : 0, lane);
+    if (tok0 != t_first) {
+      load_records(tok0);
       est_store<NW>(sKs, wk, Bk ? nbk : 0, lane);
       est_store<NW>(sVs, wv, Bv ? nbv : 0, lane);
-      __builtin_amdgcn_s_waitcnt(0xc07f);
-      __builtin_amdgcn_wave_barrier();
     }
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    __builtin_amdgcn_wave_barrier();
     unsigned kb = lds_offset(reinterpret_cast<unsigned char*>(sTab + 64 * h));
     unsigned ab = lds_offset(sA + t32 * AROW + 128 * h);
     unsigned ksb = lds_offset(reinterpret_cast<unsigned char*>(sKs));
@@ -2063,8 +2076,10 @@ int launch_attend(const AttendLaunch& L, void* stream) {
   const bool sketch = L.k_sketch != nullptr;
   const size_t fixed = ATT_FIXED_BYTES + (sketch ? 32 * AROW : 0);
   int waves = ATT_WAVES_MAX;
-  while (waves > 8 && fixed + (size_t)waves * a.region_words * 4 > 160 * 1024) waves -= 4;
-  if (fixed + (size_t)waves * a.region_words * 4 > 160 * 1024) return 1;  // (the a-table build needs >= 8 waves)
+  while (waves > 12 && fixed + (size_t)waves * a.region_words * 4 > 160 * 1024) waves -= 4;
+  // (records of at most 1024 bits always leave room for 12 waves; the
+  // a-table build assumes 12 or 16)
+  if (fixed + (size_t)waves * a.region_words * 4 > 160 * 1024) return 1;
   hipStream_t s = (hipStream_t)stream;
   for (long long c0 = 0; c0 < L.n_pairs; c0 += ATT_MAX_PAIRS) {
     const long long np = L.n_pairs - c0 < ATT_MAX_PAIRS ? L.n_pairs - c0 : ATT_MAX_PAIRS;
