@@ -1531,93 +1531,83 @@ __device__ __forceinline__ unsigned att_group_bytes(const lds_u8* str, const lds
 // holds S q scale log2(e) sqrt(pi/2)/m (hi / lo) and each score gains
 // |r_t| times its product with the token's signs, one more MFMA chain.
 // k_att_combine: one workgroup per (pair, query head), after k_att_main has
-// written every split's partial. Thread j merges the splits' (acc_j, m, l)
-// with log-sum-exp weights (fp32 weights, fp64 sums, batches of 32 splits
-// with all loads in flight) and dequantizes the mean code of V channel j;
-// meanwhile U_V is staged in LDS (rows padded to 129 floats); then thread i
-// rotates back: o_i = sum_k U_ik chat_k.
-constexpr int CMB_THREADS = 128;
-constexpr int CMB_UROW = 129;
+// written every split's partial. Thread (q, i) requests its quarter of row i
+// of U_V (32 floats, kept in registers) first; meanwhile thread j < 128
+// merges the splits' (acc_j, m, l) with log-sum-exp weights (fp32 weights,
+// fp64 sums, batches of 32 splits with all loads in flight) and dequantizes
+// the mean code of V channel j into LDS; then every thread sums its quarter
+// of o_i = sum_k U_ik chat_k and the four quarters are added through LDS.
+constexpr int CMB_THREADS = 512;
 constexpr int CMB_BATCH = 32;
-constexpr size_t CMB_LDS = (size_t)(128 * CMB_UROW + 128) * 4;
+constexpr size_t CMB_LDS = (size_t)(128 + 4 * 128) * 4;
 
 __global__ void __launch_bounds__(CMB_THREADS) k_att_combine(AttK a) {
   extern __shared__ __align__(16) unsigned char smem[];
-  float* sU = reinterpret_cast<float*>(smem);  // [128][129]
-  float* sC = sU + 128 * CMB_UROW;             // dequantized mean codes
+  float* sC = reinterpret_cast<float*>(smem);  // dequantized mean codes [128]
+  float* sQ = sC + 128;                        // quarter sums [4][128]
   const long long p = blockIdx.x;
   const int hh = blockIdx.y;
   const long long pg = a.pair_base + p;
   const int t = threadIdx.x;
+  const int i = t & 127, qt = t >> 7;  // output dim, quarter of the inputs
   const int g = a.group;
   const int S = (int)a.n_splits;
   const long long PS = att_part_stride(g);
   const unsigned char* vst = a.v_states + (size_t)state_index(a.v_map, pg, a.n_states) * STATE_BYTES;
   const DevHdr* hv = reinterpret_cast<const DevHdr*>(vst);
-  const f32x4* u4 = reinterpret_cast<const f32x4*>(vst + OFF_U32);
-  const float* ph = reinterpret_cast<const float*>(a.ws) + p * (long long)S * PS + hh * ATT_PART_FLOATS;
-  const int j = t;
-  const unsigned bits = hv->bits[j];
-  const float step = hv->step32[j], hs = hv->halfspan[j];
-  float M = -INFINITY;
-  double A = 0.0, L = 0.0;
-  for (int s0 = 0; s0 < S; s0 += CMB_BATCH) {
-    float mv[CMB_BATCH], lv[CMB_BATCH], av[CMB_BATCH];
+  const f32x4* urow = reinterpret_cast<const f32x4*>(vst + OFF_U32) + i * 32 + qt * 8;  // U[i][32qt .. +31]
+  f32x4 u[8];
 #pragma unroll
-    for (int r = 0; r < CMB_BATCH; ++r) {
-      const long long s2 = s0 + r < S ? s0 + r : S - 1;
-      mv[r] = ph[s2 * PS + 128];
-      lv[r] = ph[s2 * PS + 129];
-      av[r] = ph[s2 * PS + j];
-    }
-    if (s0 == 0) {
-      // U_V -> LDS: 4096 float4, 32 per thread, in four batches of 8
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        f32x4 uv[8];
-#pragma unroll
-        for (int r = 0; r < 8; ++r) uv[r] = u4[t + (8 * b + r) * CMB_THREADS];
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-          const int e4 = t + (8 * b + r) * CMB_THREADS;
-          const int row = e4 >> 5, col = 4 * (e4 & 31);
-#pragma unroll
-          for (int c = 0; c < 4; ++c) sU[row * CMB_UROW + col + c] = uv[r][c];
-        }
-      }
-    }
-    float Mc = M;
-#pragma unroll
-    for (int r = 0; r < CMB_BATCH; ++r) Mc = fmaxf(Mc, mv[r]);  // clamped repeats change no maximum
-    if (Mc != -INFINITY) {
-      if (M != -INFINITY && M != Mc) {
-        const double sc = (double)exp2f(M - Mc);
-        A *= sc;
-        L *= sc;
-      }
+  for (int r = 0; r < 8; ++r) u[r] = urow[r];
+  if (t < 128) {
+    const int j = t;
+    const float* ph = reinterpret_cast<const float*>(a.ws) + p * (long long)S * PS + hh * ATT_PART_FLOATS;
+    const unsigned bits = hv->bits[j];
+    const float step = hv->step32[j], hs = hv->halfspan[j];
+    float M = -INFINITY;
+    double A = 0.0, L = 0.0;
+    for (int s0 = 0; s0 < S; s0 += CMB_BATCH) {
+      float mv[CMB_BATCH], lv[CMB_BATCH], av[CMB_BATCH];
 #pragma unroll
       for (int r = 0; r < CMB_BATCH; ++r) {
-        const float f = (s0 + r < S && mv[r] != -INFINITY) ? exp2f(mv[r] - Mc) : 0.0f;
-        A += (double)(f * av[r]);
-        L += (double)(f * lv[r]);
+        const long long s2 = s0 + r < S ? s0 + r : S - 1;
+        mv[r] = ph[s2 * PS + 128];
+        lv[r] = ph[s2 * PS + 129];
+        av[r] = ph[s2 * PS + j];
       }
-      M = Mc;
-    }
-  }
-  // dequantize the mean code: step * (A / L - (L_j - 1)/2)
-  sC[j] = bits ? (float)((double)step * (A / L - (double)hs)) : 0.0f;
-  __syncthreads();
-  const int i = t;
-  const f32x4* c4 = reinterpret_cast<const f32x4*>(sC);
-  const float* ur = sU + i * CMB_UROW;
-  float o = 0.0f;
-#pragma unroll 8
-  for (int k4 = 0; k4 < 32; ++k4) {
-    const f32x4 c = c4[k4];
+      float Mc = M;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) o = __builtin_fmaf(ur[4 * k4 + e], c[e], o);
+      for (int r = 0; r < CMB_BATCH; ++r) Mc = fmaxf(Mc, mv[r]);  // clamped repeats change no maximum
+      if (Mc != -INFINITY) {
+        if (M != -INFINITY && M != Mc) {
+          const double sc = (double)exp2f(M - Mc);
+          A *= sc;
+          L *= sc;
+        }
+#pragma unroll
+        for (int r = 0; r < CMB_BATCH; ++r) {
+          const float f = (s0 + r < S && mv[r] != -INFINITY) ? exp2f(mv[r] - Mc) : 0.0f;
+          A += (double)(f * av[r]);
+          L += (double)(f * lv[r]);
+        }
+        M = Mc;
+      }
+    }
+    // dequantize the mean code: step * (A / L - (L_j - 1)/2)
+    sC[j] = bits ? (float)((double)step * (A / L - (double)hs)) : 0.0f;
   }
-  a.out[(pg * g + hh) * 128 + i] = o;
+  __syncthreads();
+  float o = 0.0f;
+  const f32x4* c4 = reinterpret_cast<const f32x4*>(sC) + qt * 8;
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    const f32x4 c = c4[r];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o = __builtin_fmaf(u[r][e], c[e], o);
+  }
+  sQ[qt * 128 + i] = o;
+  __syncthreads();
+  if (t < 128) a.out[(pg * g + hh) * 128 + i] = (sQ[i] + sQ[128 + i]) + (sQ[256 + i] + sQ[384 + i]);
 }
 
 template <int NW, bool RHT, bool SKETCH>
