@@ -47,6 +47,11 @@ __device__ __forceinline__ f32x16 mfma32_bf16(bf16x8 a, bf16x8 b, f32x16 c) {
 __device__ __forceinline__ f32x4 mfma_f16(f16x8 a, f16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
+// Two floats that bf16 holds exactly (here integers below 2^8, whose fp32
+// low halves are zero) as a bf16 pair: the two high halves, one byte permute.
+__device__ __forceinline__ unsigned bf16_pair_exact(float lo, float hi) {
+  return __builtin_amdgcn_perm(__builtin_bit_cast(unsigned, hi), __builtin_bit_cast(unsigned, lo), 0x07060302u);
+}
 
 __device__ __forceinline__ long long packed_len(long long total_bits, long long n) {
   const long long nb = (n * total_bits + 7) / 8;
@@ -63,20 +68,6 @@ __device__ __forceinline__ long long state_index(const int32_t* map, long long s
 // workgroups sharing a stream's basis share an L2.
 __device__ __forceinline__ int xcd_logical(int b, int grid) {
   return (grid % 8 == 0) ? (b % 8) * (grid / 8) + b / 8 : b;
-}
-
-// 8 unsigned bytes -> 8 bf16 (exact: codes are integers < 256)
-__device__ __forceinline__ bf16x8 bytes_to_bf16x8(u32x2 v) {
-  bf16x8 r;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) r[i] = (__bf16)(float)((v[i >> 2] >> (8 * (i & 3))) & 0xffu);
-  return r;
-}
-__device__ __forceinline__ f16x8 bytes_to_f16x8(u32x2 v) {
-  f16x8 r;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) r[i] = (_Float16)(float)((v[i >> 2] >> (8 * (i & 3))) & 0xffu);
-  return r;
 }
 
 // ======================================================================
@@ -888,21 +879,22 @@ __global__ void __launch_bounds__(DEC_THREADS, 1) k_decode_eigen(DecK a) {
       const lds_u8* tL = lds_ptr(tb);
       const lds_u8* wL = lds_ptr(wb);
       const unsigned tB = (unsigned)t32 * B;
-      bf16x8 cf[8];
+      u32x4 cf[8];
 #pragma unroll
       for (int g = 0; g < 16; ++g) {  // group: channels 64h + 4g .. +3
-        unsigned code[4] = {0u, 0u, 0u, 0u};
-        if (B > 0) {
-          const unsigned P = tB + LDS_AT(unsigned, tL + 16 * g);
-          const unsigned ix = est_idx_bit(P);
-          const unsigned w = __builtin_amdgcn_alignbit(sStr[ix + 1], sStr[ix], P & 31u);
-          const u32x4 pos = LDS_AT(u32x4, tL + 512 + 16 * g);
-          const u32x4 wid = LDS_AT(u32x4, tL + 1024 + 16 * g);
+        // (a state without kept channels, B = 0, has all-zero tables: it
+        // reads the stream's first two words and extracts zero-width codes)
+        const unsigned P = tB + LDS_AT(unsigned, tL + 16 * g);
+        const unsigned ix = est_idx_bit(P);
+        const unsigned w = __builtin_amdgcn_alignbit(sStr[ix + 1], sStr[ix], P & 31u);
+        const u32x4 pos = LDS_AT(u32x4, tL + 512 + 16 * g);
+        const u32x4 wid = LDS_AT(u32x4, tL + 1024 + 16 * g);
+        unsigned code[4];
 #pragma unroll
-          for (int j = 0; j < 4; ++j) code[j] = __builtin_amdgcn_ubfe(w, pos[j], wid[j]);
-        }
+        for (int j = 0; j < 4; ++j) code[j] = __builtin_amdgcn_ubfe(w, pos[j], wid[j]);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) cf[g >> 1][4 * (g & 1) + j] = (__bf16)(float)code[j];
+        for (int j = 0; j < 2; ++j)
+          cf[g >> 1][2 * (g & 1) + j] = bf16_pair_exact((float)code[2 * j], (float)code[2 * j + 1]);
       }
       // ---- 3: reconstruct dims 64h + 16ob + r of token t
       const long long tok = tok0 + t32;
@@ -923,8 +915,8 @@ __global__ void __launch_bounds__(DEC_THREADS, 1) k_decode_eigen(DecK a) {
           const int off = 32 * ob * UROW + 16 * ks;
           const bf16x8 wh = LDS_AT(bf16x8, wL + off);
           const bf16x8 wl = LDS_AT(bf16x8, wL + 128 * UROW + off);
-          acc = mfma32_bf16(wh, cf[ks], acc);
-          acc = mfma32_bf16(wl, cf[ks], acc);
+          acc = mfma32_bf16(wh, __builtin_bit_cast(bf16x8, cf[ks]), acc);
+          acc = mfma32_bf16(wl, __builtin_bit_cast(bf16x8, cf[ks]), acc);
         }
         if (F32OUT) {
           if (tok_ok) {
@@ -1816,15 +1808,15 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_att_main(AttK a) {
         } else {
           // codes straight to bf16 (exact); a stream without kept channels
           // (Bk = 0) reads its all-zero tables and gives code 0
-          bf16x8 bf;
+          u32x4 bf;
 #pragma unroll
           for (int hg = 0; hg < 2; ++hg) {
             float c[4];
             att_group_codes(kSL, kL, tB, 2 * ks + hg, c);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) bf[4 * hg + j] = (__bf16)c[j];
+            bf[2 * hg] = bf16_pair_exact(c[0], c[1]);
+            bf[2 * hg + 1] = bf16_pair_exact(c[2], c[3]);
           }
-          acc = mfma32_bf16(LDS_AT(bf16x8, aL + 16 * ks), bf, acc);
+          acc = mfma32_bf16(LDS_AT(bf16x8, aL + 16 * ks), __builtin_bit_cast(bf16x8, bf), acc);
         }
       }
 #pragma unroll
