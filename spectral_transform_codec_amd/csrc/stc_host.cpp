@@ -789,6 +789,17 @@ stc_status stc_state_basis(const void* state_dev, float* u_out, stc_stream_t str
   return ok();
 }
 
+// Every record 0 or 32 * 2^s bits long (s = 0..5): the attention kernel then
+// stages each record on a word-aligned slot of its own.
+static bool records_word_pow2(const stc_head_info* infos, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) {
+    const int b = infos[i].total_bits;
+    if (b == 0) continue;
+    if ((b & 31) || ((b >> 5) & ((b >> 5) - 1))) return false;
+  }
+  return true;
+}
+
 // ------------------------------------------------------------- codec calls
 static stc_status check_batch(const char* who, const void* states_dev, int64_t n_states,
                               const stc_head_info* infos, int64_t n_streams, int64_t n_tokens,
@@ -1009,6 +1020,7 @@ stc_status stc_attend_compressed_batched(const void* states_dev, int64_t n_state
   AttendLaunch a{st, k_map, st, v_map, n_states, n_pairs, n_tokens, packed_pair_stride,
                  static_cast<const unsigned char*>(k_packed_dev), static_cast<const unsigned char*>(v_packed_dev),
                  group, q_dev, out_dev, scale, static_cast<unsigned char*>(ws_dev), mb};
+  a.rec = records_word_pow2(infos, n_states);
   if (launch_attend(a, stream)) return fail(STC_EDEVICE, "attend launch: %s", hipGetErrorString(hipGetLastError()));
   return ok();
 }
@@ -1046,6 +1058,7 @@ stc_status stc_attend_compressed_sketch_batched(const void* states_dev, int64_t 
                  static_cast<const unsigned char*>(k_packed_dev), static_cast<const unsigned char*>(v_packed_dev),
                  group, q_dev, out_dev, scale, static_cast<unsigned char*>(ws_dev), mb, nullptr, nullptr, 0, false,
                  static_cast<const unsigned char*>(k_sketch_dev), k_rnorm_dev, sketch_pair_stride, rnorm_pair_stride};
+  a.rec = records_word_pow2(infos, n_states);
   if (launch_attend(a, stream)) return fail(STC_EDEVICE, "attend_sketch launch: %s", hipGetErrorString(hipGetLastError()));
   return ok();
 }
@@ -1123,6 +1136,7 @@ stc_status stc_attend_compressed(const stc_head_info* k_info, const void* k_stat
                  nullptr, 1, 1, n_tokens, 0, static_cast<const unsigned char*>(k_packed_dev),
                  static_cast<const unsigned char*>(v_packed_dev), group, q_dev, out_dev, scale,
                  static_cast<unsigned char*>(ws_dev), std::max(mbk, mbv)};
+  a.rec = records_word_pow2(k_info, 1) && records_word_pow2(v_info, 1);
   if (launch_attend(a, stream)) return fail(STC_EDEVICE, "attend launch: %s", hipGetErrorString(hipGetLastError()));
   return ok();
 }

@@ -171,6 +171,7 @@ struct AttendLaunch {
   const unsigned char* k_sketch = nullptr;  // Walsh-Hadamard keys: residual sketch and |r|, or null
   const float* k_rnorm = nullptr;
   int64_t sketch_stride = 0, rnorm_stride = 0;
+  bool rec = false;  // every record is 0 or 32 * 2^s bits: one word-aligned LDS slot per record
 };
 
 int launch_gram(const void* x, int dtype, int64_t ld, int64_t n_calib, double* gram, void* stream);

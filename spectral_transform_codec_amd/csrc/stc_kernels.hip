@@ -815,6 +815,22 @@ __device__ __forceinline__ void est_store(unsigned* str, const unsigned (&w)[NW]
   }
 }
 
+// REC layout: word c = lane + 64k of a block of 32 records of 32 * 2^sh bits
+// (sh <= 5) goes to c + (c >> sh), so record T starts at word T (2^sh + 1):
+// one pad word after each record keeps the lanes' reads on distinct banks.
+template <int NW>
+__device__ __forceinline__ void rec_store(unsigned* str, const unsigned (&w)[NW], long long nbytes, int lane,
+                                          unsigned sh) {
+  const int nw = (int)(nbytes >> 2);
+  const unsigned stride = 64u + (64u >> sh);
+  unsigned* base = str + lane + ((unsigned)lane >> sh);
+#pragma unroll
+  for (int k = 0; k < NW; ++k) {
+    if (64 * k >= nw) break;
+    if (64 * k + 64 <= nw || lane + 64 * k < nw) base[k * stride] = w[k];
+  }
+}
+
 template <int F32OUT, int NW>
 __global__ void __launch_bounds__(DEC_THREADS, 1) k_decode_eigen(DecK a) {
   extern __shared__ __align__(16) unsigned char smem[];
@@ -1409,7 +1425,11 @@ constexpr int P_WORDS = 16 * P_ROWH / 2;
 constexpr int ATT_FIXED_BYTES = 32 * AROW + 6 * 128 * 4 + 64;  // a table, unpack tables, codebook planes
 // Words of one wave's region: the K and V record streams (reused for the
 // transposed V codes once both are extracted), P, and per-head alpha.
-__host__ __device__ constexpr int att_stream_words(int max_bits) { return max_bits + (max_bits >> 5) + 8; }
+// (a block's 32 records with one pad word per 32-word run, or, in the REC
+// layout, one pad word per record)
+__host__ __device__ constexpr int att_stream_words(int max_bits) {
+  return max_bits + ((max_bits >> 5) > 32 ? (max_bits >> 5) : 32) + 8;
+}
 __host__ __device__ constexpr int att_region_words(int max_bits) {
   return (2 * att_stream_words(max_bits) > VT_WORDS ? 2 * att_stream_words(max_bits) : VT_WORDS) + P_WORDS + 32;
 }
@@ -1476,10 +1496,12 @@ __device__ __forceinline__ float half_sum(float x) {
   return __builtin_bit_cast(float, r0) + __builtin_bit_cast(float, r1);
 }
 
-// Per-lane unpack tables of a state: group record offset, offset inside the
-// group, width (128 each).
+// Per-lane unpack tables of a state: group record offset (entry 4g + 1:
+// the byte offset of the word that holds it), offset inside the group,
+// width (128 each).
 __device__ __forceinline__ void att_tables(const DevHdr* hd, unsigned* tab, int c) {
-  tab[c] = (unsigned)hd->off[c & ~3];
+  const unsigned go = (unsigned)hd->off[c & ~3];
+  tab[c] = (c & 3) == 1 ? (go >> 5) << 2 : go;
   tab[128 + c] = (unsigned)hd->off[c] - (unsigned)hd->off[c & ~3];
   tab[256 + c] = (unsigned)hd->bits[c];
 }
@@ -1492,17 +1514,32 @@ __device__ __forceinline__ unsigned att_window(const lds_u8* sb, unsigned P) {
   const lds_u8* p = sb + (est_idx_bit(P) << 2);
   return __builtin_amdgcn_alignbit(LDS_AT(unsigned, p + 4), LDS_AT(unsigned, p), P & 31u);
 }
+// REC layout (records of 32 * 2^s bits, each on its own word-aligned slot
+// of the wave's stream): str is the lane's record, and the group's word and
+// bit offsets are uniform, so the window is one add and one funnel shift.
+// Otherwise str is the stream and tB the bit where the lane's record starts.
+template <bool REC>
+__device__ __forceinline__ unsigned att_group_window(const lds_u8* str, const lds_u8* tL, unsigned tB, int g) {
+  if (REC) {
+    const u32x2 t = LDS_AT(u32x2, tL + 16 * g);
+    const lds_u8* p = str + t[1];
+    return __builtin_amdgcn_alignbit(LDS_AT(unsigned, p + 4), LDS_AT(unsigned, p), t[0] & 31u);
+  }
+  return att_window(str, tB + LDS_AT(unsigned, tL + 16 * g));
+}
 // the four codes of group g as floats (exact)
+template <bool REC>
 __device__ __forceinline__ void att_group_codes(const lds_u8* str, const lds_u8* tL, unsigned tB, int g,
                                                 float c[4]) {
-  const unsigned w = att_window(str, tB + LDS_AT(unsigned, tL + 16 * g));
+  const unsigned w = att_group_window<REC>(str, tL, tB, g);
   const u32x4 pos = LDS_AT(u32x4, tL + 512 + 16 * g);
   const u32x4 wid = LDS_AT(u32x4, tL + 1024 + 16 * g);
 #pragma unroll
   for (int j = 0; j < 4; ++j) c[j] = (float)__builtin_amdgcn_ubfe(w, pos[j], wid[j]);
 }
+template <bool REC>
 __device__ __forceinline__ unsigned att_group_bytes(const lds_u8* str, const lds_u8* tL, unsigned tB, int g) {
-  const unsigned w = att_window(str, tB + LDS_AT(unsigned, tL + 16 * g));
+  const unsigned w = att_group_window<REC>(str, tL, tB, g);
   const u32x4 pos = LDS_AT(u32x4, tL + 512 + 16 * g);
   const u32x4 wid = LDS_AT(u32x4, tL + 1024 + 16 * g);
   unsigned v = __builtin_amdgcn_ubfe(w, pos[0], wid[0]);
@@ -1602,7 +1639,7 @@ __global__ void __launch_bounds__(CMB_THREADS) k_att_combine(AttK a) {
   if (t < 128) a.out[(pg * g + hh) * 128 + i] = (sQ[i] + sQ[128 + i]) + (sQ[256 + i] + sQ[384 + i]);
 }
 
-template <int NW, bool RHT, bool SKETCH>
+template <int NW, bool RHT, bool SKETCH, bool REC>
 __global__ void __launch_bounds__(ATT_THREADS, 1) k_att_main(AttK a) {
   extern __shared__ __align__(16) unsigned char smem[];
   unsigned char* sA = smem;                                        // a table [32][AROW]
@@ -1748,23 +1785,31 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_att_main(AttK a) {
   for (int nb = 0; nb < 8; ++nb) acc_o[nb] = (f32x4){0.f, 0.f, 0.f, 0.f};
   float vscale = 1.0f;  // RHT: acc_o is in units of the current block's largest value norm
 
-  if (t_first < t_end) {  // (the a-table build is done with the wave regions)
-    est_store<NW>(sKs, wk, Bk ? nbk : 0, lane);
-    est_store<NW>(sVs, wv, Bv ? nbv : 0, lane);
-  }
+  // REC: records of 32 * 2^s bits (or none), each on its own slot
+  const unsigned shk = Bk ? (unsigned)__builtin_ctz(Bk >> 5) : 0u, shv = Bv ? (unsigned)__builtin_ctz(Bv >> 5) : 0u;
+  const unsigned rk4 = Bk ? ((Bk >> 5) + 1u) * 4u : 0u, rv4 = Bv ? ((Bv >> 5) + 1u) * 4u : 0u;
+  auto store_records = [&]() {
+    if (REC) {
+      rec_store<NW>(sKs, wk, Bk ? nbk : 0, lane, shk);
+      rec_store<NW>(sVs, wv, Bv ? nbv : 0, lane, shv);
+    } else {
+      est_store<NW>(sKs, wk, Bk ? nbk : 0, lane);
+      est_store<NW>(sVs, wv, Bv ? nbv : 0, lane);
+    }
+  };
+  if (t_first < t_end) store_records();  // (the a-table build is done with the wave regions)
   for (long long tok0 = t_first; tok0 < t_end; tok0 += (long long)nwav * ATT_BT) {
     // ---- records -> the wave's streams
     if (tok0 != t_first) {
       load_records(tok0);
-      est_store<NW>(sKs, wk, Bk ? nbk : 0, lane);
-      est_store<NW>(sVs, wv, Bv ? nbv : 0, lane);
+      store_records();
     }
     __builtin_amdgcn_s_waitcnt(0xc07f);
     __builtin_amdgcn_wave_barrier();
     unsigned kb = lds_offset(reinterpret_cast<unsigned char*>(sTab + 64 * h));
     unsigned ab = lds_offset(sA + t32 * AROW + 128 * h);
-    unsigned ksb = lds_offset(reinterpret_cast<unsigned char*>(sKs));
-    unsigned vsb = lds_offset(reinterpret_cast<unsigned char*>(sVs));
+    unsigned ksb = lds_offset(reinterpret_cast<unsigned char*>(sKs)) + (REC ? (unsigned)t32 * rk4 : 0u);
+    unsigned vsb = lds_offset(reinterpret_cast<unsigned char*>(sVs)) + (REC ? (unsigned)t32 * rv4 : 0u);
     asm volatile("" : "+v"(kb), "+v"(ab), "+v"(ksb), "+v"(vsb));
     const lds_u8* kSL = lds_ptr(ksb);
     const lds_u8* vSL = lds_ptr(vsb);
@@ -1796,7 +1841,7 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_att_main(AttK a) {
           u32x4 fh, fl;
 #pragma unroll
           for (int hg = 0; hg < 2; ++hg) {
-            const unsigned v = att_group_bytes(kSL, kL, tB, 2 * ks + hg);
+            const unsigned v = att_group_bytes<false>(kSL, kL, tB, 2 * ks + hg);
             const u32x2 vh = lut16x4(v, cbh[0], cbh[1], cbh[2], cbh[3]);
             const u32x2 vl = lut16x4(v, cbl[0], cbl[1], cbl[2], cbl[3]);
             fh[2 * hg] = vh[0]; fh[2 * hg + 1] = vh[1];
@@ -1812,7 +1857,7 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_att_main(AttK a) {
 #pragma unroll
           for (int hg = 0; hg < 2; ++hg) {
             float c[4];
-            att_group_codes(kSL, kL, tB, 2 * ks + hg, c);
+            att_group_codes<REC>(kSL, kL, tB, 2 * ks + hg, c);
             bf[2 * hg] = bf16_pair_exact(c[0], c[1]);
             bf[2 * hg + 1] = bf16_pair_exact(c[2], c[3]);
           }
@@ -1915,7 +1960,7 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_att_main(AttK a) {
     {
       const unsigned tB = (unsigned)t32 * Bv;
 #pragma unroll
-      for (int gg = 0; gg < 16; ++gg) gvb[gg] = att_group_bytes(vSL, vL, tB, gg);  // all 0 if Bv = 0 (zero widths)
+      for (int gg = 0; gg < 16; ++gg) gvb[gg] = att_group_bytes<REC>(vSL, vL, tB, gg);  // all 0 if Bv = 0 (zero widths)
     }
     __builtin_amdgcn_s_waitcnt(0xc07f);
     __builtin_amdgcn_wave_barrier();
@@ -2011,22 +2056,26 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_att_main(AttK a) {
   }
 }
 
+typedef void (*AttKernel)(AttK);
+// variant: [RHT+sketch, sketch, sketch >512, RHT, -, >512] x [stream, REC]
+static const AttKernel kAttKernels[6][2] = {
+    {k_att_main<8, true, true, false>, k_att_main<8, true, true, false>},
+    {k_att_main<8, false, true, false>, k_att_main<8, false, true, true>},
+    {k_att_main<16, false, true, false>, k_att_main<16, false, true, true>},
+    {k_att_main<8, true, false, false>, k_att_main<8, true, false, false>},
+    {k_att_main<8, false, false, false>, k_att_main<8, false, false, true>},
+    {k_att_main<16, false, false, false>, k_att_main<16, false, false, true>},
+};
+
 int launch_attend(const AttendLaunch& L, void* stream) {
   if (!g_att_attr_done) {
-    if (hipFuncSetAttribute((const void*)k_att_main<8, false, false>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            160 * 1024) != hipSuccess ||
-        hipFuncSetAttribute((const void*)k_att_main<16, false, false>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            160 * 1024) != hipSuccess ||
-        hipFuncSetAttribute((const void*)k_att_main<8, true, false>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            160 * 1024) != hipSuccess ||
-        hipFuncSetAttribute((const void*)k_att_main<8, true, true>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            160 * 1024) != hipSuccess ||
-        hipFuncSetAttribute((const void*)k_att_main<8, false, true>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            160 * 1024) != hipSuccess ||
-        hipFuncSetAttribute((const void*)k_att_main<16, false, true>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            160 * 1024) != hipSuccess ||
-        hipFuncSetAttribute((const void*)k_att_combine, hipFuncAttributeMaxDynamicSharedMemorySize, (int)CMB_LDS) !=
+    for (const auto& row : kAttKernels)
+      for (AttKernel k : row)
+        if (hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) !=
             hipSuccess)
+          return 1;
+    if (hipFuncSetAttribute((const void*)k_att_combine, hipFuncAttributeMaxDynamicSharedMemorySize, (int)CMB_LDS) !=
+        hipSuccess)
       return 1;
     g_att_attr_done = true;
   }
@@ -2071,18 +2120,8 @@ int launch_attend(const AttendLaunch& L, void* stream) {
     a.n_splits = att_n_splits(np, L.n_tokens);
     const size_t att_lds = fixed + (size_t)waves * a.region_words * 4;
     const dim3 grid((unsigned)a.n_splits, (unsigned)np);
-    if (sketch && L.rht)
-      hipLaunchKernelGGL((k_att_main<8, true, true>), grid, dim3(64 * waves), att_lds, s, a);
-    else if (sketch && L.max_bits <= 512)
-      hipLaunchKernelGGL((k_att_main<8, false, true>), grid, dim3(64 * waves), att_lds, s, a);
-    else if (sketch)
-      hipLaunchKernelGGL((k_att_main<16, false, true>), grid, dim3(64 * waves), att_lds, s, a);
-    else if (L.rht)
-      hipLaunchKernelGGL((k_att_main<8, true, false>), grid, dim3(64 * waves), att_lds, s, a);
-    else if (L.max_bits <= 512)
-      hipLaunchKernelGGL((k_att_main<8, false, false>), grid, dim3(64 * waves), att_lds, s, a);
-    else
-      hipLaunchKernelGGL((k_att_main<16, false, false>), grid, dim3(64 * waves), att_lds, s, a);
+    const int var = sketch ? (L.rht ? 0 : (L.max_bits <= 512 ? 1 : 2)) : (L.rht ? 3 : (L.max_bits <= 512 ? 4 : 5));
+    hipLaunchKernelGGL(kAttKernels[var][L.rec && !L.rht ? 1 : 0], grid, dim3(64 * waves), att_lds, s, a);
     // the splits' partials -> out, once every split has written its own
     hipLaunchKernelGGL(k_att_combine, dim3((unsigned)np, (unsigned)L.group), dim3(CMB_THREADS), CMB_LDS, s, a);
   }
