@@ -1402,6 +1402,7 @@ struct AttK {
   const float* q;
   float* out;
   float scale;
+  float v_code_offset;  // added to every V code in P.V (removed at the split merge)
   unsigned char* ws;
   long long split_tokens, n_splits;
   int stream_words, region_words;
@@ -1437,14 +1438,14 @@ __host__ __device__ constexpr int att_region_words(int max_bits) {
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
-// 4 unsigned byte codes -> 4 fp16 (exact): 0x64xx is 1024 + xx in fp16.
-__device__ __forceinline__ f16x4 bytes_to_f16x4(unsigned v) {
+// 4 unsigned byte codes c -> 4 fp16 1024 + c (exact: 0x64xx in fp16), two
+// byte permutes. P.V then sums p (1024 + c); the split merge divides by the
+// sum of the same fp16 p and removes the 1024.
+constexpr float ATT_V_CODE_OFFSET = 1024.0f;
+__device__ __forceinline__ f16x4 bytes_to_f16x4_biased(unsigned v) {
   const unsigned lo = __builtin_amdgcn_perm(v, 0x64646464u, 0x00050004u);
   const unsigned hi = __builtin_amdgcn_perm(v, 0x64646464u, 0x00070006u);
-  const f16x2 off = {(_Float16)1024.0f, (_Float16)1024.0f};
-  const f16x2 a = __builtin_bit_cast(f16x2, lo) - off;
-  const f16x2 b = __builtin_bit_cast(f16x2, hi) - off;
-  return (f16x4){a[0], a[1], b[0], b[1]};
+  return __builtin_bit_cast(f16x4, (u32x2){lo, hi});
 }
 
 // Four codes (bytes of c, each 0..7) -> four 16-bit table entries, from the
@@ -1542,11 +1543,11 @@ __device__ __forceinline__ unsigned att_group_bytes(const lds_u8* str, const lds
   const unsigned w = att_group_window<REC>(str, tL, tB, g);
   const u32x4 pos = LDS_AT(u32x4, tL + 512 + 16 * g);
   const u32x4 wid = LDS_AT(u32x4, tL + 1024 + 16 * g);
-  unsigned v = __builtin_amdgcn_ubfe(w, pos[0], wid[0]);
-  v |= __builtin_amdgcn_ubfe(w, pos[1], wid[1]) << 8;
-  v |= __builtin_amdgcn_ubfe(w, pos[2], wid[2]) << 16;
-  v |= __builtin_amdgcn_ubfe(w, pos[3], wid[3]) << 24;
-  return v;
+  const unsigned c0 = __builtin_amdgcn_ubfe(w, pos[0], wid[0]), c1 = __builtin_amdgcn_ubfe(w, pos[1], wid[1]);
+  const unsigned c2 = __builtin_amdgcn_ubfe(w, pos[2], wid[2]), c3 = __builtin_amdgcn_ubfe(w, pos[3], wid[3]);
+  // bytes (c0, c1, 0, 0) and (c2, c3, 0, 0), then (c0, c1, c2, c3)
+  return __builtin_amdgcn_perm(__builtin_amdgcn_perm(c3, c2, 0x0C0C0400u), __builtin_amdgcn_perm(c1, c0, 0x0C0C0400u),
+                               0x05040100u);
 }
 
 
@@ -1622,8 +1623,8 @@ __global__ void __launch_bounds__(CMB_THREADS) k_att_combine(AttK a) {
         M = Mc;
       }
     }
-    // dequantize the mean code: step * (A / L - (L_j - 1)/2)
-    sC[j] = bits ? (float)((double)step * (A / L - (double)hs)) : 0.0f;
+    // dequantize the mean code: step * (A / L - offset - (L_j - 1)/2)
+    sC[j] = bits ? (float)((double)step * (A / L - (double)a.v_code_offset - (double)hs)) : 0.0f;
   }
   __syncthreads();
   float o = 0.0f;
@@ -1995,7 +1996,7 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_att_main(AttK a) {
           const unsigned vb = sVT[(16 * nb + c16) * VT_ROW + 4 * kt + g4];
           f16x4 vf;
           if (RHT) vf = __builtin_bit_cast(f16x4, lut16x4(vb, cbv[0], cbv[1], cbv[2], cbv[3]));
-          else vf = bytes_to_f16x4(vb);
+          else vf = bytes_to_f16x4_biased(vb);
           acc_o[nb] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, vf, acc_o[nb], 0, 0, 0);
         }
       }
@@ -2094,6 +2095,7 @@ int launch_attend(const AttendLaunch& L, void* stream) {
   a.q = L.q;
   a.out = L.out;
   a.scale = L.scale;
+  a.v_code_offset = L.rht ? 0.0f : ATT_V_CODE_OFFSET;  // (Walsh-Hadamard V codes go through the codebook)
   a.ws = L.ws;
   a.k_norms = L.k_norms;
   a.v_norms = L.v_norms;

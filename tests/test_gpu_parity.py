@@ -296,6 +296,43 @@ def test_attention_zero_bit_streams():
             assert rel_err(out[i], wants[i]) <= 2e-3, (i, rel_err(out[i], wants[i]))
 
 
+@pytest.mark.parametrize("budget", [1.0, 2.0, 4.0, 8.0])
+def test_attention_record_layouts_agree(budget):
+    """Records of 32 * 2^s bits (here 128, 256, 512, 1024) are staged one per
+    word-aligned slot; a state array that also holds a 1.33-bit state (170-bit
+    records) makes the same pairs go through the packed stream layout. The
+    two layouts feed the same codes to the same arithmetic: outputs agree
+    bit for bit, and both match the oracle."""
+    w = synth.WORKLOADS[2]
+    n = 1700
+    states, kps, vps, qs, wants = [], [], [], [], []
+    for hd in range(3):
+        k = synth.stream(w, 0, 0, hd, 0, n=n)
+        v = synth.stream(w, 0, 0, hd, 1, n=n)
+        ks, vs = codec.calibrate_head(k, 1024, budget), codec.calibrate_head(v, 1024, budget)
+        assert int(ks["bits"].sum()) == int(vs["bits"].sum()) == round(128 * budget)
+        kp, vp = codec.encode_kv(ks, k), codec.encode_kv(vs, v)
+        q = synth.queries(w, 0, 0, hd)
+        wants.append(codec.attend_compressed(ks, vs, kp, vp, n, q.astype(np.float64)))
+        states += [gpu_state(ks), gpu_state(vs)]
+        kps.append(kp); vps.append(vp); qs.append(q)
+    odd = gpu_state(codec.calibrate_head(synth.stream(w, 0, 0, 7, 0, n=n), 1024, 1.33))
+    outs = []
+    for arr in (stc.StateArray(states), stc.StateArray(states + [odd])):
+        stride = stc.packed_bytes(arr.max_bits, n)
+        kb = np.zeros((3, stride), dtype=np.uint8)
+        vb = np.zeros((3, stride), dtype=np.uint8)
+        for i in range(3):
+            kb[i, :kps[i].shape[0]] = kps[i]; vb[i, :vps[i].shape[0]] = vps[i]
+        kmap = torch.arange(0, 6, 2, dtype=torch.int32, device=DEV)
+        outs.append(stc.attend_compressed_batched(arr, kmap, kmap + 1, torch.from_numpy(kb).to(DEV),
+                                                  torch.from_numpy(vb).to(DEV), n,
+                                                  torch.from_numpy(np.stack(qs)).to(DEV)).cpu().numpy())
+    assert np.array_equal(outs[0], outs[1])
+    for i in range(3):
+        assert rel_err(outs[0][i], wants[i]) <= 2e-3, (i, rel_err(outs[0][i], wants[i]))
+
+
 # ---------------------------------------------------------- batched codec
 def test_batched_encode_decode_shared_states():
     w = synth.WORKLOADS[5]
