@@ -226,7 +226,10 @@ stc_status stc_state_basis(const void* state_dev, float* u_out, stc_stream_t str
  * norms (Walsh-Hadamard states only) norms_dev + s*n_tokens. All streams of a
  * call have n_tokens tokens and use states of one family (all EIGEN/IDENTITY,
  * or all RHT). infos[n_states] are the host summaries of the states, used for
- * validation (packed_stream_stride must hold the largest stream).
+ * validation (packed_stream_stride must hold the largest stream) and to size
+ * and choose the kernels' on-chip layouts: each must be the one
+ * stc_calibrate_head or stc_state_init gave for its state; one that disagrees with
+ * its state is undefined behaviour.
  * x rows must be 16-byte aligned (ld*elem and x_stream_stride*elem multiples
  * of 16); packed_stream_stride a multiple of 16.                         */
 
