@@ -872,6 +872,7 @@ static stc_status encode_impl(const char* who, const void* states_dev, int64_t n
                  x_stream_stride, packed_stream_stride, x_dev, static_cast<unsigned char*>(packed_dev), norms_dev,
                  dtype == STC_F32 ? 1 : 0, mb, n_old, norms_stream_stride,
                  static_cast<unsigned char*>(sketch_dev), rnorm_dev, sketch_stream_stride, rnorm_stream_stride};
+  a.rec = records_word_pow2(infos, n_states);
   const int rc = rht ? launch_encode_rht(a, stream) : launch_encode_eigen(a, stream);
   if (rc) return fail(STC_EDEVICE, "%s launch: %s", who, hipGetErrorString(hipGetLastError()));
   return ok();

@@ -137,6 +137,7 @@ struct EncodeLaunch {
   unsigned char* sketch = nullptr;  // Walsh-Hadamard key residual sketch (16 bytes per token) or null
   float* rnorm = nullptr;           // |r| per token
   int64_t sketch_stride = 0, rnorm_stride = 0;
+  bool rec = false;  // every record is 0 or 32 * 2^s bits: the slot layout
 };
 struct DecodeLaunch {
   const unsigned char* states;

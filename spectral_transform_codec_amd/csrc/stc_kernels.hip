@@ -204,8 +204,32 @@ __device__ __forceinline__ void est_copy_out(unsigned* str, unsigned char* dst, 
   for (unsigned i = lane; i < clear; i += 64) str[i] = 0u;
 }
 
+// Slot layout (records of 32 * 2^sh bits): word w of the block sits at
+// w + (w >> sh), one pad word after each record; records never spill into
+// their pad, so the copy needs no folding.
+template <int CW>
+__device__ __forceinline__ void rec_copy_out(unsigned* str, unsigned char* dst, long long nbytes, unsigned clear,
+                                             int lane, unsigned sh) {
+  typedef unsigned vec __attribute__((ext_vector_type(CW)));
+  const int nchunk = (int)(nbytes / (4 * CW));
+  for (int c = lane; c < nchunk; c += 64) {
+    vec v;
+#pragma unroll
+    for (int e = 0; e < CW; ++e) {
+      const unsigned w = (unsigned)(CW * c + e);
+      v[e] = str[w + (w >> sh)];
+    }
+    reinterpret_cast<vec*>(dst)[c] = v;
+  }
+  __builtin_amdgcn_s_waitcnt(0xc07f);
+  __builtin_amdgcn_wave_barrier();
+  for (unsigned i = lane; i < clear; i += 64) str[i] = 0u;
+}
+
 // MODE 0: bf16 tokens, 1: fp32 tokens, 2: fp32 latent coefficients [n][128].
-template <int MODE>
+// REC (MODE 0 and 1): every record is 32 * 2^s bits, staged in the slot
+// layout, so a group's word and shift are table entries.
+template <int MODE, bool REC>
 __global__ void __launch_bounds__(ENC_THREADS, 1) k_encode_eigen(EncK a) {
   extern __shared__ __align__(16) unsigned char smem[];
   unsigned char* sUhi = smem;
@@ -276,14 +300,18 @@ __global__ void __launch_bounds__(ENC_THREADS, 1) k_encode_eigen(EncK a) {
         sInv[tid] = hdr->yhalf[tid];
         sInv[128 + tid] = (float)hdr->lm1[tid];
         reinterpret_cast<unsigned*>(sInv)[256 + tid] = (unsigned)hdr->off[tid] - (unsigned)hdr->off[tid & ~3];
-        reinterpret_cast<unsigned*>(sInv)[384 + tid] = (unsigned)hdr->off[tid & ~3];
+        // group record offset; entries 4g + 1, 4g + 2: the byte offset of
+        // its word in a record slot and the shift inside it
+        const unsigned go = (unsigned)hdr->off[tid & ~3];
+        reinterpret_cast<unsigned*>(sInv)[384 + tid] = (tid & 3) == 1 ? (go >> 5) << 2 : ((tid & 3) == 2 ? go & 31u : go);
       }
     }
     __syncthreads();
     if (B > 0) {
       const long long P_len = packed_len((long long)B, n);
       const unsigned cw_kind = (B & 3u) == 0u ? 4u : ((B & 1u) == 0u ? 2u : 1u);
-      const unsigned clear = est_idx(B + 4u) + 2u;
+      const unsigned rsh = (unsigned)__builtin_ctz((B >> 5) | 64u);  // REC: log2 of the words a record
+      const unsigned clear = REC ? 32u * ((B >> 5) + 1u) + 2u : est_idx(B + 4u) + 2u;
       // bf16 tokens: a block's fragments are requested as soon as the
       // previous block's last MFMA has read its own (same registers), so the
       // load runs under that block's last quantization and copy-out
@@ -319,13 +347,24 @@ __global__ void __launch_bounds__(ENC_THREADS, 1) k_encode_eigen(EncK a) {
         const lds_u8* pL = lds_ptr(pb);
         const bool tok_ok = tok0 + t32 >= n0 && tok0 + t32 < n;
         const unsigned tB = (unsigned)t32 * B;
+        unsigned rb = REC ? t32 * ((B >> 5) + 1u) * 4u : 0u;  // REC: byte offset of the lane's slot
+        if (REC) asm volatile("" : "+v"(rb));
+        unsigned char* sRec = reinterpret_cast<unsigned char*>(sStr) + rb;
         // ---- 3: OR a group word into the stream at record bit tB + goff; a
         // lane whose token is outside the call ORs zero (no branch, so that
-        // this work can overlap the next row block's MFMA chain)
-        auto put_group = [&](unsigned word, unsigned goff) {
-          const unsigned P = tB + goff;
-          const unsigned long long v = (unsigned long long)(tok_ok ? word : 0u) << (P & 31u);
-          unsigned* dst = sStr + est_idx_bit(P);
+        // this work can overlap the next row block's MFMA chain). gt: the
+        // group's offset, word byte offset and shift (REC) from the table.
+        auto put_group = [&](unsigned word, u32x4 gt) {
+          unsigned* dst;
+          unsigned long long v;
+          if (REC) {
+            v = (unsigned long long)(tok_ok ? word : 0u) << gt[2];
+            dst = reinterpret_cast<unsigned*>(sRec + gt[1]);
+          } else {
+            const unsigned P = tB + gt[0];
+            v = (unsigned long long)(tok_ok ? word : 0u) << (P & 31u);
+            dst = sStr + est_idx_bit(P);
+          }
           __hip_atomic_fetch_or(dst, (unsigned)v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
           __hip_atomic_fetch_or(dst + 1, (unsigned)(v >> 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         };
@@ -355,11 +394,13 @@ __global__ void __launch_bounds__(ENC_THREADS, 1) k_encode_eigen(EncK a) {
             const int coff = 4 * (16 * mb + 4 * i);  // byte offset of the group in a table
             const f32x4 lm = LDS_AT(f32x4, pL + 512 + coff);
             const u32x4 pos = LDS_AT(u32x4, pL + 1024 + coff);
-            const unsigned goff = LDS_AT(unsigned, pL + 1536 + coff);
+            u32x4 gt;
+            if (REC) gt = LDS_AT(u32x4, pL + 1536 + coff);
+            else gt[0] = LDS_AT(unsigned, pL + 1536 + coff);
             unsigned q[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) q[j] = (unsigned)__builtin_amdgcn_fmed3f(acc[4 * i + j], 0.0f, lm[j]);
-            put_group(q[0] | (q[1] << pos[1]) | (q[2] << pos[2]) | (q[3] << pos[3]), goff);
+            put_group(q[0] | (q[1] << pos[1]) | (q[2] << pos[2]) | (q[3] << pos[3]), gt);
           };
           // Two accumulators, interleaved in program order: while the chain
           // of row block mb + 1 runs on the MFMA unit, row block mb is
@@ -441,7 +482,9 @@ __global__ void __launch_bounds__(ENC_THREADS, 1) k_encode_eigen(EncK a) {
                   }
                 }
               }
-              put_group(q[0] | (q[1] << pos[1]) | (q[2] << pos[2]) | (q[3] << pos[3]), goff);
+              u32x4 gt;
+              gt[0] = goff;
+              put_group(q[0] | (q[1] << pos[1]) | (q[2] << pos[2]) | (q[3] << pos[3]), gt);
             }
           }
         }
@@ -461,12 +504,13 @@ __global__ void __launch_bounds__(ENC_THREADS, 1) k_encode_eigen(EncK a) {
           const unsigned* old = reinterpret_cast<const unsigned*>(dst);
           for (unsigned w2 = lane; w2 < wold; w2 += 64) {
             const unsigned rb = oldbits - 32u * w2;  // old bits in this word (all of them if >= 32)
-            sStr[est_idx(w2)] |= old[w2] & (rb >= 32u ? ~0u : (1u << rb) - 1u);
+            sStr[REC ? w2 + (w2 >> rsh) : est_idx(w2)] |= old[w2] & (rb >= 32u ? ~0u : (1u << rb) - 1u);
           }
           __builtin_amdgcn_s_waitcnt(0xc07f);
           __builtin_amdgcn_wave_barrier();
         }
-        if (cw_kind == 4u) est_copy_out<4>(sStr, dst, nbytes, clear, lane);
+        if (REC) rec_copy_out<4>(sStr, dst, nbytes, clear, lane, rsh);  // (records of 32 * 2^s bits: whole words)
+        else if (cw_kind == 4u) est_copy_out<4>(sStr, dst, nbytes, clear, lane);
         else if (cw_kind == 2u) est_copy_out<2>(sStr, dst, nbytes, clear, lane);
         else est_copy_out<1>(sStr, dst, nbytes, clear, lane);
       }
@@ -637,9 +681,10 @@ static bool g_enc_attr_done = false, g_dec_attr_done = false, g_att_attr_done = 
 
 int launch_encode_eigen(const EncodeLaunch& L, void* stream) {
   if (!g_enc_attr_done) {
-    if (hipFuncSetAttribute((const void*)k_encode_eigen<0>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)ENC_LDS) != hipSuccess) return 1;
-    if (hipFuncSetAttribute((const void*)k_encode_eigen<1>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)ENC_LDS) != hipSuccess) return 1;
-    if (hipFuncSetAttribute((const void*)k_encode_eigen<2>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)ENC_LDS) != hipSuccess) return 1;
+    for (const void* k : {(const void*)k_encode_eigen<0, false>, (const void*)k_encode_eigen<1, false>,
+                          (const void*)k_encode_eigen<2, false>, (const void*)k_encode_eigen<0, true>,
+                          (const void*)k_encode_eigen<1, true>})
+      if (hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)ENC_LDS) != hipSuccess) return 1;
     g_enc_attr_done = true;
   }
   EncK a;
@@ -667,9 +712,11 @@ int launch_encode_eigen(const EncodeLaunch& L, void* stream) {
   grid = (a.total_blocks + a.blocks_per_wg - 1) / a.blocks_per_wg;
   a.grid = (int)grid;
   hipStream_t s = (hipStream_t)stream;
-  if (L.mode == 0) hipLaunchKernelGGL(k_encode_eigen<0>, dim3(grid), dim3(ENC_THREADS), ENC_LDS, s, a);
-  else if (L.mode == 1) hipLaunchKernelGGL(k_encode_eigen<1>, dim3(grid), dim3(ENC_THREADS), ENC_LDS, s, a);
-  else hipLaunchKernelGGL(k_encode_eigen<2>, dim3(grid), dim3(ENC_THREADS), ENC_LDS, s, a);
+  if (L.mode == 0 && L.rec) hipLaunchKernelGGL((k_encode_eigen<0, true>), dim3(grid), dim3(ENC_THREADS), ENC_LDS, s, a);
+  else if (L.mode == 0) hipLaunchKernelGGL((k_encode_eigen<0, false>), dim3(grid), dim3(ENC_THREADS), ENC_LDS, s, a);
+  else if (L.mode == 1 && L.rec) hipLaunchKernelGGL((k_encode_eigen<1, true>), dim3(grid), dim3(ENC_THREADS), ENC_LDS, s, a);
+  else if (L.mode == 1) hipLaunchKernelGGL((k_encode_eigen<1, false>), dim3(grid), dim3(ENC_THREADS), ENC_LDS, s, a);
+  else hipLaunchKernelGGL((k_encode_eigen<2, false>), dim3(grid), dim3(ENC_THREADS), ENC_LDS, s, a);
   return hipGetLastError() != hipSuccess;
 }
 
