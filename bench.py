@@ -65,12 +65,16 @@ def parse():
 # reported for the kernel with the largest share of the step.
 KERNEL_OF_OP = {"encode": "k_encode_eigen<bf16>", "decode": "k_decode_eigen<bf16>",
                 "attend": "k_att_main", "rht_encode": "k_rht_encode", "rht_decode": "k_rht_decode"}
-# rocprofv3 kernel names of the same kernels
-PROFILE_NAME = {"k_encode_eigen<bf16>": "void stc::k_encode_eigen<0>(stc::EncK)",
-                "k_decode_eigen<bf16>": "void stc::k_decode_eigen<0, 8>(stc::DecK)",
-                "k_att_main": "void stc::k_att_main<8, false, false>(stc::AttK)",
-                "k_rht_encode": "void stc::k_rht_encode<false>(stc::RhtK)",
-                "k_rht_decode": "stc::k_rht_decode(stc::RhtK)"}
+# rocprofv3 kernel names of the same kernels (the variants the step runs:
+# records of 32 * 2^s bits at 4.0 and 2.0 bits take the slot-layout variant,
+# the 170-bit records at 1.33 bits the packed-stream one)
+PROFILE_NAME = {"k_encode_eigen<bf16>": ("void stc::k_encode_eigen<0, true>(stc::EncK)",
+                                         "void stc::k_encode_eigen<0, false>(stc::EncK)"),
+                "k_decode_eigen<bf16>": ("void stc::k_decode_eigen<0, 8>(stc::DecK)",),
+                "k_att_main": ("void stc::k_att_main<8, false, false, true>(stc::AttK)",
+                               "void stc::k_att_main<8, false, false, false>(stc::AttK)"),
+                "k_rht_encode": ("void stc::k_rht_encode<false>(stc::RhtK)",),
+                "k_rht_decode": ("stc::k_rht_decode(stc::RhtK)",)}
 KERNEL_SOURCE = os.path.join(ROOT, "spectral_transform_codec_amd", "csrc", "stc_kernels.hip")
 PROFILES = os.path.join(ROOT, "profiles")
 
@@ -621,10 +625,14 @@ def summarize(args):
         # 32-token blocks per launch of the Llama-layer step: 16 streams x
         # 32768 tokens for the codec kernels, 8 KV heads x 32768 for attention
         blocks = {"k_att_main": 8 * 32768 // 32}
-        for kname, pname in PROFILE_NAME.items():
-            if pname not in per:
+        for kname, pnames in PROFILE_NAME.items():
+            if not any(pn in per for pn in pnames):
                 continue
-            cs = per[pname]
+            cs = collections.defaultdict(list)  # dispatches of every variant
+            for pn in pnames:
+                for c, v in per.get(pn, {}).items():
+                    cs[c] += v
+            pname = " + ".join(pn for pn in pnames if pn in per)
             avg = {c: sum(v) / len(v) for c, v in cs.items()}
             nb = blocks.get(kname, 16 * 32768 // 32)
             out.append(f"== {kname}  ({pname}; {len(next(iter(cs.values())))} dispatches per counter)")
@@ -660,7 +668,7 @@ def summarize(args):
         return
     fetch_dir, write_dir = args.summarize
     kernel = args.kernel
-    pname = PROFILE_NAME.get(kernel, kernel)
+    pnames = PROFILE_NAME.get(kernel, (kernel,))
 
     def per_kernel(d, counter):
         vals = collections.defaultdict(lambda: collections.defaultdict(float))
@@ -677,7 +685,9 @@ def summarize(args):
     f_copy = max(fetch[copy_name]) * 1024.0
     w_copy = max(write[copy_name]) * 1024.0
     f_scale, w_scale = copy_bytes / f_copy, copy_bytes / w_copy
-    fk, wk = fetch[pname], write[pname]
+    fk = [v for pn in pnames for v in fetch.get(pn, [])]  # every variant's launches
+    wk = [v for pn in pnames for v in write.get(pn, [])]
+    pname = " + ".join(pn for pn in pnames if pn in fetch)
     f_avg = sum(fk) / len(fk) * 1024.0
     w_avg = sum(wk) / len(wk) * 1024.0
     traffic = f_avg * f_scale + w_avg * w_scale
