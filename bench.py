@@ -622,9 +622,11 @@ def summarize(args):
                 for cname, v in cs.items():
                     per[name][cname].append(v)
         out.append(f"kernel_source_sha256_16: {source_digest()}")
-        # 32-token blocks per launch of the Llama-layer step: 16 streams x
-        # 32768 tokens for the codec kernels, 8 KV heads x 32768 for attention
-        blocks = {"k_att_main": 8 * 32768 // 32}
+        # 32-token blocks per launch: Llama-layer step 16 streams x 32768
+        # tokens for the codec kernels, 8 KV heads x 32768 for attention; the
+        # Llama cache (--workload llama_cache) 512 streams and 256 KV heads x 131072
+        cache = args.workload == "llama_cache"
+        blocks = {"k_att_main": (256 * 131072 if cache else 8 * 32768) // 32}
         for kname, pnames in PROFILE_NAME.items():
             if not any(pn in per for pn in pnames):
                 continue
@@ -634,7 +636,7 @@ def summarize(args):
                     cs[c] += v
             pname = " + ".join(pn for pn in pnames if pn in per)
             avg = {c: sum(v) / len(v) for c, v in cs.items()}
-            nb = blocks.get(kname, 16 * 32768 // 32)
+            nb = blocks.get(kname, (512 * 131072 if cache else 16 * 32768) // 32)
             out.append(f"== {kname}  ({pname}; {len(next(iter(cs.values())))} dispatches per counter)")
             for c in sorted(avg):
                 out.append(f"   {c:40s} {avg[c]:18.1f}")
