@@ -1466,8 +1466,14 @@ constexpr int ATT_WAVES_MAX = 16;
 constexpr int ATT_THREADS = 64 * ATT_WAVES_MAX;
 constexpr int ATT_BT = 32;                       // tokens per wave block
 constexpr int AROW = 272;                        // bytes per a-table row (rows 0..15 hi, 16..31 lo)
-constexpr int VT_ROW = 9;                        // dwords per row of the [channel][token] V bytes
-constexpr int VT_WORDS = 128 * VT_ROW;
+// [channel][token] V bytes: 8 dwords a channel (4 tokens a dword), channels
+// 64..127 32 dwords further on and the dword index XOR 4 on channels with
+// bit 3 set, so that the quad-transposed writes (64 lanes: 2 halves x 4
+// channels x 8 token quads) and the P.V reads (16 channels x 4 token quads)
+// each touch 64 distinct banks
+constexpr int VT_ROW = 8;
+constexpr int VT_WORDS = 128 * VT_ROW + 32;
+__device__ __forceinline__ int vt_index(int c, int j) { return c * VT_ROW + ((c >> 6) << 5) + (j ^ (((c >> 3) & 1) << 2)); }
 constexpr int P_ROWH = 36;                       // fp16 per row of P [head][token]
 constexpr int P_WORDS = 16 * P_ROWH / 2;
 constexpr int ATT_FIXED_BYTES = 32 * AROW + 6 * 128 * 4 + 64;  // a table, unpack tables, codebook planes
@@ -2017,7 +2023,7 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_att_main(AttK a) {
 #pragma unroll
       for (int gg = 0; gg < 16; ++gg) {
         const unsigned tq = quad_transpose_bytes(gvb[gg], e);
-        sVT[(64 * h + 4 * gg + e) * VT_ROW + (t32 >> 2)] = tq;
+        sVT[vt_index(64 * h + 4 * gg + e, t32 >> 2)] = tq;
       }
     }
     __builtin_amdgcn_s_waitcnt(0xc07f);
@@ -2040,7 +2046,7 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_att_main(AttK a) {
         const f16x4 pa = *reinterpret_cast<const f16x4*>(sP + c16 * P_ROWH + 16 * kt + 4 * g4);
 #pragma unroll
         for (int nb = 0; nb < 8; ++nb) {
-          const unsigned vb = sVT[(16 * nb + c16) * VT_ROW + 4 * kt + g4];
+          const unsigned vb = sVT[vt_index(16 * nb + c16, 4 * kt + g4)];
           f16x4 vf;
           if (RHT) vf = __builtin_bit_cast(f16x4, lut16x4(vb, cbv[0], cbv[1], cbv[2], cbv[3]));
           else vf = bytes_to_f16x4_biased(vb);
