@@ -209,12 +209,43 @@ def _check_qjl_unbiased():
     tq.test_sketch_estimate_is_unbiased_on_real_codes()
 
 
+_orig_softmax = codec.softmax_attention
+
+
+def _softmax_extra_after_scale(q, khat, vhat, scale=None, extra=None):
+    d = khat.shape[1]
+    sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    if extra is None:
+        return _orig_softmax(q, khat, vhat, scale)
+    return _orig_softmax(q, khat, vhat, scale, np.asarray(extra) / sc)
+
+
+def _softmax_extra_negated(q, khat, vhat, scale=None, extra=None):
+    return _orig_softmax(q, khat, vhat, scale, None if extra is None else -np.asarray(extra))
+
+
+def _attend_eigen_raw_query(k_state, v_state, k_packed, sketch, rnorm, S, v_packed, n, q, scale=None):
+    khat = codec.reconstruct_exact(k_state, k_packed, n)
+    vhat = codec.reconstruct_exact(v_state, v_packed, n)
+    extra = qjl.score_correction(np.asarray(q, np.float64), sketch, rnorm, S, n)
+    return codec.softmax_attention(q, khat, vhat, scale, extra)
+
+
+def _check_sketch_attention():
+    tq.check_sketch_attention_converges_rht()
+    tq.check_sketch_attention_converges_eigen(0.75)
+
+
 @pytest.mark.parametrize("module,name,mutant,check", [
     (codec, "append_pack", _append_one_bit_late, _check_append),
     (codec, "allocate_bits", _alloc_operational_as_rd, tc.test_operational_allocation_is_optimal_by_brute_force),
     (codec, "allocate_bits", _alloc_grouped_by_max, tc.test_grouped_allocation_is_optimal_by_brute_force),
     (qjl, "score_correction", _corr_no_sqrt_pi_2, _check_qjl_unbiased),
-], ids=["append_one_bit_late", "operational_as_rd", "grouped_by_max", "qjl_no_sqrt_pi_2"])
+    (codec, "softmax_attention", _softmax_extra_after_scale, _check_sketch_attention),
+    (codec, "softmax_attention", _softmax_extra_negated, _check_sketch_attention),
+    (qjl, "attend_compressed_eigen", _attend_eigen_raw_query, _check_sketch_attention),
+], ids=["append_one_bit_late", "operational_as_rd", "grouped_by_max", "qjl_no_sqrt_pi_2",
+        "extra_after_scale", "extra_negated", "eigen_sketch_raw_query"])
 def test_later_row_mutant_is_caught(monkeypatch, module, name, mutant, check):
     assert not _fails(check)
     monkeypatch.setattr(module, name, mutant)

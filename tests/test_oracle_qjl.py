@@ -142,3 +142,138 @@ def test_selective_sketch_unbiased():
         sk, rn = qjl.sketch_encode_eigen(st, x, S)
         acc += base + qjl.score_correction(q @ st["U"], sk, rn, S, n)
     assert np.mean((acc / T - target) ** 2) < 0.02 * np.mean((base - target) ** 2)
+
+
+# ------------------------------------------- sketch-corrected attention (the extra term)
+def _attention_loops(q, K, V, scale):
+    """Textbook softmax attention written out token by token, fp64."""
+    g, n = q.shape[0], K.shape[0]
+    out = np.zeros((g, V.shape[1]))
+    for h in range(g):
+        s = [scale * float(np.dot(q[h], K[t])) for t in range(n)]
+        mx = max(s)
+        w = [math.exp(v - mx) for v in s]
+        tot = sum(w)
+        for t in range(n):
+            out[h] += (w[t] / tot) * V[t]
+    return out
+
+
+def test_extra_term_enters_before_the_scale():
+    """`extra` is an additive estimate of the part of q . k the reconstruction
+    misses: with extra = q . (k - K_hat) exactly, attention over K_hat equals
+    attention over the true keys; extra = 0 changes nothing."""
+    rng = np.random.default_rng(91)
+    d, n, g = 16, 9, 3
+    k = rng.standard_normal((n, d)) * 2.0
+    khat = k + 0.3 * rng.standard_normal((n, d))
+    v = rng.standard_normal((n, d))
+    q = rng.standard_normal((g, d))
+    exact = q @ (k - khat).T
+    want = _attention_loops(q, k, v, 1.0 / math.sqrt(d))
+    got = codec.softmax_attention(q, khat, v, extra=exact)
+    assert np.abs(got - want).max() <= 1e-6 * np.abs(want).max()
+    assert np.array_equal(codec.softmax_attention(q, khat, v, extra=np.zeros((g, n))),
+                          codec.softmax_attention(q, khat, v))
+    # the correction is not negligible here
+    assert np.abs(codec.softmax_attention(q, khat, v) - want).max() > 1e-2
+
+
+# With m sign rows the estimate of q_h . r_t has standard deviation
+# sigma_ht = |r_t| sqrt((pi/2 |q_h|^2 - (q_h . r_t / |r_t|)^2) / m) (the closed
+# form pinned above). If every score moves by at most D (here 5 sigma times the
+# softmax scale), output i moves by at most D R_i / 2, R_i the range of value
+# channel i over the tokens: d/dl softmax(s + l e) . v_i = Cov(e, v_i) under the
+# tilted weights, and |Cov| <= (range of e / 2)(range of v_i / 2) (Popoviciu).
+SKETCH_ROWS = 400_000
+
+
+def _convergence_bound(q, r, vhat, m, scale):
+    rn2 = np.sum(r * r, axis=1)
+    qn2 = np.sum(q * q, axis=1)
+    sig = np.sqrt(rn2[None, :] * (math.pi / 2) * qn2[:, None] / m)
+    delta = 5.0 * float(sig.max()) * scale
+    return delta * (vhat.max(axis=0) - vhat.min(axis=0)) / 2.0
+
+
+def _small_rht_caches(seed, d=16, n=10):
+    rng = np.random.default_rng(seed)
+    cb = rht.codebook_fp32(np.sort(rng.standard_normal(8)) / math.sqrt(d))
+    kst = rht.make_state(np.where(rng.random(d) < 0.5, -1, 1), cb)
+    vst = rht.make_state(np.where(rng.random(d) < 0.5, -1, 1), cb)
+    k = rng.standard_t(3, (n, d))
+    v = rng.standard_normal((n, d))
+    kp, kn = rht.encode_kv(kst, k)
+    vp, vn = rht.encode_kv(vst, v)
+    S = rng.standard_normal((SKETCH_ROWS, d)).astype(np.float32)
+    q = rng.standard_normal((3, d))
+    return kst, vst, k, kp, kn, vp, vn, S, q
+
+
+def check_sketch_attention_converges_rht(seed=92):
+    """Walsh-Hadamard keys with their residual sketch: with 400k sign rows the
+    corrected attention is attention over the unquantized keys, within the
+    sampling bound; without the correction it is not."""
+    kst, vst, k, kp, kn, vp, vn, S, q = _small_rht_caches(seed)
+    d, n = k.shape[1], k.shape[0]
+    sk, rn = qjl.sketch_encode(kst, k, kp, kn, S)
+    got = qjl.attend_compressed(kst, vst, kp, kn, sk, rn, S, vp, vn, n, q)
+    khat = rht.reconstruct_exact(kst, kp, kn, n)
+    vhat = rht.reconstruct_exact(vst, vp, vn, n)
+    scale = 1.0 / math.sqrt(d)
+    want = _attention_loops(q, k, vhat, scale)
+    bound = _convergence_bound(q, k - khat, vhat, SKETCH_ROWS, scale)
+    assert np.all(np.abs(got - want) <= bound[None, :] + 1e-6), (np.abs(got - want).max(), bound.max())
+    plain = _attention_loops(q, khat, vhat, scale)
+    assert np.abs(plain - want).max() > 1.5 * bound.max()
+
+
+def test_sketch_attention_converges_rht():
+    check_sketch_attention_converges_rht()
+
+
+def _small_eigen_caches(seed, avg, d=16, n=10):
+    rng = np.random.default_rng(seed)
+    lam = np.arange(1, d + 1, dtype=np.float64) ** -1.2
+    Q, R = np.linalg.qr(rng.standard_normal((d, d)))
+    Q = Q * np.sign(np.diag(R))[None, :]
+    calib = (rng.standard_normal((512, d)) * np.sqrt(lam)) @ Q.T
+    kst = codec.calibrate_head(calib, 512, avg)
+    vst = codec.calibrate_head((rng.standard_normal((512, d)) * np.sqrt(lam)) @ Q.T, 512, avg)
+    k = (rng.standard_normal((n, d)) * np.sqrt(lam)) @ Q.T
+    v = rng.standard_normal((n, d)) * 0.5
+    S = rng.standard_normal((SKETCH_ROWS, d)).astype(np.float32)
+    q = rng.standard_normal((3, d)) * 3.0
+    return kst, vst, k, v, S, q
+
+
+def check_sketch_attention_converges_eigen(avg, seed=93):
+    """Eigen keys with the selective sketch: the corrected attention converges
+    to attention over the keys with only their dropped channels missing,
+    x - sum_{j dropped} c_j u_j (all keys exactly when no channel is dropped)."""
+    kst, vst, k, v, S, q = _small_eigen_caches(seed, avg)
+    d, n = k.shape[1], k.shape[0]
+    kp, vp = codec.encode_kv(kst, k), codec.encode_kv(vst, v)
+    sk, rn = qjl.sketch_encode_eigen(kst, k, S)
+    got = qjl.attend_compressed_eigen(kst, vst, kp, sk, rn, S, vp, n, q)
+    U = kst["U"]
+    dropped = np.asarray(kst["bits"]) == 0
+    k_target = k - (k @ U[:, dropped]) @ U[:, dropped].T
+    khat = codec.reconstruct_exact(kst, kp, n)
+    vhat = codec.reconstruct_exact(vst, vp, n)
+    scale = 1.0 / math.sqrt(d)
+    want = _attention_loops(q, k_target, vhat, scale)
+    # the sketch sees the latent residual, whose norm is that of k_target - K_hat
+    bound = _convergence_bound(q, k_target - khat, vhat, SKETCH_ROWS, scale)
+    assert np.all(np.abs(got - want) <= bound[None, :] + 1e-6), (np.abs(got - want).max(), bound.max())
+    plain = _attention_loops(q, khat, vhat, scale)
+    assert np.abs(plain - want).max() > 1.5 * bound.max()
+    return dropped.any()
+
+
+def test_sketch_attention_converges_eigen_all_kept():
+    assert not check_sketch_attention_converges_eigen(3.0)
+
+
+def test_sketch_attention_converges_eigen_with_dropped_channels():
+    assert check_sketch_attention_converges_eigen(0.75)
