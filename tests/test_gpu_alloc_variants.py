@@ -8,6 +8,7 @@ import torch
 
 import synth
 from oracle import codec
+from parity_bounds import check_eigen_codes
 
 pytestmark = pytest.mark.gpu
 
@@ -34,9 +35,7 @@ def test_variant_widths_end_to_end(variant, param, avg):
     xd = torch.from_numpy(x.astype(np.float32)).to(DEV, torch.bfloat16)
     packed, _ = stc.encode_kv(gst, xd)
     qg = codec.unpack(packed.cpu().numpy(), st["bits"], n)
-    qo = codec.quantize(st, codec.project(st, x))
-    kept = int((st["bits"] > 0).sum())
-    assert (qg != qo).sum() <= 1e-4 * n * kept and np.abs(qg - qo).max() <= 1
+    check_eigen_codes(qg, st, x)
     xg = stc.decode_kv(gst, packed, n).float().cpu().numpy()
     xo = codec.decode_kv(st, codec.encode_kv(st, x), n, "bf16")
     r_g, r_o = codec.rel_mse(x, xg), codec.rel_mse(x, xo)

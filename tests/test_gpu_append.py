@@ -11,6 +11,7 @@ import torch
 
 import synth
 from oracle import codec, rht
+from parity_bounds import check_eigen_codes
 
 pytestmark = pytest.mark.gpu
 
@@ -52,8 +53,7 @@ def test_append_prefix_invariant(cfg, avg, dtype):
         nb = codec.packed_bytes(st["total_bits"], n)
         assert torch.equal(buf[i, :nb], full[i, :nb]), i
         qg = codec.unpack(buf[i, :nb].cpu().numpy(), st["bits"], n)
-        qo = codec.quantize(st, codec.project(st, xs[i]))
-        assert (qg != qo).mean() <= 1e-4 and np.abs(qg - qo).max() <= 1
+        check_eigen_codes(qg, st, xs[i])
 
 
 def test_append_one_token_at_a_time_matches_oracle_append():
