@@ -176,9 +176,9 @@ stc_status stc_state_init(int32_t d, int32_t xform, const double* u, const doubl
                           const uint8_t* bits, const double* steps, stc_head_info* info,
                           void* state_dev, stc_stream_t stream);
 
-/* stc_state_init plus a selective residual sketch of the keys (SpectralQuant:
- * "a selective QJL sketch on the top effective dimensions", ablation summary,
- * "Experimentele Opstelling"): sketch[i*d + j] = S_ij (host fp32, finite,
+/* stc_state_init plus a selective residual sketch of the keys (SpectralQuant
+ * applies its QJL sketch only on the leading effective dimensions; ablation
+ * summary, "Experimentele Opstelling"): sketch[i*d + j] = S_ij (host fp32, finite,
  * STC_SKETCH_BITS x d). The sketch covers r = c - c_hat on the kept channels
  * with a positive step (latent basis; 0 elsewhere): stc_sketch_kv_batched
  * writes sign(S r) and |r| per token, stc_attend_compressed_sketch_batched
@@ -206,7 +206,11 @@ stc_status stc_rht_sketch_state_init(int32_t d, const int8_t* signs, const float
                                      const float* sketch, stc_head_info* info, void* state_dev,
                                      stc_stream_t stream);
 
-/* Calibrate one stream: second moment of the first n_calib tokens of x_dev
+/* Calibrate one stream (SPECTRA summary, "Metodologia" observations 1-3 and
+ * "La Pipeline di SPECTRA" steps 1-2: the basis diagonalises the second
+ * moment of representative tokens, bits follow the eigenvalues by reverse
+ * water-filling; ablation summary, "Experimentele Opstelling": one such
+ * eigenbasis per head): second moment of the first n_calib tokens of x_dev
  * ([n][ld] of dtype, row t at x_dev + t*ld elements) computed on the GPU in
  * fp64, eigendecomposition on the host (EIGEN) or its diagonal (IDENTITY),
  * water-filling of floor(avg_bits*d+0.5) bits unless `bits` (host, d widths)
@@ -231,8 +235,19 @@ stc_status stc_state_basis(const void* state_dev, float* u_out, stc_stream_t str
  * stc_calibrate_head or stc_state_init gave for its state; one that disagrees with
  * its state is undefined behaviour.
  * x rows must be 16-byte aligned (ld*elem and x_stream_stride*elem multiples
- * of 16); packed_stream_stride a multiple of 16.                         */
+ * of 16); packed_stream_stride a multiple of 16.
+ * A map entry outside [0, n_states) is read on the device only, so the call
+ * still returns STC_OK: its stream is never coded with another state (encode,
+ * append and sketch leave its bytes untouched, decode writes NaN rows, the
+ * attention calls write NaN outputs); stc_check_state_map reports such
+ * entries on the host.                                                   */
 
+/* Encode: project every token onto its stream's basis, quantize each kept
+ * channel on its own and pack the codes as F1 records (SPECTRA summary, "La
+ * Pipeline di SPECTRA" step 3: tokens are projected into the latent space and
+ * quantized per token). Walsh-Hadamard states also write each token's fp32
+ * norm to norms_dev + s*n_tokens (ablation summary, "Experimentele
+ * Opstelling": the rotated unit vector meets a data-independent codebook). */
 stc_status stc_encode_kv_batched(const void* states_dev, int64_t n_states,
                                  const int32_t* state_of_stream_dev, const stc_head_info* infos,
                                  int64_t n_streams, int64_t n_tokens, const void* x_dev,
@@ -240,6 +255,11 @@ stc_status stc_encode_kv_batched(const void* states_dev, int64_t n_states,
                                  void* packed_dev, int64_t packed_stream_stride,
                                  float* norms_dev, stc_stream_t stream);
 
+/* Decode: unpack, dequantize (level (q - (L-1)/2) step) and rotate back,
+ * x_hat = U c_hat, rounded to dtype into x_out_dev + s*x_stream_stride, row t
+ * at + t*ld (SPECTRA summary, "La Pipeline di SPECTRA" step 3: keys and
+ * values are rebuilt on the fly). Walsh-Hadamard states read the norms at
+ * norms_dev + s*n_tokens. */
 stc_status stc_decode_kv_batched(const void* states_dev, int64_t n_states,
                                  const int32_t* state_of_stream_dev, const stc_head_info* infos,
                                  int64_t n_streams, int64_t n_tokens, const void* packed_dev,
@@ -296,7 +316,9 @@ stc_status stc_sketch_kv_batched(const void* states_dev, int64_t n_states,
                                 int64_t sketch_stream_stride, float* rnorm_dev,
                                 int64_t rnorm_stream_stride, stc_stream_t stream);
 
-/* One stream. */
+/* The same for one stream (encode: SPECTRA summary, "La Pipeline di
+ * SPECTRA" step 3, projection and per-token quantization; decode: the same
+ * step, reconstruction on the fly). */
 stc_status stc_encode_kv(const stc_head_info* info, const void* state_dev, int64_t n_tokens,
                          const void* x_dev, int32_t dtype, int64_t ld, void* packed_dev,
                          float* norms_dev, stc_stream_t stream);
@@ -311,6 +333,10 @@ stc_status stc_quantize_pack_f32(const stc_head_info* info, const void* state_de
                                  const float* coeffs_dev, void* packed_dev, stc_stream_t stream);
 
 /* ------------------------------------------------------ attention
+ * (SPECTRA summary, "La Pipeline di SPECTRA" step 3 and "Significato e
+ * Rivendicazioni": standard attention over the rebuilt keys and values, the
+ * latent form of it being the same arithmetic; SPECTRA abstract: the cache
+ * is read in full at every generated token.)
  * One decode step for n_pairs KV heads (pair p: K stream with state
  * k_state_of_pair[p] and bytes k_packed_dev + p*packed_pair_stride, V stream
  * likewise), each shared by `group` query heads (1..16):
@@ -347,7 +373,7 @@ stc_status stc_attend_compressed_sketch_batched(const void* states_dev, int64_t 
                                                 float scale, void* ws_dev, size_t ws_bytes,
                                                 stc_stream_t stream);
 
-/* One KV head. */
+/* One KV head (the same step as stc_attend_compressed_batched, same pages). */
 stc_status stc_attend_compressed(const stc_head_info* k_info, const void* k_state_dev,
                                  const stc_head_info* v_info, const void* v_state_dev,
                                  int64_t n_tokens, const void* k_packed_dev,
@@ -400,6 +426,12 @@ stc_status stc_decode_step_batched(const void* states_dev, int64_t n_states,
                                    void* v_packed_dev, int64_t packed_pair_stride, int32_t group,
                                    const float* q_dev, float* out_dev, float scale, void* ws_dev,
                                    size_t ws_bytes, stc_stream_t stream);
+
+/* Check a state map on the host: copies n entries of map_dev to the host
+ * (synchronizes `stream`) and returns STC_EINVAL, naming the first entry
+ * outside [0, n_states) in stc_last_error, if there is one. For callers that
+ * want the device-side behaviour above reported before they rely on it. */
+stc_status stc_check_state_map(const int32_t* map_dev, int64_t n, int64_t n_states, stc_stream_t stream);
 
 /* ------------------------------------------------------ diagnostics */
 const char* stc_status_str(stc_status s);

@@ -259,6 +259,13 @@ def _map_arg(m):
     return m
 
 
+def check_state_map(state_of_stream: torch.Tensor, n_states: int) -> None:
+    """Raise StcError if an entry of the int32 device map lies outside
+    [0, n_states) (synchronizes the current stream)."""
+    m = _map_arg(state_of_stream)
+    check("stc_check_state_map", lib().stc_check_state_map(_ptr(m), m.numel(), int(n_states), _stream()))
+
+
 def encode_kv_batched(states: StateArray, x: torch.Tensor, state_of_stream: Optional[torch.Tensor] = None,
                       packed: Optional[torch.Tensor] = None, norms: Optional[torch.Tensor] = None):
     """x: [S][n][128] (row and stream strides from the tensor) -> packed [S][stride] uint8

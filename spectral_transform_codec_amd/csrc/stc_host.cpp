@@ -507,6 +507,8 @@ stc_status stc_allocate_bits(int32_t d, const double* lambda, int32_t total_bits
 
 stc_status stc_eigh(int32_t d, const double* a, double* u_out, double* lambda_out) {
   if (d <= 0 || !a || !u_out || !lambda_out) return fail(STC_EINVAL, "eigh: bad arguments");
+  for (size_t k = 0; k < (size_t)d * d; ++k)
+    if (!std::isfinite(a[k])) return fail(STC_EINVAL, "eigh: entry %zu is not finite", k);
   std::vector<double> m(a, a + (size_t)d * d), v;
   // symmetrize exactly (the input is symmetric up to rounding at most)
   for (int i = 0; i < d; ++i)
@@ -762,9 +764,12 @@ stc_status stc_calibrate_head(int32_t d, int64_t n_calib, const void* x_dev, int
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (stc_status st = hip_check(hipMemcpyAsync(g.data(), gram_dev, g.size() * sizeof(double), hipMemcpyDeviceToHost, s), "gram download")) return st;
   if (stc_status st = hip_check(hipStreamSynchronize(s), "gram sync")) return st;
+  for (double v : g)
+    if (!std::isfinite(v))
+      return fail(STC_EINVAL, "calibrate_head: the second moment is not finite (NaN or Inf among the tokens)");
   std::vector<double> u((size_t)d * d), lam(d);
   if (xform == STC_XFORM_EIGEN) {
-    stc_eigh(d, g.data(), u.data(), lam.data());
+    if (stc_status st = stc_eigh(d, g.data(), u.data(), lam.data())) return st;
   } else {
     for (int j = 0; j < d; ++j) lam[j] = g[(size_t)j * d + j];
   }
@@ -786,6 +791,22 @@ stc_status stc_state_basis(const void* state_dev, float* u_out, stc_stream_t str
   if (stc_status st = hip_check(hipMemcpyAsync(u_out, static_cast<const unsigned char*>(state_dev) + OFF_U32,
                                                (size_t)D * D * sizeof(float), hipMemcpyDeviceToHost, s), "basis download")) return st;
   if (stc_status st = hip_check(hipStreamSynchronize(s), "basis sync")) return st;
+  return ok();
+}
+
+stc_status stc_check_state_map(const int32_t* map_dev, int64_t n, int64_t n_states, stc_stream_t stream) {
+  if (n < 0 || n_states < 0) return fail(STC_EINVAL, "check_state_map: negative size");
+  if (n == 0) return ok();
+  if (!map_dev) return fail(STC_EINVAL, "check_state_map: NULL map");
+  std::vector<int32_t> m((size_t)n);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (stc_status st = hip_check(hipMemcpyAsync(m.data(), map_dev, (size_t)n * sizeof(int32_t), hipMemcpyDeviceToHost, s),
+                                "map download")) return st;
+  if (stc_status st = hip_check(hipStreamSynchronize(s), "map sync")) return st;
+  for (int64_t i = 0; i < n; ++i)
+    if (m[(size_t)i] < 0 || m[(size_t)i] >= n_states)
+      return fail(STC_EINVAL, "check_state_map: entry %lld is %d, outside [0, %lld)", (long long)i, m[(size_t)i],
+                  (long long)n_states);
   return ok();
 }
 

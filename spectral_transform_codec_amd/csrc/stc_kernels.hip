@@ -58,9 +58,13 @@ __device__ __forceinline__ long long packed_len(long long total_bits, long long 
   return (nb + 15) / 16 * 16;
 }
 
+// State of stream s: map[s] (or s without a map); -1 when the entry lies
+// outside [0, n_states). Such a stream is never read from its state: encode
+// and append leave its records untouched, decode writes NaN rows, attention
+// writes NaN outputs (stc_check_state_map reports the entry on the host).
 __device__ __forceinline__ long long state_index(const int32_t* map, long long s, long long n_states) {
-  long long si = map ? (long long)map[s] : s;
-  return si < 0 ? 0 : (si >= n_states ? n_states - 1 : si);
+  const long long si = map ? (long long)map[s] : s;
+  return (si < 0 || si >= n_states) ? -1 : si;
 }
 
 // Workgroup -> work mapping that keeps consecutive logical workgroups on one
@@ -274,7 +278,12 @@ __global__ void __launch_bounds__(ENC_THREADS, 1) k_encode_eigen(EncK a) {
     const long long s = seg / a.blocks_per_stream;
     long long seg_end = (s + 1) * a.blocks_per_stream;
     if (seg_end > b_end) seg_end = b_end;
-    const unsigned char* st = a.states + (size_t)state_index(a.map, s, a.n_states) * STATE_BYTES;
+    const long long si = state_index(a.map, s, a.n_states);
+    if (si < 0) {  // (uniform over the workgroup) no state: records untouched
+      seg = seg_end;
+      continue;
+    }
+    const unsigned char* st = a.states + (size_t)si * STATE_BYTES;
     const DevHdr* hdr = reinterpret_cast<const DevHdr*>(st + OFF_HDR);
     const unsigned B = (unsigned)__builtin_amdgcn_readfirstlane(hdr->total_bits);
     __syncthreads();  // every wave is done with the previous basis
@@ -539,7 +548,9 @@ __global__ void __launch_bounds__(64 * SKE_WAVES, 2) k_sketch_eigen(EncK a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int t32 = lane & 31, h = lane >> 5;
   const long long m = a.n_tokens;  // x rows of the call; row j is token n_old + j of the stream
-  const unsigned char* st = a.states + (size_t)state_index(a.map, s, a.n_states) * STATE_BYTES;
+  const long long si = state_index(a.map, s, a.n_states);
+  if (si < 0) return;  // no state: sketch bits and norms untouched
+  const unsigned char* st = a.states + (size_t)si * STATE_BYTES;
   const DevHdr* hdr = reinterpret_cast<const DevHdr*>(st + OFF_HDR);
   if (hdr->sketch_bits == 0) return;  // the whole workgroup: no sketch matrix for this stream
   float* sTb = reinterpret_cast<float*>(smem + 4 * 128 * UROW);  // L/2, L - 1, step (per channel)
@@ -898,7 +909,21 @@ __global__ void __launch_bounds__(DEC_THREADS, 1) k_decode_eigen(DecK a) {
     const long long s = seg / a.blocks_per_stream;
     long long seg_end = (s + 1) * a.blocks_per_stream;
     if (seg_end > b_end) seg_end = b_end;
-    const unsigned char* st = a.states + (size_t)state_index(a.map, s, a.n_states) * STATE_BYTES;
+    const long long si = state_index(a.map, s, a.n_states);
+    if (si < 0) {  // (uniform over the workgroup) no state: NaN rows
+      for (long long blk = seg + wave; blk < seg_end; blk += DEC_WAVES) {
+        const long long tok0 = (blk - s * a.blocks_per_stream) * DEC_BT;
+        for (int i = lane; i < DEC_BT * 128; i += 64) {
+          const long long tok = tok0 + (i >> 7);
+          if (tok >= n) break;
+          if (F32OUT) static_cast<float*>(a.x)[s * a.x_stride + tok * a.ld + (i & 127)] = __builtin_nanf("");
+          else static_cast<unsigned short*>(a.x)[s * a.x_stride + tok * a.ld + (i & 127)] = 0x7FC0u;
+        }
+      }
+      seg = seg_end;
+      continue;
+    }
+    const unsigned char* st = a.states + (size_t)si * STATE_BYTES;
     const DevHdr* hdr = reinterpret_cast<const DevHdr*>(st + OFF_HDR);
     const unsigned B = (unsigned)__builtin_amdgcn_readfirstlane(hdr->total_bits);
     __syncthreads();  // every wave is done with the previous state
@@ -1143,7 +1168,9 @@ __global__ void __launch_bounds__(SKETCH ? 64 * RHTS_WAVES : 64 * RHT_WAVES, SKE
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int t32 = lane & 31, h = lane >> 5;
   const long long n = a.n_tokens;  // x rows of the call; row j is token n_old + j of the stream
-  const unsigned char* st = a.states + (size_t)state_index(a.map, s, a.n_states) * STATE_BYTES;
+  const long long si = state_index(a.map, s, a.n_states);
+  if (si < 0) return;  // no state: records, norms and sketch untouched
+  const unsigned char* st = a.states + (size_t)si * STATE_BYTES;
   const DevHdr* hdr = reinterpret_cast<const DevHdr*>(st + OFF_HDR);
   {
     const u32x4* g = reinterpret_cast<const u32x4*>(st + OFF_UT_HI);
@@ -1297,8 +1324,17 @@ __global__ void __launch_bounds__(RHTD_T) k_rht_decode(RhtK a) {
   __shared__ float scb[8];
   const long long s = blockIdx.y;
   const int t = threadIdx.x;
-  const DevHdr* hdr =
-      reinterpret_cast<const DevHdr*>(a.states + (size_t)state_index(a.map, s, a.n_states) * STATE_BYTES);
+  const long long si = state_index(a.map, s, a.n_states);
+  if (si < 0) {  // no state: NaN rows
+    const long long tok = (long long)blockIdx.x * RHTD_T + t;
+    if (tok < a.n_tokens)
+      for (int i = 0; i < 128; ++i) {
+        if (a.f32out) static_cast<float*>(a.xo)[s * a.x_stride + tok * a.ld + i] = __builtin_nanf("");
+        else static_cast<unsigned short*>(a.xo)[s * a.x_stride + tok * a.ld + i] = 0x7FC0u;
+      }
+    return;
+  }
+  const DevHdr* hdr = reinterpret_cast<const DevHdr*>(a.states + (size_t)si * STATE_BYTES);
   if (t < 8) scb[t] = hdr->cb[t];
   __syncthreads();
   const long long tok0 = (long long)blockIdx.x * RHTD_T;
@@ -1449,7 +1485,6 @@ struct AttK {
   const float* q;
   float* out;
   float scale;
-  float v_code_offset;  // added to every V code in P.V (removed at the split merge)
   unsigned char* ws;
   long long split_tokens, n_splits;
   int stream_words, region_words;
@@ -1491,14 +1526,18 @@ __host__ __device__ constexpr int att_region_words(int max_bits) {
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
-// 4 unsigned byte codes c -> 4 fp16 1024 + c (exact: 0x64xx in fp16), two
-// byte permutes. P.V then sums p (1024 + c); the split merge divides by the
-// sum of the same fp16 p and removes the 1024.
-constexpr float ATT_V_CODE_OFFSET = 1024.0f;
-__device__ __forceinline__ f16x4 bytes_to_f16x4_biased(unsigned v) {
+// 4 unsigned byte codes c -> 4 fp16 c: two byte permutes give 1024 + c
+// (0x64xx in fp16, exact), two packed fp16 subtractions remove the 1024
+// (exact: the results are integers below 2^8). P.V then accumulates p c, whose
+// fp32 rounding scales with the codes, not with an offset (a near-uniform
+// softmax over many tokens averages the codes to within a small fraction of
+// one level, which an offset of 1024 in the sums would swamp).
+__device__ __forceinline__ f16x4 bytes_to_f16x4(unsigned v) {
   const unsigned lo = __builtin_amdgcn_perm(v, 0x64646464u, 0x00050004u);
   const unsigned hi = __builtin_amdgcn_perm(v, 0x64646464u, 0x00070006u);
-  return __builtin_bit_cast(f16x4, (u32x2){lo, hi});
+  const f16x2 off = {(_Float16)1024.0f, (_Float16)1024.0f};
+  const f16x2 a = __builtin_bit_cast(f16x2, lo) - off, b = __builtin_bit_cast(f16x2, hi) - off;
+  return __builtin_bit_cast(f16x4, (u32x2){__builtin_bit_cast(unsigned, a), __builtin_bit_cast(unsigned, b)});
 }
 
 // Four codes (bytes of c, each 0..7) -> four 16-bit table entries, from the
@@ -1636,7 +1675,12 @@ __global__ void __launch_bounds__(CMB_THREADS) k_att_combine(AttK a) {
   const int g = a.group;
   const int S = (int)a.n_splits;
   const long long PS = att_part_stride(g);
-  const unsigned char* vst = a.v_states + (size_t)state_index(a.v_map, pg, a.n_states) * STATE_BYTES;
+  const long long ksi = state_index(a.k_map, pg, a.n_states), vsi = state_index(a.v_map, pg, a.n_states);
+  if (ksi < 0 || vsi < 0) {  // no state for the pair (k_att_main wrote no partial): NaN
+    if (t < 128) a.out[(pg * g + hh) * 128 + t] = __builtin_nanf("");
+    return;
+  }
+  const unsigned char* vst = a.v_states + (size_t)vsi * STATE_BYTES;
   const DevHdr* hv = reinterpret_cast<const DevHdr*>(vst);
   const f32x4* urow = reinterpret_cast<const f32x4*>(vst + OFF_U32) + i * 32 + qt * 8;  // U[i][32qt .. +31]
   f32x4 u[8];
@@ -1676,8 +1720,8 @@ __global__ void __launch_bounds__(CMB_THREADS) k_att_combine(AttK a) {
         M = Mc;
       }
     }
-    // dequantize the mean code: step * (A / L - offset - (L_j - 1)/2)
-    sC[j] = bits ? (float)((double)step * (A / L - (double)a.v_code_offset - (double)hs)) : 0.0f;
+    // dequantize the mean code: step * (A / L - (L_j - 1)/2)
+    sC[j] = bits ? (float)((double)step * (A / L - (double)hs)) : 0.0f;
   }
   __syncthreads();
   float o = 0.0f;
@@ -1711,8 +1755,10 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_att_main(AttK a) {
   const long long n = a.n_tokens;
   const int g = a.group;
   const bool two_rows = g > 8;  // query heads 8..15 in use
-  const unsigned char* kst = a.k_states + (size_t)state_index(a.k_map, pg, a.n_states) * STATE_BYTES;
-  const unsigned char* vst = a.v_states + (size_t)state_index(a.v_map, pg, a.n_states) * STATE_BYTES;
+  const long long ksi = state_index(a.k_map, pg, a.n_states), vsi = state_index(a.v_map, pg, a.n_states);
+  if (ksi < 0 || vsi < 0) return;  // (the whole workgroup) the merge writes NaN for this pair
+  const unsigned char* kst = a.k_states + (size_t)ksi * STATE_BYTES;
+  const unsigned char* vst = a.v_states + (size_t)vsi * STATE_BYTES;
   const DevHdr* hk = reinterpret_cast<const DevHdr*>(kst);
   const DevHdr* hv = reinterpret_cast<const DevHdr*>(vst);
   const unsigned Bk = (unsigned)__builtin_amdgcn_readfirstlane(hk->total_bits);
@@ -2049,7 +2095,7 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_att_main(AttK a) {
           const unsigned vb = sVT[vt_index(16 * nb + c16, 4 * kt + g4)];
           f16x4 vf;
           if (RHT) vf = __builtin_bit_cast(f16x4, lut16x4(vb, cbv[0], cbv[1], cbv[2], cbv[3]));
-          else vf = bytes_to_f16x4_biased(vb);
+          else vf = bytes_to_f16x4(vb);
           acc_o[nb] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, vf, acc_o[nb], 0, 0, 0);
         }
       }
@@ -2148,7 +2194,6 @@ int launch_attend(const AttendLaunch& L, void* stream) {
   a.q = L.q;
   a.out = L.out;
   a.scale = L.scale;
-  a.v_code_offset = L.rht ? 0.0f : ATT_V_CODE_OFFSET;  // (Walsh-Hadamard V codes go through the codebook)
   a.ws = L.ws;
   a.k_norms = L.k_norms;
   a.v_norms = L.v_norms;

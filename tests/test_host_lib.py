@@ -183,3 +183,11 @@ def test_allocation_variants_match_oracle():
                 got = stc.allocate_bits(lam, B, variant, param)
                 assert np.array_equal(got, want), (variant, param, B)
 
+
+
+def test_check_state_map_validates_arguments_without_device_work():
+    L = _abi.lib()
+    assert L.stc_check_state_map(None, 0, 4, None) == _abi.STC_OK
+    assert L.stc_check_state_map(None, 3, 4, None) == _abi.STC_EINVAL
+    assert b"NULL map" in L.stc_last_error()
+    assert L.stc_check_state_map(None, -1, 4, None) == _abi.STC_EINVAL
