@@ -1,0 +1,20 @@
+// Host-only stand-ins for the kernel launchers of libstc, so that the host
+// code (validation, eigensolver, water-filling, Lloyd, state building) can be
+// built with the address and undefined-behaviour sanitizers and exercised
+// without a GPU. Every launcher reports failure; the sanitized driver only
+// runs paths that return before any launch.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "../../spectral_transform_codec_amd/csrc/stc_internal.h"
+
+namespace stc {
+int launch_gram(const void*, int, int64_t, int64_t, double*, void*) { return 1; }
+int launch_encode_eigen(const EncodeLaunch&, void*) { return 1; }
+int launch_sketch_eigen(const EncodeLaunch&, void*) { return 1; }
+int launch_decode_eigen(const DecodeLaunch&, void*) { return 1; }
+int launch_encode_rht(const EncodeLaunch&, void*) { return 1; }
+int launch_decode_rht(const DecodeLaunch&, void*) { return 1; }
+int launch_attend(const AttendLaunch&, void*) { return 1; }
+}  // namespace stc
