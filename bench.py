@@ -1,20 +1,28 @@
 #!/usr/bin/env python3
 """Benchmark of the spectral transform KV-cache codec on one MI355X.
 
-Workload (one "step" = one pass of the whole hot path over one batch):
-  Llama-3.1-8B-shaped layer: 8 KV heads x {K, V} = 16 streams of 32768 bf16
-  tokens (head dim 128), spiked-Gaussian synthetic data (lambda_i = i^-1.2,
-  2 outlier channels at 20x), calibrated on the first 2048 tokens.
-  For each average budget 4.0 / 2.0 / 1.33 bits: batched encode of the 16
-  streams, batched decode, and one decode-step attention (32 query heads,
-  GQA 4) over the packed cache. Plus the Walsh-Hadamard comparison path
-  (3-bit Lloyd-Max codebook) encode + decode on 16 Student-t(3) streams of
-  the same shape. Calibration runs once, before timing.
+Default workload (one "step" = one pass of the whole hot path over one batch):
+the two full-size caches, resident in HBM:
+  * Qwen2.5-7B-shaped batched decode: 28 layers x batch 16 x 4 KV heads x
+    {K, V} = 3584 streams of 32768 bf16 tokens (head dim 128), spiked-Gaussian
+    synthetic data (lambda_i = i^-1.0, 3 outlier channels at 30x), 224 states
+    calibrated on the first 2048 tokens of batch entry 0 and shared over the
+    batch, 1.33 bits (170-bit records);
+  * Llama-3.1-8B-shaped cache: 32 layers x 8 KV heads x {K, V} = 512 streams
+    of 131072 bf16 tokens (lambda_i = i^-alpha, alpha per layer in
+    [0.8, 1.5], 2 outlier channels at 20x), 2.0 bits (256-bit records).
+  For each: one batched encode of every stream (prefill), one batched decode
+  of every stream, and one decode-step attention over every KV head (GQA 7 /
+  GQA 4) reading only the packed cache. Calibration runs once, before timing.
+  Streams are generated on the device from the seeded recipe.
 
-Prints ONE JSON line. `value` is the algorithmic bytes of all steps divided
-by their wall time on the GPU stream (GB/s); per-op figures are in
-`breakdown`; `roofline` is for the op with the largest time share;
-`cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
+Prints ONE JSON line. `value` is the algorithmic bytes of the K timed steps
+divided by their wall time on the launch stream (GB/s); per-op figures are in
+`breakdown`; `roofline` is for the kernel launch with the largest time share;
+`cpu_baseline` times the CPU oracle on a labelled sample of the same two
+workloads. `layer` holds the figures of the smaller Llama-layer step (16
+streams x 32768 tokens, budgets 4.0 / 2.0 / 1.33, Walsh-Hadamard path, warm
+and with cold caches), which are not part of `value`.
 """
 import argparse
 import json
@@ -52,10 +60,10 @@ def parse():
     ap.add_argument("--no-extras", action="store_true",
                     help="time only the step (no generation step, Walsh-Hadamard attention, sketch or cold "
                          "passes); for counter runs whose per-launch averages must cover the step's launches only")
-    ap.add_argument("--workload", default="llama_layer", choices=["llama_layer", "llama_cache", "qwen_batch"],
-                    help="llama_layer: the step above (the bench line); llama_cache: 32 layers x 8 KV heads x "
-                         "131072 tokens at 2.0 bits; qwen_batch: 28 layers x 4 KV heads x batch 16 x 32768 tokens "
-                         "at 1.33 bits (both print their own line: prefill encode, decode and the attention step)")
+    ap.add_argument("--workload", default="full", choices=["full", "llama_layer", "llama_cache", "qwen_batch"],
+                    help="full: the step above (the bench line); llama_layer: the Llama-layer step alone (its own "
+                         "line); llama_cache / qwen_batch: one of the two caches alone, timed the same way (for "
+                         "counter runs whose per-launch figures must cover one workload)")
     ap.add_argument("--kernel", default=None, help="kernel name prefix for --summarize")
     ap.add_argument("--command", default="", help="command line recorded in a summary")
     return ap.parse_args()
@@ -90,10 +98,11 @@ def source_digest():
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def stored_traffic(kernel):
-    """HBM bytes per launch of `kernel` from a committed counter summary, or
-    None if there is none or the kernel source changed since it was taken."""
-    path = os.path.join(PROFILES, "traffic_" + kernel.replace("<", "_").replace(">", "") + "_llama_layer.txt")
+def stored_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` on `workload` from a committed counter
+    summary, or None if there is none or the kernel source changed since it
+    was taken."""
+    path = os.path.join(PROFILES, "traffic_" + kernel.replace("<", "_").replace(">", "") + f"_{workload}.txt")
     if not os.path.exists(path):
         return None
     vals = {}
@@ -124,20 +133,39 @@ def main():
               "run it with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
-
-    import synth
-    import spectral_transform_codec_amd as stc
 
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(2)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    if args.workload != "llama_layer":
-        large_workload(args, dev)
+    if args.copy_mib:
+        # the reference kernel for scaling the FETCH_SIZE / WRITE_SIZE counters
+        src = torch.ones(args.copy_mib << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    if args.workload == "llama_layer":
+        line = layer_step(args, dev)
+        if not args.no_cpu_baseline:
+            line["cpu_baseline"] = cpu_baseline(args.cpu_seconds, layer=True)
+        print(json.dumps(line), flush=True)
         return
+    full_step(args, dev)
+
+
+def layer_step(args, dev):
+    """The Llama-layer step (16 streams x 32768 tokens, budgets 4.0 / 2.0 /
+    1.33 bits, plus the Walsh-Hadamard path on 16 Student-t streams): its own
+    timing, per-op breakdown, cold-cache pass and extras. Returns a dict."""
+    import numpy as np
+    import torch
+
+    import synth
+    import spectral_transform_codec_amd as stc
 
     w = synth.WORKLOADS[WORKLOAD]
     w3 = synth.WORKLOADS[RHT_WORKLOAD]
@@ -199,13 +227,6 @@ def main():
                 S * n * (256 + 48 + 4)))
 
     stream = torch.cuda.current_stream()
-    if args.copy_mib:
-        src = torch.ones(args.copy_mib << 20, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
     for _ in range(args.warmup):
         for _, fn, _ in ops:
             fn()
@@ -398,11 +419,11 @@ def main():
     dname = max(fam, key=lambda k: fam[k][0])
     d_ms, d_bytes, d_n = fam[dname]
     achieved = d_bytes / (d_ms * 1e-3) / 1e9
-    traffic = stored_traffic(dname)
+    traffic = stored_traffic(dname, "llama_layer")
     # the same figures for every single-kernel family of the step
     families = {}
     for kname, (f_ms, f_bytes, f_n) in sorted(fam.items(), key=lambda kv: -kv[1][0]):
-        f_tr = stored_traffic(kname)
+        f_tr = stored_traffic(kname, "llama_layer")
         families[kname] = {"launches_per_step": f_n, "avg_launch_us": round(1e3 * f_ms / f_n, 2),
                            "algorithmic_bytes_per_launch": int(f_bytes / f_n),
                            "achieved": round(f_bytes / (f_ms * 1e-3) / 1e9, 1),
@@ -412,11 +433,6 @@ def main():
     codec_bytes = sum(o[2] for o in ops if o[0] in codec_names)
     codec_ms = sum(per_op[nm]["ms"] for nm in codec_names)
     attn_names = [o[0] for o in ops if o[0].startswith("attend")]
-
-    # --------------------------------------------- CPU oracle baseline
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(args.cpu_seconds)
 
     line = {
         "metric": "KV codec encode/decode GB/s (% of HBM peak); compressed decode-attn tokens/s",
@@ -453,30 +469,26 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": None if traffic is None else int(traffic)},
         "roofline_by_kernel": families,
-        "cpu_baseline": cpu,
         "setup_s": round(setup_s, 2),
         "calibrate_s": round(cal_s, 2),
     }
-    print(json.dumps(line), flush=True)
+    return line
 
 
-def large_workload(args, dev):
-    """The full-size caches: every stream generated on the device from the
+def build_cache(w, n, dev):
+    """One full-size cache on the device: every stream generated from the
     workload's recipe (per-stream Haar rotation and outlier channels from the
     seeded numpy generators, lambda_i = i^-alpha per layer, Gaussian samples
-    from a seeded device generator), calibrated on its first 2048 tokens (the
-    Qwen batch: one state per layer, KV head and K/V from batch entry 0,
-    shared across the batch), then timed: one batched encode of every stream
-    (prefill), one batched decode, and the decode-attention step over all
-    layers (and batch entries) reading only the packed cache."""
+    from a seeded device generator: the same distribution as the host
+    generator, not the same numbers), calibrated on its first 2048 tokens (the
+    Qwen batch: one state per layer, KV head and K/V, from batch entry 0,
+    shared over the batch). Returns a dict of device tensors and sizes."""
     import numpy as np
     import torch
 
     import synth
     import spectral_transform_codec_amd as stc
 
-    w = synth.WORKLOADS[4 if args.workload == "llama_cache" else 5]
-    n = args.tokens or w.n_tokens
     L, Bt, H, g = w.layers, w.batch, w.kv_heads, w.group
     budget = w.budgets[0]
     S = L * Bt * H * 2                      # streams ordered (layer, batch, head, K/V)
@@ -498,15 +510,13 @@ def large_workload(args, dev):
                         sc = np.ones(128)
                         sc[idx] = w.outlier_scale
                         # x = (z sqrt(lambda)) Q^T, then the outlier channels scaled
-                        m = (torch.from_numpy(q.T * sc[None, :]).to(dev) * lam.sqrt()[:, None]).float()
-                        rot[key] = m
+                        rot[key] = (torch.from_numpy(q.T * sc[None, :]).to(dev) * lam.sqrt()[:, None]).float()
                     gen.manual_seed(((((w.cfg * 64 + l) * 64 + b) * 64 + h) * 2 + kind) * 8 + synth.P_SAMPLES)
                     z = torch.randn((n, 128), generator=gen, device=dev, dtype=torch.float32)
                     x[((l * Bt + b) * H + h) * 2 + kind] = (z @ rot[key]).to(torch.bfloat16)
                     del z
     torch.cuda.synchronize()
     setup_s = time.time() - t_setup
-    # states: one per stream, or one per (layer, head, K/V) from batch entry 0
     t_cal = time.time()
     states, smap = [], []
     for l in range(L):
@@ -523,51 +533,141 @@ def large_workload(args, dev):
     torch.cuda.synchronize()
     cal_s = time.time() - t_cal
     smap_t = torch.tensor(smap, dtype=torch.int32, device=dev)
-    kmap, vmap = smap_t[0::2].contiguous(), smap_t[1::2].contiguous()
     B = arr.max_bits
-    packed = torch.empty((S, stc.packed_bytes(B, n)), dtype=torch.uint8, device=dev)
-    qs = torch.randn((P, g, 128), generator=gen.manual_seed(w.cfg * 8 + synth.P_QUERY), device=dev)
-    ws = torch.empty(stc.attend_workspace_bytes(P, g, n), dtype=torch.uint8, device=dev)
-    out = torch.empty((P, g, 128), dtype=torch.float32, device=dev)
-    stream = torch.cuda.current_stream()
+    return {"w": w, "n": n, "S": S, "P": P, "g": g, "Bt": Bt, "B": B, "budget": budget, "x": x, "arr": arr,
+            "smap": smap_t, "kmap": smap_t[0::2].contiguous(), "vmap": smap_t[1::2].contiguous(),
+            "packed": torch.empty((S, stc.packed_bytes(B, n)), dtype=torch.uint8, device=dev),
+            "xhat": torch.empty_like(x),
+            "q": torch.randn((P, g, 128), generator=gen.manual_seed(w.cfg * 8 + synth.P_QUERY), device=dev),
+            "ws": torch.empty(stc.attend_workspace_bytes(P, g, n), dtype=torch.uint8, device=dev),
+            "out": torch.empty((P, g, 128), dtype=torch.float32, device=dev),
+            "setup_s": setup_s, "calibrate_s": cal_s}
 
-    def timed(fn, reps):
-        fn()
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(reps):
-            fn()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / reps  # ms
 
+def cache_ops(c, tag):
+    """(name, fn, algorithmic bytes, workload tag) of one cache's step:
+    encode every stream, decode every stream, one attention step."""
+    import spectral_transform_codec_amd as stc
+    n, S, P, B = c["n"], c["S"], c["P"], c["B"]
     codec_bytes = S * n * (256 + B / 8.0)
-    enc_ms = timed(lambda: stc.encode_kv_batched(arr, x, state_of_stream=smap_t, packed=packed), args.steps)
-    xhat = x  # decode overwrites the inputs (they are not needed any more)
-    dec_ms = timed(lambda: stc.decode_kv_batched(arr, packed, n, state_of_stream=smap_t, out=xhat), args.steps)
-    stc.encode_kv_batched(arr, x, state_of_stream=smap_t, packed=packed)  # the cache of the reconstruction
-    kp, vp = packed[0::2], packed[1::2]
-    att_ms = timed(lambda: stc.attend_compressed_batched(arr, kmap, vmap, kp, vp, n, qs, ws=ws, out=out),
-                   args.steps)
-    att_bytes = P * n * 2 * B / 8.0
+    kp, vp = c["packed"][0::2], c["packed"][1::2]
+    return [
+        (f"encode@{tag}", lambda: stc.encode_kv_batched(c["arr"], c["x"], state_of_stream=c["smap"],
+                                                        packed=c["packed"]), codec_bytes, tag),
+        (f"decode@{tag}", lambda: stc.decode_kv_batched(c["arr"], c["packed"], n, state_of_stream=c["smap"],
+                                                        out=c["xhat"]), codec_bytes, tag),
+        (f"attend@{tag}", lambda: stc.attend_compressed_batched(c["arr"], c["kmap"], c["vmap"], kp, vp, n, c["q"],
+                                                                ws=c["ws"], out=c["out"]),
+         P * n * 2 * B / 8.0 + 2 * c["q"].numel() * 4, tag),
+    ]
+
+
+def full_step(args, dev):
+    import torch
+
+    import synth
+
+    tags = ["qwen_batch", "llama_cache"] if args.workload == "full" else [args.workload]
+    caches = {}
+    for tag in tags:
+        w = synth.WORKLOADS[5 if tag == "qwen_batch" else 4]
+        caches[tag] = build_cache(w, args.tokens or w.n_tokens, dev)
+        print(f"bench: {tag} built ({caches[tag]['S']} streams x {caches[tag]['n']} tokens, "
+              f"setup {caches[tag]['setup_s']:.1f} s, calibration {caches[tag]['calibrate_s']:.1f} s)",
+              file=sys.stderr, flush=True)
+    ops = [op for tag in tags for op in cache_ops(caches[tag], tag)]
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        for op in ops:
+            op[1]()
+    torch.cuda.synchronize()
+    # (1) the step as a whole: events only around the K steps
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for _ in range(args.steps):
+        for op in ops:
+            op[1]()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = t0.elapsed_time(t1) / args.steps
+    # (2) per-op durations: events on the launch stream around every op
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in ops]
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for k in range(args.steps):
+        for i, op in enumerate(ops):
+            ev[k][i][0].record(stream)
+            op[1]()
+            ev[k][i][1].record(stream)
+    torch.cuda.synchronize()
+    per_op = {}
+    for i, (name, _, nbytes, tag) in enumerate(ops):
+        ms = [ev[k][i][0].elapsed_time(ev[k][i][1]) for k in range(args.steps)]
+        avg = sum(ms) / len(ms)
+        per_op[name] = {"ms": round(avg, 5), "GBps": round(nbytes / (avg * 1e-3) / 1e9, 1),
+                        "pct_hbm_peak": round(100.0 * nbytes / (avg * 1e-3) / 1e9 / HBM_PEAK_GBPS, 1),
+                        "bytes": int(nbytes)}
+    step_bytes = sum(op[2] for op in ops)
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    # roofline of the kernel launch with the largest time share (one launch
+    # per op and step): algorithmic bytes / average duration (HIP events on
+    # the launch stream); traffic from the committed counter summary of that
+    # kernel on that workload, if it matches the kernel source
+    by_kernel = {}
+    for name, _, nbytes, tag in ops:
+        kname = kernel_of(name)
+        a_ms = per_op[name]["ms"]
+        tr = stored_traffic(kname, tag)
+        by_kernel[f"{kname}@{tag}"] = {"avg_launch_us": round(1e3 * a_ms, 2),
+                                      "algorithmic_bytes_per_launch": int(nbytes),
+                                      "achieved": round(nbytes / (a_ms * 1e-3) / 1e9, 1),
+                                      "frac": round(nbytes / (a_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                                      "traffic": None if tr is None else int(tr)}
+    dom = max(ops, key=lambda op: per_op[op[0]]["ms"])
+    dkey = f"{kernel_of(dom[0])}@{dom[3]}"
+    d = by_kernel[dkey]
+    att = {}
+    for tag in tags:
+        a_ms = per_op[f"attend@{tag}"]["ms"]
+        att[tag] = {"us_per_step": round(1e3 * a_ms, 1), "steps_per_s": round(1e3 / a_ms, 1),
+                    "tokens_per_s": round(caches[tag]["Bt"] * 1e3 / a_ms, 1),
+                    "pct_hbm_peak": per_op[f"attend@{tag}"]["pct_hbm_peak"]}
+    codec_names = [op[0] for op in ops if op[0].startswith(("encode", "decode"))]
+    codec_bytes = sum(op[2] for op in ops if op[0] in codec_names)
+    codec_ms = sum(per_op[nm]["ms"] for nm in codec_names)
+    cfg = {"workload": " + ".join(caches[t]["w"].name + f" ({caches[t]['S']} streams x {caches[t]['n']} bf16 "
+                                                        f"tokens, {caches[t]['budget']} bits)" for t in tags),
+           "step": "per cache: batched encode of every stream, batched decode of every stream, one decode-attention "
+                   "step over every KV head reading only the packed cache",
+           "streams": {t: caches[t]["S"] for t in tags}, "tokens": {t: caches[t]["n"] for t in tags},
+           "budget_bits": {t: caches[t]["budget"] for t in tags}, "group": {t: caches[t]["g"] for t in tags}}
     line = {
-        "workload": args.workload, "config": w.name, "streams": S, "tokens": n, "kv_heads_per_step": P,
-        "group": g, "batch": Bt, "budget_bits": budget, "total_bits": B, "steps": args.steps,
-        "data": "synthetic (device-generated, seeded)",
-        "encode": {"ms": round(enc_ms, 4), "GBps": round(codec_bytes / (enc_ms * 1e-3) / 1e9, 1),
-                   "pct_hbm_peak": round(100 * codec_bytes / (enc_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 1),
-                   "bytes": int(codec_bytes)},
-        "decode": {"ms": round(dec_ms, 4), "GBps": round(codec_bytes / (dec_ms * 1e-3) / 1e9, 1),
-                   "pct_hbm_peak": round(100 * codec_bytes / (dec_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 1)},
-        "attention": {"us_per_step": round(att_ms * 1e3, 1), "steps_per_s": round(1e3 / att_ms, 1),
-                      "tokens_per_s": round(Bt * 1e3 / att_ms, 1),
-                      "GBps": round(att_bytes / (att_ms * 1e-3) / 1e9, 1),
-                      "pct_hbm_peak": round(100 * att_bytes / (att_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 1),
-                      "bytes": int(att_bytes)},
-        "setup_s": round(setup_s, 1), "calibrate_s": round(cal_s, 1),
+        "metric": "KV codec encode/decode GB/s (% of HBM peak); compressed decode-attn tokens/s",
+        "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (device-generated, seeded)", "config": cfg,
+        "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 1),
+        "codec_GBps": round(codec_bytes / (codec_ms * 1e-3) / 1e9, 1),
+        "codec_pct_hbm_peak": round(100.0 * codec_bytes / (codec_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 1),
+        "attention": att,
+        "breakdown": per_op,
+        "roofline": {"bound": "hbm", "kernel": dkey, "launches_per_step": 1,
+                     "algorithmic_bytes_per_launch": d["algorithmic_bytes_per_launch"],
+                     "avg_launch_us": d["avg_launch_us"], "achieved": d["achieved"], "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": d["frac"], "traffic": d["traffic"]},
+        "roofline_by_kernel": by_kernel,
+        "setup_s": {t: round(caches[t]["setup_s"], 1) for t in tags},
+        "calibrate_s": {t: round(caches[t]["calibrate_s"], 1) for t in tags},
     }
+    # the caches are not needed any more: free them before the extras
+    del ops, caches
+    torch.cuda.empty_cache()
+    if not args.no_extras and args.workload == "full":
+        line["layer"] = layer_step(args, dev)
+    if not args.no_cpu_baseline and args.workload == "full":
+        line["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(line), flush=True)
 
 
@@ -622,11 +722,14 @@ def summarize(args):
                 for cname, v in cs.items():
                     per[name][cname].append(v)
         out.append(f"kernel_source_sha256_16: {source_digest()}")
-        # 32-token blocks per launch: Llama-layer step 16 streams x 32768
-        # tokens for the codec kernels, 8 KV heads x 32768 for attention; the
-        # Llama cache (--workload llama_cache) 512 streams and 256 KV heads x 131072
-        cache = args.workload == "llama_cache"
-        blocks = {"k_att_main": (256 * 131072 if cache else 8 * 32768) // 32}
+        # 32-token blocks per launch of the codec kernels and of attention:
+        # Llama layer 16 streams / 8 KV heads x 32768 tokens; Llama cache 512
+        # streams / 256 KV heads x 131072; Qwen batch 3584 streams / 1792 KV
+        # heads x 32768
+        codec_tok, att_tok = {"llama_cache": (512 * 131072, 256 * 131072),
+                              "qwen_batch": (3584 * 32768, 1792 * 32768)}.get(args.workload,
+                                                                            (16 * 32768, 8 * 32768))
+        blocks = {"k_att_main": att_tok // 32}
         for kname, pnames in PROFILE_NAME.items():
             if not any(pn in per for pn in pnames):
                 continue
@@ -636,7 +739,7 @@ def summarize(args):
                     cs[c] += v
             pname = " + ".join(pn for pn in pnames if pn in per)
             avg = {c: sum(v) / len(v) for c, v in cs.items()}
-            nb = blocks.get(kname, (512 * 131072 if cache else 16 * 32768) // 32)
+            nb = blocks.get(kname, codec_tok // 32)
             out.append(f"== {kname}  ({pname}; {len(next(iter(cs.values())))} dispatches per counter)")
             for c in sorted(avg):
                 out.append(f"   {c:40s} {avg[c]:18.1f}")
@@ -718,11 +821,16 @@ def summarize(args):
 
 def _cpu_worker(args):
     """One process of the CPU baseline: the oracle, as it stands, on KV head
-    `head` of the Llama layer (4096 tokens at 2.0 bits: calibrate, encode,
-    decode both streams, one attention step) plus one Walsh-Hadamard stream
-    of 4096 tokens (encode + decode), repeated for about `seconds`, BLAS on
-    one thread. Returns (algorithmic bytes, repetitions, seconds)."""
-    head, seconds = args
+    pairs of the full-size workloads at their full length, BLAS on one
+    thread: calibrate K and V (2048 tokens), encode and decode both streams,
+    one attention step. The pairs alternate between the Qwen batch (32768
+    tokens, 1.33 bits) and the Llama cache (131072 tokens, 2.0 bits), starting
+    at a different pair in each process, until `seconds` have passed (a pair
+    in progress is finished). Input generation is not timed. With `layer`,
+    the sample is the Llama layer instead (4096-token KV head pairs at 2.0
+    bits plus a Walsh-Hadamard stream). Returns (algorithmic bytes,
+    description of the pairs done, seconds)."""
+    proc, seconds, layer = args
     for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
         os.environ[var] = "1"
     import numpy as np
@@ -731,39 +839,53 @@ def _cpu_worker(args):
     import synth
     from oracle import codec, rht
 
-    w, w3 = synth.WORKLOADS[WORKLOAD], synth.WORKLOADS[RHT_WORKLOAD]
-    n = 4096
-    k = synth.stream(w, 0, 0, head, 0, n=n)
-    v = synth.stream(w, 0, 0, head, 1, n=n)
-    x3 = synth.stream(w3, 0, 0, head, 0, n=n)
-    q = synth.queries(w, 0, 0, head).astype(np.float64)
-    cb = rht.codebook_fp32(rht.lloyd_max(synth.sphere_coordinate_samples(200000))[0])
-    rst = rht.make_state(synth.random_signs(3, 0, 0, head, 0), cb)
-    nbytes_rep = 2 * 2 * algorithmic_bytes(256, n, 1) + n * 2 * 256 / 8.0 + 2 * n * (256 + 48 + 4)
-    reps, total_bytes = 0, 0.0
+    done, total_bytes, busy = [], 0.0, 0.0
     with threadpool_limits(limits=1):
-        t0 = time.perf_counter()
-        while True:
-            ks, vs = codec.calibrate_head(k, 2048, 2.0), codec.calibrate_head(v, 2048, 2.0)
+        k_ = 0
+        while busy < seconds:
+            if layer:
+                w = synth.WORKLOADS[WORKLOAD]
+                cfg, lyr, b, h, n, avg = WORKLOAD, 0, 0, (proc + k_) % w.kv_heads, 4096, 2.0
+            else:
+                cfg = 5 if (proc + k_) % 2 == 0 else 4
+                w = synth.WORKLOADS[cfg]
+                j = proc * 7 + k_
+                lyr, b, h = j % w.layers, (j // w.layers) % w.batch, j % w.kv_heads
+                n, avg = w.n_tokens, w.budgets[0]
+            k = synth.stream(w, lyr, b, h, 0, n=n)
+            v = synth.stream(w, lyr, b, h, 1, n=n)
+            q = synth.queries(w, lyr, b, h).astype(np.float64)
+            t0 = time.perf_counter()
+            ks, vs = codec.calibrate_head(k, 2048, avg), codec.calibrate_head(v, 2048, avg)
             kp, vp = codec.encode_kv(ks, k), codec.encode_kv(vs, v)
             codec.decode_kv(ks, kp, n, "bf16")
             codec.decode_kv(vs, vp, n, "bf16")
             codec.attend_compressed(ks, vs, kp, vp, n, q)
-            p3, n3 = rht.encode_kv(rst, x3)
-            rht.decode_kv(rst, p3, n3, n, "bf16")
-            reps += 1
-            total_bytes += nbytes_rep
-            el = time.perf_counter() - t0
-            if el >= seconds:
-                break
-    return total_bytes, reps, el
+            B = int(ks["total_bits"])
+            nbytes = 2 * 2 * algorithmic_bytes(B, n, 1) + n * 2 * B / 8.0
+            if layer:
+                w3 = synth.WORKLOADS[RHT_WORKLOAD]
+                x3 = synth.stream(w3, 0, 0, h, 0, n=n)
+                cb = rht.codebook_fp32(rht.lloyd_max(synth.sphere_coordinate_samples(200000))[0])
+                rst = rht.make_state(synth.random_signs(3, 0, 0, h, 0), cb)
+                t1 = time.perf_counter()
+                p3, n3 = rht.encode_kv(rst, x3)
+                rht.decode_kv(rst, p3, n3, n, "bf16")
+                busy += time.perf_counter() - t1
+                nbytes += 2 * n * (256 + 48 + 4)
+            busy += time.perf_counter() - t0
+            total_bytes += nbytes
+            done.append(f"cfg{cfg}:L{lyr}/b{b}/h{h}")
+            k_ += 1
+    return total_bytes, done, busy
 
 
-def cpu_baseline(seconds):
-    """The CPU oracle, as it stands, on a bounded sample of the workload, in
-    one process per host core (at most 16, the host share of one GPU), each
-    on its own KV head (see _cpu_worker); falls back to one process if a
-    process pool cannot be started."""
+def cpu_baseline(seconds, layer=False):
+    """The CPU oracle, as it stands, on a bounded sample of the workload (see
+    _cpu_worker), in one process per host core (at most 16, the host share of
+    one GPU), BLAS on one thread each; falls back to one process if a
+    process pool cannot be started. GB/s = the sample's algorithmic bytes
+    over the longest process's busy time."""
     import multiprocessing as mp
     cores = max(1, min(16, len(os.sched_getaffinity(0))))
     model = ""
@@ -776,17 +898,22 @@ def cpu_baseline(seconds):
         pass
     try:
         with mp.get_context("spawn").Pool(cores) as pool:
-            res = pool.map(_cpu_worker, [(h % 8, seconds) for h in range(cores)])
+            res = pool.map(_cpu_worker, [(p, seconds, layer) for p in range(cores)])
     except (OSError, RuntimeError):
         cores = 1
-        res = [_cpu_worker((0, seconds))]
+        res = [_cpu_worker((0, seconds, layer))]
     total = sum(r[0] for r in res)
     el = max(r[2] for r in res)
-    reps = sum(r[1] for r in res)
+    pairs = [p for r in res for p in r[1]]
+    n5 = sum(1 for p in pairs if p.startswith("cfg5"))
+    n4 = sum(1 for p in pairs if p.startswith("cfg4"))
+    what = (f"{len(pairs)} Llama-layer KV head pairs x 4096 tokens at 2.0 bits (+ a Walsh-Hadamard stream each)"
+            if layer else
+            f"{n5} Qwen-batch KV head pairs x 32768 tokens at 1.33 bits and {n4} Llama-cache KV head pairs x "
+            f"131072 tokens at 2.0 bits, full length ({', '.join(pairs[:6])}, ...)")
     return {"value": round(total / el / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
-            "sample": f"{cores} processes x about {seconds:.0f} s, {reps} repetitions in all of (1 KV head pair x "
-                      f"4096 tokens at 2.0 bits: calibrate+encode+decode+attention; 1 Student-t stream x 4096 "
-                      f"tokens: RHT encode+decode), BLAS 1 thread per process, {el:.1f} s; host CPU: {model}"}
+            "sample": f"{cores} processes, BLAS 1 thread each, {el:.1f} s busy in the longest: {what}; per pair "
+                      f"calibrate K and V, encode, decode, one attention step; host CPU: {model}"}
 
 
 if __name__ == "__main__":
