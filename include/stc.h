@@ -357,6 +357,24 @@ stc_status stc_attend_compressed_batched(const void* states_dev, int64_t n_state
                                          float scale, void* ws_dev, size_t ws_bytes,
                                          stc_stream_t stream);
 
+/* For callers that cannot allocate (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): stc_attend_compressed_batched
+ * without a workspace argument. The split partials go to a static device
+ * array of the library (stc_attend_noalloc_max_bytes() bytes, one copy per
+ * device, held until the process ends); a call needing more
+ * (stc_attend_workspace_bytes of its shape) fails with STC_EWORKSPACE before
+ * any device work. The call allocates nothing. Calls that overlap on one
+ * device share the array and race: serialize them (one stream, or events). */
+stc_status stc_attend_compressed_batched_noalloc(const void* states_dev, int64_t n_states,
+                                                 const int32_t* k_state_of_pair_dev,
+                                                 const int32_t* v_state_of_pair_dev,
+                                                 const stc_head_info* infos, int64_t n_pairs,
+                                                 int64_t n_tokens, const void* k_packed_dev,
+                                                 const void* v_packed_dev, int64_t packed_pair_stride,
+                                                 int32_t group, const float* q_dev, float* out_dev,
+                                                 float scale, stc_stream_t stream);
+size_t stc_attend_noalloc_max_bytes(void);
+
 /* stc_attend_compressed_batched with the keys' selective residual sketch
  * (from stc_sketch_kv_batched; pair p's at k_sketch_dev + p*sketch_pair_stride,
  * 16 bytes per token, and |r| at k_rnorm_dev + p*rnorm_pair_stride): every

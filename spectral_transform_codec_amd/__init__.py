@@ -448,3 +448,23 @@ def attend_compressed_batched(states: StateArray, k_state_of_pair: torch.Tensor,
         states.infos, Pn, n, _ptr(k_packed), _ptr(v_packed), k_packed.stride(0), g, _ptr(q), _ptr(out),
         float(scale), _ptr(ws), ws.numel(), _stream()))
     return out
+
+
+def attend_noalloc_max_bytes() -> int:
+    return int(lib().stc_attend_noalloc_max_bytes())
+
+
+def attend_compressed_batched_noalloc(states: StateArray, k_state_of_pair: torch.Tensor,
+                                      v_state_of_pair: torch.Tensor, k_packed: torch.Tensor, v_packed: torch.Tensor,
+                                      n: int, q: torch.Tensor, out: torch.Tensor, scale: Optional[float] = None):
+    """attend_compressed_batched with the library's static scratch instead of
+    a workspace: out fp32 [P][g][128] must be given (the call allocates
+    nothing)."""
+    Pn, g = q.shape[0], q.shape[1]
+    assert k_packed.stride(0) == v_packed.stride(0)
+    scale = (1.0 / np.sqrt(D)) if scale is None else scale
+    check("stc_attend_compressed_batched_noalloc", lib().stc_attend_compressed_batched_noalloc(
+        _ptr(states.blob), states.n, _ptr(_map_arg(k_state_of_pair)), _ptr(_map_arg(v_state_of_pair)),
+        states.infos, Pn, n, _ptr(k_packed), _ptr(v_packed), k_packed.stride(0), g, _ptr(q), _ptr(out),
+        float(scale), _stream()))
+    return out

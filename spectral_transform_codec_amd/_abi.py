@@ -58,6 +58,9 @@ SIGNATURES = {
     "stc_quantize_pack_f32": (c_i32, [P(HeadInfo), c_vp, c_i64, c_vp, c_vp, c_vp]),
     "stc_attend_compressed_batched": (c_i32, [c_vp, c_i64, c_vp, c_vp, P(HeadInfo), c_i64, c_i64, c_vp, c_vp,
                                               c_i64, c_i32, c_vp, c_vp, c_f32, c_vp, c_size, c_vp]),
+    "stc_attend_compressed_batched_noalloc": (c_i32, [c_vp, c_i64, c_vp, c_vp, P(HeadInfo), c_i64, c_i64, c_vp,
+                                                      c_vp, c_i64, c_i32, c_vp, c_vp, c_f32, c_vp]),
+    "stc_attend_noalloc_max_bytes": (c_size, []),
     "stc_attend_compressed": (c_i32, [P(HeadInfo), c_vp, P(HeadInfo), c_vp, c_i64, c_vp, c_vp, c_i32, c_vp,
                                       c_vp, c_f32, c_vp, c_size, c_vp]),
     "stc_attend_rht_batched": (c_i32, [c_vp, c_i64, c_vp, c_vp, P(HeadInfo), c_i64, c_i64, c_vp, c_vp, c_vp, c_vp,

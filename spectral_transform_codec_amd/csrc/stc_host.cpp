@@ -1017,27 +1017,36 @@ stc_status stc_quantize_pack_f32(const stc_head_info* info, const void* state_de
   return ok();
 }
 
-stc_status stc_attend_compressed_batched(const void* states_dev, int64_t n_states, const int32_t* k_map,
-                                         const int32_t* v_map, const stc_head_info* infos, int64_t n_pairs,
-                                         int64_t n_tokens, const void* k_packed_dev, const void* v_packed_dev,
-                                         int64_t packed_pair_stride, int32_t group, const float* q_dev,
-                                         float* out_dev, float scale, void* ws_dev, size_t ws_bytes,
-                                         stc_stream_t stream) {
+// The eigen attention with a given partials area (the caller's workspace, or
+// the library's static scratch for the entry point that allocates nothing).
+static stc_status attend_eigen(const char* who, const void* states_dev, int64_t n_states, const int32_t* k_map,
+                               const int32_t* v_map, const stc_head_info* infos, int64_t n_pairs, int64_t n_tokens,
+                               const void* k_packed_dev, const void* v_packed_dev, int64_t packed_pair_stride,
+                               int32_t group, const float* q_dev, float* out_dev, float scale, void* ws_dev,
+                               size_t ws_bytes, bool scratch, stc_stream_t stream) {
   bool rht = false;
   int mb = 0;
   if (stc_status s = check_batch("attend_compressed", states_dev, n_states, infos, n_pairs, n_tokens,
                                  packed_pair_stride, &rht, &mb)) return s;
-  if (rht) return fail(STC_EUNSUPPORTED, "attend_compressed: eigen/identity states only");
-  if (group < 1 || group > 16) return fail(STC_EUNSUPPORTED, "attend_compressed: group %d outside 1..16", group);
-  if (n_tokens <= 0) return fail(STC_EINVAL, "attend_compressed: need at least one cached token");
-  if (!k_packed_dev || !v_packed_dev || !q_dev || !out_dev || !ws_dev)
-    return fail(STC_EINVAL, "attend_compressed: NULL buffer");
+  if (rht) return fail(STC_EUNSUPPORTED, "%s: eigen/identity states only", who);
+  if (group < 1 || group > 16) return fail(STC_EUNSUPPORTED, "%s: group %d outside 1..16", who, group);
+  if (n_tokens <= 0) return fail(STC_EINVAL, "%s: need at least one cached token", who);
+  if (!k_packed_dev || !v_packed_dev || !q_dev || !out_dev || (!scratch && !ws_dev))
+    return fail(STC_EINVAL, "%s: NULL buffer", who);
   if (!aligned(k_packed_dev, 16) || !aligned(v_packed_dev, 16) || !aligned(q_dev, 16) || !aligned(out_dev, 16) ||
-      !aligned(ws_dev, 256))
-    return fail(STC_EINVAL, "attend_compressed: misaligned buffer");
-  if (!std::isfinite(scale)) return fail(STC_EINVAL, "attend_compressed: scale must be finite");
+      (!scratch && !aligned(ws_dev, 256)))
+    return fail(STC_EINVAL, "%s: misaligned buffer", who);
+  if (!std::isfinite(scale)) return fail(STC_EINVAL, "%s: scale must be finite", who);
   const size_t need = stc_attend_workspace_bytes(n_pairs, group, n_tokens);
-  if (ws_bytes < need) return fail(STC_EWORKSPACE, "attend_compressed: workspace %zu < %zu", ws_bytes, need);
+  if (scratch) {
+    if (need > attend_scratch_bytes())
+      return fail(STC_EWORKSPACE, "%s: the call needs %zu bytes of partials, the static scratch holds %zu", who, need,
+                  attend_scratch_bytes());
+    if (attend_scratch(&ws_dev)) return fail(STC_EDEVICE, "%s: scratch address: %s", who,
+                                             hipGetErrorString(hipGetLastError()));
+  } else if (ws_bytes < need) {
+    return fail(STC_EWORKSPACE, "%s: workspace %zu < %zu", who, ws_bytes, need);
+  }
   const unsigned char* st = static_cast<const unsigned char*>(states_dev);
   AttendLaunch a{st, k_map, st, v_map, n_states, n_pairs, n_tokens, packed_pair_stride,
                  static_cast<const unsigned char*>(k_packed_dev), static_cast<const unsigned char*>(v_packed_dev),
@@ -1046,6 +1055,28 @@ stc_status stc_attend_compressed_batched(const void* states_dev, int64_t n_state
   if (launch_attend(a, stream)) return fail(STC_EDEVICE, "attend launch: %s", hipGetErrorString(hipGetLastError()));
   return ok();
 }
+
+stc_status stc_attend_compressed_batched(const void* states_dev, int64_t n_states, const int32_t* k_map,
+                                         const int32_t* v_map, const stc_head_info* infos, int64_t n_pairs,
+                                         int64_t n_tokens, const void* k_packed_dev, const void* v_packed_dev,
+                                         int64_t packed_pair_stride, int32_t group, const float* q_dev,
+                                         float* out_dev, float scale, void* ws_dev, size_t ws_bytes,
+                                         stc_stream_t stream) {
+  return attend_eigen("attend_compressed", states_dev, n_states, k_map, v_map, infos, n_pairs, n_tokens, k_packed_dev,
+                      v_packed_dev, packed_pair_stride, group, q_dev, out_dev, scale, ws_dev, ws_bytes, false, stream);
+}
+
+stc_status stc_attend_compressed_batched_noalloc(const void* states_dev, int64_t n_states, const int32_t* k_map,
+                                                 const int32_t* v_map, const stc_head_info* infos, int64_t n_pairs,
+                                                 int64_t n_tokens, const void* k_packed_dev, const void* v_packed_dev,
+                                                 int64_t packed_pair_stride, int32_t group, const float* q_dev,
+                                                 float* out_dev, float scale, stc_stream_t stream) {
+  return attend_eigen("attend_compressed_noalloc", states_dev, n_states, k_map, v_map, infos, n_pairs, n_tokens,
+                      k_packed_dev, v_packed_dev, packed_pair_stride, group, q_dev, out_dev, scale, nullptr, 0, true,
+                      stream);
+}
+
+size_t stc_attend_noalloc_max_bytes(void) { return attend_scratch_bytes(); }
 
 stc_status stc_attend_compressed_sketch_batched(const void* states_dev, int64_t n_states, const int32_t* k_map,
                                                 const int32_t* v_map, const stc_head_info* infos, int64_t n_pairs,

@@ -182,5 +182,10 @@ int launch_encode_rht(const EncodeLaunch& a, void* stream);
 int launch_sketch_eigen(const EncodeLaunch& a, void* stream);
 int launch_decode_rht(const DecodeLaunch& a, void* stream);
 int launch_attend(const AttendLaunch& a, void* stream);
+// The static device scratch of the attention entry point that allocates
+// nothing: its size, and its address on the current device (looked up once
+// per device; nonzero on failure).
+size_t attend_scratch_bytes();
+int attend_scratch(void** ptr);
 
 }  // namespace stc

@@ -25,6 +25,8 @@
 //  - the Walsh-Hadamard butterfly runs in registers, one token per lane.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "stc_internal.h"
 
 namespace stc {
@@ -2154,6 +2156,32 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_att_main(AttK a) {
     }
     if (4 * (c4 + 1) < g) __syncthreads();
   }
+}
+
+// Partials area of stc_attend_compressed_batched_noalloc: a file-scope device
+// array, one copy on every device the library runs on, held until the process
+// ends. Host code uses the address hipGetSymbolAddress gives on the current
+// device (looked up once per device), never the array's name. Calls that
+// overlap on one device share it and race; the partials need no clearing
+// (the main kernel writes every one the merge reads).
+constexpr size_t ATT_SCRATCH_BYTES = (size_t)32 << 20;
+static __device__ __align__(256) unsigned char scratch[ATT_SCRATCH_BYTES];
+
+size_t attend_scratch_bytes() { return ATT_SCRATCH_BYTES; }
+
+int attend_scratch(void** ptr) {
+  static std::mutex mu;
+  static void* per_device[64] = {};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 1;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!per_device[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return 1;
+    per_device[dev] = p;
+  }
+  *ptr = per_device[dev];
+  return 0;
 }
 
 typedef void (*AttKernel)(AttK);

@@ -17,4 +17,6 @@ int launch_decode_eigen(const DecodeLaunch&, void*) { return 1; }
 int launch_encode_rht(const EncodeLaunch&, void*) { return 1; }
 int launch_decode_rht(const DecodeLaunch&, void*) { return 1; }
 int launch_attend(const AttendLaunch&, void*) { return 1; }
+size_t attend_scratch_bytes() { return 0; }
+int attend_scratch(void**) { return 1; }
 }  // namespace stc
