@@ -72,13 +72,15 @@ def parse():
 # Kernel launched by each timed op that is a single kernel; the roofline is
 # reported for the kernel with the largest share of the step.
 KERNEL_OF_OP = {"encode": "k_encode_eigen<bf16>", "decode": "k_decode_eigen<bf16>",
-                "attend": "k_att_main", "rht_encode": "k_rht_encode", "rht_decode": "k_rht_decode"}
+                "attend": "k_att2", "rht_encode": "k_rht_encode", "rht_decode": "k_rht_decode"}
 # rocprofv3 kernel names of the same kernels (the variants the step runs:
 # records of 32 * 2^s bits at 4.0 and 2.0 bits take the slot-layout variant,
 # the 170-bit records at 1.33 bits the packed-stream one)
 PROFILE_NAME = {"k_encode_eigen<bf16>": ("void stc::k_encode_eigen<0, true>(stc::EncK)",
                                          "void stc::k_encode_eigen<0, false>(stc::EncK)"),
                 "k_decode_eigen<bf16>": ("void stc::k_decode_eigen<0, 8>(stc::DecK)",),
+                "k_att2": ("void stc::k_att2<4, 10, 1, 16>(stc::AttK)", "void stc::k_att2<4, 10, 2, 8>(stc::AttK)",
+                           "void stc::k_att2<8, 12, 3, 8>(stc::AttK)"),
                 "k_att_main": ("void stc::k_att_main<8, false, false, true>(stc::AttK)",
                                "void stc::k_att_main<8, false, false, false>(stc::AttK)"),
                 "k_rht_encode": ("void stc::k_rht_encode<false>(stc::RhtK)",),
@@ -729,7 +731,7 @@ def summarize(args):
         codec_tok, att_tok = {"llama_cache": (512 * 131072, 256 * 131072),
                               "qwen_batch": (3584 * 32768, 1792 * 32768)}.get(args.workload,
                                                                             (16 * 32768, 8 * 32768))
-        blocks = {"k_att_main": att_tok // 32}
+        blocks = {"k_att_main": att_tok // 32, "k_att2": att_tok // 32}
         for kname, pnames in PROFILE_NAME.items():
             if not any(pn in per for pn in pnames):
                 continue

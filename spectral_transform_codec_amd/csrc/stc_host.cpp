@@ -297,6 +297,30 @@ stc_status build_eigen_blob(int d, int xform, const double* u, const double* lam
   }
   for (int j = 0; j < d; ++j) h->bits4[j / 8] |= (uint32_t)bits[j] << (4 * (j % 8));
   fill_unpack_plan(h);
+  {
+    // attention value columns: each code cut at the record's byte boundaries
+    AttVCol* vc = reinterpret_cast<AttVCol*>(blob.data() + OFF_ATTV);
+    uint32_t* vch = reinterpret_cast<uint32_t*>(blob.data() + OFF_ATTVCH);
+    int nc = 0;
+    for (int j = 0; j < d; ++j) {
+      const int first = nc;
+      int bit = h->off[j], z = 0, rem = bits[j];
+      while (rem > 0) {
+        const int s = bit & 7, w = std::min(8 - s, rem);
+        const uint32_t m = ((1u << w) - 1u) << s;
+        vc[nc].row = (uint32_t)(bit >> 3);
+        vc[nc].mask2 = m | (m << 16);
+        vc[nc].fac = std::ldexp(1.0f, 24 - s + z);
+        vc[nc].chan = (uint32_t)j;
+        ++nc;
+        bit += w;
+        z += w;
+        rem -= w;
+      }
+      vch[j] = (uint32_t)first | ((uint32_t)(nc - first) << 16);
+    }
+    h->n_vcols = nc;
+  }
   for (int R = 0; R < D; ++R) {
     const int i = enc_row_channel(R);  // output dim of stored row R (same permutation as the encode basis)
     for (int j = 0; j < d; ++j) split_bf16(ud[(size_t)i * d + j] * steps[j], &w_hi[R * D + j], &w_lo[R * D + j]);
@@ -1017,6 +1041,19 @@ stc_status stc_quantize_pack_f32(const stc_head_info* info, const void* state_de
   return ok();
 }
 
+// 1 KiB loads that cover one 32-token block (4 B bytes) of every state's
+// stream, the block starting up to 12 bytes past a 16-byte boundary when
+// 4 B is not a multiple of 16.
+static int attend_chunks(const stc_head_info* infos, int64_t n) {
+  int c = 1;
+  for (int64_t i = 0; i < n; ++i) {
+    const int64_t bytes = 4LL * infos[i].total_bits;
+    const int64_t span = bytes + ((bytes & 15) ? 12 : 0);
+    c = std::max(c, (int)((span + 1023) / 1024));
+  }
+  return c;
+}
+
 // The eigen attention with a given partials area (the caller's workspace, or
 // the library's static scratch for the entry point that allocates nothing).
 static stc_status attend_eigen(const char* who, const void* states_dev, int64_t n_states, const int32_t* k_map,
@@ -1052,6 +1089,7 @@ static stc_status attend_eigen(const char* who, const void* states_dev, int64_t 
                  static_cast<const unsigned char*>(k_packed_dev), static_cast<const unsigned char*>(v_packed_dev),
                  group, q_dev, out_dev, scale, static_cast<unsigned char*>(ws_dev), mb};
   a.rec = records_word_pow2(infos, n_states);
+  a.att_chunks = attend_chunks(infos, n_states);
   if (launch_attend(a, stream)) return fail(STC_EDEVICE, "attend launch: %s", hipGetErrorString(hipGetLastError()));
   return ok();
 }

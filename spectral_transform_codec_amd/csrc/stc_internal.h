@@ -26,7 +26,22 @@ constexpr size_t OFF_SKP_HI = OFF_THR;
 constexpr size_t OFF_SKP_LO = OFF_THR + 32768;
 constexpr size_t OFF_SKT32 = OFF_THR + 65536;
 constexpr size_t OFF_GRAM = OFF_THR + 131072;        // double second moment [i][j]
-static_assert(OFF_GRAM + 131072 <= STATE_BYTES, "state layout overflows the blob");
+// Value columns of the attention kernel (eigen / identity states): each kept
+// channel's code cut at the record's byte boundaries, in record order; column
+// c holds the bits of record byte `row` selected by `mask2` (the mask in both
+// 16-bit halves of a word), and its fragment, read as an fp16 subnormal,
+// times `fac` is that fragment's contribution to the channel's code.
+// vch[j] = first column of channel j | number of its columns << 16.
+constexpr size_t OFF_ATTV = OFF_GRAM + 131072;
+constexpr int ATT_MAX_VCOLS = 256;
+struct AttVCol {
+  uint32_t row;
+  uint32_t mask2;
+  float fac;
+  uint32_t chan;
+};
+constexpr size_t OFF_ATTVCH = OFF_ATTV + ATT_MAX_VCOLS * sizeof(AttVCol);
+static_assert(OFF_ATTVCH + D * sizeof(uint32_t) <= STATE_BYTES, "state layout overflows the blob");
 
 // Quantizer fast path for a channel with L levels: y = c * fl(1/step) +
 // (L/2 + eps_L) in fp32 with eps_L = L * 2^-21. Against the exact count of
@@ -44,7 +59,8 @@ struct alignas(16) DevHdr {
   int32_t nmax16;       // 16 * ceil((last kept channel + 1) / 16): encode N extent
   int32_t kmax32;       // 32 * ceil((last kept channel + 1) / 32): decode K extent
   int32_t sketch_bits;  // Walsh-Hadamard states: key residual sketch bits per token (0: none)
-  int32_t pad[2];
+  int32_t n_vcols;      // eigen / identity: value columns of the attention kernel (OFF_ATTV)
+  int32_t pad;
   uint8_t bits[D];
   uint16_t off[D];      // bit offset of channel j inside a token record
   float inv_step[D];    // fl32(1 / step_j); 0 for a dropped channel or a zero step
@@ -173,6 +189,8 @@ struct AttendLaunch {
   const float* k_rnorm = nullptr;
   int64_t sketch_stride = 0, rnorm_stride = 0;
   bool rec = false;  // every record is 0 or 32 * 2^s bits: one word-aligned LDS slot per record
+  int att_chunks = 3;  // 1 KiB loads that cover one 32-token block of any stream (its records may
+                       // start 4, 8 or 12 bytes past a 16-byte boundary)
 };
 
 int launch_gram(const void* x, int dtype, int64_t ld, int64_t n_calib, double* gram, void* stream);

@@ -2158,6 +2158,485 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_att_main(AttK a) {
   }
 }
 
+// ======================================================================
+// Decode-step attention over eigen / identity caches with the packed bits
+// fed to the matrix cores (k_att2; one workgroup per (KV head, token split),
+// the same split partials and merge kernel as k_att_main).
+//
+// Scores. A K record is a string of B bits and the score is linear in them:
+// record bit c, bit k of channel j's code, carries a_j 2^k with
+// a_j = (U_K^T q)_j step_j scale log2(e). Each lane holds half of its token's
+// record, realigned to bit 0 by funnel shifts, and turns each record word w
+// into eight int8 operand words with one AND each: w & (0x01010101 << r) and
+// (w >> 4) & (0x01010101 << r), r = 0..3, whose byte q is bit 8q + r (or
+// 8q + 4 + r) of w times 2^r. The weights a_j 2^k 2^-r, scaled by a power of
+// two per query head, are split into three int8 parts that sit in rows
+// 8p + H (p = 0..2) of the 32x32x32 int8 MFMA, so the accumulators are exact
+// integers and each lane adds its heads' three parts afterwards.
+// Values. Each lane quad (four consecutive tokens) transposes its V record
+// words by byte, so that one word holds one record byte of the four tokens;
+// those words go to LDS rows [record byte][token quad]. A value column is the
+// fragment of one channel's code that lies in one record byte: lane (column,
+// token octet) reads two words of the column's row and masks the fragment of
+// tokens (0, 2) and, shifted down by 8, of tokens (1, 3) in place. Each
+// 16-bit half is then an fp16 subnormal fragment * 2^(shift - 24), exact, and
+// the words are the B operand of the fp16 16x16x32 MFMA against P (the
+// softmax weights stored in the same token order). When the waves merge, the
+// columns of each channel are added with their scales 2^(24 - shift + offset
+// of the fragment in the code), which gives the split partials in code units.
+// ======================================================================
+constexpr int AT2_WAVES = 16;
+constexpr int AT2_THREADS = 64 * AT2_WAVES;
+constexpr int AT2_PST = 136;  // fp16 per token octet of P ([octet][16 heads][8] + 8 pad: octets 4 banks apart)
+constexpr int AT2_BT = 32;    // tokens per wave block
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
+
+// byte of a score-weight row that holds record bit c: record word dw = c >> 5
+// (the i-th word of lane half dw >= R2, each half's words R2M apart), operand
+// half (c & 7) >> 2, operand word c & 3, byte (c >> 3) & 3
+__device__ __forceinline__ unsigned at2_tab_off(unsigned c, unsigned R2, unsigned R2M) {
+  const unsigned dw = c >> 5, hh = dw >= R2 ? 1u : 0u;
+  return (dw - hh * R2 + hh * R2M) * 32u + ((c & 7u) >> 2) * 16u + (c & 3u) * 4u + ((c >> 3) & 3u);
+}
+// position of token t of a block in the P / value-operand order: inside each
+// group of four tokens the order is 0, 2, 1, 3
+__device__ __forceinline__ int at2_pos(int t) { return (t & ~3) | ((t & 1) << 1) | ((t >> 1) & 1); }
+
+// The int8 operand words of record word w: half kk of its eight.
+__device__ __forceinline__ u32x4 at2_bits(unsigned w, int kk) {
+  const unsigned x = kk ? (w >> 4) : w;
+  return (u32x4){x & 0x01010101u, x & 0x02020202u, x & 0x04040404u, x & 0x08080808u};
+}
+
+// A lane's half record: R2 words from record bit 32 R2 h of token t, realigned.
+// Streams of records of B = 256 s bits (s >= 1) are word-aligned and read with
+// 16-byte loads, B = 128 with 8-byte loads; other lengths read R2 + 1 words and
+// funnel-shift them. Words past the stream end read as 0.
+// A lane's half record from a wave's staging buffer: R2 words from record bit
+// 32 R2 h of token t, the block's records starting at bit `off` of the buffer;
+// realigned to bit 0 with funnel shifts (16-byte reads when every start is
+// 16-byte aligned).
+template <int R2M>
+__device__ __forceinline__ void at2_read(unsigned (&r)[R2M], const unsigned* buf, unsigned off, unsigned B, int R2,
+                                         int t, int h) {
+#pragma unroll
+  for (int j = 0; j < R2M; ++j) r[j] = 0u;
+  if (B == 0) return;
+  if ((B & 255u) == 0u) {
+    // records of 256 s bits were staged by at2_stage in the order below:
+    // 16-byte chunk q of half h of token t at chunk t + 32 h + 64 q
+#pragma unroll
+    for (int j = 0; j < R2M; j += 4)
+      if (j < R2) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(buf + 4 * (t + 32 * h + 64 * (j >> 2)));
+        r[j] = v[0]; r[j + 1] = v[1]; r[j + 2] = v[2]; r[j + 3] = v[3];
+      }
+    return;
+  }
+  const unsigned P = off + (unsigned)t * B + 32u * (unsigned)R2 * (unsigned)h;
+  const unsigned* w = buf + (P >> 5);
+  if ((P & 127u) == 0u && (B & 127u) == 0u) {   // (uniform: off, B and R2 multiples of 128 bits, 4 words)
+#pragma unroll
+    for (int j = 0; j < R2M; j += 4)
+      if (j < R2) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(w + j);
+        r[j] = v[0]; r[j + 1] = v[1]; r[j + 2] = v[2]; r[j + 3] = v[3];
+      }
+    return;
+  }
+  const unsigned sh = P & 31u;
+  unsigned x[R2M + 1];
+#pragma unroll
+  for (int j = 0; j <= R2M; ++j) x[j] = j <= R2 ? w[j] : 0u;
+#pragma unroll
+  for (int j = 0; j < R2M; ++j) r[j] = __builtin_amdgcn_alignbit(x[j + 1], x[j], sh);
+}
+
+// Request the records of block blk of one stream (4 B bytes from byte 4 B blk)
+// into a wave's staging buffer: NCH loads of 16 bytes per lane straight to
+// LDS, from the 16-byte boundary at or below the block's first byte (returned
+// in bits, the offset of the records in the buffer). Lanes past the stream
+// end load its first 16 bytes instead, so every call issues NCH loads.
+template <int NCH>
+__device__ __forceinline__ unsigned at2_stage(const unsigned char* stream, long long blk, unsigned B, long long plen,
+                                              unsigned* buf, int lane) {
+  const long long start = blk * 4LL * (long long)B;
+  const long long base = start & ~15LL;
+  // records of 256 s bits: slot lane of load c takes chunk 2 s t + s h + c of
+  // the block (t = lane & 31, h = lane >> 5), so that the 16-byte reads of
+  // 16 consecutive lanes cover 64 banks (in block order they would pair up)
+  const bool swz = (B & 255u) == 0u;
+  const long long s_ = (long long)(B >> 8);
+  const long long chunk = swz ? 2 * s_ * (lane & 31) + s_ * (lane >> 5) : (long long)lane;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    long long byte = swz ? base + 16LL * (chunk + c) : base + 1024LL * c + 16LL * lane;
+    if (byte + 16 > plen) byte = 0;
+    __builtin_amdgcn_global_load_lds(stream + byte, (__attribute__((address_space(3))) void*)(buf + 256 * c), 16, 0,
+                                     0);
+  }
+  return (unsigned)(start - base) * 8u;
+}
+
+// Dynamic LDS of k_att2<R2M, NT, NCH, W>: the score weights, the value column
+// table and the per-head scales, then the larger of the prologue scratch, the
+// W wave regions and the merge scratch.
+__host__ __device__ constexpr size_t at2_lds_bytes(int R2M, int NT, int NCH, int W) {
+  const size_t fixed = (size_t)32 * (64 * R2M + 16) + ATT_MAX_VCOLS * 8 + 8 * 4;
+  const size_t pro = (size_t)(128 * 8 + 8 * 8 * 128 + 8 * 128) * 4 + 2 * 64 * R2M + 8 * 4;
+  const size_t waves = (size_t)W * (4 * 256 * NCH + 64 * R2M + 32 + 4 * AT2_PST / 2 + 32) * 4;
+  const size_t merge = (size_t)W * 4 * (16 * NT + 4) * 4;
+  const size_t big = pro > waves ? (pro > merge ? pro : merge) : (waves > merge ? waves : merge);
+  return fixed + big;
+}
+
+// R2M: record words per half record at most (records of at most 64 R2M bits);
+// NT: value tiles at most; NCH: 1 KiB loads per stream and block; W: waves.
+template <int R2M, int NT, int NCH, int W>
+__global__ void __launch_bounds__(64 * W, 1) k_att2(AttK a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  constexpr int TABW = 64 * R2M;               // bytes of a score-weight row (record bits <= 64 R2M)
+  constexpr int TROW = TABW + 16;              // row stride: rows 4 banks apart, so 16 lanes' reads hit 64 banks
+  constexpr int VROWS = 8 * R2M;               // record bytes
+  constexpr int VPAD = 32;                     // words between the two halves' rows
+  constexpr int VWORDS = VROWS * 8 + VPAD;
+  constexpr int SWORDS = 256 * NCH;            // words of one staging buffer
+  constexpr int WREG = 4 * SWORDS + VWORDS + 4 * AT2_PST / 2 + 32;  // words per wave region
+  signed char* sA = reinterpret_cast<signed char*>(smem);            // [32][TROW]
+  u32x2* sVc = reinterpret_cast<u32x2*>(smem + 32 * TROW);           // [256] (row word offset, mask2)
+  float* sInvS = reinterpret_cast<float*>(sVc + ATT_MAX_VCOLS);     // [8]
+  unsigned* sReg0 = reinterpret_cast<unsigned*>(sInvS + 8);         // wave regions / prologue scratch
+  const int nwav = W;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int t32 = lane & 31, h = lane >> 5;
+  const int c16 = lane & 15, g4 = lane >> 4;
+  const long long sp = blockIdx.x, p = blockIdx.y;
+  const long long pg = a.pair_base + p;
+  const long long n = a.n_tokens;
+  const int g = a.group;
+  const long long ksi = state_index(a.k_map, pg, a.n_states), vsi = state_index(a.v_map, pg, a.n_states);
+  if (ksi < 0 || vsi < 0) return;  // (the whole workgroup) the merge writes NaN for this pair
+  const unsigned char* kst = a.k_states + (size_t)ksi * STATE_BYTES;
+  const unsigned char* vst = a.v_states + (size_t)vsi * STATE_BYTES;
+  const DevHdr* hk = reinterpret_cast<const DevHdr*>(kst);
+  const DevHdr* hv = reinterpret_cast<const DevHdr*>(vst);
+  const unsigned Bk = (unsigned)__builtin_amdgcn_readfirstlane(hk->total_bits);
+  const unsigned Bv = (unsigned)__builtin_amdgcn_readfirstlane(hv->total_bits);
+  const int R2k = (int)((((Bk + 31u) >> 5) + 1u) >> 1), R2v = (int)((((Bv + 31u) >> 5) + 1u) >> 1);
+  const int ncols = __builtin_amdgcn_readfirstlane(hv->n_vcols);
+  const long long t_begin = sp * a.split_tokens;
+  long long t_end = t_begin + a.split_tokens;
+  if (t_end > n) t_end = n;
+
+  // ------------------------------------------------------------ prologue
+  {
+    float* sqT = reinterpret_cast<float*>(sReg0);        // q^T [128][8]
+    float* red = sqT + 128 * 8;                          // [8 parts][8 heads][128]
+    float* sAf = red + 8 * 8 * 128;                      // a [8][128]
+    unsigned short* sBit = reinterpret_cast<unsigned short*>(sAf + 8 * 128);  // [TABW] record bit -> j | k << 8
+    float* sS = reinterpret_cast<float*>(sBit + TABW);   // [8] per-head scales
+    for (int i = tid; i < 32 * TROW / 16; i += blockDim.x) reinterpret_cast<u32x4*>(sA)[i] = (u32x4){0u, 0u, 0u, 0u};
+    for (int i = tid; i < TABW; i += blockDim.x) sBit[i] = 0xFFFFu;
+    const float* qp = a.q + pg * g * 128;
+    for (int e = tid; e < 128 * 8; e += blockDim.x) {
+      const int r = e >> 3, hh = e & 7;
+      sqT[e] = hh < g ? qp[hh * 128 + r] : 0.0f;
+    }
+    constexpr int PARTS = W / 2, RPP = 128 / PARTS;  // parts of the rows of U_K, rows per part
+    const int j = tid & 127, part = tid >> 7;
+    const float* u = reinterpret_cast<const float*>(kst + OFF_U32);
+    __syncthreads();
+    if (tid < 128) {
+      const unsigned b = hk->bits[tid], o = hk->off[tid];
+      for (unsigned k = 0; k < b; ++k) sBit[o + k] = (unsigned short)(tid | (k << 8));
+    }
+    float acc[8];
+#pragma unroll
+    for (int hh = 0; hh < 8; ++hh) acc[hh] = 0.0f;
+#pragma unroll
+    for (int k0 = 0; k0 < RPP; k0 += 16) {
+      float ur[16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) ur[k] = u[(part + PARTS * (k0 + k)) * 128 + j];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const f32x4* q4 = reinterpret_cast<const f32x4*>(sqT + (part + PARTS * (k0 + k)) * 8);
+        const f32x4 q0 = q4[0], q1 = q4[1];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[e] = __builtin_fmaf(ur[k], q0[e], acc[e]);
+          acc[4 + e] = __builtin_fmaf(ur[k], q1[e], acc[4 + e]);
+        }
+      }
+    }
+#pragma unroll
+    for (int hh = 0; hh < 8; ++hh) red[(part * 8 + hh) * 128 + j] = acc[hh];
+    __syncthreads();
+    for (int e = tid; e < 8 * 128; e += 64 * W) {
+      const int hh = e >> 7, c = e & 127;
+      float v = 0.0f;
+      if (hh < g && hk->bits[c] > 0) {
+        float sum = 0.0f;
+        for (int pt = 0; pt < PARTS; ++pt) sum += red[(pt * 8 + hh) * 128 + c];
+        v = sum * hk->step32[c] * a.scale * LOG2E;
+      }
+      sAf[hh * 128 + c] = v;
+    }
+    __syncthreads();
+    if (tid < 8) {
+      // the largest weight of head tid is at most max_j |a_j| 2^(b_j - 1): scale it to at most 2^20
+      float M = 0.0f;
+      for (int c = 0; c < 128; ++c) {
+        const unsigned b = hk->bits[c];
+        if (b) M = fmaxf(M, fabsf(sAf[tid * 128 + c]) * (float)(1u << (b - 1)));
+      }
+      int ex = 0;
+      frexpf(M, &ex);
+      const float S = M > 0.0f ? ldexpf(1.0f, 20 - ex) : 1.0f;
+      sS[tid] = S;
+      sInvS[tid] = 1.0f / S;
+    }
+    if (tid < ATT_MAX_VCOLS) {
+      const AttVCol* vc = reinterpret_cast<const AttVCol*>(vst + OFF_ATTV);
+      u32x2 e = (u32x2){0u, 0u};
+      if (tid < ncols) {
+        // record byte k of lane half hh sits in row k - 4 R2v hh + 4 R2M hh of the value rows
+        const unsigned row = vc[tid].row, hh = row >= 4u * (unsigned)R2v ? 1u : 0u;
+        e = (u32x2){(row - 4u * (unsigned)R2v * hh + 4u * R2M * hh) * 8u + hh * (unsigned)VPAD, vc[tid].mask2};
+      }
+      sVc[tid] = e;
+    }
+    __syncthreads();
+    // int8 parts of round(S_h a_j 2^(k - (c & 3))): rows 8p + h
+    for (int e = tid; e < 8 * TABW; e += blockDim.x) {
+      const int hh = e / TABW, c = e - hh * TABW;
+      const unsigned bj = sBit[c];
+      if (hh < g && bj != 0xFFFFu && (unsigned)c < Bk) {
+        const int jj = bj & 255, k = bj >> 8;
+        const float w = sAf[hh * 128 + jj] * ldexpf(sS[hh], k - (c & 3));
+        const int A = (int)rintf(w);
+        const int a2 = ((A + 64) & 127) - 64;
+        const int r1 = (A - a2) >> 7;
+        const int a1 = ((r1 + 64) & 127) - 64;
+        const int a0 = (r1 - a1) >> 7;
+        const unsigned o = at2_tab_off((unsigned)c, (unsigned)R2k, (unsigned)R2M);
+        sA[hh * TROW + o] = (signed char)a0;
+        sA[(8 + hh) * TROW + o] = (signed char)a1;
+        sA[(16 + hh) * TROW + o] = (signed char)a2;
+      }
+    }
+    __syncthreads();
+  }
+
+  // wave regions: two staging buffers per stream, value rows, P, alpha, maxima
+  unsigned* sStage = sReg0 + wave * WREG;                                 // [stage][K, V][SWORDS]
+  unsigned* sV = sStage + 4 * SWORDS;                                     // value rows
+  _Float16* sP = reinterpret_cast<_Float16*>(sV + VWORDS);                // P [4 octets][16 heads][8] (+ pad)
+  float* sAl = reinterpret_cast<float*>(sP + 4 * AT2_PST);               // alpha per head
+  float* sM = sAl + 16;                                                    // running max per head
+  for (int i = lane; i < 4 * AT2_PST / 2; i += 64) reinterpret_cast<unsigned*>(sP)[i] = 0u;
+  if (lane < 16) {
+    sM[lane] = -INFINITY;
+    sAl[lane] = 1.0f;
+  }
+  float l_run[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  f32x4 acc_v[NT];
+#pragma unroll
+  for (int T = 0; T < NT; ++T) acc_v[T] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  float invS[4];
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) invS[jj] = sInvS[4 * h + jj];
+  const long long PkL = packed_len((long long)Bk, n), PvL = packed_len((long long)Bv, n);
+  const unsigned char* gk = a.k_packed + pg * a.packed_stride;
+  const unsigned char* gv = a.v_packed + pg * a.packed_stride;
+  const int e4 = t32 & 3;
+  const unsigned pos = (unsigned)at2_pos(t32);
+  // the wave's blocks: tok0 = t_begin + 32 (wave + W k); the records of the
+  // next block are requested (straight to LDS) before the current one is
+  // processed, so each wave keeps one block in flight behind the one it works on
+  const long long stride = (long long)nwav * AT2_BT;
+  long long tok0 = t_begin + (long long)wave * AT2_BT;
+  unsigned offk[2] = {0u, 0u}, offv[2] = {0u, 0u};
+  __builtin_amdgcn_s_waitcnt(0xc07f);
+  __builtin_amdgcn_wave_barrier();
+  if (tok0 < t_end) {
+    offk[0] = at2_stage<NCH>(gk, tok0 / AT2_BT, Bk, PkL, sStage, lane);
+    offv[0] = at2_stage<NCH>(gv, tok0 / AT2_BT, Bv, PvL, sStage + SWORDS, lane);
+  }
+  int stg = 0;
+  for (; tok0 < t_end; tok0 += stride, stg ^= 1) {
+    const bool has_next = tok0 + stride < t_end;
+    if (has_next) {
+      offk[stg ^ 1] = at2_stage<NCH>(gk, (tok0 + stride) / AT2_BT, Bk, PkL, sStage + (stg ^ 1) * 2 * SWORDS, lane);
+      offv[stg ^ 1] = at2_stage<NCH>(gv, (tok0 + stride) / AT2_BT, Bv, PvL, sStage + (stg ^ 1) * 2 * SWORDS + SWORDS,
+                                     lane);
+      // the current block's 2 NCH loads are done once at most the next block's 2 NCH remain
+      __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * NCH));  // vmcnt(2 NCH)
+    } else {
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    }
+    __builtin_amdgcn_wave_barrier();
+    const bool tok_ok = tok0 + t32 < t_end;
+    unsigned rk[R2M], rv[R2M];
+    const unsigned* bk = sStage + stg * 2 * SWORDS;
+    at2_read<R2M>(rv, bk + SWORDS, offv[stg], Bv, R2v, t32, h);
+    at2_read<R2M>(rk, bk, offk[stg], Bk, R2k, t32, h);
+    // ---- value records -> LDS rows [record byte][token quad] (byte transpose per lane quad)
+#pragma unroll
+    for (int i = 0; i < R2M; ++i) {
+      const unsigned y = quad_transpose_bytes(rv[i], e4);
+      const int row = 4 * (i + h * R2M) + e4;
+      sV[row * 8 + (h ? VPAD : 0) + (t32 >> 2)] = y;
+    }
+    // ---- scores: int8 MFMAs, A = weights (rows 8p + H), B = the record bits
+    i32x16 acc;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[e] = 0;
+    {
+      unsigned ab = lds_offset(reinterpret_cast<unsigned char*>(sA) + t32 * TROW + h * R2M * 32);
+      asm volatile("" : "+v"(ab));
+      const lds_u8* aL = lds_ptr(ab);
+      // (words past a half record are 0 and meet zero weights: no branch on R2k)
+#pragma unroll
+      for (int i = 0; i < R2M; ++i) {
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          const u32x4 av = LDS_AT(u32x4, aL + 32 * i + 16 * kk);
+          acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4, av),
+                                                      __builtin_bit_cast(i32x4, at2_bits(rk[i], kk)), acc, 0, 0, 0);
+        }
+      }
+    }
+    float sc[4];
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int H = 4 * h + jj;
+      const float s = __builtin_fmaf((float)((acc[jj] << 7) + acc[4 + jj]), 128.0f, (float)acc[8 + jj]);
+      sc[jj] = (tok_ok && H < g) ? s * invS[jj] : -INFINITY;
+    }
+    // ---- online softmax; P (fp16) -> sP[head][pos], alpha -> sAl
+    {
+      const f32x4 mold = *reinterpret_cast<const f32x4*>(sM + 4 * h);
+      bool slow = false;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+        if (4 * h + jj < g) slow |= !(sc[jj] <= mold[jj] + 8.0f);
+      if (!__any(slow)) {
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int H = 4 * h + jj;
+          const float pv = H < g ? __builtin_amdgcn_exp2f(sc[jj] - mold[jj]) : 0.0f;
+          const _Float16 ph = (_Float16)pv;
+          l_run[jj] += (float)ph;
+          sP[(pos >> 3) * AT2_PST + H * 8 + (pos & 7)] = ph;
+        }
+        if (t32 == 0) *reinterpret_cast<f32x4*>(sAl + 4 * h) = (f32x4){1.0f, 1.0f, 1.0f, 1.0f};
+      } else {
+        f32x4 mnw, al;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int H = 4 * h + jj;
+          const float mx = half_max(sc[jj]);
+          const float mnew = fmaxf(mold[jj], mx);
+          const float alpha = (mnew == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(mold[jj] - mnew);
+          const float pv = (mnew == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(sc[jj] - mnew);
+          const _Float16 ph = (_Float16)pv;
+          l_run[jj] = l_run[jj] * alpha + (float)ph;
+          mnw[jj] = mnew;
+          al[jj] = alpha;
+          sP[(pos >> 3) * AT2_PST + H * 8 + (pos & 7)] = ph;
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // every lane has read the old maxima
+        __builtin_amdgcn_wave_barrier();
+        if (t32 == 0) {
+          *reinterpret_cast<f32x4*>(sM + 4 * h) = mnw;
+          *reinterpret_cast<f32x4*>(sAl + 4 * h) = al;
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // the wave's value rows and P are in LDS
+    __builtin_amdgcn_wave_barrier();
+    // ---- rescale and accumulate P x V: heads 4 g4 + r, columns 16 T + c16
+    {
+      const f32x4 al = *reinterpret_cast<const f32x4*>(sAl + 4 * g4);
+      if (!__all(al[0] == 1.0f && al[1] == 1.0f && al[2] == 1.0f && al[3] == 1.0f)) {
+#pragma unroll
+        for (int T = 0; T < NT; ++T)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc_v[T][r] *= al[r];
+      }
+      const f16x8 pa = *reinterpret_cast<const f16x8*>(sP + g4 * AT2_PST + c16 * 8);  // 16 lanes: 64 banks
+      // (columns past the state's have a zero mask: no branch on the tile count)
+#pragma unroll
+      for (int T = 0; T < NT; ++T) {
+        const u32x2 cm = sVc[16 * T + c16];
+        const u32x2 vv = *reinterpret_cast<const u32x2*>(sV + cm[0] + 2 * g4);
+        const u32x4 vb = (u32x4){vv[0] & cm[1], (vv[0] >> 8) & cm[1], vv[1] & cm[1], (vv[1] >> 8) & cm[1]};
+        acc_v[T] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, __builtin_bit_cast(f16x8, vb), acc_v[T], 0, 0, 0);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    __builtin_amdgcn_wave_barrier();
+  }
+  // ---- l over the half's tokens; the maxima out of LDS before it is reused
+  float mfin[4];
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) {
+    l_run[jj] = half_sum(l_run[jj]);
+    mfin[jj] = sM[4 * h + jj];
+  }
+  // ---- merge the waves, four heads at a time: scratch [wave][4][CST]
+  constexpr int CST = 16 * NT + 4;
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(sReg0);
+  float* part = reinterpret_cast<float*>(a.ws) + (p * a.n_splits + sp) * att_part_stride(g);
+  const AttVCol* vcg = reinterpret_cast<const AttVCol*>(vst + OFF_ATTV);
+  const unsigned* vch = reinterpret_cast<const unsigned*>(vst + OFF_ATTVCH);
+  for (int c4 = 0; c4 * 4 < g; ++c4) {
+    float* mine = red + wave * 4 * CST;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int H = 4 * h + jj;
+      if (t32 == 0 && (H >> 2) == c4) {
+        mine[(H & 3) * CST + 16 * NT] = mfin[jj];
+        mine[(H & 3) * CST + 16 * NT + 1] = l_run[jj];
+      }
+    }
+    if (g4 == c4) {
+#pragma unroll
+      for (int T = 0; T < NT; ++T)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mine[r * CST + 16 * T + c16] = acc_v[T][r];
+    }
+    __syncthreads();
+    const int nh = g - 4 * c4 < 4 ? g - 4 * c4 : 4;
+    for (int e = tid; e < nh * 128; e += blockDim.x) {
+      const int hh = e >> 7, jj = e & 127;
+      const unsigned cc = vch[jj];
+      const int c0 = (int)(cc & 0xFFFFu), nc = (int)(cc >> 16);
+      float M = -INFINITY;
+      for (int w = 0; w < nwav; ++w) M = fmaxf(M, red[(w * 4 + hh) * CST + 16 * NT]);
+      float A = 0.0f, Ls = 0.0f;
+      for (int w = 0; w < nwav; ++w) {
+        const float* rw = red + (w * 4 + hh) * CST;
+        const float mw = rw[16 * NT];
+        const float f = (mw == -INFINITY) ? 0.0f : exp2f(mw - M);
+        float v = 0.0f;
+        for (int k = 0; k < nc; ++k) v += vcg[c0 + k].fac * rw[c0 + k];
+        A += f * v;
+        Ls += f * rw[16 * NT + 1];
+      }
+      float* ph = part + (4 * c4 + hh) * ATT_PART_FLOATS;
+      ph[jj] = A;
+      if (jj == 0) { ph[128] = M; ph[129] = Ls; }
+    }
+    if (4 * (c4 + 1) < g) __syncthreads();
+  }
+}
+
 // Partials area of stc_attend_compressed_batched_noalloc: a file-scope device
 // array, one copy on every device the library runs on, held until the process
 // ends. Host code uses the address hipGetSymbolAddress gives on the current
@@ -2205,6 +2684,13 @@ int launch_attend(const AttendLaunch& L, void* stream) {
     if (hipFuncSetAttribute((const void*)k_att_combine, hipFuncAttributeMaxDynamicSharedMemorySize, (int)CMB_LDS) !=
         hipSuccess)
       return 1;
+    if (hipFuncSetAttribute((const void*)k_att2<4, 10, 1, 16>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)at2_lds_bytes(4, 10, 1, 16)) != hipSuccess ||
+        hipFuncSetAttribute((const void*)k_att2<4, 10, 2, 8>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)at2_lds_bytes(4, 10, 2, 8)) != hipSuccess ||
+        hipFuncSetAttribute((const void*)k_att2<8, 12, 3, 8>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)at2_lds_bytes(8, 12, 3, 8)) != hipSuccess)
+      return 1;
     g_att_attr_done = true;
   }
   AttK a;
@@ -2248,8 +2734,17 @@ int launch_attend(const AttendLaunch& L, void* stream) {
     a.n_splits = att_n_splits(np, L.n_tokens);
     const size_t att_lds = fixed + (size_t)waves * a.region_words * 4;
     const dim3 grid((unsigned)a.n_splits, (unsigned)np);
-    const int var = sketch ? (L.rht ? 0 : (L.max_bits <= 512 ? 1 : 2)) : (L.rht ? 3 : (L.max_bits <= 512 ? 4 : 5));
-    hipLaunchKernelGGL(kAttKernels[var][L.rec && !L.rht ? 1 : 0], grid, dim3(64 * waves), att_lds, s, a);
+    if (!sketch && !L.rht && L.group <= 8 && L.max_bits <= 512) {
+      if (L.max_bits <= 256 && L.att_chunks <= 1)
+        hipLaunchKernelGGL((k_att2<4, 10, 1, 16>), grid, dim3(64 * 16), at2_lds_bytes(4, 10, 1, 16), s, a);
+      else if (L.max_bits <= 256)
+        hipLaunchKernelGGL((k_att2<4, 10, 2, 8>), grid, dim3(64 * 8), at2_lds_bytes(4, 10, 2, 8), s, a);
+      else
+        hipLaunchKernelGGL((k_att2<8, 12, 3, 8>), grid, dim3(64 * 8), at2_lds_bytes(8, 12, 3, 8), s, a);
+    } else {
+      const int var = sketch ? (L.rht ? 0 : (L.max_bits <= 512 ? 1 : 2)) : (L.rht ? 3 : (L.max_bits <= 512 ? 4 : 5));
+      hipLaunchKernelGGL(kAttKernels[var][L.rec && !L.rht ? 1 : 0], grid, dim3(64 * waves), att_lds, s, a);
+    }
     // the splits' partials -> out, once every split has written its own
     hipLaunchKernelGGL(k_att_combine, dim3((unsigned)np, (unsigned)L.group), dim3(CMB_THREADS), CMB_LDS, s, a);
   }
