@@ -79,14 +79,24 @@ KERNEL_OF_OP = {"encode": "k_encode_eigen<bf16>", "decode": "k_decode_eigen<bf16
 PROFILE_NAME = {"k_encode_eigen<bf16>": ("void stc::k_encode_eigen<0, true>(stc::EncK)",
                                          "void stc::k_encode_eigen<0, false>(stc::EncK)"),
                 "k_decode_eigen<bf16>": ("void stc::k_decode_eigen<0, 8>(stc::DecK)",),
-                "k_att2": ("void stc::k_att2<4, 10, 1, 16>(stc::AttK)", "void stc::k_att2<4, 10, 2, 8>(stc::AttK)",
-                           "void stc::k_att2<8, 12, 3, 8>(stc::AttK)"),
+                "k_att2": ("void stc::k_att2<*",),  # (every instance; a trailing * matches a prefix)
                 "k_att_main": ("void stc::k_att_main<8, false, false, true>(stc::AttK)",
                                "void stc::k_att_main<8, false, false, false>(stc::AttK)"),
                 "k_rht_encode": ("void stc::k_rht_encode<false>(stc::RhtK)",),
                 "k_rht_decode": ("stc::k_rht_decode(stc::RhtK)",)}
 KERNEL_SOURCE = os.path.join(ROOT, "spectral_transform_codec_amd", "csrc", "stc_kernels.hip")
 PROFILES = os.path.join(ROOT, "profiles")
+
+
+def _present(pnames, names):
+    """The profiled kernel names among `names` that the patterns pnames cover."""
+    out = []
+    for pn in pnames:
+        if pn.endswith("*"):
+            out += sorted(n for n in names if n.startswith(pn[:-1]))
+        elif pn in names:
+            out.append(pn)
+    return out
 
 
 def kernel_of(op_name):
@@ -732,8 +742,9 @@ def summarize(args):
                               "qwen_batch": (3584 * 32768, 1792 * 32768)}.get(args.workload,
                                                                             (16 * 32768, 8 * 32768))
         blocks = {"k_att_main": att_tok // 32, "k_att2": att_tok // 32}
-        for kname, pnames in PROFILE_NAME.items():
-            if not any(pn in per for pn in pnames):
+        for kname, pats in PROFILE_NAME.items():
+            pnames = _present(pats, per)
+            if not pnames:
                 continue
             cs = collections.defaultdict(list)  # dispatches of every variant
             for pn in pnames:
@@ -775,7 +786,7 @@ def summarize(args):
         return
     fetch_dir, write_dir = args.summarize
     kernel = args.kernel
-    pnames = PROFILE_NAME.get(kernel, (kernel,))
+    pats = PROFILE_NAME.get(kernel, (kernel,))
 
     def per_kernel(d, counter):
         vals = collections.defaultdict(lambda: collections.defaultdict(float))
@@ -792,6 +803,7 @@ def summarize(args):
     f_copy = max(fetch[copy_name]) * 1024.0
     w_copy = max(write[copy_name]) * 1024.0
     f_scale, w_scale = copy_bytes / f_copy, copy_bytes / w_copy
+    pnames = _present(pats, fetch)
     fk = [v for pn in pnames for v in fetch.get(pn, [])]  # every variant's launches
     wk = [v for pn in pnames for v in write.get(pn, [])]
     pname = " + ".join(pn for pn in pnames if pn in fetch)

@@ -1054,6 +1054,28 @@ static int attend_chunks(const stc_head_info* infos, int64_t n) {
   return c;
 }
 
+// Value columns of the attention kernels: the pieces of the kept codes cut at
+// the record's byte boundaries (the largest count over the states).
+static int attend_vcols(const stc_head_info* infos, int64_t n) {
+  int most = 0;
+  for (int64_t i = 0; i < n; ++i) {
+    int off = 0, nc = 0;
+    for (int j = 0; j < infos[i].d && j < STC_D; ++j) {
+      const int b = infos[i].bits[j];
+      if (b > 0) nc += (off + b - 1) / 8 - off / 8 + 1;
+      off += b;
+    }
+    most = std::max(most, nc);
+  }
+  return most;
+}
+
+static bool records_256(const stc_head_info* infos, int64_t n) {
+  for (int64_t i = 0; i < n; ++i)
+    if (infos[i].total_bits != 256) return false;
+  return n > 0;
+}
+
 // The eigen attention with a given partials area (the caller's workspace, or
 // the library's static scratch for the entry point that allocates nothing).
 static stc_status attend_eigen(const char* who, const void* states_dev, int64_t n_states, const int32_t* k_map,
@@ -1090,6 +1112,8 @@ static stc_status attend_eigen(const char* who, const void* states_dev, int64_t 
                  group, q_dev, out_dev, scale, static_cast<unsigned char*>(ws_dev), mb};
   a.rec = records_word_pow2(infos, n_states);
   a.att_chunks = attend_chunks(infos, n_states);
+  a.max_vcols = attend_vcols(infos, n_states);
+  a.rec256 = records_256(infos, n_states);
   if (launch_attend(a, stream)) return fail(STC_EDEVICE, "attend launch: %s", hipGetErrorString(hipGetLastError()));
   return ok();
 }
@@ -1228,6 +1252,9 @@ stc_status stc_attend_compressed(const stc_head_info* k_info, const void* k_stat
                  static_cast<const unsigned char*>(v_packed_dev), group, q_dev, out_dev, scale,
                  static_cast<unsigned char*>(ws_dev), std::max(mbk, mbv)};
   a.rec = records_word_pow2(k_info, 1) && records_word_pow2(v_info, 1);
+  a.att_chunks = std::max(attend_chunks(k_info, 1), attend_chunks(v_info, 1));
+  a.max_vcols = std::max(attend_vcols(k_info, 1), attend_vcols(v_info, 1));
+  a.rec256 = records_256(k_info, 1) && records_256(v_info, 1);
   if (launch_attend(a, stream)) return fail(STC_EDEVICE, "attend launch: %s", hipGetErrorString(hipGetLastError()));
   return ok();
 }

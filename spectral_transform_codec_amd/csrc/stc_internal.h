@@ -116,11 +116,25 @@ inline size_t packed_bytes(int64_t total_bits, int64_t n) {
 // shape; shared by the workspace-size query and the launcher.
 constexpr int ATT_TILE = 256;
 inline int64_t att_split_tokens(int64_t n_pairs, int64_t n_tokens) {
-  // about one workgroup per CU in total; a pair has at most that many splits
-  const int64_t target = 256;
-  int64_t tiles = (n_tokens + ATT_TILE - 1) / ATT_TILE;
-  int64_t per = (n_pairs * tiles + target - 1) / target;
-  if (per < 1) per = 1;
+  // at least one round of 768 workgroups (three per CU); among up to twice
+  // the fewest splits per pair, the count that fills the last round best; a
+  // pair has at most one split per tile
+  const int64_t round = 768;
+  const int64_t tiles = (n_tokens + ATT_TILE - 1) / ATT_TILE;
+  int64_t s0 = (round + n_pairs - 1) / n_pairs;
+  if (s0 > tiles) s0 = tiles;
+  if (s0 < 1) s0 = 1;
+  int64_t best = s0;
+  double best_fill = 0.0;
+  for (int64_t s = s0; s <= 2 * s0 && s <= tiles; ++s) {
+    const int64_t wg = n_pairs * s;
+    const double fill = (double)wg / (double)(((wg + round - 1) / round) * round);
+    if (fill > best_fill + 1e-9) {
+      best_fill = fill;
+      best = s;
+    }
+  }
+  const int64_t per = (tiles + best - 1) / best;
   return per * ATT_TILE;
 }
 inline int64_t att_n_splits(int64_t n_pairs, int64_t n_tokens) {
@@ -191,6 +205,8 @@ struct AttendLaunch {
   bool rec = false;  // every record is 0 or 32 * 2^s bits: one word-aligned LDS slot per record
   int att_chunks = 3;  // 1 KiB loads that cover one 32-token block of any stream (its records may
                        // start 4, 8 or 12 bytes past a 16-byte boundary)
+  int max_vcols = 256;  // value columns of the states at most (code fragments cut at record bytes)
+  bool rec256 = false;  // every record is 256 bits
 };
 
 int launch_gram(const void* x, int dtype, int64_t ld, int64_t n_calib, double* gram, void* stream);

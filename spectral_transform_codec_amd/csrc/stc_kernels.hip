@@ -2166,29 +2166,41 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_att_main(AttK a) {
 // Scores. A K record is a string of B bits and the score is linear in them:
 // record bit c, bit k of channel j's code, carries a_j 2^k with
 // a_j = (U_K^T q)_j step_j scale log2(e). Each lane holds half of its token's
-// record, realigned to bit 0 by funnel shifts, and turns each record word w
-// into eight int8 operand words with one AND each: w & (0x01010101 << r) and
+// record, realigned to bit 0, and turns each record word w into eight int8
+// operand words with one AND each: w & (0x01010101 << r) and
 // (w >> 4) & (0x01010101 << r), r = 0..3, whose byte q is bit 8q + r (or
 // 8q + 4 + r) of w times 2^r. The weights a_j 2^k 2^-r, scaled by a power of
 // two per query head, are split into three int8 parts that sit in rows
-// 8p + H (p = 0..2) of the 32x32x32 int8 MFMA, so the accumulators are exact
-// integers and each lane adds its heads' three parts afterwards.
+// 4H + p (p = 0..2) of the 32x32x32 int8 MFMA, so the accumulators are exact
+// integers and a lane finds the three parts of heads H = 2i + h (h its half
+// of the wave) in accumulators 4i .. 4i + 2.
 // Values. Each lane quad (four consecutive tokens) transposes its V record
-// words by byte, so that one word holds one record byte of the four tokens;
-// those words go to LDS rows [record byte][token quad]. A value column is the
-// fragment of one channel's code that lies in one record byte: lane (column,
-// token octet) reads two words of the column's row and masks the fragment of
-// tokens (0, 2) and, shifted down by 8, of tokens (1, 3) in place. Each
-// 16-bit half is then an fp16 subnormal fragment * 2^(shift - 24), exact, and
-// the words are the B operand of the fp16 16x16x32 MFMA against P (the
-// softmax weights stored in the same token order). When the waves merge, the
-// columns of each channel are added with their scales 2^(24 - shift + offset
-// of the fragment in the code), which gives the split partials in code units.
+// words by byte and splits each result into the bytes of tokens (0, 2) and of
+// tokens (1, 3), each byte in the low half of a 16-bit field; both words go to
+// LDS rows [record byte][token quad]. A value column is the fragment of one
+// channel's code that lies in one record byte: lane (column, token octet)
+// reads the four words of two quads of the column's row and masks the
+// fragment in place. Each 16-bit half is then an fp16 subnormal fragment
+// * 2^(shift - 24), exact, and the words are the B operand of the fp16
+// 16x16x32 MFMA against P (the softmax weights stored in the same token
+// order). When the waves merge, the columns of each channel are added with
+// their scales 2^(24 - shift + offset of the fragment in the code), which
+// gives the split partials in code units.
 // ======================================================================
-constexpr int AT2_WAVES = 16;
-constexpr int AT2_THREADS = 64 * AT2_WAVES;
 constexpr int AT2_PST = 136;  // fp16 per token octet of P ([octet][16 heads][8] + 8 pad: octets 4 banks apart)
 constexpr int AT2_BT = 32;    // tokens per wave block
+// Word offset of value row r ([quad][tokens 0,2 | 1,3], 16 words). For records
+// of at most 256 bits, 24 r + 12 (r >> 2) + 8 (r >> 3): the 16-byte reads of
+// any 16 consecutive rows fall in 16 different 4-bank groups of the 64, and
+// the 8-byte writes of four rows by 16 lanes in 32 different banks (LDS
+// writes go 32 banks at a time); longer records: 16 r, to fit the LDS.
+__host__ __device__ constexpr unsigned at2_vrow(int R2M, unsigned r) {
+  return R2M <= 4 ? 24u * r + 12u * (r >> 2) + 8u * (r >> 3) : 16u * r;
+}
+// stages of the record ring of one wave (blocks in flight: stages - 1)
+__host__ __device__ constexpr int at2_nst(int NCH) { return NCH == 1 ? 3 : 2; }
+// weight-table rows: three per head of the instance, then one of zeros
+__host__ __device__ constexpr int at2_trows(bool G4) { return G4 ? 13 : 25; }
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x16 __attribute__((ext_vector_type(16)));
 
@@ -2209,46 +2221,40 @@ __device__ __forceinline__ u32x4 at2_bits(unsigned w, int kk) {
   return (u32x4){x & 0x01010101u, x & 0x02020202u, x & 0x04040404u, x & 0x08080808u};
 }
 
-// A lane's half record: R2 words from record bit 32 R2 h of token t, realigned.
-// Streams of records of B = 256 s bits (s >= 1) are word-aligned and read with
-// 16-byte loads, B = 128 with 8-byte loads; other lengths read R2 + 1 words and
-// funnel-shift them. Words past the stream end read as 0.
+// Record byte 4i + e of the four tokens of a lane quad (e = lane & 3, x the
+// lane's record word i), split by token parity: .x = bytes of tokens 0 and 2
+// in bits 0-7 and 16-23, .y = those of tokens 1 and 3 (two DPP moves and
+// three byte permutes).
+__device__ __forceinline__ u32x2 at2_quad_split(unsigned x, unsigned sel1, unsigned sel_e, unsigned sel_o) {
+  const unsigned p1 = (unsigned)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, false);  // lane e^1
+  const unsigned y = __builtin_amdgcn_perm(p1, x, sel1);
+  const unsigned p2 = (unsigned)__builtin_amdgcn_mov_dpp((int)y, 0x4E, 0xF, 0xF, false);  // lane e^2
+  return (u32x2){__builtin_amdgcn_perm(p2, y, sel_e), __builtin_amdgcn_perm(p2, y, sel_o)};
+}
+
 // A lane's half record from a wave's staging buffer: R2 words from record bit
-// 32 R2 h of token t, the block's records starting at bit `off` of the buffer;
-// realigned to bit 0 with funnel shifts (16-byte reads when every start is
-// 16-byte aligned).
-template <int R2M>
+// 32 R2 h of token t, the block's records starting at bit `off` of the buffer,
+// realigned to bit 0. SWZ: records of 256 bits staged by at2_stage<.., true>
+// (16-byte chunk q of half h of token t at chunk t + 32 h + 64 q); otherwise
+// R2M + 1 words funnel-shifted. Words past the half record hold other bits,
+// which meet zero weights and columns that never read them.
+template <int R2M, bool SWZ>
 __device__ __forceinline__ void at2_read(unsigned (&r)[R2M], const unsigned* buf, unsigned off, unsigned B, int R2,
                                          int t, int h) {
+  if (SWZ) {
 #pragma unroll
-  for (int j = 0; j < R2M; ++j) r[j] = 0u;
-  if (B == 0) return;
-  if ((B & 255u) == 0u) {
-    // records of 256 s bits were staged by at2_stage in the order below:
-    // 16-byte chunk q of half h of token t at chunk t + 32 h + 64 q
-#pragma unroll
-    for (int j = 0; j < R2M; j += 4)
-      if (j < R2) {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(buf + 4 * (t + 32 * h + 64 * (j >> 2)));
-        r[j] = v[0]; r[j + 1] = v[1]; r[j + 2] = v[2]; r[j + 3] = v[3];
-      }
+    for (int j = 0; j < R2M; j += 4) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(buf + 4 * (t + 32 * h + 64 * (j >> 2)));
+      r[j] = v[0]; r[j + 1] = v[1]; r[j + 2] = v[2]; r[j + 3] = v[3];
+    }
     return;
   }
   const unsigned P = off + (unsigned)t * B + 32u * (unsigned)R2 * (unsigned)h;
   const unsigned* w = buf + (P >> 5);
-  if ((P & 127u) == 0u && (B & 127u) == 0u) {   // (uniform: off, B and R2 multiples of 128 bits, 4 words)
-#pragma unroll
-    for (int j = 0; j < R2M; j += 4)
-      if (j < R2) {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(w + j);
-        r[j] = v[0]; r[j + 1] = v[1]; r[j + 2] = v[2]; r[j + 3] = v[3];
-      }
-    return;
-  }
   const unsigned sh = P & 31u;
   unsigned x[R2M + 1];
 #pragma unroll
-  for (int j = 0; j <= R2M; ++j) x[j] = j <= R2 ? w[j] : 0u;
+  for (int j = 0; j <= R2M; ++j) x[j] = w[j];
 #pragma unroll
   for (int j = 0; j < R2M; ++j) r[j] = __builtin_amdgcn_alignbit(x[j + 1], x[j], sh);
 }
@@ -2257,21 +2263,20 @@ __device__ __forceinline__ void at2_read(unsigned (&r)[R2M], const unsigned* buf
 // into a wave's staging buffer: NCH loads of 16 bytes per lane straight to
 // LDS, from the 16-byte boundary at or below the block's first byte (returned
 // in bits, the offset of the records in the buffer). Lanes past the stream
-// end load its first 16 bytes instead, so every call issues NCH loads.
-template <int NCH>
+// end load its first 16 bytes instead, so every call issues NCH loads (a
+// stream of no bytes passes another valid address as `stream`).
+template <int NCH, bool SWZ>
 __device__ __forceinline__ unsigned at2_stage(const unsigned char* stream, long long blk, unsigned B, long long plen,
                                               unsigned* buf, int lane) {
   const long long start = blk * 4LL * (long long)B;
   const long long base = start & ~15LL;
-  // records of 256 s bits: slot lane of load c takes chunk 2 s t + s h + c of
-  // the block (t = lane & 31, h = lane >> 5), so that the 16-byte reads of
-  // 16 consecutive lanes cover 64 banks (in block order they would pair up)
-  const bool swz = (B & 255u) == 0u;
-  const long long s_ = (long long)(B >> 8);
-  const long long chunk = swz ? 2 * s_ * (lane & 31) + s_ * (lane >> 5) : (long long)lane;
+  // SWZ (B = 256): slot lane of load c takes chunk 2 t + h + c of the block
+  // (t = lane & 31, h = lane >> 5), so that the 16-byte reads of 16
+  // consecutive lanes cover 64 banks (in block order they would pair up)
+  const long long chunk = SWZ ? 2 * (lane & 31) + (lane >> 5) : (long long)lane;
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
-    long long byte = swz ? base + 16LL * (chunk + c) : base + 1024LL * c + 16LL * lane;
+    long long byte = SWZ ? base + 16LL * (chunk + c) : base + 1024LL * c + 16LL * lane;
     if (byte + 16 > plen) byte = 0;
     __builtin_amdgcn_global_load_lds(stream + byte, (__attribute__((address_space(3))) void*)(buf + 256 * c), 16, 0,
                                      0);
@@ -2279,35 +2284,42 @@ __device__ __forceinline__ unsigned at2_stage(const unsigned char* stream, long 
   return (unsigned)(start - base) * 8u;
 }
 
-// Dynamic LDS of k_att2<R2M, NT, NCH, W>: the score weights, the value column
-// table and the per-head scales, then the larger of the prologue scratch, the
-// W wave regions and the merge scratch.
-__host__ __device__ constexpr size_t at2_lds_bytes(int R2M, int NT, int NCH, int W) {
-  const size_t fixed = (size_t)32 * (64 * R2M + 16) + ATT_MAX_VCOLS * 8 + 8 * 4;
-  const size_t pro = (size_t)(128 * 8 + 8 * 8 * 128 + 8 * 128) * 4 + 2 * 64 * R2M + 8 * 4;
-  const size_t waves = (size_t)W * (4 * 256 * NCH + 64 * R2M + 32 + 4 * AT2_PST / 2 + 32) * 4;
+// Dynamic LDS of k_att2<R2M, NT, NCH, W, .., G4>: the score weights, the
+// value column table and the per-head scales, then the larger of the prologue
+// scratch, the W wave regions and the merge scratch.
+__host__ __device__ constexpr size_t at2_lds_bytes(int R2M, int NT, int NCH, int W, bool G4) {
+  const size_t fixed = (size_t)at2_trows(G4) * (64 * R2M + 16) + ATT_MAX_VCOLS * 8 + 8 * 4;
+  const size_t pro = (size_t)(128 * 8 + (W / 2) * 8 * 128 + 8 * 128) * 4 + 2 * 64 * R2M + 8 * 4;
+  const size_t vwords = (size_t)at2_vrow(R2M, 8 * R2M - 1) + 16;
+  const size_t waves = (size_t)W * (2 * at2_nst(NCH) * 256 * NCH + vwords + 4 * AT2_PST / 2 + 16) * 4;
   const size_t merge = (size_t)W * 4 * (16 * NT + 4) * 4;
   const size_t big = pro > waves ? (pro > merge ? pro : merge) : (waves > merge ? waves : merge);
   return fixed + big;
 }
 
 // R2M: record words per half record at most (records of at most 64 R2M bits);
-// NT: value tiles at most; NCH: 1 KiB loads per stream and block; W: waves.
-template <int R2M, int NT, int NCH, int W>
-__global__ void __launch_bounds__(64 * W, 1) k_att2(AttK a) {
+// NT: value tiles (columns <= 16 NT); NCH: 1 KiB loads per stream and block;
+// W: waves; SWZ: every record is 256 bits (R2M = 4, NCH = 1); G4: group <= 4
+// (a lane's heads are 2i + h for i < 2, otherwise i < 4).
+template <int R2M, int NT, int NCH, int W, bool SWZ, bool G4>
+__global__ void __launch_bounds__(64 * W, W == 4 ? 3 : 1) k_att2(AttK a) {
+  static_assert(!SWZ || (R2M == 4 && NCH == 1), "256-bit records: four words per half, one load per block");
   extern __shared__ __align__(16) unsigned char smem[];
+  constexpr int NHL = G4 ? 2 : 4;              // heads per lane
+  constexpr int NH = G4 ? 4 : 8;               // heads of the weight table
   constexpr int TABW = 64 * R2M;               // bytes of a score-weight row (record bits <= 64 R2M)
   constexpr int TROW = TABW + 16;              // row stride: rows 4 banks apart, so 16 lanes' reads hit 64 banks
-  constexpr int VROWS = 8 * R2M;               // record bytes
-  constexpr int VPAD = 32;                     // words between the two halves' rows
-  constexpr int VWORDS = VROWS * 8 + VPAD;
+  constexpr int TROWS = at2_trows(G4);         // rows 3H + p of head H, part p; then a row of zeros
+  constexpr int VWORDS = (int)at2_vrow(R2M, 8 * R2M - 1) + 16;  // value rows: 4 R2M record bytes per lane half
   constexpr int SWORDS = 256 * NCH;            // words of one staging buffer
-  constexpr int WREG = 4 * SWORDS + VWORDS + 4 * AT2_PST / 2 + 32;  // words per wave region
-  signed char* sA = reinterpret_cast<signed char*>(smem);            // [32][TROW]
-  u32x2* sVc = reinterpret_cast<u32x2*>(smem + 32 * TROW);           // [256] (row word offset, mask2)
+  constexpr int NST = at2_nst(NCH);            // ring stages (blocks in flight: NST - 1)
+  constexpr int WREG = 2 * NST * SWORDS + VWORDS + 4 * AT2_PST / 2 + 16;  // words per wave region
+  static_assert(3 * NH + 1 == TROWS, "weight-table rows");
+  static_assert(WREG % 4 == 0 && (TROWS * TROW) % 16 == 0, "16-byte aligned LDS regions");
+  signed char* sA = reinterpret_cast<signed char*>(smem);            // [TROWS][TROW]
+  u32x2* sVc = reinterpret_cast<u32x2*>(smem + TROWS * TROW);        // [256] (row word offset, mask2)
   float* sInvS = reinterpret_cast<float*>(sVc + ATT_MAX_VCOLS);     // [8]
   unsigned* sReg0 = reinterpret_cast<unsigned*>(sInvS + 8);         // wave regions / prologue scratch
-  const int nwav = W;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -2334,18 +2346,18 @@ __global__ void __launch_bounds__(64 * W, 1) k_att2(AttK a) {
   // ------------------------------------------------------------ prologue
   {
     float* sqT = reinterpret_cast<float*>(sReg0);        // q^T [128][8]
-    float* red = sqT + 128 * 8;                          // [8 parts][8 heads][128]
-    float* sAf = red + 8 * 8 * 128;                      // a [8][128]
+    constexpr int PARTS = W / 2, RPP = 128 / PARTS;  // parts of the rows of U_K, rows per part
+    float* red = sqT + 128 * 8;                          // [PARTS][8 heads][128]
+    float* sAf = red + PARTS * 8 * 128;                  // a [8][128]
     unsigned short* sBit = reinterpret_cast<unsigned short*>(sAf + 8 * 128);  // [TABW] record bit -> j | k << 8
     float* sS = reinterpret_cast<float*>(sBit + TABW);   // [8] per-head scales
-    for (int i = tid; i < 32 * TROW / 16; i += blockDim.x) reinterpret_cast<u32x4*>(sA)[i] = (u32x4){0u, 0u, 0u, 0u};
+    for (int i = tid; i < TROWS * TROW / 16; i += blockDim.x) reinterpret_cast<u32x4*>(sA)[i] = (u32x4){0u, 0u, 0u, 0u};
     for (int i = tid; i < TABW; i += blockDim.x) sBit[i] = 0xFFFFu;
     const float* qp = a.q + pg * g * 128;
     for (int e = tid; e < 128 * 8; e += blockDim.x) {
       const int r = e >> 3, hh = e & 7;
       sqT[e] = hh < g ? qp[hh * 128 + r] : 0.0f;
     }
-    constexpr int PARTS = W / 2, RPP = 128 / PARTS;  // parts of the rows of U_K, rows per part
     const int j = tid & 127, part = tid >> 7;
     const float* u = reinterpret_cast<const float*>(kst + OFF_U32);
     __syncthreads();
@@ -2403,15 +2415,15 @@ __global__ void __launch_bounds__(64 * W, 1) k_att2(AttK a) {
       const AttVCol* vc = reinterpret_cast<const AttVCol*>(vst + OFF_ATTV);
       u32x2 e = (u32x2){0u, 0u};
       if (tid < ncols) {
-        // record byte k of lane half hh sits in row k - 4 R2v hh + 4 R2M hh of the value rows
+        // record byte k of lane half hh sits in value row k - 4 R2v hh + 4 R2M hh
         const unsigned row = vc[tid].row, hh = row >= 4u * (unsigned)R2v ? 1u : 0u;
-        e = (u32x2){(row - 4u * (unsigned)R2v * hh + 4u * R2M * hh) * 8u + hh * (unsigned)VPAD, vc[tid].mask2};
+        e = (u32x2){at2_vrow(R2M, row - 4u * (unsigned)R2v * hh + 4u * R2M * hh), vc[tid].mask2};
       }
       sVc[tid] = e;
     }
     __syncthreads();
-    // int8 parts of round(S_h a_j 2^(k - (c & 3))): rows 8p + h
-    for (int e = tid; e < 8 * TABW; e += blockDim.x) {
+    // int8 parts of round(S_h a_j 2^(k - (c & 3))): rows 3h + p
+    for (int e = tid; e < NH * TABW; e += blockDim.x) {
       const int hh = e / TABW, c = e - hh * TABW;
       const unsigned bj = sBit[c];
       if (hh < g && bj != 0xFFFFu && (unsigned)c < Bk) {
@@ -2423,171 +2435,197 @@ __global__ void __launch_bounds__(64 * W, 1) k_att2(AttK a) {
         const int a1 = ((r1 + 64) & 127) - 64;
         const int a0 = (r1 - a1) >> 7;
         const unsigned o = at2_tab_off((unsigned)c, (unsigned)R2k, (unsigned)R2M);
-        sA[hh * TROW + o] = (signed char)a0;
-        sA[(8 + hh) * TROW + o] = (signed char)a1;
-        sA[(16 + hh) * TROW + o] = (signed char)a2;
+        sA[(3 * hh) * TROW + o] = (signed char)a0;
+        sA[(3 * hh + 1) * TROW + o] = (signed char)a1;
+        sA[(3 * hh + 2) * TROW + o] = (signed char)a2;
       }
     }
     __syncthreads();
   }
 
-  // wave regions: two staging buffers per stream, value rows, P, alpha, maxima
+  // wave regions: NST staging buffers per stream, value rows, P, alpha
   unsigned* sStage = sReg0 + wave * WREG;                                 // [stage][K, V][SWORDS]
-  unsigned* sV = sStage + 4 * SWORDS;                                     // value rows
+  unsigned* sV = sStage + 2 * NST * SWORDS;                               // value rows (at2_vrow)
   _Float16* sP = reinterpret_cast<_Float16*>(sV + VWORDS);                // P [4 octets][16 heads][8] (+ pad)
-  float* sAl = reinterpret_cast<float*>(sP + 4 * AT2_PST);               // alpha per head
-  float* sM = sAl + 16;                                                    // running max per head
+  float* sAl = reinterpret_cast<float*>(sP + 4 * AT2_PST);               // alpha per head [16]
   for (int i = lane; i < 4 * AT2_PST / 2; i += 64) reinterpret_cast<unsigned*>(sP)[i] = 0u;
-  if (lane < 16) {
-    sM[lane] = -INFINITY;
-    sAl[lane] = 1.0f;
+  if (lane < 16) sAl[lane] = 1.0f;
+  // per head of the lane (H = 2i + h): running max, its threshold of the
+  // fast path in unscaled score units, the scales, the running sum
+  float mold[NHL], thr[NHL], invS[NHL], Ssc[NHL], l_run[NHL];
+  bool hval[NHL];
+#pragma unroll
+  for (int i = 0; i < NHL; ++i) {
+    const int H = 2 * i + h;
+    invS[i] = sInvS[H];
+    Ssc[i] = 1.0f / invS[i];  // (a power of two)
+    mold[i] = -INFINITY;
+    thr[i] = -INFINITY;
+    l_run[i] = 0.0f;
+    hval[i] = H < g;
   }
-  float l_run[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   f32x4 acc_v[NT];
 #pragma unroll
   for (int T = 0; T < NT; ++T) acc_v[T] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  float invS[4];
+  // value columns of this lane: LDS address of the four words it reads and
+  // the fragment mask (columns past the state's have mask 0)
+  unsigned vaddr[NT], vmask[NT];
+  {
+    const unsigned vb0 = lds_offset(reinterpret_cast<unsigned char*>(sV));
 #pragma unroll
-  for (int jj = 0; jj < 4; ++jj) invS[jj] = sInvS[4 * h + jj];
+    for (int T = 0; T < NT; ++T) {
+      const u32x2 cm = sVc[16 * T + c16];
+      vaddr[T] = vb0 + 4u * (cm[0] + 4u * (unsigned)g4);
+      vmask[T] = cm[1];
+      asm volatile("" : "+v"(vaddr[T]), "+v"(vmask[T]));
+    }
+  }
   const long long PkL = packed_len((long long)Bk, n), PvL = packed_len((long long)Bv, n);
-  const unsigned char* gk = a.k_packed + pg * a.packed_stride;
-  const unsigned char* gv = a.v_packed + pg * a.packed_stride;
+  // (a stream of no bytes stages from its state instead, which is never read)
+  const unsigned char* gk = PkL > 0 ? a.k_packed + pg * a.packed_stride : kst;
+  const unsigned char* gv = PvL > 0 ? a.v_packed + pg * a.packed_stride : vst;
   const int e4 = t32 & 3;
+  const unsigned sel1 = (e4 & 1) ? 0x03070105u : 0x06020400u;
+  const unsigned sel_e = (e4 & 2) ? 0x0C020C06u : 0x0C040C00u;
+  const unsigned sel_o = (e4 & 2) ? 0x0C030C07u : 0x0C050C01u;
   const unsigned pos = (unsigned)at2_pos(t32);
-  // the wave's blocks: tok0 = t_begin + 32 (wave + W k); the records of the
-  // next block are requested (straight to LDS) before the current one is
-  // processed, so each wave keeps one block in flight behind the one it works on
-  const long long stride = (long long)nwav * AT2_BT;
+  bool resc = false;  // (uniform) a rescale of the value accumulators is pending
+  // the wave's blocks: tok0 = t_begin + 32 (wave + W k). The records of the
+  // next NST - 1 blocks are requested (straight to LDS) before the current
+  // one is processed; past the split's end the requests are of the stream's
+  // first 16 bytes (never read), so that every step issues 2 NCH loads
+  const long long stride = (long long)W * AT2_BT;
   long long tok0 = t_begin + (long long)wave * AT2_BT;
-  unsigned offk[2] = {0u, 0u}, offv[2] = {0u, 0u};
+  unsigned offk[NST], offv[NST];
   __builtin_amdgcn_s_waitcnt(0xc07f);
   __builtin_amdgcn_wave_barrier();
-  if (tok0 < t_end) {
-    offk[0] = at2_stage<NCH>(gk, tok0 / AT2_BT, Bk, PkL, sStage, lane);
-    offv[0] = at2_stage<NCH>(gv, tok0 / AT2_BT, Bv, PvL, sStage + SWORDS, lane);
+#pragma unroll
+  for (int st = 0; st < NST - 1; ++st) {
+    const long long tb = tok0 + st * stride;
+    const bool real = tb < t_end;
+    unsigned* buf = sStage + st * 2 * SWORDS;
+    offk[st] = at2_stage<NCH, SWZ>(gk, real ? tb / AT2_BT : 0, Bk, real ? PkL : 0, buf, lane);
+    offv[st] = at2_stage<NCH, SWZ>(gv, real ? tb / AT2_BT : 0, Bv, real ? PvL : 0, buf + SWORDS, lane);
   }
-  int stg = 0;
-  for (; tok0 < t_end; tok0 += stride, stg ^= 1) {
-    const bool has_next = tok0 + stride < t_end;
-    if (has_next) {
-      offk[stg ^ 1] = at2_stage<NCH>(gk, (tok0 + stride) / AT2_BT, Bk, PkL, sStage + (stg ^ 1) * 2 * SWORDS, lane);
-      offv[stg ^ 1] = at2_stage<NCH>(gv, (tok0 + stride) / AT2_BT, Bv, PvL, sStage + (stg ^ 1) * 2 * SWORDS + SWORDS,
-                                     lane);
-      // the current block's 2 NCH loads are done once at most the next block's 2 NCH remain
-      __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * NCH));  // vmcnt(2 NCH)
-    } else {
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  int cur = 0;  // ring stage of the current block
+  for (; tok0 < t_end; tok0 += stride) {
+    {
+      const long long tb = tok0 + (NST - 1) * stride;
+      const bool real = tb < t_end;
+      unsigned* buf = sStage + (cur == 0 ? NST - 1 : cur - 1) * 2 * SWORDS;
+      offk[NST - 1] = at2_stage<NCH, SWZ>(gk, real ? tb / AT2_BT : 0, Bk, real ? PkL : 0, buf, lane);
+      offv[NST - 1] = at2_stage<NCH, SWZ>(gv, real ? tb / AT2_BT : 0, Bv, real ? PvL : 0, buf + SWORDS, lane);
     }
+    // the current block's loads are done once at most the later blocks' remain
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * NCH * (NST - 1)));  // vmcnt(2 NCH (NST - 1))
     __builtin_amdgcn_wave_barrier();
     const bool tok_ok = tok0 + t32 < t_end;
     unsigned rk[R2M], rv[R2M];
-    const unsigned* bk = sStage + stg * 2 * SWORDS;
-    at2_read<R2M>(rv, bk + SWORDS, offv[stg], Bv, R2v, t32, h);
-    at2_read<R2M>(rk, bk, offk[stg], Bk, R2k, t32, h);
-    // ---- value records -> LDS rows [record byte][token quad] (byte transpose per lane quad)
+    const unsigned* bk = sStage + cur * 2 * SWORDS;
+    at2_read<R2M, SWZ>(rv, bk + SWORDS, offv[0], Bv, R2v, t32, h);
+    at2_read<R2M, SWZ>(rk, bk, offk[0], Bk, R2k, t32, h);
+#pragma unroll
+    for (int st = 0; st < NST - 1; ++st) {
+      offk[st] = offk[st + 1];
+      offv[st] = offv[st + 1];
+    }
+    cur = cur == NST - 1 ? 0 : cur + 1;
+    // ---- value records -> LDS rows [record byte][token quad][parity]
 #pragma unroll
     for (int i = 0; i < R2M; ++i) {
-      const unsigned y = quad_transpose_bytes(rv[i], e4);
-      const int row = 4 * (i + h * R2M) + e4;
-      sV[row * 8 + (h ? VPAD : 0) + (t32 >> 2)] = y;
+      const u32x2 y = at2_quad_split(rv[i], sel1, sel_e, sel_o);
+      const unsigned row = (unsigned)(4 * (i + h * R2M) + e4);
+      *reinterpret_cast<u32x2*>(sV + at2_vrow(R2M, row) + 2 * (t32 >> 2)) = y;
     }
-    // ---- scores: int8 MFMAs, A = weights (rows 8p + H), B = the record bits
+    // ---- scores: int8 MFMAs, A = weights (rows 4H + p), B = the record bits
     i32x16 acc;
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[e] = 0;
     {
-      unsigned ab = lds_offset(reinterpret_cast<unsigned char*>(sA) + t32 * TROW + h * R2M * 32);
+      // lane row t32 = 4H + p of the MFMA holds part p of head H: table row
+      // 3H + p, or the zero row for p = 3 and heads past the table
+      const int trow = ((t32 & 3) == 3 || (t32 >> 2) >= NH) ? 3 * NH : 3 * (t32 >> 2) + (t32 & 3);
+      unsigned ab = lds_offset(reinterpret_cast<unsigned char*>(sA) + trow * TROW + h * R2M * 32);
       asm volatile("" : "+v"(ab));
       const lds_u8* aL = lds_ptr(ab);
-      // (words past a half record are 0 and meet zero weights: no branch on R2k)
+      // (all of the block's weight reads are issued first, so that their
+      // latencies overlap; words past a half record meet zero weights)
+      u32x4 av[2 * R2M];
+#pragma unroll
+      for (int e = 0; e < 2 * R2M; ++e) av[e] = LDS_AT(u32x4, aL + 16 * e);
 #pragma unroll
       for (int i = 0; i < R2M; ++i) {
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          const u32x4 av = LDS_AT(u32x4, aL + 32 * i + 16 * kk);
-          acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4, av),
+        for (int kk = 0; kk < 2; ++kk)
+          acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4, av[2 * i + kk]),
                                                       __builtin_bit_cast(i32x4, at2_bits(rk[i], kk)), acc, 0, 0, 0);
-        }
       }
     }
-    float sc[4];
+    // unscaled scores of the lane's heads (-inf past the split)
+    float su[NHL];
+    bool slow = false;
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const int H = 4 * h + jj;
-      const float s = __builtin_fmaf((float)((acc[jj] << 7) + acc[4 + jj]), 128.0f, (float)acc[8 + jj]);
-      sc[jj] = (tok_ok && H < g) ? s * invS[jj] : -INFINITY;
+    for (int i = 0; i < NHL; ++i) {
+      const float s = __builtin_fmaf((float)((acc[4 * i] << 7) + acc[4 * i + 1]), 128.0f, (float)acc[4 * i + 2]);
+      su[i] = tok_ok ? s : -INFINITY;
+      slow |= hval[i] && !(su[i] <= thr[i]);
     }
-    // ---- online softmax; P (fp16) -> sP[head][pos], alpha -> sAl
-    {
-      const f32x4 mold = *reinterpret_cast<const f32x4*>(sM + 4 * h);
-      bool slow = false;
+    // ---- online softmax; P (fp16) -> sP[octet][head][8]
+    if (!__any(slow)) {
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj)
-        if (4 * h + jj < g) slow |= !(sc[jj] <= mold[jj] + 8.0f);
-      if (!__any(slow)) {
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const int H = 4 * h + jj;
-          const float pv = H < g ? __builtin_amdgcn_exp2f(sc[jj] - mold[jj]) : 0.0f;
-          const _Float16 ph = (_Float16)pv;
-          l_run[jj] += (float)ph;
-          sP[(pos >> 3) * AT2_PST + H * 8 + (pos & 7)] = ph;
-        }
-        if (t32 == 0) *reinterpret_cast<f32x4*>(sAl + 4 * h) = (f32x4){1.0f, 1.0f, 1.0f, 1.0f};
-      } else {
-        f32x4 mnw, al;
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const int H = 4 * h + jj;
-          const float mx = half_max(sc[jj]);
-          const float mnew = fmaxf(mold[jj], mx);
-          const float alpha = (mnew == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(mold[jj] - mnew);
-          const float pv = (mnew == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(sc[jj] - mnew);
-          const _Float16 ph = (_Float16)pv;
-          l_run[jj] = l_run[jj] * alpha + (float)ph;
-          mnw[jj] = mnew;
-          al[jj] = alpha;
-          sP[(pos >> 3) * AT2_PST + H * 8 + (pos & 7)] = ph;
-        }
-        __builtin_amdgcn_s_waitcnt(0xc07f);  // every lane has read the old maxima
-        __builtin_amdgcn_wave_barrier();
-        if (t32 == 0) {
-          *reinterpret_cast<f32x4*>(sM + 4 * h) = mnw;
-          *reinterpret_cast<f32x4*>(sAl + 4 * h) = al;
-        }
+      for (int i = 0; i < NHL; ++i) {
+        const _Float16 ph = (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(su[i], invS[i], -mold[i]));
+        l_run[i] += (float)ph;
+        sP[(pos >> 3) * AT2_PST + (2 * i + h) * 8 + (pos & 7)] = ph;
       }
+    } else {
+#pragma unroll
+      for (int i = 0; i < NHL; ++i) {
+        const float s = su[i] * invS[i];
+        const float mnew = fmaxf(mold[i], half_max(s));
+        const float alpha = (mnew == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(mold[i] - mnew);
+        const float pv = (mnew == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(s - mnew);
+        const _Float16 ph = (_Float16)pv;
+        l_run[i] = l_run[i] * alpha + (float)ph;
+        mold[i] = mnew;
+        thr[i] = (mnew + 8.0f) * Ssc[i];
+        sP[(pos >> 3) * AT2_PST + (2 * i + h) * 8 + (pos & 7)] = ph;
+        if (t32 == 0) sAl[2 * i + h] = alpha;
+      }
+      resc = true;
     }
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // the wave's value rows and P are in LDS
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // the wave's value rows, P and alpha are in LDS
     __builtin_amdgcn_wave_barrier();
     // ---- rescale and accumulate P x V: heads 4 g4 + r, columns 16 T + c16
     {
-      const f32x4 al = *reinterpret_cast<const f32x4*>(sAl + 4 * g4);
-      if (!__all(al[0] == 1.0f && al[1] == 1.0f && al[2] == 1.0f && al[3] == 1.0f)) {
+      if (resc) {
+        const f32x4 al = *reinterpret_cast<const f32x4*>(sAl + 4 * g4);
 #pragma unroll
         for (int T = 0; T < NT; ++T)
 #pragma unroll
           for (int r = 0; r < 4; ++r) acc_v[T][r] *= al[r];
+        // (every slow block writes the alphas of all the lanes' heads again;
+        // those of other heads stay 1)
+        resc = false;
       }
       const f16x8 pa = *reinterpret_cast<const f16x8*>(sP + g4 * AT2_PST + c16 * 8);  // 16 lanes: 64 banks
-      // (columns past the state's have a zero mask: no branch on the tile count)
+      u32x4 vv[NT];
+#pragma unroll
+      for (int T = 0; T < NT; ++T) vv[T] = LDS_AT(u32x4, lds_ptr(vaddr[T]));
 #pragma unroll
       for (int T = 0; T < NT; ++T) {
-        const u32x2 cm = sVc[16 * T + c16];
-        const u32x2 vv = *reinterpret_cast<const u32x2*>(sV + cm[0] + 2 * g4);
-        const u32x4 vb = (u32x4){vv[0] & cm[1], (vv[0] >> 8) & cm[1], vv[1] & cm[1], (vv[1] >> 8) & cm[1]};
+        const unsigned m = vmask[T];
+        const u32x4 vb = (u32x4){vv[T][0] & m, vv[T][1] & m, vv[T][2] & m, vv[T][3] & m};
         acc_v[T] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, __builtin_bit_cast(f16x8, vb), acc_v[T], 0, 0, 0);
       }
     }
     __builtin_amdgcn_s_waitcnt(0xc07f);
     __builtin_amdgcn_wave_barrier();
   }
-  // ---- l over the half's tokens; the maxima out of LDS before it is reused
-  float mfin[4];
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the requests past the end have landed before LDS is reused
+  // ---- l over the half's tokens
 #pragma unroll
-  for (int jj = 0; jj < 4; ++jj) {
-    l_run[jj] = half_sum(l_run[jj]);
-    mfin[jj] = sM[4 * h + jj];
-  }
+  for (int i = 0; i < NHL; ++i) l_run[i] = half_sum(l_run[i]);
   // ---- merge the waves, four heads at a time: scratch [wave][4][CST]
   constexpr int CST = 16 * NT + 4;
   __syncthreads();
@@ -2595,14 +2633,15 @@ __global__ void __launch_bounds__(64 * W, 1) k_att2(AttK a) {
   float* part = reinterpret_cast<float*>(a.ws) + (p * a.n_splits + sp) * att_part_stride(g);
   const AttVCol* vcg = reinterpret_cast<const AttVCol*>(vst + OFF_ATTV);
   const unsigned* vch = reinterpret_cast<const unsigned*>(vst + OFF_ATTVCH);
+  const bool cols_ok = ncols <= 16 * NT;  // (the launch chose NT from the states' column counts)
   for (int c4 = 0; c4 * 4 < g; ++c4) {
     float* mine = red + wave * 4 * CST;
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const int H = 4 * h + jj;
+    for (int i = 0; i < NHL; ++i) {
+      const int H = 2 * i + h;
       if (t32 == 0 && (H >> 2) == c4) {
-        mine[(H & 3) * CST + 16 * NT] = mfin[jj];
-        mine[(H & 3) * CST + 16 * NT + 1] = l_run[jj];
+        mine[(H & 3) * CST + 16 * NT] = mold[i];
+        mine[(H & 3) * CST + 16 * NT + 1] = l_run[i];
       }
     }
     if (g4 == c4) {
@@ -2618,19 +2657,20 @@ __global__ void __launch_bounds__(64 * W, 1) k_att2(AttK a) {
       const unsigned cc = vch[jj];
       const int c0 = (int)(cc & 0xFFFFu), nc = (int)(cc >> 16);
       float M = -INFINITY;
-      for (int w = 0; w < nwav; ++w) M = fmaxf(M, red[(w * 4 + hh) * CST + 16 * NT]);
+      for (int w = 0; w < W; ++w) M = fmaxf(M, red[(w * 4 + hh) * CST + 16 * NT]);
       float A = 0.0f, Ls = 0.0f;
-      for (int w = 0; w < nwav; ++w) {
+      for (int w = 0; w < W; ++w) {
         const float* rw = red + (w * 4 + hh) * CST;
         const float mw = rw[16 * NT];
         const float f = (mw == -INFINITY) ? 0.0f : exp2f(mw - M);
         float v = 0.0f;
-        for (int k = 0; k < nc; ++k) v += vcg[c0 + k].fac * rw[c0 + k];
+        for (int k = 0; k < nc; ++k)
+          if (c0 + k < 16 * NT) v += vcg[c0 + k].fac * rw[c0 + k];
         A += f * v;
         Ls += f * rw[16 * NT + 1];
       }
       float* ph = part + (4 * c4 + hh) * ATT_PART_FLOATS;
-      ph[jj] = A;
+      ph[jj] = cols_ok ? A : __builtin_nanf("");
       if (jj == 0) { ph[128] = M; ph[129] = Ls; }
     }
     if (4 * (c4 + 1) < g) __syncthreads();
@@ -2663,6 +2703,18 @@ int attend_scratch(void** ptr) {
   return 0;
 }
 
+template <int R2M, int NT, int NCH, int W, bool SWZ, bool G4>
+static int at2_attr() {
+  return hipFuncSetAttribute((const void*)k_att2<R2M, NT, NCH, W, SWZ, G4>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                             (int)at2_lds_bytes(R2M, NT, NCH, W, G4)) != hipSuccess;
+}
+template <int R2M, int NT, int NCH, int W, bool SWZ, bool G4>
+static void at2_launch(dim3 grid, hipStream_t s, const AttK& a) {
+  static_assert(at2_lds_bytes(R2M, NT, NCH, W, G4) <= 160 * 1024, "k_att2 LDS");
+  hipLaunchKernelGGL((k_att2<R2M, NT, NCH, W, SWZ, G4>), grid, dim3(64 * W), at2_lds_bytes(R2M, NT, NCH, W, G4), s,
+                     a);
+}
+
 typedef void (*AttKernel)(AttK);
 // variant: [RHT+sketch, sketch, sketch >512, RHT, -, >512] x [stream, REC]
 static const AttKernel kAttKernels[6][2] = {
@@ -2684,12 +2736,11 @@ int launch_attend(const AttendLaunch& L, void* stream) {
     if (hipFuncSetAttribute((const void*)k_att_combine, hipFuncAttributeMaxDynamicSharedMemorySize, (int)CMB_LDS) !=
         hipSuccess)
       return 1;
-    if (hipFuncSetAttribute((const void*)k_att2<4, 10, 1, 16>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)at2_lds_bytes(4, 10, 1, 16)) != hipSuccess ||
-        hipFuncSetAttribute((const void*)k_att2<4, 10, 2, 8>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)at2_lds_bytes(4, 10, 2, 8)) != hipSuccess ||
-        hipFuncSetAttribute((const void*)k_att2<8, 12, 3, 8>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)at2_lds_bytes(8, 12, 3, 8)) != hipSuccess)
+    if (at2_attr<4, 10, 1, 4, true, true>() || at2_attr<4, 10, 1, 4, true, false>() ||
+        at2_attr<3, 8, 1, 4, false, false>() || at2_attr<4, 8, 1, 4, false, false>() ||
+        at2_attr<4, 10, 1, 4, false, false>() ||
+        at2_attr<4, 10, 1, 4, false, true>() || at2_attr<4, 10, 2, 8, false, false>() ||
+        at2_attr<8, 12, 3, 8, false, false>())
       return 1;
     g_att_attr_done = true;
   }
@@ -2734,13 +2785,22 @@ int launch_attend(const AttendLaunch& L, void* stream) {
     a.n_splits = att_n_splits(np, L.n_tokens);
     const size_t att_lds = fixed + (size_t)waves * a.region_words * 4;
     const dim3 grid((unsigned)a.n_splits, (unsigned)np);
-    if (!sketch && !L.rht && L.group <= 8 && L.max_bits <= 512) {
-      if (L.max_bits <= 256 && L.att_chunks <= 1)
-        hipLaunchKernelGGL((k_att2<4, 10, 1, 16>), grid, dim3(64 * 16), at2_lds_bytes(4, 10, 1, 16), s, a);
-      else if (L.max_bits <= 256)
-        hipLaunchKernelGGL((k_att2<4, 10, 2, 8>), grid, dim3(64 * 8), at2_lds_bytes(4, 10, 2, 8), s, a);
-      else
-        hipLaunchKernelGGL((k_att2<8, 12, 3, 8>), grid, dim3(64 * 8), at2_lds_bytes(8, 12, 3, 8), s, a);
+    if (!sketch && !L.rht && L.group <= 8 && L.max_bits <= 512 && L.max_vcols <= 192) {
+      const bool g4 = L.group <= 4;
+      if (L.max_bits <= 256 && L.att_chunks <= 1) {
+        if (L.rec256)
+          g4 ? at2_launch<4, 10, 1, 4, true, true>(grid, s, a) : at2_launch<4, 10, 1, 4, true, false>(grid, s, a);
+        else if (!g4 && L.max_vcols <= 128 && L.max_bits <= 192)
+          at2_launch<3, 8, 1, 4, false, false>(grid, s, a);
+        else if (!g4 && L.max_vcols <= 128)
+          at2_launch<4, 8, 1, 4, false, false>(grid, s, a);
+        else
+          g4 ? at2_launch<4, 10, 1, 4, false, true>(grid, s, a) : at2_launch<4, 10, 1, 4, false, false>(grid, s, a);
+      } else if (L.max_bits <= 256) {
+        at2_launch<4, 10, 2, 8, false, false>(grid, s, a);
+      } else {
+        at2_launch<8, 12, 3, 8, false, false>(grid, s, a);
+      }
     } else {
       const int var = sketch ? (L.rht ? 0 : (L.max_bits <= 512 ? 1 : 2)) : (L.rht ? 3 : (L.max_bits <= 512 ? 4 : 5));
       hipLaunchKernelGGL(kAttKernels[var][L.rec && !L.rht ? 1 : 0], grid, dim3(64 * waves), att_lds, s, a);

@@ -17,6 +17,7 @@ import numpy as np
 import pytest
 import torch
 
+import att_variants
 import synth
 from oracle import codec, rht
 from parity_bounds import (assert_rht_code_diffs_at_boundaries, check_eigen_codes,
@@ -274,6 +275,25 @@ def test_attention_batched_gqa7():
                                         n, torch.from_numpy(np.stack(qs)).to(DEV)).cpu().numpy()
     for i in range(pairs):
         assert rel_err(out[i], wants[i]) <= 2e-3
+
+
+@pytest.mark.parametrize("case", att_variants.CASES, ids=lambda c: f"cfg{c[0]}-{c[1]:.3f}-g{c[2]}")
+def test_attention_kernel_variants(case):
+    """One case per instance of the packed-bit attention kernel (record
+    widths, value-column counts and groups that select each one)."""
+    cfg, avg, g, n, spec = case
+    w = synth.WORKLOADS[cfg]
+    k = synth.stream(w, 0, 0, 1, 0, n=n)
+    v = synth.stream(w, 0, 0, 1, 1, n=n)
+    n_c = min(w.n_calib, n)
+    bits = None if spec is None else att_variants.widths(spec)
+    ks, vs = codec.calibrate_head(k, n_c, avg, bits=bits), codec.calibrate_head(v, n_c, avg, bits=bits)
+    kp, vp = codec.encode_kv(ks, k), codec.encode_kv(vs, v)
+    q = np.random.default_rng(cfg * 100 + g).standard_normal((g, 128)).astype(np.float32)
+    want = codec.attend_compressed(ks, vs, kp, vp, n, q.astype(np.float64))
+    got = stc.attend_compressed(gpu_state(ks), gpu_state(vs), torch.from_numpy(kp).to(DEV),
+                                torch.from_numpy(vp).to(DEV), n, torch.from_numpy(q).to(DEV)).cpu().numpy()
+    assert rel_err(got, want) <= 2e-3, rel_err(got, want)
 
 
 def test_attention_zero_bit_streams():
