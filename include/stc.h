@@ -108,9 +108,10 @@ size_t stc_state_bytes(void);
 /* ceil(n_tokens * total_bits / 8) rounded up to a multiple of 16 (format F1). */
 size_t stc_packed_bytes(int32_t total_bits, int64_t n_tokens);
 /* Workspace of stc_attend_compressed_batched: the per-split partial results
- * (written by one kernel, merged by the next). It needs no initialisation
- * and can be reused by later calls of any shape in stream order (not by
- * calls that run at the same time). */
+ * (written by one kernel, merged by the next) and the per-pair score weights
+ * of the packed-bit kernel (written by a kernel that runs before it). It
+ * needs no initialisation and can be reused by later calls of any shape in
+ * stream order (not by calls that run at the same time). */
 size_t stc_attend_workspace_bytes(int64_t n_pairs, int32_t group, int64_t n_tokens);
 
 /* ------------------------------------------------------- host math

@@ -383,11 +383,14 @@ size_t stc_packed_bytes(int32_t total_bits, int64_t n_tokens) {
 
 size_t stc_attend_workspace_bytes(int64_t n_pairs, int32_t group, int64_t n_tokens) {
   if (n_pairs <= 0 || n_tokens <= 0 || group <= 0) return 256;
-  // one launch covers at most ATT_MAX_PAIRS pairs; launches reuse the partials
+  // one launch covers at most ATT_MAX_PAIRS pairs; launches reuse the area,
+  // which holds the larger of a full launch's and the last launch's needs
   const int64_t np = n_pairs < ATT_MAX_PAIRS ? n_pairs : ATT_MAX_PAIRS;
-  const int64_t splits = att_n_splits(np, n_tokens);
-  size_t parts = (size_t)np * splits * att_part_stride(group) * sizeof(float);
-  return (parts + 255) / 256 * 256;
+  const int64_t last = n_pairs % ATT_MAX_PAIRS;
+  int64_t floats = att_launch_floats(np, n_tokens, group);
+  if (last) floats = std::max(floats, att_launch_floats(last, n_tokens, group));
+  const size_t bytes = (size_t)floats * sizeof(float);
+  return (bytes + 255) / 256 * 256;
 }
 
 int32_t stc_total_bits(float avg_bits, int32_t d) {

@@ -142,14 +142,24 @@ inline int64_t att_n_splits(int64_t n_pairs, int64_t n_tokens) {
   return (n_tokens + s - 1) / s;
 }
 constexpr int ATT_PART_FLOATS = D + 2;              // per (pair, split, head): acc[128], m, l
+// per pair, after a launch's partials: the packed-bit kernel's score weights
+// a [8 heads][128] and the 8 per-head scales (padded to whole 128-byte lines)
+constexpr int ATT_PREP_FLOATS = 8 * D + 32;
 // floats of one (pair, split) partial block: group x (acc, m, l), padded to
 // whole 128-byte lines so that no line is written by two workgroups
 __host__ __device__ inline int64_t att_part_stride(int group) {
   return ((int64_t)group * ATT_PART_FLOATS + 31) / 32 * 32;
 }
 // Attention workspace: the split partials of one launch, which covers at
-// most ATT_MAX_PAIRS pairs (launches of one call reuse it in stream order).
+// most ATT_MAX_PAIRS pairs (launches of one call reuse it in stream order),
+// then the per-pair score weights of the packed-bit kernel.
 constexpr int64_t ATT_MAX_PAIRS = 16384;
+inline int64_t att_partial_floats(int64_t np, int64_t n_tokens, int group) {
+  return np * att_n_splits(np, n_tokens) * att_part_stride(group);
+}
+inline int64_t att_launch_floats(int64_t np, int64_t n_tokens, int group) {
+  return att_partial_floats(np, n_tokens, group) + np * ATT_PREP_FLOATS;
+}
 
 // Host-side launchers implemented in stc_kernels.hip.
 struct EncodeLaunch {

@@ -1497,6 +1497,7 @@ struct AttK {
   const unsigned char* k_sketch;  // key residual sketch (16 bytes per token) and |r|, or null
   const float* k_rnorm;
   long long sketch_stride, rnorm_stride;
+  float* prep;  // per pair of the launch: score weights and head scales (k_att2_prep), ATT_PREP_FLOATS each
 };
 
 constexpr int ATT_WAVES_MAX = 16;
@@ -1654,23 +1655,23 @@ __device__ __forceinline__ unsigned att_group_bytes(const lds_u8* str, const lds
 // SKETCH (RHT only): keys carry the 1-bit residual sketch; a second table
 // holds S q scale log2(e) sqrt(pi/2)/m (hi / lo) and each score gains
 // |r_t| times its product with the token's signs, one more MFMA chain.
-// k_att_combine: one workgroup per (pair, query head), after k_att_main has
-// written every split's partial. Thread (q, i) requests its quarter of row i
-// of U_V (32 floats, kept in registers) first; meanwhile thread j < 128
-// merges the splits' (acc_j, m, l) with log-sum-exp weights (fp32 weights,
-// fp64 sums, batches of 32 splits with all loads in flight) and dequantizes
-// the mean code of V channel j into LDS; then every thread sums its quarter
-// of o_i = sum_k U_ik chat_k and the four quarters are added through LDS.
+// k_att_combine: one workgroup per pair, after the main kernel has written
+// every split's partial. Thread (q, i) requests its quarter of row i of U_V
+// (32 floats, kept in registers) first; meanwhile the threads merge, per
+// (head, V channel j), the splits' (acc_j, m, l) with log-sum-exp weights
+// (fp32 weights, fp64 sums, batches of 8 splits with all loads in flight)
+// and dequantize the mean code into LDS; then every thread sums its quarter
+// of o_i = sum_k U_ik chat_k for each head and the four quarters are added
+// through LDS. U_V is read once per pair.
 constexpr int CMB_THREADS = 512;
-constexpr int CMB_BATCH = 32;
-constexpr size_t CMB_LDS = (size_t)(128 + 4 * 128) * 4;
+constexpr int CMB_BATCH = 8;
+constexpr size_t CMB_LDS = (size_t)(16 * 128 + 4 * 16 * 128) * 4;
 
 __global__ void __launch_bounds__(CMB_THREADS) k_att_combine(AttK a) {
   extern __shared__ __align__(16) unsigned char smem[];
-  float* sC = reinterpret_cast<float*>(smem);  // dequantized mean codes [128]
-  float* sQ = sC + 128;                        // quarter sums [4][128]
+  float* sC = reinterpret_cast<float*>(smem);  // dequantized mean codes [head][128]
+  float* sQ = sC + 16 * 128;                   // quarter sums [4][head][128]
   const long long p = blockIdx.x;
-  const int hh = blockIdx.y;
   const long long pg = a.pair_base + p;
   const int t = threadIdx.x;
   const int i = t & 127, qt = t >> 7;  // output dim, quarter of the inputs
@@ -1678,8 +1679,8 @@ __global__ void __launch_bounds__(CMB_THREADS) k_att_combine(AttK a) {
   const int S = (int)a.n_splits;
   const long long PS = att_part_stride(g);
   const long long ksi = state_index(a.k_map, pg, a.n_states), vsi = state_index(a.v_map, pg, a.n_states);
-  if (ksi < 0 || vsi < 0) {  // no state for the pair (k_att_main wrote no partial): NaN
-    if (t < 128) a.out[(pg * g + hh) * 128 + t] = __builtin_nanf("");
+  if (ksi < 0 || vsi < 0) {  // no state for the pair (the main kernel wrote no partial): NaN
+    for (int e = t; e < g * 128; e += CMB_THREADS) a.out[pg * g * 128 + e] = __builtin_nanf("");
     return;
   }
   const unsigned char* vst = a.v_states + (size_t)vsi * STATE_BYTES;
@@ -1688,8 +1689,8 @@ __global__ void __launch_bounds__(CMB_THREADS) k_att_combine(AttK a) {
   f32x4 u[8];
 #pragma unroll
   for (int r = 0; r < 8; ++r) u[r] = urow[r];
-  if (t < 128) {
-    const int j = t;
+  for (int e = t; e < g * 128; e += CMB_THREADS) {
+    const int hh = e >> 7, j = e & 127;
     const float* ph = reinterpret_cast<const float*>(a.ws) + p * (long long)S * PS + hh * ATT_PART_FLOATS;
     const unsigned bits = hv->bits[j];
     const float step = hv->step32[j], hs = hv->halfspan[j];
@@ -1723,20 +1724,26 @@ __global__ void __launch_bounds__(CMB_THREADS) k_att_combine(AttK a) {
       }
     }
     // dequantize the mean code: step * (A / L - (L_j - 1)/2)
-    sC[j] = bits ? (float)((double)step * (A / L - (double)hs)) : 0.0f;
+    sC[hh * 128 + j] = bits ? (float)((double)step * (A / L - (double)hs)) : 0.0f;
   }
   __syncthreads();
-  float o = 0.0f;
-  const f32x4* c4 = reinterpret_cast<const f32x4*>(sC) + qt * 8;
+  for (int hh = 0; hh < g; ++hh) {
+    float o = 0.0f;
+    const f32x4* c4 = reinterpret_cast<const f32x4*>(sC + hh * 128) + qt * 8;
 #pragma unroll
-  for (int r = 0; r < 8; ++r) {
-    const f32x4 c = c4[r];
+    for (int r = 0; r < 8; ++r) {
+      const f32x4 c = c4[r];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) o = __builtin_fmaf(u[r][e], c[e], o);
+      for (int e = 0; e < 4; ++e) o = __builtin_fmaf(u[r][e], c[e], o);
+    }
+    sQ[(qt * 16 + hh) * 128 + i] = o;
   }
-  sQ[qt * 128 + i] = o;
   __syncthreads();
-  if (t < 128) a.out[(pg * g + hh) * 128 + i] = (sQ[i] + sQ[128 + i]) + (sQ[256 + i] + sQ[384 + i]);
+  for (int e = t; e < g * 128; e += CMB_THREADS) {
+    const int hh = e >> 7, ii = e & 127;
+    a.out[(pg * g + hh) * 128 + ii] = (sQ[hh * 128 + ii] + sQ[(16 + hh) * 128 + ii]) +
+                                      (sQ[(32 + hh) * 128 + ii] + sQ[(48 + hh) * 128 + ii]);
+  }
 }
 
 template <int NW, bool RHT, bool SKETCH, bool REC>
@@ -2260,39 +2267,127 @@ __device__ __forceinline__ void at2_read(unsigned (&r)[R2M], const unsigned* buf
 }
 
 // Request the records of block blk of one stream (4 B bytes from byte 4 B blk)
-// into a wave's staging buffer: NCH loads of 16 bytes per lane straight to
-// LDS, from the 16-byte boundary at or below the block's first byte (returned
-// in bits, the offset of the records in the buffer). Lanes past the stream
-// end load its first 16 bytes instead, so every call issues NCH loads (a
-// stream of no bytes passes another valid address as `stream`).
+// into a wave's staging buffer: NCH buffer loads of 16 bytes per lane
+// straight to LDS, from the 16-byte boundary at or below the block's first
+// byte (returned in bits, the offset of the records in the buffer). Load c of
+// a lane reads rel[c] bytes past that boundary (at2_stage_rel) through a
+// buffer resource whose range ends at the block's last byte (256-bit records:
+// at the block's end) and at the stream's plen bytes: lanes past it read
+// zeros and move no data. A stream of no bytes (or a request past a split's
+// end) passes plen 0.
 template <int NCH, bool SWZ>
 __device__ __forceinline__ unsigned at2_stage(const unsigned char* stream, long long blk, unsigned B, long long plen,
-                                              unsigned* buf, int lane) {
+                                              unsigned* buf, const unsigned (&rel)[NCH]) {
   const long long start = blk * 4LL * (long long)B;
   const long long base = start & ~15LL;
-  // SWZ (B = 256): slot lane of load c takes chunk 2 t + h + c of the block
-  // (t = lane & 31, h = lane >> 5), so that the 16-byte reads of 16
-  // consecutive lanes cover 64 banks (in block order they would pair up)
-  const long long chunk = SWZ ? 2 * (lane & 31) + (lane >> 5) : (long long)lane;
+  long long lim = plen - base;  // bytes past base that the lanes may read (uniform)
+  if (!SWZ && lim > start - base + 4LL * (long long)B) lim = start - base + 4LL * (long long)B;
+  if (lim < 0) lim = 0;
+  if (lim > 1024LL * NCH) lim = 1024LL * NCH;  // (the loads reach no further)
+#if defined(__HIP_DEVICE_COMPILE__)  // (buffer resources exist in the device pass only)
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(stream + (lim > 0 ? base : 0)), (short)0, (int)lim, 0x00020000);
 #pragma unroll
-  for (int c = 0; c < NCH; ++c) {
-    long long byte = SWZ ? base + 16LL * (chunk + c) : base + 1024LL * c + 16LL * lane;
-    if (byte + 16 > plen) byte = 0;
-    __builtin_amdgcn_global_load_lds(stream + byte, (__attribute__((address_space(3))) void*)(buf + 256 * c), 16, 0,
-                                     0);
-  }
+  for (int c = 0; c < NCH; ++c)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(buf + 256 * c), 16, rel[c],
+                                             0, 0, 0);
+#endif
   return (unsigned)(start - base) * 8u;
+}
+// Per-lane byte offsets of at2_stage's loads: 16 lane + 1024 c; for 256-bit
+// records (SWZ) slot lane of the block's chunks takes chunk 2 t + h + c
+// (t = lane & 31, h = lane >> 5), so that the 16-byte reads of 16
+// consecutive lanes cover 64 banks (in block order they would pair up).
+template <int NCH, bool SWZ>
+__device__ __forceinline__ void at2_stage_rel(unsigned (&rel)[NCH], int lane) {
+#pragma unroll
+  for (int c = 0; c < NCH; ++c)
+    rel[c] = SWZ ? 16u * (unsigned)(2 * (lane & 31) + (lane >> 5) + c) : 1024u * c + 16u * (unsigned)lane;
+}
+
+// Score weights of the packed-bit kernel, once per pair (its splits share
+// them): a_j = (U_K^T q)_j step_j scale log2(e) for the group's heads (0 for
+// dropped channels and heads past the group), and per head the power of two
+// S that scales the largest weight max_j |a_j| 2^(b_j - 1) to at most 2^20.
+// 1024 threads: thread (part, j) sums rows part, part + 8, .. of U_K for
+// channel j and all eight heads (its 16 loads in flight at once); the eight
+// parts are added through LDS.
+constexpr int PREP_PARTS = 8;
+__global__ void __launch_bounds__(128 * PREP_PARTS) k_att2_prep(AttK a) {
+  __shared__ __align__(16) float sqT[128 * 8];   // q^T [128][8]
+  __shared__ float red[PREP_PARTS][8][128];
+  const int tid = threadIdx.x;
+  const long long p = blockIdx.x, pg = a.pair_base + p;
+  const int g = a.group;
+  const long long ksi = state_index(a.k_map, pg, a.n_states), vsi = state_index(a.v_map, pg, a.n_states);
+  if (ksi < 0 || vsi < 0) return;  // (the main kernel writes nothing for this pair either)
+  const unsigned char* kst = a.k_states + (size_t)ksi * STATE_BYTES;
+  const DevHdr* hk = reinterpret_cast<const DevHdr*>(kst);
+  const int j = tid & 127, part = tid >> 7;
+  const float* u = reinterpret_cast<const float*>(kst + OFF_U32);
+  constexpr int RPP = 128 / PREP_PARTS;
+  float ur[RPP];
+#pragma unroll
+  for (int k = 0; k < RPP; ++k) ur[k] = u[(part + PREP_PARTS * k) * 128 + j];
+  const float* qp = a.q + pg * g * 128;
+  {
+    const int r = tid >> 3, hh = tid & 7;
+    sqT[tid] = hh < g ? qp[hh * 128 + r] : 0.0f;
+  }
+  __syncthreads();
+  float acc[8];
+#pragma unroll
+  for (int hh = 0; hh < 8; ++hh) acc[hh] = 0.0f;
+#pragma unroll
+  for (int k = 0; k < RPP; ++k) {
+    const f32x4* q4 = reinterpret_cast<const f32x4*>(sqT + (part + PREP_PARTS * k) * 8);
+    const f32x4 q0 = q4[0], q1 = q4[1];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc[e] = __builtin_fmaf(ur[k], q0[e], acc[e]);
+      acc[4 + e] = __builtin_fmaf(ur[k], q1[e], acc[4 + e]);
+    }
+  }
+#pragma unroll
+  for (int hh = 0; hh < 8; ++hh) red[part][hh][j] = acc[hh];
+  __syncthreads();
+  float* pre = a.prep + p * ATT_PREP_FLOATS;
+  __shared__ float wmax[16];
+  {
+    const int hh = tid >> 7, c = tid & 127;
+    const unsigned b = hk->bits[c];
+    float v = 0.0f;
+    if (hh < g && b > 0) {
+      float sum = 0.0f;
+#pragma unroll
+      for (int pt = 0; pt < PREP_PARTS; ++pt) sum += red[pt][hh][c];
+      v = sum * hk->step32[c] * a.scale * LOG2E;
+    }
+    pre[tid] = v;
+    // the largest weight of the head: max over c of |a_c| 2^(b_c - 1), two waves per head
+    float m = b > 0 ? fabsf(v) * (float)(1u << (b - 1)) : 0.0f;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+    if ((tid & 63) == 0) wmax[tid >> 6] = m;
+  }
+  __syncthreads();
+  if (tid < 8) {
+    const float M = fmaxf(wmax[2 * tid], wmax[2 * tid + 1]);
+    int ex = 0;
+    frexpf(M, &ex);
+    pre[8 * 128 + tid] = M > 0.0f ? ldexpf(1.0f, 20 - ex) : 1.0f;
+  }
 }
 
 // Dynamic LDS of k_att2<R2M, NT, NCH, W, .., G4>: the score weights, the
 // value column table and the per-head scales, then the larger of the prologue
 // scratch, the W wave regions and the merge scratch.
 __host__ __device__ constexpr size_t at2_lds_bytes(int R2M, int NT, int NCH, int W, bool G4) {
-  const size_t fixed = (size_t)at2_trows(G4) * (64 * R2M + 16) + ATT_MAX_VCOLS * 8 + 8 * 4;
-  const size_t pro = (size_t)(128 * 8 + (W / 2) * 8 * 128 + 8 * 128) * 4 + 2 * 64 * R2M + 8 * 4;
+  const size_t fixed = (size_t)at2_trows(G4) * (64 * R2M + 16) + ATT_MAX_VCOLS * 8 + 8 * 4 + 128 * 4 + ATT_MAX_VCOLS * 4;
+  const size_t pro = (size_t)8 * 128 * 4 + 2 * 64 * R2M + 8 * 4;
   const size_t vwords = (size_t)at2_vrow(R2M, 8 * R2M - 1) + 16;
   const size_t waves = (size_t)W * (2 * at2_nst(NCH) * 256 * NCH + vwords + 4 * AT2_PST / 2 + 16) * 4;
-  const size_t merge = (size_t)W * 4 * (16 * NT + 4) * 4;
+  const size_t merge = (size_t)W * 8 * (16 * NT + 4) * 4;
   const size_t big = pro > waves ? (pro > merge ? pro : merge) : (waves > merge ? waves : merge);
   return fixed + big;
 }
@@ -2319,7 +2414,9 @@ __global__ void __launch_bounds__(64 * W, W == 4 ? 3 : 1) k_att2(AttK a) {
   signed char* sA = reinterpret_cast<signed char*>(smem);            // [TROWS][TROW]
   u32x2* sVc = reinterpret_cast<u32x2*>(smem + TROWS * TROW);        // [256] (row word offset, mask2)
   float* sInvS = reinterpret_cast<float*>(sVc + ATT_MAX_VCOLS);     // [8]
-  unsigned* sReg0 = reinterpret_cast<unsigned*>(sInvS + 8);         // wave regions / prologue scratch
+  unsigned* sVch = reinterpret_cast<unsigned*>(sInvS + 8);          // [128] channel: first column | count << 16
+  float* sFac = reinterpret_cast<float*>(sVch + 128);                // [256] column scale 2^(24 - shift + offset)
+  unsigned* sReg0 = reinterpret_cast<unsigned*>(sFac + ATT_MAX_VCOLS);  // wave regions / prologue scratch
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -2345,71 +2442,23 @@ __global__ void __launch_bounds__(64 * W, W == 4 ? 3 : 1) k_att2(AttK a) {
 
   // ------------------------------------------------------------ prologue
   {
-    float* sqT = reinterpret_cast<float*>(sReg0);        // q^T [128][8]
-    constexpr int PARTS = W / 2, RPP = 128 / PARTS;  // parts of the rows of U_K, rows per part
-    float* red = sqT + 128 * 8;                          // [PARTS][8 heads][128]
-    float* sAf = red + PARTS * 8 * 128;                  // a [8][128]
+    // the pair's score weights a [8][128] and head scales (k_att2_prep)
+    float* sAf = reinterpret_cast<float*>(sReg0);                             // a [8][128]
     unsigned short* sBit = reinterpret_cast<unsigned short*>(sAf + 8 * 128);  // [TABW] record bit -> j | k << 8
-    float* sS = reinterpret_cast<float*>(sBit + TABW);   // [8] per-head scales
+    float* sS = reinterpret_cast<float*>(sBit + TABW);                        // [8] per-head scales
+    const float* pre = a.prep + p * ATT_PREP_FLOATS;
     for (int i = tid; i < TROWS * TROW / 16; i += blockDim.x) reinterpret_cast<u32x4*>(sA)[i] = (u32x4){0u, 0u, 0u, 0u};
     for (int i = tid; i < TABW; i += blockDim.x) sBit[i] = 0xFFFFu;
-    const float* qp = a.q + pg * g * 128;
-    for (int e = tid; e < 128 * 8; e += blockDim.x) {
-      const int r = e >> 3, hh = e & 7;
-      sqT[e] = hh < g ? qp[hh * 128 + r] : 0.0f;
+    for (int e = tid; e < 8 * 128 / 4; e += blockDim.x)
+      reinterpret_cast<f32x4*>(sAf)[e] = reinterpret_cast<const f32x4*>(pre)[e];
+    if (tid < 8) {
+      sS[tid] = pre[8 * 128 + tid];
+      sInvS[tid] = 1.0f / pre[8 * 128 + tid];
     }
-    const int j = tid & 127, part = tid >> 7;
-    const float* u = reinterpret_cast<const float*>(kst + OFF_U32);
     __syncthreads();
     if (tid < 128) {
       const unsigned b = hk->bits[tid], o = hk->off[tid];
       for (unsigned k = 0; k < b; ++k) sBit[o + k] = (unsigned short)(tid | (k << 8));
-    }
-    float acc[8];
-#pragma unroll
-    for (int hh = 0; hh < 8; ++hh) acc[hh] = 0.0f;
-#pragma unroll
-    for (int k0 = 0; k0 < RPP; k0 += 16) {
-      float ur[16];
-#pragma unroll
-      for (int k = 0; k < 16; ++k) ur[k] = u[(part + PARTS * (k0 + k)) * 128 + j];
-#pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        const f32x4* q4 = reinterpret_cast<const f32x4*>(sqT + (part + PARTS * (k0 + k)) * 8);
-        const f32x4 q0 = q4[0], q1 = q4[1];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          acc[e] = __builtin_fmaf(ur[k], q0[e], acc[e]);
-          acc[4 + e] = __builtin_fmaf(ur[k], q1[e], acc[4 + e]);
-        }
-      }
-    }
-#pragma unroll
-    for (int hh = 0; hh < 8; ++hh) red[(part * 8 + hh) * 128 + j] = acc[hh];
-    __syncthreads();
-    for (int e = tid; e < 8 * 128; e += 64 * W) {
-      const int hh = e >> 7, c = e & 127;
-      float v = 0.0f;
-      if (hh < g && hk->bits[c] > 0) {
-        float sum = 0.0f;
-        for (int pt = 0; pt < PARTS; ++pt) sum += red[(pt * 8 + hh) * 128 + c];
-        v = sum * hk->step32[c] * a.scale * LOG2E;
-      }
-      sAf[hh * 128 + c] = v;
-    }
-    __syncthreads();
-    if (tid < 8) {
-      // the largest weight of head tid is at most max_j |a_j| 2^(b_j - 1): scale it to at most 2^20
-      float M = 0.0f;
-      for (int c = 0; c < 128; ++c) {
-        const unsigned b = hk->bits[c];
-        if (b) M = fmaxf(M, fabsf(sAf[tid * 128 + c]) * (float)(1u << (b - 1)));
-      }
-      int ex = 0;
-      frexpf(M, &ex);
-      const float S = M > 0.0f ? ldexpf(1.0f, 20 - ex) : 1.0f;
-      sS[tid] = S;
-      sInvS[tid] = 1.0f / S;
     }
     if (tid < ATT_MAX_VCOLS) {
       const AttVCol* vc = reinterpret_cast<const AttVCol*>(vst + OFF_ATTV);
@@ -2420,6 +2469,8 @@ __global__ void __launch_bounds__(64 * W, W == 4 ? 3 : 1) k_att2(AttK a) {
         e = (u32x2){at2_vrow(R2M, row - 4u * (unsigned)R2v * hh + 4u * R2M * hh), vc[tid].mask2};
       }
       sVc[tid] = e;
+      sFac[tid] = tid < ncols ? vc[tid].fac : 0.0f;
+      if (tid < 128) sVch[tid] = reinterpret_cast<const unsigned*>(vst + OFF_ATTVCH)[tid];
     }
     __syncthreads();
     // int8 parts of round(S_h a_j 2^(k - (c & 3))): rows 3h + p
@@ -2497,6 +2548,8 @@ __global__ void __launch_bounds__(64 * W, W == 4 ? 3 : 1) k_att2(AttK a) {
   const long long stride = (long long)W * AT2_BT;
   long long tok0 = t_begin + (long long)wave * AT2_BT;
   unsigned offk[NST], offv[NST];
+  unsigned srel[NCH];
+  at2_stage_rel<NCH, SWZ>(srel, lane);
   __builtin_amdgcn_s_waitcnt(0xc07f);
   __builtin_amdgcn_wave_barrier();
 #pragma unroll
@@ -2504,8 +2557,8 @@ __global__ void __launch_bounds__(64 * W, W == 4 ? 3 : 1) k_att2(AttK a) {
     const long long tb = tok0 + st * stride;
     const bool real = tb < t_end;
     unsigned* buf = sStage + st * 2 * SWORDS;
-    offk[st] = at2_stage<NCH, SWZ>(gk, real ? tb / AT2_BT : 0, Bk, real ? PkL : 0, buf, lane);
-    offv[st] = at2_stage<NCH, SWZ>(gv, real ? tb / AT2_BT : 0, Bv, real ? PvL : 0, buf + SWORDS, lane);
+    offk[st] = at2_stage<NCH, SWZ>(gk, real ? tb / AT2_BT : 0, Bk, real ? PkL : 0, buf, srel);
+    offv[st] = at2_stage<NCH, SWZ>(gv, real ? tb / AT2_BT : 0, Bv, real ? PvL : 0, buf + SWORDS, srel);
   }
   int cur = 0;  // ring stage of the current block
   for (; tok0 < t_end; tok0 += stride) {
@@ -2513,8 +2566,8 @@ __global__ void __launch_bounds__(64 * W, W == 4 ? 3 : 1) k_att2(AttK a) {
       const long long tb = tok0 + (NST - 1) * stride;
       const bool real = tb < t_end;
       unsigned* buf = sStage + (cur == 0 ? NST - 1 : cur - 1) * 2 * SWORDS;
-      offk[NST - 1] = at2_stage<NCH, SWZ>(gk, real ? tb / AT2_BT : 0, Bk, real ? PkL : 0, buf, lane);
-      offv[NST - 1] = at2_stage<NCH, SWZ>(gv, real ? tb / AT2_BT : 0, Bv, real ? PvL : 0, buf + SWORDS, lane);
+      offk[NST - 1] = at2_stage<NCH, SWZ>(gk, real ? tb / AT2_BT : 0, Bk, real ? PkL : 0, buf, srel);
+      offv[NST - 1] = at2_stage<NCH, SWZ>(gv, real ? tb / AT2_BT : 0, Bv, real ? PvL : 0, buf + SWORDS, srel);
     }
     // the current block's loads are done once at most the later blocks' remain
     __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * NCH * (NST - 1)));  // vmcnt(2 NCH (NST - 1))
@@ -2626,54 +2679,52 @@ __global__ void __launch_bounds__(64 * W, W == 4 ? 3 : 1) k_att2(AttK a) {
   // ---- l over the half's tokens
 #pragma unroll
   for (int i = 0; i < NHL; ++i) l_run[i] = half_sum(l_run[i]);
-  // ---- merge the waves, four heads at a time: scratch [wave][4][CST]
+  // ---- merge the waves: scratch [wave][8 heads][CST]
   constexpr int CST = 16 * NT + 4;
   __syncthreads();
   float* red = reinterpret_cast<float*>(sReg0);
   float* part = reinterpret_cast<float*>(a.ws) + (p * a.n_splits + sp) * att_part_stride(g);
-  const AttVCol* vcg = reinterpret_cast<const AttVCol*>(vst + OFF_ATTV);
-  const unsigned* vch = reinterpret_cast<const unsigned*>(vst + OFF_ATTVCH);
   const bool cols_ok = ncols <= 16 * NT;  // (the launch chose NT from the states' column counts)
-  for (int c4 = 0; c4 * 4 < g; ++c4) {
-    float* mine = red + wave * 4 * CST;
+  {
+    float* mine = red + wave * 8 * CST;
 #pragma unroll
     for (int i = 0; i < NHL; ++i) {
       const int H = 2 * i + h;
-      if (t32 == 0 && (H >> 2) == c4) {
-        mine[(H & 3) * CST + 16 * NT] = mold[i];
-        mine[(H & 3) * CST + 16 * NT + 1] = l_run[i];
+      if (t32 == 0) {
+        mine[H * CST + 16 * NT] = mold[i];
+        mine[H * CST + 16 * NT + 1] = l_run[i];
       }
     }
-    if (g4 == c4) {
+    if (g4 < 2) {
 #pragma unroll
       for (int T = 0; T < NT; ++T)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) mine[r * CST + 16 * T + c16] = acc_v[T][r];
+        for (int r = 0; r < 4; ++r) mine[(4 * g4 + r) * CST + 16 * T + c16] = acc_v[T][r];
     }
-    __syncthreads();
-    const int nh = g - 4 * c4 < 4 ? g - 4 * c4 : 4;
-    for (int e = tid; e < nh * 128; e += blockDim.x) {
-      const int hh = e >> 7, jj = e & 127;
-      const unsigned cc = vch[jj];
-      const int c0 = (int)(cc & 0xFFFFu), nc = (int)(cc >> 16);
-      float M = -INFINITY;
-      for (int w = 0; w < W; ++w) M = fmaxf(M, red[(w * 4 + hh) * CST + 16 * NT]);
-      float A = 0.0f, Ls = 0.0f;
-      for (int w = 0; w < W; ++w) {
-        const float* rw = red + (w * 4 + hh) * CST;
-        const float mw = rw[16 * NT];
-        const float f = (mw == -INFINITY) ? 0.0f : exp2f(mw - M);
-        float v = 0.0f;
-        for (int k = 0; k < nc; ++k)
-          if (c0 + k < 16 * NT) v += vcg[c0 + k].fac * rw[c0 + k];
-        A += f * v;
-        Ls += f * rw[16 * NT + 1];
-      }
-      float* ph = part + (4 * c4 + hh) * ATT_PART_FLOATS;
-      ph[jj] = cols_ok ? A : __builtin_nanf("");
-      if (jj == 0) { ph[128] = M; ph[129] = Ls; }
+  }
+  __syncthreads();
+  for (int e = tid; e < g * 128; e += blockDim.x) {
+    const int hh = e >> 7, jj = e & 127;
+    const unsigned cc = sVch[jj];
+    const int c0 = (int)(cc & 0xFFFFu), nc = (int)(cc >> 16);
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < W; ++w) M = fmaxf(M, red[(w * 8 + hh) * CST + 16 * NT]);
+    float A = 0.0f, Ls = 0.0f;
+#pragma unroll
+    for (int w = 0; w < W; ++w) {
+      const float* rw = red + (w * 8 + hh) * CST;
+      const float mw = rw[16 * NT];
+      const float f = (mw == -INFINITY) ? 0.0f : exp2f(mw - M);
+      float v = 0.0f;
+      for (int k = 0; k < nc; ++k)
+        if (c0 + k < 16 * NT) v += sFac[c0 + k] * rw[c0 + k];
+      A += f * v;
+      Ls += f * rw[16 * NT + 1];
     }
-    if (4 * (c4 + 1) < g) __syncthreads();
+    float* ph = part + hh * ATT_PART_FLOATS;
+    ph[jj] = cols_ok ? A : __builtin_nanf("");
+    if (jj == 0) { ph[128] = M; ph[129] = Ls; }
   }
 }
 
@@ -2744,7 +2795,7 @@ int launch_attend(const AttendLaunch& L, void* stream) {
       return 1;
     g_att_attr_done = true;
   }
-  AttK a;
+  AttK a{};
   a.k_states = L.k_states;
   a.k_map = L.k_map;
   a.v_states = L.v_states;
@@ -2787,6 +2838,8 @@ int launch_attend(const AttendLaunch& L, void* stream) {
     const dim3 grid((unsigned)a.n_splits, (unsigned)np);
     if (!sketch && !L.rht && L.group <= 8 && L.max_bits <= 512 && L.max_vcols <= 192) {
       const bool g4 = L.group <= 4;
+      a.prep = reinterpret_cast<float*>(a.ws) + att_partial_floats(np, L.n_tokens, L.group);
+      hipLaunchKernelGGL(k_att2_prep, dim3((unsigned)np), dim3(128 * PREP_PARTS), 0, s, a);
       if (L.max_bits <= 256 && L.att_chunks <= 1) {
         if (L.rec256)
           g4 ? at2_launch<4, 10, 1, 4, true, true>(grid, s, a) : at2_launch<4, 10, 1, 4, true, false>(grid, s, a);
@@ -2806,7 +2859,7 @@ int launch_attend(const AttendLaunch& L, void* stream) {
       hipLaunchKernelGGL(kAttKernels[var][L.rec && !L.rht ? 1 : 0], grid, dim3(64 * waves), att_lds, s, a);
     }
     // the splits' partials -> out, once every split has written its own
-    hipLaunchKernelGGL(k_att_combine, dim3((unsigned)np, (unsigned)L.group), dim3(CMB_THREADS), CMB_LDS, s, a);
+    hipLaunchKernelGGL(k_att_combine, dim3((unsigned)np), dim3(CMB_THREADS), CMB_LDS, s, a);
   }
   return hipGetLastError() != hipSuccess;
 }
