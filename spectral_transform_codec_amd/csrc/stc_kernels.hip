@@ -1582,6 +1582,13 @@ __device__ __forceinline__ float half_max(float x) {
   const unsigned r0 = r[0], r1 = r[1];  // (a bit cast of a vector element reads element 0)
   return fmaxf(__builtin_bit_cast(float, r0), __builtin_bit_cast(float, r1));
 }
+// Max over the 16 lanes of each row (DPP within the row).
+__device__ __forceinline__ float row16_max(float x) {
+  x = fmaxf(x, dpp_f<0xB1>(x));   // quad_perm [1,0,3,2]
+  x = fmaxf(x, dpp_f<0x4E>(x));   // quad_perm [2,3,0,1]
+  x = fmaxf(x, dpp_f<0x141>(x));  // row_half_mirror
+  return fmaxf(x, dpp_f<0x140>(x));  // row_mirror
+}
 __device__ __forceinline__ float half_sum(float x) {
   x += dpp_f<0xB1>(x);
   x += dpp_f<0x4E>(x);
@@ -2218,6 +2225,13 @@ __device__ __forceinline__ unsigned at2_tab_off(unsigned c, unsigned R2, unsigne
   const unsigned dw = c >> 5, hh = dw >= R2 ? 1u : 0u;
   return (dw - hh * R2 + hh * R2M) * 32u + ((c & 7u) >> 2) * 16u + (c & 3u) * 4u + ((c >> 3) & 3u);
 }
+// The same for the 16x16x64 layout of 256-bit records and groups up to 4:
+// word dw of a record is taken by k-block dw >> 1 at steps 2 (dw & 1) and
+// 2 (dw & 1) + 1 (its two operand halves); a row holds [step][k-block][16].
+__device__ __forceinline__ unsigned at2_tab_off16(unsigned c) {
+  const unsigned dw = c >> 5, kk = (c & 7u) >> 2;
+  return (2u * (dw & 1u) + kk) * 64u + (dw >> 1) * 16u + (c & 3u) * 4u + ((c >> 3) & 3u);
+}
 // position of token t of a block in the P / value-operand order: inside each
 // group of four tokens the order is 0, 2, 1, 3
 __device__ __forceinline__ int at2_pos(int t) { return (t & ~3) | ((t & 1) << 1) | ((t >> 1) & 1); }
@@ -2276,23 +2290,27 @@ __device__ __forceinline__ void at2_read(unsigned (&r)[R2M], const unsigned* buf
 // zeros and move no data. A stream of no bytes (or a request past a split's
 // end) passes plen 0.
 template <int NCH, bool SWZ>
-__device__ __forceinline__ unsigned at2_stage(const unsigned char* stream, long long blk, unsigned B, long long plen,
+__device__ __forceinline__ unsigned at2_stage(const unsigned char* stream, unsigned blk, unsigned B, unsigned plen,
                                               unsigned* buf, const unsigned (&rel)[NCH]) {
-  const long long start = blk * 4LL * (long long)B;
-  const long long base = start & ~15LL;
-  long long lim = plen - base;  // bytes past base that the lanes may read (uniform)
-  if (!SWZ && lim > start - base + 4LL * (long long)B) lim = start - base + 4LL * (long long)B;
+  // (streams of this kernel hold fewer than 2^31 bytes: 32-bit scalar arithmetic)
+  const unsigned start = blk * 4u * B;
+  const unsigned base = start & ~15u;
+  int lim = (int)plen - (int)base;  // bytes past base that the lanes may read (uniform)
+  if (!SWZ && lim > (int)(start - base + 4u * B)) lim = (int)(start - base + 4u * B);
   if (lim < 0) lim = 0;
-  if (lim > 1024LL * NCH) lim = 1024LL * NCH;  // (the loads reach no further)
+  if (lim > 1024 * NCH) lim = 1024 * NCH;  // (the loads reach no further)
 #if defined(__HIP_DEVICE_COMPILE__)  // (buffer resources exist in the device pass only)
-  const __amdgpu_buffer_rsrc_t rs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(stream + (lim > 0 ? base : 0)), (short)0, (int)lim, 0x00020000);
+  // (uniform by construction; readfirstlane keeps the resource in scalar registers)
+  const unsigned long long ad = (unsigned long long)(stream + (lim > 0 ? base : 0u));
+  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)ad), hi = __builtin_amdgcn_readfirstlane((unsigned)(ad >> 32));
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(((unsigned long long)hi << 32) | lo), (short)0, __builtin_amdgcn_readfirstlane(lim), 0x00020000);
 #pragma unroll
   for (int c = 0; c < NCH; ++c)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(buf + 256 * c), 16, rel[c],
                                              0, 0, 0);
 #endif
-  return (unsigned)(start - base) * 8u;
+  return (start - base) * 8u;
 }
 // Per-lane byte offsets of at2_stage's loads: 16 lane + 1024 c; for 256-bit
 // records (SWZ) slot lane of the block's chunks takes chunk 2 t + h + c
@@ -2383,7 +2401,8 @@ __global__ void __launch_bounds__(128 * PREP_PARTS) k_att2_prep(AttK a) {
 // value column table and the per-head scales, then the larger of the prologue
 // scratch, the W wave regions and the merge scratch.
 __host__ __device__ constexpr size_t at2_lds_bytes(int R2M, int NT, int NCH, int W, bool G4) {
-  const size_t fixed = (size_t)at2_trows(G4) * (64 * R2M + 16) + ATT_MAX_VCOLS * 8 + 8 * 4 + 128 * 4 + ATT_MAX_VCOLS * 4;
+  const size_t fixed =
+      (size_t)at2_trows(G4) * (64 * R2M + 16) + ATT_MAX_VCOLS * 8 + 8 * 4 + 128 * 4 + ATT_MAX_VCOLS * 4 + 16 * 4;
   const size_t pro = (size_t)8 * 128 * 4 + 2 * 64 * R2M + 8 * 4;
   const size_t vwords = (size_t)at2_vrow(R2M, 8 * R2M - 1) + 16;
   const size_t waves = (size_t)W * (2 * at2_nst(NCH) * 256 * NCH + vwords + 4 * AT2_PST / 2 + 16) * 4;
@@ -2400,7 +2419,12 @@ template <int R2M, int NT, int NCH, int W, bool SWZ, bool G4>
 __global__ void __launch_bounds__(64 * W, W == 4 ? 3 : 1) k_att2(AttK a) {
   static_assert(!SWZ || (R2M == 4 && NCH == 1), "256-bit records: four words per half, one load per block");
   extern __shared__ __align__(16) unsigned char smem[];
-  constexpr int NHL = G4 ? 2 : 4;              // heads per lane
+  // S16: 256-bit records and groups up to 4 take the scores from 16x16x64
+  // MFMAs (rows 4H + p: the four heads fill them), lane (c16, g4) holding
+  // head g4 for tokens c16 and 16 + c16; otherwise 32x32x32, lane (t32, h)
+  // holding heads 2i + h for token t32
+  constexpr bool S16 = SWZ && G4;
+  constexpr int NHL = G4 ? 2 : 4;              // score slots per lane
   constexpr int NH = G4 ? 4 : 8;               // heads of the weight table
   constexpr int TABW = 64 * R2M;               // bytes of a score-weight row (record bits <= 64 R2M)
   constexpr int TROW = TABW + 16;              // row stride: rows 4 banks apart, so 16 lanes' reads hit 64 banks
@@ -2416,7 +2440,8 @@ __global__ void __launch_bounds__(64 * W, W == 4 ? 3 : 1) k_att2(AttK a) {
   float* sInvS = reinterpret_cast<float*>(sVc + ATT_MAX_VCOLS);     // [8]
   unsigned* sVch = reinterpret_cast<unsigned*>(sInvS + 8);          // [128] channel: first column | count << 16
   float* sFac = reinterpret_cast<float*>(sVch + 128);                // [256] column scale 2^(24 - shift + offset)
-  unsigned* sReg0 = reinterpret_cast<unsigned*>(sFac + ATT_MAX_VCOLS);  // wave regions / prologue scratch
+  unsigned* sOnes = reinterpret_cast<unsigned*>(sFac + ATT_MAX_VCOLS);  // [16] fp16 pairs (1, 1): the sum column
+  unsigned* sReg0 = sOnes + 16;                                         // wave regions / prologue scratch
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -2471,6 +2496,7 @@ __global__ void __launch_bounds__(64 * W, W == 4 ? 3 : 1) k_att2(AttK a) {
       sVc[tid] = e;
       sFac[tid] = tid < ncols ? vc[tid].fac : 0.0f;
       if (tid < 128) sVch[tid] = reinterpret_cast<const unsigned*>(vst + OFF_ATTVCH)[tid];
+      if (tid < 16) sOnes[tid] = 0x3C003C00u;
     }
     __syncthreads();
     // int8 parts of round(S_h a_j 2^(k - (c & 3))): rows 3h + p
@@ -2485,7 +2511,7 @@ __global__ void __launch_bounds__(64 * W, W == 4 ? 3 : 1) k_att2(AttK a) {
         const int r1 = (A - a2) >> 7;
         const int a1 = ((r1 + 64) & 127) - 64;
         const int a0 = (r1 - a1) >> 7;
-        const unsigned o = at2_tab_off((unsigned)c, (unsigned)R2k, (unsigned)R2M);
+        const unsigned o = S16 ? at2_tab_off16((unsigned)c) : at2_tab_off((unsigned)c, (unsigned)R2k, (unsigned)R2M);
         sA[(3 * hh) * TROW + o] = (signed char)a0;
         sA[(3 * hh + 1) * TROW + o] = (signed char)a1;
         sA[(3 * hh + 2) * TROW + o] = (signed char)a2;
@@ -2502,51 +2528,54 @@ __global__ void __launch_bounds__(64 * W, W == 4 ? 3 : 1) k_att2(AttK a) {
   for (int i = lane; i < 4 * AT2_PST / 2; i += 64) reinterpret_cast<unsigned*>(sP)[i] = 0u;
   if (lane < 16) sAl[lane] = 1.0f;
   // per head of the lane (H = 2i + h): running max, its threshold of the
-  // fast path in unscaled score units, the scales, the running sum
-  float mold[NHL], thr[NHL], invS[NHL], Ssc[NHL], l_run[NHL];
+  // fast path in unscaled score units, the scales. (The running sum of P is
+  // the value column ncols, whose operand is fp16 1 for every token.)
+  float mold[NHL], thr[NHL], invS[NHL];
   bool hval[NHL];
 #pragma unroll
   for (int i = 0; i < NHL; ++i) {
-    const int H = 2 * i + h;
+    const int H = S16 ? g4 : 2 * i + h;
     invS[i] = sInvS[H];
-    Ssc[i] = 1.0f / invS[i];  // (a power of two)
     mold[i] = -INFINITY;
     thr[i] = -INFINITY;
-    l_run[i] = 0.0f;
     hval[i] = H < g;
   }
   f32x4 acc_v[NT];
 #pragma unroll
   for (int T = 0; T < NT; ++T) acc_v[T] = (f32x4){0.f, 0.f, 0.f, 0.f};
   // value columns of this lane: LDS address of the four words it reads and
-  // the fragment mask (columns past the state's have mask 0)
+  // the fragment mask (columns past the state's have mask 0; column ncols
+  // reads the ones)
   unsigned vaddr[NT], vmask[NT];
   {
     const unsigned vb0 = lds_offset(reinterpret_cast<unsigned char*>(sV));
+    const unsigned ones = lds_offset(reinterpret_cast<unsigned char*>(sOnes));
 #pragma unroll
     for (int T = 0; T < NT; ++T) {
       const u32x2 cm = sVc[16 * T + c16];
-      vaddr[T] = vb0 + 4u * (cm[0] + 4u * (unsigned)g4);
-      vmask[T] = cm[1];
+      const bool sumcol = 16 * T + c16 == ncols;
+      vaddr[T] = sumcol ? ones + 16u * (unsigned)g4 : vb0 + 4u * (cm[0] + 4u * (unsigned)g4);
+      vmask[T] = sumcol ? 0xFFFFFFFFu : cm[1];
       asm volatile("" : "+v"(vaddr[T]), "+v"(vmask[T]));
     }
   }
-  const long long PkL = packed_len((long long)Bk, n), PvL = packed_len((long long)Bv, n);
-  // (a stream of no bytes stages from its state instead, which is never read)
-  const unsigned char* gk = PkL > 0 ? a.k_packed + pg * a.packed_stride : kst;
-  const unsigned char* gv = PvL > 0 ? a.v_packed + pg * a.packed_stride : vst;
+  const unsigned PkL = (unsigned)packed_len((long long)Bk, n), PvL = (unsigned)packed_len((long long)Bv, n);
+  const unsigned char* gk = a.k_packed + pg * a.packed_stride;
+  const unsigned char* gv = a.v_packed + pg * a.packed_stride;
   const int e4 = t32 & 3;
   const unsigned sel1 = (e4 & 1) ? 0x03070105u : 0x06020400u;
   const unsigned sel_e = (e4 & 2) ? 0x0C020C06u : 0x0C040C00u;
   const unsigned sel_o = (e4 & 2) ? 0x0C030C07u : 0x0C050C01u;
   const unsigned pos = (unsigned)at2_pos(t32);
   bool resc = false;  // (uniform) a rescale of the value accumulators is pending
-  // the wave's blocks: tok0 = t_begin + 32 (wave + W k). The records of the
-  // next NST - 1 blocks are requested (straight to LDS) before the current
-  // one is processed; past the split's end the requests are of the stream's
-  // first 16 bytes (never read), so that every step issues 2 NCH loads
-  const long long stride = (long long)W * AT2_BT;
-  long long tok0 = t_begin + (long long)wave * AT2_BT;
+  // the wave's blocks: tok0 = t_begin + 32 (wave + W k) (token counts below
+  // 2^31: 32-bit scalar arithmetic). The records of the next NST - 1 blocks
+  // are requested (straight to LDS) before the current one is processed;
+  // past the split's end the requests are of nothing (plen 0), so that every
+  // step issues 2 NCH loads
+  const int stride = W * AT2_BT;
+  const int tend = (int)t_end;
+  int tok0 = (int)t_begin + wave * AT2_BT;
   unsigned offk[NST], offv[NST];
   unsigned srel[NCH];
   at2_stage_rel<NCH, SWZ>(srel, lane);
@@ -2554,29 +2583,30 @@ __global__ void __launch_bounds__(64 * W, W == 4 ? 3 : 1) k_att2(AttK a) {
   __builtin_amdgcn_wave_barrier();
 #pragma unroll
   for (int st = 0; st < NST - 1; ++st) {
-    const long long tb = tok0 + st * stride;
-    const bool real = tb < t_end;
+    const int tb = tok0 + st * stride;
+    const bool real = tb < tend;
     unsigned* buf = sStage + st * 2 * SWORDS;
-    offk[st] = at2_stage<NCH, SWZ>(gk, real ? tb / AT2_BT : 0, Bk, real ? PkL : 0, buf, srel);
-    offv[st] = at2_stage<NCH, SWZ>(gv, real ? tb / AT2_BT : 0, Bv, real ? PvL : 0, buf + SWORDS, srel);
+    offk[st] = at2_stage<NCH, SWZ>(gk, real ? (unsigned)tb / AT2_BT : 0u, Bk, real ? PkL : 0u, buf, srel);
+    offv[st] = at2_stage<NCH, SWZ>(gv, real ? (unsigned)tb / AT2_BT : 0u, Bv, real ? PvL : 0u, buf + SWORDS, srel);
   }
   int cur = 0;  // ring stage of the current block
-  for (; tok0 < t_end; tok0 += stride) {
+  for (; tok0 < tend; tok0 += stride) {
     {
-      const long long tb = tok0 + (NST - 1) * stride;
-      const bool real = tb < t_end;
+      const int tb = tok0 + (NST - 1) * stride;
+      const bool real = tb < tend;
       unsigned* buf = sStage + (cur == 0 ? NST - 1 : cur - 1) * 2 * SWORDS;
-      offk[NST - 1] = at2_stage<NCH, SWZ>(gk, real ? tb / AT2_BT : 0, Bk, real ? PkL : 0, buf, srel);
-      offv[NST - 1] = at2_stage<NCH, SWZ>(gv, real ? tb / AT2_BT : 0, Bv, real ? PvL : 0, buf + SWORDS, srel);
+      offk[NST - 1] = at2_stage<NCH, SWZ>(gk, real ? (unsigned)tb / AT2_BT : 0u, Bk, real ? PkL : 0u, buf, srel);
+      offv[NST - 1] =
+          at2_stage<NCH, SWZ>(gv, real ? (unsigned)tb / AT2_BT : 0u, Bv, real ? PvL : 0u, buf + SWORDS, srel);
     }
     // the current block's loads are done once at most the later blocks' remain
     __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * NCH * (NST - 1)));  // vmcnt(2 NCH (NST - 1))
     __builtin_amdgcn_wave_barrier();
-    const bool tok_ok = tok0 + t32 < t_end;
+    const bool tail = tok0 + AT2_BT > tend;  // (uniform) the split ends inside this block
     unsigned rk[R2M], rv[R2M];
     const unsigned* bk = sStage + cur * 2 * SWORDS;
     at2_read<R2M, SWZ>(rv, bk + SWORDS, offv[0], Bv, R2v, t32, h);
-    at2_read<R2M, SWZ>(rk, bk, offk[0], Bk, R2k, t32, h);
+    if constexpr (!S16) at2_read<R2M, SWZ>(rk, bk, offk[0], Bk, R2k, t32, h);
 #pragma unroll
     for (int st = 0; st < NST - 1; ++st) {
       offk[st] = offk[st + 1];
@@ -2591,10 +2621,36 @@ __global__ void __launch_bounds__(64 * W, W == 4 ? 3 : 1) k_att2(AttK a) {
       *reinterpret_cast<u32x2*>(sV + at2_vrow(R2M, row) + 2 * (t32 >> 2)) = y;
     }
     // ---- scores: int8 MFMAs, A = weights (rows 4H + p), B = the record bits
-    i32x16 acc;
+    float su[NHL];  // unscaled scores of the lane's slots (-inf past the split)
+    if constexpr (S16) {
+      const int trow = ((c16 & 3) == 3 || (c16 >> 2) >= NH) ? 3 * NH : 3 * (c16 >> 2) + (c16 & 3);
+      unsigned ab = lds_offset(reinterpret_cast<unsigned char*>(sA) + trow * TROW + g4 * 16);
+      asm volatile("" : "+v"(ab));
+      const lds_u8* aL = lds_ptr(ab);
+      u32x4 av[4];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) acc[e] = 0;
-    {
+      for (int st = 0; st < 4; ++st) av[st] = LDS_AT(u32x4, aL + 64 * st);
+      // token 16 G + c16: words 2 g4, 2 g4 + 1 of its record (chunk g4 >> 1,
+      // staged at slot token + 32 (g4 >> 1))
+      u32x2 kw[2];
+#pragma unroll
+      for (int G = 0; G < 2; ++G)
+        kw[G] = *reinterpret_cast<const u32x2*>(bk + 4 * (16 * G + c16 + 32 * (g4 >> 1)) + 2 * (g4 & 1));
+#pragma unroll
+      for (int G = 0; G < 2; ++G) {
+        i32x4 a16 = (i32x4){0, 0, 0, 0};
+#pragma unroll
+        for (int st = 0; st < 4; ++st)
+          a16 = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, av[st]),
+                                                      __builtin_bit_cast(i32x4, at2_bits(kw[G][st >> 1], st & 1)), a16,
+                                                      0, 0, 0);
+        su[G] = __builtin_fmaf((float)((a16[0] << 7) + a16[1]), 128.0f, (float)a16[2]);
+        if (tail && tok0 + 16 * G + c16 >= tend) su[G] = -INFINITY;
+      }
+    } else {
+      i32x16 acc;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[e] = 0;
       // lane row t32 = 4H + p of the MFMA holds part p of head H: table row
       // 3H + p, or the zero row for p = 3 and heads past the table
       const int trow = ((t32 & 3) == 3 || (t32 >> 2) >= NH) ? 3 * NH : 3 * (t32 >> 2) + (t32 & 3);
@@ -2613,39 +2669,44 @@ __global__ void __launch_bounds__(64 * W, W == 4 ? 3 : 1) k_att2(AttK a) {
           acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4, av[2 * i + kk]),
                                                       __builtin_bit_cast(i32x4, at2_bits(rk[i], kk)), acc, 0, 0, 0);
       }
+#pragma unroll
+      for (int i = 0; i < NHL; ++i) {
+        su[i] = __builtin_fmaf((float)((acc[4 * i] << 7) + acc[4 * i + 1]), 128.0f, (float)acc[4 * i + 2]);
+        if (tail && tok0 + t32 >= tend) su[i] = -INFINITY;
+      }
     }
-    // unscaled scores of the lane's heads (-inf past the split)
-    float su[NHL];
     bool slow = false;
 #pragma unroll
-    for (int i = 0; i < NHL; ++i) {
-      const float s = __builtin_fmaf((float)((acc[4 * i] << 7) + acc[4 * i + 1]), 128.0f, (float)acc[4 * i + 2]);
-      su[i] = tok_ok ? s : -INFINITY;
-      slow |= hval[i] && !(su[i] <= thr[i]);
-    }
-    // ---- online softmax; P (fp16) -> sP[octet][head][8]
-    if (!__any(slow)) {
+    for (int i = 0; i < NHL; ++i) slow |= hval[i] && !(su[i] <= thr[i]);
+    // ---- online softmax. A score above its head's max + 8 (log2 units)
+    // raises the max first (rare once the max has settled): alpha =
+    // 2^(m_old - m_new) rescales the value accumulators before P x V.
+    if (__any(slow)) {
+      float mx16 = 0.0f;
+      if constexpr (S16) mx16 = row16_max(fmaxf(su[0], su[1]) * invS[0]);
 #pragma unroll
       for (int i = 0; i < NHL; ++i) {
-        const _Float16 ph = (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(su[i], invS[i], -mold[i]));
-        l_run[i] += (float)ph;
-        sP[(pos >> 3) * AT2_PST + (2 * i + h) * 8 + (pos & 7)] = ph;
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < NHL; ++i) {
-        const float s = su[i] * invS[i];
-        const float mnew = fmaxf(mold[i], half_max(s));
-        const float alpha = (mnew == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(mold[i] - mnew);
-        const float pv = (mnew == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(s - mnew);
-        const _Float16 ph = (_Float16)pv;
-        l_run[i] = l_run[i] * alpha + (float)ph;
-        mold[i] = mnew;
-        thr[i] = (mnew + 8.0f) * Ssc[i];
-        sP[(pos >> 3) * AT2_PST + (2 * i + h) * 8 + (pos & 7)] = ph;
-        if (t32 == 0) sAl[2 * i + h] = alpha;
+        const float mx = S16 ? mx16 : half_max(su[i] * invS[i]);
+        const float mnew = fmaxf(mold[i], mx);
+        // (no token of the head so far: max 0, every P and sum so far 0)
+        const float mset = mnew == -INFINITY ? 0.0f : mnew;
+        const float alpha = mold[i] == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(mold[i] - mset);
+        mold[i] = mset;
+        thr[i] = (mset + 8.0f) / invS[i];
+        if (S16 ? (c16 == 0 && i == 0) : t32 == 0) sAl[S16 ? g4 : 2 * i + h] = alpha;
       }
       resc = true;
+    }
+    // P (fp16) -> sP[octet][head][8]
+#pragma unroll
+    for (int i = 0; i < NHL; ++i) {
+      const _Float16 ph = (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(su[i], invS[i], -mold[i]));
+      if constexpr (S16) {
+        const unsigned ps = (unsigned)at2_pos(16 * i + c16);
+        sP[(ps >> 3) * AT2_PST + g4 * 8 + (ps & 7)] = ph;
+      } else {
+        sP[(pos >> 3) * AT2_PST + (2 * i + h) * 8 + (pos & 7)] = ph;
+      }
     }
     __builtin_amdgcn_s_waitcnt(0xc07f);  // the wave's value rows, P and alpha are in LDS
     __builtin_amdgcn_wave_barrier();
@@ -2676,23 +2737,20 @@ __global__ void __launch_bounds__(64 * W, W == 4 ? 3 : 1) k_att2(AttK a) {
     __builtin_amdgcn_wave_barrier();
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the requests past the end have landed before LDS is reused
-  // ---- l over the half's tokens
-#pragma unroll
-  for (int i = 0; i < NHL; ++i) l_run[i] = half_sum(l_run[i]);
   // ---- merge the waves: scratch [wave][8 heads][CST]
   constexpr int CST = 16 * NT + 4;
   __syncthreads();
   float* red = reinterpret_cast<float*>(sReg0);
   float* part = reinterpret_cast<float*>(a.ws) + (p * a.n_splits + sp) * att_part_stride(g);
-  const bool cols_ok = ncols <= 16 * NT;  // (the launch chose NT from the states' column counts)
+  const bool cols_ok = ncols < 16 * NT;  // (the launch chose NT from the states' column counts, plus the sum column)
   {
     float* mine = red + wave * 8 * CST;
 #pragma unroll
     for (int i = 0; i < NHL; ++i) {
-      const int H = 2 * i + h;
-      if (t32 == 0) {
-        mine[H * CST + 16 * NT] = mold[i];
-        mine[H * CST + 16 * NT + 1] = l_run[i];
+      if constexpr (S16) {
+        if (c16 == 0 && i == 0) mine[g4 * CST + 16 * NT] = mold[0];
+      } else {
+        if (t32 == 0) mine[(2 * i + h) * CST + 16 * NT] = mold[i];
       }
     }
     if (g4 < 2) {
@@ -2720,7 +2778,7 @@ __global__ void __launch_bounds__(64 * W, W == 4 ? 3 : 1) k_att2(AttK a) {
       for (int k = 0; k < nc; ++k)
         if (c0 + k < 16 * NT) v += sFac[c0 + k] * rw[c0 + k];
       A += f * v;
-      Ls += f * rw[16 * NT + 1];
+      Ls += f * rw[ncols];  // (the sum column)
     }
     float* ph = part + hh * ATT_PART_FLOATS;
     ph[jj] = cols_ok ? A : __builtin_nanf("");
@@ -2836,16 +2894,19 @@ int launch_attend(const AttendLaunch& L, void* stream) {
     a.n_splits = att_n_splits(np, L.n_tokens);
     const size_t att_lds = fixed + (size_t)waves * a.region_words * 4;
     const dim3 grid((unsigned)a.n_splits, (unsigned)np);
-    if (!sketch && !L.rht && L.group <= 8 && L.max_bits <= 512 && L.max_vcols <= 192) {
+    // (k_att2: value columns plus the sum column fit the tiles; token counts
+    // and stream bytes below 2^31 for its 32-bit arithmetic)
+    const bool small = L.n_tokens < (1LL << 30) && L.n_tokens * (long long)L.max_bits / 8 < (1LL << 31) - 65536;
+    if (!sketch && !L.rht && L.group <= 8 && L.max_bits <= 512 && L.max_vcols <= 191 && small) {
       const bool g4 = L.group <= 4;
       a.prep = reinterpret_cast<float*>(a.ws) + att_partial_floats(np, L.n_tokens, L.group);
       hipLaunchKernelGGL(k_att2_prep, dim3((unsigned)np), dim3(128 * PREP_PARTS), 0, s, a);
       if (L.max_bits <= 256 && L.att_chunks <= 1) {
         if (L.rec256)
           g4 ? at2_launch<4, 10, 1, 4, true, true>(grid, s, a) : at2_launch<4, 10, 1, 4, true, false>(grid, s, a);
-        else if (!g4 && L.max_vcols <= 128 && L.max_bits <= 192)
+        else if (!g4 && L.max_vcols <= 127 && L.max_bits <= 192)
           at2_launch<3, 8, 1, 4, false, false>(grid, s, a);
-        else if (!g4 && L.max_vcols <= 128)
+        else if (!g4 && L.max_vcols <= 127)
           at2_launch<4, 8, 1, 4, false, false>(grid, s, a);
         else
           g4 ? at2_launch<4, 10, 1, 4, false, true>(grid, s, a) : at2_launch<4, 10, 1, 4, false, false>(grid, s, a);

@@ -13,8 +13,8 @@ import numpy as np
 CASES = [
     (5, 2.0, 7, 2500, None),    # 256-bit records, group 7
     (1, 2.0, 4, 2500, None),    # 256-bit records, group 4
-    (5, 1.33, 7, 2500, None),   # 170-bit records, at most 128 columns, group 7: three-word halves
-    (5, 1.6, 7, 2500, None),    # 205-bit records, more than 128 columns, group 7
+    (5, 1.33, 7, 2500, None),   # 170-bit records, at most 127 columns, group 7: three-word halves
+    (5, 1.6, 7, 2500, None),    # 205-bit records, more than 127 columns, group 7
     (5, 1.9, 8, 2500, None),    # 243-bit records, group 8
     (2, 1.2, 3, 2500, None),    # 154-bit records, group 3
     (2, 3.0, 4, 1500, None),    # 384-bit records: halves of up to 8 words, three loads per block
@@ -52,15 +52,15 @@ def instance(total_bits_list, bits_list, group):
     mv = max(value_columns(b) for b in bits_list)
     chunks = max(-(-((4 * t) + (12 if (4 * t) % 16 else 0)) // 1024) for t in total_bits_list)
     chunks = max(chunks, 1)
-    if group > 8 or mb > 512 or mv > 192:
+    if group > 8 or mb > 512 or mv > 191:
         return None
     g4 = group <= 4
     if mb <= 256 and chunks <= 1:
         if all(t == 256 for t in total_bits_list):
             return (4, 10, 1, 4, True, g4)
-        if not g4 and mv <= 128 and mb <= 192:
+        if not g4 and mv <= 127 and mb <= 192:
             return (3, 8, 1, 4, False, False)
-        if not g4 and mv <= 128:
+        if not g4 and mv <= 127:
             return (4, 8, 1, 4, False, False)
         return (4, 10, 1, 4, False, g4)
     if mb <= 256:
