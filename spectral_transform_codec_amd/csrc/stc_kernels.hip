@@ -2204,10 +2204,11 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) k_att_main(AttK a) {
 constexpr int AT2_PST = 136;  // fp16 per token octet of P ([octet][16 heads][8] + 8 pad: octets 4 banks apart)
 constexpr int AT2_BT = 32;    // tokens per wave block
 // Word offset of value row r ([quad][tokens 0,2 | 1,3], 16 words). For records
-// of at most 256 bits, 24 r + 12 (r >> 2) + 8 (r >> 3): the 16-byte reads of
-// any 16 consecutive rows fall in 16 different 4-bank groups of the 64, and
-// the 8-byte writes of four rows by 16 lanes in 32 different banks (LDS
-// writes go 32 banks at a time); longer records: 16 r, to fit the LDS.
+// of at most 256 bits, 24 r + 12 (r >> 2) + 8 (r >> 3): the 8-byte writes of
+// four rows by 16 lanes fall in 32 different banks and the 16-byte reads of
+// consecutive rows spread over the 64 (this layout measured faster than
+// octet-major rows, whose writes conflict); longer records: 16 r, to fit the
+// LDS.
 __host__ __device__ constexpr unsigned at2_vrow(int R2M, unsigned r) {
   return R2M <= 4 ? 24u * r + 12u * (r >> 2) + 8u * (r >> 3) : 16u * r;
 }
@@ -2253,16 +2254,30 @@ __device__ __forceinline__ u32x2 at2_quad_split(unsigned x, unsigned sel1, unsig
   return (u32x2){__builtin_amdgcn_perm(p2, y, sel_e), __builtin_amdgcn_perm(p2, y, sel_o)};
 }
 
+// Staging modes: AT2_GEN, the block's bytes from the 16-byte boundary at or
+// below its start, in order; AT2_SWZ (256-bit records), chunk q of half h of
+// token t at slot t + 32 h + 64 q; AT2_DIRECT (half records of at most 96
+// bits), slot t + 32 h holds the 16 bytes from the word that holds the first
+// bit of half h of token t.
+constexpr int AT2_GEN = 0, AT2_SWZ = 1, AT2_DIRECT = 2;
 // A lane's half record from a wave's staging buffer: R2 words from record bit
-// 32 R2 h of token t, the block's records starting at bit `off` of the buffer,
-// realigned to bit 0. SWZ: records of 256 bits staged by at2_stage<.., true>
-// (16-byte chunk q of half h of token t at chunk t + 32 h + 64 q); otherwise
-// R2M + 1 words funnel-shifted. Words past the half record hold other bits,
-// which meet zero weights and columns that never read them.
-template <int R2M, bool SWZ>
+// 32 R2 h of token t, realigned to bit 0 (AT2_GEN: the block's records start
+// at bit `off` of the buffer; AT2_DIRECT: off is the lane's bit shift). Words
+// past the half record hold other bits, which meet zero weights and columns
+// that never read them.
+template <int R2M, int MODE>
 __device__ __forceinline__ void at2_read(unsigned (&r)[R2M], const unsigned* buf, unsigned off, unsigned B, int R2,
                                          int t, int h) {
-  if (SWZ) {
+  if (MODE == AT2_DIRECT) {
+    // slot t + 32 h holds the 16 bytes from the word that holds the half
+    // record's first bit; off is that bit's position in the word
+    const u32x4 v = *reinterpret_cast<const u32x4*>(buf + 4 * (t + 32 * h));
+    const unsigned x[4] = {v[0], v[1], v[2], v[3]};
+#pragma unroll
+    for (int j = 0; j < R2M; ++j) r[j] = __builtin_amdgcn_alignbit(x[j + 1], x[j], off);
+    return;
+  }
+  if (MODE == AT2_SWZ) {
 #pragma unroll
     for (int j = 0; j < R2M; j += 4) {
       const u32x4 v = *reinterpret_cast<const u32x4*>(buf + 4 * (t + 32 * h + 64 * (j >> 2)));
@@ -2289,16 +2304,19 @@ __device__ __forceinline__ void at2_read(unsigned (&r)[R2M], const unsigned* buf
 // at the block's end) and at the stream's plen bytes: lanes past it read
 // zeros and move no data. A stream of no bytes (or a request past a split's
 // end) passes plen 0.
-template <int NCH, bool SWZ>
+template <int NCH, int MODE>
 __device__ __forceinline__ unsigned at2_stage(const unsigned char* stream, unsigned blk, unsigned B, unsigned plen,
                                               unsigned* buf, const unsigned (&rel)[NCH]) {
   // (streams of this kernel hold fewer than 2^31 bytes: 32-bit scalar arithmetic)
   const unsigned start = blk * 4u * B;
-  const unsigned base = start & ~15u;
+  // AT2_DIRECT: the resource starts at the block (4-byte aligned) and reaches
+  // 16 bytes past it (the lanes' 16-byte windows), or the stream's end
+  const unsigned base = MODE == AT2_DIRECT ? start : start & ~15u;
   int lim = (int)plen - (int)base;  // bytes past base that the lanes may read (uniform)
-  if (!SWZ && lim > (int)(start - base + 4u * B)) lim = (int)(start - base + 4u * B);
+  if (MODE == AT2_GEN && lim > (int)(start - base + 4u * B)) lim = (int)(start - base + 4u * B);
+  if (MODE == AT2_DIRECT && lim > (int)(4u * B + 16u)) lim = (int)(4u * B + 16u);
   if (lim < 0) lim = 0;
-  if (lim > 1024 * NCH) lim = 1024 * NCH;  // (the loads reach no further)
+  if (lim > 1024 * NCH + 16) lim = 1024 * NCH + 16;  // (the loads reach no further)
 #if defined(__HIP_DEVICE_COMPILE__)  // (buffer resources exist in the device pass only)
   // (uniform by construction; readfirstlane keeps the resource in scalar registers)
   const unsigned long long ad = (unsigned long long)(stream + (lim > 0 ? base : 0u));
@@ -2312,16 +2330,22 @@ __device__ __forceinline__ unsigned at2_stage(const unsigned char* stream, unsig
 #endif
   return (start - base) * 8u;
 }
-// Per-lane byte offsets of at2_stage's loads: 16 lane + 1024 c; for 256-bit
-// records (SWZ) slot lane of the block's chunks takes chunk 2 t + h + c
-// (t = lane & 31, h = lane >> 5), so that the 16-byte reads of 16
-// consecutive lanes cover 64 banks (in block order they would pair up).
-template <int NCH, bool SWZ>
-__device__ __forceinline__ void at2_stage_rel(unsigned (&rel)[NCH], int lane) {
+// Per-lane byte offsets of at2_stage's loads: AT2_GEN, 16 lane + 1024 c;
+// AT2_SWZ, slot lane takes chunk 2 t + h + c (t = lane & 31, h = lane >> 5),
+// so that the 16-byte reads of 16 consecutive lanes cover 64 banks (in block
+// order they would pair up); AT2_DIRECT, the word that holds bit t B + 32 R2 h
+// (sh: that bit's position in the word).
+template <int NCH, int MODE>
+__device__ __forceinline__ void at2_stage_rel(unsigned (&rel)[NCH], unsigned& sh, int lane, unsigned B, int R2) {
+  const unsigned P = (unsigned)(lane & 31) * B + 32u * (unsigned)R2 * (unsigned)(lane >> 5);
+  sh = P & 31u;
 #pragma unroll
   for (int c = 0; c < NCH; ++c)
-    rel[c] = SWZ ? 16u * (unsigned)(2 * (lane & 31) + (lane >> 5) + c) : 1024u * c + 16u * (unsigned)lane;
+    rel[c] = MODE == AT2_SWZ      ? 16u * (unsigned)(2 * (lane & 31) + (lane >> 5) + c)
+             : MODE == AT2_DIRECT ? 4u * (P >> 5)
+                                  : 1024u * c + 16u * (unsigned)lane;
 }
+
 
 // Score weights of the packed-bit kernel, once per pair (its splits share
 // them): a_j = (U_K^T q)_j step_j scale log2(e) for the group's heads (0 for
@@ -2424,6 +2448,7 @@ __global__ void __launch_bounds__(64 * W, W == 4 ? 3 : 1) k_att2(AttK a) {
   // head g4 for tokens c16 and 16 + c16; otherwise 32x32x32, lane (t32, h)
   // holding heads 2i + h for token t32
   constexpr bool S16 = SWZ && G4;
+  constexpr int MODE = SWZ ? AT2_SWZ : (R2M <= 3 && NCH == 1 ? AT2_DIRECT : AT2_GEN);
   constexpr int NHL = G4 ? 2 : 4;              // score slots per lane
   constexpr int NH = G4 ? 4 : 8;               // heads of the weight table
   constexpr int TABW = 64 * R2M;               // bytes of a score-weight row (record bits <= 64 R2M)
@@ -2577,8 +2602,9 @@ __global__ void __launch_bounds__(64 * W, W == 4 ? 3 : 1) k_att2(AttK a) {
   const int tend = (int)t_end;
   int tok0 = (int)t_begin + wave * AT2_BT;
   unsigned offk[NST], offv[NST];
-  unsigned srel[NCH];
-  at2_stage_rel<NCH, SWZ>(srel, lane);
+  unsigned krel[NCH], vrel[NCH], ksh, vsh;
+  at2_stage_rel<NCH, MODE>(krel, ksh, lane, Bk, R2k);
+  at2_stage_rel<NCH, MODE>(vrel, vsh, lane, Bv, R2v);
   __builtin_amdgcn_s_waitcnt(0xc07f);
   __builtin_amdgcn_wave_barrier();
 #pragma unroll
@@ -2586,8 +2612,8 @@ __global__ void __launch_bounds__(64 * W, W == 4 ? 3 : 1) k_att2(AttK a) {
     const int tb = tok0 + st * stride;
     const bool real = tb < tend;
     unsigned* buf = sStage + st * 2 * SWORDS;
-    offk[st] = at2_stage<NCH, SWZ>(gk, real ? (unsigned)tb / AT2_BT : 0u, Bk, real ? PkL : 0u, buf, srel);
-    offv[st] = at2_stage<NCH, SWZ>(gv, real ? (unsigned)tb / AT2_BT : 0u, Bv, real ? PvL : 0u, buf + SWORDS, srel);
+    offk[st] = at2_stage<NCH, MODE>(gk, real ? (unsigned)tb / AT2_BT : 0u, Bk, real ? PkL : 0u, buf, krel);
+    offv[st] = at2_stage<NCH, MODE>(gv, real ? (unsigned)tb / AT2_BT : 0u, Bv, real ? PvL : 0u, buf + SWORDS, vrel);
   }
   int cur = 0;  // ring stage of the current block
   for (; tok0 < tend; tok0 += stride) {
@@ -2595,9 +2621,9 @@ __global__ void __launch_bounds__(64 * W, W == 4 ? 3 : 1) k_att2(AttK a) {
       const int tb = tok0 + (NST - 1) * stride;
       const bool real = tb < tend;
       unsigned* buf = sStage + (cur == 0 ? NST - 1 : cur - 1) * 2 * SWORDS;
-      offk[NST - 1] = at2_stage<NCH, SWZ>(gk, real ? (unsigned)tb / AT2_BT : 0u, Bk, real ? PkL : 0u, buf, srel);
+      offk[NST - 1] = at2_stage<NCH, MODE>(gk, real ? (unsigned)tb / AT2_BT : 0u, Bk, real ? PkL : 0u, buf, krel);
       offv[NST - 1] =
-          at2_stage<NCH, SWZ>(gv, real ? (unsigned)tb / AT2_BT : 0u, Bv, real ? PvL : 0u, buf + SWORDS, srel);
+          at2_stage<NCH, MODE>(gv, real ? (unsigned)tb / AT2_BT : 0u, Bv, real ? PvL : 0u, buf + SWORDS, vrel);
     }
     // the current block's loads are done once at most the later blocks' remain
     __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * NCH * (NST - 1)));  // vmcnt(2 NCH (NST - 1))
@@ -2605,8 +2631,8 @@ __global__ void __launch_bounds__(64 * W, W == 4 ? 3 : 1) k_att2(AttK a) {
     const bool tail = tok0 + AT2_BT > tend;  // (uniform) the split ends inside this block
     unsigned rk[R2M], rv[R2M];
     const unsigned* bk = sStage + cur * 2 * SWORDS;
-    at2_read<R2M, SWZ>(rv, bk + SWORDS, offv[0], Bv, R2v, t32, h);
-    if constexpr (!S16) at2_read<R2M, SWZ>(rk, bk, offk[0], Bk, R2k, t32, h);
+    at2_read<R2M, MODE>(rv, bk + SWORDS, MODE == AT2_DIRECT ? vsh : offv[0], Bv, R2v, t32, h);
+    if constexpr (!S16) at2_read<R2M, MODE>(rk, bk, MODE == AT2_DIRECT ? ksh : offk[0], Bk, R2k, t32, h);
 #pragma unroll
     for (int st = 0; st < NST - 1; ++st) {
       offk[st] = offk[st + 1];
@@ -2633,9 +2659,15 @@ __global__ void __launch_bounds__(64 * W, W == 4 ? 3 : 1) k_att2(AttK a) {
       // token 16 G + c16: words 2 g4, 2 g4 + 1 of its record (chunk g4 >> 1,
       // staged at slot token + 32 (g4 >> 1))
       u32x2 kw[2];
-#pragma unroll
-      for (int G = 0; G < 2; ++G)
-        kw[G] = *reinterpret_cast<const u32x2*>(bk + 4 * (16 * G + c16 + 32 * (g4 >> 1)) + 2 * (g4 & 1));
+      {
+        unsigned ka = lds_offset(reinterpret_cast<unsigned char*>(const_cast<unsigned*>(bk))) +
+                      4u * (4u * (unsigned)(c16 + 32 * (g4 >> 1)) + 2u * (unsigned)(g4 & 1));
+        kw[0] = LDS_AT(u32x2, lds_ptr(ka));
+        // (an opaque address: the two 8-byte reads stay separate; merged
+        // into one two-address read they would conflict)
+        asm volatile("" : "+v"(ka));
+        kw[1] = LDS_AT(u32x2, lds_ptr(ka + 256u));
+      }
 #pragma unroll
       for (int G = 0; G < 2; ++G) {
         i32x4 a16 = (i32x4){0, 0, 0, 0};
