@@ -115,11 +115,13 @@ inline size_t packed_bytes(int64_t total_bits, int64_t n) {
 // Attention split geometry (tokens per workgroup) as a function of the call's
 // shape; shared by the workspace-size query and the launcher.
 constexpr int ATT_TILE = 256;
-inline int64_t att_split_tokens(int64_t n_pairs, int64_t n_tokens) {
-  // at least one round of 768 workgroups (three per CU); among up to twice
-  // the fewest splits per pair, the count that fills the last round best; a
-  // pair has at most one split per tile
-  const int64_t round = 768;
+// `round`: workgroups resident at once (256 CUs times the kernel's workgroups
+// per CU); the workspace covers every kernel's split count (ATT_ROUNDS).
+constexpr int64_t ATT_ROUNDS[2] = {768, 1024};
+inline int64_t att_split_tokens(int64_t n_pairs, int64_t n_tokens, int64_t round) {
+  // at least one round of workgroups; among up to twice the fewest splits
+  // per pair, the count that fills the last round best; a pair has at most
+  // one split per tile
   const int64_t tiles = (n_tokens + ATT_TILE - 1) / ATT_TILE;
   int64_t s0 = (round + n_pairs - 1) / n_pairs;
   if (s0 > tiles) s0 = tiles;
@@ -137,8 +139,8 @@ inline int64_t att_split_tokens(int64_t n_pairs, int64_t n_tokens) {
   const int64_t per = (tiles + best - 1) / best;
   return per * ATT_TILE;
 }
-inline int64_t att_n_splits(int64_t n_pairs, int64_t n_tokens) {
-  int64_t s = att_split_tokens(n_pairs, n_tokens);
+inline int64_t att_n_splits(int64_t n_pairs, int64_t n_tokens, int64_t round) {
+  int64_t s = att_split_tokens(n_pairs, n_tokens, round);
   return (n_tokens + s - 1) / s;
 }
 constexpr int ATT_PART_FLOATS = D + 2;              // per (pair, split, head): acc[128], m, l
@@ -154,11 +156,16 @@ __host__ __device__ inline int64_t att_part_stride(int group) {
 // most ATT_MAX_PAIRS pairs (launches of one call reuse it in stream order),
 // then the per-pair score weights of the packed-bit kernel.
 constexpr int64_t ATT_MAX_PAIRS = 16384;
-inline int64_t att_partial_floats(int64_t np, int64_t n_tokens, int group) {
-  return np * att_n_splits(np, n_tokens) * att_part_stride(group);
+inline int64_t att_partial_floats(int64_t np, int64_t n_tokens, int group, int64_t round) {
+  return np * att_n_splits(np, n_tokens, round) * att_part_stride(group);
 }
 inline int64_t att_launch_floats(int64_t np, int64_t n_tokens, int group) {
-  return att_partial_floats(np, n_tokens, group) + np * ATT_PREP_FLOATS;
+  int64_t most = 0;
+  for (int64_t round : ATT_ROUNDS) {
+    const int64_t f = att_partial_floats(np, n_tokens, group, round) + np * ATT_PREP_FLOATS;
+    most = f > most ? f : most;
+  }
+  return most;
 }
 
 // Host-side launchers implemented in stc_kernels.hip.

@@ -2212,8 +2212,21 @@ constexpr int AT2_BT = 32;    // tokens per wave block
 __host__ __device__ constexpr unsigned at2_vrow(int R2M, unsigned r) {
   return R2M <= 4 ? 24u * r + 12u * (r >> 2) + 8u * (r >> 3) : 16u * r;
 }
-// stages of the record ring of one wave (blocks in flight: stages - 1)
-__host__ __device__ constexpr int at2_nst(int NCH) { return NCH == 1 ? 3 : 2; }
+// Workgroups per CU of k_att2<R2M, .., NCH, W, SWZ, G4>: four for the
+// four-wave instances whose registers fit 128 per lane (256-bit records with
+// groups up to 4; records of at most 96-bit halves), else three (four waves)
+// or one (eight waves).
+__host__ __device__ constexpr int at2_occ(int R2M, int NCH, int W, bool SWZ, bool G4) {
+  return W == 4 ? (NCH == 1 && ((SWZ && G4) || R2M == 3) ? 4 : 3) : 1;
+}
+// stages of the record ring of one wave (blocks in flight: stages - 1): two
+// at four workgroups per CU, to fit the LDS
+__host__ __device__ constexpr int at2_nst(int NCH, int OCC) { return NCH == 1 && OCC < 4 ? 3 : 2; }
+// value rows of at most 256-bit records at four workgroups per CU: 16 r
+// words, to fit the LDS
+__host__ __device__ constexpr unsigned at2_vrowo(int R2M, int OCC, unsigned r) {
+  return OCC == 4 && R2M == 4 ? 16u * r : at2_vrow(R2M, r);
+}
 // weight-table rows: three per head of the instance, then one of zeros
 __host__ __device__ constexpr int at2_trows(bool G4) { return G4 ? 13 : 25; }
 typedef int i32x4 __attribute__((ext_vector_type(4)));
@@ -2424,12 +2437,13 @@ __global__ void __launch_bounds__(128 * PREP_PARTS) k_att2_prep(AttK a) {
 // Dynamic LDS of k_att2<R2M, NT, NCH, W, .., G4>: the score weights, the
 // value column table and the per-head scales, then the larger of the prologue
 // scratch, the W wave regions and the merge scratch.
-__host__ __device__ constexpr size_t at2_lds_bytes(int R2M, int NT, int NCH, int W, bool G4) {
+__host__ __device__ constexpr size_t at2_lds_bytes(int R2M, int NT, int NCH, int W, bool SWZ, bool G4) {
+  const int occ = at2_occ(R2M, NCH, W, SWZ, G4);
   const size_t fixed =
       (size_t)at2_trows(G4) * (64 * R2M + 16) + ATT_MAX_VCOLS * 8 + 8 * 4 + 128 * 4 + ATT_MAX_VCOLS * 4 + 16 * 4;
   const size_t pro = (size_t)8 * 128 * 4 + 2 * 64 * R2M + 8 * 4;
-  const size_t vwords = (size_t)at2_vrow(R2M, 8 * R2M - 1) + 16;
-  const size_t waves = (size_t)W * (2 * at2_nst(NCH) * 256 * NCH + vwords + 4 * AT2_PST / 2 + 16) * 4;
+  const size_t vwords = (size_t)at2_vrowo(R2M, occ, 8 * R2M - 1) + 16;
+  const size_t waves = (size_t)W * (2 * at2_nst(NCH, occ) * 256 * NCH + vwords + 4 * AT2_PST / 2 + 16) * 4;
   const size_t merge = (size_t)W * 8 * (16 * NT + 4) * 4;
   const size_t big = pro > waves ? (pro > merge ? pro : merge) : (waves > merge ? waves : merge);
   return fixed + big;
@@ -2440,7 +2454,7 @@ __host__ __device__ constexpr size_t at2_lds_bytes(int R2M, int NT, int NCH, int
 // W: waves; SWZ: every record is 256 bits (R2M = 4, NCH = 1); G4: group <= 4
 // (a lane's heads are 2i + h for i < 2, otherwise i < 4).
 template <int R2M, int NT, int NCH, int W, bool SWZ, bool G4>
-__global__ void __launch_bounds__(64 * W, W == 4 ? 3 : 1) k_att2(AttK a) {
+__global__ void __launch_bounds__(64 * W, at2_occ(R2M, NCH, W, SWZ, G4)) k_att2(AttK a) {
   static_assert(!SWZ || (R2M == 4 && NCH == 1), "256-bit records: four words per half, one load per block");
   extern __shared__ __align__(16) unsigned char smem[];
   // S16: 256-bit records and groups up to 4 take the scores from 16x16x64
@@ -2454,9 +2468,10 @@ __global__ void __launch_bounds__(64 * W, W == 4 ? 3 : 1) k_att2(AttK a) {
   constexpr int TABW = 64 * R2M;               // bytes of a score-weight row (record bits <= 64 R2M)
   constexpr int TROW = TABW + 16;              // row stride: rows 4 banks apart, so 16 lanes' reads hit 64 banks
   constexpr int TROWS = at2_trows(G4);         // rows 3H + p of head H, part p; then a row of zeros
-  constexpr int VWORDS = (int)at2_vrow(R2M, 8 * R2M - 1) + 16;  // value rows: 4 R2M record bytes per lane half
+  constexpr int OCC = at2_occ(R2M, NCH, W, SWZ, G4);
+  constexpr int VWORDS = (int)at2_vrowo(R2M, OCC, 8 * R2M - 1) + 16;  // value rows: 4 R2M record bytes per lane half
   constexpr int SWORDS = 256 * NCH;            // words of one staging buffer
-  constexpr int NST = at2_nst(NCH);            // ring stages (blocks in flight: NST - 1)
+  constexpr int NST = at2_nst(NCH, OCC);       // ring stages (blocks in flight: NST - 1)
   constexpr int WREG = 2 * NST * SWORDS + VWORDS + 4 * AT2_PST / 2 + 16;  // words per wave region
   static_assert(3 * NH + 1 == TROWS, "weight-table rows");
   static_assert(WREG % 4 == 0 && (TROWS * TROW) % 16 == 0, "16-byte aligned LDS regions");
@@ -2516,7 +2531,7 @@ __global__ void __launch_bounds__(64 * W, W == 4 ? 3 : 1) k_att2(AttK a) {
       if (tid < ncols) {
         // record byte k of lane half hh sits in value row k - 4 R2v hh + 4 R2M hh
         const unsigned row = vc[tid].row, hh = row >= 4u * (unsigned)R2v ? 1u : 0u;
-        e = (u32x2){at2_vrow(R2M, row - 4u * (unsigned)R2v * hh + 4u * R2M * hh), vc[tid].mask2};
+        e = (u32x2){at2_vrowo(R2M, OCC, row - 4u * (unsigned)R2v * hh + 4u * R2M * hh), vc[tid].mask2};
       }
       sVc[tid] = e;
       sFac[tid] = tid < ncols ? vc[tid].fac : 0.0f;
@@ -2644,7 +2659,7 @@ __global__ void __launch_bounds__(64 * W, W == 4 ? 3 : 1) k_att2(AttK a) {
     for (int i = 0; i < R2M; ++i) {
       const u32x2 y = at2_quad_split(rv[i], sel1, sel_e, sel_o);
       const unsigned row = (unsigned)(4 * (i + h * R2M) + e4);
-      *reinterpret_cast<u32x2*>(sV + at2_vrow(R2M, row) + 2 * (t32 >> 2)) = y;
+      *reinterpret_cast<u32x2*>(sV + at2_vrowo(R2M, OCC, row) + 2 * (t32 >> 2)) = y;
     }
     // ---- scores: int8 MFMAs, A = weights (rows 4H + p), B = the record bits
     float su[NHL];  // unscaled scores of the lane's slots (-inf past the split)
@@ -2847,13 +2862,13 @@ int attend_scratch(void** ptr) {
 template <int R2M, int NT, int NCH, int W, bool SWZ, bool G4>
 static int at2_attr() {
   return hipFuncSetAttribute((const void*)k_att2<R2M, NT, NCH, W, SWZ, G4>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                             (int)at2_lds_bytes(R2M, NT, NCH, W, G4)) != hipSuccess;
+                             (int)at2_lds_bytes(R2M, NT, NCH, W, SWZ, G4)) != hipSuccess;
 }
 template <int R2M, int NT, int NCH, int W, bool SWZ, bool G4>
 static void at2_launch(dim3 grid, hipStream_t s, const AttK& a) {
-  static_assert(at2_lds_bytes(R2M, NT, NCH, W, G4) <= 160 * 1024, "k_att2 LDS");
-  hipLaunchKernelGGL((k_att2<R2M, NT, NCH, W, SWZ, G4>), grid, dim3(64 * W), at2_lds_bytes(R2M, NT, NCH, W, G4), s,
-                     a);
+  static_assert(at2_lds_bytes(R2M, NT, NCH, W, SWZ, G4) * at2_occ(R2M, NCH, W, SWZ, G4) <= 160 * 1024, "k_att2 LDS");
+  hipLaunchKernelGGL((k_att2<R2M, NT, NCH, W, SWZ, G4>), grid, dim3(64 * W), at2_lds_bytes(R2M, NT, NCH, W, SWZ, G4),
+                     s, a);
 }
 
 typedef void (*AttKernel)(AttK);
@@ -2918,34 +2933,47 @@ int launch_attend(const AttendLaunch& L, void* stream) {
   // a-table build assumes 12 or 16)
   if (fixed + (size_t)waves * a.region_words * 4 > 160 * 1024) return 1;
   hipStream_t s = (hipStream_t)stream;
+  // the packed-bit kernel's instance (-1: the older kernel): value columns
+  // plus the sum column fit the tiles; token counts and stream bytes below
+  // 2^31 for its 32-bit arithmetic
+  const bool small = L.n_tokens < (1LL << 30) && L.n_tokens * (long long)L.max_bits / 8 < (1LL << 31) - 65536;
+  int inst = -1;
+  if (!sketch && !L.rht && L.group <= 8 && L.max_bits <= 512 && L.max_vcols <= 191 && small) {
+    const bool g4 = L.group <= 4;
+    if (L.max_bits <= 256 && L.att_chunks <= 1) {
+      if (L.rec256) inst = g4 ? 0 : 1;
+      else if (!g4 && L.max_vcols <= 127 && L.max_bits <= 192) inst = 2;
+      else if (!g4 && L.max_vcols <= 127) inst = 3;
+      else inst = g4 ? 4 : 5;
+    } else {
+      inst = L.max_bits <= 256 ? 6 : 7;
+    }
+  }
+  static constexpr int kOcc[8] = {at2_occ(4, 1, 4, true, true),   at2_occ(4, 1, 4, true, false),
+                                  at2_occ(3, 1, 4, false, false), at2_occ(4, 1, 4, false, false),
+                                  at2_occ(4, 1, 4, false, true),  at2_occ(4, 1, 4, false, false),
+                                  at2_occ(4, 2, 8, false, false), at2_occ(8, 3, 8, false, false)};
+  const int64_t round = inst >= 0 && kOcc[inst] == 4 ? ATT_ROUNDS[1] : ATT_ROUNDS[0];
   for (long long c0 = 0; c0 < L.n_pairs; c0 += ATT_MAX_PAIRS) {
     const long long np = L.n_pairs - c0 < ATT_MAX_PAIRS ? L.n_pairs - c0 : ATT_MAX_PAIRS;
     a.pair_base = c0;
     a.n_pairs = np;
-    a.split_tokens = att_split_tokens(np, L.n_tokens);
-    a.n_splits = att_n_splits(np, L.n_tokens);
+    a.split_tokens = att_split_tokens(np, L.n_tokens, round);
+    a.n_splits = att_n_splits(np, L.n_tokens, round);
     const size_t att_lds = fixed + (size_t)waves * a.region_words * 4;
     const dim3 grid((unsigned)a.n_splits, (unsigned)np);
-    // (k_att2: value columns plus the sum column fit the tiles; token counts
-    // and stream bytes below 2^31 for its 32-bit arithmetic)
-    const bool small = L.n_tokens < (1LL << 30) && L.n_tokens * (long long)L.max_bits / 8 < (1LL << 31) - 65536;
-    if (!sketch && !L.rht && L.group <= 8 && L.max_bits <= 512 && L.max_vcols <= 191 && small) {
-      const bool g4 = L.group <= 4;
-      a.prep = reinterpret_cast<float*>(a.ws) + att_partial_floats(np, L.n_tokens, L.group);
+    if (inst >= 0) {
+      a.prep = reinterpret_cast<float*>(a.ws) + att_partial_floats(np, L.n_tokens, L.group, round);
       hipLaunchKernelGGL(k_att2_prep, dim3((unsigned)np), dim3(128 * PREP_PARTS), 0, s, a);
-      if (L.max_bits <= 256 && L.att_chunks <= 1) {
-        if (L.rec256)
-          g4 ? at2_launch<4, 10, 1, 4, true, true>(grid, s, a) : at2_launch<4, 10, 1, 4, true, false>(grid, s, a);
-        else if (!g4 && L.max_vcols <= 127 && L.max_bits <= 192)
-          at2_launch<3, 8, 1, 4, false, false>(grid, s, a);
-        else if (!g4 && L.max_vcols <= 127)
-          at2_launch<4, 8, 1, 4, false, false>(grid, s, a);
-        else
-          g4 ? at2_launch<4, 10, 1, 4, false, true>(grid, s, a) : at2_launch<4, 10, 1, 4, false, false>(grid, s, a);
-      } else if (L.max_bits <= 256) {
-        at2_launch<4, 10, 2, 8, false, false>(grid, s, a);
-      } else {
-        at2_launch<8, 12, 3, 8, false, false>(grid, s, a);
+      switch (inst) {
+        case 0: at2_launch<4, 10, 1, 4, true, true>(grid, s, a); break;
+        case 1: at2_launch<4, 10, 1, 4, true, false>(grid, s, a); break;
+        case 2: at2_launch<3, 8, 1, 4, false, false>(grid, s, a); break;
+        case 3: at2_launch<4, 8, 1, 4, false, false>(grid, s, a); break;
+        case 4: at2_launch<4, 10, 1, 4, false, true>(grid, s, a); break;
+        case 5: at2_launch<4, 10, 1, 4, false, false>(grid, s, a); break;
+        case 6: at2_launch<4, 10, 2, 8, false, false>(grid, s, a); break;
+        default: at2_launch<8, 12, 3, 8, false, false>(grid, s, a); break;
       }
     } else {
       const int var = sketch ? (L.rht ? 0 : (L.max_bits <= 512 ? 1 : 2)) : (L.rht ? 3 : (L.max_bits <= 512 ? 4 : 5));
