@@ -41,7 +41,10 @@ struct AttVCol {
   uint32_t chan;
 };
 constexpr size_t OFF_ATTVCH = OFF_ATTV + ATT_MAX_VCOLS * sizeof(AttVCol);
-static_assert(OFF_ATTVCH + D * sizeof(uint32_t) <= STATE_BYTES, "state layout overflows the blob");
+// fp16 W rows (the W_HI order) scaled by 2^e16, e16 = 13 - floor(log2 max |W|):
+// the single-pass decode of low budgets
+constexpr size_t OFF_W16 = (OFF_ATTVCH + D * sizeof(uint32_t) + 255) / 256 * 256;
+static_assert(OFF_W16 + 32768 <= STATE_BYTES, "state layout overflows the blob");
 
 // Quantizer fast path for a channel with L levels: y = c * fl(1/step) +
 // (L/2 + eps_L) in fp32 with eps_L = L * 2^-21. Against the exact count of
@@ -94,6 +97,8 @@ struct alignas(16) DevHdr {
   // planes 0/1 low/high bytes of bf16(cb), 2/3 of bf16(cb - bf16(cb)),
   // 4/5 of fp16(cb)
   uint32_t cbt[12];
+  float bias16[D];      // decode with fp16 W: sum_j W16_ij 2^-e16 (L_j - 1)/2, natural dim order
+  uint32_t code16;      // fp16 pair (2^-e16, 2^-e16): the codes' scale in that decode
 };
 static_assert(sizeof(DevHdr) <= OFF_U32, "header too large");
 
@@ -196,6 +201,7 @@ struct DecodeLaunch {
   void* x;
   int f32out;
   int max_bits;
+  bool w16 = false;  // bf16 output from the fp16 W rows in one pass (low budgets; see decode_w16_ok)
 };
 struct AttendLaunch {
   const unsigned char* k_states;

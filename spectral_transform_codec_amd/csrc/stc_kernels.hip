@@ -49,6 +49,14 @@ __device__ __forceinline__ f32x16 mfma32_bf16(bf16x8 a, bf16x8 b, f32x16 c) {
 __device__ __forceinline__ f32x4 mfma_f16(f16x8 a, f16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
+// Two floats rounded to bf16 (nearest even), packed low / high: one
+// v_cvt_pk_bf16_f32.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
+}
 // Two floats that bf16 holds exactly (here integers below 2^8, whose fp32
 // low halves are zero) as a bf16 pair: the two high halves, one byte permute.
 __device__ __forceinline__ unsigned bf16_pair_exact(float lo, float hi) {
@@ -891,7 +899,9 @@ __device__ __forceinline__ void rec_store(unsigned* str, const unsigned (&w)[NW]
   }
 }
 
-template <int F32OUT, int NW>
+// W16: one MFMA pass with the fp16 W rows and fp16 codes (bf16 output of low
+// budgets; the host decides), else the bf16 hi and lo passes.
+template <int F32OUT, int NW, bool W16>
 __global__ void __launch_bounds__(DEC_THREADS, 1) k_decode_eigen(DecK a) {
   extern __shared__ __align__(16) unsigned char smem[];
   unsigned char* sWhi = smem;
@@ -930,19 +940,19 @@ __global__ void __launch_bounds__(DEC_THREADS, 1) k_decode_eigen(DecK a) {
     const unsigned B = (unsigned)__builtin_amdgcn_readfirstlane(hdr->total_bits);
     __syncthreads();  // every wave is done with the previous state
     {
-      const u32x4* ghi = reinterpret_cast<const u32x4*>(st + OFF_W_HI);
+      const u32x4* ghi = reinterpret_cast<const u32x4*>(st + (W16 ? OFF_W16 : OFF_W_HI));
       const u32x4* glo = reinterpret_cast<const u32x4*>(st + OFF_W_LO);
       for (int i = tid; i < 128 * 16; i += DEC_THREADS) {
         const int row = i >> 4, c = i & 15;
         *reinterpret_cast<u32x4*>(sWhi + row * UROW + c * 16) = ghi[i];
-        *reinterpret_cast<u32x4*>(sWhi + 128 * UROW + row * UROW + c * 16) = glo[i];
+        if (!W16) *reinterpret_cast<u32x4*>(sWhi + 128 * UROW + row * UROW + c * 16) = glo[i];
       }
     }
     if (tid < 128) {
       sTab[tid] = (unsigned)hdr->off[tid & ~3];                              // group record offset
       sTab[128 + tid] = (unsigned)hdr->off[tid] - (unsigned)hdr->off[tid & ~3];  // offset in the group
       sTab[256 + tid] = (unsigned)hdr->bits[tid];                            // width
-      reinterpret_cast<float*>(sTab)[384 + tid] = -hdr->bias[tid];          // -bias, natural dim order
+      reinterpret_cast<float*>(sTab)[384 + tid] = -(W16 ? hdr->bias16[tid] : hdr->bias[tid]);  // natural dim order
     }
     __syncthreads();
     const long long P_len = packed_len((long long)B, n);
@@ -969,6 +979,8 @@ __global__ void __launch_bounds__(DEC_THREADS, 1) k_decode_eigen(DecK a) {
       const lds_u8* tL = lds_ptr(tb);
       const lds_u8* wL = lds_ptr(wb);
       const unsigned tB = (unsigned)t32 * B;
+      // W16: the codes' scale 2^-e16 (exact products in fp16)
+      const f16x2 cscale = __builtin_bit_cast(f16x2, (unsigned)__builtin_amdgcn_readfirstlane(hdr->code16));
       u32x4 cf[8];
 #pragma unroll
       for (int g = 0; g < 16; ++g) {  // group: channels 64h + 4g .. +3
@@ -984,7 +996,11 @@ __global__ void __launch_bounds__(DEC_THREADS, 1) k_decode_eigen(DecK a) {
         for (int j = 0; j < 4; ++j) code[j] = __builtin_amdgcn_ubfe(w, pos[j], wid[j]);
 #pragma unroll
         for (int j = 0; j < 2; ++j)
-          cf[g >> 1][2 * (g & 1) + j] = bf16_pair_exact((float)code[2 * j], (float)code[2 * j + 1]);
+          cf[g >> 1][2 * (g & 1) + j] =
+              W16 ? __builtin_bit_cast(unsigned, (f16x2){(_Float16)(unsigned short)code[2 * j],
+                                                         (_Float16)(unsigned short)code[2 * j + 1]} *
+                                                     cscale)
+                  : bf16_pair_exact((float)code[2 * j], (float)code[2 * j + 1]);
       }
       // ---- 3: reconstruct dims 64h + 16ob + r of token t
       const long long tok = tok0 + t32;
@@ -1003,10 +1019,15 @@ __global__ void __launch_bounds__(DEC_THREADS, 1) k_decode_eigen(DecK a) {
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
           const int off = 32 * ob * UROW + 16 * ks;
-          const bf16x8 wh = LDS_AT(bf16x8, wL + off);
-          const bf16x8 wl = LDS_AT(bf16x8, wL + 128 * UROW + off);
-          acc = mfma32_bf16(wh, __builtin_bit_cast(bf16x8, cf[ks]), acc);
-          acc = mfma32_bf16(wl, __builtin_bit_cast(bf16x8, cf[ks]), acc);
+          if (W16) {
+            const f16x8 w = LDS_AT(f16x8, wL + off);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(w, __builtin_bit_cast(f16x8, cf[ks]), acc, 0, 0, 0);
+          } else {
+            const bf16x8 wh = LDS_AT(bf16x8, wL + off);
+            const bf16x8 wl = LDS_AT(bf16x8, wL + 128 * UROW + off);
+            acc = mfma32_bf16(wh, __builtin_bit_cast(bf16x8, cf[ks]), acc);
+            acc = mfma32_bf16(wl, __builtin_bit_cast(bf16x8, cf[ks]), acc);
+          }
         }
         if (F32OUT) {
           if (tok_ok) {
@@ -1020,8 +1041,7 @@ __global__ void __launch_bounds__(DEC_THREADS, 1) k_decode_eigen(DecK a) {
           for (int e = 0; e < 8; ++e) {
             const float v0 = acc[2 * e];
             const float v1 = acc[2 * e + 1];
-            pk[ob][e >> 2][e & 3] = (unsigned)__builtin_bit_cast(unsigned short, (__bf16)v0) |
-                                    ((unsigned)__builtin_bit_cast(unsigned short, (__bf16)v1) << 16);
+            pk[ob][e >> 2][e & 3] = pack_bf16x2(v0, v1);
           }
         }
       }
@@ -1066,10 +1086,10 @@ __global__ void __launch_bounds__(DEC_THREADS, 1) k_decode_eigen(DecK a) {
 
 int launch_decode_eigen(const DecodeLaunch& L, void* stream) {
   if (!g_dec_attr_done) {
-    if (hipFuncSetAttribute((const void*)k_decode_eigen<0, 8>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)DEC_LDS) != hipSuccess) return 1;
-    if (hipFuncSetAttribute((const void*)k_decode_eigen<1, 8>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)DEC_LDS) != hipSuccess) return 1;
-    if (hipFuncSetAttribute((const void*)k_decode_eigen<0, 16>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)DEC_LDS) != hipSuccess) return 1;
-    if (hipFuncSetAttribute((const void*)k_decode_eigen<1, 16>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)DEC_LDS) != hipSuccess) return 1;
+    for (const void* k : {(const void*)k_decode_eigen<0, 8, false>, (const void*)k_decode_eigen<1, 8, false>,
+                          (const void*)k_decode_eigen<0, 16, false>, (const void*)k_decode_eigen<1, 16, false>,
+                          (const void*)k_decode_eigen<0, 8, true>, (const void*)k_decode_eigen<0, 16, true>})
+      if (hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)DEC_LDS) != hipSuccess) return 1;
     g_dec_attr_done = true;
   }
   DecK a;
@@ -1097,11 +1117,14 @@ int launch_decode_eigen(const DecodeLaunch& L, void* stream) {
   // records of up to 512 bits: 8 staging words per lane, else 16
   const bool small = L.max_bits <= 512;
   if (L.f32out) {
-    if (small) hipLaunchKernelGGL((k_decode_eigen<1, 8>), dim3(grid), dim3(DEC_THREADS), DEC_LDS, s, a);
-    else hipLaunchKernelGGL((k_decode_eigen<1, 16>), dim3(grid), dim3(DEC_THREADS), DEC_LDS, s, a);
+    if (small) hipLaunchKernelGGL((k_decode_eigen<1, 8, false>), dim3(grid), dim3(DEC_THREADS), DEC_LDS, s, a);
+    else hipLaunchKernelGGL((k_decode_eigen<1, 16, false>), dim3(grid), dim3(DEC_THREADS), DEC_LDS, s, a);
+  } else if (L.w16) {
+    if (small) hipLaunchKernelGGL((k_decode_eigen<0, 8, true>), dim3(grid), dim3(DEC_THREADS), DEC_LDS, s, a);
+    else hipLaunchKernelGGL((k_decode_eigen<0, 16, true>), dim3(grid), dim3(DEC_THREADS), DEC_LDS, s, a);
   } else {
-    if (small) hipLaunchKernelGGL((k_decode_eigen<0, 8>), dim3(grid), dim3(DEC_THREADS), DEC_LDS, s, a);
-    else hipLaunchKernelGGL((k_decode_eigen<0, 16>), dim3(grid), dim3(DEC_THREADS), DEC_LDS, s, a);
+    if (small) hipLaunchKernelGGL((k_decode_eigen<0, 8, false>), dim3(grid), dim3(DEC_THREADS), DEC_LDS, s, a);
+    else hipLaunchKernelGGL((k_decode_eigen<0, 16, false>), dim3(grid), dim3(DEC_THREADS), DEC_LDS, s, a);
   }
   return hipGetLastError() != hipSuccess;
 }
@@ -1374,9 +1397,7 @@ __global__ void __launch_bounds__(RHTD_T) k_rht_decode(RhtK a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int i = 8 * c + 2 * e;
-          const unsigned lo = __builtin_bit_cast(unsigned short, (__bf16)(v[i] * m * hdr->sign[i]));
-          const unsigned hi = __builtin_bit_cast(unsigned short, (__bf16)(v[i + 1] * m * hdr->sign[i + 1]));
-          pk[e] = lo | (hi << 16);
+          pk[e] = pack_bf16x2(v[i] * m * hdr->sign[i], v[i + 1] * m * hdr->sign[i + 1]);
         }
         *reinterpret_cast<u32x4*>(row + 16 * c) = pk;
       }
@@ -1527,7 +1548,6 @@ __host__ __device__ constexpr int att_region_words(int max_bits) {
 }
 
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 // 4 unsigned byte codes c -> 4 fp16 c: two byte permutes give 1024 + c
 // (0x64xx in fp16, exact), two packed fp16 subtractions remove the 1024

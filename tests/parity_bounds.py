@@ -124,3 +124,33 @@ def check_eigen_codes(q_gpu, st, x, gpu_state=None, max_frac=1e-4):
     eps, step_rel = projection_eps(x, st["U"], st["steps"], st["bits"], basis_err, step_rel)
     assert_code_diffs_at_boundaries(q_gpu, q_or, c, st, eps, step_rel, max_frac)
     return q_or
+
+
+def decode_w16(st, dtype):
+    """Whether the library may decode this state in one fp16 pass: bf16
+    output, at most 2 bits per value, largest kept step in [2^-7, 2^20] (the
+    library's rule; in a batch every state must meet it, so a state that meets
+    it may also go through the bf16 pair)."""
+    bits = np.asarray(st["bits"])
+    steps = np.asarray(st["steps"], np.float64)[bits > 0]
+    smax = float(steps.max()) if steps.size else 0.0
+    return dtype == "bf16" and int(bits.sum()) <= 2 * bits.shape[0] and (smax == 0.0 or 2.0 ** -7 <= smax <= 2.0 ** 20)
+
+
+def decode_arith(st, dtype):
+    """Bound on the GPU decode's error before the output rounding, per output
+    dim. bf16 pair: each W_ij = U_ij step_j is held to 2^-17 relative and the
+    exact integer codes are summed in fp32: 2^-15 sum_j |U_ij| step_j (L_j - 1).
+    One fp16 pass: W_ij 2^e rounded to fp16 with its largest entry in
+    [2^13, 2^14), so 2^-11 relative or 2^-25 absolute in the scaled units
+    (below 2^-38 of the largest |W| after scaling back), against a bias of the
+    same fp16 entries: the error is sum_j dW_ij (q_j - (L_j - 1)/2) <=
+    2^-11 sum_j |W_ij| (L_j - 1)/2 + 2^-38 max|W| sum_j (L_j - 1)/2, plus the
+    fp32 sums (2^-16 of the same magnitude)."""
+    bits = np.asarray(st["bits"])
+    levels_m1 = np.where(bits > 0, (1 << bits.astype(np.int64)) - 1, 0).astype(np.float64)
+    mag = np.abs(np.asarray(st["U"], np.float64)) @ (np.asarray(st["steps"], np.float64) * levels_m1)
+    if decode_w16(st, dtype):
+        wmax = float((np.abs(np.asarray(st["U"], np.float64)) * np.asarray(st["steps"], np.float64)[None, :]).max())
+        return (2.0 ** -12 + 2.0 ** -16) * mag + 2.0 ** -39 * wmax * levels_m1.sum()
+    return 2.0 ** -15 * mag

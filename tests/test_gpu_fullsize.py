@@ -24,7 +24,7 @@ import torch
 
 import synth
 from oracle import codec
-from parity_bounds import check_eigen_codes
+from parity_bounds import check_eigen_codes, decode_arith
 
 pytestmark = pytest.mark.gpu
 
@@ -62,8 +62,7 @@ def check_decode(st, q_gpu, x_tokens, x_gpu_tokens):
     exact = codec.reconstruct_exact(st, codec.pack(q_gpu, st["bits"]), q_gpu.shape[0])
     xo = codec.round_to_bf16(exact)
     ulp = np.abs(exact) * 2.0 ** -7
-    levels_m1 = np.where(st["bits"] > 0, (1 << st["bits"].astype(np.int64)) - 1, 0)
-    arith = 2.0 ** -15 * (np.abs(st["U"]) @ (st["steps"] * levels_m1))
+    arith = decode_arith(st, "bf16")
     assert np.all(np.abs(x_gpu_tokens - xo) <= ulp + arith[None, :])
     q_or = codec.quantize(st, codec.project(st, x_tokens))
     x_or = codec.decode_kv(st, codec.pack(q_or, st["bits"]), q_or.shape[0], "bf16")

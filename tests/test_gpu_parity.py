@@ -20,7 +20,7 @@ import torch
 import att_variants
 import synth
 from oracle import codec, rht
-from parity_bounds import (assert_rht_code_diffs_at_boundaries, check_eigen_codes,
+from parity_bounds import (assert_rht_code_diffs_at_boundaries, check_eigen_codes, decode_arith,
                            rht_rotation_eps)
 
 pytestmark = pytest.mark.gpu
@@ -156,13 +156,11 @@ def test_decode_matches_oracle(cfg, n, avg, dtype):
     r_o, r_g = codec.rel_mse(x, xo), codec.rel_mse(x, xg)
     assert abs(r_g - r_o) <= 1e-3 * r_o, (r_g, r_o)
     # element-wise: one rounding step of the output dtype apart, plus the
-    # error of the GPU's arithmetic before rounding. Each basis-times-step
-    # entry is held as a bf16 pair (relative error <= 2^-17) and the codes are
-    # summed in fp32, so that error is below 2^-15 sum_j |U_ij| step_j (L_j-1).
+    # error of the GPU's arithmetic before rounding (parity_bounds.decode_arith:
+    # the bf16 pair of W, or for low budgets with bf16 output one fp16 pass)
     exact = codec.reconstruct_exact(ost, po, n)
     ulp = np.abs(exact) * (2.0 ** -7 if dtype == "bf16" else 2.0 ** -23)
-    levels_m1 = np.where(ost["bits"] > 0, (1 << ost["bits"].astype(np.int64)) - 1, 0)
-    arith = 2.0 ** -15 * (np.abs(ost["U"]) @ (ost["steps"] * levels_m1))
+    arith = decode_arith(ost, dtype)
     assert np.all(np.abs(xg - xo) <= ulp + arith[None, :])
 
 
