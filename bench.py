@@ -574,6 +574,53 @@ def cache_ops(c, tag):
     ]
 
 
+def rht_encode_kernels(c, args, dev):
+    """Walsh-Hadamard encode of the whole cache input (every stream, 3-bit
+    codebook) with each encode kernel in turn: the +-1 matrix on the matrix
+    cores and the register butterfly. Average of K launches (HIP events on the
+    launch stream), bytes = bf16 tokens in + 48-byte records + fp32 norms out.
+    Not part of value."""
+    import torch
+
+    import synth
+    import spectral_transform_codec_amd as stc
+    n, S = c["n"], c["S"]
+    import numpy as np
+    cb = stc.lloyd_max(synth.sphere_coordinate_samples())[0].astype(np.float32)
+    n_st = 16
+    arr = stc.StateArray([stc.rht_state_init(synth.random_signs(4, 0, 0, h, 0), cb) for h in range(n_st)])
+    smap = torch.arange(S, dtype=torch.int32, device=dev) % n_st
+    packed = torch.empty((S, stc.packed_bytes(384, n)), dtype=torch.uint8, device=dev)
+    norms = torch.empty((S, n), dtype=torch.float32, device=dev)
+    nbytes = S * n * (256 + 48 + 4)
+    stream = torch.cuda.current_stream()
+    out = {}
+    before = stc.get_rht_encode_kernel()
+    try:
+        for name, kind in (("mfma", stc.RHT_ENCODE_MFMA), ("butterfly", stc.RHT_ENCODE_BUTTERFLY)):
+            stc.set_rht_encode_kernel(kind)
+            fn = lambda: stc.encode_kv_batched(arr, c["x"], state_of_stream=smap, packed=packed, norms=norms)
+            for _ in range(2):
+                fn()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(args.steps):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / args.steps
+            out[name] = {"ms": round(ms, 4), "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                         "pct_hbm_peak": round(100.0 * nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 1)}
+    finally:
+        stc.set_rht_encode_kernel(before)
+    out["bytes"] = int(nbytes)
+    out["streams"], out["tokens"] = S, n
+    del packed, norms
+    return out
+
+
 def full_step(args, dev):
     import torch
 
@@ -673,6 +720,8 @@ def full_step(args, dev):
         "setup_s": {t: round(caches[t]["setup_s"], 1) for t in tags},
         "calibrate_s": {t: round(caches[t]["calibrate_s"], 1) for t in tags},
     }
+    if "llama_cache" in caches and not args.no_extras:
+        line["rht_encode_llama_cache"] = rht_encode_kernels(caches["llama_cache"], args, dev)
     # the caches are not needed any more: free them before the extras
     del ops, caches
     torch.cuda.empty_cache()

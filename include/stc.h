@@ -452,6 +452,22 @@ stc_status stc_decode_step_batched(const void* states_dev, int64_t n_states,
  * want the device-side behaviour above reported before they rely on it. */
 stc_status stc_check_state_map(const int32_t* map_dev, int64_t n, int64_t n_states, stc_stream_t stream);
 
+/* Kernel of the Walsh-Hadamard encode without the residual sketch (TurboQuant
+ * ablation summary, "Experimentele Opstelling": a random sign flip and a
+ * Walsh-Hadamard transform before the fixed 3-bit codebook). Both kernels
+ * write the same records and norms up to fp32 summation order:
+ *   STC_RHT_ENCODE_MFMA       the transform as a +-1 matrix on the matrix
+ *                             cores (exact in bf16, fp32 sums)
+ *   STC_RHT_ENCODE_BUTTERFLY  the fast transform as fp32 butterflies in
+ *                             registers (one cross-lane swap stage)
+ * The choice is process-wide and applies to launches issued after the call;
+ * any other kind returns STC_EINVAL. The sketch encode always uses the
+ * matrix cores (its sketch is a dense product). */
+#define STC_RHT_ENCODE_MFMA 0
+#define STC_RHT_ENCODE_BUTTERFLY 1
+stc_status stc_set_rht_encode_kernel(int32_t kind);
+int32_t stc_get_rht_encode_kernel(void);
+
 /* ------------------------------------------------------ diagnostics */
 const char* stc_status_str(stc_status s);
 /* Message of the last error on the calling thread ("" if none). */

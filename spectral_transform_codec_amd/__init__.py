@@ -21,7 +21,8 @@ __all__ = [
     "State", "StateArray", "calibrate_head", "state_init", "rht_state_init", "encode_kv", "decode_kv",
     "encode_kv_batched", "decode_kv_batched", "attend_compressed", "attend_compressed_batched",
     "quantize_pack_f32", "state_bytes", "packed_bytes", "attend_workspace_bytes", "total_bits",
-    "delta_star", "water_fill", "eigh", "lloyd_max", "StcError",
+    "delta_star", "water_fill", "eigh", "lloyd_max", "StcError", "set_rht_encode_kernel",
+    "get_rht_encode_kernel", "RHT_ENCODE_MFMA", "RHT_ENCODE_BUTTERFLY",
 ]
 
 _P = ctypes.POINTER
@@ -264,6 +265,20 @@ def check_state_map(state_of_stream: torch.Tensor, n_states: int) -> None:
     [0, n_states) (synchronizes the current stream)."""
     m = _map_arg(state_of_stream)
     check("stc_check_state_map", lib().stc_check_state_map(_ptr(m), m.numel(), int(n_states), _stream()))
+
+
+RHT_ENCODE_MFMA = 0
+RHT_ENCODE_BUTTERFLY = 1
+
+
+def set_rht_encode_kernel(kind: int) -> None:
+    """Walsh-Hadamard encode kernel for later launches: RHT_ENCODE_MFMA (the +-1
+    matrix on the matrix cores) or RHT_ENCODE_BUTTERFLY (register butterflies)."""
+    check("stc_set_rht_encode_kernel", lib().stc_set_rht_encode_kernel(int(kind)))
+
+
+def get_rht_encode_kernel() -> int:
+    return int(lib().stc_get_rht_encode_kernel())
 
 
 def encode_kv_batched(states: StateArray, x: torch.Tensor, state_of_stream: Optional[torch.Tensor] = None,

@@ -69,6 +69,8 @@ SIGNATURES = {
     "stc_decode_step_batched": (c_i32, [c_vp, c_i64, c_vp, c_vp, P(HeadInfo), c_i64, c_i64, c_vp, c_vp, c_i32,
                                         c_vp, c_vp, c_i64, c_i32, c_vp, c_vp, c_f32, c_vp, c_size, c_vp]),
     "stc_check_state_map": (c_i32, [c_vp, c_i64, c_i64, c_vp]),
+    "stc_set_rht_encode_kernel": (c_i32, [c_i32]),
+    "stc_get_rht_encode_kernel": (c_i32, []),
     "stc_status_str": (c_cp, [c_i32]),
     "stc_last_error": (c_cp, []),
 }

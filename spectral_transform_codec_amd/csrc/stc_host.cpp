@@ -11,6 +11,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -23,6 +24,11 @@
 #include "stc_internal.h"
 
 using namespace stc;
+
+namespace {
+std::atomic<int> g_rht_encode_kernel{STC_RHT_ENCODE_BUTTERFLY};
+}
+int stc::rht_encode_kernel() { return g_rht_encode_kernel.load(std::memory_order_relaxed); }
 
 namespace {
 
@@ -864,6 +870,15 @@ stc_status stc_state_basis(const void* state_dev, float* u_out, stc_stream_t str
   if (stc_status st = hip_check(hipStreamSynchronize(s), "basis sync")) return st;
   return ok();
 }
+
+stc_status stc_set_rht_encode_kernel(int32_t kind) {
+  if (kind != STC_RHT_ENCODE_MFMA && kind != STC_RHT_ENCODE_BUTTERFLY)
+    return fail(STC_EINVAL, "set_rht_encode_kernel: kind %d", (int)kind);
+  g_rht_encode_kernel.store(kind, std::memory_order_relaxed);
+  return ok();
+}
+
+int32_t stc_get_rht_encode_kernel(void) { return g_rht_encode_kernel.load(std::memory_order_relaxed); }
 
 stc_status stc_check_state_map(const int32_t* map_dev, int64_t n, int64_t n_states, stc_stream_t stream) {
   if (n < 0 || n_states < 0) return fail(STC_EINVAL, "check_state_map: negative size");

@@ -13,16 +13,24 @@
 // include/stc.h; this file implements exactly those.
 //
 // Hardware mapping:
-//  - projection and reconstruction are dense 128-wide contractions on bf16
-//    MFMA (v_mfma_f32_16x16x32_bf16). The basis is split into bf16 high and
-//    low parts (two MFMA passes; three for fp32 tokens) so the fp32 result
-//    carries ~16 significant bits of the basis, enough for code parity with
-//    the fp64 definition. Codes are exact small integers in bf16.
-//  - bit packing / unpacking run one token per lane with the per-channel
-//    widths in scalar registers (uniform control flow), going through LDS to
-//    change between the MFMA layouts and the token-per-lane layout, and to
-//    turn the variable-length records into coalesced 128-bit HBM accesses.
-//  - the Walsh-Hadamard butterfly runs in registers, one token per lane.
+//  - projection and reconstruction are dense 128-wide contractions on the
+//    matrix cores (v_mfma_f32_32x32x16_bf16, 32 tokens per wave). The basis
+//    is split into bf16 high and low parts (two passes; three for fp32
+//    tokens) so the fp32 result carries ~16 significant bits of the basis,
+//    enough for code parity with the fp64 definition. Codes are exact small
+//    integers in bf16. The bf16 decode of budgets up to 2 bits per value
+//    takes one fp16 pass (v_mfma_f32_32x32x16_f16) with the basis scaled by
+//    a power of two and codes scaled back exactly.
+//  - bit packing and unpacking go through a per-wave LDS stream, which
+//    turns the variable-length records into coalesced HBM accesses and
+//    moves codes between the matrix-core layouts and the records.
+//  - attention reads the packed records straight into the matrix cores:
+//    scores from the K record bits on int8 MFMAs, softmax weights times the
+//    V codes on fp16 MFMAs, records staged to LDS by buffer loads.
+//  - the Walsh-Hadamard encode runs either as a +-1 matrix on the matrix
+//    cores or as fp32 butterflies in registers (two lanes per token, one
+//    cross-lane swap stage); its decode runs the butterflies one token per
+//    lane.
 #include <hip/hip_runtime.h>
 
 #include <mutex>
@@ -1034,7 +1042,8 @@ __global__ void __launch_bounds__(DEC_THREADS, 1) k_decode_eigen(DecK a) {
             float* o = static_cast<float*>(a.x) + s * a.x_stride + tok * a.ld + 64 * h + 16 * ob;
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4)
-              reinterpret_cast<f32x4*>(o)[q4] = (f32x4){acc[4 * q4], acc[4 * q4 + 1], acc[4 * q4 + 2], acc[4 * q4 + 3]};
+              __builtin_nontemporal_store((f32x4){acc[4 * q4], acc[4 * q4 + 1], acc[4 * q4 + 2], acc[4 * q4 + 3]},
+                                          reinterpret_cast<f32x4*>(o) + q4);
           }
         } else {
 #pragma unroll
@@ -1049,7 +1058,9 @@ __global__ void __launch_bounds__(DEC_THREADS, 1) k_decode_eigen(DecK a) {
         // Two rounds through the LDS stream (free once the codes are out):
         // the lanes of half r put their 128-byte row halves (one cache line
         // each) into rows of 33 words, then the wave writes the 32 lines with
-        // 16-byte stores, eight lanes per line.
+        // 16-byte stores, eight lanes per line. The reconstructed rows are
+        // stored non-temporally: they are not read back by this library, and
+        // cached dirty lines would be written back during the launches after.
         const int nrow = (int)(n - tok0 < DEC_BT ? n - tok0 : DEC_BT);
         unsigned short* obase = static_cast<unsigned short*>(a.x) + s * a.x_stride + tok0 * a.ld;
 #pragma unroll
@@ -1072,7 +1083,7 @@ __global__ void __launch_bounds__(DEC_THREADS, 1) k_decode_eigen(DecK a) {
             if (row < nrow) {
               const u32x4 v = (u32x4){sStr[33 * row + 4 * c], sStr[33 * row + 4 * c + 1], sStr[33 * row + 4 * c + 2],
                                       sStr[33 * row + 4 * c + 3]};
-              *reinterpret_cast<u32x4*>(obase + row * a.ld + 64 * r + 8 * c) = v;
+              __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(obase + row * a.ld + 64 * r + 8 * c));
             }
           }
         }
@@ -1163,6 +1174,18 @@ __device__ __forceinline__ void fwht128(float v[128]) {
         v[i] = x0 + x1;
         v[i + h] = x0 - x1;
       }
+}
+
+// 3-bit code of a rotated value c: the count of the sorted scaled
+// thresholds T_0 <= .. <= T_6 that are <= c, by binary search.
+__device__ __forceinline__ unsigned rht_code(float c, const float T[7]) {
+  const bool b2 = c >= T[3];
+  const float t1 = b2 ? T[5] : T[1];
+  const bool b1 = c >= t1;
+  const float ta = b1 ? T[6] : T[4], tb = b1 ? T[2] : T[0];
+  const float t0 = b2 ? ta : tb;
+  const bool b0 = c >= t0;
+  return (b2 ? 4u : 0u) | (b1 ? 2u : 0u) | (b0 ? 1u : 0u);
 }
 
 // Encode: a wave takes blocks of 32 tokens. The rotation H D x is one
@@ -1268,13 +1291,7 @@ __global__ void __launch_bounds__(SKETCH ? 64 * RHTS_WAVES : 64 * RHT_WAVES, SKE
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const float c = acc[e];
-        // count of thresholds <= c by binary search over the sorted T
-        const bool b2 = c >= T[3];
-        const float t1 = b2 ? T[5] : T[1];
-        const bool b1 = c >= t1;
-        const float t0 = b2 ? (b1 ? T[6] : T[4]) : (b1 ? T[2] : T[0]);
-        const bool b0 = c >= t0;
-        const unsigned q = (b2 ? 4u : 0u) + (b1 ? 2u : 0u) + (b0 ? 1u : 0u);
+        const unsigned q = rht_code(c, T);
         const int bp = 3 * (16 * mb + e);  // bit of channel 64h + 16mb + e in the half record
         w[bp >> 5] |= q << (bp & 31);
         if ((bp & 31) > 29) w[(bp >> 5) + 1] |= q >> (32 - (bp & 31));
@@ -1336,6 +1353,120 @@ __global__ void __launch_bounds__(SKETCH ? 64 * RHTS_WAVES : 64 * RHT_WAVES, SKE
         *reinterpret_cast<u32x2*>(a.sketch + s * a.sketch_stride + tk * 16 + 8 * h) = (u32x2){zw[0], zw[1]};
         if (h == 0) a.rnorm[s * a.rnorm_stride + tk] = sqrtf(ee) * 0.08838834764831845f;
       }
+    }
+  }
+}
+
+// Butterfly encode (no matrix product): the same blocks of 32 tokens per
+// wave and the same input fragments, lane (h, t) holding channels
+// 16 ks + 8 h + i (ks, i < 8) of token t. The signs D flip bf16 sign bits
+// by one XOR per value pair (masks per half in LDS); the fast Walsh-Hadamard
+// transform then runs in fp32 registers: the butterflies of channel bits 0,
+// 1, 2, 4, 5 and 6 inside the lane (64 values), then one permlane32 swap per
+// register pair trades channel bit 6 for bit 3 between the two halves of
+// the wave, and the bit-3 butterfly finishes inside the lane. Afterwards
+// lane (h, t) holds channels 64 h + [0, 64) of token t, the half record it
+// writes, exactly as the matrix-core kernel does; the quantizer and the
+// record layout are the same.
+constexpr int RHTB_WAVES = 4;
+__global__ void __launch_bounds__(64 * RHTB_WAVES, 4) k_rht_encode_bfly(RhtK a) {
+  __shared__ __align__(16) unsigned smask[2][32];
+  const long long s = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int t32 = lane & 31, h = lane >> 5;
+  const long long n = a.n_tokens;
+  const long long si = state_index(a.map, s, a.n_states);
+  if (si < 0) return;  // no state: records and norms untouched
+  const DevHdr* hdr = reinterpret_cast<const DevHdr*>(a.states + (size_t)si * STATE_BYTES + OFF_HDR);
+  if (tid < 64) {
+    // word k of half hh: channels c0 = 16 (k / 4) + 8 hh + 2 (k % 4) and c0 + 1 (bf16 sign bits 15, 31)
+    const int hh = tid >> 5, k = tid & 31;
+    const int c0 = 16 * (k >> 2) + 8 * hh + 2 * (k & 3);
+    smask[hh][k] = (hdr->sign[c0] < 0.0f ? 0x8000u : 0u) | (hdr->sign[c0 + 1] < 0.0f ? 0x80000000u : 0u);
+  }
+  float thr[7];
+#pragma unroll
+  for (int k = 0; k < 7; ++k) thr[k] = hdr->cb_thr[k];
+  __syncthreads();
+  const u32x4* mrow = reinterpret_cast<const u32x4*>(&smask[h][0]);
+  const long long nblk = (n + ENC_BT - 1) / ENC_BT;
+  const long long b0 = ((long long)blockIdx.x * RHTB_WAVES + wave) * RHT_BPW;
+  for (long long blk = b0; blk < b0 + RHT_BPW && blk < nblk; ++blk) {
+    const long long tok0 = blk * ENC_BT;
+    const unsigned last = (unsigned)(n - 1 - tok0);
+    const unsigned r = (unsigned)t32 < last ? (unsigned)t32 : last;
+    const unsigned short* row = static_cast<const unsigned short*>(a.x) + s * a.x_stride + (tok0 + r) * a.ld;
+    u32x4 xw[8];
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) xw[ks] = *reinterpret_cast<const u32x4*>(row + 16 * ks + 8 * h);
+    float ss = 0.0f;
+    // v[8 ks + i]: channel 16 ks + 8 h + i; D and the bit-0 butterfly on each bf16 pair
+    float v[64];
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const u32x4 m = mrow[ks];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const unsigned w = xw[ks][e];
+        const float x0 = __uint_as_float(w << 16), x1 = __uint_as_float(w & 0xffff0000u);
+        ss = __builtin_fmaf(x0, x0, ss);
+        ss = __builtin_fmaf(x1, x1, ss);
+        const unsigned ws = w ^ m[e];
+        const float y0 = __uint_as_float(ws << 16), y1 = __uint_as_float(ws & 0xffff0000u);
+        v[8 * ks + 2 * e] = y0 + y1;
+        v[8 * ks + 2 * e + 1] = y0 - y1;
+      }
+    }
+    {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(ss), __float_as_uint(ss), false, false);
+      const unsigned s_lo = sw[0], s_hi = sw[1];
+      ss = __uint_as_float(s_lo) + __uint_as_float(s_hi);
+    }
+    // channel bits 1, 2 (register bits 1, 2) and 4, 5, 6 (register bits 3, 4, 5)
+#pragma unroll
+    for (int hb = 2; hb < 64; hb <<= 1)
+#pragma unroll
+      for (int i = 0; i < 64; ++i)
+        if (!(i & hb)) {
+          const float p = v[i], q = v[i + hb];
+          v[i] = p + q;
+          v[i + hb] = p - q;
+        }
+    // channel bit 3 across the halves: lower lanes receive the pair of v[i]
+    // (channel bit 6 clear), upper lanes that of v[i + 32]; afterwards v[i]
+    // is channel 64 h + 16 (i / 8) + i % 8 and v[i + 32] the same + 8
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[i]), __float_as_uint(v[i + 32]), false,
+                                                        false);
+      const float p = __uint_as_float(sw[0]), q = __uint_as_float(sw[1]);
+      v[i] = p + q;
+      v[i + 32] = p - q;
+    }
+    const float nu = sqrtf(ss);
+    const float sc = nu * 11.313708498984761f;
+    float T[7];
+#pragma unroll
+    for (int k = 0; k < 7; ++k) T[k] = nu > 0.0f ? thr[k] * sc : thr[k];
+    unsigned w[6] = {0u, 0u, 0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 64; ++i) {
+      const int jl = 16 * ((i & 31) >> 3) + 8 * (i >> 5) + (i & 7);  // channel 64 h + jl
+      const unsigned q = rht_code(v[i], T);
+      const int bp = 3 * jl;
+      w[bp >> 5] |= q << (bp & 31);
+      if ((bp & 31) > 29) w[(bp >> 5) + 1] |= q >> (32 - (bp & 31));
+      if ((i & 7) == 7) __builtin_amdgcn_sched_barrier(0);  // compare masks of 8 values live at a time
+    }
+    if (tok0 + t32 < n) {
+      const long long tk = a.n_old + tok0 + t32;
+      u32x2* dst = reinterpret_cast<u32x2*>(a.packed + s * a.packed_stride + tk * 48 + 24 * h);
+      dst[0] = (u32x2){w[0], w[1]};
+      dst[1] = (u32x2){w[2], w[3]};
+      dst[2] = (u32x2){w[4], w[5]};
+      if (h == 0) a.norms[s * a.norms_stride + tk] = nu;
     }
   }
 }
@@ -1411,8 +1542,8 @@ __global__ void __launch_bounds__(RHTD_T) k_rht_decode(RhtK a) {
   unsigned char* obase = static_cast<unsigned char*>(a.xo) + (s * a.x_stride + tok0 * a.ld) * esz;
   for (int i = t; i < ntok * cpr; i += RHTD_T) {
     const int r = i / cpr, c = i - r * cpr;
-    *reinterpret_cast<u32x4*>(obase + ((long long)r * a.ld) * esz + 16 * c) =
-        *reinterpret_cast<const u32x4*>(smem + r * rowb + 16 * c);
+    __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(smem + r * rowb + 16 * c),
+                                reinterpret_cast<u32x4*>(obase + ((long long)r * a.ld) * esz + 16 * c));
   }
 }
 
@@ -1445,6 +1576,9 @@ int launch_encode_rht(const EncodeLaunch& L, void* stream) {
     }
     dim3 grid((unsigned)((nblk + RHTS_WAVES * RHT_BPW - 1) / (RHTS_WAVES * RHT_BPW)), (unsigned)L.n_streams);
     hipLaunchKernelGGL(k_rht_encode<true>, grid, dim3(64 * RHTS_WAVES), RHTS_LDS, (hipStream_t)stream, a);
+  } else if (rht_encode_kernel() == 1) {
+    dim3 grid((unsigned)((nblk + RHTB_WAVES * RHT_BPW - 1) / (RHTB_WAVES * RHT_BPW)), (unsigned)L.n_streams);
+    hipLaunchKernelGGL(k_rht_encode_bfly, grid, dim3(64 * RHTB_WAVES), 0, (hipStream_t)stream, a);
   } else {
     dim3 grid((unsigned)((nblk + RHT_WAVES * RHT_BPW - 1) / (RHT_WAVES * RHT_BPW)), (unsigned)L.n_streams);
     hipLaunchKernelGGL(k_rht_encode<false>, grid, dim3(64 * RHT_WAVES), RHT_LDS, (hipStream_t)stream, a);

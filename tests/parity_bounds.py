@@ -63,8 +63,10 @@ def assert_code_diffs_at_boundaries(q_gpu, q_or, c, st, eps, step_rel=0.0, max_f
 
 
 def rht_rotation_eps(x):
-    """Walsh-Hadamard encode: the kernel forms H D x exactly in bf16 products
-    (entries +-1) summed in fp32 (128 terms: error <= 128 * 2^-24 sum |x|), the
+    """Walsh-Hadamard encode: the kernel forms H D x either from exact bf16
+    products (entries +-1) summed in fp32 on the matrix cores (128 terms: error
+    <= 128 * 2^-24 sum |x|) or by seven fp32 butterfly stages (each output's
+    error <= 7 * 2^-24 sum |x|, inside the same bound), the
     norm |x| in fp32 (relative error <= 2^-18, one sum of squares and a square
     root) and compares against thresholds scaled by |x| sqrt(d) in fp32. In units
     of y = H D x / (|x| sqrt(d)) the bound per token is

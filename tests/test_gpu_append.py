@@ -83,7 +83,17 @@ def rht_codebook():
     return rht.codebook_fp32(c)
 
 
-def test_append_walsh_hadamard(rht_codebook):
+@pytest.mark.parametrize("kernel", [stc.RHT_ENCODE_MFMA, stc.RHT_ENCODE_BUTTERFLY], ids=["mfma", "butterfly"])
+def test_append_walsh_hadamard(rht_codebook, kernel):
+    before = stc.get_rht_encode_kernel()
+    stc.set_rht_encode_kernel(kernel)
+    try:
+        _append_walsh_hadamard(rht_codebook)
+    finally:
+        stc.set_rht_encode_kernel(before)
+
+
+def _append_walsh_hadamard(rht_codebook):
     w = synth.WORKLOADS[3]
     n = CHUNKS[-1]
     xs = [synth.stream(w, 0, 0, h, 0, n=n) for h in range(2)]

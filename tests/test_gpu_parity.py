@@ -398,8 +398,17 @@ def rht_codebook():
     return rht.codebook_fp32(c)
 
 
+@pytest.fixture(params=[stc.RHT_ENCODE_MFMA, stc.RHT_ENCODE_BUTTERFLY], ids=["mfma", "butterfly"])
+def rht_kernel(request):
+    """Runs the test once per Walsh-Hadamard encode kernel."""
+    before = stc.get_rht_encode_kernel()
+    stc.set_rht_encode_kernel(request.param)
+    yield request.param
+    stc.set_rht_encode_kernel(before)
+
+
 @pytest.mark.parametrize("n", [1, 1000, 32768])
-def test_rht_encode_matches_oracle(rht_codebook, n):
+def test_rht_encode_matches_oracle(rht_codebook, rht_kernel, n):
     w = synth.WORKLOADS[3]
     x = synth.stream(w, 0, 0, 2, 0, n=n)
     signs = synth.random_signs(3, 0, 0, 2, 0)
@@ -432,7 +441,7 @@ def test_rht_decode_matches_oracle(rht_codebook):
     assert np.all(np.abs(xg - xo) <= 1.01 * np.abs(exact) * 2.0 ** -7 + 1e-6 * np.abs(exact).max())
 
 
-def test_rht_batched(rht_codebook):
+def test_rht_batched(rht_codebook, rht_kernel):
     w = synth.WORKLOADS[3]
     n = 2000
     xs = [synth.stream(w, 0, 0, h, 0, n=n) for h in range(3)]

@@ -191,3 +191,20 @@ def test_check_state_map_validates_arguments_without_device_work():
     assert L.stc_check_state_map(None, 3, 4, None) == _abi.STC_EINVAL
     assert b"NULL map" in L.stc_last_error()
     assert L.stc_check_state_map(None, -1, 4, None) == _abi.STC_EINVAL
+
+
+def test_rht_encode_kernel_choice():
+    """The Walsh-Hadamard encode kernel choice takes the two declared kinds and
+    refuses others, leaving the previous choice in place."""
+    L = _abi.lib()
+    before = L.stc_get_rht_encode_kernel()
+    try:
+        assert L.stc_set_rht_encode_kernel(1) == _abi.STC_OK
+        assert L.stc_get_rht_encode_kernel() == 1
+        assert L.stc_set_rht_encode_kernel(2) == _abi.STC_EINVAL
+        assert L.stc_set_rht_encode_kernel(-1) == _abi.STC_EINVAL
+        assert L.stc_get_rht_encode_kernel() == 1
+        assert L.stc_set_rht_encode_kernel(0) == _abi.STC_OK
+        assert L.stc_get_rht_encode_kernel() == 0
+    finally:
+        L.stc_set_rht_encode_kernel(before)
