@@ -435,8 +435,11 @@ stc_status stc_attend_rht_batched(const void* states_dev, int64_t n_states,
  * records are those a full encode would write (the stream is append-only),
  * and attention reads them back from the packed cache like every other
  * token. EIGEN/IDENTITY states only; ws_dev as for
- * stc_attend_compressed_batched with n_old + 1 tokens. Four launches on
- * `stream` (the two appends, attention, the split merge). */
+ * stc_attend_compressed_batched with n_old + 1 tokens; the new-token rows
+ * must be 16-byte aligned. With bf16 rows the launches on `stream` are
+ * those of the attention call alone: its first launch (per-KV-head score
+ * weights) also forms and appends the two records, which the next launch
+ * reads; fp32 rows take one launch more for the appends. */
 stc_status stc_decode_step_batched(const void* states_dev, int64_t n_states,
                                    const int32_t* k_state_of_pair_dev,
                                    const int32_t* v_state_of_pair_dev, const stc_head_info* infos,

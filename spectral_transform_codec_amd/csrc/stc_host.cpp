@@ -1166,7 +1166,8 @@ static stc_status attend_eigen(const char* who, const void* states_dev, int64_t 
                                const int32_t* v_map, const stc_head_info* infos, int64_t n_pairs, int64_t n_tokens,
                                const void* k_packed_dev, const void* v_packed_dev, int64_t packed_pair_stride,
                                int32_t group, const float* q_dev, float* out_dev, float scale, void* ws_dev,
-                               size_t ws_bytes, bool scratch, stc_stream_t stream) {
+                               size_t ws_bytes, bool scratch, stc_stream_t stream,
+                               const void* k_new = nullptr, const void* v_new = nullptr, int new_f32 = 0) {
   bool rht = false;
   int mb = 0;
   if (stc_status s = check_batch("attend_compressed", states_dev, n_states, infos, n_pairs, n_tokens,
@@ -1198,6 +1199,9 @@ static stc_status attend_eigen(const char* who, const void* states_dev, int64_t 
   a.att_chunks = attend_chunks(infos, n_states);
   a.max_vcols = attend_vcols(infos, n_states);
   a.rec256 = records_256(infos, n_states);
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.new_f32 = new_f32;
   if (launch_attend(a, stream)) return fail(STC_EDEVICE, "attend launch: %s", hipGetErrorString(hipGetLastError()));
   return ok();
 }
@@ -1358,18 +1362,17 @@ stc_status stc_decode_step_batched(const void* states_dev, int64_t n_states, con
   if (group < 1 || group > 16) return fail(STC_EUNSUPPORTED, "decode_step: group %d outside 1..16", group);
   if (!q_dev || !out_dev || !ws_dev) return fail(STC_EINVAL, "decode_step: NULL buffer");
   if (!std::isfinite(scale)) return fail(STC_EINVAL, "decode_step: scale must be finite");
+  if (dtype != STC_F32 && dtype != STC_BF16) return fail(STC_EUNSUPPORTED, "decode_step: dtype %d", dtype);
+  if (n_pairs > 0 && (!k_new_dev || !v_new_dev)) return fail(STC_EINVAL, "decode_step: NULL new-token rows");
+  if (!aligned(k_new_dev, 16) || !aligned(v_new_dev, 16))
+    return fail(STC_EINVAL, "decode_step: new-token rows must be 16-byte aligned");
   const size_t need = stc_attend_workspace_bytes(n_pairs, group, n_old + 1);
   if (ws_bytes < need) return fail(STC_EWORKSPACE, "decode_step: workspace %zu < %zu", ws_bytes, need);
-  // the new K and V token of every KV head, then one attention step over all n_old + 1
-  if (stc_status s = encode_impl("decode_step (K append)", states_dev, n_states, k_map, infos, n_pairs, n_old, 1,
-                                 k_new_dev, dtype, D, D, k_packed_dev, packed_pair_stride, nullptr, 0, stream))
-    return s;
-  if (stc_status s = encode_impl("decode_step (V append)", states_dev, n_states, v_map, infos, n_pairs, n_old, 1,
-                                 v_new_dev, dtype, D, D, v_packed_dev, packed_pair_stride, nullptr, 0, stream))
-    return s;
-  return stc_attend_compressed_batched(states_dev, n_states, k_map, v_map, infos, n_pairs, n_old + 1, k_packed_dev,
-                                       v_packed_dev, packed_pair_stride, group, q_dev, out_dev, scale, ws_dev,
-                                       ws_bytes, stream);
+  // the new K and V token of every KV head are appended by the attention's
+  // first launch, then attention runs over all n_old + 1 tokens
+  return attend_eigen("decode_step", states_dev, n_states, k_map, v_map, infos, n_pairs, n_old + 1, k_packed_dev,
+                      v_packed_dev, packed_pair_stride, group, q_dev, out_dev, scale, ws_dev, ws_bytes, false, stream,
+                      k_new_dev, v_new_dev, dtype == STC_F32 ? 1 : 0);
 }
 
 }  // extern "C"

@@ -230,6 +230,11 @@ struct AttendLaunch {
                        // start 4, 8 or 12 bytes past a 16-byte boundary)
   int max_vcols = 256;  // value columns of the states at most (code fragments cut at record bytes)
   bool rec256 = false;  // every record is 256 bits
+  // generation step: new K and V rows [pair][128] appended as token n_tokens - 1
+  // before the attention reads the caches (eigen / identity states, no sketch)
+  const void* k_new = nullptr;
+  const void* v_new = nullptr;
+  int new_f32 = 0;
 };
 
 int launch_gram(const void* x, int dtype, int64_t ld, int64_t n_calib, double* gram, void* stream);

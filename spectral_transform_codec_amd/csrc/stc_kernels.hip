@@ -1653,6 +1653,12 @@ struct AttK {
   const float* k_rnorm;
   long long sketch_stride, rnorm_stride;
   float* prep;  // per pair of the launch: score weights and head scales (k_att2_prep), ATT_PREP_FLOATS each
+  // generation step: pair p's new K and V token rows (128 elements, bf16 or
+  // fp32) appended as token n_tokens - 1 before the scores are formed; null
+  // for a plain attention call
+  const void* k_new;
+  const void* v_new;
+  int new_f32;
 };
 
 constexpr int ATT_WAVES_MAX = 16;
@@ -2522,6 +2528,122 @@ __device__ __forceinline__ void at2_stage_rel(unsigned (&rel)[NCH], unsigned& sh
 // channel j and all eight heads (its 16 loads in flight at once); the eight
 // parts are added through LDS.
 constexpr int PREP_PARTS = 8;
+// Generation-step append, one wave per stream: the record of one token is
+// formed exactly as k_encode_eigen forms it (the same MFMA chain on the same
+// basis rows, the token in every column of the block, the same quantizer and
+// group words), so the appended bytes equal those of an encode of the whole
+// stream. It is written over the stream's words from the record's first bit
+// to the 16-byte end of the stream; the bits of earlier records in its first
+// word are kept. sbuf: 64 words of LDS for this wave.
+template <bool F32>
+__device__ void append_record(const unsigned char* st, const void* x, unsigned char* stream, long long n_old,
+                              unsigned* sbuf, int lane) {
+  const DevHdr* hdr = reinterpret_cast<const DevHdr*>(st + OFF_HDR);
+  const unsigned B = (unsigned)__builtin_amdgcn_readfirstlane(hdr->total_bits);
+  if (B == 0) return;  // no kept channel: the stream has no bytes
+  const int t32 = lane & 31, h = lane >> 5;
+  bf16x8 xh[8], xl[8];
+  if (F32) {
+    const float* row = static_cast<const float*>(x);
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const f32x4 v0 = *reinterpret_cast<const f32x4*>(row + 16 * ks + 8 * h);
+      const f32x4 v1 = *reinterpret_cast<const f32x4*>(row + 16 * ks + 8 * h + 4);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float f = e < 4 ? v0[e] : v1[e - 4];
+        const __bf16 hi = (__bf16)f;
+        xh[ks][e] = hi;
+        xl[ks][e] = (__bf16)(f - (float)hi);
+      }
+    }
+  } else {
+    const unsigned short* row = static_cast<const unsigned short*>(x);
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) xh[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(row + 16 * ks + 8 * h));
+  }
+  sbuf[lane] = 0u;
+  __builtin_amdgcn_s_waitcnt(0xc07f);
+  __builtin_amdgcn_wave_barrier();
+  const long long P0 = n_old * (long long)B;
+  const unsigned sh0 = (unsigned)(P0 & 31);
+  const unsigned char* uh = st + OFF_UT_HI + t32 * 256 + 16 * h;
+  const unsigned char* ul = st + OFF_UT_LO + t32 * 256 + 16 * h;
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) {
+    // channels 64h + 16mb + 4i + j of the token in acc[4i + j] (rows of the
+    // basis permuted by the state builder), the chain started from yhalf
+    f32x16 acc;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[4 * i + j] = hdr->yhalf[64 * h + 16 * mb + 4 * i + j];
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const bf16x8 ah = *reinterpret_cast<const bf16x8*>(uh + 32 * mb * 256 + 32 * ks);
+      const bf16x8 al = *reinterpret_cast<const bf16x8*>(ul + 32 * mb * 256 + 32 * ks);
+      acc = mfma32_bf16(ah, xh[ks], acc);
+      acc = mfma32_bf16(al, xh[ks], acc);
+      if (F32) acc = mfma32_bf16(ah, xl[ks], acc);
+    }
+    if (t32 == 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int c0 = 64 * h + 16 * mb + 4 * i;
+        const unsigned goff = (unsigned)hdr->off[c0];
+        unsigned word = 0u;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const unsigned q = (unsigned)__builtin_amdgcn_fmed3f(acc[4 * i + j], 0.0f, (float)hdr->lm1[c0 + j]);
+          word |= q << ((unsigned)hdr->off[c0 + j] - goff);
+        }
+        const unsigned rb = sh0 + goff;
+        const unsigned long long v = (unsigned long long)word << (rb & 31u);
+        __hip_atomic_fetch_or(sbuf + (rb >> 5), (unsigned)v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        __hip_atomic_fetch_or(sbuf + (rb >> 5) + 1, (unsigned)(v >> 32), __ATOMIC_RELAXED,
+                              __HIP_MEMORY_SCOPE_WORKGROUP);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);  // one row block's basis rows in registers at a time
+  }
+  __builtin_amdgcn_s_waitcnt(0xc07f);
+  __builtin_amdgcn_wave_barrier();
+  const long long w0 = P0 >> 5;
+  const int nw = (int)(packed_len((long long)B, n_old + 1) / 4 - w0);  // <= 33 + 3 words
+  unsigned* s32 = reinterpret_cast<unsigned*>(stream);
+  if (lane < nw) {
+    unsigned v = sbuf[lane];
+    if (lane == 0 && sh0 != 0u) v |= s32[w0] & ((1u << sh0) - 1u);
+    s32[w0 + lane] = v;
+  }
+}
+
+// The appends of a generation step, K on wave 0 and V on wave 1 (streams
+// without a state are left as they are). F32: fp32 token rows (else bf16).
+template <bool F32>
+__device__ __forceinline__ void att_append_pair(const AttK& a, long long pg, long long ksi, long long vsi,
+                                                unsigned (*sbuf)[64], int tid) {
+  const int wave = tid >> 6, lane = tid & 63;
+  const long long n_old = a.n_tokens - 1;
+  const long long si = wave == 0 ? ksi : vsi;
+  if (wave > 1 || si < 0) return;
+  const unsigned char* st = (wave == 0 ? a.k_states : a.v_states) + (size_t)si * STATE_BYTES;
+  unsigned char* stream = const_cast<unsigned char*>(wave == 0 ? a.k_packed : a.v_packed) + pg * a.packed_stride;
+  const unsigned char* x = static_cast<const unsigned char*>(wave == 0 ? a.k_new : a.v_new) + pg * 128 * (F32 ? 4 : 2);
+  append_record<F32>(st, x, stream, n_old, sbuf[wave], lane);
+}
+
+// The appends in a launch of their own: fp32 token rows (their three-pass
+// chain needs more registers than the prep kernel's 1024 threads leave), or
+// attention instances without the prep launch.
+__global__ void __launch_bounds__(128) k_att_append(AttK a) {
+  __shared__ unsigned sbuf[2][64];
+  const long long pg = a.pair_base + blockIdx.x;
+  const long long ksi = state_index(a.k_map, pg, a.n_states), vsi = state_index(a.v_map, pg, a.n_states);
+  if (a.new_f32) att_append_pair<true>(a, pg, ksi, vsi, sbuf, threadIdx.x);
+  else att_append_pair<false>(a, pg, ksi, vsi, sbuf, threadIdx.x);
+}
+
 __global__ void __launch_bounds__(128 * PREP_PARTS) k_att2_prep(AttK a) {
   __shared__ __align__(16) float sqT[128 * 8];   // q^T [128][8]
   __shared__ float red[PREP_PARTS][8][128];
@@ -2529,6 +2651,10 @@ __global__ void __launch_bounds__(128 * PREP_PARTS) k_att2_prep(AttK a) {
   const long long p = blockIdx.x, pg = a.pair_base + p;
   const int g = a.group;
   const long long ksi = state_index(a.k_map, pg, a.n_states), vsi = state_index(a.v_map, pg, a.n_states);
+  __shared__ unsigned sapp[2][64];
+  // generation step: the new token's K and V records go into the caches
+  // first (the main kernel, the next launch, reads them with the rest)
+  if (a.k_new && !a.new_f32) att_append_pair<false>(a, pg, ksi, vsi, sapp, tid);
   if (ksi < 0 || vsi < 0) return;  // (the main kernel writes nothing for this pair either)
   const unsigned char* kst = a.k_states + (size_t)ksi * STATE_BYTES;
   const DevHdr* hk = reinterpret_cast<const DevHdr*>(kst);
@@ -3077,6 +3203,9 @@ int launch_attend(const AttendLaunch& L, void* stream) {
   a.k_rnorm = L.k_rnorm;
   a.sketch_stride = L.sketch_stride;
   a.rnorm_stride = L.rnorm_stride;
+  a.k_new = L.k_new;
+  a.v_new = L.v_new;
+  a.new_f32 = L.new_f32;
   a.stream_words = att_stream_words(L.max_bits);
   a.region_words = att_region_words(L.max_bits);
   const bool sketch = L.k_sketch != nullptr;
@@ -3118,6 +3247,7 @@ int launch_attend(const AttendLaunch& L, void* stream) {
     const dim3 grid((unsigned)a.n_splits, (unsigned)np);
     if (inst >= 0) {
       a.prep = reinterpret_cast<float*>(a.ws) + att_partial_floats(np, L.n_tokens, L.group, round);
+      if (L.k_new && L.new_f32) hipLaunchKernelGGL(k_att_append, dim3((unsigned)np), dim3(128), 0, s, a);
       hipLaunchKernelGGL(k_att2_prep, dim3((unsigned)np), dim3(128 * PREP_PARTS), 0, s, a);
       switch (inst) {
         case 0: at2_launch<4, 10, 1, 4, true, true>(grid, s, a); break;
@@ -3130,6 +3260,7 @@ int launch_attend(const AttendLaunch& L, void* stream) {
         default: at2_launch<8, 12, 3, 8, false, false>(grid, s, a); break;
       }
     } else {
+      if (L.k_new) hipLaunchKernelGGL(k_att_append, dim3((unsigned)np), dim3(128), 0, s, a);
       const int var = sketch ? (L.rht ? 0 : (L.max_bits <= 512 ? 1 : 2)) : (L.rht ? 3 : (L.max_bits <= 512 ? 4 : 5));
       hipLaunchKernelGGL(kAttKernels[var][L.rec && !L.rht ? 1 : 0], grid, dim3(64 * waves), att_lds, s, a);
     }

@@ -108,20 +108,25 @@ def _append_walsh_hadamard(rht_codebook):
     assert torch.equal(norms[:, :n], fnorm)
 
 
-@pytest.mark.parametrize("n_old,g", [(777, 4), (31, 7), (0, 4)])
-def test_decode_step_equals_attention_over_full_cache(n_old, g):
+# The new tokens' records are formed inside the attention's first launch for
+# bf16 rows; fp32 rows, groups above 8 and records above 512 bits take the
+# appends' own launch. Both must equal an encode of the whole stream.
+@pytest.mark.parametrize("n_old,g,dtype,budget", [(777, 4, "bf16", 2.0), (31, 7, "bf16", 2.0), (0, 4, "bf16", 2.0),
+                                                  (500, 4, "f32", 2.0), (95, 8, "f32", 4.0),
+                                                  (300, 16, "bf16", 2.0), (200, 4, "bf16", 6.0)])
+def test_decode_step_equals_attention_over_full_cache(n_old, g, dtype, budget):
     w = synth.WORKLOADS[2]
     pairs = 3
     n = n_old + 1
     ks = [synth.stream(w, 0, 0, h, 0, n=n) for h in range(pairs)]
     vs = [synth.stream(w, 0, 0, h, 1, n=n) for h in range(pairs)]
-    sk = [codec.calibrate_head(synth.stream(w, 0, 0, h, 0, n=2048), 2048, 2.0) for h in range(pairs)]
-    sv = [codec.calibrate_head(synth.stream(w, 0, 0, h, 1, n=2048), 2048, 2.0) for h in range(pairs)]
+    sk = [codec.calibrate_head(synth.stream(w, 0, 0, h, 0, n=2048), 2048, budget) for h in range(pairs)]
+    sv = [codec.calibrate_head(synth.stream(w, 0, 0, h, 1, n=2048), 2048, budget) for h in range(pairs)]
     arr = stc.StateArray([gpu_state(s) for pair in zip(sk, sv) for s in pair])
     kmap = torch.arange(0, 2 * pairs, 2, dtype=torch.int32, device=DEV)
     vmap = kmap + 1
-    kx = torch.stack([dev_tensor(k, "bf16") for k in ks])
-    vx = torch.stack([dev_tensor(v, "bf16") for v in vs])
+    kx = torch.stack([dev_tensor(k, dtype) for k in ks])
+    vx = torch.stack([dev_tensor(v, dtype) for v in vs])
     rng = np.random.default_rng(5 + n_old)
     q = torch.from_numpy(rng.standard_normal((pairs, g, 128)).astype(np.float32)).to(DEV)
     stride = stc.packed_bytes(arr.max_bits, n)
