@@ -201,7 +201,7 @@ def layer_step(args, dev):
     budgets = list(w.budgets)
     arrays = {}
     for b in budgets:
-        arrays[b] = stc.StateArray([stc.calibrate_head(x2[s], w.n_calib, b) for s in range(S)])
+        arrays[b] = stc.calibrate_heads_batched(x2, w.n_calib, b)
     torch.cuda.synchronize()
     cal_s = time.time() - t_cal
     cb, _ = stc.lloyd_max(synth.sphere_coordinate_samples())
@@ -530,18 +530,17 @@ def build_cache(w, n, dev):
     torch.cuda.synchronize()
     setup_s = time.time() - t_setup
     t_cal = time.time()
-    states, smap = [], []
-    for l in range(L):
-        for b in range(Bt):
-            for h in range(H):
-                for kind in (0, 1):
-                    s_ = ((l * Bt + b) * H + h) * 2 + kind
-                    if w.share_over_batch and b > 0:
-                        smap.append(smap[((l * Bt + 0) * H + h) * 2 + kind])
-                    else:
-                        states.append(stc.calibrate_head(x[s_], min(w.n_calib, n), budget))
-                        smap.append(len(states) - 1)
-    arr = stc.StateArray(states)
+    n_c = min(w.n_calib, n)
+    if w.share_over_batch:
+        # batch entry 0 of every (layer, KV head, K/V), gathered into one
+        # [L * H * 2][n_calib][128] tensor; state index (l, h, kind)
+        xc = x.view(L, Bt, H * 2, n, 128)[:, 0, :, :n_c].reshape(L * H * 2, n_c, 128)
+        smap = [(l * H + h) * 2 + kind for l in range(L) for b in range(Bt) for h in range(H) for kind in (0, 1)]
+    else:
+        xc = x[:, :n_c]
+        smap = list(range(S))
+    arr = stc.calibrate_heads_batched(xc, n_c, budget)
+    del xc
     torch.cuda.synchronize()
     cal_s = time.time() - t_cal
     smap_t = torch.tensor(smap, dtype=torch.int32, device=dev)

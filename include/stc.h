@@ -220,6 +220,22 @@ stc_status stc_calibrate_head(int32_t d, int64_t n_calib, const void* x_dev, int
                               int64_t ld, float avg_bits, const uint8_t* bits, int32_t xform,
                               stc_head_info* info, void* state_dev, stc_stream_t stream);
 
+/* Calibrate n_streams heads in one call (same SPECTRA summary passages as
+ * stc_calibrate_head): stream s takes the first n_calib rows at
+ * x_dev + s * x_stream_stride elements (row stride ld, dtype STC_BF16 or
+ * STC_F32), its widths by stc_water_fill of avg_bits, and its state goes to
+ * states_dev + s * stc_state_bytes() (256-byte aligned; the layout of the
+ * batched calls) with its summary in infos[s]. One launch forms every second
+ * moment; the eigenbases, widths and blobs are then built on host threads
+ * and uploaded at once. Each state equals the one stc_calibrate_head would
+ * build from the same rows. Synchronizes `stream`. A failing stream (a
+ * non-finite second moment, ...) returns its status, names the stream in
+ * stc_last_error and leaves the states undefined. */
+stc_status stc_calibrate_heads_batched(int32_t d, int64_t n_streams, int64_t n_calib,
+                                       const void* x_dev, int32_t dtype, int64_t ld,
+                                       int64_t x_stream_stride, float avg_bits, int32_t xform,
+                                       stc_head_info* infos, void* states_dev, stc_stream_t stream);
+
 /* Read back a state's basis as fp32, row-major d*d (u[i*d+j] = U_ij).
  * Synchronizes `stream`. */
 stc_status stc_state_basis(const void* state_dev, float* u_out, stc_stream_t stream);

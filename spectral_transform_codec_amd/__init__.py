@@ -22,7 +22,7 @@ __all__ = [
     "encode_kv_batched", "decode_kv_batched", "attend_compressed", "attend_compressed_batched",
     "quantize_pack_f32", "state_bytes", "packed_bytes", "attend_workspace_bytes", "total_bits",
     "delta_star", "water_fill", "eigh", "lloyd_max", "StcError", "set_rht_encode_kernel",
-    "get_rht_encode_kernel", "RHT_ENCODE_MFMA", "RHT_ENCODE_BUTTERFLY",
+    "get_rht_encode_kernel", "RHT_ENCODE_MFMA", "RHT_ENCODE_BUTTERFLY", "calibrate_heads_batched",
 ]
 
 _P = ctypes.POINTER
@@ -220,6 +220,36 @@ class StateArray:
         self.n = len(states)
         self.max_bits = max(int(s.info.total_bits) for s in states)
         self.xform = int(states[0].info.xform)
+
+    @classmethod
+    def _from_blob(cls, blob: torch.Tensor, infos) -> "StateArray":
+        """An array over an existing [n][state_bytes] blob and its summaries
+        (the states are views of the blob)."""
+        self = cls.__new__(cls)
+        self.blob = blob
+        self.infos = infos
+        self.n = blob.shape[0]
+        self.states = []
+        for i in range(self.n):
+            info = HeadInfo()
+            ctypes.memmove(ctypes.byref(info), ctypes.byref(infos[i]), ctypes.sizeof(HeadInfo))
+            self.states.append(State(blob[i], info))
+        self.max_bits = max(int(infos[i].total_bits) for i in range(self.n))
+        self.xform = int(infos[0].xform)
+        return self
+
+
+def calibrate_heads_batched(x: torch.Tensor, n_calib: int, avg_bits: float, xform: int = XFORM_EIGEN) -> StateArray:
+    """x: [S][n][128] bf16/fp32 on the GPU (row and stream strides from the
+    tensor): one state per stream from its first n_calib rows, in one call."""
+    assert x.dim() == 3 and x.shape[2] == D and x.stride(2) == 1 and x.shape[1] >= n_calib
+    S = x.shape[0]
+    infos = (HeadInfo * S)()
+    blob = torch.zeros((S, state_bytes()), dtype=torch.uint8, device=x.device)
+    check("stc_calibrate_heads_batched", lib().stc_calibrate_heads_batched(
+        D, S, int(n_calib), _ptr(x), _dtype_code(x), x.stride(1), x.stride(0), float(avg_bits), xform, infos,
+        _ptr(blob), _stream()))
+    return StateArray._from_blob(blob, infos)
 
 
 # ------------------------------------------------------------------ codec

@@ -36,6 +36,8 @@ SIGNATURES = {
     "stc_rht_state_init": (c_i32, [c_i32, P(ctypes.c_int8), P(c_f32), P(HeadInfo), c_vp, c_vp]),
     "stc_calibrate_head": (c_i32, [c_i32, c_i64, c_vp, c_i32, c_i64, c_f32, P(c_u8), c_i32, P(HeadInfo),
                                    c_vp, c_vp]),
+    "stc_calibrate_heads_batched": (c_i32, [c_i32, c_i64, c_i64, c_vp, c_i32, c_i64, c_i64, c_f32, c_i32,
+                                            P(HeadInfo), c_vp, c_vp]),
     "stc_state_basis": (c_i32, [c_vp, P(c_f32), c_vp]),
     "stc_encode_kv_batched": (c_i32, [c_vp, c_i64, c_vp, P(HeadInfo), c_i64, c_i64, c_vp, c_i32, c_i64, c_i64,
                                       c_vp, c_i64, c_vp, c_vp]),

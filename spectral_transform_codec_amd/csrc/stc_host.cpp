@@ -19,6 +19,7 @@
 #include <limits>
 #include <numeric>
 #include <string>
+#include <thread>
 #include <vector>
 
 #include "stc_internal.h"
@@ -811,53 +812,145 @@ stc_status stc_rht_sketch_state_init(int32_t d, const int8_t* signs, const float
   return rht_state_build(d, signs, codebook, sketch, info, state_dev, stream);
 }
 
-stc_status stc_calibrate_head(int32_t d, int64_t n_calib, const void* x_dev, int32_t dtype, int64_t ld,
-                              float avg_bits, const uint8_t* bits, int32_t xform, stc_head_info* info,
-                              void* state_dev, stc_stream_t stream) {
-  if (d != D) return fail(STC_EUNSUPPORTED, "calibrate_head: d=%d (only %d is supported)", d, D);
+}  // extern "C"
+
+namespace {
+
+// Calibration arguments shared by the single and batched calls; budget out.
+stc_status check_calibration(const char* who, int32_t d, int64_t n_calib, const void* x_dev, int32_t dtype,
+                             int64_t ld, float avg_bits, const uint8_t* bits, int32_t xform, int32_t* budget) {
+  if (d != D) return fail(STC_EUNSUPPORTED, "%s: d=%d (only %d is supported)", who, d, D);
   if (xform != STC_XFORM_EIGEN && xform != STC_XFORM_IDENTITY)
-    return fail(STC_EUNSUPPORTED, "calibrate_head: xform %d (use stc_rht_state_init for RHT)", xform);
-  if (dtype != STC_F32 && dtype != STC_BF16) return fail(STC_EUNSUPPORTED, "calibrate_head: dtype %d", dtype);
-  if (!x_dev || !info) return fail(STC_EINVAL, "calibrate_head: NULL argument");
-  if (n_calib <= 0) return fail(STC_EINVAL, "calibrate_head: n_calib must be positive");
-  if (ld < d) return fail(STC_EINVAL, "calibrate_head: ld < d");
-  if (!aligned(x_dev, 16) || (ld * elem_size(dtype)) % 16) return fail(STC_EINVAL, "calibrate_head: x rows must be 16-byte aligned");
-  if (stc_status s = check_state_ptr(state_dev, "state_dev")) return s;
-  if (!(avg_bits >= 0.0f) || !std::isfinite(avg_bits)) return fail(STC_EBUDGET, "calibrate_head: bad budget");
-  const int32_t budget = stc_total_bits(avg_bits, d);
-  if (budget > STC_MAX_BITS * d) return fail(STC_EBUDGET, "calibrate_head: budget %d > %d", budget, STC_MAX_BITS * d);
+    return fail(STC_EUNSUPPORTED, "%s: xform %d (use stc_rht_state_init for RHT)", who, xform);
+  if (dtype != STC_F32 && dtype != STC_BF16) return fail(STC_EUNSUPPORTED, "%s: dtype %d", who, dtype);
+  if (!x_dev) return fail(STC_EINVAL, "%s: NULL argument", who);
+  if (n_calib <= 0) return fail(STC_EINVAL, "%s: n_calib must be positive", who);
+  if (ld < d) return fail(STC_EINVAL, "%s: ld < d", who);
+  if (!aligned(x_dev, 16) || (ld * elem_size(dtype)) % 16)
+    return fail(STC_EINVAL, "%s: x rows must be 16-byte aligned", who);
+  if (!(avg_bits >= 0.0f) || !std::isfinite(avg_bits)) return fail(STC_EBUDGET, "%s: bad budget", who);
+  *budget = stc_total_bits(avg_bits, d);
+  if (*budget > STC_MAX_BITS * d) return fail(STC_EBUDGET, "%s: budget %d > %d", who, *budget, STC_MAX_BITS * d);
   if (bits) {
     int sum = 0;
     for (int j = 0; j < d; ++j) {
-      if (bits[j] > STC_MAX_BITS) return fail(STC_EBUDGET, "calibrate_head: width > 8 at channel %d", j);
+      if (bits[j] > STC_MAX_BITS) return fail(STC_EBUDGET, "%s: width > 8 at channel %d", who, j);
       sum += bits[j];
     }
-    if (sum != budget) return fail(STC_EBUDGET, "calibrate_head: widths sum to %d, budget is %d", sum, budget);
+    if (sum != *budget) return fail(STC_EBUDGET, "%s: widths sum to %d, budget is %d", who, sum, *budget);
   }
-  // second moment on the GPU (fp64), into the state's scratch region
-  double* gram_dev = reinterpret_cast<double*>(static_cast<unsigned char*>(state_dev) + OFF_GRAM);
-  if (launch_gram(x_dev, dtype, ld, n_calib, gram_dev, stream)) return fail(STC_EDEVICE, "gram launch: %s", hipGetErrorString(hipGetLastError()));
-  std::vector<double> g((size_t)d * d);
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (stc_status st = hip_check(hipMemcpyAsync(g.data(), gram_dev, g.size() * sizeof(double), hipMemcpyDeviceToHost, s), "gram download")) return st;
-  if (stc_status st = hip_check(hipStreamSynchronize(s), "gram sync")) return st;
-  for (double v : g)
-    if (!std::isfinite(v))
-      return fail(STC_EINVAL, "calibrate_head: the second moment is not finite (NaN or Inf among the tokens)");
+  return STC_OK;
+}
+
+// Host part of a calibration: second moment g (d x d) -> basis, widths,
+// state blob (with g kept in its scratch region) and summary.
+stc_status state_from_gram(const char* who, const double* g, int32_t xform, int32_t budget, const uint8_t* bits,
+                           stc_head_info* info, std::vector<unsigned char>& blob) {
+  const int d = D;
+  for (int i = 0; i < d * d; ++i)
+    if (!std::isfinite(g[i]))
+      return fail(STC_EINVAL, "%s: the second moment is not finite (NaN or Inf among the tokens)", who);
   std::vector<double> u((size_t)d * d), lam(d);
   if (xform == STC_XFORM_EIGEN) {
-    if (stc_status st = stc_eigh(d, g.data(), u.data(), lam.data())) return st;
+    if (stc_status st = stc_eigh(d, g, u.data(), lam.data())) return st;
   } else {
     for (int j = 0; j < d; ++j) lam[j] = g[(size_t)j * d + j];
   }
   std::vector<uint8_t> b(d);
   if (bits) std::copy(bits, bits + d, b.begin());
   else if (stc_status st = stc_water_fill(d, lam.data(), budget, b.data())) return st;
+  if (stc_status st = build_eigen_blob(d, xform, xform == STC_XFORM_EIGEN ? u.data() : nullptr, lam.data(), b.data(),
+                                       nullptr, info, blob))
+    return st;
+  std::memcpy(blob.data() + OFF_GRAM, g, (size_t)d * d * sizeof(double));
+  return STC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+stc_status stc_calibrate_head(int32_t d, int64_t n_calib, const void* x_dev, int32_t dtype, int64_t ld,
+                              float avg_bits, const uint8_t* bits, int32_t xform, stc_head_info* info,
+                              void* state_dev, stc_stream_t stream) {
+  int32_t budget = 0;
+  if (stc_status s = check_calibration("calibrate_head", d, n_calib, x_dev, dtype, ld, avg_bits, bits, xform, &budget))
+    return s;
+  if (!info) return fail(STC_EINVAL, "calibrate_head: NULL argument");
+  if (stc_status s = check_state_ptr(state_dev, "state_dev")) return s;
+  // second moment on the GPU (fp64), into the state's scratch region
+  double* gram_dev = reinterpret_cast<double*>(static_cast<unsigned char*>(state_dev) + OFF_GRAM);
+  if (launch_gram(x_dev, dtype, ld, 0, n_calib, 1, gram_dev, 0, stream))
+    return fail(STC_EDEVICE, "gram launch: %s", hipGetErrorString(hipGetLastError()));
+  std::vector<double> g((size_t)d * d);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (stc_status st = hip_check(hipMemcpyAsync(g.data(), gram_dev, g.size() * sizeof(double), hipMemcpyDeviceToHost, s), "gram download")) return st;
+  if (stc_status st = hip_check(hipStreamSynchronize(s), "gram sync")) return st;
   std::vector<unsigned char> blob;
-  build_eigen_blob(d, xform, xform == STC_XFORM_EIGEN ? u.data() : nullptr, lam.data(), b.data(), nullptr, info, blob);
-  // keep the second moment in the blob's scratch region
-  std::memcpy(blob.data() + OFF_GRAM, g.data(), g.size() * sizeof(double));
+  if (stc_status st = state_from_gram("calibrate_head", g.data(), xform, budget, bits, info, blob)) return st;
   if (stc_status st = upload(blob, state_dev, stream)) return st;
+  return ok();
+}
+
+stc_status stc_calibrate_heads_batched(int32_t d, int64_t n_streams, int64_t n_calib, const void* x_dev,
+                                       int32_t dtype, int64_t ld, int64_t x_stream_stride, float avg_bits,
+                                       int32_t xform, stc_head_info* infos, void* states_dev, stc_stream_t stream) {
+  int32_t budget = 0;
+  if (stc_status s = check_calibration("calibrate_heads_batched", d, n_calib, x_dev, dtype, ld, avg_bits, nullptr,
+                                       xform, &budget))
+    return s;
+  if (n_streams < 0) return fail(STC_EINVAL, "calibrate_heads_batched: negative stream count");
+  if (n_streams == 0) return ok();
+  if (!infos) return fail(STC_EINVAL, "calibrate_heads_batched: NULL infos");
+  if (stc_status s = check_state_ptr(states_dev, "states_dev")) return s;
+  if (n_streams > 1 && (x_stream_stride < (n_calib - 1) * ld + D || (x_stream_stride * elem_size(dtype)) % 16))
+    return fail(STC_EINVAL, "calibrate_heads_batched: x stream stride must cover n_calib rows and keep 16-byte "
+                            "alignment");
+  if (n_streams > (1 << 20)) return fail(STC_EINVAL, "calibrate_heads_batched: at most 2^20 streams");
+  // every stream's second moment in one launch, into each state's scratch region
+  unsigned char* base = static_cast<unsigned char*>(states_dev);
+  if (launch_gram(x_dev, dtype, ld, x_stream_stride, n_calib, n_streams,
+                  reinterpret_cast<double*>(base + OFF_GRAM), (int64_t)(STATE_BYTES / sizeof(double)), stream))
+    return fail(STC_EDEVICE, "gram launch: %s", hipGetErrorString(hipGetLastError()));
+  const size_t dd = (size_t)D * D;
+  std::vector<double> g(dd * (size_t)n_streams);
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  if (stc_status st = hip_check(hipMemcpy2DAsync(g.data(), dd * sizeof(double), base + OFF_GRAM, STATE_BYTES,
+                                                 dd * sizeof(double), (size_t)n_streams, hipMemcpyDeviceToHost, hs),
+                                "gram download"))
+    return st;
+  if (stc_status st = hip_check(hipStreamSynchronize(hs), "gram sync")) return st;
+  // the lazily filled step tables, before the workers read them
+  for (int b = 1; b <= STC_MAX_BITS; ++b) (void)stc_delta_star(b);
+  // eigenbasis, widths and blob of each stream on the host, streams spread
+  // over worker threads; each worker keeps the first failure it meets
+  std::vector<unsigned char> all((size_t)n_streams * STATE_BYTES);
+  const unsigned hw = std::thread::hardware_concurrency();
+  const int64_t n_thr = std::min<int64_t>(n_streams, std::max(1u, std::min(hw, 16u)));
+  std::atomic<int64_t> next{0};
+  std::vector<stc_status> thr_status((size_t)n_thr, STC_OK);
+  std::vector<std::string> thr_msg((size_t)n_thr);
+  auto work = [&](int64_t t) {
+    std::vector<unsigned char> blob;
+    for (int64_t i = next.fetch_add(1); i < n_streams; i = next.fetch_add(1)) {
+      stc_status st = state_from_gram("calibrate_heads_batched", g.data() + dd * (size_t)i, xform, budget, nullptr,
+                                      &infos[i], blob);
+      if (st) {
+        thr_status[(size_t)t] = st;
+        thr_msg[(size_t)t] = "stream " + std::to_string(i) + ": " + stc_last_error();
+        next.store(n_streams);
+        return;
+      }
+      std::memcpy(all.data() + (size_t)i * STATE_BYTES, blob.data(), STATE_BYTES);
+    }
+  };
+  std::vector<std::thread> pool;
+  for (int64_t t = 1; t < n_thr; ++t) pool.emplace_back(work, t);
+  work(0);
+  for (auto& th : pool) th.join();
+  for (int64_t t = 0; t < n_thr; ++t)
+    if (thr_status[(size_t)t]) return fail(thr_status[(size_t)t], "%s", thr_msg[(size_t)t].c_str());
+  if (stc_status st = upload(all, states_dev, stream)) return st;
   return ok();
 }
 

@@ -237,7 +237,10 @@ struct AttendLaunch {
   int new_f32 = 0;
 };
 
-int launch_gram(const void* x, int dtype, int64_t ld, int64_t n_calib, double* gram, void* stream);
+// second moments of n_streams streams (rows x + s * x_stride, elements) into
+// gram + s * gram_stride (doubles), one launch
+int launch_gram(const void* x, int dtype, int64_t ld, int64_t x_stride, int64_t n_calib, int64_t n_streams,
+                double* gram, int64_t gram_stride, void* stream);
 int launch_encode_eigen(const EncodeLaunch& a, void* stream);
 int launch_decode_eigen(const DecodeLaunch& a, void* stream);
 int launch_encode_rht(const EncodeLaunch& a, void* stream);

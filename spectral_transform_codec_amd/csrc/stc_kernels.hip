@@ -93,11 +93,16 @@ __device__ __forceinline__ int xcd_logical(int b, int grid) {
 }
 
 // ======================================================================
-// Second moment (calibration): one workgroup per stream, fp64 accumulation
-// of exact fp32 products in token order. Thread (ti, tj) owns entries
-// (ti + 16u, tj + 16v), so (a, b) and (b, a) see identical sums.
+// Second moment (calibration): one workgroup per stream (blockIdx.x; rows
+// at x + stream * x_stride, the result at gram + stream * gram_stride), fp64
+// accumulation of exact fp32 products in token order. Thread (ti, tj) owns
+// entries (ti + 16u, tj + 16v), so (a, b) and (b, a) see identical sums.
 // ======================================================================
-__global__ void __launch_bounds__(256) k_gram(const void* x, int dtype, long long ld, long long n, double* gram) {
+__global__ void __launch_bounds__(256) k_gram(const void* x0, int dtype, long long ld, long long x_stride, long long n,
+                                              double* gram0, long long gram_stride) {
+  const long long sidx = blockIdx.x;
+  const void* x = static_cast<const unsigned char*>(x0) + sidx * x_stride * (dtype == STC_F32 ? 4 : 2);
+  double* gram = gram0 + sidx * gram_stride;
   __shared__ float sx[64][132];
   const int tid = threadIdx.x, ti = tid >> 4, tj = tid & 15;
   double acc[8][8];
@@ -136,9 +141,10 @@ __global__ void __launch_bounds__(256) k_gram(const void* x, int dtype, long lon
   (void)inv_n;
 }
 
-int launch_gram(const void* x, int dtype, int64_t ld, int64_t n_calib, double* gram, void* stream) {
-  hipLaunchKernelGGL(k_gram, dim3(1), dim3(256), 0, (hipStream_t)stream, x, dtype, (long long)ld,
-                     (long long)n_calib, gram);
+int launch_gram(const void* x, int dtype, int64_t ld, int64_t x_stride, int64_t n_calib, int64_t n_streams,
+                double* gram, int64_t gram_stride, void* stream) {
+  hipLaunchKernelGGL(k_gram, dim3((unsigned)n_streams), dim3(256), 0, (hipStream_t)stream, x, dtype, (long long)ld,
+                     (long long)x_stride, (long long)n_calib, gram, (long long)gram_stride);
   return hipGetLastError() != hipSuccess;
 }
 

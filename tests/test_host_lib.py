@@ -208,3 +208,23 @@ def test_rht_encode_kernel_choice():
         assert L.stc_get_rht_encode_kernel() == 0
     finally:
         L.stc_set_rht_encode_kernel(before)
+
+
+def test_batched_calibration_validates_arguments_without_device_work():
+    L = _abi.lib()
+    infos = (_abi.HeadInfo * 4)()
+    fake = ctypes.c_void_p(4096)           # aligned, never dereferenced on these paths
+    call = L.stc_calibrate_heads_batched
+    # head dim, dtype, negative counts, budget
+    assert call(64, 4, 2048, fake, _abi.BF16, 128, 2048 * 128, 2.0, 1, infos, fake, None) == _abi.STC_EUNSUPPORTED
+    assert call(128, 4, 2048, fake, 7, 128, 2048 * 128, 2.0, 1, infos, fake, None) == _abi.STC_EUNSUPPORTED
+    assert call(128, -1, 2048, fake, _abi.BF16, 128, 2048 * 128, 2.0, 1, infos, fake, None) == _abi.STC_EINVAL
+    assert call(128, 4, 0, fake, _abi.BF16, 128, 2048 * 128, 2.0, 1, infos, fake, None) == _abi.STC_EINVAL
+    assert call(128, 4, 2048, fake, _abi.BF16, 128, 2048 * 128, 9.0, 1, infos, fake, None) == _abi.STC_EBUDGET
+    # stream stride that does not cover n_calib rows; misaligned rows; NULL summaries
+    assert call(128, 4, 2048, fake, _abi.BF16, 128, 2047 * 128, 2.0, 1, infos, fake, None) == _abi.STC_EINVAL
+    assert call(128, 4, 2048, ctypes.c_void_p(4098), _abi.BF16, 128, 2048 * 128, 2.0, 1, infos, fake,
+                None) == _abi.STC_EINVAL
+    assert call(128, 4, 2048, fake, _abi.BF16, 128, 2048 * 128, 2.0, 1, None, fake, None) == _abi.STC_EINVAL
+    # no streams: nothing to do
+    assert call(128, 0, 2048, fake, _abi.BF16, 128, 0, 2.0, 1, infos, fake, None) == _abi.STC_OK
