@@ -10,7 +10,7 @@
 #include "../../spectral_transform_codec_amd/csrc/stc_internal.h"
 
 namespace stc {
-int launch_gram(const void*, int, int64_t, int64_t, double*, void*) { return 1; }
+int launch_gram(const void*, int, int64_t, int64_t, int64_t, int64_t, double*, int64_t, void*) { return 1; }
 int launch_encode_eigen(const EncodeLaunch&, void*) { return 1; }
 int launch_sketch_eigen(const EncodeLaunch&, void*) { return 1; }
 int launch_decode_eigen(const DecodeLaunch&, void*) { return 1; }
