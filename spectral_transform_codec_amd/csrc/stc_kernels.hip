@@ -971,18 +971,36 @@ __global__ void __launch_bounds__(DEC_THREADS, 1) k_decode_eigen(DecK a) {
     __syncthreads();
     const long long P_len = packed_len((long long)B, n);
     const unsigned cw_kind = (B & 3u) == 0u ? 4u : ((B & 1u) == 0u ? 2u : 1u);
+    // bytes of a block's records (the stream's last block may be short)
+    auto rec_bytes = [&](long long tt2, long long& start) {
+      start = tt2 * 4LL * (long long)B;
+      const long long nb = 4LL * (long long)B;
+      return nb > P_len - start ? P_len - start : nb;
+    };
+    // NW <= 4 (records of at most 256 bits): the next block's records are
+    // requested as soon as the current ones are in LDS, into the same
+    // registers, so the load runs under this block's work
+    constexpr bool PREF = NW <= 4;
+    unsigned wr[NW];
+    if (PREF && B > 0 && seg + wave < seg_end) {
+      long long st0;
+      const long long nb0 = rec_bytes(seg + wave - s * a.blocks_per_stream, st0);
+      est_load<NW>(wr, a.packed + s * a.packed_stride + st0, nb0, lane);
+    }
     for (long long blk = seg + wave; blk < seg_end; blk += DEC_WAVES) {
       const long long tt = blk - s * a.blocks_per_stream;
       const long long tok0 = tt * DEC_BT;
       // ---- 1: records -> LDS stream
       if (B > 0) {
-        const long long start = tt * 4LL * (long long)B;
-        long long nbytes = 4LL * (long long)B;
-        if (nbytes > P_len - start) nbytes = P_len - start;
-        const unsigned char* src = a.packed + s * a.packed_stride + start;
-        unsigned wr[NW];
-        est_load<NW>(wr, src, nbytes, lane);
+        long long start;
+        const long long nbytes = rec_bytes(tt, start);
+        if (!PREF) est_load<NW>(wr, a.packed + s * a.packed_stride + start, nbytes, lane);
         est_store<NW>(sStr, wr, nbytes, lane);
+        if (PREF && blk + DEC_WAVES < seg_end) {
+          long long st2;
+          const long long nb2 = rec_bytes(tt + DEC_WAVES, st2);
+          est_load<NW>(wr, a.packed + s * a.packed_stride + st2, nb2, lane);
+        }
         __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
         __builtin_amdgcn_wave_barrier();
       }
@@ -1105,7 +1123,8 @@ int launch_decode_eigen(const DecodeLaunch& L, void* stream) {
   if (!g_dec_attr_done) {
     for (const void* k : {(const void*)k_decode_eigen<0, 8, false>, (const void*)k_decode_eigen<1, 8, false>,
                           (const void*)k_decode_eigen<0, 16, false>, (const void*)k_decode_eigen<1, 16, false>,
-                          (const void*)k_decode_eigen<0, 8, true>, (const void*)k_decode_eigen<0, 16, true>})
+                          (const void*)k_decode_eigen<0, 8, true>, (const void*)k_decode_eigen<0, 16, true>,
+                          (const void*)k_decode_eigen<0, 4, true>, (const void*)k_decode_eigen<0, 4, false>})
       if (hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)DEC_LDS) != hipSuccess) return 1;
     g_dec_attr_done = true;
   }
@@ -1137,10 +1156,12 @@ int launch_decode_eigen(const DecodeLaunch& L, void* stream) {
     if (small) hipLaunchKernelGGL((k_decode_eigen<1, 8, false>), dim3(grid), dim3(DEC_THREADS), DEC_LDS, s, a);
     else hipLaunchKernelGGL((k_decode_eigen<1, 16, false>), dim3(grid), dim3(DEC_THREADS), DEC_LDS, s, a);
   } else if (L.w16) {
-    if (small) hipLaunchKernelGGL((k_decode_eigen<0, 8, true>), dim3(grid), dim3(DEC_THREADS), DEC_LDS, s, a);
+    if (L.max_bits <= 256) hipLaunchKernelGGL((k_decode_eigen<0, 4, true>), dim3(grid), dim3(DEC_THREADS), DEC_LDS, s, a);
+    else if (small) hipLaunchKernelGGL((k_decode_eigen<0, 8, true>), dim3(grid), dim3(DEC_THREADS), DEC_LDS, s, a);
     else hipLaunchKernelGGL((k_decode_eigen<0, 16, true>), dim3(grid), dim3(DEC_THREADS), DEC_LDS, s, a);
   } else {
-    if (small) hipLaunchKernelGGL((k_decode_eigen<0, 8, false>), dim3(grid), dim3(DEC_THREADS), DEC_LDS, s, a);
+    if (L.max_bits <= 256) hipLaunchKernelGGL((k_decode_eigen<0, 4, false>), dim3(grid), dim3(DEC_THREADS), DEC_LDS, s, a);
+    else if (small) hipLaunchKernelGGL((k_decode_eigen<0, 8, false>), dim3(grid), dim3(DEC_THREADS), DEC_LDS, s, a);
     else hipLaunchKernelGGL((k_decode_eigen<0, 16, false>), dim3(grid), dim3(DEC_THREADS), DEC_LDS, s, a);
   }
   return hipGetLastError() != hipSuccess;

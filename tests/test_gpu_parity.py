@@ -20,7 +20,7 @@ import torch
 import att_variants
 import synth
 from oracle import codec, rht
-from parity_bounds import (assert_rht_code_diffs_at_boundaries, check_eigen_codes, decode_arith,
+from parity_bounds import (assert_rht_code_diffs_at_boundaries, check_eigen_codes, decode_arith, decode_w16,
                            rht_rotation_eps)
 
 pytestmark = pytest.mark.gpu
@@ -162,6 +162,23 @@ def test_decode_matches_oracle(cfg, n, avg, dtype):
     ulp = np.abs(exact) * (2.0 ** -7 if dtype == "bf16" else 2.0 ** -23)
     arith = decode_arith(ost, dtype)
     assert np.all(np.abs(xg - xo) <= ulp + arith[None, :])
+
+
+@pytest.mark.parametrize("scale,avg", [(2.0 ** -12, 2.0), (2.0 ** -12, 1.33), (1.0, 3.0)])
+def test_decode_low_budget_bf16_pair(scale, avg):
+    """bf16 output of records of at most 256 bits whose steps fall below
+    2^-7 (tiny activations), or budgets above 2 bits: the bf16 hi / lo pair
+    instead of the fp16 pass, for short records and long ones, against the
+    oracle as above (the ragged last block included)."""
+    w, x = stream_case(2, 3001, head=5)
+    x = x * scale
+    ost = codec.calibrate_head(x, 2048, avg)
+    assert not decode_w16(ost, "bf16")
+    po = codec.encode_kv(ost, x)
+    xg = stc.decode_kv(gpu_state(ost), torch.from_numpy(po).to(DEV), 3001).float().cpu().numpy().astype(np.float64)
+    xo = codec.decode_kv(ost, po, 3001, "bf16")
+    exact = codec.reconstruct_exact(ost, po, 3001)
+    assert np.all(np.abs(xg - xo) <= np.abs(exact) * 2.0 ** -7 + decode_arith(ost, "bf16")[None, :])
 
 
 @pytest.mark.parametrize("cfg,n,avg,dtype", [(1, 4096, 2.0, "f32"), (2, 8192, 2.0, "bf16")])
