@@ -5,9 +5,9 @@ amplification of its score noise in "Statistische Validatie en Jensen's
 Ongelijkheid"). Test infrastructure only: the tests, the smoke check and the
 CPU baseline of the benchmark use it; the library never does.
 
-The eigen cache gets the "selective" sketch of SpectralQuant (ablation
-summary, "Experimentele Opstelling": a selective QJL sketch on the top
-effective dimensions). READING: it covers the quantization residual of the
+The eigen cache gets SpectralQuant's selective sketch (ablation summary,
+"Experimentele Opstelling": SpectralQuant restricts its QJL sketch to the
+leading effective dimensions). READING: it covers the quantization residual of the
 water-filled channels, r_j = c_j - c_hat_j for the kept channels with a
 positive step, in the latent basis (0 for dropped channels); the query is
 taken to the same basis, so the estimate of (U^T q) . r is
