@@ -3026,7 +3026,11 @@ __global__ void __launch_bounds__(64 * W, at2_occ(R2M, NCH, W, SWZ, G4)) k_att2(
 #pragma unroll
       for (int i = 0; i < NHL; ++i) {
         su[i] = __builtin_fmaf((float)((acc[4 * i] << 7) + acc[4 * i + 1]), 128.0f, (float)acc[4 * i + 2]);
-        if (tail && tok0 + t32 >= tend) su[i] = -INFINITY;
+      }
+      if (tail) {  // (uniform) tokens past the split
+#pragma unroll
+        for (int i = 0; i < NHL; ++i)
+          if (tok0 + t32 >= tend) su[i] = -INFINITY;
       }
     }
     bool slow = false;
@@ -3035,7 +3039,7 @@ __global__ void __launch_bounds__(64 * W, at2_occ(R2M, NCH, W, SWZ, G4)) k_att2(
     // ---- online softmax. A score above its head's max + 8 (log2 units)
     // raises the max first (rare once the max has settled): alpha =
     // 2^(m_old - m_new) rescales the value accumulators before P x V.
-    if (__any(slow)) {
+    if (__builtin_amdgcn_ballot_w64(slow) != 0) {
       float mx16 = 0.0f;
       if constexpr (S16) mx16 = row16_max(fmaxf(su[0], su[1]) * invS[0]);
 #pragma unroll
