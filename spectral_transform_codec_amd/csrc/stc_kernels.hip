@@ -1849,27 +1849,70 @@ __device__ __forceinline__ unsigned att_group_bytes(const lds_u8* str, const lds
 // SKETCH (RHT only): keys carry the 1-bit residual sketch; a second table
 // holds S q scale log2(e) sqrt(pi/2)/m (hi / lo) and each score gains
 // |r_t| times its product with the token's signs, one more MFMA chain.
-// k_att_combine: one workgroup per pair, after the main kernel has written
-// every split's partial. Thread (q, i) requests its quarter of row i of U_V
-// (32 floats, kept in registers) first; meanwhile the threads merge, per
-// (head, V channel j), the splits' (acc_j, m, l) with log-sum-exp weights
-// (fp32 weights, fp64 sums, batches of 8 splits with all loads in flight)
-// and dequantize the mean code into LDS; then every thread sums its quarter
-// of o_i = sum_k U_ik chat_k for each head and the four quarters are added
-// through LDS. U_V is read once per pair.
-constexpr int CMB_THREADS = 512;
+// Split merge, after the main kernel has written every split's partial:
+// per (query head, V channel j) the splits' (acc_j, m, l) merge with
+// log-sum-exp weights (fp32 weights, fp64 sums, batches of 8 splits with all
+// loads in flight), the mean code is dequantized, and o = U_V chat is formed
+// for every head.
+//  k_att_combine: one 256-thread workgroup per pair (many pairs): each
+//   thread merges whole elements, then thread (half, i) sums its half of row
+//   i of U_V (read once per pair, 16 floats at a time) against every head's
+//   codes and the two halves are added through LDS.
+//  k_att_combine_head: one 1024-thread workgroup per (pair, query head) (few
+//   pairs with many splits): eight threads per channel merge interleaved
+//   eighths of the splits, the eighths are merged in a fixed order, and eight
+//   threads per output dim sum sixteen inputs each.
+constexpr int CMB_THREADS = 256;
 constexpr int CMB_BATCH = 8;
-constexpr size_t CMB_LDS = (size_t)(16 * 128 + 4 * 16 * 128) * 4;
+constexpr int CMBH_THREADS = 1024;
+// dynamic LDS of k_att_combine: mean codes [g][128], half sums [2][g][128]
+__host__ __device__ constexpr size_t cmb_lds_bytes(int g) { return (size_t)3 * g * 128 * 4; }
+
+// Merge splits s0, s0 + step, ... (< S) of element j of a head's partials ph:
+// running maximum M and the sums A (weighted codes) and L (weights).
+__device__ __forceinline__ void cmb_merge(const float* ph, int S, int s0, int step, long long PS, int j, float& M,
+                                          double& A, double& L) {
+  M = -INFINITY;
+  A = 0.0;
+  L = 0.0;
+  for (int sb = s0; sb < S; sb += CMB_BATCH * step) {
+    float mv[CMB_BATCH], lv[CMB_BATCH], av[CMB_BATCH];
+#pragma unroll
+    for (int r = 0; r < CMB_BATCH; ++r) {
+      const int s2 = sb + r * step;
+      const long long sc = s2 < S ? s2 : s0;  // (past the end: a repeat that gets weight 0)
+      mv[r] = ph[sc * PS + 128];
+      lv[r] = ph[sc * PS + 129];
+      av[r] = ph[sc * PS + j];
+    }
+    float Mc = M;
+#pragma unroll
+    for (int r = 0; r < CMB_BATCH; ++r) Mc = fmaxf(Mc, mv[r]);  // repeats change no maximum
+    if (Mc != -INFINITY) {
+      if (M != -INFINITY && M != Mc) {
+        const double sc = (double)exp2f(M - Mc);
+        A *= sc;
+        L *= sc;
+      }
+#pragma unroll
+      for (int r = 0; r < CMB_BATCH; ++r) {
+        const float f = (sb + r * step < S && mv[r] != -INFINITY) ? exp2f(mv[r] - Mc) : 0.0f;
+        A += (double)(f * av[r]);
+        L += (double)(f * lv[r]);
+      }
+      M = Mc;
+    }
+  }
+}
 
 __global__ void __launch_bounds__(CMB_THREADS) k_att_combine(AttK a) {
   extern __shared__ __align__(16) unsigned char smem[];
+  const int g = a.group;
   float* sC = reinterpret_cast<float*>(smem);  // dequantized mean codes [head][128]
-  float* sQ = sC + 16 * 128;                   // quarter sums [4][head][128]
+  float* sQ = sC + g * 128;                    // half sums [2][head][128]
   const long long p = blockIdx.x;
   const long long pg = a.pair_base + p;
   const int t = threadIdx.x;
-  const int i = t & 127, qt = t >> 7;  // output dim, quarter of the inputs
-  const int g = a.group;
   const int S = (int)a.n_splits;
   const long long PS = att_part_stride(g);
   const long long ksi = state_index(a.k_map, pg, a.n_states), vsi = state_index(a.v_map, pg, a.n_states);
@@ -1879,64 +1922,118 @@ __global__ void __launch_bounds__(CMB_THREADS) k_att_combine(AttK a) {
   }
   const unsigned char* vst = a.v_states + (size_t)vsi * STATE_BYTES;
   const DevHdr* hv = reinterpret_cast<const DevHdr*>(vst);
-  const f32x4* urow = reinterpret_cast<const f32x4*>(vst + OFF_U32) + i * 32 + qt * 8;  // U[i][32qt .. +31]
-  f32x4 u[8];
-#pragma unroll
-  for (int r = 0; r < 8; ++r) u[r] = urow[r];
   for (int e = t; e < g * 128; e += CMB_THREADS) {
     const int hh = e >> 7, j = e & 127;
     const float* ph = reinterpret_cast<const float*>(a.ws) + p * (long long)S * PS + hh * ATT_PART_FLOATS;
-    const unsigned bits = hv->bits[j];
-    const float step = hv->step32[j], hs = hv->halfspan[j];
-    float M = -INFINITY;
-    double A = 0.0, L = 0.0;
-    for (int s0 = 0; s0 < S; s0 += CMB_BATCH) {
-      float mv[CMB_BATCH], lv[CMB_BATCH], av[CMB_BATCH];
-#pragma unroll
-      for (int r = 0; r < CMB_BATCH; ++r) {
-        const long long s2 = s0 + r < S ? s0 + r : S - 1;
-        mv[r] = ph[s2 * PS + 128];
-        lv[r] = ph[s2 * PS + 129];
-        av[r] = ph[s2 * PS + j];
-      }
-      float Mc = M;
-#pragma unroll
-      for (int r = 0; r < CMB_BATCH; ++r) Mc = fmaxf(Mc, mv[r]);  // clamped repeats change no maximum
-      if (Mc != -INFINITY) {
-        if (M != -INFINITY && M != Mc) {
-          const double sc = (double)exp2f(M - Mc);
-          A *= sc;
-          L *= sc;
-        }
-#pragma unroll
-        for (int r = 0; r < CMB_BATCH; ++r) {
-          const float f = (s0 + r < S && mv[r] != -INFINITY) ? exp2f(mv[r] - Mc) : 0.0f;
-          A += (double)(f * av[r]);
-          L += (double)(f * lv[r]);
-        }
-        M = Mc;
-      }
-    }
+    float M;
+    double A, L;
+    cmb_merge(ph, S, 0, 1, PS, j, M, A, L);
     // dequantize the mean code: step * (A / L - (L_j - 1)/2)
-    sC[hh * 128 + j] = bits ? (float)((double)step * (A / L - (double)hs)) : 0.0f;
+    sC[hh * 128 + j] = hv->bits[j] ? (float)((double)hv->step32[j] * (A / L - (double)hv->halfspan[j])) : 0.0f;
   }
   __syncthreads();
-  for (int hh = 0; hh < g; ++hh) {
-    float o = 0.0f;
-    const f32x4* c4 = reinterpret_cast<const f32x4*>(sC + hh * 128) + qt * 8;
+  const int i = t & 127, half = t >> 7;
+  const f32x4* urow = reinterpret_cast<const f32x4*>(vst + OFF_U32) + i * 32 + half * 16;  // U[i][64 half ..]
+  float o[16];
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const f32x4 c = c4[r];
+  for (int hh = 0; hh < 16; ++hh) o[hh] = 0.0f;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) o = __builtin_fmaf(u[r][e], c[e], o);
+  for (int jc = 0; jc < 4; ++jc) {
+    f32x4 u[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) u[r] = urow[4 * jc + r];
+#pragma unroll
+    for (int hh = 0; hh < 16; ++hh) {
+      if (hh < g) {
+        const f32x4* c4 = reinterpret_cast<const f32x4*>(sC + hh * 128 + 64 * half + 16 * jc);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const f32x4 c = c4[r];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[hh] = __builtin_fmaf(u[r][e], c[e], o[hh]);
+        }
+      }
     }
-    sQ[(qt * 16 + hh) * 128 + i] = o;
   }
+#pragma unroll
+  for (int hh = 0; hh < 16; ++hh)
+    if (hh < g) sQ[(half * g + hh) * 128 + i] = o[hh];
   __syncthreads();
   for (int e = t; e < g * 128; e += CMB_THREADS) {
     const int hh = e >> 7, ii = e & 127;
-    a.out[(pg * g + hh) * 128 + ii] = (sQ[hh * 128 + ii] + sQ[(16 + hh) * 128 + ii]) +
-                                      (sQ[(32 + hh) * 128 + ii] + sQ[(48 + hh) * 128 + ii]);
+    a.out[(pg * g + hh) * 128 + ii] = sQ[hh * 128 + ii] + sQ[(g + hh) * 128 + ii];
+  }
+}
+
+__global__ void __launch_bounds__(CMBH_THREADS) k_att_combine_head(AttK a) {
+  __shared__ float sM[8][128];
+  __shared__ double sA[8][128], sL[8][128];
+  __shared__ __align__(16) float sC[128];
+  __shared__ float sR[8][128];
+  const int g = a.group;
+  const long long p = blockIdx.x;
+  const int hh = blockIdx.y;
+  const long long pg = a.pair_base + p;
+  const int t = threadIdx.x;
+  const int S = (int)a.n_splits;
+  const long long PS = att_part_stride(g);
+  const long long ksi = state_index(a.k_map, pg, a.n_states), vsi = state_index(a.v_map, pg, a.n_states);
+  if (ksi < 0 || vsi < 0) {  // no state for the pair: NaN
+    if (t < 128) a.out[(pg * g + hh) * 128 + t] = __builtin_nanf("");
+    return;
+  }
+  const unsigned char* vst = a.v_states + (size_t)vsi * STATE_BYTES;
+  const DevHdr* hv = reinterpret_cast<const DevHdr*>(vst);
+  const int j = t & 127, eighth = t >> 7;
+  // row i = j of U_V, inputs 16 eighth .. + 15, requested before the merge
+  const f32x4* urow = reinterpret_cast<const f32x4*>(vst + OFF_U32) + j * 32 + eighth * 4;
+  f32x4 u[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) u[r] = urow[r];
+  {
+    const float* ph = reinterpret_cast<const float*>(a.ws) + p * (long long)S * PS + hh * ATT_PART_FLOATS;
+    float M;
+    double A, L;
+    cmb_merge(ph, S, eighth, 8, PS, j, M, A, L);
+    sM[eighth][j] = M;
+    sA[eighth][j] = A;
+    sL[eighth][j] = L;
+  }
+  __syncthreads();
+  if (t < 128) {
+    float M = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) M = fmaxf(M, sM[e][t]);
+    double A = 0.0, L = 0.0;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float me = sM[e][t];
+        if (me != -INFINITY) {
+          const double f = (double)exp2f(me - M);
+          A += f * sA[e][t];
+          L += f * sL[e][t];
+        }
+      }
+    }
+    sC[t] = hv->bits[t] ? (float)((double)hv->step32[t] * (A / L - (double)hv->halfspan[t])) : 0.0f;
+  }
+  __syncthreads();
+  float o = 0.0f;
+  const f32x4* c4 = reinterpret_cast<const f32x4*>(sC + 16 * eighth);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const f32x4 c = c4[r];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o = __builtin_fmaf(u[r][e], c[e], o);
+  }
+  sR[eighth][j] = o;
+  __syncthreads();
+  if (t < 128) {
+    float r = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r += sR[e][t];
+    a.out[(pg * g + hh) * 128 + t] = r;
   }
 }
 
@@ -2554,7 +2651,7 @@ __device__ __forceinline__ void at2_stage_rel(unsigned (&rel)[NCH], unsigned& sh
 // 1024 threads: thread (part, j) sums rows part, part + 8, .. of U_K for
 // channel j and all eight heads (its 16 loads in flight at once); the eight
 // parts are added through LDS.
-constexpr int PREP_PARTS = 8;
+constexpr int PREP_PARTS = 2;  // (256 threads: many workgroups per CU)
 // Generation-step append, one wave per stream: the record of one token is
 // formed exactly as k_encode_eigen forms it (the same MFMA chain on the same
 // basis rows, the token in every column of the block, the same quantizer and
@@ -2671,9 +2768,12 @@ __global__ void __launch_bounds__(128) k_att_append(AttK a) {
   else att_append_pair<false>(a, pg, ksi, vsi, sbuf, threadIdx.x);
 }
 
+// APPEND: a generation step's bf16 new-token rows are appended first.
+template <bool APPEND>
 __global__ void __launch_bounds__(128 * PREP_PARTS) k_att2_prep(AttK a) {
   __shared__ __align__(16) float sqT[128 * 8];   // q^T [128][8]
   __shared__ float red[PREP_PARTS][8][128];
+  __shared__ float wmax[8][2];
   const int tid = threadIdx.x;
   const long long p = blockIdx.x, pg = a.pair_base + p;
   const int g = a.group;
@@ -2681,60 +2781,71 @@ __global__ void __launch_bounds__(128 * PREP_PARTS) k_att2_prep(AttK a) {
   __shared__ unsigned sapp[2][64];
   // generation step: the new token's K and V records go into the caches
   // first (the main kernel, the next launch, reads them with the rest)
-  if (a.k_new && !a.new_f32) att_append_pair<false>(a, pg, ksi, vsi, sapp, tid);
+  if (APPEND) att_append_pair<false>(a, pg, ksi, vsi, sapp, tid);
   if (ksi < 0 || vsi < 0) return;  // (the main kernel writes nothing for this pair either)
   const unsigned char* kst = a.k_states + (size_t)ksi * STATE_BYTES;
   const DevHdr* hk = reinterpret_cast<const DevHdr*>(kst);
   const int j = tid & 127, part = tid >> 7;
   const float* u = reinterpret_cast<const float*>(kst + OFF_U32);
-  constexpr int RPP = 128 / PREP_PARTS;
-  float ur[RPP];
-#pragma unroll
-  for (int k = 0; k < RPP; ++k) ur[k] = u[(part + PREP_PARTS * k) * 128 + j];
   const float* qp = a.q + pg * g * 128;
-  {
-    const int r = tid >> 3, hh = tid & 7;
-    sqT[tid] = hh < g ? qp[hh * 128 + r] : 0.0f;
+  for (int e = tid; e < 128 * 8; e += 128 * PREP_PARTS) {
+    const int r = e >> 3, hh = e & 7;
+    sqT[e] = hh < g ? qp[hh * 128 + r] : 0.0f;
   }
   __syncthreads();
+  // thread (part, j): rows part + PREP_PARTS k of column j of U_K, in chunks
+  // of 16 rows (loads of a chunk in flight together)
+  constexpr int RPP = 128 / PREP_PARTS;
   float acc[8];
 #pragma unroll
   for (int hh = 0; hh < 8; ++hh) acc[hh] = 0.0f;
 #pragma unroll
-  for (int k = 0; k < RPP; ++k) {
-    const f32x4* q4 = reinterpret_cast<const f32x4*>(sqT + (part + PREP_PARTS * k) * 8);
-    const f32x4 q0 = q4[0], q1 = q4[1];
+  for (int k0 = 0; k0 < RPP; k0 += 16) {
+    float ur[16];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      acc[e] = __builtin_fmaf(ur[k], q0[e], acc[e]);
-      acc[4 + e] = __builtin_fmaf(ur[k], q1[e], acc[4 + e]);
+    for (int k = 0; k < 16; ++k) ur[k] = u[(part + PREP_PARTS * (k0 + k)) * 128 + j];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const f32x4* q4 = reinterpret_cast<const f32x4*>(sqT + (part + PREP_PARTS * (k0 + k)) * 8);
+      const f32x4 q0 = q4[0], q1 = q4[1];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[e] = __builtin_fmaf(ur[k], q0[e], acc[e]);
+        acc[4 + e] = __builtin_fmaf(ur[k], q1[e], acc[4 + e]);
+      }
     }
   }
 #pragma unroll
   for (int hh = 0; hh < 8; ++hh) red[part][hh][j] = acc[hh];
   __syncthreads();
   float* pre = a.prep + p * ATT_PREP_FLOATS;
-  __shared__ float wmax[16];
   {
-    const int hh = tid >> 7, c = tid & 127;
+    // thread (half, c): channel c of heads 4 half .. 4 half + 3; the two
+    // waves of a half hold channels 0..63 and 64..127
+    const int c = tid & 127, half = tid >> 7;
     const unsigned b = hk->bits[c];
-    float v = 0.0f;
-    if (hh < g && b > 0) {
-      float sum = 0.0f;
+    const float f = hk->step32[c] * a.scale * LOG2E;
 #pragma unroll
-      for (int pt = 0; pt < PREP_PARTS; ++pt) sum += red[pt][hh][c];
-      v = sum * hk->step32[c] * a.scale * LOG2E;
+    for (int r = 0; r < 4; ++r) {
+      const int hh = 4 * half + r;
+      float v = 0.0f;
+      if (hh < g && b > 0) {
+        float sum = 0.0f;
+#pragma unroll
+        for (int pt = 0; pt < PREP_PARTS; ++pt) sum += red[pt][hh][c];
+        v = sum * f;
+      }
+      pre[hh * 128 + c] = v;
+      // the largest weight of the head: max over c of |a_c| 2^(b_c - 1)
+      float m = b > 0 ? fabsf(v) * (float)(1u << (b - 1)) : 0.0f;
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+      if ((tid & 63) == 0) wmax[hh][(tid >> 6) & 1] = m;
     }
-    pre[tid] = v;
-    // the largest weight of the head: max over c of |a_c| 2^(b_c - 1), two waves per head
-    float m = b > 0 ? fabsf(v) * (float)(1u << (b - 1)) : 0.0f;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
-    if ((tid & 63) == 0) wmax[tid >> 6] = m;
   }
   __syncthreads();
   if (tid < 8) {
-    const float M = fmaxf(wmax[2 * tid], wmax[2 * tid + 1]);
+    const float M = fmaxf(wmax[tid][0], wmax[tid][1]);
     int ex = 0;
     frexpf(M, &ex);
     pre[8 * 128 + tid] = M > 0.0f ? ldexpf(1.0f, 20 - ex) : 1.0f;
@@ -3200,8 +3311,8 @@ int launch_attend(const AttendLaunch& L, void* stream) {
         if (hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) !=
             hipSuccess)
           return 1;
-    if (hipFuncSetAttribute((const void*)k_att_combine, hipFuncAttributeMaxDynamicSharedMemorySize, (int)CMB_LDS) !=
-        hipSuccess)
+    if (hipFuncSetAttribute((const void*)k_att_combine, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)cmb_lds_bytes(16)) != hipSuccess)
       return 1;
     if (at2_attr<4, 10, 1, 4, true, true>() || at2_attr<4, 10, 1, 4, true, false>() ||
         at2_attr<3, 8, 1, 4, false, false>() || at2_attr<4, 8, 1, 4, false, false>() ||
@@ -3279,7 +3390,8 @@ int launch_attend(const AttendLaunch& L, void* stream) {
     if (inst >= 0) {
       a.prep = reinterpret_cast<float*>(a.ws) + att_partial_floats(np, L.n_tokens, L.group, round);
       if (L.k_new && L.new_f32) hipLaunchKernelGGL(k_att_append, dim3((unsigned)np), dim3(128), 0, s, a);
-      hipLaunchKernelGGL(k_att2_prep, dim3((unsigned)np), dim3(128 * PREP_PARTS), 0, s, a);
+      if (L.k_new && !L.new_f32) hipLaunchKernelGGL(k_att2_prep<true>, dim3((unsigned)np), dim3(128 * PREP_PARTS), 0, s, a);
+      else hipLaunchKernelGGL(k_att2_prep<false>, dim3((unsigned)np), dim3(128 * PREP_PARTS), 0, s, a);
       switch (inst) {
         case 0: at2_launch<4, 10, 1, 4, true, true>(grid, s, a); break;
         case 1: at2_launch<4, 10, 1, 4, true, false>(grid, s, a); break;
@@ -3296,7 +3408,12 @@ int launch_attend(const AttendLaunch& L, void* stream) {
       hipLaunchKernelGGL(kAttKernels[var][L.rec && !L.rht ? 1 : 0], grid, dim3(64 * waves), att_lds, s, a);
     }
     // the splits' partials -> out, once every split has written its own
-    hipLaunchKernelGGL(k_att_combine, dim3((unsigned)np), dim3(CMB_THREADS), CMB_LDS, s, a);
+    // few pairs with many splits: a workgroup per (pair, query head), the
+    // splits merged eight ways; else a workgroup per pair
+    if (np <= 64 && a.n_splits >= 16)
+      hipLaunchKernelGGL(k_att_combine_head, dim3((unsigned)np, (unsigned)L.group), dim3(CMBH_THREADS), 0, s, a);
+    else
+      hipLaunchKernelGGL(k_att_combine, dim3((unsigned)np), dim3(CMB_THREADS), cmb_lds_bytes(L.group), s, a);
   }
   return hipGetLastError() != hipSuccess;
 }
