@@ -122,7 +122,7 @@ inline size_t packed_bytes(int64_t total_bits, int64_t n) {
 constexpr int ATT_TILE = 256;
 // `round`: workgroups resident at once (256 CUs times the kernel's workgroups
 // per CU); the workspace covers every kernel's split count (ATT_ROUNDS).
-constexpr int64_t ATT_ROUNDS[2] = {768, 1024};
+constexpr int64_t ATT_ROUNDS[3] = {256, 768, 1024};
 inline int64_t att_split_tokens(int64_t n_pairs, int64_t n_tokens, int64_t round) {
   // at least one round of workgroups; among up to twice the fewest splits
   // per pair, the count that fills the last round best; a pair has at most

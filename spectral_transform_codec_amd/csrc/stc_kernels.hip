@@ -3378,7 +3378,10 @@ int launch_attend(const AttendLaunch& L, void* stream) {
                                   at2_occ(3, 1, 4, false, false), at2_occ(4, 1, 4, false, false),
                                   at2_occ(4, 1, 4, false, true),  at2_occ(4, 1, 4, false, false),
                                   at2_occ(4, 2, 8, false, false), at2_occ(8, 3, 8, false, false)};
-  const int64_t round = inst >= 0 && kOcc[inst] == 4 ? ATT_ROUNDS[1] : ATT_ROUNDS[0];
+  // one round of workgroups: the CUs times the instance's workgroups per CU
+  // (the older family: one per CU)
+  const int64_t round = inst >= 0 ? (kOcc[inst] == 4 ? ATT_ROUNDS[2] : kOcc[inst] == 3 ? ATT_ROUNDS[1] : ATT_ROUNDS[0])
+                                  : ATT_ROUNDS[0];
   for (long long c0 = 0; c0 < L.n_pairs; c0 += ATT_MAX_PAIRS) {
     const long long np = L.n_pairs - c0 < ATT_MAX_PAIRS ? L.n_pairs - c0 : ATT_MAX_PAIRS;
     a.pair_base = c0;
