@@ -963,7 +963,7 @@ __global__ void __launch_bounds__(DEC_THREADS, 1) k_decode_eigen(DecK a) {
       }
     }
     if (tid < 128) {
-      sTab[tid] = (unsigned)hdr->off[tid & ~3];                              // group record offset
+      sTab[tid] = tid < 32 ? (unsigned)hdr->off[4 * tid] : 0u;              // record offset of group tid
       sTab[128 + tid] = (unsigned)hdr->off[tid] - (unsigned)hdr->off[tid & ~3];  // offset in the group
       sTab[256 + tid] = (unsigned)hdr->bits[tid];                            // width
       reinterpret_cast<float*>(sTab)[384 + tid] = -(W16 ? hdr->bias16[tid] : hdr->bias[tid]);  // natural dim order
@@ -1014,25 +1014,48 @@ __global__ void __launch_bounds__(DEC_THREADS, 1) k_decode_eigen(DecK a) {
       // W16: the codes' scale 2^-e16 (exact products in fp16)
       const f16x2 cscale = __builtin_bit_cast(f16x2, (unsigned)__builtin_amdgcn_readfirstlane(hdr->code16));
       u32x4 cf[8];
+      // groups (channels 64h + 4g .. +3) four at a time: the four record
+      // offsets in one read, the position and width tables and then the
+      // eight stream words requested together, so that a batch waits on LDS
+      // twice instead of once per read
+      const lds_u8* tG = lds_ptr(lds_offset(reinterpret_cast<unsigned char*>(sTab + 16 * h)));
+      // (two at a time in the fp32-output and 16-word instances, whose
+      // registers would not hold four)
+      constexpr int GB = (F32OUT || NW > 8) ? 2 : 4;
 #pragma unroll
-      for (int g = 0; g < 16; ++g) {  // group: channels 64h + 4g .. +3
+      for (int gb = 0; gb < 16; gb += GB) {
         // (a state without kept channels, B = 0, has all-zero tables: it
         // reads the stream's first two words and extracts zero-width codes)
-        const unsigned P = tB + LDS_AT(unsigned, tL + 16 * g);
-        const unsigned ix = est_idx_bit(P);
-        const unsigned w = __builtin_amdgcn_alignbit(sStr[ix + 1], sStr[ix], P & 31u);
-        const u32x4 pos = LDS_AT(u32x4, tL + 512 + 16 * g);
-        const u32x4 wid = LDS_AT(u32x4, tL + 1024 + 16 * g);
-        unsigned code[4];
+        const u32x4 go = LDS_AT(u32x4, tG + 4 * (gb & ~3));
+        u32x4 pos[GB], wid[GB];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) code[j] = __builtin_amdgcn_ubfe(w, pos[j], wid[j]);
+        for (int k = 0; k < GB; ++k) {
+          pos[k] = LDS_AT(u32x4, tL + 512 + 16 * (gb + k));
+          wid[k] = LDS_AT(u32x4, tL + 1024 + 16 * (gb + k));
+        }
+        unsigned P[GB], lo[GB], hi[GB];
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-          cf[g >> 1][2 * (g & 1) + j] =
-              W16 ? __builtin_bit_cast(unsigned, (f16x2){(_Float16)(unsigned short)code[2 * j],
-                                                         (_Float16)(unsigned short)code[2 * j + 1]} *
-                                                     cscale)
-                  : bf16_pair_exact((float)code[2 * j], (float)code[2 * j + 1]);
+        for (int k = 0; k < GB; ++k) {
+          P[k] = tB + go[(gb & 3) + k];
+          const unsigned ix = est_idx_bit(P[k]);
+          lo[k] = sStr[ix];
+          hi[k] = sStr[ix + 1];
+        }
+#pragma unroll
+        for (int k = 0; k < GB; ++k) {
+          const int g = gb + k;
+          const unsigned w = __builtin_amdgcn_alignbit(hi[k], lo[k], P[k] & 31u);
+          unsigned code[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) code[j] = __builtin_amdgcn_ubfe(w, pos[k][j], wid[k][j]);
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            cf[g >> 1][2 * (g & 1) + j] =
+                W16 ? __builtin_bit_cast(unsigned, (f16x2){(_Float16)(unsigned short)code[2 * j],
+                                                           (_Float16)(unsigned short)code[2 * j + 1]} *
+                                                       cscale)
+                    : bf16_pair_exact((float)code[2 * j], (float)code[2 * j + 1]);
+        }
       }
       // ---- 3: reconstruct dims 64h + 16ob + r of token t
       const long long tok = tok0 + t32;
