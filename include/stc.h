@@ -487,6 +487,19 @@ stc_status stc_check_state_map(const int32_t* map_dev, int64_t n, int64_t n_stat
 stc_status stc_set_rht_encode_kernel(int32_t kind);
 int32_t stc_get_rht_encode_kernel(void);
 
+/* Debug builds (libstc_debug.so, compiled with -DSTC_DEBUG): the kernels
+ * check the indices they compute (LDS stream words, record byte ranges inside
+ * a stream's capacity, staging offsets, value rows); a failed check sets one
+ * bit of a device word and skips the access it guards. stc_debug_flags
+ * synchronizes `stream`, stores the word in *flags and clears it; bits:
+ * 0 encode stream word, 1 encode copy-out range, 2 decode stream word,
+ * 3 decode record range, 4 attention staging, 5 attention value rows,
+ * 6 generation-step append range, 7 Walsh-Hadamard encode range. Release
+ * builds have no checks: *flags = 0. stc_debug_build returns 1 for a debug
+ * build, else 0. */
+int32_t stc_debug_build(void);
+stc_status stc_debug_flags(uint32_t* flags, stc_stream_t stream);
+
 /* ------------------------------------------------------ diagnostics */
 const char* stc_status_str(stc_status s);
 /* Message of the last error on the calling thread ("" if none). */

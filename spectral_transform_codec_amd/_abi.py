@@ -5,6 +5,7 @@ import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libstc.so")
+DEBUG_LIB_PATH = os.path.join(HERE, "libstc_debug.so")  # the same library with device index checks
 
 D = 128
 STC_OK, STC_EINVAL, STC_EUNSUPPORTED, STC_EBUDGET, STC_EWORKSPACE, STC_EDEVICE = 0, -1, -2, -3, -4, -5
@@ -73,26 +74,55 @@ SIGNATURES = {
     "stc_check_state_map": (c_i32, [c_vp, c_i64, c_i64, c_vp]),
     "stc_set_rht_encode_kernel": (c_i32, [c_i32]),
     "stc_get_rht_encode_kernel": (c_i32, []),
+    "stc_debug_build": (c_i32, []),
+    "stc_debug_flags": (c_i32, [P(ctypes.c_uint32), c_vp]),
     "stc_status_str": (c_cp, [c_i32]),
     "stc_last_error": (c_cp, []),
 }
 
 _lib = None
+_loaded = {}
+
+
+def load(path):
+    """The library at `path` with every declared signature (loaded once)."""
+    if path not in _loaded:
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: build it with __graft_entry__.build() "
+                               "(python -m spectral_transform_codec_amd.build)")
+        h = ctypes.CDLL(path)
+        for name, (res, args) in SIGNATURES.items():
+            f = getattr(h, name)
+            f.restype = res
+            f.argtypes = args
+        _loaded[path] = h
+    return _loaded[path]
 
 
 def lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
-                               "(python -m spectral_transform_codec_amd.build)")
-        h = ctypes.CDLL(LIB_PATH)
-        for name, (res, args) in SIGNATURES.items():
-            f = getattr(h, name)
-            f.restype = res
-            f.argtypes = args
-        _lib = h
+        _lib = load(LIB_PATH)
     return _lib
+
+
+class use_library:
+    """Route the binding's calls to the library at `path` inside a `with`
+    block (for the debug build), then back to the one before."""
+
+    def __init__(self, path):
+        self.path = path
+
+    def __enter__(self):
+        global _lib
+        self.prev = _lib
+        _lib = load(self.path)
+        return _lib
+
+    def __exit__(self, *exc):
+        global _lib
+        _lib = self.prev
+        return False
 
 
 class StcError(RuntimeError):

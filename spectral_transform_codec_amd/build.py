@@ -36,21 +36,28 @@ def _run(cmd):
         raise RuntimeError(f"build step failed ({r.returncode}): {' '.join(cmd)}")
 
 
+DEBUG_LIB = os.path.join(HERE, "libstc_debug.so")
+
+
 def build(verbose: bool = True) -> str:
-    """Compile the HIP kernels and the host library into libstc.so (always
-    recompiles) and return its path."""
+    """Compile the HIP kernels and the host library into libstc.so, and the
+    kernels once more with -DSTC_DEBUG (device index checks) into
+    libstc_debug.so (always recompiles); return the release library's path."""
     hipcc = _hipcc()
     os.makedirs(BUILD, exist_ok=True)
     k_obj = os.path.join(BUILD, "stc_kernels.o")
+    kd_obj = os.path.join(BUILD, "stc_kernels_debug.o")
     h_obj = os.path.join(BUILD, "stc_host.o")
     _run([hipcc, *HIP_FLAGS, "-c", os.path.join(CSRC, "stc_kernels.hip"), "-o", k_obj])
+    _run([hipcc, *HIP_FLAGS, "-DSTC_DEBUG", "-c", os.path.join(CSRC, "stc_kernels.hip"), "-o", kd_obj])
     rocm = os.path.dirname(os.path.dirname(os.path.realpath(hipcc)))
     _run([hipcc, "-x", "c++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-D__HIP_PLATFORM_AMD__",
           "-I" + os.path.join(rocm, "include"), "-c",
           os.path.join(CSRC, "stc_host.cpp"), "-o", h_obj])
-    tmp = LIB + ".tmp"
-    _run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, k_obj, h_obj])
-    os.replace(tmp, LIB)
+    for lib, kobj in ((LIB, k_obj), (DEBUG_LIB, kd_obj)):
+        tmp = lib + ".tmp"
+        _run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, kobj, h_obj])
+        os.replace(tmp, lib)
     return LIB
 
 

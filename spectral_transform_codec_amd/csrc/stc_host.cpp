@@ -973,6 +973,16 @@ stc_status stc_set_rht_encode_kernel(int32_t kind) {
 
 int32_t stc_get_rht_encode_kernel(void) { return g_rht_encode_kernel.load(std::memory_order_relaxed); }
 
+int32_t stc_debug_build(void) { return debug_build(); }
+
+stc_status stc_debug_flags(uint32_t* flags, stc_stream_t stream) {
+  if (!flags) return fail(STC_EINVAL, "debug_flags: NULL output");
+  unsigned f = 0u;
+  if (read_debug_flags(&f, stream)) return fail(STC_EDEVICE, "debug_flags: %s", hipGetErrorString(hipGetLastError()));
+  *flags = f;
+  return ok();
+}
+
 stc_status stc_check_state_map(const int32_t* map_dev, int64_t n, int64_t n_states, stc_stream_t stream) {
   if (n < 0 || n_states < 0) return fail(STC_EINVAL, "check_state_map: negative size");
   if (n == 0) return ok();

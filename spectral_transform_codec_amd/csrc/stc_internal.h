@@ -247,6 +247,10 @@ int launch_encode_rht(const EncodeLaunch& a, void* stream);
 // Walsh-Hadamard encode kernel: 0 the +-1 matrix on the matrix cores, 1 the
 // register butterfly (stc_set_rht_encode_kernel)
 int rht_encode_kernel();
+// debug builds: read and clear the device check word (synchronizes stream);
+// release builds: 0
+int read_debug_flags(unsigned* out, void* stream);
+int debug_build();
 int launch_sketch_eigen(const EncodeLaunch& a, void* stream);
 int launch_decode_rht(const DecodeLaunch& a, void* stream);
 int launch_attend(const AttendLaunch& a, void* stream);

@@ -39,6 +39,34 @@
 
 namespace stc {
 
+// Debug builds (-DSTC_DEBUG, libstc_debug.so): device-side checks of the
+// indices the kernels compute (LDS stream words, record byte ranges inside a
+// stream's capacity, staging offsets, value rows). A failed check sets its
+// bit in stc_debug_word (a vector atomic) and the access it guards is
+// skipped, so the launch completes; stc_debug_flags reads and clears the
+// word. Release builds compile every check to `true`.
+enum : unsigned {
+  DBG_ENC_STREAM = 0,   // encode: LDS stream word of a group
+  DBG_ENC_RANGE = 1,    // encode: copy-out past the stream's capacity
+  DBG_DEC_STREAM = 2,   // decode: LDS stream word of a group
+  DBG_DEC_RANGE = 3,    // decode: record bytes past the stream
+  DBG_ATT_STAGE = 4,    // attention: staged record words past a staging buffer
+  DBG_ATT_VROW = 5,     // attention: value row past the wave's rows
+  DBG_APPEND = 6,       // generation step: record words past the stream's capacity
+  DBG_RHT_RANGE = 7,    // Walsh-Hadamard encode: record past the stream's capacity
+};
+#ifdef STC_DEBUG
+__device__ unsigned stc_debug_word;
+__device__ __forceinline__ bool dbg_check(bool ok, unsigned bit) {
+  if (__builtin_expect(ok, 1)) return true;
+  __hip_atomic_fetch_or(&stc_debug_word, 1u << bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return false;
+}
+#define STC_CHECK(cond, bit) dbg_check((cond), (bit))
+#else
+#define STC_CHECK(cond, bit) true
+#endif
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -139,6 +167,34 @@ __global__ void __launch_bounds__(256) k_gram(const void* x0, int dtype, long lo
 #pragma unroll
     for (int v = 0; v < 8; ++v) gram[(ti + 16 * u) * 128 + tj + 16 * v] = acc[u][v] / (double)n;
   (void)inv_n;
+}
+
+int read_debug_flags(unsigned* out, void* stream) {
+#ifdef STC_DEBUG
+  hipStream_t s = (hipStream_t)stream;
+  unsigned zero = 0u;
+  if (hipMemcpyFromSymbolAsync(out, HIP_SYMBOL(stc_debug_word), sizeof(unsigned), 0, hipMemcpyDeviceToHost, s) !=
+          hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess)
+    return 1;
+  if (hipMemcpyToSymbolAsync(HIP_SYMBOL(stc_debug_word), &zero, sizeof(unsigned), 0, hipMemcpyHostToDevice, s) !=
+          hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess)
+    return 1;
+  return 0;
+#else
+  (void)stream;
+  *out = 0u;
+  return 0;
+#endif
+}
+
+int debug_build() {
+#ifdef STC_DEBUG
+  return 1;
+#else
+  return 0;
+#endif
 }
 
 int launch_gram(const void* x, int dtype, int64_t ld, int64_t x_stride, int64_t n_calib, int64_t n_streams,
@@ -398,6 +454,7 @@ __global__ void __launch_bounds__(ENC_THREADS, 1) k_encode_eigen(EncK a) {
             v = (unsigned long long)(tok_ok ? word : 0u) << (P & 31u);
             dst = sStr + est_idx_bit(P);
           }
+          if (!STC_CHECK((unsigned)(dst - sStr) + 1u < (unsigned)EST_WORDS, DBG_ENC_STREAM)) return;
           __hip_atomic_fetch_or(dst, (unsigned)v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
           __hip_atomic_fetch_or(dst + 1, (unsigned)(v >> 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         };
@@ -542,6 +599,7 @@ __global__ void __launch_bounds__(ENC_THREADS, 1) k_encode_eigen(EncK a) {
           __builtin_amdgcn_s_waitcnt(0xc07f);
           __builtin_amdgcn_wave_barrier();
         }
+        if (!STC_CHECK(a.packed_stride == 0 || start + nbytes <= a.packed_stride, DBG_ENC_RANGE)) nbytes = 0;
         if (REC) rec_copy_out<4>(sStr, dst, nbytes, clear, lane, rsh);  // (records of 32 * 2^s bits: whole words)
         else if (cw_kind == 4u) est_copy_out<4>(sStr, dst, nbytes, clear, lane);
         else if (cw_kind == 2u) est_copy_out<2>(sStr, dst, nbytes, clear, lane);
@@ -974,8 +1032,9 @@ __global__ void __launch_bounds__(DEC_THREADS, 1) k_decode_eigen(DecK a) {
     // bytes of a block's records (the stream's last block may be short)
     auto rec_bytes = [&](long long tt2, long long& start) {
       start = tt2 * 4LL * (long long)B;
-      const long long nb = 4LL * (long long)B;
-      return nb > P_len - start ? P_len - start : nb;
+      const long long nb0 = 4LL * (long long)B;
+      const long long nb = nb0 > P_len - start ? P_len - start : nb0;
+      return STC_CHECK(a.packed_stride == 0 || start + nb <= a.packed_stride, DBG_DEC_RANGE) ? nb : 0LL;
     };
     // NW <= 4 (records of at most 256 bits): the next block's records are
     // requested as soon as the current ones are in LDS, into the same
@@ -1038,8 +1097,12 @@ __global__ void __launch_bounds__(DEC_THREADS, 1) k_decode_eigen(DecK a) {
         for (int k = 0; k < GB; ++k) {
           P[k] = tB + go[(gb & 3) + k];
           const unsigned ix = est_idx_bit(P[k]);
-          lo[k] = sStr[ix];
-          hi[k] = sStr[ix + 1];
+          if (STC_CHECK(ix + 1u < (unsigned)EST_WORDS, DBG_DEC_STREAM)) {
+            lo[k] = sStr[ix];
+            hi[k] = sStr[ix + 1];
+          } else {
+            lo[k] = hi[k] = 0u;
+          }
         }
 #pragma unroll
         for (int k = 0; k < GB; ++k) {
@@ -1364,7 +1427,8 @@ __global__ void __launch_bounds__(SKETCH ? 64 * RHTS_WAVES : 64 * RHT_WAVES, SKE
       }
       __builtin_amdgcn_sched_barrier(0);  // one row block's accumulators live at a time
     }
-    if (tok0 + t32 < n) {
+    if (tok0 + t32 < n && STC_CHECK(a.packed_stride == 0 || (a.n_old + tok0 + t32 + 1) * 48 <= a.packed_stride,
+                                    DBG_RHT_RANGE)) {
       const long long tk = a.n_old + tok0 + t32;
       u32x2* dst = reinterpret_cast<u32x2*>(a.packed + s * a.packed_stride + tk * 48 + 24 * h);
       dst[0] = (u32x2){w[0], w[1]};
@@ -1510,7 +1574,8 @@ __global__ void __launch_bounds__(64 * RHTB_WAVES, 4) k_rht_encode_bfly(RhtK a) 
       if ((bp & 31) > 29) w[(bp >> 5) + 1] |= q >> (32 - (bp & 31));
       if ((i & 7) == 7) __builtin_amdgcn_sched_barrier(0);  // compare masks of 8 values live at a time
     }
-    if (tok0 + t32 < n) {
+    if (tok0 + t32 < n && STC_CHECK(a.packed_stride == 0 || (a.n_old + tok0 + t32 + 1) * 48 <= a.packed_stride,
+                                    DBG_RHT_RANGE)) {
       const long long tk = a.n_old + tok0 + t32;
       u32x2* dst = reinterpret_cast<u32x2*>(a.packed + s * a.packed_stride + tk * 48 + 24 * h);
       dst[0] = (u32x2){w[0], w[1]};
@@ -2587,7 +2652,7 @@ constexpr int AT2_GEN = 0, AT2_SWZ = 1, AT2_DIRECT = 2;
 // that never read them.
 template <int R2M, int MODE>
 __device__ __forceinline__ void at2_read(unsigned (&r)[R2M], const unsigned* buf, unsigned off, unsigned B, int R2,
-                                         int t, int h) {
+                                         int t, int h, unsigned lim) {
   if (MODE == AT2_DIRECT) {
     // slot t + 32 h holds the 16 bytes from the word that holds the half
     // record's first bit; off is that bit's position in the word
@@ -2609,6 +2674,7 @@ __device__ __forceinline__ void at2_read(unsigned (&r)[R2M], const unsigned* buf
   const unsigned* w = buf + (P >> 5);
   const unsigned sh = P & 31u;
   unsigned x[R2M + 1];
+  if (!STC_CHECK((P >> 5) + R2M < lim, DBG_ATT_STAGE)) w = buf;
 #pragma unroll
   for (int j = 0; j <= R2M; ++j) x[j] = w[j];
 #pragma unroll
@@ -2684,7 +2750,7 @@ constexpr int PREP_PARTS = 2;  // (256 threads: many workgroups per CU)
 // word are kept. sbuf: 64 words of LDS for this wave.
 template <bool F32>
 __device__ void append_record(const unsigned char* st, const void* x, unsigned char* stream, long long n_old,
-                              unsigned* sbuf, int lane) {
+                              long long stride, unsigned* sbuf, int lane) {
   const DevHdr* hdr = reinterpret_cast<const DevHdr*>(st + OFF_HDR);
   const unsigned B = (unsigned)__builtin_amdgcn_readfirstlane(hdr->total_bits);
   if (B == 0) return;  // no kept channel: the stream has no bytes
@@ -2758,7 +2824,7 @@ __device__ void append_record(const unsigned char* st, const void* x, unsigned c
   const long long w0 = P0 >> 5;
   const int nw = (int)(packed_len((long long)B, n_old + 1) / 4 - w0);  // <= 33 + 3 words
   unsigned* s32 = reinterpret_cast<unsigned*>(stream);
-  if (lane < nw) {
+  if (lane < nw && STC_CHECK(stride == 0 || 4 * (w0 + nw) <= stride, DBG_APPEND)) {
     unsigned v = sbuf[lane];
     if (lane == 0 && sh0 != 0u) v |= s32[w0] & ((1u << sh0) - 1u);
     s32[w0 + lane] = v;
@@ -2777,7 +2843,7 @@ __device__ __forceinline__ void att_append_pair(const AttK& a, long long pg, lon
   const unsigned char* st = (wave == 0 ? a.k_states : a.v_states) + (size_t)si * STATE_BYTES;
   unsigned char* stream = const_cast<unsigned char*>(wave == 0 ? a.k_packed : a.v_packed) + pg * a.packed_stride;
   const unsigned char* x = static_cast<const unsigned char*>(wave == 0 ? a.k_new : a.v_new) + pg * 128 * (F32 ? 4 : 2);
-  append_record<F32>(st, x, stream, n_old, sbuf[wave], lane);
+  append_record<F32>(st, x, stream, n_old, a.packed_stride, sbuf[wave], lane);
 }
 
 // The appends in a launch of their own: fp32 token rows (their three-pass
@@ -3087,8 +3153,8 @@ __global__ void __launch_bounds__(64 * W, at2_occ(R2M, NCH, W, SWZ, G4)) k_att2(
     const bool tail = tok0 + AT2_BT > tend;  // (uniform) the split ends inside this block
     unsigned rk[R2M], rv[R2M];
     const unsigned* bk = sStage + cur * 2 * SWORDS;
-    at2_read<R2M, MODE>(rv, bk + SWORDS, MODE == AT2_DIRECT ? vsh : offv[0], Bv, R2v, t32, h);
-    if constexpr (!S16) at2_read<R2M, MODE>(rk, bk, MODE == AT2_DIRECT ? ksh : offk[0], Bk, R2k, t32, h);
+    at2_read<R2M, MODE>(rv, bk + SWORDS, MODE == AT2_DIRECT ? vsh : offv[0], Bv, R2v, t32, h, SWORDS);
+    if constexpr (!S16) at2_read<R2M, MODE>(rk, bk, MODE == AT2_DIRECT ? ksh : offk[0], Bk, R2k, t32, h, SWORDS);
 #pragma unroll
     for (int st = 0; st < NST - 1; ++st) {
       offk[st] = offk[st + 1];
@@ -3100,7 +3166,8 @@ __global__ void __launch_bounds__(64 * W, at2_occ(R2M, NCH, W, SWZ, G4)) k_att2(
     for (int i = 0; i < R2M; ++i) {
       const u32x2 y = at2_quad_split(rv[i], sel1, sel_e, sel_o);
       const unsigned row = (unsigned)(4 * (i + h * R2M) + e4);
-      *reinterpret_cast<u32x2*>(sV + at2_vrowo(R2M, OCC, row) + 2 * (t32 >> 2)) = y;
+      const unsigned vo = at2_vrowo(R2M, OCC, row) + 2 * (t32 >> 2);
+      if (STC_CHECK(vo + 2u <= (unsigned)VWORDS, DBG_ATT_VROW)) *reinterpret_cast<u32x2*>(sV + vo) = y;
     }
     // ---- scores: int8 MFMAs, A = weights (rows 4H + p), B = the record bits
     float su[NHL];  // unscaled scores of the lane's slots (-inf past the split)

@@ -33,6 +33,20 @@ def test_exports_every_declared_symbol():
     assert set(names) == set(_abi.SIGNATURES), set(names) ^ set(_abi.SIGNATURES)
 
 
+def test_debug_build_exports_every_declared_symbol():
+    """The debug build (device index checks) has the same C ABI and says so;
+    the release build has no checks and reports no flags."""
+    D = _abi.load(_abi.DEBUG_LIB_PATH)
+    for name in _declared_symbols():
+        assert hasattr(D, name), name
+    assert D.stc_debug_build() == 1
+    L = _abi.lib()
+    assert L.stc_debug_build() == 0
+    f = ctypes.c_uint32(7)
+    assert L.stc_debug_flags(ctypes.byref(f), None) == _abi.STC_OK and f.value == 0
+    assert L.stc_debug_flags(None, None) == _abi.STC_EINVAL
+
+
 def test_sizes():
     assert stc.state_bytes() == 512 * 1024
     for b, n in [(170, 4096), (256, 1), (384, 32768), (13, 7), (0, 5)]:
