@@ -19,4 +19,9 @@ int launch_decode_rht(const DecodeLaunch&, void*) { return 1; }
 int launch_attend(const AttendLaunch&, void*) { return 1; }
 size_t attend_scratch_bytes() { return 0; }
 int attend_scratch(void**) { return 1; }
+int read_debug_flags(unsigned* out, void*) {
+  *out = 0u;
+  return 0;
+}
+int debug_build() { return 0; }
 }  // namespace stc
