@@ -824,7 +824,8 @@ def summarize(args):
     if args.summarize_trace:
         agg = collections.defaultdict(list)
         for name, _, _, ns in _profile_rows(args.summarize_trace, False):
-            agg[name].append(ns)
+            if args.kernel is None or args.kernel in name:  # (--kernel: a name filter, e.g. the namespace)
+                agg[name].append(ns)
         tot = sum(sum(v) for v in agg.values())
         out.append(f"{'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'share%':>7}  kernel")
         for name, v in sorted(agg.items(), key=lambda kv: -sum(kv[1])):
