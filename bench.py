@@ -620,6 +620,37 @@ def rht_encode_kernels(c, args, dev):
     return out
 
 
+def copy_ceiling(args, dev):
+    """The practical ceiling of a read + write pattern: device copies of
+    4 GiB (far past the 256 MiB memory-side cache), read + written bytes per
+    second, with the library's streaming copy kernel and with torch's copy.
+    Not part of value."""
+    import torch
+
+    import spectral_transform_codec_amd as stc
+    nbytes = 4 << 30
+    src = torch.ones(nbytes, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    stream = torch.cuda.current_stream()
+    out = {"bytes_copied": nbytes}
+    for name, fn in (("stream_copy", lambda: stc.stream_copy(dst, src)), ("torch_copy", lambda: dst.copy_(src))):
+        for _ in range(2):
+            fn()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(5):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        gbps = 2 * nbytes * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+        out[name] = {"GBps": round(gbps, 1), "pct_hbm_peak": round(100.0 * gbps / HBM_PEAK_GBPS, 1)}
+    del src, dst
+    torch.cuda.empty_cache()
+    return out
+
+
 def full_step(args, dev):
     import torch
 
@@ -724,6 +755,8 @@ def full_step(args, dev):
     # the caches are not needed any more: free them before the extras
     del ops, caches
     torch.cuda.empty_cache()
+    if not args.no_extras:
+        line["achievable"] = copy_ceiling(args, dev)
     if not args.no_extras and args.workload == "full":
         line["layer"] = layer_step(args, dev)
     if not args.no_cpu_baseline and args.workload == "full":

@@ -500,6 +500,13 @@ int32_t stc_get_rht_encode_kernel(void);
 int32_t stc_debug_build(void);
 stc_status stc_debug_flags(uint32_t* flags, stc_stream_t stream);
 
+/* Measurement helper: a plain streaming copy of `bytes` (a multiple of 16;
+ * both buffers 16-byte aligned, not overlapping) on `stream`, with 16-byte
+ * loads and non-temporal stores: the practical ceiling of a read + write
+ * pattern against which the codec kernels' rates are read (it computes
+ * nothing of the method). STC_EINVAL on a bad size or pointer. */
+stc_status stc_stream_copy(void* dst_dev, const void* src_dev, int64_t bytes, stc_stream_t stream);
+
 /* ------------------------------------------------------ diagnostics */
 const char* stc_status_str(stc_status s);
 /* Message of the last error on the calling thread ("" if none). */

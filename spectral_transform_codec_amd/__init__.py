@@ -311,6 +311,15 @@ def get_rht_encode_kernel() -> int:
     return int(lib().stc_get_rht_encode_kernel())
 
 
+def stream_copy(dst: torch.Tensor, src: torch.Tensor) -> None:
+    """Measurement helper: copy src's bytes into dst (both contiguous, same
+    byte size, a multiple of 16) with the library's streaming copy kernel."""
+    assert dst.is_contiguous() and src.is_contiguous()
+    nb = src.numel() * src.element_size()
+    assert dst.numel() * dst.element_size() == nb
+    check("stc_stream_copy", lib().stc_stream_copy(_ptr(dst), _ptr(src), nb, _stream()))
+
+
 def encode_kv_batched(states: StateArray, x: torch.Tensor, state_of_stream: Optional[torch.Tensor] = None,
                       packed: Optional[torch.Tensor] = None, norms: Optional[torch.Tensor] = None):
     """x: [S][n][128] (row and stream strides from the tensor) -> packed [S][stride] uint8

@@ -75,6 +75,7 @@ SIGNATURES = {
     "stc_set_rht_encode_kernel": (c_i32, [c_i32]),
     "stc_get_rht_encode_kernel": (c_i32, []),
     "stc_debug_build": (c_i32, []),
+    "stc_stream_copy": (c_i32, [c_vp, c_vp, c_i64, c_vp]),
     "stc_debug_flags": (c_i32, [P(ctypes.c_uint32), c_vp]),
     "stc_status_str": (c_cp, [c_i32]),
     "stc_last_error": (c_cp, []),

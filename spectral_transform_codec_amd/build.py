@@ -47,16 +47,18 @@ def build(verbose: bool = True) -> str:
     os.makedirs(BUILD, exist_ok=True)
     k_obj = os.path.join(BUILD, "stc_kernels.o")
     kd_obj = os.path.join(BUILD, "stc_kernels_debug.o")
+    c_obj = os.path.join(BUILD, "stc_copy.o")
     h_obj = os.path.join(BUILD, "stc_host.o")
     _run([hipcc, *HIP_FLAGS, "-c", os.path.join(CSRC, "stc_kernels.hip"), "-o", k_obj])
     _run([hipcc, *HIP_FLAGS, "-DSTC_DEBUG", "-c", os.path.join(CSRC, "stc_kernels.hip"), "-o", kd_obj])
+    _run([hipcc, *HIP_FLAGS, "-c", os.path.join(CSRC, "stc_copy.hip"), "-o", c_obj])
     rocm = os.path.dirname(os.path.dirname(os.path.realpath(hipcc)))
     _run([hipcc, "-x", "c++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-D__HIP_PLATFORM_AMD__",
           "-I" + os.path.join(rocm, "include"), "-c",
           os.path.join(CSRC, "stc_host.cpp"), "-o", h_obj])
     for lib, kobj in ((LIB, k_obj), (DEBUG_LIB, kd_obj)):
         tmp = lib + ".tmp"
-        _run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, kobj, h_obj])
+        _run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, kobj, c_obj, h_obj])
         os.replace(tmp, lib)
     return LIB
 

@@ -975,6 +975,16 @@ int32_t stc_get_rht_encode_kernel(void) { return g_rht_encode_kernel.load(std::m
 
 int32_t stc_debug_build(void) { return debug_build(); }
 
+stc_status stc_stream_copy(void* dst_dev, const void* src_dev, int64_t bytes, stc_stream_t stream) {
+  if (bytes < 0 || bytes % 16) return fail(STC_EINVAL, "stream_copy: bytes must be a non-negative multiple of 16");
+  if (bytes == 0) return ok();
+  if (!dst_dev || !src_dev || !aligned(dst_dev, 16) || !aligned(src_dev, 16))
+    return fail(STC_EINVAL, "stream_copy: NULL or misaligned buffer");
+  if (launch_stream_copy(dst_dev, src_dev, bytes, stream))
+    return fail(STC_EDEVICE, "stream_copy launch: %s", hipGetErrorString(hipGetLastError()));
+  return ok();
+}
+
 stc_status stc_debug_flags(uint32_t* flags, stc_stream_t stream) {
   if (!flags) return fail(STC_EINVAL, "debug_flags: NULL output");
   unsigned f = 0u;

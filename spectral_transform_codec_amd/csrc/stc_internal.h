@@ -250,6 +250,7 @@ int rht_encode_kernel();
 // debug builds: read and clear the device check word (synchronizes stream);
 // release builds: 0
 int read_debug_flags(unsigned* out, void* stream);
+int launch_stream_copy(void* dst, const void* src, int64_t bytes, void* stream);
 int debug_build();
 int launch_sketch_eigen(const EncodeLaunch& a, void* stream);
 int launch_decode_rht(const DecodeLaunch& a, void* stream);

@@ -24,4 +24,5 @@ int read_debug_flags(unsigned* out, void*) {
   return 0;
 }
 int debug_build() { return 0; }
+int launch_stream_copy(void*, const void*, int64_t, void*) { return 1; }
 }  // namespace stc

@@ -537,3 +537,15 @@ def test_out_of_range_state_map_entries():
     ok = stc.attend_compressed_batched(arr, good[0::2].contiguous(), good[1::2].contiguous(), ref[0::2], ref[1::2],
                                        n, q).cpu().numpy()
     assert np.array_equal(out[0], ok[0]) and np.all(np.isnan(out[1]))
+
+
+def test_stream_copy():
+    """The measurement helper's copy moves every byte (ragged tail of the
+    grid-stride loop included)."""
+    g = torch.Generator(device=DEV)
+    g.manual_seed(11)
+    for nb in (16, 4096 + 48, (1 << 22) + 16 * 7):
+        src = torch.randint(0, 256, (nb,), dtype=torch.uint8, device=DEV, generator=g)
+        dst = torch.zeros_like(src)
+        stc.stream_copy(dst, src)
+        assert torch.equal(dst, src)

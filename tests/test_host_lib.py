@@ -242,3 +242,13 @@ def test_batched_calibration_validates_arguments_without_device_work():
     assert call(128, 4, 2048, fake, _abi.BF16, 128, 2048 * 128, 2.0, 1, None, fake, None) == _abi.STC_EINVAL
     # no streams: nothing to do
     assert call(128, 0, 2048, fake, _abi.BF16, 128, 0, 2.0, 1, infos, fake, None) == _abi.STC_OK
+
+
+def test_stream_copy_validates_arguments_without_device_work():
+    L = _abi.lib()
+    fake = ctypes.c_void_p(4096)
+    assert L.stc_stream_copy(fake, fake, 0, None) == _abi.STC_OK
+    assert L.stc_stream_copy(fake, fake, 24, None) == _abi.STC_EINVAL
+    assert L.stc_stream_copy(fake, fake, -16, None) == _abi.STC_EINVAL
+    assert L.stc_stream_copy(ctypes.c_void_p(4100), fake, 32, None) == _abi.STC_EINVAL
+    assert L.stc_stream_copy(None, fake, 32, None) == _abi.STC_EINVAL
