@@ -227,7 +227,7 @@ stc_status stc_calibrate_head(int32_t d, int64_t n_calib, const void* x_dev, int
  * states_dev + s * stc_state_bytes() (256-byte aligned; the layout of the
  * batched calls) with its summary in infos[s]. One launch forms every second
  * moment; the eigenbases, widths and blobs are then built on host threads
- * and uploaded at once. Each state equals the one stc_calibrate_head would
+ * and uploaded, 256 streams at a time (host memory stays near 160 MB). Each state equals the one stc_calibrate_head would
  * build from the same rows. Synchronizes `stream`. A failing stream (a
  * non-finite second moment, ...) returns its status, names the stream in
  * stc_last_error and leaves the states undefined. */

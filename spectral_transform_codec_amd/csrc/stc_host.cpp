@@ -912,45 +912,56 @@ stc_status stc_calibrate_heads_batched(int32_t d, int64_t n_streams, int64_t n_c
   if (launch_gram(x_dev, dtype, ld, x_stream_stride, n_calib, n_streams,
                   reinterpret_cast<double*>(base + OFF_GRAM), (int64_t)(STATE_BYTES / sizeof(double)), stream))
     return fail(STC_EDEVICE, "gram launch: %s", hipGetErrorString(hipGetLastError()));
+  // the host part in chunks of at most 256 streams (host memory stays near
+  // 160 MB whatever the batch): download the chunk's second moments, build
+  // its eigenbases, widths and blobs on worker threads, upload its states
   const size_t dd = (size_t)D * D;
-  std::vector<double> g(dd * (size_t)n_streams);
+  constexpr int64_t CHUNK = 256;
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
-  if (stc_status st = hip_check(hipMemcpy2DAsync(g.data(), dd * sizeof(double), base + OFF_GRAM, STATE_BYTES,
-                                                 dd * sizeof(double), (size_t)n_streams, hipMemcpyDeviceToHost, hs),
-                                "gram download"))
-    return st;
-  if (stc_status st = hip_check(hipStreamSynchronize(hs), "gram sync")) return st;
   // the lazily filled step tables, before the workers read them
   for (int b = 1; b <= STC_MAX_BITS; ++b) (void)stc_delta_star(b);
-  // eigenbasis, widths and blob of each stream on the host, streams spread
-  // over worker threads; each worker keeps the first failure it meets
-  std::vector<unsigned char> all((size_t)n_streams * STATE_BYTES);
   const unsigned hw = std::thread::hardware_concurrency();
-  const int64_t n_thr = std::min<int64_t>(n_streams, std::max(1u, std::min(hw, 16u)));
-  std::atomic<int64_t> next{0};
-  std::vector<stc_status> thr_status((size_t)n_thr, STC_OK);
-  std::vector<std::string> thr_msg((size_t)n_thr);
-  auto work = [&](int64_t t) {
-    std::vector<unsigned char> blob;
-    for (int64_t i = next.fetch_add(1); i < n_streams; i = next.fetch_add(1)) {
-      stc_status st = state_from_gram("calibrate_heads_batched", g.data() + dd * (size_t)i, xform, budget, nullptr,
-                                      &infos[i], blob);
-      if (st) {
-        thr_status[(size_t)t] = st;
-        thr_msg[(size_t)t] = "stream " + std::to_string(i) + ": " + stc_last_error();
-        next.store(n_streams);
-        return;
+  std::vector<double> g(dd * (size_t)std::min(n_streams, CHUNK));
+  std::vector<unsigned char> all((size_t)std::min(n_streams, CHUNK) * STATE_BYTES);
+  for (int64_t c0 = 0; c0 < n_streams; c0 += CHUNK) {
+    const int64_t nc = std::min(CHUNK, n_streams - c0);
+    if (stc_status st = hip_check(hipMemcpy2DAsync(g.data(), dd * sizeof(double), base + c0 * STATE_BYTES + OFF_GRAM,
+                                                   STATE_BYTES, dd * sizeof(double), (size_t)nc,
+                                                   hipMemcpyDeviceToHost, hs),
+                                  "gram download"))
+      return st;
+    if (stc_status st = hip_check(hipStreamSynchronize(hs), "gram sync")) return st;
+    // streams spread over worker threads; each worker keeps the first failure it meets
+    const int64_t n_thr = std::min<int64_t>(nc, std::max(1u, std::min(hw, 16u)));
+    std::atomic<int64_t> next{0};
+    std::vector<stc_status> thr_status((size_t)n_thr, STC_OK);
+    std::vector<std::string> thr_msg((size_t)n_thr);
+    auto work = [&](int64_t t) {
+      std::vector<unsigned char> blob;
+      for (int64_t i = next.fetch_add(1); i < nc; i = next.fetch_add(1)) {
+        stc_status st = state_from_gram("calibrate_heads_batched", g.data() + dd * (size_t)i, xform, budget, nullptr,
+                                        &infos[c0 + i], blob);
+        if (st) {
+          thr_status[(size_t)t] = st;
+          thr_msg[(size_t)t] = "stream " + std::to_string(c0 + i) + ": " + stc_last_error();
+          next.store(nc);
+          return;
+        }
+        std::memcpy(all.data() + (size_t)i * STATE_BYTES, blob.data(), STATE_BYTES);
       }
-      std::memcpy(all.data() + (size_t)i * STATE_BYTES, blob.data(), STATE_BYTES);
-    }
-  };
-  std::vector<std::thread> pool;
-  for (int64_t t = 1; t < n_thr; ++t) pool.emplace_back(work, t);
-  work(0);
-  for (auto& th : pool) th.join();
-  for (int64_t t = 0; t < n_thr; ++t)
-    if (thr_status[(size_t)t]) return fail(thr_status[(size_t)t], "%s", thr_msg[(size_t)t].c_str());
-  if (stc_status st = upload(all, states_dev, stream)) return st;
+    };
+    std::vector<std::thread> pool;
+    for (int64_t t = 1; t < n_thr; ++t) pool.emplace_back(work, t);
+    work(0);
+    for (auto& th : pool) th.join();
+    for (int64_t t = 0; t < n_thr; ++t)
+      if (thr_status[(size_t)t]) return fail(thr_status[(size_t)t], "%s", thr_msg[(size_t)t].c_str());
+    if (stc_status st = hip_check(hipMemcpyAsync(base + c0 * STATE_BYTES, all.data(), (size_t)nc * STATE_BYTES,
+                                                 hipMemcpyHostToDevice, hs),
+                                  "state upload"))
+      return st;
+    if (stc_status st = hip_check(hipStreamSynchronize(hs), "state upload sync")) return st;
+  }
   return ok();
 }
 

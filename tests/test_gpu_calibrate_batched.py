@@ -62,3 +62,16 @@ def test_batched_non_finite_stream_named():
     x = torch.from_numpy(xs).to(torch.bfloat16).to(DEV)
     with pytest.raises(stc.StcError, match="stream 2"):
         stc.calibrate_heads_batched(x, 2048, 2.0)
+
+
+def test_batched_chunk_boundaries():
+    """More streams than one host chunk (256): states on both sides of the
+    chunk boundaries equal the single-stream call's."""
+    w = synth.WORKLOADS[2]
+    base = np.stack([synth.stream(w, 0, 0, h // 2, h % 2, n=2048) for h in range(6)]).astype(np.float32)
+    xs = np.concatenate([base] * 50)           # 300 streams
+    x = torch.from_numpy(xs).to(torch.bfloat16).to(DEV)
+    arr = stc.calibrate_heads_batched(x, 2048, 2.0)
+    assert arr.n == 300
+    for i in (0, 255, 256, 299):
+        _same_state(arr, i, stc.calibrate_head(x[i], 2048, 2.0))
