@@ -2618,6 +2618,15 @@ __device__ __forceinline__ unsigned at2_tab_off16(unsigned c) {
   const unsigned dw = c >> 5, kk = (c & 7u) >> 2;
   return (2u * (dw & 1u) + kk) * 64u + (dw >> 1) * 16u + (c & 3u) * 4u + ((c >> 3) & 3u);
 }
+// The unscaled score from the three parts' accumulators: the integer
+// 2^14 p0 + 2^7 p1 + p2 is S times the score, and S (at most 2^20 over the
+// largest weight |a_j| 2^(b_j - 1)) keeps it within 2^28 for 128 channels,
+// so the int32 sum is exact and one conversion rounds it.
+__device__ __forceinline__ float at2_score(int p0, int p1, int p2) {
+  int x = p0 * 128 + p1;
+  asm("" : "+v"(x));  // (kept as two shift-adds, not reassociated into three operations)
+  return (float)(x * 128 + p2);
+}
 // position of token t of a block in the P / value-operand order: inside each
 // group of four tokens the order is 0, 2, 1, 3
 __device__ __forceinline__ int at2_pos(int t) { return (t & ~3) | ((t & 1) << 1) | ((t >> 1) & 1); }
@@ -2701,8 +2710,10 @@ __device__ __forceinline__ unsigned at2_stage(const unsigned char* stream, unsig
   int lim = (int)plen - (int)base;  // bytes past base that the lanes may read (uniform)
   if (MODE == AT2_GEN && lim > (int)(start - base + 4u * B)) lim = (int)(start - base + 4u * B);
   if (MODE == AT2_DIRECT && lim > (int)(4u * B + 16u)) lim = (int)(4u * B + 16u);
-  if (lim < 0) lim = 0;
-  if (lim > 1024 * NCH + 16) lim = 1024 * NCH + 16;  // (the loads reach no further)
+  // (scalar clamps: the first value passes readfirstlane, so that the two are
+  // not merged into one vector med3)
+  lim = __builtin_amdgcn_readfirstlane(lim < 0 ? 0 : lim);
+  if (MODE != AT2_DIRECT && lim > 1024 * NCH + 16) lim = 1024 * NCH + 16;  // (the loads reach no further)
 #if defined(__HIP_DEVICE_COMPILE__)  // (buffer resources exist in the device pass only)
   // (uniform by construction; readfirstlane keeps the resource in scalar registers)
   const unsigned long long ad = (unsigned long long)(stream + (lim > 0 ? base : 0u));
@@ -3106,6 +3117,17 @@ __global__ void __launch_bounds__(64 * W, at2_occ(R2M, NCH, W, SWZ, G4)) k_att2(
       asm volatile("" : "+v"(vaddr[T]), "+v"(vmask[T]));
     }
   }
+  // LDS address of the lane's score-weight row. 16x16x64: lane row c16 =
+  // 4H + p holds part p of head H, k-block g4; 32x32x32: lane row t32 = 4H + p,
+  // half h. Table row 3H + p, or the zero row for p = 3 and heads past the
+  // table.
+  unsigned abase;
+  {
+    const int rr = S16 ? c16 : t32;
+    const int trow = ((rr & 3) == 3 || (rr >> 2) >= NH) ? 3 * NH : 3 * (rr >> 2) + (rr & 3);
+    abase = lds_offset(reinterpret_cast<unsigned char*>(sA) + trow * TROW + (S16 ? g4 * 16 : h * R2M * 32));
+    asm volatile("" : "+v"(abase));
+  }
   const unsigned PkL = (unsigned)packed_len((long long)Bk, n), PvL = (unsigned)packed_len((long long)Bv, n);
   const unsigned char* gk = a.k_packed + pg * a.packed_stride;
   const unsigned char* gv = a.v_packed + pg * a.packed_stride;
@@ -3172,10 +3194,7 @@ __global__ void __launch_bounds__(64 * W, at2_occ(R2M, NCH, W, SWZ, G4)) k_att2(
     // ---- scores: int8 MFMAs, A = weights (rows 4H + p), B = the record bits
     float su[NHL];  // unscaled scores of the lane's slots (-inf past the split)
     if constexpr (S16) {
-      const int trow = ((c16 & 3) == 3 || (c16 >> 2) >= NH) ? 3 * NH : 3 * (c16 >> 2) + (c16 & 3);
-      unsigned ab = lds_offset(reinterpret_cast<unsigned char*>(sA) + trow * TROW + g4 * 16);
-      asm volatile("" : "+v"(ab));
-      const lds_u8* aL = lds_ptr(ab);
+      const lds_u8* aL = lds_ptr(abase);
       u32x4 av[4];
 #pragma unroll
       for (int st = 0; st < 4; ++st) av[st] = LDS_AT(u32x4, aL + 64 * st);
@@ -3199,19 +3218,14 @@ __global__ void __launch_bounds__(64 * W, at2_occ(R2M, NCH, W, SWZ, G4)) k_att2(
           a16 = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, av[st]),
                                                       __builtin_bit_cast(i32x4, at2_bits(kw[G][st >> 1], st & 1)), a16,
                                                       0, 0, 0);
-        su[G] = __builtin_fmaf((float)((a16[0] << 7) + a16[1]), 128.0f, (float)a16[2]);
+        su[G] = at2_score(a16[0], a16[1], a16[2]);
         if (tail && tok0 + 16 * G + c16 >= tend) su[G] = -INFINITY;
       }
     } else {
       i32x16 acc;
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[e] = 0;
-      // lane row t32 = 4H + p of the MFMA holds part p of head H: table row
-      // 3H + p, or the zero row for p = 3 and heads past the table
-      const int trow = ((t32 & 3) == 3 || (t32 >> 2) >= NH) ? 3 * NH : 3 * (t32 >> 2) + (t32 & 3);
-      unsigned ab = lds_offset(reinterpret_cast<unsigned char*>(sA) + trow * TROW + h * R2M * 32);
-      asm volatile("" : "+v"(ab));
-      const lds_u8* aL = lds_ptr(ab);
+      const lds_u8* aL = lds_ptr(abase);
       // (all of the block's weight reads are issued first, so that their
       // latencies overlap; words past a half record meet zero weights)
       u32x4 av[2 * R2M];
@@ -3226,7 +3240,7 @@ __global__ void __launch_bounds__(64 * W, at2_occ(R2M, NCH, W, SWZ, G4)) k_att2(
       }
 #pragma unroll
       for (int i = 0; i < NHL; ++i) {
-        su[i] = __builtin_fmaf((float)((acc[4 * i] << 7) + acc[4 * i + 1]), 128.0f, (float)acc[4 * i + 2]);
+        su[i] = at2_score(acc[4 * i], acc[4 * i + 1], acc[4 * i + 2]);
       }
       if (tail) {  // (uniform) tokens past the split
 #pragma unroll
@@ -3250,7 +3264,10 @@ __global__ void __launch_bounds__(64 * W, at2_occ(R2M, NCH, W, SWZ, G4)) k_att2(
         // (no token of the head so far: max 0, every P and sum so far 0)
         const float mset = mnew == -INFINITY ? 0.0f : mnew;
         const float alpha = mold[i] == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(mold[i] - mset);
-        mold[i] = mset;
+        // (a copy after the last use of the old max, which alpha's operand
+        // makes it: the running max keeps one register through the loop,
+        // with no moves on the fast path)
+        asm volatile("v_mov_b32 %0, %1" : "=v"(mold[i]) : "v"(mset), "v"(alpha));
         thr[i] = (mset + 8.0f) / invS[i];
         if (S16 ? (c16 == 0 && i == 0) : t32 == 0) sAl[S16 ? g4 : 2 * i + h] = alpha;
       }
