@@ -1774,6 +1774,9 @@ struct AttK {
   const void* k_new;
   const void* v_new;
   int new_f32;
+  // packed-bit kernel with one split per pair: each workgroup forms its
+  // pair's output itself (the merge kernel is not launched)
+  int direct;
 };
 
 constexpr int ATT_WAVES_MAX = 16;
@@ -1993,6 +1996,56 @@ __device__ __forceinline__ void cmb_merge(const float* ph, int S, int s0, int st
   }
 }
 
+// Mean code of V channel j from the merged sums: step_j (A / L - (L_j - 1)/2),
+// 0 for a dropped channel.
+__device__ __forceinline__ float cmb_code(const DevHdr* hv, int j, double A, double L) {
+  return hv->bits[j] ? (float)((double)hv->step32[j] * (A / L - (double)hv->halfspan[j])) : 0.0f;
+}
+
+// o = U_V chat for every head of a pair, from the mean codes sC [g][128]:
+// thread (half, i) of the first CMB_THREADS sums its half of row i of U_V
+// (16 floats at a time) against every head's codes; the halves are added
+// through sQ [2][g][128] and written to out [g][128]. Every thread of the
+// workgroup calls it (it holds a barrier).
+__device__ __forceinline__ void cmb_rotate(const float* sC, float* sQ, const unsigned char* vst, int g, float* out,
+                                           int t) {
+  if (t < CMB_THREADS) {
+    const int i = t & 127, half = t >> 7;
+    const f32x4* urow = reinterpret_cast<const f32x4*>(vst + OFF_U32) + i * 32 + half * 16;  // U[i][64 half ..]
+    float o[16];
+#pragma unroll
+    for (int hh = 0; hh < 16; ++hh) o[hh] = 0.0f;
+#pragma unroll
+    for (int jc = 0; jc < 4; ++jc) {
+      f32x4 u[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) u[r] = urow[4 * jc + r];
+#pragma unroll
+      for (int hh = 0; hh < 16; ++hh) {
+        if (hh < g) {
+          const f32x4* c4 = reinterpret_cast<const f32x4*>(sC + hh * 128 + 64 * half + 16 * jc);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const f32x4 c = c4[r];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[hh] = __builtin_fmaf(u[r][e], c[e], o[hh]);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int hh = 0; hh < 16; ++hh)
+      if (hh < g) sQ[(half * g + hh) * 128 + i] = o[hh];
+  }
+  __syncthreads();
+  if (t < CMB_THREADS) {
+    for (int e = t; e < g * 128; e += CMB_THREADS) {
+      const int hh = e >> 7, ii = e & 127;
+      out[hh * 128 + ii] = sQ[hh * 128 + ii] + sQ[(g + hh) * 128 + ii];
+    }
+  }
+}
+
 __global__ void __launch_bounds__(CMB_THREADS) k_att_combine(AttK a) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int g = a.group;
@@ -2016,41 +2069,10 @@ __global__ void __launch_bounds__(CMB_THREADS) k_att_combine(AttK a) {
     float M;
     double A, L;
     cmb_merge(ph, S, 0, 1, PS, j, M, A, L);
-    // dequantize the mean code: step * (A / L - (L_j - 1)/2)
-    sC[hh * 128 + j] = hv->bits[j] ? (float)((double)hv->step32[j] * (A / L - (double)hv->halfspan[j])) : 0.0f;
+    sC[hh * 128 + j] = cmb_code(hv, j, A, L);
   }
   __syncthreads();
-  const int i = t & 127, half = t >> 7;
-  const f32x4* urow = reinterpret_cast<const f32x4*>(vst + OFF_U32) + i * 32 + half * 16;  // U[i][64 half ..]
-  float o[16];
-#pragma unroll
-  for (int hh = 0; hh < 16; ++hh) o[hh] = 0.0f;
-#pragma unroll
-  for (int jc = 0; jc < 4; ++jc) {
-    f32x4 u[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) u[r] = urow[4 * jc + r];
-#pragma unroll
-    for (int hh = 0; hh < 16; ++hh) {
-      if (hh < g) {
-        const f32x4* c4 = reinterpret_cast<const f32x4*>(sC + hh * 128 + 64 * half + 16 * jc);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const f32x4 c = c4[r];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) o[hh] = __builtin_fmaf(u[r][e], c[e], o[hh]);
-        }
-      }
-    }
-  }
-#pragma unroll
-  for (int hh = 0; hh < 16; ++hh)
-    if (hh < g) sQ[(half * g + hh) * 128 + i] = o[hh];
-  __syncthreads();
-  for (int e = t; e < g * 128; e += CMB_THREADS) {
-    const int hh = e >> 7, ii = e & 127;
-    a.out[(pg * g + hh) * 128 + ii] = sQ[hh * 128 + ii] + sQ[(g + hh) * 128 + ii];
-  }
+  cmb_rotate(sC, sQ, vst, g, a.out + pg * g * 128, t);
 }
 
 __global__ void __launch_bounds__(CMBH_THREADS) k_att_combine_head(AttK a) {
@@ -2104,7 +2126,7 @@ __global__ void __launch_bounds__(CMBH_THREADS) k_att_combine_head(AttK a) {
         }
       }
     }
-    sC[t] = hv->bits[t] ? (float)((double)hv->step32[t] * (A / L - (double)hv->halfspan[t])) : 0.0f;
+    sC[t] = cmb_code(hv, t, A, L);
   }
   __syncthreads();
   float o = 0.0f;
@@ -3010,7 +3032,11 @@ __global__ void __launch_bounds__(64 * W, at2_occ(R2M, NCH, W, SWZ, G4)) k_att2(
   const long long n = a.n_tokens;
   const int g = a.group;
   const long long ksi = state_index(a.k_map, pg, a.n_states), vsi = state_index(a.v_map, pg, a.n_states);
-  if (ksi < 0 || vsi < 0) return;  // (the whole workgroup) the merge writes NaN for this pair
+  if (ksi < 0 || vsi < 0) {  // (the whole workgroup) no state: NaN, written here or by the merge
+    if (a.direct)
+      for (int e = tid; e < g * 128; e += blockDim.x) a.out[pg * g * 128 + e] = __builtin_nanf("");
+    return;
+  }
   const unsigned char* kst = a.k_states + (size_t)ksi * STATE_BYTES;
   const unsigned char* vst = a.v_states + (size_t)vsi * STATE_BYTES;
   const DevHdr* hk = reinterpret_cast<const DevHdr*>(kst);
@@ -3337,7 +3363,16 @@ __global__ void __launch_bounds__(64 * W, at2_occ(R2M, NCH, W, SWZ, G4)) k_att2(
     }
   }
   __syncthreads();
-  for (int e = tid; e < g * 128; e += blockDim.x) {
+  // the split's partial (acc, m, l) per head; with one split per pair
+  // (direct), the mean codes, as the merge would form them from this one
+  // partial (weight exp2(m - m) = 1; nothing merged for a split without
+  // tokens)
+  constexpr int NE = 8 * 128 / (64 * W);  // elements per thread at most
+  float code[NE];
+#pragma unroll
+  for (int k = 0; k < NE; ++k) {
+    const int e = tid + 64 * W * k;
+    if (e >= g * 128) break;
     const int hh = e >> 7, jj = e & 127;
     const unsigned cc = sVch[jj];
     const int c0 = (int)(cc & 0xFFFFu), nc = (int)(cc >> 16);
@@ -3351,14 +3386,32 @@ __global__ void __launch_bounds__(64 * W, at2_occ(R2M, NCH, W, SWZ, G4)) k_att2(
       const float mw = rw[16 * NT];
       const float f = (mw == -INFINITY) ? 0.0f : exp2f(mw - M);
       float v = 0.0f;
-      for (int k = 0; k < nc; ++k)
-        if (c0 + k < 16 * NT) v += sFac[c0 + k] * rw[c0 + k];
+      for (int k2 = 0; k2 < nc; ++k2)
+        if (c0 + k2 < 16 * NT) v += sFac[c0 + k2] * rw[c0 + k2];
       A += f * v;
       Ls += f * rw[ncols];  // (the sum column)
     }
-    float* ph = part + hh * ATT_PART_FLOATS;
-    ph[jj] = cols_ok ? A : __builtin_nanf("");
-    if (jj == 0) { ph[128] = M; ph[129] = Ls; }
+    if (!cols_ok) A = __builtin_nanf("");
+    if (a.direct) {
+      code[k] = M == -INFINITY ? cmb_code(hv, jj, 0.0, 0.0) : cmb_code(hv, jj, (double)A, (double)Ls);
+    } else {
+      float* ph = part + hh * ATT_PART_FLOATS;
+      ph[jj] = A;
+      if (jj == 0) { ph[128] = M; ph[129] = Ls; }
+    }
+  }
+  if (a.direct) {  // (uniform)
+    static_assert((size_t)3 * 8 * 128 <= (size_t)W * 8 * CST, "mean codes and half sums fit the merge scratch");
+    float* sC = red;            // [g][128] mean codes
+    float* sQ = red + g * 128;  // [2][g][128] half sums
+    __syncthreads();            // every thread is done reading the wave partials
+#pragma unroll
+    for (int k = 0; k < NE; ++k) {
+      const int e = tid + 64 * W * k;
+      if (e < g * 128) sC[e] = code[k];
+    }
+    __syncthreads();
+    cmb_rotate(sC, sQ, vst, g, a.out + pg * g * 128, tid);
   }
 }
 
@@ -3497,6 +3550,7 @@ int launch_attend(const AttendLaunch& L, void* stream) {
     a.n_splits = att_n_splits(np, L.n_tokens, round);
     const size_t att_lds = fixed + (size_t)waves * a.region_words * 4;
     const dim3 grid((unsigned)a.n_splits, (unsigned)np);
+    a.direct = inst >= 0 && a.n_splits == 1;
     if (inst >= 0) {
       a.prep = reinterpret_cast<float*>(a.ws) + att_partial_floats(np, L.n_tokens, L.group, round);
       if (L.k_new && L.new_f32) hipLaunchKernelGGL(k_att_append, dim3((unsigned)np), dim3(128), 0, s, a);
@@ -3518,8 +3572,10 @@ int launch_attend(const AttendLaunch& L, void* stream) {
       hipLaunchKernelGGL(kAttKernels[var][L.rec && !L.rht ? 1 : 0], grid, dim3(64 * waves), att_lds, s, a);
     }
     // the splits' partials -> out, once every split has written its own
+    // (the packed-bit kernel with one split per pair has written out itself);
     // few pairs with many splits: a workgroup per (pair, query head), the
     // splits merged eight ways; else a workgroup per pair
+    if (a.direct) continue;
     if (np <= 64 && a.n_splits >= 16)
       hipLaunchKernelGGL(k_att_combine_head, dim3((unsigned)np, (unsigned)L.group), dim3(CMBH_THREADS), 0, s, a);
     else

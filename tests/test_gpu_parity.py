@@ -292,6 +292,40 @@ def test_attention_batched_gqa7():
         assert rel_err(out[i], wants[i]) <= 2e-3
 
 
+def test_attention_one_split_per_pair():
+    """With a full round of pairs each pair gets one workgroup, which forms
+    the output itself instead of leaving a partial for the merge kernel. 3072
+    copies of one GQA-7 pair (one split each: whole rounds at 1, 3 or 4
+    workgroups per CU) against the same pair alone
+    (four splits and the merge): the copies agree bit for bit, and both paths
+    agree with the oracle within 2e-3 (they differ from each other by the
+    fp16 rounding of the softmax weights, which each split scales by its own
+    running maximum)."""
+    w = synth.WORKLOADS[5]
+    n, pairs = 1000, 3072
+    k = synth.stream(w, 0, 0, 2, 0, n=n)
+    v = synth.stream(w, 0, 0, 2, 1, n=n)
+    ks, vs = codec.calibrate_head(k, n, 1.33), codec.calibrate_head(v, n, 1.33)
+    kp, vp = codec.encode_kv(ks, k), codec.encode_kv(vs, v)
+    q = synth.queries(w, 0, 0, 2)
+    want = codec.attend_compressed(ks, vs, kp, vp, n, q.astype(np.float64))
+    arr = stc.StateArray([gpu_state(ks), gpu_state(vs)])
+    stride = stc.packed_bytes(arr.max_bits, n)
+    kb = torch.zeros((pairs, stride), dtype=torch.uint8, device=DEV)
+    vb = torch.zeros((pairs, stride), dtype=torch.uint8, device=DEV)
+    kb[:, :kp.shape[0]] = torch.from_numpy(kp).to(DEV)
+    vb[:, :vp.shape[0]] = torch.from_numpy(vp).to(DEV)
+    qd = torch.from_numpy(q).to(DEV)
+    zeros = torch.zeros(pairs, dtype=torch.int32, device=DEV)
+    many = stc.attend_compressed_batched(arr, zeros, zeros + 1, kb, vb, n,
+                                         qd.unsqueeze(0).expand(pairs, -1, -1).contiguous()).cpu().numpy()
+    one = stc.attend_compressed_batched(arr, zeros[:1], zeros[:1] + 1, kb[:1], vb[:1], n,
+                                        qd.unsqueeze(0)).cpu().numpy()[0]
+    assert np.all(many == many[0])
+    assert rel_err(many[0], want) <= 2e-3, rel_err(many[0], want)
+    assert rel_err(one, want) <= 2e-3, rel_err(one, want)
+
+
 @pytest.mark.parametrize("case", att_variants.CASES, ids=lambda c: f"cfg{c[0]}-{c[1]:.3f}-g{c[2]}")
 def test_attention_kernel_variants(case):
     """One case per instance of the packed-bit attention kernel (record
@@ -509,14 +543,16 @@ def test_attention_workspace_reused_across_shapes():
             assert rel_err(out[i], wants[i]) <= 2e-3, (pairs, g, n, i, rel_err(out[i], wants[i]))
 
 
-def test_out_of_range_state_map_entries():
+@pytest.mark.parametrize("n", [700, 200])
+def test_out_of_range_state_map_entries(n):
     """A map entry outside [0, n_states) never codes a stream with another
     state: encode leaves its bytes untouched, decode writes NaN rows, attention
-    NaN outputs; the other streams are unaffected and check_state_map names it."""
+    NaN outputs; the other streams are unaffected and check_state_map names it.
+    700 tokens: three splits per pair and the merge kernel; 200: one split,
+    whose workgroup writes the output itself."""
     w = synth.WORKLOADS[2]
-    n = 700
     xs = [synth.stream(w, 0, 0, h, kind, n=n) for h in range(2) for kind in (0, 1)]
-    sts = [codec.calibrate_head(x, 512, 2.0) for x in xs]
+    sts = [codec.calibrate_head(x, min(512, n), 2.0) for x in xs]
     arr = stc.StateArray([gpu_state(st) for st in sts])
     x = torch.stack([dev_tensor(xi, "bf16") for xi in xs])
     good = torch.tensor([0, 1, 2, 3], dtype=torch.int32, device=DEV)
