@@ -470,13 +470,25 @@ __global__ void __launch_bounds__(ENC_THREADS, 1) k_encode_eigen(EncK a) {
               for (int j = 0; j < 4; ++j) acc[4 * i + j] = yh[j];
             }
           };
+          // The basis rows of chain step i = 8 mb + ks are read LA steps
+          // ahead of their MFMAs, and a scheduling barrier keeps the reads
+          // there: left to itself the compiler issues each read right before
+          // its MFMA and waits for it. (fp32 tokens, three MFMAs per step,
+          // keep LA = 0: their registers would not hold the extra rows.)
+          constexpr int LA = MODE == 0 ? 1 : 0;
+          bf16x8 ahr[LA + 1], alr[LA + 1];
+          auto readA = [&](const int i) {
+            const int off = 32 * (i >> 3) * UROW + 32 * (i & 7);
+            ahr[i % (LA + 1)] = LDS_AT(bf16x8, uL + off);
+            alr[i % (LA + 1)] = LDS_AT(bf16x8, uL + 128 * UROW + off);
+          };
           auto chain_step = [&](const int mb, const int ks, f32x16& acc) {
-            const int off = 32 * mb * UROW + 32 * ks;
-            const bf16x8 ah = LDS_AT(bf16x8, uL + off);
-            const bf16x8 al = LDS_AT(bf16x8, uL + 128 * UROW + off);
-            acc = mfma32_bf16(ah, xh[ks], acc);
-            acc = mfma32_bf16(al, xh[ks], acc);
-            if (MODE == 1) acc = mfma32_bf16(ah, xl[ks], acc);
+            const int i = 8 * mb + ks;
+            if (i + LA < 32) readA(i + LA);
+            if (LA > 0) __builtin_amdgcn_sched_barrier(0);
+            acc = mfma32_bf16(ahr[i % (LA + 1)], xh[ks], acc);
+            acc = mfma32_bf16(alr[i % (LA + 1)], xh[ks], acc);
+            if (MODE == 1) acc = mfma32_bf16(ahr[i % (LA + 1)], xl[ks], acc);
           };
           // ---- 2: the code is floor(acc) clamped to [0, L-1], per group of
           // four channels
@@ -496,6 +508,8 @@ __global__ void __launch_bounds__(ENC_THREADS, 1) k_encode_eigen(EncK a) {
           // of row block mb + 1 runs on the MFMA unit, row block mb is
           // quantized (one group of four channels per two steps).
           f32x16 acc0, acc1;
+#pragma unroll
+          for (int i = 0; i < LA; ++i) readA(i);
           chain_init(0, acc0);
 #pragma unroll
           for (int ks = 0; ks < 8; ++ks) chain_step(0, ks, acc0);
@@ -1124,6 +1138,19 @@ __global__ void __launch_bounds__(DEC_THREADS, 1) k_decode_eigen(DecK a) {
       const long long tok = tok0 + t32;
       const bool tok_ok = tok < n;
       u32x4 pk[4][2];  // bf16 output, dims 64h + 16ob + 8c .. +7 in pk[ob][c]
+      // the rows of W for chain step i = 8 ob + ks, read DLA steps ahead of
+      // their MFMA (kept there by a scheduling barrier, as in the encode;
+      // the bf16 hi / lo pair keeps DLA = 0: its registers would not hold
+      // the extra rows)
+      constexpr int DLA = W16 ? 1 : 0;
+      u32x4 whr[DLA + 1], wlr[DLA + 1];
+      auto readW = [&](const int i) {
+        const int off = 32 * (i >> 3) * UROW + 16 * (i & 7);
+        whr[i % (DLA + 1)] = LDS_AT(u32x4, wL + off);
+        if (!W16) wlr[i % (DLA + 1)] = LDS_AT(u32x4, wL + 128 * UROW + off);
+      };
+#pragma unroll
+      for (int i = 0; i < DLA; ++i) readW(i);
 #pragma unroll
       for (int ob = 0; ob < 4; ++ob) {
         // the accumulator starts at -bias
@@ -1136,15 +1163,15 @@ __global__ void __launch_bounds__(DEC_THREADS, 1) k_decode_eigen(DecK a) {
         }
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
-          const int off = 32 * ob * UROW + 16 * ks;
+          const int i = 8 * ob + ks;
+          if (i + DLA < 32) readW(i + DLA);
+          if (DLA > 0) __builtin_amdgcn_sched_barrier(0);
           if (W16) {
-            const f16x8 w = LDS_AT(f16x8, wL + off);
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(w, __builtin_bit_cast(f16x8, cf[ks]), acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, whr[i % (DLA + 1)]),
+                                                         __builtin_bit_cast(f16x8, cf[ks]), acc, 0, 0, 0);
           } else {
-            const bf16x8 wh = LDS_AT(bf16x8, wL + off);
-            const bf16x8 wl = LDS_AT(bf16x8, wL + 128 * UROW + off);
-            acc = mfma32_bf16(wh, __builtin_bit_cast(bf16x8, cf[ks]), acc);
-            acc = mfma32_bf16(wl, __builtin_bit_cast(bf16x8, cf[ks]), acc);
+            acc = mfma32_bf16(__builtin_bit_cast(bf16x8, whr[i % (DLA + 1)]), __builtin_bit_cast(bf16x8, cf[ks]), acc);
+            acc = mfma32_bf16(__builtin_bit_cast(bf16x8, wlr[i % (DLA + 1)]), __builtin_bit_cast(bf16x8, cf[ks]), acc);
           }
         }
         if (F32OUT) {
