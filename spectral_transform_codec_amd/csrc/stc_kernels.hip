@@ -508,6 +508,10 @@ __global__ void __launch_bounds__(ENC_THREADS, 1) k_encode_eigen(EncK a) {
           // of row block mb + 1 runs on the MFMA unit, row block mb is
           // quantized (one group of four channels per two steps).
           f32x16 acc0, acc1;
+          // bf16 tokens: the wave's MFMA chains run at raised priority, so
+          // that the SIMD's arbiter favours waves that keep the matrix core
+          // fed over waves in their copy-out (measured about 1% faster)
+          if (MODE == 0) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
           for (int i = 0; i < LA; ++i) readA(i);
           chain_init(0, acc0);
@@ -524,6 +528,7 @@ __global__ void __launch_bounds__(ENC_THREADS, 1) k_encode_eigen(EncK a) {
               if (ks & 1) quant_group(mb, ks >> 1, cur);
             }
             if (MODE == 0 && mb == 2 && blk + ENC_WAVES < seg_end) load_frags(s, tt + ENC_WAVES);
+            if (MODE == 0 && mb == 2) __builtin_amdgcn_s_setprio(0);  // the chains are done
           }
         } else {
 #pragma unroll
